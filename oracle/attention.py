@@ -1,0 +1,222 @@
+"""Plain fp64 CPU oracle for the single-pass attention backward (and the forward
+that produces its inputs O, m, l).
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import or call this
+module: only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` use it. It shares no code with the HIP library.
+
+What it computes, and where the pages define it:
+
+* Backward, per (sequence b, head h), following the eight per-tile steps of the
+  PyPTO-Gym SK-16 article ("single-pass attention backward (FA Grad)"), §3.1,
+  with the dtype discipline of its §4.2 reduced to exact fp64 arithmetic:
+    1. S  = Q K^T                        (the scale is applied in step 2)
+    2. P  = exp(S*scale - m) / l         (m, l are the caller's row statistics)
+    3. dP = dO V^T
+    4. D  = rowsum(O * dO)               (from the O the caller passes)
+    5. dS = P * (dP - D)
+    6. dK = scale * dS^T Q
+    7. dV = P^T dO
+    8. dQ = scale * dS K
+  The article runs these per (q_tile, kv_tile) pair and accumulates; the sum
+  over tiles equals the untiled matrix products written here, so the oracle
+  uses the whole (b, h) slice at once and does no tiling of its own.
+* Masks: the codes of ``MaskType`` in jax ``_src/cudnn/fused_attention_stablehlo.py``
+  (NO_MASK=0, PADDING=1, CAUSAL=2, PADDING_CAUSAL=3). Causal visibility is
+  top-left aligned in sequence-local coordinates (key j visible from query i
+  iff j <= i); the pages do not fix the alignment when the two lengths differ.
+* Sequence layout: packed modes (NO_MASK, CAUSAL) place sequence b at rows
+  [cu[b], cu[b+1]) as in the article's ``actual_q``/``actual_kv`` offsets (§三).
+  Padded modes (PADDING, PADDING_CAUSAL) place sequence b at rows
+  [b*max_seqlen, b*max_seqlen + L_b) with L_b = cu[b+1] - cu[b], i.e. the
+  BTNH padded layout of the jax page with per-batch valid lengths; the other
+  rows of the slot are padding.
+* Forward (input producer only): m = row max of the scaled visible logits,
+  l = sum over visible keys of exp(scaled logit - m), O = P V; this is the
+  reading under which step 2 above is the softmax.
+
+Rows outside every sequence: forward gives O = 0, m = 0, l = 1 (finite filler
+that the backward never reads); backward gives dQ = dK = dV = 0. A valid query
+row with no visible key (only when its sequence has no keys) gets P = 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MASK_NONE = 0
+MASK_PADDING = 1
+MASK_CAUSAL = 2
+MASK_PADDING_CAUSAL = 3
+
+
+def is_causal(mask: int) -> bool:
+    return mask in (MASK_CAUSAL, MASK_PADDING_CAUSAL)
+
+
+def is_padded(mask: int) -> bool:
+    return mask in (MASK_PADDING, MASK_PADDING_CAUSAL)
+
+
+def segments(cu, mask: int, max_seqlen: int):
+    """Return [(first_row, length)] per sequence (layout reading in the module docstring)."""
+    cu = [int(x) for x in np.asarray(cu).reshape(-1)]
+    out = []
+    for b in range(len(cu) - 1):
+        length = cu[b + 1] - cu[b]
+        start = b * max_seqlen if is_padded(mask) else cu[b]
+        out.append((start, length))
+    return out
+
+
+def visible(lq: int, lk: int, causal: bool) -> np.ndarray:
+    """Boolean [lq, lk]: may query i attend to key j (sequence-local indices)."""
+    i = np.arange(lq)[:, None]
+    j = np.arange(lk)[None, :]
+    if causal:
+        return j <= i
+    return np.ones((lq, lk), dtype=bool)
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # torch tensor (any dtype) -> exact fp64 values
+        x = x.detach().cpu().double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def softmax_probs(s_scaled: np.ndarray, m: np.ndarray, l: np.ndarray, vis: np.ndarray) -> np.ndarray:
+    """Step 2: P = exp(S*scale - m) / l on visible entries, 0 elsewhere.
+
+    ``s_scaled`` already holds S*scale. Rows whose l is not positive (no
+    visible key) give P = 0.
+    """
+    z = np.where(vis, s_scaled - m[:, None], -np.inf)
+    ok = (l > 0)[:, None]
+    return np.where(vis & ok, np.exp(z) / np.where(ok, l[:, None], 1.0), 0.0)
+
+
+def forward_head(q, k, v, scale: float, causal: bool):
+    """Forward for one (b, h): returns O [Lq,d], m [Lq], l [Lq] in fp64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lq, lk = q.shape[0], k.shape[0]
+    vis = visible(lq, lk, causal)
+    s = scale * (q @ k.T)
+    has_key = vis.any(axis=1)
+    m = np.where(has_key, np.max(np.where(vis, s, -np.inf), axis=1, initial=-np.inf), 0.0)
+    e = np.where(vis, np.exp(np.where(vis, s - m[:, None], 0.0)), 0.0)
+    l = np.where(has_key, e.sum(axis=1), 1.0)
+    p = np.where(has_key[:, None], e / l[:, None], 0.0)
+    o = p @ v
+    return o, m, l
+
+
+def backward_head(q, k, v, o, do, m, l, scale: float, causal: bool):
+    """Backward for one (b, h), steps 1-8 of the module docstring.
+
+    Inputs are one sequence's rows of one head; everything is promoted to fp64.
+    Returns a dict with dq, dk, dv and the intermediates p, dp, dvec, ds.
+    """
+    q, k, v, o, do = _f64(q), _f64(k), _f64(v), _f64(o), _f64(do)
+    m, l = _f64(m), _f64(l)
+    vis = visible(q.shape[0], k.shape[0], causal)
+    s = q @ k.T                                   # 1
+    p = softmax_probs(scale * s, m, l, vis)       # 2
+    dp = do @ v.T                                 # 3
+    dvec = np.sum(o * do, axis=1)                 # 4
+    ds = p * (dp - dvec[:, None])                 # 5
+    dk = scale * (ds.T @ q)                       # 6
+    dv = p.T @ do                                 # 7
+    dq = scale * (ds @ k)                         # 8
+    return {"dq": dq, "dk": dk, "dv": dv, "p": p, "dp": dp, "dvec": dvec, "ds": ds}
+
+
+def forward(q, k, v, cu_q, cu_kv, scale: float, mask: int, max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
+    """Forward over [T, H, d] inputs. Returns fp64 O [Tq,H,d], m [Tq,H], l [Tq,H]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    tq, h_count, d = q.shape
+    o = np.zeros((tq, h_count, v.shape[2]))
+    m = np.zeros((tq, h_count))
+    l = np.ones((tq, h_count))
+    causal = is_causal(mask)
+    for (qs, lq), (ks, lk) in zip(segments(cu_q, mask, max_seqlen_q), segments(cu_kv, mask, max_seqlen_kv)):
+        if lq <= 0:
+            continue
+        for h in range(h_count):
+            ob, mb, lb = forward_head(q[qs:qs + lq, h], k[ks:ks + lk, h], v[ks:ks + lk, h], scale, causal)
+            o[qs:qs + lq, h], m[qs:qs + lq, h], l[qs:qs + lq, h] = ob, mb, lb
+    return o, m, l
+
+
+def backward(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int,
+             max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
+    """Backward over [T, H, d] inputs. Returns fp64 dQ [Tq,H,d], dK, dV [Tkv,H,d]."""
+    q, k, v, o, do = _f64(q), _f64(k), _f64(v), _f64(o), _f64(do)
+    m, l = _f64(m), _f64(l)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    causal = is_causal(mask)
+    for (qs, lq), (ks, lk) in zip(segments(cu_q, mask, max_seqlen_q), segments(cu_kv, mask, max_seqlen_kv)):
+        if lq <= 0 and lk <= 0:
+            continue
+        qsl, ksl = slice(qs, qs + max(lq, 0)), slice(ks, ks + max(lk, 0))
+        for h in range(q.shape[1]):
+            r = backward_head(q[qsl, h], k[ksl, h], v[ksl, h], o[qsl, h], do[qsl, h],
+                              m[qsl, h], l[qsl, h], scale, causal)
+            dq[qsl, h], dk[ksl, h], dv[ksl, h] = r["dq"], r["dk"], r["dv"]
+    return dq, dk, dv
+
+
+def backward_rows(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int, b: int, h: int,
+                  q_rows, kv_rows, max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
+    """Selected outputs of one (b, h), each computed on its own.
+
+    dQ row i needs row i of P and dS (all keys); dK/dV row j needs column j of
+    P and dS (all queries). Indices are sequence-local. Returns
+    (dq [len(q_rows), d], dk [len(kv_rows), d], dv [len(kv_rows), d]) in fp64.
+    This is the same step list as ``backward_head``, restricted to the rows or
+    columns asked for, so that full-size problems can be checked on samples.
+    """
+    qs, lq = segments(cu_q, mask, max_seqlen_q)[b]
+    ks, lk = segments(cu_kv, mask, max_seqlen_kv)[b]
+    causal = is_causal(mask)
+    Q, K, V = _f64(q[qs:qs + lq, h]), _f64(k[ks:ks + lk, h]), _f64(v[ks:ks + lk, h])
+    O, dO = _f64(o[qs:qs + lq, h]), _f64(do[qs:qs + lq, h])
+    M, L = _f64(m[qs:qs + lq, h]), _f64(l[qs:qs + lq, h])
+    dq_out, dk_out, dv_out = [], [], []
+    for i in q_rows:
+        vis = visible(lq, lk, causal)[i:i + 1]
+        s = (Q[i:i + 1] @ K.T)
+        p = softmax_probs(scale * s, M[i:i + 1], L[i:i + 1], vis)
+        dp = dO[i:i + 1] @ V.T
+        dvec = np.sum(O[i] * dO[i])
+        ds = p * (dp - dvec)
+        dq_out.append(scale * (ds @ K)[0])
+    if len(kv_rows):
+        dvec_all = np.sum(O * dO, axis=1)
+    for j in kv_rows:
+        vis = visible(lq, lk, causal)[:, j:j + 1]
+        s = Q @ K[j:j + 1].T
+        p = softmax_probs(scale * s, M, L, vis)
+        dp = dO @ V[j:j + 1].T
+        ds = p * (dp - dvec_all[:, None])
+        dk_out.append(scale * (ds.T @ Q)[0])
+        dv_out.append((p.T @ dO)[0])
+    d = q.shape[2]
+    dv_d = v.shape[2]
+    return (np.array(dq_out).reshape(-1, d), np.array(dk_out).reshape(-1, d),
+            np.array(dv_out).reshape(-1, dv_d))
+
+
+def loss(q, k, v, do, cu_q, cu_kv, scale: float, mask: int, max_seqlen_q: int = 0, max_seqlen_kv: int = 0) -> float:
+    """Scalar sum(O * dO) with dO a fixed cotangent; its gradient is (dQ, dK, dV)."""
+    o, _, _ = forward(q, k, v, cu_q, cu_kv, scale, mask, max_seqlen_q, max_seqlen_kv)
+    return float(np.sum(o * _f64(do)))
+
+
+def valid_rows(cu, mask: int, max_seqlen: int, total: int) -> np.ndarray:
+    """Boolean [total]: rows that belong to some sequence."""
+    ok = np.zeros(total, dtype=bool)
+    for start, length in segments(cu, mask, max_seqlen):
+        if length > 0:
+            ok[max(start, 0):min(start + length, total)] = True
+    return ok

@@ -1,0 +1,374 @@
+"""Pins of the fp64 oracle against facts it does not derive from itself.
+
+Every check here runs on the CPU. The backward's definition is the eight
+per-tile steps of the PyPTO-Gym SK-16 article, §3.1; the mask codes are jax's
+cuDNN ``MaskType``. The pins:
+
+* a hand-derived closed form (two keys, rational softmax weights);
+* central finite differences of sum(O * dO) w.r.t. Q, K, V on tiny shapes,
+  every mask type, packed varlen and padded layouts;
+* invariants: dS rows sum to 0 (so dK columns sum to 0), dV columns sum to dO
+  columns, rowsum(O*dO) = rowsum(P*dP), causal zero patterns;
+* closed forms: one key, all-equal V rows, Q = 0;
+* torch fp64 autograd of softmax(scale*QK^T + mask) V, an independent library;
+* planted mistakes in the oracle's own source, each caught by one of the above.
+"""
+import inspect
+import math
+import textwrap
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as A
+from oracle.attention import MASK_CAUSAL, MASK_NONE, MASK_PADDING, MASK_PADDING_CAUSAL
+
+
+# ---------------------------------------------------------------- helpers
+
+def _rand(shape, rng, mult=1.0):
+    return rng.standard_normal(shape) * mult
+
+
+def make_problem(mask, lens_q, lens_kv, heads=2, d=4, seed=0, padded_len=0, mult=1.0):
+    rng = np.random.default_rng(seed)
+    if A.is_padded(mask):
+        tq = tkv = len(lens_q) * padded_len
+        msq = mskv = padded_len
+    else:
+        tq, tkv = sum(lens_q), sum(lens_kv)
+        msq, mskv = max(lens_q), max(lens_kv)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
+    cu_kv = np.concatenate([[0], np.cumsum(lens_kv)]).astype(np.int64)
+    return dict(q=_rand((tq, heads, d), rng, mult), k=_rand((tkv, heads, d), rng, mult),
+                v=_rand((tkv, heads, d), rng), do=_rand((tq, heads, d), rng),
+                cu_q=cu_q, cu_kv=cu_kv, scale=1.0 / math.sqrt(d), mask=mask,
+                max_seqlen_q=msq, max_seqlen_kv=mskv)
+
+
+def exact_backward(p):
+    """Backward fed with the unrounded fp64 forward (exact mode)."""
+    o, m, l = A.forward(p["q"], p["k"], p["v"], p["cu_q"], p["cu_kv"], p["scale"], p["mask"],
+                        p["max_seqlen_q"], p["max_seqlen_kv"])
+    dq, dk, dv = A.backward(p["q"], p["k"], p["v"], o, p["do"], m, l, p["cu_q"], p["cu_kv"],
+                            p["scale"], p["mask"], p["max_seqlen_q"], p["max_seqlen_kv"])
+    return o, m, l, dq, dk, dv
+
+
+def fd_grads(p, eps=1e-6):
+    """Central differences of loss = sum(O * dO) for every element of Q, K, V."""
+    out = {}
+    for name in ("q", "k", "v"):
+        x = p[name]
+        g = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = A.loss(p["q"], p["k"], p["v"], p["do"], p["cu_q"], p["cu_kv"], p["scale"], p["mask"],
+                        p["max_seqlen_q"], p["max_seqlen_kv"])
+            x[idx] = keep - eps
+            lm = A.loss(p["q"], p["k"], p["v"], p["do"], p["cu_q"], p["cu_kv"], p["scale"], p["mask"],
+                        p["max_seqlen_q"], p["max_seqlen_kv"])
+            x[idx] = keep
+            g[idx] = (lp - lm) / (2 * eps)
+        out[name] = g
+    return out
+
+
+def fd_error(p):
+    _, _, _, dq, dk, dv = exact_backward(p)
+    fd = fd_grads(p)
+    err = 0.0   # worst over Q, K, V of max|fd - analytic| / max|analytic|
+    for name, an in (("q", dq), ("k", dk), ("v", dv)):
+        if an.size:
+            err = max(err, float(np.max(np.abs(fd[name] - an))) / max(float(np.max(np.abs(an))), 1e-30))
+    return err
+
+
+def torch_reference(p):
+    """Independent gradients: torch fp64 autograd of softmax(scale*QK^T + bias) V per (b, h)."""
+    q = torch.tensor(p["q"], requires_grad=True)
+    k = torch.tensor(p["k"], requires_grad=True)
+    v = torch.tensor(p["v"], requires_grad=True)
+    do = torch.tensor(p["do"])
+    nb = len(p["cu_q"]) - 1
+    padded = p["mask"] in (MASK_PADDING, MASK_PADDING_CAUSAL)
+    causal = p["mask"] in (MASK_CAUSAL, MASK_PADDING_CAUSAL)
+    total = torch.zeros((), dtype=torch.float64)
+    for b in range(nb):
+        lq = int(p["cu_q"][b + 1] - p["cu_q"][b])
+        lk = int(p["cu_kv"][b + 1] - p["cu_kv"][b])
+        qs = b * p["max_seqlen_q"] if padded else int(p["cu_q"][b])
+        ks = b * p["max_seqlen_kv"] if padded else int(p["cu_kv"][b])
+        if lq == 0 or lk == 0:
+            continue
+        for h in range(q.shape[1]):
+            qh, kh, vh = q[qs:qs + lq, h], k[ks:ks + lk, h], v[ks:ks + lk, h]
+            logits = p["scale"] * qh @ kh.T
+            if causal:
+                bias = torch.triu(torch.full((lq, lk), float("-inf"), dtype=torch.float64), diagonal=1)
+                logits = logits + bias
+            out = torch.softmax(logits, dim=-1) @ vh
+            total = total + (out * do[qs:qs + lq, h]).sum()
+    total.backward()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+def torch_error(p):
+    _, _, _, dq, dk, dv = exact_backward(p)
+    tq, tk, tv = torch_reference(p)
+    return max(float(np.max(np.abs(a - b))) / max(1.0, float(np.max(np.abs(b))))
+               for a, b in ((dq, tq), (dk, tk), (dv, tv)))
+
+
+FD_CASES = [
+    # (mask, lens_q, lens_kv, d, padded_len)
+    (MASK_NONE, [1], [1], 4, 0),
+    (MASK_NONE, [3], [5], 4, 0),
+    (MASK_NONE, [8], [2], 8, 0),
+    (MASK_NONE, [3, 5], [2, 4], 4, 0),            # two packed sequences
+    (MASK_CAUSAL, [5], [5], 4, 0),
+    (MASK_CAUSAL, [8], [8], 8, 0),
+    (MASK_CAUSAL, [2, 5], [3, 5], 4, 0),          # packed, Lq != Lk in the first sequence
+    (MASK_PADDING, [5, 3], [5, 2], 4, 5),
+    (MASK_PADDING_CAUSAL, [5, 3], [5, 3], 4, 5),
+    (MASK_PADDING_CAUSAL, [2, 1], [3, 2], 4, 3),
+]
+
+
+# ---------------------------------------------------------------- closed form from a hand derivation
+
+LN3 = math.log(3.0)
+
+
+def _two_key(mask, cu_q):
+    # scale 0.5, q = 1, keys (0, 2 ln 3) -> scaled logits (0, ln 3): P = (1/4, 3/4) when both keys are seen
+    nq = cu_q[-1]
+    return dict(q=np.ones((nq, 1, 1)), k=np.array([[[0.0]], [[2 * LN3]]]), v=np.array([[[1.0]], [[5.0]]]),
+                do=np.full((nq, 1, 1), 2.0), cu_q=np.array(cu_q), cu_kv=np.array([0, 2]), scale=0.5,
+                mask=mask, max_seqlen_q=nq, max_seqlen_kv=2)
+
+
+def test_closed_form_two_keys_causal():
+    # row 0 sees key 0 only: P=(1,0), O=1, D=2, dP=(2,10), dS=(0,0)
+    # row 1 sees both: m=ln3, l=4/3, P=(1/4,3/4), O=4, D=8, dS=(-3/2, 3/2)
+    p = _two_key(MASK_CAUSAL, [0, 2])
+    o, m, l, dq, dk, dv = exact_backward(p)
+    np.testing.assert_allclose(o[:, 0, 0], [1.0, 4.0], rtol=1e-15)
+    np.testing.assert_allclose(m[:, 0], [0.0, LN3], rtol=1e-15)
+    np.testing.assert_allclose(l[:, 0], [1.0, 4.0 / 3.0], rtol=1e-15)
+    np.testing.assert_allclose(dq[:, 0, 0], [0.0, 1.5 * LN3], rtol=1e-14, atol=1e-15)   # 0.5 * 3/2 * 2 ln 3
+    np.testing.assert_allclose(dk[:, 0, 0], [-0.75, 0.75], rtol=1e-14)                # 0.5 * (-3/2, 3/2)
+    np.testing.assert_allclose(dv[:, 0, 0], [2.5, 1.5], rtol=1e-14)                   # (1*2 + 2/4, 3/4*2)
+
+
+def test_closed_form_two_keys_one_query():
+    p = _two_key(MASK_NONE, [0, 1])
+    o, m, l, dq, dk, dv = exact_backward(p)
+    np.testing.assert_allclose([o[0, 0, 0], m[0, 0], l[0, 0]], [4.0, LN3, 4.0 / 3.0], rtol=1e-15)
+    np.testing.assert_allclose(dq[0, 0, 0], 1.5 * LN3, rtol=1e-14)
+    np.testing.assert_allclose(dk[:, 0, 0], [-0.75, 0.75], rtol=1e-14)
+    np.testing.assert_allclose(dv[:, 0, 0], [0.5, 1.5], rtol=1e-14)
+
+
+# ---------------------------------------------------------------- finite differences
+
+@pytest.mark.parametrize("mask,lq,lk,d,padded", FD_CASES)
+def test_finite_differences(mask, lq, lk, d, padded):
+    p = make_problem(mask, lq, lk, heads=2, d=d, seed=len(lq) * 7 + sum(lq) + mask, padded_len=padded)
+    assert fd_error(p) < 2e-6
+
+
+def test_padding_rows_get_zero_and_are_not_read():
+    p = make_problem(MASK_PADDING_CAUSAL, [5, 3], [5, 2], heads=2, d=4, seed=3, padded_len=5)
+    o, m, l, dq, dk, dv = exact_backward(p)
+    vq = A.valid_rows(p["cu_q"], p["mask"], 5, 10)
+    vk = A.valid_rows(p["cu_kv"], p["mask"], 5, 10)
+    assert vq.tolist() == [True] * 5 + [True] * 3 + [False] * 2
+    assert vk.tolist() == [True] * 5 + [True] * 2 + [False] * 3
+    assert np.all(dq[~vq] == 0) and np.all(dk[~vk] == 0) and np.all(dv[~vk] == 0)
+    # garbage (NaN) in the padding rows of every input leaves the valid outputs unchanged
+    q2, k2, v2, o2, do2 = (x.copy() for x in (p["q"], p["k"], p["v"], o, p["do"]))
+    m2, l2 = m.copy(), l.copy()
+    for x, ok in ((q2, vq), (o2, vq), (do2, vq), (m2, vq), (l2, vq), (k2, vk), (v2, vk)):
+        x[~ok] = np.nan
+    dq2, dk2, dv2 = A.backward(q2, k2, v2, o2, do2, m2, l2, p["cu_q"], p["cu_kv"], p["scale"], p["mask"], 5, 5)
+    assert np.array_equal(dq2[vq], dq[vq]) and np.array_equal(dk2[vk], dk[vk]) and np.array_equal(dv2[vk], dv[vk])
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("mask", [MASK_NONE, MASK_CAUSAL])
+def test_ds_rows_sum_to_zero_and_dk_columns_vanish(mask):
+    rng = np.random.default_rng(11)
+    q, k, v, do = (rng.standard_normal((40, 16)) for _ in range(4))
+    scale = 0.25
+    o, m, l = A.forward_head(q, k, v, scale, mask == MASK_CAUSAL)
+    r = A.backward_head(q, k, v, o, do, m, l, scale, mask == MASK_CAUSAL)
+    assert np.max(np.abs(r["ds"].sum(axis=1))) < 1e-13
+    assert np.max(np.abs(r["dk"].sum(axis=0))) < 1e-12
+
+
+@pytest.mark.parametrize("mask", [MASK_NONE, MASK_CAUSAL])
+def test_dv_column_sums_equal_do_column_sums(mask):
+    rng = np.random.default_rng(12)
+    q, k, v, do = (rng.standard_normal((33, 8)) for _ in range(4))
+    o, m, l = A.forward_head(q, k, v, 0.3, mask == MASK_CAUSAL)
+    r = A.backward_head(q, k, v, o, do, m, l, 0.3, mask == MASK_CAUSAL)
+    np.testing.assert_allclose(r["dv"].sum(axis=0), do.sum(axis=0), atol=1e-13)
+
+
+def test_d_identity_rowsum_o_do_equals_rowsum_p_dp():
+    # ties the article's D = rowsum(O*dO) (step 4) to the softmax-backward form rowsum(P*dP)
+    # used by the PyPTO block-attention-residual backward for its grad_logits
+    rng = np.random.default_rng(13)
+    q, k, v, do = (rng.standard_normal((25, 8)) for _ in range(4))
+    for causal in (False, True):
+        o, m, l = A.forward_head(q, k, v, 0.5, causal)
+        r = A.backward_head(q, k, v, o, do, m, l, 0.5, causal)
+        np.testing.assert_allclose(r["dvec"], np.sum(r["p"] * r["dp"], axis=1), atol=1e-13)
+
+
+def test_causal_zero_patterns():
+    rng = np.random.default_rng(14)
+    n, d, scale = 12, 8, 0.35
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    o, m, l = A.forward_head(q, k, v, scale, True)
+    r = A.backward_head(q, k, v, o, do, m, l, scale, True)
+    assert np.all(np.triu(r["p"], 1) == 0)
+    assert np.max(np.abs(r["dq"][0])) < 1e-14                 # row 0 sees key 0 only: P00 = 1, dS00 = 0
+    last = n - 1                                              # key n-1 is seen by row n-1 only
+    np.testing.assert_allclose(r["dv"][last], r["p"][last, last] * do[last], rtol=1e-14)
+    np.testing.assert_allclose(r["dk"][last], scale * r["ds"][last, last] * q[last], rtol=1e-12, atol=1e-15)
+    # keys/values after row i do not reach rows 0..i
+    i = 5
+    k2, v2 = k.copy(), v.copy()
+    k2[i + 1:] = rng.standard_normal(k2[i + 1:].shape) * 3
+    v2[i + 1:] = rng.standard_normal(v2[i + 1:].shape) * 3
+    o2, m2, l2 = A.forward_head(q, k2, v2, scale, True)
+    r2 = A.backward_head(q, k2, v2, o2, do, m2, l2, scale, True)
+    assert np.array_equal(o2[:i + 1], o[:i + 1]) and np.array_equal(m2[:i + 1], m[:i + 1])
+    assert np.array_equal(r2["dq"][:i + 1], r["dq"][:i + 1])
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_single_key():
+    rng = np.random.default_rng(15)
+    q, do = rng.standard_normal((7, 4)), rng.standard_normal((7, 4))
+    k, v = rng.standard_normal((1, 4)), rng.standard_normal((1, 4))
+    o, m, l = A.forward_head(q, k, v, 0.5, False)
+    r = A.backward_head(q, k, v, o, do, m, l, 0.5, False)
+    np.testing.assert_allclose(r["p"], 1.0, rtol=1e-15)
+    assert np.max(np.abs(r["dq"])) < 1e-14 and np.max(np.abs(r["dk"])) < 1e-13
+    np.testing.assert_allclose(r["dv"][0], do.sum(axis=0), rtol=1e-13)
+
+
+def test_equal_value_rows_give_zero_dq_dk():
+    rng = np.random.default_rng(16)
+    q, k, do = (rng.standard_normal((9, 4)) for _ in range(3))
+    v = np.tile(rng.standard_normal((1, 4)), (9, 1))
+    for causal in (False, True):
+        o, m, l = A.forward_head(q, k, v, 0.5, causal)
+        r = A.backward_head(q, k, v, o, do, m, l, 0.5, causal)
+        assert np.max(np.abs(r["dq"])) < 1e-13 and np.max(np.abs(r["dk"])) < 1e-13
+
+
+def test_zero_queries_give_uniform_softmax():
+    rng = np.random.default_rng(17)
+    lq, lk = 6, 5
+    q = np.zeros((lq, 4))
+    k, v = rng.standard_normal((lk, 4)), rng.standard_normal((lk, 4))
+    do = rng.standard_normal((lq, 4))
+    o, m, l = A.forward_head(q, k, v, 0.5, False)
+    r = A.backward_head(q, k, v, o, do, m, l, 0.5, False)
+    np.testing.assert_allclose(r["p"], 1.0 / lk, rtol=1e-15)
+    np.testing.assert_allclose(r["dv"], np.tile(do.sum(axis=0) / lk, (lk, 1)), rtol=1e-13)
+    np.testing.assert_allclose(o, np.tile(v.mean(axis=0), (lq, 1)), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- independent library
+
+@pytest.mark.parametrize("mask,lq,lk,d,padded", FD_CASES + [
+    (MASK_NONE, [64, 37], [64, 37], 32, 0),
+    (MASK_CAUSAL, [96], [96], 64, 0),
+    (MASK_PADDING_CAUSAL, [80, 50], [80, 50], 16, 80),
+])
+def test_torch_fp64_autograd(mask, lq, lk, d, padded):
+    p = make_problem(mask, lq, lk, heads=2, d=d, seed=99 + sum(lq), padded_len=padded, mult=2.0)
+    assert torch_error(p) < 1e-12
+
+
+# ---------------------------------------------------------------- sampled rows == full backward
+
+@pytest.mark.parametrize("mask", [MASK_NONE, MASK_CAUSAL, MASK_PADDING_CAUSAL])
+def test_backward_rows_matches_full(mask):
+    padded = 40 if A.is_padded(mask) else 0
+    p = make_problem(mask, [40, 23], [40, 23], heads=3, d=16, seed=5, padded_len=padded)
+    o, m, l, dq, dk, dv = exact_backward(p)
+    for b, (qs, lq) in enumerate(A.segments(p["cu_q"], mask, p["max_seqlen_q"])):
+        ks = A.segments(p["cu_kv"], mask, p["max_seqlen_kv"])[b][0]
+        rows = [0, 1, lq // 2, lq - 1]
+        sq, sk, sv = A.backward_rows(p["q"], p["k"], p["v"], o, p["do"], m, l, p["cu_q"], p["cu_kv"],
+                                     p["scale"], mask, b, 2, rows, rows, p["max_seqlen_q"], p["max_seqlen_kv"])
+        np.testing.assert_allclose(sq, dq[[qs + r for r in rows], 2], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(sk, dk[[ks + r for r in rows], 2], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(sv, dv[[ks + r for r in rows], 2], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- planted mistakes are caught
+
+def _mutant(monkeypatch, func_name, old, new):
+    """Replace ``func_name`` in the oracle module by a copy of its source with one edit."""
+    src = textwrap.dedent(inspect.getsource(getattr(A, func_name)))
+    assert old in src, f"mutation target not found in {func_name}: {old!r}"
+    ns = {}
+    exec(compile(src.replace(old, new), f"<mutant {func_name}>", "exec"), A.__dict__, ns)
+    monkeypatch.setattr(A, func_name, ns[func_name])
+
+
+MUTANTS = [
+    ("backward_head", "ds = p * (dp - dvec[:, None])", "ds = p * dp", "D dropped"),
+    ("backward_head", "ds = p * (dp - dvec[:, None])", "ds = p * (dvec[:, None] - dp)", "sign of dS"),
+    ("backward_head", "dk = scale * (ds.T @ q)", "dk = (ds.T @ q)", "scale dropped from dK"),
+    ("backward_head", "dq = scale * (ds @ k)", "dq = (ds @ k)", "scale dropped from dQ"),
+    ("backward_head", "dv = p.T @ do", "dv = p @ do", "transposed P in dV"),
+    ("backward_head", "dq = scale * (ds @ k)", "dq = scale * (ds @ v)", "wrong operand in dQ"),
+    ("backward_head", "p = softmax_probs(scale * s, m, l, vis)", "p = softmax_probs(s, m, l, vis)",
+     "scale missing in the softmax"),
+    ("softmax_probs", "np.exp(z) / np.where(ok, l[:, None], 1.0)", "np.exp(z)", "division by l dropped"),
+    ("backward_head", "dvec = np.sum(o * do, axis=1)", "dvec = np.sum(o * do, axis=0)[:o.shape[0]]",
+     "wrong reduction axis for D"),
+]
+
+
+@pytest.mark.parametrize("func,old,new,what", MUTANTS, ids=[m[3] for m in MUTANTS])
+def test_planted_mistake_fails_finite_differences(monkeypatch, func, old, new, what):
+    p = make_problem(MASK_CAUSAL, [5, 4], [5, 4], heads=1, d=4, seed=21)
+    assert fd_error(p) < 2e-6
+    _mutant(monkeypatch, func, old, new)
+    try:
+        err = fd_error(p)
+    except ValueError:          # a shape error is also a caught mistake
+        err = float("inf")
+    assert err > 1e-3, what
+
+
+@pytest.mark.parametrize("old,new,what", [
+    ("return j <= i", "return j < i", "causal diagonal excluded"),
+    ("return j <= i", "return j >= i", "causal mask flipped"),
+])
+def test_planted_mask_mistake_fails_torch_check(monkeypatch, old, new, what):
+    p = make_problem(MASK_CAUSAL, [6, 5], [6, 5], heads=1, d=4, seed=22)
+    assert torch_error(p) < 1e-12
+    _mutant(monkeypatch, "visible", old, new)
+    assert torch_error(p) > 1e-3, what
+
+
+def test_planted_layout_mistake_fails_torch_check(monkeypatch):
+    # padded slots must start at b * max_seqlen, not at the cumulative offset
+    p = make_problem(MASK_PADDING, [5, 3], [5, 3], heads=1, d=4, seed=23, padded_len=6)
+    assert torch_error(p) < 1e-12
+    _mutant(monkeypatch, "segments", "start = b * max_seqlen if is_padded(mask) else cu[b]", "start = cu[b]")
+    assert torch_error(p) > 1e-3
