@@ -1,0 +1,247 @@
+// fa_bwd.hip -- C ABI of the single-pass attention backward (include/fa_bwd.h):
+// host-side validation, the handle's device workspace and the three launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <new>
+#include <vector>
+
+#include "fa_bwd.h"
+#include "fa_bwd_kernels.hpp"
+
+struct fa_bwd_handle {
+  fa_bwd_desc desc;
+  int device;
+  float* dq_acc;  // [H][total_q][head_dim]
+  float* lse2;    // [H][total_q]
+  float* dvec;    // [H][total_q]
+  bool profiling;
+  std::vector<hipEvent_t> events;  // 4 per recorded run
+  int64_t recorded;                // runs whose events are in `events`
+};
+
+namespace {
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+constexpr int64_t kMaxGrid = 0x7fffffff;
+constexpr int64_t kMaxProfiledRuns = 4096;
+
+void release_events(fa_bwd_handle* h) {
+  for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+  h->events.clear();
+  h->recorded = 0;
+}
+
+fa_bwd_status check_desc(const fa_bwd_desc* d) {
+  if (!d) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (d->batch < 1 || d->num_heads < 1 || d->max_seqlen_q < 1 || d->max_seqlen_kv < 1 || d->total_q < 1 ||
+      d->total_kv < 1)
+    return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (d->head_dim != 64 && d->head_dim != 128) return FA_BWD_ERR_UNSUPPORTED;
+  if (d->deterministic != 0) return FA_BWD_ERR_UNSUPPORTED;
+  // index arithmetic stays in int64; grids must fit the launch limits
+  const int64_t rows = (d->total_q > d->total_kv ? d->total_q : d->total_kv);
+  if (rows > (int64_t(1) << 40) / d->num_heads) return FA_BWD_ERR_INVALID_ARGUMENT;
+  const int64_t kv_tiles = (d->max_seqlen_kv + 127) / 128;
+  if (kv_tiles * d->num_heads * d->batch > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
+  const int64_t rows_per_block = 256 / (d->head_dim / 8);
+  if ((rows * d->num_heads + rows_per_block - 1) / rows_per_block > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
+  return FA_BWD_OK;
+}
+
+template <int D>
+fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* m, const float* l, const int32_t* cu_q, const int32_t* cu_kv, float scale,
+                     int32_t mask, void* dq, void* dk, void* dv, hipStream_t stream) {
+  const fa_bwd_desc& d = h->desc;
+  const int padded = (mask == FA_BWD_MASK_PADDING || mask == FA_BWD_MASK_PADDING_CAUSAL) ? 1 : 0;
+  const int causal = (mask == FA_BWD_MASK_CAUSAL || mask == FA_BWD_MASK_PADDING_CAUSAL) ? 1 : 0;
+  using fa::bf16;
+
+  fa::PreArgs pa;
+  pa.o = static_cast<const bf16*>(o);
+  pa.dout = static_cast<const bf16*>(dout);
+  pa.m = m;
+  pa.l = l;
+  pa.cu_q = cu_q;
+  pa.cu_kv = cu_kv;
+  pa.lse2 = h->lse2;
+  pa.dvec = h->dvec;
+  pa.dq_acc = h->dq_acc;
+  pa.dk = static_cast<bf16*>(dk);
+  pa.dv = static_cast<bf16*>(dv);
+  pa.total_q = d.total_q;
+  pa.total_kv = d.total_kv;
+  pa.H = d.num_heads;
+  pa.batch = d.batch;
+  pa.max_seqlen_kv = d.max_seqlen_kv;
+  pa.padded = padded;
+  const int64_t rows = (d.total_q > d.total_kv ? d.total_q : d.total_kv) * d.num_heads;
+  constexpr int RPB = 256 / (D / 8);
+  hipEvent_t* ev = nullptr;
+  if (h->profiling && h->recorded < kMaxProfiledRuns) {
+    const size_t base = (size_t)h->recorded * 4;
+    if (h->events.size() < base + 4) {
+      for (int i = 0; i < 4; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return FA_BWD_ERR_HIP;
+        h->events.push_back(e);
+      }
+    }
+    ev = &h->events[base];
+    ++h->recorded;
+  }
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return FA_BWD_ERR_HIP;
+  hipLaunchKernelGGL(fa::fa_bwd_pre<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, pa);
+  if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return FA_BWD_ERR_HIP;
+
+  fa::MainArgs ma;
+  ma.q = static_cast<const bf16*>(q);
+  ma.k = static_cast<const bf16*>(k);
+  ma.v = static_cast<const bf16*>(v);
+  ma.dout = static_cast<const bf16*>(dout);
+  ma.lse2 = h->lse2;
+  ma.dvec = h->dvec;
+  ma.cu_q = cu_q;
+  ma.cu_kv = cu_kv;
+  ma.dq_acc = h->dq_acc;
+  ma.dk = static_cast<bf16*>(dk);
+  ma.dv = static_cast<bf16*>(dv);
+  ma.total_q = d.total_q;
+  ma.total_kv = d.total_kv;
+  ma.H = d.num_heads;
+  ma.batch = d.batch;
+  ma.max_seqlen_q = d.max_seqlen_q;
+  ma.max_seqlen_kv = d.max_seqlen_kv;
+  ma.padded = padded;
+  ma.causal = causal;
+  ma.scale_log2 = scale * fa::kLog2e;
+  ma.scale = scale;
+  const int64_t kv_tiles = (d.max_seqlen_kv + fa::MainCfg<D>::BN - 1) / fa::MainCfg<D>::BN;
+  hipLaunchKernelGGL(fa::fa_bwd_main<D>, dim3((unsigned)(kv_tiles * d.num_heads * d.batch)), dim3(256), 0, stream,
+                     ma);
+  if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
+  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return FA_BWD_ERR_HIP;
+
+  const int64_t qrows = d.total_q * d.num_heads;
+  hipLaunchKernelGGL(fa::fa_bwd_dq_cast<D>, dim3((unsigned)((qrows + RPB - 1) / RPB)), dim3(256), 0, stream,
+                     (const float*)h->dq_acc, static_cast<bf16*>(dq), d.total_q, d.num_heads, scale);
+  if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
+  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return FA_BWD_ERR_HIP;
+  return FA_BWD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
+  if (!out) return FA_BWD_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  const fa_bwd_status st = check_desc(desc);
+  if (st != FA_BWD_OK) return st;
+  fa_bwd_handle* h = new (std::nothrow) fa_bwd_handle();
+  if (!h) return FA_BWD_ERR_OUT_OF_MEMORY;
+  h->desc = *desc;
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return FA_BWD_ERR_HIP;
+  }
+  const size_t stats = (size_t)desc->total_q * desc->num_heads;
+  const size_t acc = stats * desc->head_dim;
+  if (hipMalloc(&h->dq_acc, acc * sizeof(float)) != hipSuccess ||
+      hipMalloc(&h->lse2, stats * sizeof(float)) != hipSuccess ||
+      hipMalloc(&h->dvec, stats * sizeof(float)) != hipSuccess) {
+    (void)hipGetLastError();
+    if (h->dq_acc) (void)hipFree(h->dq_acc);
+    if (h->lse2) (void)hipFree(h->lse2);
+    if (h->dvec) (void)hipFree(h->dvec);
+    delete h;
+    return FA_BWD_ERR_OUT_OF_MEMORY;
+  }
+  *out = h;
+  return FA_BWD_OK;
+}
+
+fa_bwd_status fa_bwd_run(fa_bwd_handle* h, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* m, const float* l, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* dq, void* dk, void* dv,
+                         void* stream) {
+  if (!h || !q || !k || !v || !o || !dout || !m || !l || !cu_seqlens_q || !cu_seqlens_kv || !dq || !dk || !dv)
+    return FA_BWD_ERR_INVALID_ARGUMENT;
+  const void* vec[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : vec)
+    if (!aligned(p, 16)) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (!aligned(m, 4) || !aligned(l, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_kv, 4))
+    return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (mask < FA_BWD_MASK_NONE || mask > FA_BWD_MASK_PADDING_CAUSAL) return FA_BWD_ERR_INVALID_ARGUMENT;
+  const fa_bwd_desc& d = h->desc;
+  if (mask == FA_BWD_MASK_PADDING || mask == FA_BWD_MASK_PADDING_CAUSAL) {
+    if ((int64_t)d.batch * d.max_seqlen_q > d.total_q || (int64_t)d.batch * d.max_seqlen_kv > d.total_kv)
+      return FA_BWD_ERR_INVALID_ARGUMENT;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d.head_dim == 128)
+    return launch<128>(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, s);
+  return launch<64>(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, s);
+}
+
+fa_bwd_status fa_bwd_destroy(fa_bwd_handle* h) {
+  if (!h) return FA_BWD_OK;
+  int prev = 0;
+  fa_bwd_status st = FA_BWD_OK;
+  if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(h->device) != hipSuccess) st = FA_BWD_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) st = FA_BWD_ERR_HIP;
+  if (hipFree(h->dq_acc) != hipSuccess) st = FA_BWD_ERR_HIP;
+  if (hipFree(h->lse2) != hipSuccess) st = FA_BWD_ERR_HIP;
+  if (hipFree(h->dvec) != hipSuccess) st = FA_BWD_ERR_HIP;
+  release_events(h);
+  (void)hipSetDevice(prev);
+  delete h;
+  return st;
+}
+
+const char* fa_bwd_status_string(fa_bwd_status s) {
+  switch (s) {
+    case FA_BWD_OK: return "ok";
+    case FA_BWD_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FA_BWD_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_BWD_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case FA_BWD_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const fa_bwd_desc* fa_bwd_get_desc(const fa_bwd_handle* h) { return h ? &h->desc : nullptr; }
+
+fa_bwd_status fa_bwd_profile_enable(fa_bwd_handle* h, int32_t enable) {
+  if (!h) return FA_BWD_ERR_INVALID_ARGUMENT;
+  fa_bwd_status st = FA_BWD_OK;
+  if (!h->events.empty() && hipDeviceSynchronize() != hipSuccess) st = FA_BWD_ERR_HIP;
+  release_events(h);
+  h->profiling = enable != 0;
+  return st;
+}
+
+fa_bwd_status fa_bwd_profile_collect(fa_bwd_handle* h, float* ms, int32_t max_runs, int32_t* n_runs) {
+  if (!h || !n_runs || max_runs < 0 || (max_runs > 0 && !ms)) return FA_BWD_ERR_INVALID_ARGUMENT;
+  *n_runs = 0;
+  const int64_t n = h->recorded < max_runs ? h->recorded : max_runs;
+  for (int64_t r = 0; r < n; ++r) {
+    hipEvent_t* e = &h->events[(size_t)r * 4];
+    if (hipEventSynchronize(e[3]) != hipSuccess) return FA_BWD_ERR_HIP;
+    for (int s = 0; s < 3; ++s)
+      if (hipEventElapsedTime(&ms[r * 3 + s], e[s], e[s + 1]) != hipSuccess) return FA_BWD_ERR_HIP;
+  }
+  *n_runs = (int32_t)n;
+  // keep the events for reuse, forget the runs
+  h->recorded = 0;
+  return FA_BWD_OK;
+}
+
+}  // extern "C"

@@ -31,6 +31,11 @@ MASK_CAUSAL = 2
 MASK_PADDING_CAUSAL = 3
 
 
+def is_padded_mask(mask: int) -> bool:
+    """Padded layouts: each sequence sits in a fixed-length slot (see the C header)."""
+    return mask in (MASK_PADDING, MASK_PADDING_CAUSAL)
+
+
 @dataclass
 class Case:
     name: str

@@ -1,0 +1,133 @@
+/*
+ * fa_bwd.h -- single-pass attention backward on AMD MI355X (gfx950), C ABI.
+ *
+ * Computes the gradients dQ, dK, dV of softmax attention from the forward's
+ * inputs Q, K, V, its output O, the incoming gradient dO and the forward's
+ * softmax row statistics m (row max) and l (row sum). The per-tile arithmetic
+ * is the eight steps of the PyPTO-Gym SK-16 article ("single-pass attention
+ * backward (FA Grad)"), section 3.1:
+ *     S = Q K^T, P = exp(S*scale - m) / l, dP = dO V^T, D = rowsum(O*dO),
+ *     dS = P*(dP - D), dV = P^T dO, dK = scale * dS^T Q, dQ = scale * dS K,
+ * with the inputs in bf16, all softmax arithmetic and accumulation in fp32 and
+ * the outputs in bf16 (the article's dtype table, section 4.2).
+ *
+ * Layout (the article's [total, heads, head_dim] tensors, section 三, and the
+ * BTNH layout with the batch and sequence axes flattened, jax cuDNN wrapper,
+ * AttentionLayout): every bf16 tensor is a contiguous row-major
+ * [T][H][head_dim] array (token-major, then head, then feature); m and l are
+ * contiguous fp32 [T_q][H]. All tensor pointers are DEVICE pointers, owned by
+ * the caller, 16-byte aligned.
+ *
+ * Sequences (the article's actual_q / actual_kv offsets, section 三; jax
+ * cuDNN wrapper, dot_product_attention and _fix_seqlen_offsets):
+ *   cu_seqlens_q/kv are DEVICE int32 arrays of batch+1 non-decreasing entries
+ *   with cu[0] = 0. L_b = cu[b+1] - cu[b] is the valid length of sequence b.
+ *   - FA_BWD_MASK_NONE, FA_BWD_MASK_CAUSAL (packed varlen): sequence b is rows
+ *     [cu[b], cu[b+1]); no attention across sequences; cu[batch] <= total.
+ *   - FA_BWD_MASK_PADDING, FA_BWD_MASK_PADDING_CAUSAL (padded): sequence b
+ *     occupies the slot of rows [b*max_seqlen, (b+1)*max_seqlen) and its first
+ *     L_b <= max_seqlen rows are valid; the rest of the slot is padding.
+ *   Causal masks are top-left aligned in sequence-local coordinates: key j is
+ *   visible from query i iff j <= i.
+ *   Rows outside every sequence (padding, or rows at or after cu[batch]) are
+ *   never read, and their dQ/dK/dV are written as 0. The contents of
+ *   cu_seqlens are preconditions: the library does not read them on the host;
+ *   device code never touches a row outside [0, total) whatever they hold.
+ *
+ * Outputs dq/dk/dv are fully overwritten (no pre-zeroing needed).
+ * Masks use the codes of jax's cuDNN MaskType (NO_MASK, PADDING, CAUSAL,
+ * PADDING_CAUSAL); ALIBI is not supported.
+ */
+#ifndef FA_BWD_H
+#define FA_BWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fa_bwd_handle fa_bwd_handle; /* opaque: sizes + device workspace */
+
+typedef enum {
+  FA_BWD_MASK_NONE = 0,
+  FA_BWD_MASK_PADDING = 1,
+  FA_BWD_MASK_CAUSAL = 2,
+  FA_BWD_MASK_PADDING_CAUSAL = 3
+} fa_bwd_mask;
+
+typedef enum {
+  FA_BWD_OK = 0,
+  FA_BWD_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad mask code, bad scale, misalignment */
+  FA_BWD_ERR_UNSUPPORTED = 2,      /* head_dim other than 64 or 128, deterministic mode */
+  FA_BWD_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed in fa_bwd_create */
+  FA_BWD_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} fa_bwd_status;
+
+typedef struct {
+  int32_t batch;         /* number of sequences (entries of cu_seqlens minus one), >= 1 */
+  int32_t num_heads;     /* heads of Q, K and V (no grouped heads), >= 1 */
+  int32_t head_dim;      /* 64 or 128 */
+  int32_t max_seqlen_q;  /* >= every L_b of the queries; the slot length in padded modes; >= 1 */
+  int32_t max_seqlen_kv; /* same for keys/values */
+  int64_t total_q;       /* rows of q, o, do, dq, m, l; >= 1 */
+  int64_t total_kv;      /* rows of k, v, dk, dv; >= 1 */
+  int32_t deterministic; /* must be 0: dQ is accumulated with fp32 atomics (order not fixed) */
+} fa_bwd_desc;
+
+/* Validates desc and allocates the device workspace of the handle on the
+ * current HIP device: an fp32 dQ accumulator of total_q*H*head_dim floats and
+ * two fp32 [H][total_q] row-statistic arrays. On success *out holds a new
+ * handle; on failure *out is set to NULL. Host-side checks run before any HIP
+ * call. */
+fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out);
+
+/* Enqueues the backward on `stream` (a hipStream_t; NULL = the default
+ * stream) and returns without waiting. The caller synchronises its stream
+ * before reading dq/dk/dv.
+ *   q, o, dout: bf16 [total_q][H][head_dim]        (read only)
+ *   k, v:       bf16 [total_kv][H][head_dim]       (read only)
+ *   m, l:       fp32 [total_q][H], row max of the scaled visible logits and
+ *               the row sum of exp(scaled logit - m) over visible keys, as the
+ *               forward produced them (not recomputed here; l > 0 on valid rows)
+ *   cu_seqlens_q, cu_seqlens_kv: int32 [batch+1] device arrays (see above)
+ *   scale:      the softmax scale applied to Q K^T (finite, > 0), e.g. 1/sqrt(head_dim)
+ *   mask:       an fa_bwd_mask code
+ *   dq:         bf16 [total_q][H][head_dim]  (written)
+ *   dk, dv:     bf16 [total_kv][H][head_dim] (written)
+ * Every argument is checked on the host first; an invalid one returns
+ * FA_BWD_ERR_INVALID_ARGUMENT with nothing enqueued. FA_BWD_ERR_HIP reports a
+ * failed launch. The handle's workspace is reused by every call, so one
+ * handle must not be used by two calls that can overlap in time (two streams). */
+fa_bwd_status fa_bwd_run(fa_bwd_handle* h, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* m, const float* l, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* dq, void* dk, void* dv,
+                         void* stream);
+
+/* Frees the workspace and the handle (NULL is accepted). Waits for the
+ * device to finish work that may still use the workspace. */
+fa_bwd_status fa_bwd_destroy(fa_bwd_handle* h);
+
+/* Static English text for a status code. */
+const char* fa_bwd_status_string(fa_bwd_status s);
+
+/* Descriptor the handle was created with (for bindings); NULL on NULL. */
+const fa_bwd_desc* fa_bwd_get_desc(const fa_bwd_handle* h);
+
+/* Per-kernel timing for benchmarks. While enabled, every fa_bwd_run also
+ * records four HIP events on its stream, around its three kernels
+ * (row preprocessing, main kernel, dQ cast); recording does not wait.
+ * Enabling or disabling forgets the runs recorded so far. At most 4096 runs
+ * are kept; later runs are not recorded. */
+fa_bwd_status fa_bwd_profile_enable(fa_bwd_handle* h, int32_t enable);
+
+/* Waits for the recorded runs, writes min(max_runs, recorded) rows of three
+ * floats (milliseconds of the preprocessing, main and cast kernels) to the
+ * HOST array ms, stores the row count in *n_runs, and forgets the runs. */
+fa_bwd_status fa_bwd_profile_collect(fa_bwd_handle* h, float* ms, int32_t max_runs, int32_t* n_runs);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_BWD_H */

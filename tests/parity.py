@@ -1,0 +1,72 @@
+"""Shared helpers of the GPU parity tests: feed the HIP library and the fp64
+oracle the same seeded inputs and compare per gradient tensor.
+
+Tolerance (per tensor, over the rows compared): relative L2 error
+||gpu - ref||_2 / ||ref||_2 <= 1e-2 and max |gpu - ref| <= 3e-2 * max |ref|;
+rows outside every sequence must be exactly zero.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from attention_backward_fa_amd import binding
+
+REL_L2_TOL = 1e-2
+MAX_ABS_TOL = 3e-2
+
+
+def oracle_stats(inp):
+    """O (bf16), m, l (fp32) from the oracle's fp64 forward on the bf16 inputs."""
+    o, m, l = oracle.forward(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_kv"], inp["scale"], inp["mask"],
+                             inp["max_seqlen_q"], inp["max_seqlen_kv"])
+    return (torch.from_numpy(o).to(torch.bfloat16), torch.from_numpy(m).to(torch.float32),
+            torch.from_numpy(l).to(torch.float32))
+
+
+def run_gpu(inp, o, m, l, device="cuda"):
+    """Run the HIP backward once; returns CPU fp32 dq, dk, dv."""
+    dev = torch.device(device)
+    t = {k: inp[k].to(dev) for k in ("q", "k", "v", "do", "cu_q", "cu_kv")}
+    dq, dk, dv = binding.attention_backward(t["q"], t["k"], t["v"], o.to(dev), t["do"], m.to(dev), l.to(dev),
+                                            t["cu_q"], t["cu_kv"], inp["scale"], inp["mask"],
+                                            inp["max_seqlen_q"], inp["max_seqlen_kv"])
+    torch.cuda.synchronize()
+    return dq.float().cpu(), dk.float().cpu(), dv.float().cpu()
+
+
+def oracle_backward(inp, o, m, l):
+    return oracle.backward(inp["q"], inp["k"], inp["v"], o, inp["do"], m, l, inp["cu_q"], inp["cu_kv"],
+                           inp["scale"], inp["mask"], inp["max_seqlen_q"], inp["max_seqlen_kv"])
+
+
+def metrics(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    ref_l2 = np.linalg.norm(ref)
+    ref_max = np.max(np.abs(ref)) if ref.size else 0.0
+    err = gpu - ref
+    rel_l2 = np.linalg.norm(err) / ref_l2 if ref_l2 > 0 else np.linalg.norm(err)
+    max_ratio = np.max(np.abs(err)) / ref_max if ref_max > 0 else (np.max(np.abs(err)) if err.size else 0.0)
+    return float(rel_l2), float(max_ratio)
+
+
+def assert_close(name, gpu, ref):
+    assert np.all(np.isfinite(np.asarray(gpu))), f"{name}: non-finite values"
+    rel_l2, max_ratio = metrics(gpu, ref)
+    assert rel_l2 <= REL_L2_TOL and max_ratio <= MAX_ABS_TOL, \
+        f"{name}: rel_l2={rel_l2:.3e} (tol {REL_L2_TOL}), max_abs/max_ref={max_ratio:.3e} (tol {MAX_ABS_TOL})"
+    return rel_l2, max_ratio
+
+
+def check_full(inp, gpu, ref):
+    """Compare every valid row; rows outside every sequence must be exactly 0."""
+    vq = oracle.valid_rows(inp["cu_q"], inp["mask"], inp["max_seqlen_q"], inp["q"].shape[0])
+    vk = oracle.valid_rows(inp["cu_kv"], inp["mask"], inp["max_seqlen_kv"], inp["k"].shape[0])
+    out = {}
+    for name, g, r, ok in (("dq", gpu[0], ref[0], vq), ("dk", gpu[1], ref[1], vk), ("dv", gpu[2], ref[2], vk)):
+        g = g.numpy() if hasattr(g, "numpy") else g
+        assert np.all(g[~ok] == 0), f"{name}: rows outside every sequence are not zero"
+        out[name] = assert_close(name, g[ok], r[ok])
+    return out

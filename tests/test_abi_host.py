@@ -1,0 +1,109 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function ``include/fa_bwd.h`` declares, and rejects bad arguments before
+any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from attention_backward_fa_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_bwd.h")
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(fa_bwd_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declarations_match_binding():
+    assert declared_functions() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings():
+    assert B.fa_bwd_status_string(0) == "ok"
+    assert B.fa_bwd_status_string(1) == "invalid argument"
+    assert B.fa_bwd_status_string(2) == "unsupported configuration"
+    assert B.fa_bwd_status_string(3) == "out of device memory"
+    assert B.fa_bwd_status_string(4) == "HIP runtime error"
+    assert B.fa_bwd_status_string(99) == "unknown status"
+
+
+def _create(**kw):
+    d = dict(batch=1, num_heads=1, head_dim=128, max_seqlen_q=128, max_seqlen_kv=128, total_q=128, total_kv=128,
+             deterministic=0)
+    d.update(kw)
+    lib = B.load_library()
+    h = ctypes.c_void_p(0x1234)
+    st = lib.fa_bwd_create(ctypes.byref(B.FaBwdDesc(**d)), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(num_heads=0), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(max_seqlen_q=0), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(max_seqlen_kv=-5), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(total_q=0), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(total_kv=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(head_dim=96), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(head_dim=256), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(head_dim=0), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(deterministic=1), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(total_q=1 << 40, num_heads=8), B.FA_BWD_ERR_INVALID_ARGUMENT),          # index range
+    (dict(max_seqlen_kv=1 << 30, num_heads=1 << 10, batch=1 << 10), B.FA_BWD_ERR_INVALID_ARGUMENT),  # grid size
+])
+def test_create_rejects_bad_descriptors_before_any_hip_call(kw, status):
+    st, h = _create(**kw)
+    assert st == status
+    assert h.value is None   # *out is cleared on failure
+
+
+def test_create_null_arguments():
+    lib = B.load_library()
+    h = ctypes.c_void_p()
+    assert lib.fa_bwd_create(None, ctypes.byref(h)) == B.FA_BWD_ERR_INVALID_ARGUMENT
+    assert lib.fa_bwd_create(ctypes.byref(B.FaBwdDesc(1, 1, 128, 1, 1, 1, 1, 0)), None) == B.FA_BWD_ERR_INVALID_ARGUMENT
+
+
+def test_run_and_profile_reject_null_handle():
+    lib = B.load_library()
+    p = ctypes.c_void_p(256)
+    assert lib.fa_bwd_run(None, *([p] * 9), ctypes.c_float(0.1), 0, p, p, p, None) == B.FA_BWD_ERR_INVALID_ARGUMENT
+    n = ctypes.c_int32()
+    assert lib.fa_bwd_profile_collect(None, None, 0, ctypes.byref(n)) == B.FA_BWD_ERR_INVALID_ARGUMENT
+    assert lib.fa_bwd_profile_enable(None, 1) == B.FA_BWD_ERR_INVALID_ARGUMENT
+    assert not lib.fa_bwd_get_desc(None)
+
+
+def test_destroy_null_is_ok():
+    assert B.load_library().fa_bwd_destroy(None) == B.FA_BWD_OK
+
+
+def test_binding_maps_status_to_exceptions():
+    with pytest.raises(ValueError):
+        B.fa_bwd_create(0, 1, 128, 1, 1, 1, 1)
+    with pytest.raises(NotImplementedError):
+        B.fa_bwd_create(1, 1, 80, 1, 1, 1, 1)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = B._lib
+    try:
+        B._lib = None
+        with pytest.raises(RuntimeError, match="missing"):
+            B.load_library(str(tmp_path / "nope.so"))
+    finally:
+        B._lib = saved

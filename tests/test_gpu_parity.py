@@ -1,0 +1,69 @@
+"""GPU parity: the HIP backward against the fp64 oracle on the same seeded
+inputs, every valid row compared, at sizes the oracle finishes in seconds.
+
+Cases: the tiny workload (1 head, 128 tokens, d 64), the d in {64, 128} rows
+of the PyPTO-Gym SK-16 test matrix (§七) as packed sequences, and ragged
+cases for every mask type (lengths that are not multiples of the 64-row q
+step or the 128-row kv tile, a single-token sequence, an empty sequence,
+Lq != Lk, padded slots with garbage in the padding rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+from attention_backward_fa_amd import inputs as I
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+NONE, PAD, CAUSAL, PADC = I.MASK_NONE, I.MASK_PADDING, I.MASK_CAUSAL, I.MASK_PADDING_CAUSAL
+
+CASES = [
+    I.CASES["tiny"],
+    I.CASES["sk16_t01"],
+    I.CASES["sk16_t05"],
+    I.CASES["sk16_t06"],
+    I.custom_case("ragged_none_d128", 3, 128, NONE, 201, [1, 77, 200, 333]),
+    I.custom_case("ragged_causal_d128", 2, 128, CAUSAL, 202, [129, 300, 64, 1]),
+    I.custom_case("ragged_causal_d64", 2, 64, CAUSAL, 203, [255, 257]),
+    I.custom_case("kv_longer_none", 2, 128, NONE, 204, [100, 250], [180, 64]),
+    I.custom_case("kv_longer_causal", 2, 128, CAUSAL, 205, [100, 250], [180, 64]),
+    I.custom_case("empty_sequence", 2, 128, NONE, 206, [90, 0, 150]),
+    I.custom_case("padded_d128", 2, 128, PAD, 207, [300, 131], padded_len=300),
+    I.custom_case("padded_causal_d128", 2, 128, PADC, 208, [300, 131], padded_len=320, qk_mult=2.0),
+    I.custom_case("padded_causal_d64", 2, 64, PADC, 209, [97, 200], [150, 64], padded_len=256),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c.name for c in CASES])
+def test_parity_full(case):
+    inp = I.make(case)
+    print(f"[parity] {case.name}: T_q={inp['q'].shape[0]} H={case.heads} d={case.head_dim} mask={case.mask}",
+          flush=True)
+    o, m, l = P.oracle_stats(inp)
+    if I.is_padded_mask(case.mask):
+        # the backward must not read padding rows: fill them with NaN
+        vq = torch.from_numpy(P.oracle.valid_rows(inp["cu_q"], case.mask, inp["max_seqlen_q"], inp["q"].shape[0]))
+        o[~vq] = float("nan")
+        m[~vq] = float("nan")
+        l[~vq] = float("nan")
+        inp["do"][~vq] = float("nan")
+        inp["q"][~vq] = float("nan")
+        vk = torch.from_numpy(P.oracle.valid_rows(inp["cu_kv"], case.mask, inp["max_seqlen_kv"], inp["k"].shape[0]))
+        inp["k"][~vk] = float("nan")
+        inp["v"][~vk] = float("nan")
+    gpu = P.run_gpu(inp, o, m, l)
+    ref = P.oracle_backward(inp, o, m, l)
+    res = P.check_full(inp, gpu, ref)
+    print(f"[parity] {case.name}: " + " ".join(f"{k}: rel_l2={v[0]:.2e} max={v[1]:.2e}" for k, v in res.items()),
+          flush=True)
+
+
+def test_repeat_runs_agree():
+    """Atomic summation order may change between runs; results stay within tolerance of each other."""
+    inp = I.make(I.CASES["sk16_t01"])
+    o, m, l = P.oracle_stats(inp)
+    a = P.run_gpu(inp, o, m, l)
+    b = P.run_gpu(inp, o, m, l)
+    for x, y in zip(a, b):
+        P.assert_close("repeat", x.numpy(), y.numpy().astype(np.float64))
