@@ -122,8 +122,11 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.scale_log2 = scale * fa::kLog2e;
   ma.scale = scale;
   const int64_t kv_tiles = (d.max_seqlen_kv + fa::MainCfg<D>::BN - 1) / fa::MainCfg<D>::BN;
-  hipLaunchKernelGGL(fa::fa_bwd_main<D>, dim3((unsigned)(kv_tiles * d.num_heads * d.batch)), dim3(256), 0, stream,
-                     ma);
+  const dim3 grid((unsigned)(kv_tiles * d.num_heads * d.batch));
+  if (causal)
+    fa::fa_bwd_main<D, true><<<grid, dim3(256), 0, stream>>>(ma);
+  else
+    fa::fa_bwd_main<D, false><<<grid, dim3(256), 0, stream>>>(ma);
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return FA_BWD_ERR_HIP;
 
@@ -245,3 +248,4 @@ fa_bwd_status fa_bwd_profile_collect(fa_bwd_handle* h, float* ms, int32_t max_ru
 }
 
 }  // extern "C"
+

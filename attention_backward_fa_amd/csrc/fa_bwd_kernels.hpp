@@ -13,6 +13,8 @@
 //                  go to the fp32 accumulator with global atomics. MFMA bound.
 //   fa_bwd_dq_cast dQ = bf16(scale * accumulator). HBM bound.
 #pragma once
+#include <type_traits>
+
 #include "cdna4.hpp"
 
 namespace fa {
@@ -111,32 +113,71 @@ struct MainArgs {
 
 template <int D>
 struct MainCfg {
-  static constexpr int BN = 128;       // kv rows per workgroup (32 per wave)
-  static constexpr int BM = 64;        // q rows per step
-  static constexpr int NW = 4;         // waves
-  static constexpr int KSD = D / 16;   // MFMA k-steps over the head dim
-  static constexpr int NTD = D / 32;   // 32-wide output tiles over the head dim
-  static constexpr int QS = D + 8;     // LDS row stride (elements) of Q/dO tiles and of the K tile
-  static constexpr int SS = BM + 8;    // LDS row stride of dS^T
-  static constexpr int TPW = D / 64;   // dQ output tiles per wave
-  static constexpr int NCH = BM * D / 8 / 256;  // 16-byte chunks per thread per q tile
-  static constexpr int TILE = BM * QS;          // elements of one Q or dO buffer
-  static constexpr int LDS_BYTES = 4 * TILE * 2 + BN * SS * 2 + 4 * BM * 4;
-  static_assert(BN * QS <= 2 * TILE, "K tile must fit in the two Q buffers");
+  static constexpr int BN = 128;                 // kv rows per workgroup (32 per wave)
+  static constexpr int BM = 64;                  // q rows per step
+  static constexpr int NW = 4;                   // waves
+  static constexpr int KSD = D / 16;             // MFMA k-steps over the head dim
+  static constexpr int NTD = D / 32;             // 32-wide output tiles over the head dim
+  static constexpr int TPW = D / 64;             // dQ output tiles per wave
+  static constexpr int QS = D + 8;               // row stride (elements) of the Q, dO and K tiles
+  static constexpr int SS = BM + 8;              // row stride (elements) of dS^T
+  static constexpr int CPR = QS / 8;             // 16-byte chunks per padded row
+  static constexpr int TILE = BM * QS;           // elements of one Q or dO buffer
+  static constexpr int TILE_BYTES = TILE * 2;
+  static constexpr int NDMA = TILE_BYTES / 1024; // 1 KB LDS-DMA transfers per tile
+  static constexpr int OFF_K = 0;                          // K tile [BN][QS]
+  static constexpr int OFF_Q = OFF_K + BN * QS * 2;        // Q [2][BM][QS]
+  static constexpr int OFF_DO = OFF_Q + 2 * TILE_BYTES;    // dO [2][BM][QS]
+  static constexpr int OFF_DS = OFF_DO + 2 * TILE_BYTES;   // dS^T [BN][SS]
+  static constexpr int OFF_ST = OFF_DS + BN * SS * 2;      // [2 buffers][lse2, D][BM] fp32
+  static constexpr int LDS_BYTES = OFF_ST + 4 * BM * 4;
+  static_assert(TILE_BYTES % 1024 == 0, "a tile is a whole number of 1 KB transfers");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int D>
+// Row of a 32-row M-tile (Q, dO) that MFMA row m reads, and kv row of the 128-row tile that
+// k-index k of the dQ GEMM reads. With rows padded by 16 bytes, this interleave makes the
+// 16-byte operand reads (16 consecutive m) and the 4-row transpose reads (m = 4u..4u+3)
+// touch distinct LDS banks.
+__device__ __forceinline__ constexpr int tile_row(int m) { return ((m >> 2) & 3) + 4 * (m & 3) + 16 * (m >> 4); }
+
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Buffer resource over [base, base + bytes): loads past the end return 0 and atomics past
+// the end are dropped (raw buffer, stride 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// Rows [start, start + len) of a sequence, clamped to the rows that exist, so that
+// every later row check is a single comparison against the length.
+__device__ __forceinline__ int clamp_len(int64_t start, int len, int64_t total) {
+  if (start < 0 || start >= total || len <= 0) return 0;
+  return (int)((int64_t)len < total - start ? (int64_t)len : total - start);
+}
+
+__device__ __forceinline__ int imin(int x, int y) { return x < y ? x : y; }
+
+template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_main(MainArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using C = MainCfg<D>;
   constexpr int BN = C::BN, BM = C::BM, QS = C::QS, SS = C::SS;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
-  bf16* s_q = (bf16*)smem;                    // [2][BM][QS]
-  bf16* s_do = s_q + 2 * C::TILE;             // [2][BM][QS]
-  bf16* s_dst = s_do + 2 * C::TILE;           // [BN][SS]: dS transposed (kv-major)
-  float* s_lse = (float*)(s_dst + BN * SS);   // [2][BM]
-  float* s_dd = s_lse + 2 * BM;               // [2][BM]
-  bf16* s_k = s_q;                            // setup only: K tile [BN][QS]
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  bf16* s_k = (bf16*)(smem + C::OFF_K);
+  bf16* s_q = (bf16*)(smem + C::OFF_Q);
+  bf16* s_do = (bf16*)(smem + C::OFF_DO);
+  bf16* s_dst = (bf16*)(smem + C::OFF_DS);
+  float* s_st = (float*)(smem + C::OFF_ST);
 
   const int HB = a.H * a.batch;
   const int tile = blockIdx.x / HB;  // heavy (low) kv tiles of every head dispatch first
@@ -146,50 +187,43 @@ void fa_bwd_main(MainArgs a) {
   int Lq, Lk;
   seq_of(a.cu_q, b, a.padded, a.max_seqlen_q, q_start, Lq);
   seq_of(a.cu_kv, b, a.padded, a.max_seqlen_kv, kv_start, Lk);
+  Lq = clamp_len(q_start, Lq, a.total_q);
+  Lk = clamp_len(kv_start, Lk, a.total_kv);
   const int kv0 = tile * BN;
   if (kv0 >= Lk) return;
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
   const int64_t rs = (int64_t)a.H * D;  // elements between consecutive tokens
-  const bf16* kb = a.k + (int64_t)h * D;
-  const bf16* vb = a.v + (int64_t)h * D;
-  const bf16* qb = a.q + (int64_t)h * D;
-  const bf16* db = a.dout + (int64_t)h * D;
+  const int rsb = (int)(rs * 2);        // bytes between consecutive tokens
+  const bf16* kb = a.k + (kv_start + kv0) * rs + (int64_t)h * D;
+  const bf16* vb = a.v + (kv_start + kv0) * rs + (int64_t)h * D;
+  const bf16* qb = a.q + q_start * rs + (int64_t)h * D;
+  const bf16* db = a.dout + q_start * rs + (int64_t)h * D;
+  const float* lse_b = a.lse2 + (int64_t)h * a.total_q + q_start;
+  const float* dd_b = a.dvec + (int64_t)h * a.total_q + q_start;
+  float* dq_b = a.dq_acc + ((int64_t)h * a.total_q + q_start) * D;
 
-  // ---- K, V as B operands of S = Q K^T and dP = dO V^T: row kv0+32w+c, features 16ks+8hh..+7
-  bf16x8 kf[C::KSD], vf[C::KSD];
-  {
-    const int r = kv0 + 32 * w + c;
-    const int64_t gr = kv_start + r;
-    const bool ok = r < Lk && gr >= 0 && gr < a.total_kv;
-    const bf16x8 z = {};
-#pragma unroll
-    for (int ks = 0; ks < C::KSD; ++ks) {
-      kf[ks] = ok ? *(const bf16x8*)(kb + gr * rs + 16 * ks + 8 * hh) : z;
-      vf[ks] = ok ? *(const bf16x8*)(vb + gr * rs + 16 * ks + 8 * hh) : z;
-    }
-  }
-  // ---- K tile through LDS, then K^T fragments (B operand of dQ = dS K) for this wave's feature slice
+  // ---- K tile -> LDS (kept for the dQ GEMM); K, V B-operand fragments of S and dP -> registers
+  const int kv_rows = imin(Lk - kv0, BN);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (int64_t)kv_rows * rsb);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (int64_t)kv_rows * rsb);
   for (int ch = tid; ch < BN * D / 8; ch += 256) {
     const int r = ch / (D / 8), col = (ch % (D / 8)) * 8;
-    const int64_t gr = kv_start + kv0 + r;
-    const bool ok = kv0 + r < Lk && gr >= 0 && gr < a.total_kv;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    *(u32x4*)(s_k + r * QS + col) = ok ? *(const u32x4*)(kb + gr * rs + col) : z;
+    *(u32x4*)(s_k + r * QS + col) = buf_load16(rk, r * rsb + col * 2);
   }
-  __syncthreads();
-  const int ntq = (w * C::TPW) >> 1;  // this wave's 32-wide feature slice of dQ
-  bf16x8 ktf[BN / 16];
-  {
-    const int col = 32 * ntq + 16 * (g & 1) + 4 * (gi & 3);
+  bf16x8 kf[C::KSD], vf[C::KSD];
 #pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks) {
-      const int r0 = 16 * ks + 8 * hh + (gi >> 2);
-      ktf[ks] = concat(lds_read_tr4(s_k + r0 * QS + col), lds_read_tr4(s_k + (r0 + 4) * QS + col));
-    }
+  for (int ks = 0; ks < C::KSD; ++ks) {
+    const int off = (32 * w + c) * rsb + (16 * ks + 8 * hh) * 2;
+    kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+    vf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
   }
-  __syncthreads();
+  {  // zero both Q and dO buffers once: rows past the sequence then hold zeros or earlier valid rows
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int o = tid * 16; o < 4 * C::TILE_BYTES; o += 256 * 16) *(u32x4*)(smem + C::OFF_Q + o) = z;
+  }
+  __syncthreads();  // zero fill and K tile written before any LDS-DMA lands
 
   f32x16 accK[C::NTD], accV[C::NTD];
 #pragma unroll
@@ -199,57 +233,59 @@ void fa_bwd_main(MainArgs a) {
   }
 
   const int n_qt = (Lq + BM - 1) / BM;
-  int qt = a.causal ? kv0 / BM : 0;
-
-  // global -> registers for q tile `t`
-  u32x4 pq[C::NCH], pd[C::NCH];
-  float pst = 0.f;
-  auto fetch = [&](int t) {
-    const int i0 = t * BM;
-#pragma unroll
-    for (int u = 0; u < C::NCH; ++u) {
-      const int ch = tid + 256 * u;
-      const int r = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      const int64_t gr = q_start + i0 + r;
-      const bool ok = i0 + r < Lq && gr >= 0 && gr < a.total_q;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      pq[u] = ok ? *(const u32x4*)(qb + gr * rs + col) : z;
-      pd[u] = ok ? *(const u32x4*)(db + gr * rs + col) : z;
-    }
-    if (tid < 2 * BM) {
-      const int r = tid & (BM - 1);
-      const int64_t gr = q_start + i0 + r;
-      const bool ok = i0 + r < Lq && gr >= 0 && gr < a.total_q;
-      const float* src = tid < BM ? a.lse2 : a.dvec;
-      pst = ok ? src[(int64_t)h * a.total_q + gr] : 0.f;
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::NCH; ++u) {
-      const int ch = tid + 256 * u;
-      const int r = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *(u32x4*)(s_q + buf * C::TILE + r * QS + col) = pq[u];
-      *(u32x4*)(s_do + buf * C::TILE + r * QS + col) = pd[u];
-    }
-    if (tid < 2 * BM) (tid < BM ? s_lse : s_dd)[buf * BM + (tid & (BM - 1))] = pst;
-  };
-
-  int buf = 0;
-  if (qt < n_qt) {
-    fetch(qt);
-    stash(0);
-  }
-  __syncthreads();
-
+  int qt = CAUSAL ? kv0 / BM : 0;
+  const int ntq = (w * C::TPW) >> 1;  // this wave's 32-wide feature slice of dQ
   const int jcol = kv0 + 32 * w + c;  // this lane's key row (sequence-local) in S and dP
-  for (; qt < n_qt; ++qt, buf ^= 1) {
-    const bool has_next = qt + 1 < n_qt;
-    if (has_next) fetch(qt + 1);
-    const int i0 = qt * BM;
-    const bf16* sq = s_q + buf * C::TILE;
-    const bf16* sd = s_do + buf * C::TILE;
 
+  // LDS-DMA: transfer j lands lane L at tile byte 1024 j + 16 L = padded row (64 j + L) / CPR,
+  // chunk (64 j + L) % CPR; the pad chunk re-reads chunk 0 of its row (never used).
+  constexpr int NJ = (C::NDMA + C::NW - 1) / C::NW;
+  int dma_off[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int p16 = 64 * (w + C::NW * jj) + lane;
+    const int r = p16 / C::CPR, ch = p16 % C::CPR;
+    dma_off[jj] = r * rsb + (ch < D / 8 ? ch : 0) * 16;
+  }
+  auto issue_tile = [&](int t, int bi) {
+    const int i0 = t * BM;
+    const int64_t bytes = (int64_t)imin(Lq - i0, BM) * rsb;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb + (int64_t)i0 * rs, bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(db + (int64_t)i0 * rs, bytes);
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int j = w + C::NW * jj;
+      if (j < C::NDMA) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rq, (__attribute__((address_space(3))) void*)(smem + C::OFF_Q + bi * C::TILE_BYTES + 1024 * j), 16,
+            dma_off[jj], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rd, (__attribute__((address_space(3))) void*)(smem + C::OFF_DO + bi * C::TILE_BYTES + 1024 * j), 16,
+            dma_off[jj], 0, 0, 0);
+      }
+    }
+  };
+  // row statistics of q tile t in MFMA row order: threads 0..63 lse2, 64..127 D. Rows past the
+  // sequence get lse2 = +inf, so their P (and dS) is exactly 0 without a mask.
+  auto load_stats = [&](int t) -> float {
+    const int mi = tid & (BM - 1);
+    const int r = t * BM + 32 * (mi >> 5) + tile_row(mi & 31);
+    if (tid >= 2 * BM) return 0.f;
+    if (r >= Lq) return tid < BM ? __builtin_inff() : 0.f;
+    return (tid < BM ? lse_b : dd_b)[r];
+  };
+  auto store_stats = [&](int bi, float v) {
+    if (tid < 2 * BM) s_st[bi * 2 * BM + tid] = v;
+  };
+
+  // one q tile: steps 1-7 of the per-tile math for this wave's 32 keys. Keys past the sequence
+  // need no mask: their K rows are zero in LDS (no dQ contribution) and their dK/dV rows are
+  // never written. Only the causal predicate is applied.
+  auto tile_step = [&](int bi, int i0) {
+    const bf16* sq = s_q + bi * C::TILE;
+    const bf16* sd = s_do + bi * C::TILE;
+    const float* st = s_st + bi * 2 * BM;
+    const int jrel = jcol - i0;  // causal: key j is visible from tile row r iff jrel <= r
     // steps 1 and 3: S = Q K^T, dP = dO V^T  ([q 64] x [kv 32] per wave)
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -257,43 +293,38 @@ void fa_bwd_main(MainArgs a) {
       s[mt] = f32x16{};
       dp[mt] = f32x16{};
     }
+    const int arow = tile_row(c) * QS + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < C::KSD; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 qa = *(const bf16x8*)(sq + (32 * mt + c) * QS + 16 * ks + 8 * hh);
-        const bf16x8 da = *(const bf16x8*)(sd + (32 * mt + c) * QS + 16 * ks + 8 * hh);
+        const bf16x8 qa = *(const bf16x8*)(sq + arow + 32 * mt * QS + 16 * ks);
+        const bf16x8 da = *(const bf16x8*)(sd + arow + 32 * mt * QS + 16 * ks);
         s[mt] = mfma32x32x16(qa, kf[ks], s[mt]);
         dp[mt] = mfma32x32x16(da, vf[ks], dp[mt]);
       }
     }
-
-    // steps 2 and 5: P = exp2(S*scale*log2e - lse2), masked; dS = P (dP - D); both to bf16
-    const bool edge = (i0 + BM > Lq) || (kv0 + BN > Lk) || (a.causal && i0 < kv0 + BN - 1);
+    // steps 2 and 5: P = exp2(S*scale*log2e - lse2), dS = P (dP - D), both to bf16
     bf16x8 pk[2][2], dsk[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        const int rloc = 32 * mt + 8 * a4 + 4 * hh;
-        const f32x4 lse = *(const f32x4*)(s_lse + buf * BM + rloc);
-        const f32x4 dd = *(const f32x4*)(s_dd + buf * BM + rloc);
+        const int mrow = 32 * mt + 8 * a4 + 4 * hh;  // MFMA row of bb = 0
+        const f32x4 lse = *(const f32x4*)(st + mrow);
+        const f32x4 dd = *(const f32x4*)(st + BM + mrow);
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int j = 4 * a4 + bb;
           float p = fast_exp2(s[mt][j] * a.scale_log2 - lse[bb]);
-          if (edge) {
-            const int i = i0 + rloc + bb;
-            const bool vis = i < Lq && jcol < Lk && (!a.causal || jcol <= i);
-            p = vis ? p : 0.f;
-          }
+          if constexpr (CAUSAL) p = (jrel <= 32 * mt + tile_row(8 * a4 + 4 * hh + bb)) ? p : 0.f;
           const float ds = p * (dp[mt][j] - dd[bb]);
           pk[mt][j >> 3][j & 7] = to_bf16(p);
           dsk[mt][j >> 3][j & 7] = to_bf16(ds);
         }
       }
     }
-    // dS^T to LDS: row = this lane's key, 4 consecutive queries per store
+    // dS^T to LDS: row = this lane's key, 4 consecutive MFMA rows per store
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -304,49 +335,76 @@ void fa_bwd_main(MainArgs a) {
         *(bf16x4*)(s_dst + (32 * w + c) * SS + 32 * mt + 8 * a4 + 4 * hh) = v4;
       }
     }
-
-    // steps 7 and 6: dV += P^T dO, dK += dS^T Q  (scale applied at write-back)
+    // steps 7 and 6: dV += P^T dO, dK += dS^T Q (scale applied at write-back). The k-index e of
+    // the A operand is MFMA row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4; the
+    // transpose reads fetch the matching tile rows.
+    const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
 #pragma unroll
     for (int nt = 0; nt < C::NTD; ++nt) {
-      const int col = 32 * nt + 16 * (g & 1) + 4 * (gi & 3);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const int r0 = 32 * mt + 16 * s2 + 4 * hh + (gi >> 2);
-          const bf16x8 bdo = concat(lds_read_tr4(sd + r0 * QS + col), lds_read_tr4(sd + (r0 + 8) * QS + col));
-          const bf16x8 bq = concat(lds_read_tr4(sq + r0 * QS + col), lds_read_tr4(sq + (r0 + 8) * QS + col));
+          const int o = brow + (32 * mt + 16 * s2) * QS + 32 * nt;
+          const bf16x8 bdo = concat(lds_read_tr4(sd + o), lds_read_tr4(sd + o + 2 * QS));
+          const bf16x8 bq = concat(lds_read_tr4(sq + o), lds_read_tr4(sq + o + 2 * QS));
           accV[nt] = mfma32x32x16(pk[mt][s2], bdo, accV[nt]);
           accK[nt] = mfma32x32x16(dsk[mt][s2], bq, accK[nt]);
         }
       }
     }
-    __syncthreads();  // dS^T complete
+  };
 
-    // step 8: dQ partial = dS K over this tile's 128 keys, added to the fp32 accumulator
+  int buf = 0;
+  if (qt < n_qt) {
+    issue_tile(qt, 0);
+    store_stats(0, load_stats(qt));
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+
+  for (; qt < n_qt; ++qt, buf ^= 1) {
+    const bool has_next = qt + 1 < n_qt;
+    float st_next = 0.f;
+    if (has_next) {
+      issue_tile(qt + 1, buf ^ 1);
+      st_next = load_stats(qt + 1);
+    }
+    const int i0 = qt * BM;
+    tile_step(buf, i0);
+    __syncthreads();  // dS^T complete
+    if (has_next) store_stats(buf ^ 1, st_next);
+
+    // step 8: dQ partial = dS K over this tile's 128 keys, added to the fp32 accumulator.
+    // k-index 16 ks + 8 hh + 4 half + e reads kv row 16 ks + 2 hh + half + 4 e.
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(dq_b + (int64_t)i0 * D, (int64_t)imin(Lq - i0, BM) * D * 4);
+    const int krow = 2 * hh + 4 * (gi >> 2);
+    const int tcol = 16 * (g & 1) + 4 * (gi & 3);
 #pragma unroll
     for (int tt = 0; tt < C::TPW; ++tt) {
       const int mtq = (w * C::TPW + tt) & 1;
-      const int col = 32 * mtq + 16 * (g & 1) + 4 * (gi & 3);
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < BN / 16; ++ks) {
-        const int r0 = 16 * ks + 8 * hh + (gi >> 2);
-        const bf16x8 af = concat(lds_read_tr4(s_dst + r0 * SS + col), lds_read_tr4(s_dst + (r0 + 4) * SS + col));
-        acc = mfma32x32x16(af, ktf[ks], acc);
+        const int ra = (16 * ks + krow) * SS + 32 * mtq + tcol;
+        const int rb = (16 * ks + krow) * QS + 32 * ntq + tcol;
+        const bf16x8 af = concat(lds_read_tr4(s_dst + ra), lds_read_tr4(s_dst + ra + SS));
+        const bf16x8 bk = concat(lds_read_tr4(s_k + rb), lds_read_tr4(s_k + rb + QS));
+        acc = mfma32x32x16(af, bk, acc);
       }
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-          const int i = i0 + 32 * mtq + 8 * a4 + 4 * hh + bb;
-          const int64_t gr = q_start + i;
-          if (i < Lq && gr >= 0 && gr < a.total_q)
-            unsafeAtomicAdd(a.dq_acc + ((int64_t)h * a.total_q + gr) * D + 32 * ntq + c, acc[4 * a4 + bb]);
+          const int row = 32 * mtq + tile_row(8 * a4 + 4 * hh + bb);
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[4 * a4 + bb], rq, (row * D + 32 * ntq + c) * 4, 0, 0);
         }
       }
     }
-    if (has_next) stash(buf ^ 1);
+    // the next tile's LDS-DMA (issued before this tile's atomics) must land before the barrier
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(16 * C::TPW));
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
 
@@ -358,15 +416,15 @@ void fa_bwd_main(MainArgs a) {
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         const int r = kv0 + 32 * w + 8 * a4 + 4 * hh + bb;
-        const int64_t gr = kv_start + r;
-        if (r < Lk && gr >= 0 && gr < a.total_kv) {
-          const int64_t o = gr * rs + (int64_t)h * D + 32 * nt + c;
+        if (r < Lk) {
+          const int64_t o = (kv_start + r) * rs + (int64_t)h * D + 32 * nt + c;
           a.dk[o] = to_bf16(accK[nt][4 * a4 + bb] * a.scale);
           a.dv[o] = to_bf16(accV[nt][4 * a4 + bb]);
         }
       }
     }
   }
+#endif
 }
 
 // ------------------------------------------------------------------ stage 3

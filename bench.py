@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the single-pass attention backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal]
+
+One step = one ``fa_bwd_run`` (row preprocess + main kernel + dQ cast) over
+the whole workload, inputs already resident in HBM. The default workload is
+the causal one: batch 1, 32 heads, 8192 tokens, head_dim 128. Throughput is
+algorithmic TFLOP/s, counting 10*Lq*Lk*d FLOPs per (sequence, head) -- the
+five GEMMs of the backward -- halved for causal masks.
+
+Inputs: seeded synthetic Q, K, V, dO (``attention_backward_fa_amd.inputs``);
+O, m, l come from a plain fp32 torch forward on the GPU (input preparation,
+outside the timed region).
+
+Prints ONE JSON line with the metric, a ``roofline`` object for the main
+kernel (its duration taken from HIP events the library records around it
+on the same stream during the timed steps) and a ``cpu_baseline`` object
+(the fp64 oracle's backward timed on this host's cores over a bounded sample
+of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FA-bwd TFLOP/s + % bf16 MFMA peak, S=8192 H=32 D=128 causal, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+MASK_NAMES = {0: "none", 1: "padding", 2: "causal", 3: "padding_causal"}
+
+
+def algorithmic_flops(inp) -> float:
+    """10 * Lq * Lk * d per (sequence, head); half of that under a causal mask."""
+    causal = inp["mask"] in (2, 3)
+    d = inp["q"].shape[2]
+    h = inp["q"].shape[1]
+    total = 0.0
+    for lq, lk in zip(inp["seqlens_q"], inp["seqlens_kv"]):
+        f = 10.0 * lq * lk * d * h
+        total += f / 2 if causal else f
+    return total
+
+
+def segments(inp):
+    padded = inp["mask"] in (1, 3)
+    out = []
+    cq, ck = inp["cu_q"].tolist(), inp["cu_kv"].tolist()
+    for b in range(len(cq) - 1):
+        qs = b * inp["max_seqlen_q"] if padded else cq[b]
+        ks = b * inp["max_seqlen_kv"] if padded else ck[b]
+        out.append((qs, cq[b + 1] - cq[b], ks, ck[b + 1] - ck[b]))
+    return out
+
+
+def torch_forward_stats(inp, device, block=4096):
+    """Input preparation: O (bf16), m, l (fp32) from a plain fp32 softmax-attention
+    forward in torch on the GPU, query rows in blocks. Rows outside every
+    sequence get O = 0, m = 0, l = 1."""
+    import torch
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    tq, h, d = q.shape
+    scale = inp["scale"]
+    causal = inp["mask"] in (2, 3)
+    o = torch.zeros((tq, h, v.shape[2]), dtype=torch.bfloat16, device=device)
+    m = torch.zeros((tq, h), dtype=torch.float32, device=device)
+    l = torch.ones((tq, h), dtype=torch.float32, device=device)
+    for qs, lq, ks, lk in segments(inp):
+        if lq <= 0 or lk <= 0:
+            continue
+        kt = k[ks:ks + lk].to(device).float().permute(1, 2, 0).contiguous()   # [H, d, Lk]
+        vb = v[ks:ks + lk].to(device).float().permute(1, 0, 2).contiguous()   # [H, Lk, d]
+        for i0 in range(0, lq, block):
+            i1 = min(lq, i0 + block)
+            qb = q[qs + i0:qs + i1].to(device).float().permute(1, 0, 2).contiguous()  # [H, n, d]
+            s = torch.bmm(qb, kt) * scale                                             # [H, n, Lk]
+            if causal:
+                rows = torch.arange(i0, i1, device=device)[:, None]
+                cols = torch.arange(lk, device=device)[None, :]
+                s.masked_fill_((cols > rows)[None], float("-inf"))
+            mb = s.amax(dim=-1)
+            e = torch.exp(s - mb[..., None])
+            del s
+            lb = e.sum(dim=-1)
+            ob = torch.bmm(e, vb) / lb[..., None]
+            del e
+            o[qs + i0:qs + i1] = ob.permute(1, 0, 2).to(torch.bfloat16)
+            m[qs + i0:qs + i1] = mb.T
+            l[qs + i0:qs + i1] = lb.T
+    return o, m, l
+
+
+def make_workload(name: str, device):
+    """Seeded inputs of a named workload on `device`, with O, m, l from the torch forward."""
+    import torch
+    from attention_backward_fa_amd import inputs
+    inp = inputs.make(name)
+    o, m, l = torch_forward_stats(inp, device)
+    dev = {key: inp[key].to(device) for key in ("q", "k", "v", "do", "cu_q", "cu_kv")}
+    dev.update(o=o, m=m, l=l)
+    return inp, dev
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        info = [x for x in threadpool_info() if x.get("user_api") == "blas"]
+        if info:
+            return int(info[0]["num_threads"])
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(inp, dev, target_s: float = 15.0):
+    """The fp64 oracle's backward, as it stands, on (sequence, head) slices of the
+    same workload and the same inputs the GPU saw; sample grown until ~target_s."""
+    import numpy as np
+    import oracle
+    o, m, l = dev["o"].float().cpu().numpy(), dev["m"].cpu().numpy(), dev["l"].cpu().numpy()
+    q, k, v, do = (inp[x].float().numpy() for x in ("q", "k", "v", "do"))
+    causal = inp["mask"] in (2, 3)
+    d, heads = q.shape[2], q.shape[1]
+    pairs = [(b, h) for b in range(len(inp["seqlens_q"])) for h in range(heads)]
+    segs = segments(inp)
+    done, flops, elapsed = [], 0.0, 0.0
+    for b, h in pairs:
+        qs, lq, ks, lk = segs[b]
+        if lq <= 0 or lk <= 0:
+            continue
+        t0 = time.perf_counter()
+        oracle.backward_head(q[qs:qs + lq, h], k[ks:ks + lk, h], v[ks:ks + lk, h], o[qs:qs + lq, h],
+                             do[qs:qs + lq, h], m[qs:qs + lq, h], l[qs:qs + lq, h], inp["scale"], causal)
+        elapsed += time.perf_counter() - t0
+        f = 10.0 * lq * lk * d
+        flops += f / 2 if causal else f
+        done.append((b, h))
+        if elapsed >= target_s:
+            break
+    del np
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle backward on {len(done)} of {len(pairs)} (sequence, head) slices of the same "
+                      f"workload and inputs ({elapsed:.1f} s); same FLOP count as the metric",
+            "seconds": elapsed}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="causal")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the backward shards by (sequence, head) with no exchange, so N GPUs run N independent copies)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from attention_backward_fa_amd import binding
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    print(f"[bench] preparing workload {args.workload}", file=sys.stderr, flush=True)
+    inp, dev = make_workload(args.workload, device)
+    flops = algorithmic_flops(inp)
+    tq, heads, d = inp["q"].shape
+    op = binding.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0])
+    dq, dk, dv = (torch.empty_like(dev[x]) for x in ("q", "k", "v"))
+
+    def step():
+        op.run(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["m"], dev["l"], dev["cu_q"], dev["cu_kv"],
+               inp["scale"], inp["mask"], dq, dk, dv)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    binding.fa_bwd_profile_enable(op.handle, True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    stages = binding.fa_bwd_profile_collect(op.handle)
+    binding.fa_bwd_profile_enable(op.handle, False)
+    finite = all(bool(torch.isfinite(x).all()) for x in (dq, dk, dv))
+    op.close()
+    print(f"[bench] {args.steps} steps: {ms:.4f} ms/step", file=sys.stderr, flush=True)
+    pre_ms = sum(s[0] for s in stages) / len(stages)
+    main_ms = sum(s[1] for s in stages) / len(stages)
+    cast_ms = sum(s[2] for s in stages) / len(stages)
+    tflops = flops / (ms * 1e-3) / 1e12
+    achieved = flops / (main_ms * 1e-3) / 1e12
+
+    seqlens = sorted(set(inp["seqlens_q"]))
+    config = {"workload": f"{args.workload}: batch {inp['batch']}, {heads} heads, "
+                          f"seqlens {seqlens if len(seqlens) < 5 else str(len(inp['seqlens_q'])) + ' varlen'}, "
+                          f"head_dim {d}, mask {MASK_NAMES[inp['mask']]}",
+              "batch": inp["batch"], "heads": heads, "head_dim": d, "seq_len": inp["max_seqlen_q"],
+              "total_tokens": tq, "mask": MASK_NAMES[inp["mask"]], "seed": inp["seed"],
+              "algorithmic_flops": flops}
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config,
+        "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {"fa_bwd_pre": round(pre_ms, 5), "fa_bwd_main": round(main_ms, 5),
+                       "fa_bwd_dq_cast": round(cast_ms, 5)},
+        "roofline": {"bound": "mfma", "kernel": "fa_bwd_main", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "outputs_finite": finite,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, dev, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
