@@ -22,6 +22,10 @@ FA_BWD_ERR_UNSUPPORTED = 2
 FA_BWD_ERR_OUT_OF_MEMORY = 3
 FA_BWD_ERR_HIP = 4
 
+FA_BWD_ALGO_DEFAULT = 0
+FA_BWD_ALGO_SINGLE_PASS = 1
+FA_BWD_ALGO_RECOMPUTE_DQ = 2
+
 FA_BWD_MASK_NONE = 0
 FA_BWD_MASK_PADDING = 1
 FA_BWD_MASK_CAUSAL = 2
@@ -35,7 +39,7 @@ EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_destroy", "fa_bwd_status_stri
 class FaBwdDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_kv", ctypes.c_int32),
-                ("total_q", ctypes.c_int64), ("total_kv", ctypes.c_int64), ("deterministic", ctypes.c_int32)]
+                ("total_q", ctypes.c_int64), ("total_kv", ctypes.c_int64), ("algorithm", ctypes.c_int32)]
 
 
 _lib = None
@@ -84,9 +88,9 @@ def _check(status: int, what: str) -> None:
 
 
 def fa_bwd_create(batch: int, num_heads: int, head_dim: int, max_seqlen_q: int, max_seqlen_kv: int,
-                  total_q: int, total_kv: int, deterministic: int = 0) -> ctypes.c_void_p:
+                  total_q: int, total_kv: int, algorithm: int = FA_BWD_ALGO_DEFAULT) -> ctypes.c_void_p:
     """Create a handle (and its device workspace on the current device)."""
-    desc = FaBwdDesc(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv, deterministic)
+    desc = FaBwdDesc(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv, algorithm)
     handle = ctypes.c_void_p()
     _check(load_library().fa_bwd_create(ctypes.byref(desc), ctypes.byref(handle)), "fa_bwd_create")
     return handle
@@ -162,8 +166,10 @@ def fa_bwd_profile_collect(handle, max_runs: int = 4096):
 class FaBwd:
     """Owns one handle; ``run`` allocates nothing when the outputs are passed in."""
 
-    def __init__(self, batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv):
-        self.handle = fa_bwd_create(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv)
+    def __init__(self, batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv,
+                 algorithm=FA_BWD_ALGO_DEFAULT):
+        self.handle = fa_bwd_create(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv,
+                                    algorithm)
 
     def run(self, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq=None, dk=None, dv=None,
             stream=None):
@@ -187,8 +193,8 @@ class FaBwd:
 
 
 def attention_backward(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale: float, mask: int,
-                       max_seqlen_q: int, max_seqlen_kv: int):
+                       max_seqlen_q: int, max_seqlen_kv: int, algorithm: int = FA_BWD_ALGO_DEFAULT):
     """One-shot call: create a handle, run on the current stream, destroy (which waits)."""
     with FaBwd(cu_seqlens_q.numel() - 1, q.shape[1], q.shape[2], max_seqlen_q, max_seqlen_kv,
-               q.shape[0], k.shape[0]) as op:
+               q.shape[0], k.shape[0], algorithm) as op:
         return op.run(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask)

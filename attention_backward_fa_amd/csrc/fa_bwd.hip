@@ -13,6 +13,7 @@
 
 struct fa_bwd_handle {
   fa_bwd_desc desc;
+  bool single_pass;  // FA_BWD_ALGO_SINGLE_PASS (else recompute form)
   int device;
   float* dq_acc;  // [H][total_q][head_dim]
   float* lse2;    // [H][total_q]
@@ -41,12 +42,14 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
       d->total_kv < 1)
     return FA_BWD_ERR_INVALID_ARGUMENT;
   if (d->head_dim != 64 && d->head_dim != 128) return FA_BWD_ERR_UNSUPPORTED;
-  if (d->deterministic != 0) return FA_BWD_ERR_UNSUPPORTED;
+  if (d->algorithm < FA_BWD_ALGO_DEFAULT || d->algorithm > FA_BWD_ALGO_RECOMPUTE_DQ) return FA_BWD_ERR_INVALID_ARGUMENT;
   // index arithmetic stays in int64; grids must fit the launch limits
   const int64_t rows = (d->total_q > d->total_kv ? d->total_q : d->total_kv);
   if (rows > (int64_t(1) << 40) / d->num_heads) return FA_BWD_ERR_INVALID_ARGUMENT;
   const int64_t kv_tiles = (d->max_seqlen_kv + 127) / 128;
   if (kv_tiles * d->num_heads * d->batch > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
+  const int64_t q_tiles = (d->max_seqlen_q + 127) / 128;
+  if (q_tiles * d->num_heads * d->batch > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
   const int64_t rows_per_block = 256 / (d->head_dim / 8);
   if ((rows * d->num_heads + rows_per_block - 1) / rows_per_block > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
   return FA_BWD_OK;
@@ -70,13 +73,15 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   pa.cu_kv = cu_kv;
   pa.lse2 = h->lse2;
   pa.dvec = h->dvec;
-  pa.dq_acc = h->dq_acc;
+  pa.dq_acc = h->single_pass ? h->dq_acc : nullptr;
+  pa.dq = h->single_pass ? nullptr : static_cast<bf16*>(dq);
   pa.dk = static_cast<bf16*>(dk);
   pa.dv = static_cast<bf16*>(dv);
   pa.total_q = d.total_q;
   pa.total_kv = d.total_kv;
   pa.H = d.num_heads;
   pa.batch = d.batch;
+  pa.max_seqlen_q = d.max_seqlen_q;
   pa.max_seqlen_kv = d.max_seqlen_kv;
   pa.padded = padded;
   const int64_t rows = (d.total_q > d.total_kv ? d.total_q : d.total_kv) * d.num_heads;
@@ -109,6 +114,7 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.cu_q = cu_q;
   ma.cu_kv = cu_kv;
   ma.dq_acc = h->dq_acc;
+  ma.dq = static_cast<bf16*>(dq);
   ma.dk = static_cast<bf16*>(dk);
   ma.dv = static_cast<bf16*>(dv);
   ma.total_q = d.total_q;
@@ -123,16 +129,32 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.scale = scale;
   const int64_t kv_tiles = (d.max_seqlen_kv + fa::MainCfg<D>::BN - 1) / fa::MainCfg<D>::BN;
   const dim3 grid((unsigned)(kv_tiles * d.num_heads * d.batch));
-  if (causal)
-    fa::fa_bwd_main<D, true><<<grid, dim3(256), 0, stream>>>(ma);
-  else
-    fa::fa_bwd_main<D, false><<<grid, dim3(256), 0, stream>>>(ma);
+  if (h->single_pass) {
+    if (causal)
+      fa::fa_bwd_main<D, true, true><<<grid, dim3(256), 0, stream>>>(ma);
+    else
+      fa::fa_bwd_main<D, false, true><<<grid, dim3(256), 0, stream>>>(ma);
+  } else {
+    if (causal)
+      fa::fa_bwd_main<D, true, false><<<grid, dim3(256), 0, stream>>>(ma);
+    else
+      fa::fa_bwd_main<D, false, false><<<grid, dim3(256), 0, stream>>>(ma);
+  }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return FA_BWD_ERR_HIP;
 
-  const int64_t qrows = d.total_q * d.num_heads;
-  hipLaunchKernelGGL(fa::fa_bwd_dq_cast<D>, dim3((unsigned)((qrows + RPB - 1) / RPB)), dim3(256), 0, stream,
-                     (const float*)h->dq_acc, static_cast<bf16*>(dq), d.total_q, d.num_heads, scale);
+  if (h->single_pass) {
+    const int64_t qrows = d.total_q * d.num_heads;
+    hipLaunchKernelGGL(fa::fa_bwd_dq_cast<D>, dim3((unsigned)((qrows + RPB - 1) / RPB)), dim3(256), 0, stream,
+                       (const float*)h->dq_acc, static_cast<bf16*>(dq), d.total_q, d.num_heads, scale);
+  } else {
+    const int64_t q_tiles = (d.max_seqlen_q + fa::DqCfg<D>::BQ - 1) / fa::DqCfg<D>::BQ;
+    const dim3 qgrid((unsigned)(q_tiles * d.num_heads * d.batch));
+    if (causal)
+      fa::fa_bwd_dq<D, true><<<qgrid, dim3(256), 0, stream>>>(ma);
+    else
+      fa::fa_bwd_dq<D, false><<<qgrid, dim3(256), 0, stream>>>(ma);
+  }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return FA_BWD_ERR_HIP;
   return FA_BWD_OK;
@@ -150,13 +172,14 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
   fa_bwd_handle* h = new (std::nothrow) fa_bwd_handle();
   if (!h) return FA_BWD_ERR_OUT_OF_MEMORY;
   h->desc = *desc;
+  h->single_pass = desc->algorithm == FA_BWD_ALGO_SINGLE_PASS;
   if (hipGetDevice(&h->device) != hipSuccess) {
     delete h;
     return FA_BWD_ERR_HIP;
   }
   const size_t stats = (size_t)desc->total_q * desc->num_heads;
   const size_t acc = stats * desc->head_dim;
-  if (hipMalloc(&h->dq_acc, acc * sizeof(float)) != hipSuccess ||
+  if ((h->single_pass && hipMalloc(&h->dq_acc, acc * sizeof(float)) != hipSuccess) ||
       hipMalloc(&h->lse2, stats * sizeof(float)) != hipSuccess ||
       hipMalloc(&h->dvec, stats * sizeof(float)) != hipSuccess) {
     (void)hipGetLastError();
@@ -200,7 +223,7 @@ fa_bwd_status fa_bwd_destroy(fa_bwd_handle* h) {
   fa_bwd_status st = FA_BWD_OK;
   if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(h->device) != hipSuccess) st = FA_BWD_ERR_HIP;
   if (hipDeviceSynchronize() != hipSuccess) st = FA_BWD_ERR_HIP;
-  if (hipFree(h->dq_acc) != hipSuccess) st = FA_BWD_ERR_HIP;
+  if (h->dq_acc && hipFree(h->dq_acc) != hipSuccess) st = FA_BWD_ERR_HIP;
   if (hipFree(h->lse2) != hipSuccess) st = FA_BWD_ERR_HIP;
   if (hipFree(h->dvec) != hipSuccess) st = FA_BWD_ERR_HIP;
   release_events(h);

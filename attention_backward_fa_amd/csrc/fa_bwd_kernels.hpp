@@ -50,11 +50,12 @@ struct PreArgs {
   const int* cu_kv;
   float* lse2;    // [H][total_q]: m*log2(e) + log2(l)
   float* dvec;    // [H][total_q]: rowsum(O*dO)
-  float* dq_acc;  // [H][total_q][D]
+  float* dq_acc;  // [H][total_q][D], zeroed when not null
+  bf16* dq;       // when not null: rows outside every sequence are zeroed
   bf16* dk;
   bf16* dv;
   int64_t total_q, total_kv;
-  int H, batch, max_seqlen_kv, padded;
+  int H, batch, max_seqlen_q, max_seqlen_kv, padded;
 };
 
 template <int D>
@@ -74,10 +75,16 @@ __global__ __launch_bounds__(256) void fa_bwd_pre(PreArgs a) {
     for (int e = 0; e < 8; ++e) acc += from_bf16(ov[e]) * from_bf16(gv[e]);
 #pragma unroll
     for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
-    float* accrow = a.dq_acc + ((int64_t)h * a.total_q + t) * D + sub * 8;
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4*)accrow = z;
-    *(f32x4*)(accrow + 4) = z;
+    if (a.dq_acc) {
+      float* accrow = a.dq_acc + ((int64_t)h * a.total_q + t) * D + sub * 8;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)accrow = z;
+      *(f32x4*)(accrow + 4) = z;
+    }
+    if (a.dq && !row_in_sequence(t, a.cu_q, a.batch, a.padded, a.max_seqlen_q)) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *(u32x4*)(a.dq + off) = z;
+    }
     if (sub == 0) {
       const int64_t sidx = (int64_t)h * a.total_q + t;
       a.dvec[sidx] = acc;
@@ -102,7 +109,8 @@ struct MainArgs {
   const float* dvec;
   const int* cu_q;
   const int* cu_kv;
-  float* dq_acc;
+  float* dq_acc;  // fp32 [H][total_q][D] accumulator (single-pass form)
+  bf16* dq;       // bf16 output (recompute form)
   bf16* dk;
   bf16* dv;
   int64_t total_q, total_kv;
@@ -166,7 +174,10 @@ __device__ __forceinline__ int clamp_len(int64_t start, int len, int64_t total) 
 
 __device__ __forceinline__ int imin(int x, int y) { return x < y ? x : y; }
 
-template <int D, bool CAUSAL>
+// WITH_DQ: the single-pass form that also forms the dQ partial of every (q tile, kv tile)
+// pair and adds it to the fp32 accumulator with atomics; without it the kernel produces dK
+// and dV only and dQ comes from fa_bwd_dq.
+template <int D, bool CAUSAL, bool WITH_DQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_main(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -208,9 +219,11 @@ void fa_bwd_main(MainArgs a) {
   const int kv_rows = imin(Lk - kv0, BN);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (int64_t)kv_rows * rsb);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (int64_t)kv_rows * rsb);
-  for (int ch = tid; ch < BN * D / 8; ch += 256) {
-    const int r = ch / (D / 8), col = (ch % (D / 8)) * 8;
-    *(u32x4*)(s_k + r * QS + col) = buf_load16(rk, r * rsb + col * 2);
+  if constexpr (WITH_DQ) {
+    for (int ch = tid; ch < BN * D / 8; ch += 256) {
+      const int r = ch / (D / 8), col = (ch % (D / 8)) * 8;
+      *(u32x4*)(s_k + r * QS + col) = buf_load16(rk, r * rsb + col * 2);
+    }
   }
   bf16x8 kf[C::KSD], vf[C::KSD];
 #pragma unroll
@@ -324,9 +337,9 @@ void fa_bwd_main(MainArgs a) {
         }
       }
     }
-    // dS^T to LDS: row = this lane's key, 4 consecutive MFMA rows per store
+    // dS^T to LDS (for the dQ GEMM): row = this lane's key, 4 consecutive MFMA rows per store
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2 && WITH_DQ; ++mt) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const bf16x8 src = dsk[mt][a4 >> 1];
@@ -372,6 +385,14 @@ void fa_bwd_main(MainArgs a) {
     }
     const int i0 = qt * BM;
     tile_step(buf, i0);
+    if constexpr (!WITH_DQ) {
+      if (has_next) store_stats(buf ^ 1, st_next);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next tile's LDS-DMA has landed
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      continue;
+    }
     __syncthreads();  // dS^T complete
     if (has_next) store_stats(buf ^ 1, st_next);
 
@@ -421,6 +442,200 @@ void fa_bwd_main(MainArgs a) {
           a.dk[o] = to_bf16(accK[nt][4 * a4 + bb] * a.scale);
           a.dv[o] = to_bf16(accV[nt][4 * a4 + bb]);
         }
+      }
+    }
+  }
+#endif
+}
+
+
+// ------------------------------------------------------------------ stage 2b: dQ by recompute
+
+template <int D>
+struct DqCfg {
+  static constexpr int BQ = 128;                 // q rows per workgroup (32 per wave)
+  static constexpr int BK = 64;                  // kv rows per step
+  static constexpr int NW = 4;
+  static constexpr int KSD = D / 16;
+  static constexpr int NTD = D / 32;
+  static constexpr int QS = D + 8;               // padded row stride of the K and V tiles
+  static constexpr int CPR = QS / 8;
+  static constexpr int TILE = BK * QS;
+  static constexpr int TILE_BYTES = TILE * 2;
+  static constexpr int NDMA = TILE_BYTES / 1024;
+  static constexpr int OFF_K = 0;                          // K [2][BK][QS]
+  static constexpr int OFF_V = OFF_K + 2 * TILE_BYTES;     // V [2][BK][QS]
+  static constexpr int LDS_BYTES = OFF_V + 2 * TILE_BYTES;
+  static_assert(TILE_BYTES % 1024 == 0, "a tile is a whole number of 1 KB transfers");
+};
+
+// dQ of one (q tile, head, sequence): loops over the kv tiles, recomputes S^T = K Q^T and
+// dP^T = V dO^T with the forward's statistics (steps 1-5 of the per-tile math), and
+// accumulates dQ^T = K^T dS^T (step 8) in registers; dQ is written once, in bf16.
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dq(MainArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = DqCfg<D>;
+  constexpr int BQ = C::BQ, BK = C::BK, QS = C::QS;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+  const int HB = a.H * a.batch;
+  const int tr = blockIdx.x / HB;
+  const int hb = blockIdx.x - tr * HB;
+  const int b = hb / a.H, h = hb - (hb / a.H) * a.H;
+  int64_t q_start, kv_start;
+  int Lq, Lk;
+  seq_of(a.cu_q, b, a.padded, a.max_seqlen_q, q_start, Lq);
+  seq_of(a.cu_kv, b, a.padded, a.max_seqlen_kv, kv_start, Lk);
+  Lq = clamp_len(q_start, Lq, a.total_q);
+  Lk = clamp_len(kv_start, Lk, a.total_kv);
+  // causal: the q tiles with the most keys (the last ones) dispatch first
+  const int n_qt_max = (a.max_seqlen_q + BQ - 1) / BQ;
+  const int qtile = CAUSAL ? n_qt_max - 1 - tr : tr;
+  const int i0 = qtile * BQ;
+  if (i0 >= Lq) return;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
+  const int64_t rs = (int64_t)a.H * D;
+  const int rsb = (int)(rs * 2);
+  const bf16* kb = a.k + kv_start * rs + (int64_t)h * D;
+  const bf16* vb = a.v + kv_start * rs + (int64_t)h * D;
+  const bf16* qb = a.q + (q_start + i0) * rs + (int64_t)h * D;
+  const bf16* db = a.dout + (q_start + i0) * rs + (int64_t)h * D;
+  const int qi = i0 + 32 * w + c;  // this lane's query row (sequence-local) in S^T, dP^T and dQ^T
+
+  // Q, dO as B operands of S^T = K Q^T and dP^T = V dO^T: row qi, features 16 ks + 8 hh ..+7
+  const int q_rows = imin(Lq - i0, BQ);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (int64_t)q_rows * rsb);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(db, (int64_t)q_rows * rsb);
+  bf16x8 qf[C::KSD], df[C::KSD];
+#pragma unroll
+  for (int ks = 0; ks < C::KSD; ++ks) {
+    const int off = (32 * w + c) * rsb + (16 * ks + 8 * hh) * 2;
+    qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+    df[ks] = __builtin_bit_cast(bf16x8, buf_load16(rd, off));
+  }
+  // rows past the sequence: lse2 = +inf makes P (and dS) exactly 0
+  const float lse = qi < Lq ? a.lse2[(int64_t)h * a.total_q + q_start + qi] : __builtin_inff();
+  const float dd = qi < Lq ? a.dvec[(int64_t)h * a.total_q + q_start + qi] : 0.f;
+
+  int n_kt = (Lk + BK - 1) / BK;
+  if (CAUSAL) n_kt = imin(n_kt, (i0 + BQ - 1) / BK + 1);
+
+  {  // zero the K and V buffers once (rows past the sequence are masked, but must be finite)
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int o = tid * 16; o < C::LDS_BYTES; o += 256 * 16) *(u32x4*)(smem + o) = z;
+  }
+  __syncthreads();
+
+  constexpr int NJ = (C::NDMA + C::NW - 1) / C::NW;
+  int dma_off[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int p16 = 64 * (w + C::NW * jj) + lane;
+    const int r = p16 / C::CPR, ch = p16 % C::CPR;
+    dma_off[jj] = r * rsb + (ch < D / 8 ? ch : 0) * 16;
+  }
+  auto issue_kv = [&](int t, int bi) {
+    const int j0 = t * BK;
+    const int64_t bytes = (int64_t)imin(Lk - j0, BK) * rsb;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (int64_t)j0 * rs, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (int64_t)j0 * rs, bytes);
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int j = w + C::NW * jj;
+      if (j < C::NDMA) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void*)(smem + C::OFF_K + bi * C::TILE_BYTES + 1024 * j), 16,
+            dma_off[jj], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(smem + C::OFF_V + bi * C::TILE_BYTES + 1024 * j), 16,
+            dma_off[jj], 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[C::NTD];
+#pragma unroll
+  for (int nt = 0; nt < C::NTD; ++nt) acc[nt] = f32x16{};
+
+  int buf = 0;
+  if (n_kt > 0) issue_kv(0, 0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+
+  const int arow = tile_row(c) * QS + 8 * hh;
+  const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
+  for (int t = 0; t < n_kt; ++t, buf ^= 1) {
+    if (t + 1 < n_kt) issue_kv(t + 1, buf ^ 1);
+    const bf16* sk = (const bf16*)(smem + C::OFF_K + buf * C::TILE_BYTES);
+    const bf16* sv = (const bf16*)(smem + C::OFF_V + buf * C::TILE_BYTES);
+    // steps 1 and 3, transposed: S^T = K Q^T, dP^T = V dO^T  ([kv 64] x [q 32] per wave)
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt] = f32x16{};
+      dp[mt] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KSD; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 ka = *(const bf16x8*)(sk + arow + 32 * mt * QS + 16 * ks);
+        const bf16x8 va = *(const bf16x8*)(sv + arow + 32 * mt * QS + 16 * ks);
+        s[mt] = mfma32x32x16(ka, qf[ks], s[mt]);
+        dp[mt] = mfma32x32x16(va, df[ks], dp[mt]);
+      }
+    }
+    // steps 2 and 5: P = exp2(S*scale*log2e - lse2), dS = P (dP - D); key row j = t*BK + kv row.
+    // Visible iff j < Lk and (causal) j <= qi: one bound per lane on the tile-local kv row.
+    const int lim = CAUSAL ? imin(Lk - 1, qi) - t * BK : Lk - 1 - t * BK;
+    bf16x8 dsk[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int j = 4 * a4 + bb;
+          float p = fast_exp2(s[mt][j] * a.scale_log2 - lse);
+          p = (32 * mt + tile_row(8 * a4 + 4 * hh + bb) <= lim) ? p : 0.f;
+          dsk[mt][j >> 3][j & 7] = to_bf16(p * (dp[mt][j] - dd));
+        }
+      }
+    }
+    // step 8, transposed: dQ^T += K^T dS^T. The k-index e of dS^T is kv MFMA row
+    // 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4; the transpose reads fetch those K rows.
+#pragma unroll
+    for (int nt = 0; nt < C::NTD; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int o = brow + (32 * mt + 16 * s2) * QS + 32 * nt;
+          const bf16x8 kt = concat(lds_read_tr4(sk + o), lds_read_tr4(sk + o + 2 * QS));
+          acc[nt] = mfma32x32x16(kt, dsk[mt][s2], acc[nt]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next K/V tiles have landed
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  }
+
+  // dQ = scale * (dQ^T)^T in bf16: this lane holds features 32 nt + 8 a4 + 4 hh + bb of row qi
+  if (qi < Lq) {
+    bf16* dst = a.dq + (q_start + qi) * rs + (int64_t)h * D + 4 * hh;
+#pragma unroll
+    for (int nt = 0; nt < C::NTD; ++nt) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const bf16x4 v4 = {to_bf16(acc[nt][4 * a4] * a.scale), to_bf16(acc[nt][4 * a4 + 1] * a.scale),
+                           to_bf16(acc[nt][4 * a4 + 2] * a.scale), to_bf16(acc[nt][4 * a4 + 3] * a.scale)};
+        *(bf16x4*)(dst + 32 * nt + 8 * a4) = v4;
       }
     }
   }

@@ -56,10 +56,23 @@ typedef enum {
   FA_BWD_MASK_PADDING_CAUSAL = 3
 } fa_bwd_mask;
 
+/* How dQ is formed. Both forms compute the same per-tile math (steps 1-8) and
+ * agree within the fp32 rounding of the accumulation order. */
+typedef enum {
+  FA_BWD_ALGO_DEFAULT = 0,      /* the faster form on this GPU: FA_BWD_ALGO_RECOMPUTE_DQ */
+  FA_BWD_ALGO_SINGLE_PASS = 1,  /* the article's single-pass structure: one main kernel forms the dK, dV and
+                                   dQ contributions of every (q tile, kv tile) pair; dQ partial sums are
+                                   added to an fp32 workspace with global atomics (summation order not
+                                   fixed), then cast to bf16 */
+  FA_BWD_ALGO_RECOMPUTE_DQ = 2  /* the article's two-pass fallback: a kv-outer kernel forms dK, dV and a
+                                   q-outer kernel recomputes S and dP to form dQ in registers; no
+                                   atomics, no dQ workspace, bitwise reproducible */
+} fa_bwd_algo;
+
 typedef enum {
   FA_BWD_OK = 0,
   FA_BWD_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad mask code, bad scale, misalignment */
-  FA_BWD_ERR_UNSUPPORTED = 2,      /* head_dim other than 64 or 128, deterministic mode */
+  FA_BWD_ERR_UNSUPPORTED = 2,      /* head_dim other than 64 or 128 */
   FA_BWD_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed in fa_bwd_create */
   FA_BWD_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
 } fa_bwd_status;
@@ -72,14 +85,14 @@ typedef struct {
   int32_t max_seqlen_kv; /* same for keys/values */
   int64_t total_q;       /* rows of q, o, do, dq, m, l; >= 1 */
   int64_t total_kv;      /* rows of k, v, dk, dv; >= 1 */
-  int32_t deterministic; /* must be 0: dQ is accumulated with fp32 atomics (order not fixed) */
+  int32_t algorithm;     /* an fa_bwd_algo code */
 } fa_bwd_desc;
 
 /* Validates desc and allocates the device workspace of the handle on the
- * current HIP device: an fp32 dQ accumulator of total_q*H*head_dim floats and
- * two fp32 [H][total_q] row-statistic arrays. On success *out holds a new
- * handle; on failure *out is set to NULL. Host-side checks run before any HIP
- * call. */
+ * current HIP device: two fp32 [H][total_q] row-statistic arrays and, for
+ * FA_BWD_ALGO_SINGLE_PASS only, an fp32 dQ accumulator of total_q*H*head_dim
+ * floats. On success *out holds a new handle; on failure *out is set to NULL.
+ * Host-side checks run before any HIP call. */
 fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out);
 
 /* Enqueues the backward on `stream` (a hipStream_t; NULL = the default
@@ -115,14 +128,15 @@ const char* fa_bwd_status_string(fa_bwd_status s);
 const fa_bwd_desc* fa_bwd_get_desc(const fa_bwd_handle* h);
 
 /* Per-kernel timing for benchmarks. While enabled, every fa_bwd_run also
- * records four HIP events on its stream, around its three kernels
- * (row preprocessing, main kernel, dQ cast); recording does not wait.
+ * records four HIP events on its stream, around its three kernels (row
+ * preprocessing, main kernel, then the dQ cast in single-pass form or the dQ
+ * kernel in recompute form); recording does not wait.
  * Enabling or disabling forgets the runs recorded so far. At most 4096 runs
  * are kept; later runs are not recorded. */
 fa_bwd_status fa_bwd_profile_enable(fa_bwd_handle* h, int32_t enable);
 
 /* Waits for the recorded runs, writes min(max_runs, recorded) rows of three
- * floats (milliseconds of the preprocessing, main and cast kernels) to the
+ * floats (milliseconds of the preprocessing, main and third kernels) to the
  * HOST array ms, stores the row count in *n_runs, and forgets the runs. */
 fa_bwd_status fa_bwd_profile_collect(fa_bwd_handle* h, float* ms, int32_t max_runs, int32_t* n_runs);
 

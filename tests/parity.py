@@ -25,13 +25,13 @@ def oracle_stats(inp):
             torch.from_numpy(l).to(torch.float32))
 
 
-def run_gpu(inp, o, m, l, device="cuda"):
+def run_gpu(inp, o, m, l, device="cuda", algorithm=binding.FA_BWD_ALGO_DEFAULT):
     """Run the HIP backward once; returns CPU fp32 dq, dk, dv."""
     dev = torch.device(device)
     t = {k: inp[k].to(dev) for k in ("q", "k", "v", "do", "cu_q", "cu_kv")}
     dq, dk, dv = binding.attention_backward(t["q"], t["k"], t["v"], o.to(dev), t["do"], m.to(dev), l.to(dev),
                                             t["cu_q"], t["cu_kv"], inp["scale"], inp["mask"],
-                                            inp["max_seqlen_q"], inp["max_seqlen_kv"])
+                                            inp["max_seqlen_q"], inp["max_seqlen_kv"], algorithm)
     torch.cuda.synchronize()
     return dq.float().cpu(), dk.float().cpu(), dv.float().cpu()
 

@@ -43,7 +43,7 @@ def test_status_strings():
 
 def _create(**kw):
     d = dict(batch=1, num_heads=1, head_dim=128, max_seqlen_q=128, max_seqlen_kv=128, total_q=128, total_kv=128,
-             deterministic=0)
+             algorithm=0)
     d.update(kw)
     lib = B.load_library()
     h = ctypes.c_void_p(0x1234)
@@ -61,7 +61,8 @@ def _create(**kw):
     (dict(head_dim=96), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(head_dim=256), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(head_dim=0), B.FA_BWD_ERR_UNSUPPORTED),
-    (dict(deterministic=1), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(algorithm=3), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(algorithm=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(total_q=1 << 40, num_heads=8), B.FA_BWD_ERR_INVALID_ARGUMENT),          # index range
     (dict(max_seqlen_kv=1 << 30, num_heads=1 << 10, batch=1 << 10), B.FA_BWD_ERR_INVALID_ARGUMENT),  # grid size
 ])

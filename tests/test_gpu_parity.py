@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+from attention_backward_fa_amd import binding as B
 from attention_backward_fa_amd import inputs as I
 from tests import parity as P
 
@@ -35,11 +36,15 @@ CASES = [
 ]
 
 
+ALGOS = {"recompute": B.FA_BWD_ALGO_RECOMPUTE_DQ, "singlepass": B.FA_BWD_ALGO_SINGLE_PASS}
+
+
+@pytest.mark.parametrize("algo", list(ALGOS))
 @pytest.mark.parametrize("case", CASES, ids=[c.name for c in CASES])
-def test_parity_full(case):
+def test_parity_full(case, algo):
     inp = I.make(case)
-    print(f"[parity] {case.name}: T_q={inp['q'].shape[0]} H={case.heads} d={case.head_dim} mask={case.mask}",
-          flush=True)
+    print(f"[parity] {case.name} ({algo}): T_q={inp['q'].shape[0]} H={case.heads} d={case.head_dim} "
+          f"mask={case.mask}", flush=True)
     o, m, l = P.oracle_stats(inp)
     if I.is_padded_mask(case.mask):
         # the backward must not read padding rows: fill them with NaN
@@ -52,18 +57,37 @@ def test_parity_full(case):
         vk = torch.from_numpy(P.oracle.valid_rows(inp["cu_kv"], case.mask, inp["max_seqlen_kv"], inp["k"].shape[0]))
         inp["k"][~vk] = float("nan")
         inp["v"][~vk] = float("nan")
-    gpu = P.run_gpu(inp, o, m, l)
+    gpu = P.run_gpu(inp, o, m, l, algorithm=ALGOS[algo])
     ref = P.oracle_backward(inp, o, m, l)
     res = P.check_full(inp, gpu, ref)
-    print(f"[parity] {case.name}: " + " ".join(f"{k}: rel_l2={v[0]:.2e} max={v[1]:.2e}" for k, v in res.items()),
+    print(f"[parity] {case.name} ({algo}): " + " ".join(f"{k}: rel_l2={v[0]:.2e} max={v[1]:.2e}" for k, v in res.items()),
           flush=True)
 
 
-def test_repeat_runs_agree():
+def test_repeat_runs_agree_single_pass():
     """Atomic summation order may change between runs; results stay within tolerance of each other."""
     inp = I.make(I.CASES["sk16_t01"])
     o, m, l = P.oracle_stats(inp)
-    a = P.run_gpu(inp, o, m, l)
-    b = P.run_gpu(inp, o, m, l)
+    a = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_SINGLE_PASS)
+    b = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_SINGLE_PASS)
     for x, y in zip(a, b):
         P.assert_close("repeat", x.numpy(), y.numpy().astype(np.float64))
+
+
+def test_recompute_is_bitwise_reproducible():
+    """No atomics in the recompute form: repeated runs are bitwise identical."""
+    inp = I.make(I.custom_case("repro", 4, 128, I.MASK_CAUSAL, 210, [700, 333]))
+    o, m, l = P.oracle_stats(inp)
+    a = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_RECOMPUTE_DQ)
+    b = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_RECOMPUTE_DQ)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_algorithms_agree():
+    inp = I.make(I.custom_case("agree", 2, 64, I.MASK_NONE, 211, [400, 129]))
+    o, m, l = P.oracle_stats(inp)
+    a = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_RECOMPUTE_DQ)
+    b = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_SINGLE_PASS)
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])   # dK, dV: same kernel code path order
+    P.assert_close("dq", a[0].numpy(), b[0].numpy().astype(np.float64))
