@@ -31,6 +31,8 @@ def command(out: str = LIB) -> list:
             # packed fp32 VALU forms are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-munsafe-fp-atomics", "-Wno-unused-result",
+            # MFMA accumulators in VGPRs: the softmax reads S and dP without AGPR copies
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
             *SOURCES, "-o", out]
 

@@ -136,9 +136,9 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
       fa::fa_bwd_main<D, false, true><<<grid, dim3(256), 0, stream>>>(ma);
   } else {
     if (causal)
-      fa::fa_bwd_main<D, true, false><<<grid, dim3(256), 0, stream>>>(ma);
+      fa::fa_bwd_dkdv<D, true><<<grid, dim3(512), 0, stream>>>(ma);
     else
-      fa::fa_bwd_main<D, false, false><<<grid, dim3(256), 0, stream>>>(ma);
+      fa::fa_bwd_dkdv<D, false><<<grid, dim3(512), 0, stream>>>(ma);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return FA_BWD_ERR_HIP;

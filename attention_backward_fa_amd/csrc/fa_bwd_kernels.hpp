@@ -299,28 +299,22 @@ void fa_bwd_main(MainArgs a) {
     const bf16* sd = s_do + bi * C::TILE;
     const float* st = s_st + bi * 2 * BM;
     const int jrel = jcol - i0;  // causal: key j is visible from tile row r iff jrel <= r
-    // steps 1 and 3: S = Q K^T, dP = dO V^T  ([q 64] x [kv 32] per wave)
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = f32x16{};
-      dp[mt] = f32x16{};
-    }
     const int arow = tile_row(c) * QS + 8 * hh;
+    const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
+    // steps 1 and 3 for M-tile mt: S = Q K^T, dP = dO V^T  ([q 32] x [kv 32] per wave)
+    auto sdp = [&](int mt, f32x16& s, f32x16& dp) {
+      s = f32x16{};
+      dp = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < C::KSD; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int ks = 0; ks < C::KSD; ++ks) {
         const bf16x8 qa = *(const bf16x8*)(sq + arow + 32 * mt * QS + 16 * ks);
         const bf16x8 da = *(const bf16x8*)(sd + arow + 32 * mt * QS + 16 * ks);
-        s[mt] = mfma32x32x16(qa, kf[ks], s[mt]);
-        dp[mt] = mfma32x32x16(da, vf[ks], dp[mt]);
+        s = mfma32x32x16(qa, kf[ks], s);
+        dp = mfma32x32x16(da, vf[ks], dp);
       }
-    }
-    // steps 2 and 5: P = exp2(S*scale*log2e - lse2), dS = P (dP - D), both to bf16
-    bf16x8 pk[2][2], dsk[2][2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    };
+    // steps 2 and 5 for M-tile mt: P = exp2(S*scale*log2e - lse2), dS = P (dP - D), both to bf16
+    auto softmax_ds = [&](int mt, const f32x16& s, const f32x16& dp, bf16x8 (&pk)[2], bf16x8 (&dsk)[2]) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int mrow = 32 * mt + 8 * a4 + 4 * hh;  // MFMA row of bb = 0
@@ -329,40 +323,73 @@ void fa_bwd_main(MainArgs a) {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int j = 4 * a4 + bb;
-          float p = fast_exp2(s[mt][j] * a.scale_log2 - lse[bb]);
+          float p = fast_exp2(s[j] * a.scale_log2 - lse[bb]);
           if constexpr (CAUSAL) p = (jrel <= 32 * mt + tile_row(8 * a4 + 4 * hh + bb)) ? p : 0.f;
-          const float ds = p * (dp[mt][j] - dd[bb]);
-          pk[mt][j >> 3][j & 7] = to_bf16(p);
-          dsk[mt][j >> 3][j & 7] = to_bf16(ds);
+          const float ds = p * (dp[j] - dd[bb]);
+          pk[j >> 3][j & 7] = to_bf16(p);
+          dsk[j >> 3][j & 7] = to_bf16(ds);
         }
       }
-    }
-    // dS^T to LDS (for the dQ GEMM): row = this lane's key, 4 consecutive MFMA rows per store
+    };
+    // steps 7 and 6 for M-tile mt: dV += P^T dO, dK += dS^T Q (scale applied at write-back). The
+    // k-index e of the A operand is MFMA row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4;
+    // the transpose reads fetch the matching tile rows.
+    auto dvdk = [&](int mt, const bf16x8 (&pk)[2], const bf16x8 (&dsk)[2]) {
 #pragma unroll
-    for (int mt = 0; mt < 2 && WITH_DQ; ++mt) {
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const bf16x8 src = dsk[mt][a4 >> 1];
-        const int o4 = 4 * (a4 & 1);
-        const bf16x4 v4 = {src[o4], src[o4 + 1], src[o4 + 2], src[o4 + 3]};
-        *(bf16x4*)(s_dst + (32 * w + c) * SS + 32 * mt + 8 * a4 + 4 * hh) = v4;
-      }
-    }
-    // steps 7 and 6: dV += P^T dO, dK += dS^T Q (scale applied at write-back). The k-index e of
-    // the A operand is MFMA row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4; the
-    // transpose reads fetch the matching tile rows.
-    const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
-#pragma unroll
-    for (int nt = 0; nt < C::NTD; ++nt) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int nt = 0; nt < C::NTD; ++nt) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int o = brow + (32 * mt + 16 * s2) * QS + 32 * nt;
           const bf16x8 bdo = concat(lds_read_tr4(sd + o), lds_read_tr4(sd + o + 2 * QS));
           const bf16x8 bq = concat(lds_read_tr4(sq + o), lds_read_tr4(sq + o + 2 * QS));
-          accV[nt] = mfma32x32x16(pk[mt][s2], bdo, accV[nt]);
-          accK[nt] = mfma32x32x16(dsk[mt][s2], bq, accK[nt]);
+          accV[nt] = mfma32x32x16(pk[s2], bdo, accV[nt]);
+          accK[nt] = mfma32x32x16(dsk[s2], bq, accK[nt]);
+        }
+      }
+    };
+    // Software pipeline over the two M-tiles: the softmax of one M-tile runs on the VALU while
+    // the matrix cores work on the other's GEMMs.
+    f32x16 s0, dp0, s1, dp1;
+    bf16x8 pk0[2], dsk0[2], pk1[2], dsk1[2];
+    sdp(0, s0, dp0);
+    sdp(1, s1, dp1);
+    softmax_ds(0, s0, dp0, pk0, dsk0);
+    dvdk(0, pk0, dsk0);
+    softmax_ds(1, s1, dp1, pk1, dsk1);
+    dvdk(1, pk1, dsk1);
+    // interleave: [S/dP 0] [S/dP 1 | softmax 0] [dV/dK 0 | softmax 1] [dV/dK 1]
+#pragma unroll
+    for (int i = 0; i < C::KSD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+    }
+#pragma unroll
+    for (int i = 0; i < C::KSD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 112 / C::KSD, 0);  // softmax VALU
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * C::NTD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 112 / (2 * C::NTD), 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * C::NTD; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    // dS^T to LDS (for the dQ GEMM): row = this lane's key, 4 consecutive MFMA rows per store
+    if constexpr (WITH_DQ) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const bf16x8 src = (mt == 0 ? dsk0 : dsk1)[a4 >> 1];
+          const int o4 = 4 * (a4 & 1);
+          const bf16x4 v4 = {src[o4], src[o4 + 1], src[o4 + 2], src[o4 + 3]};
+          *(bf16x4*)(s_dst + (32 * w + c) * SS + 32 * mt + 8 * a4 + 4 * hh) = v4;
         }
       }
     }
@@ -449,7 +476,249 @@ void fa_bwd_main(MainArgs a) {
 }
 
 
+// ------------------------------------------------------------------ stage 2a': dK and dV, two waves per SIMD
+
+template <int D>
+struct DkdvCfg {
+  static constexpr int BN = 128;                 // kv rows per workgroup: 4 row groups of 32
+  static constexpr int BM = 64;                  // q rows per step
+  static constexpr int NW = 8;                   // waves: 4 row groups x 2 roles
+  static constexpr int KSD = D / 16;
+  static constexpr int NTD = D / 32;
+  static constexpr int QS = D + 8;
+  static constexpr int CPR = QS / 8;
+  static constexpr int TILE = BM * QS;
+  static constexpr int TILE_BYTES = TILE * 2;
+  static constexpr int NDMA = TILE_BYTES / 1024;
+  static constexpr int P_BYTES = 4 * 64 * 32 * 4;        // fp32 P of the 4 row groups, 32 values per lane
+  static constexpr int OFF_Q = 0;                        // Q [2][BM][QS]
+  static constexpr int OFF_DO = OFF_Q + 2 * TILE_BYTES;  // dO [2][BM][QS]
+  static constexpr int OFF_P = OFF_DO + 2 * TILE_BYTES;  // P exchange [group][16-byte chunk][lane]
+  static constexpr int OFF_ST = OFF_P + P_BYTES;         // [2 buffers][lse2, D][BM] fp32
+  static constexpr int LDS_BYTES = OFF_ST + 4 * BM * 4;
+  static_assert(TILE_BYTES % 1024 == 0, "a tile is a whole number of 1 KB transfers");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// dK and dV of one (kv tile, head, sequence). Eight waves: row group r = w % 4 owns kv rows
+// 32 r .. 32 r + 31; the wave with role 0 forms S = Q K^T, P and dV += P^T dO, the wave with
+// role 1 forms dP = dO V^T, dS = P (dP - D) with the P its partner passes through LDS, and
+// dK += dS^T Q. Each wave so holds one fp32 accumulator tile, two waves fit on a SIMD, and one's
+// softmax runs beside the other's MFMAs.
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkdv(MainArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = DkdvCfg<D>;
+  constexpr int BN = C::BN, BM = C::BM, QS = C::QS;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  bf16* s_q = (bf16*)(smem + C::OFF_Q);
+  bf16* s_do = (bf16*)(smem + C::OFF_DO);
+  float* s_st = (float*)(smem + C::OFF_ST);
+
+  const int HB = a.H * a.batch;
+  const int tile = blockIdx.x / HB;  // heavy (low) kv tiles of every head dispatch first
+  const int hb = blockIdx.x - tile * HB;
+  const int b = hb / a.H, h = hb - (hb / a.H) * a.H;
+  int64_t q_start, kv_start;
+  int Lq, Lk;
+  seq_of(a.cu_q, b, a.padded, a.max_seqlen_q, q_start, Lq);
+  seq_of(a.cu_kv, b, a.padded, a.max_seqlen_kv, kv_start, Lk);
+  Lq = clamp_len(q_start, Lq, a.total_q);
+  Lk = clamp_len(kv_start, Lk, a.total_kv);
+  const int kv0 = tile * BN;
+  if (kv0 >= Lk) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int grp = w & 3, role = w >> 2;
+  const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
+  const int64_t rs = (int64_t)a.H * D;
+  const int rsb = (int)(rs * 2);
+  const bf16* kb = a.k + (kv_start + kv0) * rs + (int64_t)h * D;
+  const bf16* vb = a.v + (kv_start + kv0) * rs + (int64_t)h * D;
+  const bf16* qb = a.q + q_start * rs + (int64_t)h * D;
+  const bf16* db = a.dout + q_start * rs + (int64_t)h * D;
+  const float* lse_b = a.lse2 + (int64_t)h * a.total_q + q_start;
+  const float* dd_b = a.dvec + (int64_t)h * a.total_q + q_start;
+
+  // B operand of this wave's first GEMM: K rows (role 0, for S) or V rows (role 1, for dP)
+  const int kv_rows = imin(Lk - kv0, BN);
+  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(role == 0 ? kb : vb, (int64_t)kv_rows * rsb);
+  bf16x8 bf[C::KSD];
+#pragma unroll
+  for (int ks = 0; ks < C::KSD; ++ks)
+    bf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rkv, (32 * grp + c) * rsb + (16 * ks + 8 * hh) * 2));
+  {  // zero the Q and dO buffers once: rows past the sequence then hold zeros or earlier valid rows
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int o = tid * 16; o < 4 * C::TILE_BYTES; o += 512 * 16) *(u32x4*)(smem + C::OFF_Q + o) = z;
+  }
+  __syncthreads();
+
+  f32x16 acc[C::NTD];  // dV (role 0) or dK / scale (role 1) of rows 32 grp .. 32 grp + 31
+#pragma unroll
+  for (int nt = 0; nt < C::NTD; ++nt) acc[nt] = f32x16{};
+
+  const int n_qt = (Lq + BM - 1) / BM;
+  int qt = CAUSAL ? kv0 / BM : 0;
+  const int jcol = kv0 + 32 * grp + c;  // this lane's key row (sequence-local)
+
+  constexpr int NJ = (C::NDMA + C::NW - 1) / C::NW;
+  int dma_off[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int p16 = 64 * (w + C::NW * jj) + lane;
+    const int r = p16 / C::CPR, ch = p16 % C::CPR;
+    dma_off[jj] = r * rsb + (ch < D / 8 ? ch : 0) * 16;
+  }
+  auto issue_tile = [&](int t, int bi) {
+    const int i0 = t * BM;
+    const int64_t bytes = (int64_t)imin(Lq - i0, BM) * rsb;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb + (int64_t)i0 * rs, bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(db + (int64_t)i0 * rs, bytes);
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int j = w + C::NW * jj;
+      if (j < C::NDMA) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rq, (__attribute__((address_space(3))) void*)(smem + C::OFF_Q + bi * C::TILE_BYTES + 1024 * j), 16,
+            dma_off[jj], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rd, (__attribute__((address_space(3))) void*)(smem + C::OFF_DO + bi * C::TILE_BYTES + 1024 * j), 16,
+            dma_off[jj], 0, 0, 0);
+      }
+    }
+  };
+  // row statistics of q tile t in MFMA row order: threads 0..63 lse2, 64..127 D; rows past the
+  // sequence get lse2 = +inf, so their P (and dS) is exactly 0 without a mask
+  auto load_stats = [&](int t) -> float {
+    const int mi = tid & (BM - 1);
+    const int r = t * BM + 32 * (mi >> 5) + tile_row(mi & 31);
+    if (tid >= 2 * BM) return 0.f;
+    if (r >= Lq) return tid < BM ? __builtin_inff() : 0.f;
+    return (tid < BM ? lse_b : dd_b)[r];
+  };
+  auto store_stats = [&](int bi, float v) {
+    if (tid < 2 * BM) s_st[bi * 2 * BM + tid] = v;
+  };
+  // P exchange: 16-byte chunk k of lane L of group grp at OFF_P + ((grp * 8 + k) * 64 + L) * 16
+  float* s_p = (float*)(smem + C::OFF_P) + (grp * 8 * 64 + lane) * 4;
+
+  int buf = 0;
+  if (qt < n_qt) {
+    issue_tile(qt, 0);
+    store_stats(0, load_stats(qt));
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+
+  const int arow = tile_row(c) * QS + 8 * hh;
+  const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
+  for (; qt < n_qt; ++qt, buf ^= 1) {
+    const bool has_next = qt + 1 < n_qt;
+    float st_next = 0.f;
+    if (has_next) {
+      issue_tile(qt + 1, buf ^ 1);
+      st_next = load_stats(qt + 1);
+    }
+    const int i0 = qt * BM;
+    const bf16* sq = s_q + buf * C::TILE;
+    const bf16* sd = s_do + buf * C::TILE;
+    const float* st = s_st + buf * 2 * BM;
+    // steps 1 (role 0) or 3 (role 1): S = Q K^T or dP = dO V^T, [q 64] x [kv 32] per wave
+    const bf16* ta = role == 0 ? sq : sd;
+    f32x16 x[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) x[mt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KSD; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 av = *(const bf16x8*)(ta + arow + 32 * mt * QS + 16 * ks);
+        x[mt] = mfma32x32x16(av, bf[ks], x[mt]);
+      }
+    }
+    bf16x8 opk[2][2];  // P (role 0) or dS (role 1) in bf16, the A operand of the second GEMM
+    if (role == 0) {
+      // step 2: P = exp2(S*scale*log2e - lse2) (causal entries with key > query are 0)
+      const int jrel = jcol - i0;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 lse = *(const f32x4*)(st + 32 * mt + 8 * a4 + 4 * hh);
+          f32x4 p4;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const int j = 4 * a4 + bb;
+            float p = fast_exp2(x[mt][j] * a.scale_log2 - lse[bb]);
+            if constexpr (CAUSAL) p = (jrel <= 32 * mt + tile_row(8 * a4 + 4 * hh + bb)) ? p : 0.f;
+            p4[bb] = p;
+            opk[mt][j >> 3][j & 7] = to_bf16(p);
+          }
+          *(f32x4*)(s_p + (4 * mt + a4) * 64 * 4) = p4;
+        }
+      }
+    }
+    __syncthreads();  // P of every row group visible
+    if (role == 1) {
+      // step 5: dS = P (dP - D) with the partner wave's fp32 P
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f32x4 dd = *(const f32x4*)(st + BM + 32 * mt + 8 * a4 + 4 * hh);
+          const f32x4 p4 = *(const f32x4*)(s_p + (4 * mt + a4) * 64 * 4);
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const int j = 4 * a4 + bb;
+            opk[mt][j >> 3][j & 7] = to_bf16(p4[bb] * (x[mt][j] - dd[bb]));
+          }
+        }
+      }
+    }
+    // steps 7 (role 0) and 6 (role 1): dV += P^T dO, dK += dS^T Q. The k-index e of the A
+    // operand is MFMA row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4; the transpose
+    // reads fetch the matching tile rows.
+    const bf16* tb = role == 0 ? sd : sq;
+#pragma unroll
+    for (int nt = 0; nt < C::NTD; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int o = brow + (32 * mt + 16 * s2) * QS + 32 * nt;
+          const bf16x8 bt = concat(lds_read_tr4(tb + o), lds_read_tr4(tb + o + 2 * QS));
+          acc[nt] = mfma32x32x16(opk[mt][s2], bt, acc[nt]);
+        }
+      }
+    }
+    if (has_next) store_stats(buf ^ 1, st_next);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next tile's LDS-DMA has landed
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  }
+
+  // write-back: role 0 dV, role 1 dK = scale * acc, bf16, rows 32 grp .. 32 grp + 31
+  bf16* out = role == 0 ? a.dv : a.dk;
+  const float osc = role == 0 ? 1.f : a.scale;
+#pragma unroll
+  for (int nt = 0; nt < C::NTD; ++nt) {
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int r = kv0 + 32 * grp + 8 * a4 + 4 * hh + bb;
+        if (r < Lk) out[(kv_start + r) * rs + (int64_t)h * D + 32 * nt + c] = to_bf16(acc[nt][4 * a4 + bb] * osc);
+      }
+    }
+  }
+#endif
+}
+
 // ------------------------------------------------------------------ stage 2b: dQ by recompute
+
 
 template <int D>
 struct DqCfg {
@@ -473,7 +742,7 @@ struct DqCfg {
 // dP^T = V dO^T with the forward's statistics (steps 1-5 of the per-tile math), and
 // accumulates dQ^T = K^T dS^T (step 8) in registers; dQ is written once, in bf16.
 template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = DqCfg<D>;
