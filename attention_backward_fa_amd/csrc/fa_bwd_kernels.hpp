@@ -481,8 +481,8 @@ void fa_bwd_main(MainArgs a) {
 template <int D>
 struct DkdvCfg {
   static constexpr int BN = 128;                 // kv rows per workgroup: 4 row groups of 32
-  static constexpr int BM = 64;                  // q rows per step
-  static constexpr int NW = 8;                   // waves: 4 row groups x 2 roles
+  static constexpr int BM = 64;                  // q rows per step: 2 M-tiles of 32
+  static constexpr int NW = 8;                   // waves: 4 row groups x 2 M-tiles
   static constexpr int KSD = D / 16;
   static constexpr int NTD = D / 32;
   static constexpr int QS = D + 8;
@@ -490,21 +490,23 @@ struct DkdvCfg {
   static constexpr int TILE = BM * QS;
   static constexpr int TILE_BYTES = TILE * 2;
   static constexpr int NDMA = TILE_BYTES / 1024;
-  static constexpr int P_BYTES = 4 * 64 * 32 * 4;        // fp32 P of the 4 row groups, 32 values per lane
+  static constexpr int X_BYTES = 4 * 2 * 2 * 64 * 16;    // bf16 P / dS halves: [group][M-tile][chunk][lane]
   static constexpr int OFF_Q = 0;                        // Q [2][BM][QS]
   static constexpr int OFF_DO = OFF_Q + 2 * TILE_BYTES;  // dO [2][BM][QS]
-  static constexpr int OFF_P = OFF_DO + 2 * TILE_BYTES;  // P exchange [group][16-byte chunk][lane]
-  static constexpr int OFF_ST = OFF_P + P_BYTES;         // [2 buffers][lse2, D][BM] fp32
+  static constexpr int OFF_X = OFF_DO + 2 * TILE_BYTES;  // exchange of P (M-tile 1) and dS (M-tile 0)
+  static constexpr int OFF_ST = OFF_X + X_BYTES;         // [2 buffers][lse2, D][BM] fp32
   static constexpr int LDS_BYTES = OFF_ST + 4 * BM * 4;
   static_assert(TILE_BYTES % 1024 == 0, "a tile is a whole number of 1 KB transfers");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget (one 8-wave workgroup per CU)");
 };
 
 // dK and dV of one (kv tile, head, sequence). Eight waves: row group r = w % 4 owns kv rows
-// 32 r .. 32 r + 31; the wave with role 0 forms S = Q K^T, P and dV += P^T dO, the wave with
-// role 1 forms dP = dO V^T, dS = P (dP - D) with the P its partner passes through LDS, and
-// dK += dS^T Q. Each wave so holds one fp32 accumulator tile, two waves fit on a SIMD, and one's
-// softmax runs beside the other's MFMAs.
+// 32 r .. 32 r + 31, and the two waves of a group each take one 32-row M-tile mt = w / 4 of the
+// 64-row q step: both form S = Q K^T, dP = dO V^T, P and dS for their M-tile (steps 1-5). The
+// wave of M-tile 0 then accumulates dV += P^T dO over the whole q step, the other dK += dS^T Q;
+// each passes the bf16 half its partner needs (dS of M-tile 0, P of M-tile 1) through LDS.
+// Each wave so holds one fp32 accumulator tile, two waves fit on a SIMD, and one's softmax runs
+// beside the other's MFMAs.
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv(MainArgs a) {
@@ -531,7 +533,7 @@ void fa_bwd_dkdv(MainArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int grp = w & 3, role = w >> 2;
+  const int grp = w & 3, mt = w >> 2;  // kv row group; M-tile of steps 1-5; 0: dV wave, 1: dK wave
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
   const int64_t rs = (int64_t)a.H * D;
   const int rsb = (int)(rs * 2);
@@ -542,20 +544,24 @@ void fa_bwd_dkdv(MainArgs a) {
   const float* lse_b = a.lse2 + (int64_t)h * a.total_q + q_start;
   const float* dd_b = a.dvec + (int64_t)h * a.total_q + q_start;
 
-  // B operand of this wave's first GEMM: K rows (role 0, for S) or V rows (role 1, for dP)
+  // K and V rows 32 grp + c as B operands of S = Q K^T and dP = dO V^T
   const int kv_rows = imin(Lk - kv0, BN);
-  const __amdgpu_buffer_rsrc_t rkv = make_rsrc(role == 0 ? kb : vb, (int64_t)kv_rows * rsb);
-  bf16x8 bf[C::KSD];
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (int64_t)kv_rows * rsb);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (int64_t)kv_rows * rsb);
+  bf16x8 kf[C::KSD], vf[C::KSD];
 #pragma unroll
-  for (int ks = 0; ks < C::KSD; ++ks)
-    bf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rkv, (32 * grp + c) * rsb + (16 * ks + 8 * hh) * 2));
+  for (int ks = 0; ks < C::KSD; ++ks) {
+    const int off = (32 * grp + c) * rsb + (16 * ks + 8 * hh) * 2;
+    kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+    vf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
+  }
   {  // zero the Q and dO buffers once: rows past the sequence then hold zeros or earlier valid rows
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int o = tid * 16; o < 4 * C::TILE_BYTES; o += 512 * 16) *(u32x4*)(smem + C::OFF_Q + o) = z;
   }
   __syncthreads();
 
-  f32x16 acc[C::NTD];  // dV (role 0) or dK / scale (role 1) of rows 32 grp .. 32 grp + 31
+  f32x16 acc[C::NTD];  // dV (M-tile 0 wave) or dK / scale (M-tile 1 wave) of rows 32 grp .. +31
 #pragma unroll
   for (int nt = 0; nt < C::NTD; ++nt) acc[nt] = f32x16{};
 
@@ -601,8 +607,8 @@ void fa_bwd_dkdv(MainArgs a) {
   auto store_stats = [&](int bi, float v) {
     if (tid < 2 * BM) s_st[bi * 2 * BM + tid] = v;
   };
-  // P exchange: 16-byte chunk k of lane L of group grp at OFF_P + ((grp * 8 + k) * 64 + L) * 16
-  float* s_p = (float*)(smem + C::OFF_P) + (grp * 8 * 64 + lane) * 4;
+  // exchange slot of 16-byte chunk k for M-tile m of this group, this lane
+  auto xslot = [&](int m, int k) { return (bf16x8*)(smem + C::OFF_X) + ((grp * 2 + m) * 2 + k) * 64 + lane; };
 
   int buf = 0;
   if (qt < n_qt) {
@@ -612,7 +618,7 @@ void fa_bwd_dkdv(MainArgs a) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
 
-  const int arow = tile_row(c) * QS + 8 * hh;
+  const int arow = (32 * mt + tile_row(c)) * QS + 8 * hh;
   const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
   for (; qt < n_qt; ++qt, buf ^= 1) {
     const bool has_next = qt + 1 < n_qt;
@@ -624,72 +630,58 @@ void fa_bwd_dkdv(MainArgs a) {
     const int i0 = qt * BM;
     const bf16* sq = s_q + buf * C::TILE;
     const bf16* sd = s_do + buf * C::TILE;
-    const float* st = s_st + buf * 2 * BM;
-    // steps 1 (role 0) or 3 (role 1): S = Q K^T or dP = dO V^T, [q 64] x [kv 32] per wave
-    const bf16* ta = role == 0 ? sq : sd;
-    f32x16 x[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) x[mt] = f32x16{};
+    const float* st = s_st + buf * 2 * BM + 32 * mt;
+    // steps 1 and 3 for this wave's M-tile: S = Q K^T, dP = dO V^T  ([q 32] x [kv 32])
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KSD; ++ks) {
+      const bf16x8 qa = *(const bf16x8*)(sq + arow + 16 * ks);
+      const bf16x8 da = *(const bf16x8*)(sd + arow + 16 * ks);
+      s = mfma32x32x16(qa, kf[ks], s);
+      dp = mfma32x32x16(da, vf[ks], dp);
+    }
+    // steps 2 and 5: P = exp2(S*scale*log2e - lse2) (causal: 0 where key > query), dS = P (dP - D)
+    const int jrel = jcol - i0 - 32 * mt;  // key j visible from M-tile row r iff jrel <= r
+    bf16x8 pk[2], dsk[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 av = *(const bf16x8*)(ta + arow + 32 * mt * QS + 16 * ks);
-        x[mt] = mfma32x32x16(av, bf[ks], x[mt]);
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const f32x4 lse = *(const f32x4*)(st + 8 * a4 + 4 * hh);
+      const f32x4 dd = *(const f32x4*)(st + BM + 8 * a4 + 4 * hh);
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int j = 4 * a4 + bb;
+        float p = fast_exp2(s[j] * a.scale_log2 - lse[bb]);
+        if constexpr (CAUSAL) p = (jrel <= tile_row(8 * a4 + 4 * hh + bb)) ? p : 0.f;
+        pk[j >> 3][j & 7] = to_bf16(p);
+        dsk[j >> 3][j & 7] = to_bf16(p * (dp[j] - dd[bb]));
       }
     }
-    bf16x8 opk[2][2];  // P (role 0) or dS (role 1) in bf16, the A operand of the second GEMM
-    if (role == 0) {
-      // step 2: P = exp2(S*scale*log2e - lse2) (causal entries with key > query are 0)
-      const int jrel = jcol - i0;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 lse = *(const f32x4*)(st + 32 * mt + 8 * a4 + 4 * hh);
-          f32x4 p4;
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const int j = 4 * a4 + bb;
-            float p = fast_exp2(x[mt][j] * a.scale_log2 - lse[bb]);
-            if constexpr (CAUSAL) p = (jrel <= 32 * mt + tile_row(8 * a4 + 4 * hh + bb)) ? p : 0.f;
-            p4[bb] = p;
-            opk[mt][j >> 3][j & 7] = to_bf16(p);
-          }
-          *(f32x4*)(s_p + (4 * mt + a4) * 64 * 4) = p4;
-        }
-      }
-    }
-    __syncthreads();  // P of every row group visible
-    if (role == 1) {
-      // step 5: dS = P (dP - D) with the partner wave's fp32 P
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 dd = *(const f32x4*)(st + BM + 32 * mt + 8 * a4 + 4 * hh);
-          const f32x4 p4 = *(const f32x4*)(s_p + (4 * mt + a4) * 64 * 4);
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const int j = 4 * a4 + bb;
-            opk[mt][j >> 3][j & 7] = to_bf16(p4[bb] * (x[mt][j] - dd[bb]));
-          }
-        }
-      }
-    }
-    // steps 7 (role 0) and 6 (role 1): dV += P^T dO, dK += dS^T Q. The k-index e of the A
-    // operand is MFMA row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4; the transpose
-    // reads fetch the matching tile rows.
-    const bf16* tb = role == 0 ? sd : sq;
+    // pass the half the partner needs: dS of M-tile 0 to the dK wave, P of M-tile 1 to the dV wave
+    // (selects on the wave-uniform mt; no runtime indexing, so everything stays in registers)
+    const bool v_wave = mt == 0;
+    *xslot(mt, 0) = v_wave ? dsk[0] : pk[0];
+    *xslot(mt, 1) = v_wave ? dsk[1] : pk[1];
+    __syncthreads();  // exchange visible
+    const bf16x8 own0 = v_wave ? pk[0] : dsk[0], own1 = v_wave ? pk[1] : dsk[1];
+    const bf16x8 oth0 = *xslot(1 - mt, 0), oth1 = *xslot(1 - mt, 1);
+    bf16x8 opk[2][2];  // A operands of the second GEMM, per M-tile and k-step
+    opk[0][0] = v_wave ? own0 : oth0;
+    opk[0][1] = v_wave ? own1 : oth1;
+    opk[1][0] = v_wave ? oth0 : own0;
+    opk[1][1] = v_wave ? oth1 : own1;
+    // steps 7 (M-tile 0 wave) and 6 (M-tile 1 wave): dV += P^T dO, dK += dS^T Q over both M-tiles.
+    // The k-index e of the A operand is MFMA row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4;
+    // the transpose reads fetch the matching tile rows.
+    const bf16* tb = mt == 0 ? sd : sq;
 #pragma unroll
     for (int nt = 0; nt < C::NTD; ++nt) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int m2 = 0; m2 < 2; ++m2) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const int o = brow + (32 * mt + 16 * s2) * QS + 32 * nt;
+          const int o = brow + (32 * m2 + 16 * s2) * QS + 32 * nt;
           const bf16x8 bt = concat(lds_read_tr4(tb + o), lds_read_tr4(tb + o + 2 * QS));
-          acc[nt] = mfma32x32x16(opk[mt][s2], bt, acc[nt]);
+          acc[nt] = mfma32x32x16(opk[m2][s2], bt, acc[nt]);
         }
       }
     }
@@ -700,9 +692,9 @@ void fa_bwd_dkdv(MainArgs a) {
     __syncthreads();
   }
 
-  // write-back: role 0 dV, role 1 dK = scale * acc, bf16, rows 32 grp .. 32 grp + 31
-  bf16* out = role == 0 ? a.dv : a.dk;
-  const float osc = role == 0 ? 1.f : a.scale;
+  // write-back: M-tile 0 wave dV, M-tile 1 wave dK = scale * acc, bf16, rows 32 grp .. 32 grp + 31
+  bf16* out = mt == 0 ? a.dv : a.dk;
+  const float osc = mt == 0 ? 1.f : a.scale;
 #pragma unroll
   for (int nt = 0; nt < C::NTD; ++nt) {
 #pragma unroll
