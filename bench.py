@@ -41,7 +41,7 @@ ALGORITHMS = {"default": 0, "single-pass": 1, "recompute": 2}
 # share of the 5-GEMM algorithmic FLOPs each kernel runs itself (S, dP, dV, dK, dQ are 2*Lq*Lk*d each)
 KERNEL_SHARE = {
     1: {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_dq_cast": 0.0},
-    2: {"fa_bwd_pre": 0.0, "fa_bwd_main": 0.8, "fa_bwd_dq": 0.6},
+    2: {"fa_bwd_pre": 0.0, "fa_bwd_dkdv": 0.8, "fa_bwd_dq": 0.6},
 }
 
 
@@ -116,6 +116,58 @@ def make_workload(name: str, device):
     return inp, dev
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_bwd_traffic_causal_s8192_h32_d128.md")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources and the build script (sorted by name)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "attention_backward_fa_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".hpp", ".h")))
+    files += [os.path.join(ROOT, "include", "fa_bwd.h"), os.path.join(ROOT, "attention_backward_fa_amd", "build.py")]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str, workload: str, algorithm: int):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+    when the summary is absent, covers another kernel/workload/algorithm, or was
+    taken on kernel sources other than the current ones."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                rec[k.strip("`")] = v.strip().strip("`")
+    try:
+        ok = (rec["kernel"] == kernel and rec["workload"] == workload and int(rec["algorithm"]) == algorithm
+              and rec["source_sha256"] == kernel_source_hash())
+        return float(rec["traffic_bytes_per_launch"]) if ok else None
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int, device) -> None:
+    """Counter calibration for rocprofv3 --pmc runs: three launches of torch's
+    elementwise negation over `mib` MiB of fp32 (reads and writes exactly mib MiB
+    each), so FETCH_SIZE / WRITE_SIZE of a kernel of known traffic can be read."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: 3 x neg over {mib} MiB read + {mib} MiB written", file=sys.stderr, flush=True)
+    del src, dst
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -162,12 +214,14 @@ def cpu_baseline(inp, dev, target_s: float = 15.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--algorithm", choices=list(ALGORITHMS), default="default")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run a known-traffic elementwise kernel over MIB MiB (for --pmc counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -182,6 +236,8 @@ def main():
         sys.exit(1)
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+    if args.calibrate_copy > 0:
+        copy_calibration(args.calibrate_copy, device)
     print(f"[bench] preparing workload {args.workload}", file=sys.stderr, flush=True)
     inp, dev = make_workload(args.workload, device)
     flops = algorithmic_flops(inp)
@@ -237,7 +293,7 @@ def main():
         "kernels_ms": {n: round(v, 5) for n, v in kern_ms.items()},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "work_flops": dom_flops},
+                     "traffic": recorded_traffic(dom, args.workload, algo_used), "work_flops": dom_flops},
         "outputs_finite": finite,
     }
     if not args.no_cpu_baseline:

@@ -2,4 +2,5 @@
 from .attention import (  # noqa: F401
     MASK_CAUSAL, MASK_NONE, MASK_PADDING, MASK_PADDING_CAUSAL, backward, backward_head,
     backward_rows, forward, forward_head, is_causal, is_padded, loss, segments, valid_rows, visible,
+    visible_block,
 )

@@ -68,13 +68,19 @@ def segments(cu, mask: int, max_seqlen: int):
     return out
 
 
-def visible(lq: int, lk: int, causal: bool) -> np.ndarray:
-    """Boolean [lq, lk]: may query i attend to key j (sequence-local indices)."""
-    i = np.arange(lq)[:, None]
-    j = np.arange(lk)[None, :]
+def visible_block(rows, cols, causal: bool) -> np.ndarray:
+    """Boolean [len(rows), len(cols)]: may query rows[a] attend to key cols[b]
+    (sequence-local indices; causal: key j visible from query i iff j <= i)."""
+    i = np.asarray(rows)[:, None]
+    j = np.asarray(cols)[None, :]
     if causal:
         return j <= i
-    return np.ones((lq, lk), dtype=bool)
+    return np.ones((i.shape[0], j.shape[1]), dtype=bool)
+
+
+def visible(lq: int, lk: int, causal: bool) -> np.ndarray:
+    """Boolean [lq, lk]: visibility of every (query, key) pair of one sequence."""
+    return visible_block(np.arange(lq), np.arange(lk), causal)
 
 
 def _f64(x) -> np.ndarray:
@@ -184,7 +190,7 @@ def backward_rows(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int, b:
     M, L = _f64(m[qs:qs + lq, h]), _f64(l[qs:qs + lq, h])
     dq_out, dk_out, dv_out = [], [], []
     for i in q_rows:
-        vis = visible(lq, lk, causal)[i:i + 1]
+        vis = visible_block([i], np.arange(lk), causal)
         s = (Q[i:i + 1] @ K.T)
         p = softmax_probs(scale * s, M[i:i + 1], L[i:i + 1], vis)
         dp = dO[i:i + 1] @ V.T
@@ -194,7 +200,7 @@ def backward_rows(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int, b:
     if len(kv_rows):
         dvec_all = np.sum(O * dO, axis=1)
     for j in kv_rows:
-        vis = visible(lq, lk, causal)[:, j:j + 1]
+        vis = visible_block(np.arange(lq), [j], causal)
         s = Q @ K[j:j + 1].T
         p = softmax_probs(scale * s, M, L, vis)
         dp = dO @ V[j:j + 1].T

@@ -362,7 +362,7 @@ def test_planted_mistake_fails_finite_differences(monkeypatch, func, old, new, w
 def test_planted_mask_mistake_fails_torch_check(monkeypatch, old, new, what):
     p = make_problem(MASK_CAUSAL, [6, 5], [6, 5], heads=1, d=4, seed=22)
     assert torch_error(p) < 1e-12
-    _mutant(monkeypatch, "visible", old, new)
+    _mutant(monkeypatch, "visible_block", old, new)
     assert torch_error(p) > 1e-3, what
 
 
