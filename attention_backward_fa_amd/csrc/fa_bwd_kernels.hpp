@@ -1,17 +1,21 @@
-// fa_bwd_kernels.hpp -- the three device stages of the single-pass attention
-// backward on gfx950:
+// fa_bwd_kernels.hpp -- device code of the attention backward on gfx950.
 //   fa_bwd_pre     per (token, head) row: D = rowsum(O*dO) (step 4 of the
 //                  PyPTO-Gym SK-16 article's per-tile math, section 3.1),
 //                  the base-2 log-sum-exp of the forward's (m, l), a zeroed
-//                  fp32 dQ accumulator row, and zeroed dK/dV rows outside
-//                  every sequence. HBM bound.
-//   fa_bwd_main    one workgroup per (kv tile, head, sequence): keeps the
-//                  tile's K, V and its fp32 dK, dV accumulators in registers,
-//                  streams the q tiles through LDS and runs the five GEMMs of
-//                  steps 1, 3, 6, 7, 8 on bf16 MFMA with the softmax
-//                  recompute and dS (steps 2, 5) on the VALU; dQ partial sums
-//                  go to the fp32 accumulator with global atomics. MFMA bound.
-//   fa_bwd_dq_cast dQ = bf16(scale * accumulator). HBM bound.
+//                  fp32 dQ accumulator row (single-pass form), and zeroed
+//                  dQ/dK/dV rows outside every sequence. HBM bound.
+//   fa_bwd_main    single-pass form, one workgroup per (kv tile, head,
+//                  sequence): keeps the tile's K, V and its fp32 dK, dV
+//                  accumulators in registers, streams the q tiles through LDS
+//                  and runs the five GEMMs of steps 1, 3, 6, 7, 8 on bf16 MFMA
+//                  with the softmax recompute and dS (steps 2, 5) on the VALU;
+//                  dQ partial sums go to the fp32 accumulator with global
+//                  atomics.
+//   fa_bwd_dq_cast single-pass form: dQ = bf16(scale * accumulator). HBM bound.
+//   fa_bwd_dkdv    recompute form, kv-outer: steps 1-3 and 5-7 with two
+//                  waves per SIMD; dK, dV written once per kv tile.
+//   fa_bwd_dq      recompute form, q-outer: recomputes S^T and dP^T and
+//                  accumulates dQ (step 8) in registers; no atomics.
 #pragma once
 #include <type_traits>
 
