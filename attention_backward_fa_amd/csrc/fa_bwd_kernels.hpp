@@ -637,12 +637,24 @@ void fa_bwd_dkdv(MainArgs a) {
     const float* st = s_st + buf * 2 * BM + 32 * mt;
     // steps 1 and 3 for this wave's M-tile: S = Q K^T, dP = dO V^T  ([q 32] x [kv 32])
     f32x16 s = f32x16{}, dp = f32x16{};
+    {
+      constexpr int PF = 2;
+      bf16x8 qa[C::KSD], da[C::KSD];
 #pragma unroll
-    for (int ks = 0; ks < C::KSD; ++ks) {
-      const bf16x8 qa = *(const bf16x8*)(sq + arow + 16 * ks);
-      const bf16x8 da = *(const bf16x8*)(sd + arow + 16 * ks);
-      s = mfma32x32x16(qa, kf[ks], s);
-      dp = mfma32x32x16(da, vf[ks], dp);
+      for (int ks = 0; ks < PF; ++ks) {
+        qa[ks] = *(const bf16x8*)(sq + arow + 16 * ks);
+        da[ks] = *(const bf16x8*)(sd + arow + 16 * ks);
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::KSD; ++ks) {
+        if (ks + PF < C::KSD) {
+          qa[ks + PF] = *(const bf16x8*)(sq + arow + 16 * (ks + PF));
+          da[ks + PF] = *(const bf16x8*)(sd + arow + 16 * (ks + PF));
+        }
+        s = mfma32x32x16(qa[ks], kf[ks], s);
+        dp = mfma32x32x16(da[ks], vf[ks], dp);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // steps 2 and 5: P = exp2(S*scale*log2e - lse2) (causal: 0 where key > query), dS = P (dP - D)
     const int jrel = jcol - i0 - 32 * mt;  // key j visible from M-tile row r iff jrel <= r
@@ -677,16 +689,23 @@ void fa_bwd_dkdv(MainArgs a) {
     // The k-index e of the A operand is MFMA row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4;
     // the transpose reads fetch the matching tile rows.
     const bf16* tb = mt == 0 ? sd : sq;
+    {
+      constexpr int NB = 4 * C::NTD, PF = 3;
+      bf16x8 bt[NB];
+      auto bt_load = [&](int i) {
+        const int ksi = i / C::NTD, nt = i % C::NTD;  // ksi = 2 m2 + s2
+        const int o = brow + 16 * ksi * QS + 32 * nt;
+        return concat(lds_read_tr4(tb + o), lds_read_tr4(tb + o + 2 * QS));
+      };
 #pragma unroll
-    for (int nt = 0; nt < C::NTD; ++nt) {
+      for (int i = 0; i < PF; ++i) bt[i] = bt_load(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int o = brow + (32 * m2 + 16 * s2) * QS + 32 * nt;
-          const bf16x8 bt = concat(lds_read_tr4(tb + o), lds_read_tr4(tb + o + 2 * QS));
-          acc[nt] = mfma32x32x16(opk[m2][s2], bt, acc[nt]);
-        }
+      for (int i = 0; i < NB; ++i) {
+        if (i + PF < NB) bt[i + PF] = bt_load(i + PF);
+        const int ksi = i / C::NTD, nt = i % C::NTD;
+        acc[nt] = mfma32x32x16(opk[ksi >> 1][ksi & 1], bt[i], acc[nt]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (has_next) store_stats(buf ^ 1, st_next);
@@ -844,14 +863,27 @@ void fa_bwd_dq(MainArgs a) {
       s[mt] = f32x16{};
       dp[mt] = f32x16{};
     }
+    {  // operands read PF k-steps ahead into distinct registers, one scheduling fence per k-step
+      constexpr int PF = 2;
+      bf16x8 ka[C::KSD][2], va[C::KSD][2];
+      auto ld = [&](int ks) {
 #pragma unroll
-    for (int ks = 0; ks < C::KSD; ++ks) {
+        for (int mt = 0; mt < 2; ++mt) {
+          ka[ks][mt] = *(const bf16x8*)(sk + arow + 32 * mt * QS + 16 * ks);
+          va[ks][mt] = *(const bf16x8*)(sv + arow + 32 * mt * QS + 16 * ks);
+        }
+      };
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 ka = *(const bf16x8*)(sk + arow + 32 * mt * QS + 16 * ks);
-        const bf16x8 va = *(const bf16x8*)(sv + arow + 32 * mt * QS + 16 * ks);
-        s[mt] = mfma32x32x16(ka, qf[ks], s[mt]);
-        dp[mt] = mfma32x32x16(va, df[ks], dp[mt]);
+      for (int ks = 0; ks < PF; ++ks) ld(ks);
+#pragma unroll
+      for (int ks = 0; ks < C::KSD; ++ks) {
+        if (ks + PF < C::KSD) ld(ks + PF);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          s[mt] = mfma32x32x16(ka[ks][mt], qf[ks], s[mt]);
+          dp[mt] = mfma32x32x16(va[ks][mt], df[ks], dp[mt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // steps 2 and 5: P = exp2(S*scale*log2e - lse2), dS = P (dP - D); key row j = t*BK + kv row.
@@ -871,18 +903,27 @@ void fa_bwd_dq(MainArgs a) {
         }
       }
     }
-    // step 8, transposed: dQ^T += K^T dS^T. The k-index e of dS^T is kv MFMA row
-    // 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4; the transpose reads fetch those K rows.
+    // step 8, transposed: dQ^T += K^T dS^T. k-step ksi = 2 mt + s2: its k-index e is kv MFMA row
+    // 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4 of M-tile mt; the transpose reads fetch
+    // those K rows. k-steps run outside the NTD independent accumulators; A operands are read PF
+    // MFMAs ahead.
+    {
+      constexpr int NB = 4 * C::NTD, PF = 3;
+      bf16x8 kt[NB];
+      auto kt_load = [&](int i) {
+        const int ksi = i / C::NTD, nt = i % C::NTD;
+        const int o = brow + 16 * ksi * QS + 32 * nt;
+        return concat(lds_read_tr4(sk + o), lds_read_tr4(sk + o + 2 * QS));
+      };
 #pragma unroll
-    for (int nt = 0; nt < C::NTD; ++nt) {
+      for (int i = 0; i < PF; ++i) kt[i] = kt_load(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int o = brow + (32 * mt + 16 * s2) * QS + 32 * nt;
-          const bf16x8 kt = concat(lds_read_tr4(sk + o), lds_read_tr4(sk + o + 2 * QS));
-          acc[nt] = mfma32x32x16(kt, dsk[mt][s2], acc[nt]);
-        }
+      for (int i = 0; i < NB; ++i) {
+        if (i + PF < NB) kt[i + PF] = kt_load(i + PF);
+        const int ksi = i / C::NTD, nt = i % C::NTD;
+        acc[nt] = mfma32x32x16(kt[i], dsk[ksi >> 1][ksi & 1], acc[nt]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);

@@ -89,5 +89,7 @@ def test_algorithms_agree():
     o, m, l = P.oracle_stats(inp)
     a = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_RECOMPUTE_DQ)
     b = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_SINGLE_PASS)
-    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])   # dK, dV: same kernel code path order
-    P.assert_close("dq", a[0].numpy(), b[0].numpy().astype(np.float64))
+    # the two forms sum in different orders (dQ atomics vs owned rows; token order inside the MFMA
+    # k-steps), so they agree to rounding, not bitwise
+    for name, x, y in zip(("dq", "dk", "dv"), a, b):
+        P.assert_close(name, x.numpy(), y.numpy().astype(np.float64))
