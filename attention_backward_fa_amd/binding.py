@@ -32,8 +32,8 @@ FA_BWD_MASK_CAUSAL = 2
 FA_BWD_MASK_PADDING_CAUSAL = 3
 
 # every symbol include/fa_bwd.h declares
-EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_destroy", "fa_bwd_status_string", "fa_bwd_get_desc",
-            "fa_bwd_profile_enable", "fa_bwd_profile_collect")
+EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_fwd_run", "fa_bwd_destroy", "fa_bwd_status_string",
+            "fa_bwd_get_desc", "fa_bwd_profile_enable", "fa_bwd_profile_collect")
 
 
 class FaBwdDesc(ctypes.Structure):
@@ -58,6 +58,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_create.restype = i32
     lib.fa_bwd_run.argtypes = [vp] * 10 + [f32, i32] + [vp] * 4
     lib.fa_bwd_run.restype = i32
+    lib.fa_fwd_run.argtypes = [vp] * 6 + [f32, i32] + [vp] * 4
+    lib.fa_fwd_run.restype = i32
     lib.fa_bwd_destroy.argtypes = [vp]
     lib.fa_bwd_destroy.restype = i32
     lib.fa_bwd_status_string.argtypes = [i32]
@@ -151,6 +153,33 @@ def fa_bwd_run(handle, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scal
     _check(st, "fa_bwd_run")
 
 
+def fa_fwd_run(handle, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, mask: int, o, m, l,
+               stream=None) -> None:
+    """Enqueue the forward (O, m, l for the backward) on ``stream`` (default: torch's current stream).
+
+    Tensors: q, o bf16 [total_q, H, d]; k, v bf16 [total_kv, H, d]; m, l fp32 [total_q, H] (written);
+    cu_seqlens_* int32 [batch + 1]; all on one GPU.
+    """
+    import torch
+    d = fa_bwd_get_desc(handle)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(f"q: expected a GPU tensor, got device {dev}")
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    qs = (d.total_q, d.num_heads, d.head_dim)
+    ks = (d.total_kv, d.num_heads, d.head_dim)
+    ptrs = [
+        _expect(q, "q", qs, bf, dev), _expect(k, "k", ks, bf, dev), _expect(v, "v", ks, bf, dev),
+        _expect(cu_seqlens_q, "cu_seqlens_q", (d.batch + 1,), i32, dev),
+        _expect(cu_seqlens_kv, "cu_seqlens_kv", (d.batch + 1,), i32, dev),
+    ]
+    outs = [_expect(o, "o", qs, bf, dev), _expect(m, "m", qs[:2], f32, dev), _expect(l, "l", qs[:2], f32, dev)]
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = load_library().fa_fwd_run(handle, *ptrs, ctypes.c_float(scale), int(mask), *outs, ctypes.c_void_p(stream))
+    _check(st, "fa_fwd_run")
+
+
 def fa_bwd_profile_enable(handle, enable: bool) -> None:
     _check(load_library().fa_bwd_profile_enable(handle, 1 if enable else 0), "fa_bwd_profile_enable")
 
@@ -180,6 +209,14 @@ class FaBwd:
         fa_bwd_run(self.handle, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, stream)
         return dq, dk, dv
 
+    def forward(self, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o=None, m=None, l=None, stream=None):
+        import torch
+        o = torch.empty_like(q) if o is None else o
+        m = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if m is None else m
+        l = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if l is None else l
+        fa_fwd_run(self.handle, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o, m, l, stream)
+        return o, m, l
+
     def close(self):
         if self.handle is not None and self.handle.value:
             fa_bwd_destroy(self.handle)
@@ -198,3 +235,11 @@ def attention_backward(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scal
     with FaBwd(cu_seqlens_q.numel() - 1, q.shape[1], q.shape[2], max_seqlen_q, max_seqlen_kv,
                q.shape[0], k.shape[0], algorithm) as op:
         return op.run(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask)
+
+
+def attention_forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, mask: int, max_seqlen_q: int,
+                      max_seqlen_kv: int):
+    """One-shot forward: returns O (bf16), m, l (fp32) on q's device."""
+    with FaBwd(cu_seqlens_q.numel() - 1, q.shape[1], q.shape[2], max_seqlen_q, max_seqlen_kv,
+               q.shape[0], k.shape[0]) as op:
+        return op.forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask)

@@ -160,6 +160,75 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   return FA_BWD_OK;
 }
 
+template <int D>
+fa_bwd_status launch_fwd(fa_bwd_handle* h, const void* q, const void* k, const void* v, const int32_t* cu_q,
+                         const int32_t* cu_kv, float scale, int32_t mask, void* o, float* m, float* l,
+                         hipStream_t stream) {
+  const fa_bwd_desc& d = h->desc;
+  const int padded = (mask == FA_BWD_MASK_PADDING || mask == FA_BWD_MASK_PADDING_CAUSAL) ? 1 : 0;
+  const int causal = (mask == FA_BWD_MASK_CAUSAL || mask == FA_BWD_MASK_PADDING_CAUSAL) ? 1 : 0;
+  using fa::bf16;
+  fa::FwdArgs fa;
+  fa.q = static_cast<const bf16*>(q);
+  fa.k = static_cast<const bf16*>(k);
+  fa.v = static_cast<const bf16*>(v);
+  fa.cu_q = cu_q;
+  fa.cu_kv = cu_kv;
+  fa.o = static_cast<bf16*>(o);
+  fa.m = m;
+  fa.l = l;
+  fa.total_q = d.total_q;
+  fa.total_kv = d.total_kv;
+  fa.H = d.num_heads;
+  fa.batch = d.batch;
+  fa.max_seqlen_q = d.max_seqlen_q;
+  fa.max_seqlen_kv = d.max_seqlen_kv;
+  fa.padded = padded;
+  fa.scale_log2 = scale * fa::kLog2e;
+  hipEvent_t* ev = nullptr;
+  if (h->profiling && h->recorded < kMaxProfiledRuns) {
+    const size_t base = (size_t)h->recorded * 4;
+    if (h->events.size() < base + 4) {
+      for (int i = 0; i < 4; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return FA_BWD_ERR_HIP;
+        h->events.push_back(e);
+      }
+    }
+    ev = &h->events[base];
+    ++h->recorded;
+  }
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t rows = d.total_q * d.num_heads;
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return FA_BWD_ERR_HIP;
+  hipLaunchKernelGGL(fa::fa_fwd_fill<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, fa);
+  if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return FA_BWD_ERR_HIP;
+  using QC = fa::DqCfg<D>;
+  const int64_t q_tiles = (d.max_seqlen_q + QC::BQ - 1) / QC::BQ;
+  const dim3 grid((unsigned)(q_tiles * d.num_heads * d.batch));
+  if (causal)
+    fa::fa_fwd<D, true><<<grid, dim3(256), 0, stream>>>(fa);
+  else
+    fa::fa_fwd<D, false><<<grid, dim3(256), 0, stream>>>(fa);
+  if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
+  if (ev && (hipEventRecord(ev[2], stream) != hipSuccess || hipEventRecord(ev[3], stream) != hipSuccess))
+    return FA_BWD_ERR_HIP;
+  return FA_BWD_OK;
+}
+
+// Host checks shared by fa_bwd_run and fa_fwd_run.
+fa_bwd_status check_run(const fa_bwd_handle* h, float scale, int32_t mask) {
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (mask < FA_BWD_MASK_NONE || mask > FA_BWD_MASK_PADDING_CAUSAL) return FA_BWD_ERR_INVALID_ARGUMENT;
+  const fa_bwd_desc& d = h->desc;
+  if (mask == FA_BWD_MASK_PADDING || mask == FA_BWD_MASK_PADDING_CAUSAL) {
+    if ((int64_t)d.batch * d.max_seqlen_q > d.total_q || (int64_t)d.batch * d.max_seqlen_kv > d.total_kv)
+      return FA_BWD_ERR_INVALID_ARGUMENT;
+  }
+  return FA_BWD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -204,17 +273,30 @@ fa_bwd_status fa_bwd_run(fa_bwd_handle* h, const void* q, const void* k, const v
     if (!aligned(p, 16)) return FA_BWD_ERR_INVALID_ARGUMENT;
   if (!aligned(m, 4) || !aligned(l, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_kv, 4))
     return FA_BWD_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_BWD_ERR_INVALID_ARGUMENT;
-  if (mask < FA_BWD_MASK_NONE || mask > FA_BWD_MASK_PADDING_CAUSAL) return FA_BWD_ERR_INVALID_ARGUMENT;
+  const fa_bwd_status cs = check_run(h, scale, mask);
+  if (cs != FA_BWD_OK) return cs;
   const fa_bwd_desc& d = h->desc;
-  if (mask == FA_BWD_MASK_PADDING || mask == FA_BWD_MASK_PADDING_CAUSAL) {
-    if ((int64_t)d.batch * d.max_seqlen_q > d.total_q || (int64_t)d.batch * d.max_seqlen_kv > d.total_kv)
-      return FA_BWD_ERR_INVALID_ARGUMENT;
-  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.head_dim == 128)
     return launch<128>(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, s);
   return launch<64>(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, s);
+}
+
+fa_bwd_status fa_fwd_run(fa_bwd_handle* h, const void* q, const void* k, const void* v,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, float scale, int32_t mask,
+                         void* o, float* m, float* l, void* stream) {
+  if (!h || !q || !k || !v || !cu_seqlens_q || !cu_seqlens_kv || !o || !m || !l) return FA_BWD_ERR_INVALID_ARGUMENT;
+  const void* vec[] = {q, k, v, o};
+  for (const void* p : vec)
+    if (!aligned(p, 16)) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (!aligned(m, 4) || !aligned(l, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_kv, 4))
+    return FA_BWD_ERR_INVALID_ARGUMENT;
+  const fa_bwd_status cs = check_run(h, scale, mask);
+  if (cs != FA_BWD_OK) return cs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (h->desc.head_dim == 128)
+    return launch_fwd<128>(h, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o, m, l, s);
+  return launch_fwd<64>(h, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o, m, l, s);
 }
 
 fa_bwd_status fa_bwd_destroy(fa_bwd_handle* h) {

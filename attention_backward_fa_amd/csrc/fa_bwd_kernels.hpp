@@ -948,6 +948,239 @@ void fa_bwd_dq(MainArgs a) {
 #endif
 }
 
+// ------------------------------------------------------------------ forward: O, m, l
+
+struct FwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const int* cu_q;
+  const int* cu_kv;
+  bf16* o;   // [total_q][H][D]
+  float* m;  // [total_q][H]: row max of the scaled visible logits
+  float* l;  // [total_q][H]: row sum of exp(scaled logit - m) over visible keys
+  int64_t total_q, total_kv;
+  int H, batch, max_seqlen_q, max_seqlen_kv, padded;
+  float scale_log2;  // scale * log2(e)
+};
+
+// Rows outside every sequence: O = 0, m = 0, l = 1 (finite values a backward never reads).
+template <int D>
+__global__ __launch_bounds__(256) void fa_fwd_fill(FwdArgs a) {
+  constexpr int TPR = D / 8;
+  constexpr int RPB = 256 / TPR;
+  const int sub = threadIdx.x % TPR;
+  const int64_t pair = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;  // = t * H + h
+  const int64_t t = pair / a.H;
+  if (t >= a.total_q || row_in_sequence(t, a.cu_q, a.batch, a.padded, a.max_seqlen_q)) return;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  *(u32x4*)(a.o + pair * D + sub * 8) = z;
+  if (sub == 0) {
+    a.m[pair] = 0.f;
+    a.l[pair] = 1.f;
+  }
+}
+
+// Forward of one (q tile, head, sequence), the producer of the backward's inputs: S^T = K Q^T on
+// bf16 MFMA, softmax with a running row maximum (the forward that the per-tile backward math
+// inverts: P = exp(S*scale - m) / l), O^T += V^T P^T in registers; O = O^T^T / l, m and l written
+// once per row. Same tiling as the dQ kernel: Q in registers, K and V tiles of 64 keys streamed
+// through LDS, each lane owns one query row (its MFMA column), so the running maximum, the row sum
+// and the rescaling of its O row are per-lane values combined with the partner lane (lane ^ 32).
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void fa_fwd(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using C = DqCfg<D>;
+  constexpr int BQ = C::BQ, BK = C::BK, QS = C::QS;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+
+  const int HB = a.H * a.batch;
+  const int tr = blockIdx.x / HB;
+  const int hb = blockIdx.x - tr * HB;
+  const int b = hb / a.H, h = hb - (hb / a.H) * a.H;
+  int64_t q_start, kv_start;
+  int Lq, Lk;
+  seq_of(a.cu_q, b, a.padded, a.max_seqlen_q, q_start, Lq);
+  seq_of(a.cu_kv, b, a.padded, a.max_seqlen_kv, kv_start, Lk);
+  Lq = clamp_len(q_start, Lq, a.total_q);
+  Lk = clamp_len(kv_start, Lk, a.total_kv);
+  const int n_qt_max = (a.max_seqlen_q + BQ - 1) / BQ;
+  const int qtile = CAUSAL ? n_qt_max - 1 - tr : tr;  // causal: q tiles with the most keys first
+  const int i0 = qtile * BQ;
+  if (i0 >= Lq) return;
+
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
+  const int64_t rs = (int64_t)a.H * D;
+  const int rsb = (int)(rs * 2);
+  const bf16* kb = a.k + kv_start * rs + (int64_t)h * D;
+  const bf16* vb = a.v + kv_start * rs + (int64_t)h * D;
+  const bf16* qb = a.q + (q_start + i0) * rs + (int64_t)h * D;
+  const int qi = i0 + 32 * w + c;  // this lane's query row (sequence-local)
+
+  const int q_rows = imin(Lq - i0, BQ);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (int64_t)q_rows * rsb);
+  bf16x8 qf[C::KSD];
+#pragma unroll
+  for (int ks = 0; ks < C::KSD; ++ks)
+    qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, (32 * w + c) * rsb + (16 * ks + 8 * hh) * 2));
+
+  int n_kt = (Lk + BK - 1) / BK;
+  if (CAUSAL) n_kt = imin(n_kt, (i0 + BQ - 1) / BK + 1);
+
+  {  // zero the K and V buffers once (keys past the sequence are masked, but must be finite)
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int o = tid * 16; o < C::LDS_BYTES; o += 256 * 16) *(u32x4*)(smem + o) = z;
+  }
+  __syncthreads();
+
+  constexpr int NJ = (C::NDMA + C::NW - 1) / C::NW;
+  int dma_off[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int p16 = 64 * (w + C::NW * jj) + lane;
+    const int r = p16 / C::CPR, ch = p16 % C::CPR;
+    dma_off[jj] = r * rsb + (ch < D / 8 ? ch : 0) * 16;
+  }
+  auto issue_kv = [&](int t, int bi) {
+    const int j0 = t * BK;
+    const int64_t bytes = (int64_t)imin(Lk - j0, BK) * rsb;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (int64_t)j0 * rs, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (int64_t)j0 * rs, bytes);
+#pragma unroll
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int j = w + C::NW * jj;
+      if (j < C::NDMA) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (__attribute__((address_space(3))) void*)(smem + C::OFF_K + bi * C::TILE_BYTES + 1024 * j), 16,
+            dma_off[jj], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(smem + C::OFF_V + bi * C::TILE_BYTES + 1024 * j), 16,
+            dma_off[jj], 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[C::NTD];  // O^T of this lane's row: features 32 nt + 8 a4 + 4 hh + bb
+#pragma unroll
+  for (int nt = 0; nt < C::NTD; ++nt) acc[nt] = f32x16{};
+  float mrun = -__builtin_inff();  // running max of S*scale*log2(e) over the keys seen
+  float lrun = 0.f;                // this lane's part of sum exp2(S*scale*log2(e) - mrun)
+
+  int buf = 0;
+  if (n_kt > 0) issue_kv(0, 0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __syncthreads();
+
+  const int arow = tile_row(c) * QS + 8 * hh;
+  const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
+  for (int t = 0; t < n_kt; ++t, buf ^= 1) {
+    if (t + 1 < n_kt) issue_kv(t + 1, buf ^ 1);
+    const bf16* sk = (const bf16*)(smem + C::OFF_K + buf * C::TILE_BYTES);
+    const bf16* sv = (const bf16*)(smem + C::OFF_V + buf * C::TILE_BYTES);
+    // S^T = K Q^T ([kv 64] x [q 32] per wave), operands read PF k-steps ahead
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    {
+      constexpr int PF = 2;
+      bf16x8 ka[C::KSD][2];
+      auto ld = [&](int ks) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) ka[ks][mt] = *(const bf16x8*)(sk + arow + 32 * mt * QS + 16 * ks);
+      };
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) ld(ks);
+#pragma unroll
+      for (int ks = 0; ks < C::KSD; ++ks) {
+        if (ks + PF < C::KSD) ld(ks + PF);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) s[mt] = mfma32x32x16(ka[ks][mt], qf[ks], s[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // visible iff key j < Lk and (causal) j <= qi: one bound per lane on the tile-local key
+    const int lim = CAUSAL ? imin(Lk - 1, qi) - t * BK : Lk - 1 - t * BK;
+    float x[2][16];
+    float tmax = -__builtin_inff();
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bool vis = 32 * mt + tile_row(8 * (j >> 2) + 4 * hh + (j & 3)) <= lim;
+        x[mt][j] = vis ? s[mt][j] * a.scale_log2 : -__builtin_inff();
+        tmax = fmaxf(tmax, x[mt][j]);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(mrun, tmax);
+    // no visible key yet: keep everything at zero (mnew = -inf would make exp2 produce NaN)
+    const float mref = mnew == -__builtin_inff() ? 0.f : mnew;
+    const float alpha = fast_exp2(mrun - mref);  // 0 while mrun = -inf
+    mrun = mnew;
+    bf16x8 pk[2][2];
+    float psum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = fast_exp2(x[mt][j] - mref);
+        psum += p;
+        pk[mt][j >> 3][j & 7] = to_bf16(p);
+      }
+    }
+    lrun = lrun * alpha + psum;
+#pragma unroll
+    for (int nt = 0; nt < C::NTD; ++nt) acc[nt] *= alpha;
+    // O^T += V^T P^T: k-step ksi = 2 mt + s2, k-index e is key MFMA row 16 s2 + 4 hh + e (e < 4) or
+    // 16 s2 + 8 + 4 hh + e - 4 of M-tile mt; the transpose reads fetch those V rows
+    {
+      constexpr int NB = 4 * C::NTD, PF = 3;
+      bf16x8 vt[NB];
+      auto vt_load = [&](int i) {
+        const int ksi = i / C::NTD, nt = i % C::NTD;
+        const int o = brow + 16 * ksi * QS + 32 * nt;
+        return concat(lds_read_tr4(sv + o), lds_read_tr4(sv + o + 2 * QS));
+      };
+#pragma unroll
+      for (int i = 0; i < PF; ++i) vt[i] = vt_load(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (i + PF < NB) vt[i + PF] = vt_load(i + PF);
+        const int ksi = i / C::NTD, nt = i % C::NTD;
+        acc[nt] = mfma32x32x16(vt[i], pk[ksi >> 1][ksi & 1], acc[nt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next K/V tiles have landed
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  }
+
+  const float lsum = lrun + __shfl_xor(lrun, 32);
+  if (qi < Lq) {
+    const bool any = mrun != -__builtin_inff();  // a valid row without keys: O = 0, m = 0, l = 1
+    const float inv = any ? 1.f / lsum : 0.f;
+    bf16* dst = a.o + (q_start + qi) * rs + (int64_t)h * D + 4 * hh;
+#pragma unroll
+    for (int nt = 0; nt < C::NTD; ++nt) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const bf16x4 v4 = {to_bf16(acc[nt][4 * a4] * inv), to_bf16(acc[nt][4 * a4 + 1] * inv),
+                           to_bf16(acc[nt][4 * a4 + 2] * inv), to_bf16(acc[nt][4 * a4 + 3] * inv)};
+        *(bf16x4*)(dst + 32 * nt + 8 * a4) = v4;
+      }
+    }
+    if (hh == 0) {
+      const int64_t idx = (q_start + qi) * a.H + h;
+      a.m[idx] = any ? mrun * (1.f / kLog2e) : 0.f;
+      a.l[idx] = any ? lsum : 1.f;
+    }
+  }
+#endif
+}
+
 // ------------------------------------------------------------------ stage 3
 
 template <int D>

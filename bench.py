@@ -211,6 +211,62 @@ def cpu_baseline(inp, dev, target_s: float = 15.0):
             "seconds": elapsed}
 
 
+def bench_forward(args, device):
+    """The forward kernel (O, m, l for the backward) on the same workload: 4 * Lq * Lk * d FLOPs per
+    (sequence, head) -- the two GEMMs S = Q K^T and O = P V -- halved under a causal mask."""
+    import torch
+    from attention_backward_fa_amd import binding, inputs
+    print(f"[bench] forward, preparing workload {args.workload}", file=sys.stderr, flush=True)
+    inp = inputs.make(args.workload)
+    dev = {key: inp[key].to(device) for key in ("q", "k", "v", "cu_q", "cu_kv")}
+    flops = algorithmic_flops(inp) * 0.4
+    tq, heads, d = inp["q"].shape
+    op = binding.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0])
+    o = torch.empty_like(dev["q"])
+    m = torch.empty((tq, heads), dtype=torch.float32, device=device)
+    l = torch.empty((tq, heads), dtype=torch.float32, device=device)
+
+    def step():
+        op.forward(dev["q"], dev["k"], dev["v"], dev["cu_q"], dev["cu_kv"], inp["scale"], inp["mask"], o, m, l)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    binding.fa_bwd_profile_enable(op.handle, True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    stages = binding.fa_bwd_profile_collect(op.handle)
+    binding.fa_bwd_profile_enable(op.handle, False)
+    finite = bool(torch.isfinite(o).all()) and bool(torch.isfinite(m).all())
+    op.close()
+    fill_ms = sum(s_[0] for s_ in stages) / len(stages)
+    fwd_ms = sum(s_[1] for s_ in stages) / len(stages)
+    tflops = flops / (ms * 1e-3) / 1e12
+    achieved = flops / (fwd_ms * 1e-3) / 1e12
+    seqlens = sorted(set(inp["seqlens_q"]))
+    out = {
+        "metric": "FA-fwd TFLOP/s (forward producing O, m, l), % bf16 MFMA peak", "value": round(tflops, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: batch {inp['batch']}, {heads} heads, "
+                               f"seqlens {seqlens if len(seqlens) < 5 else str(len(inp['seqlens_q'])) + ' varlen'}, "
+                               f"head_dim {d}, mask {MASK_NAMES[inp['mask']]}", "path": "forward",
+                   "algorithmic_flops": flops},
+        "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {"fa_fwd_fill": round(fill_ms, 5), "fa_fwd": round(fwd_ms, 5)},
+        "roofline": {"bound": "mfma", "kernel": "fa_fwd", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "work_flops": flops},
+        "outputs_finite": finite,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +278,8 @@ def main():
     ap.add_argument("--algorithm", choices=list(ALGORITHMS), default="default")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a known-traffic elementwise kernel over MIB MiB (for --pmc counter scaling)")
+    ap.add_argument("--path", choices=("backward", "forward"), default="backward",
+                    help="forward: time the forward that produces O, m, l instead (its own metric)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -238,6 +296,8 @@ def main():
     torch.cuda.set_device(device)
     if args.calibrate_copy > 0:
         copy_calibration(args.calibrate_copy, device)
+    if args.path == "forward":
+        return bench_forward(args, device)
     print(f"[bench] preparing workload {args.workload}", file=sys.stderr, flush=True)
     inp, dev = make_workload(args.workload, device)
     flops = algorithmic_flops(inp)

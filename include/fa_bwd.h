@@ -117,6 +117,24 @@ fa_bwd_status fa_bwd_run(fa_bwd_handle* h, const void* q, const void* k, const v
                          const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* dq, void* dk, void* dv,
                          void* stream);
 
+/* Forward that produces the backward's inputs, for callers without one of their own: enqueues on
+ * `stream` O = softmax(scale * Q K^T, masked) V together with the row statistics the backward
+ * consumes, for the sizes of the handle (its workspace is not used; FA_BWD_ALGO_* is ignored).
+ * The softmax is the one step 2 of the SK-16 article inverts, P = exp(S*scale - m) / l.
+ *   q:          bf16 [total_q][H][head_dim]   (read only)
+ *   k, v:       bf16 [total_kv][H][head_dim]  (read only)
+ *   cu_seqlens_q, cu_seqlens_kv, scale, mask: as for fa_bwd_run
+ *   o:          bf16 [total_q][H][head_dim]   (written)
+ *   m:          fp32 [total_q][H]  (written) row max of the scaled visible logits
+ *   l:          fp32 [total_q][H]  (written) row sum of exp(scaled logit - m) over visible keys
+ * Rows outside every sequence get O = 0, m = 0, l = 1; a row whose sequence has no keys gets the
+ * same. Argument checks and errors as for fa_bwd_run (m, l need 4-byte, the rest 16-byte
+ * alignment). With profiling enabled, the recorded row holds (fill of rows outside sequences,
+ * forward kernel, 0). */
+fa_bwd_status fa_fwd_run(fa_bwd_handle* h, const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* o, float* m, float* l,
+                         void* stream);
+
 /* Frees the workspace and the handle (NULL is accepted). Waits for the
  * device to finish work that may still use the workspace. */
 fa_bwd_status fa_bwd_destroy(fa_bwd_handle* h);

@@ -172,6 +172,32 @@ def backward(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int,
     return dq, dk, dv
 
 
+def forward_rows(q, k, v, cu_q, cu_kv, scale: float, mask: int, b: int, h: int, q_rows,
+                 max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
+    """O, m, l of selected query rows of one (b, h), each row computed on its own with the steps
+    of ``forward_head``; indices are sequence-local. Returns fp64 O [n, d], m [n], l [n]."""
+    qs, lq = segments(cu_q, mask, max_seqlen_q)[b]
+    ks, lk = segments(cu_kv, mask, max_seqlen_kv)[b]
+    causal = is_causal(mask)
+    Q, K, V = _f64(q[qs:qs + lq, h]), _f64(k[ks:ks + lk, h]), _f64(v[ks:ks + lk, h])
+    o_out, m_out, l_out = [], [], []
+    for i in q_rows:
+        vis = visible_block([i], np.arange(lk), causal)[0]
+        s = scale * (Q[i] @ K.T)
+        if not vis.any():
+            o_out.append(np.zeros(V.shape[1]))
+            m_out.append(0.0)
+            l_out.append(1.0)
+            continue
+        m = np.max(s[vis])
+        e = np.where(vis, np.exp(np.where(vis, s - m, 0.0)), 0.0)
+        l = e.sum()
+        o_out.append((e / l) @ V)
+        m_out.append(m)
+        l_out.append(l)
+    return np.array(o_out).reshape(-1, V.shape[1]), np.array(m_out), np.array(l_out)
+
+
 def backward_rows(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int, b: int, h: int,
                   q_rows, kv_rows, max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
     """Selected outputs of one (b, h), each computed on its own.

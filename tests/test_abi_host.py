@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "fa_bwd.h")
 
 def declared_functions():
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(fa_bwd_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(fa_(?:bwd|fwd)_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declarations_match_binding():

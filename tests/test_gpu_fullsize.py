@@ -96,3 +96,38 @@ def test_fullsize_sampled(name, algo):
     res = {nm: P.assert_close(nm, np.concatenate(got[nm]), np.concatenate(ref[nm])) for nm in got}
     print(f"[fullsize] {name} ({algo}): " + " ".join(f"{k}: rel_l2={v[0]:.2e} max={v[1]:.2e}"
                                                      for k, v in res.items()), flush=True)
+
+
+@pytest.mark.parametrize("name", ["causal", "longpad"])
+def test_fullsize_forward_sampled(name):
+    """The forward at full size, in the configuration bench.py --path forward times."""
+    from attention_backward_fa_amd import inputs
+    inp = inputs.make(name)
+    tq, heads, d = inp["q"].shape
+    dev = torch.device("cuda:0")
+    t = {k: inp[k].to(dev) for k in ("q", "k", "v", "cu_q", "cu_kv")}
+    print(f"[fullsize-forward] {name}: T_q={tq} H={heads} d={d} mask={inp['mask']}", flush=True)
+    with B.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0]) as op:
+        o, m, l = op.forward(t["q"], t["k"], t["v"], t["cu_q"], t["cu_kv"], inp["scale"], inp["mask"])
+        torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(m).all()) and bool((l > 0).all())
+    vq = torch.from_numpy(oracle.valid_rows(inp["cu_q"], inp["mask"], inp["max_seqlen_q"], tq)).to(dev)
+    assert int((o[~vq] != 0).sum()) == 0 and bool((m[~vq] == 0).all()) and bool((l[~vq] == 1).all())
+    rng = np.random.default_rng(2000 + inp["seed"])
+    segq = oracle.segments(inp["cu_q"], inp["mask"], inp["max_seqlen_q"])
+    got_o, ref_o, dm, dlse = [], [], 0.0, 0.0
+    for b, h in _pairs(inp, rng):
+        qs, lq = segq[b]
+        rows = _rows(lq, rng)
+        ro, rm, rl = oracle.forward_rows(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_kv"], inp["scale"],
+                                         inp["mask"], b, h, rows, inp["max_seqlen_q"], inp["max_seqlen_kv"])
+        idx = [qs + r for r in rows]
+        got_o.append(o[idx, h].float().cpu().numpy())
+        ref_o.append(ro)
+        gm = m[idx, h].cpu().numpy().astype(np.float64)
+        gl = l[idx, h].cpu().numpy().astype(np.float64)
+        dm = max(dm, float(np.max(np.abs(gm - rm))))
+        dlse = max(dlse, float(np.max(np.abs(gm + np.log(gl) - rm - np.log(rl)))))
+    rel, mx = P.assert_close("o", np.concatenate(got_o), np.concatenate(ref_o))
+    assert dm <= 1e-3 and dlse <= 1e-3, f"m err {dm:.2e}, lse err {dlse:.2e}"
+    print(f"[fullsize-forward] {name}: o rel_l2={rel:.2e} max={mx:.2e} m err {dm:.2e} lse err {dlse:.2e}", flush=True)

@@ -11,6 +11,8 @@ cuDNN ``MaskType``. The pins:
   columns, rowsum(O*dO) = rowsum(P*dP), causal zero patterns;
 * closed forms: one key, all-equal V rows, Q = 0;
 * torch fp64 autograd of softmax(scale*QK^T + mask) V, an independent library;
+* the forward on its own: O, the row max of the scaled logits and m + ln(l) against torch's
+  softmax attention, max and logsumexp; the sampled-row forward against the full one;
 * planted mistakes in the oracle's own source, each caught by one of the above.
 """
 import inspect
@@ -298,6 +300,66 @@ def test_zero_queries_give_uniform_softmax():
 def test_torch_fp64_autograd(mask, lq, lk, d, padded):
     p = make_problem(mask, lq, lk, heads=2, d=d, seed=99 + sum(lq), padded_len=padded, mult=2.0)
     assert torch_error(p) < 1e-12
+
+
+# ---------------------------------------------------------------- the forward on its own
+
+def torch_forward(p):
+    """Independent forward: torch fp64 softmax attention per (b, h); O, row max of the scaled
+    logits and their logsumexp (rows outside every sequence: O = 0, m = 0, lse = 0)."""
+    q, k, v = (torch.tensor(p[x]) for x in ("q", "k", "v"))
+    padded = p["mask"] in (MASK_PADDING, MASK_PADDING_CAUSAL)
+    causal = p["mask"] in (MASK_CAUSAL, MASK_PADDING_CAUSAL)
+    o = torch.zeros_like(q)
+    m = torch.zeros(q.shape[:2], dtype=torch.float64)
+    lse = torch.zeros(q.shape[:2], dtype=torch.float64)
+    for b in range(len(p["cu_q"]) - 1):
+        lq = int(p["cu_q"][b + 1] - p["cu_q"][b])
+        lk = int(p["cu_kv"][b + 1] - p["cu_kv"][b])
+        qs = b * p["max_seqlen_q"] if padded else int(p["cu_q"][b])
+        ks = b * p["max_seqlen_kv"] if padded else int(p["cu_kv"][b])
+        if lq == 0 or lk == 0:
+            continue
+        for h in range(q.shape[1]):
+            logits = p["scale"] * q[qs:qs + lq, h] @ k[ks:ks + lk, h].T
+            if causal:
+                logits = logits + torch.triu(torch.full((lq, lk), float("-inf"), dtype=torch.float64), diagonal=1)
+            o[qs:qs + lq, h] = torch.softmax(logits, dim=-1) @ v[ks:ks + lk, h]
+            m[qs:qs + lq, h] = logits.max(dim=-1).values
+            lse[qs:qs + lq, h] = torch.logsumexp(logits, dim=-1)
+    return o.numpy(), m.numpy(), lse.numpy()
+
+
+@pytest.mark.parametrize("mask,lq,lk,d,padded", FD_CASES + [
+    (MASK_NONE, [64, 37], [64, 37], 32, 0),
+    (MASK_CAUSAL, [96], [96], 64, 0),
+    (MASK_PADDING_CAUSAL, [80, 50], [80, 50], 16, 80),
+])
+def test_forward_matches_torch(mask, lq, lk, d, padded):
+    p = make_problem(mask, lq, lk, heads=2, d=d, seed=7 + sum(lq), padded_len=padded, mult=2.0)
+    o, m, l = A.forward(p["q"], p["k"], p["v"], p["cu_q"], p["cu_kv"], p["scale"], p["mask"],
+                        p["max_seqlen_q"], p["max_seqlen_kv"])
+    to, tm, tlse = torch_forward(p)
+    np.testing.assert_allclose(o, to, rtol=1e-12, atol=1e-13)
+    valid = A.valid_rows(p["cu_q"], mask, p["max_seqlen_q"], p["q"].shape[0])
+    np.testing.assert_allclose(m[valid], tm[valid], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose((m + np.log(l))[valid], tlse[valid], rtol=1e-12, atol=1e-12)
+    assert np.all(o[~valid] == 0) and np.all(m[~valid] == 0) and np.all(l[~valid] == 1)
+
+
+@pytest.mark.parametrize("mask", [MASK_NONE, MASK_CAUSAL, MASK_PADDING_CAUSAL])
+def test_forward_rows_matches_forward(mask):
+    padded = 40 if A.is_padded(mask) else 0
+    p = make_problem(mask, [40, 23], [40, 23], heads=3, d=16, seed=6, padded_len=padded)
+    o, m, l = A.forward(p["q"], p["k"], p["v"], p["cu_q"], p["cu_kv"], p["scale"], mask,
+                        p["max_seqlen_q"], p["max_seqlen_kv"])
+    for b, (qs, lq) in enumerate(A.segments(p["cu_q"], mask, p["max_seqlen_q"])):
+        rows = [0, 1, lq // 2, lq - 1]
+        ro, rm, rl = A.forward_rows(p["q"], p["k"], p["v"], p["cu_q"], p["cu_kv"], p["scale"], mask, b, 1, rows,
+                                    p["max_seqlen_q"], p["max_seqlen_kv"])
+        np.testing.assert_allclose(ro, o[[qs + r for r in rows], 1], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(rm, m[[qs + r for r in rows], 1], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(rl, l[[qs + r for r in rows], 1], rtol=1e-12, atol=1e-14)
 
 
 # ---------------------------------------------------------------- sampled rows == full backward
