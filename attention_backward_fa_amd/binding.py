@@ -32,8 +32,8 @@ FA_BWD_MASK_CAUSAL = 2
 FA_BWD_MASK_PADDING_CAUSAL = 3
 
 # every symbol include/fa_bwd.h declares
-EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_fwd_run", "fa_bwd_destroy", "fa_bwd_status_string",
-            "fa_bwd_get_desc", "fa_bwd_profile_enable", "fa_bwd_profile_collect")
+EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_run_lse", "fa_fwd_run", "fa_bwd_destroy",
+            "fa_bwd_status_string", "fa_bwd_get_desc", "fa_bwd_profile_enable", "fa_bwd_profile_collect")
 
 
 class FaBwdDesc(ctypes.Structure):
@@ -58,6 +58,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_create.restype = i32
     lib.fa_bwd_run.argtypes = [vp] * 10 + [f32, i32] + [vp] * 4
     lib.fa_bwd_run.restype = i32
+    lib.fa_bwd_run_lse.argtypes = [vp] * 9 + [f32, i32] + [vp] * 4
+    lib.fa_bwd_run_lse.restype = i32
     lib.fa_fwd_run.argtypes = [vp] * 6 + [f32, i32] + [vp] * 4
     lib.fa_fwd_run.restype = i32
     lib.fa_bwd_destroy.argtypes = [vp]
@@ -153,6 +155,31 @@ def fa_bwd_run(handle, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scal
     _check(st, "fa_bwd_run")
 
 
+def fa_bwd_run_lse(handle, q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_kv, scale: float, mask: int,
+                   dq, dk, dv, stream=None) -> None:
+    """The backward with one log-sum-exp per row (lse = m + ln l, fp32 [total_q, H]) instead of (m, l)."""
+    import torch
+    d = fa_bwd_get_desc(handle)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(f"q: expected a GPU tensor, got device {dev}")
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    qs = (d.total_q, d.num_heads, d.head_dim)
+    ks = (d.total_kv, d.num_heads, d.head_dim)
+    ptrs = [
+        _expect(q, "q", qs, bf, dev), _expect(k, "k", ks, bf, dev), _expect(v, "v", ks, bf, dev),
+        _expect(o, "o", qs, bf, dev), _expect(dout, "dout", qs, bf, dev), _expect(lse, "lse", qs[:2], f32, dev),
+        _expect(cu_seqlens_q, "cu_seqlens_q", (d.batch + 1,), i32, dev),
+        _expect(cu_seqlens_kv, "cu_seqlens_kv", (d.batch + 1,), i32, dev),
+    ]
+    outs = [_expect(dq, "dq", qs, bf, dev), _expect(dk, "dk", ks, bf, dev), _expect(dv, "dv", ks, bf, dev)]
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = load_library().fa_bwd_run_lse(handle, *ptrs, ctypes.c_float(scale), int(mask), *outs,
+                                       ctypes.c_void_p(stream))
+    _check(st, "fa_bwd_run_lse")
+
+
 def fa_fwd_run(handle, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, mask: int, o, m, l,
                stream=None) -> None:
     """Enqueue the forward (O, m, l for the backward) on ``stream`` (default: torch's current stream).
@@ -207,6 +234,16 @@ class FaBwd:
         dk = torch.empty_like(k) if dk is None else dk
         dv = torch.empty_like(v) if dv is None else dv
         fa_bwd_run(self.handle, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, stream)
+        return dq, dk, dv
+
+    def run_lse(self, q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq=None, dk=None, dv=None,
+                stream=None):
+        import torch
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        fa_bwd_run_lse(self.handle, q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv,
+                       stream)
         return dq, dk, dv
 
     def forward(self, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o=None, m=None, l=None, stream=None):

@@ -229,6 +229,27 @@ fa_bwd_status check_run(const fa_bwd_handle* h, float scale, int32_t mask) {
   return FA_BWD_OK;
 }
 
+// (m, l) or, with l null, the log-sum-exp in m: shared checks and launch of both backward entries.
+fa_bwd_status run_common(fa_bwd_handle* h, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* m, const float* l, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* dq, void* dk, void* dv,
+                         void* stream) {
+  if (!h || !q || !k || !v || !o || !dout || !m || !cu_seqlens_q || !cu_seqlens_kv || !dq || !dk || !dv)
+    return FA_BWD_ERR_INVALID_ARGUMENT;
+  const void* vec[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : vec)
+    if (!aligned(p, 16)) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (!aligned(m, 4) || (l && !aligned(l, 4)) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_kv, 4))
+    return FA_BWD_ERR_INVALID_ARGUMENT;
+  const fa_bwd_status cs = check_run(h, scale, mask);
+  if (cs != FA_BWD_OK) return cs;
+  const fa_bwd_desc& d = h->desc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d.head_dim == 128)
+    return launch<128>(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, s);
+  return launch<64>(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -266,20 +287,16 @@ fa_bwd_status fa_bwd_run(fa_bwd_handle* h, const void* q, const void* k, const v
                          const void* dout, const float* m, const float* l, const int32_t* cu_seqlens_q,
                          const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* dq, void* dk, void* dv,
                          void* stream) {
-  if (!h || !q || !k || !v || !o || !dout || !m || !l || !cu_seqlens_q || !cu_seqlens_kv || !dq || !dk || !dv)
-    return FA_BWD_ERR_INVALID_ARGUMENT;
-  const void* vec[] = {q, k, v, o, dout, dq, dk, dv};
-  for (const void* p : vec)
-    if (!aligned(p, 16)) return FA_BWD_ERR_INVALID_ARGUMENT;
-  if (!aligned(m, 4) || !aligned(l, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_kv, 4))
-    return FA_BWD_ERR_INVALID_ARGUMENT;
-  const fa_bwd_status cs = check_run(h, scale, mask);
-  if (cs != FA_BWD_OK) return cs;
-  const fa_bwd_desc& d = h->desc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d.head_dim == 128)
-    return launch<128>(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, s);
-  return launch<64>(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, s);
+  if (!l) return FA_BWD_ERR_INVALID_ARGUMENT;
+  return run_common(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, stream);
+}
+
+fa_bwd_status fa_bwd_run_lse(fa_bwd_handle* h, const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* dq, void* dk, void* dv,
+                             void* stream) {
+  if (!lse) return FA_BWD_ERR_INVALID_ARGUMENT;
+  return run_common(h, q, k, v, o, dout, lse, nullptr, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, stream);
 }
 
 fa_bwd_status fa_fwd_run(fa_bwd_handle* h, const void* q, const void* k, const void* v,

@@ -48,8 +48,8 @@ __device__ __forceinline__ bool row_in_sequence(int64_t t, const int* cu, int ba
 struct PreArgs {
   const bf16* o;
   const bf16* dout;
-  const float* m;
-  const float* l;
+  const float* m;  // row max, or the log-sum-exp when l is null
+  const float* l;  // row sum, or null
   const int* cu_q;
   const int* cu_kv;
   float* lse2;    // [H][total_q]: m*log2(e) + log2(l)
@@ -92,7 +92,8 @@ __global__ __launch_bounds__(256) void fa_bwd_pre(PreArgs a) {
     if (sub == 0) {
       const int64_t sidx = (int64_t)h * a.total_q + t;
       a.dvec[sidx] = acc;
-      a.lse2[sidx] = a.m[pair] * kLog2e + __log2f(a.l[pair]);
+      // (m, l) from the forward, or (when l is null) m holds the log-sum-exp m + ln(l) itself
+      a.lse2[sidx] = a.l ? a.m[pair] * kLog2e + __log2f(a.l[pair]) : a.m[pair] * kLog2e;
     }
   }
   if (t < a.total_kv && !row_in_sequence(t, a.cu_kv, a.batch, a.padded, a.max_seqlen_kv)) {

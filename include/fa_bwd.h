@@ -117,6 +117,15 @@ fa_bwd_status fa_bwd_run(fa_bwd_handle* h, const void* q, const void* k, const v
                          const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* dq, void* dk, void* dv,
                          void* stream);
 
+/* The same backward with the softmax statistics as one log-sum-exp per row (the single statistic
+ * the jax cuDNN wrapper keeps): lse = m + ln(l), fp32 [total_q][H], so that step 2 reads
+ * P = exp(S*scale - lse). Every other argument, check and error as for fa_bwd_run; lse must not be
+ * NULL and must be 4-byte aligned. */
+fa_bwd_status fa_bwd_run_lse(fa_bwd_handle* h, const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* dq, void* dk, void* dv,
+                             void* stream);
+
 /* Forward that produces the backward's inputs, for callers without one of their own: enqueues on
  * `stream` O = softmax(scale * Q K^T, masked) V together with the row statistics the backward
  * consumes, for the sizes of the handle (its workspace is not used; FA_BWD_ALGO_* is ignored).

@@ -172,6 +172,15 @@ def backward(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int,
     return dq, dk, dv
 
 
+def backward_from_lse(q, k, v, o, do, lse, cu_q, cu_kv, scale: float, mask: int,
+                      max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
+    """Backward from one log-sum-exp statistic per row (lse = m + ln l, the single softmax statistic
+    of the jax cuDNN wrapper): step 2 reads P = exp(S*scale - lse), which is the step-2 formula with
+    m = lse and l = 1."""
+    lse = _f64(lse)
+    return backward(q, k, v, o, do, lse, np.ones_like(lse), cu_q, cu_kv, scale, mask, max_seqlen_q, max_seqlen_kv)
+
+
 def forward_rows(q, k, v, cu_q, cu_kv, scale: float, mask: int, b: int, h: int, q_rows,
                  max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
     """O, m, l of selected query rows of one (b, h), each row computed on its own with the steps

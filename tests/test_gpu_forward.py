@@ -78,3 +78,25 @@ def test_forward_then_backward(case):
                           inp["scale"], inp["mask"], inp["max_seqlen_q"], inp["max_seqlen_kv"])
     res = P.check_full(inp, (dq.float().cpu(), dk.float().cpu(), dv.float().cpu()), ref)
     print(f"[chain] {case.name}: " + " ".join(f"{k}: rel_l2={v[0]:.2e}" for k, v in res.items()), flush=True)
+
+
+LSE_CASES = [c for c in CASES if c.name in ("tiny", "ragged_causal_d128", "padded_causal_d64", "empty_sequence")]
+
+
+@pytest.mark.parametrize("case", LSE_CASES, ids=[c.name for c in LSE_CASES])
+def test_backward_from_lse(case):
+    """fa_bwd_run_lse with lse = m + ln(l) against the oracle backward from the same statistic."""
+    inp = I.make(case)
+    o, m, l = P.oracle_stats(inp)
+    lse = (m.double() + torch.log(l.double())).float()
+    dev = torch.device("cuda")
+    t = {k: inp[k].to(dev) for k in ("q", "k", "v", "do", "cu_q", "cu_kv")}
+    with B.FaBwd(inp["batch"], case.heads, case.head_dim, inp["max_seqlen_q"], inp["max_seqlen_kv"],
+                 inp["q"].shape[0], inp["k"].shape[0]) as op:
+        dq, dk, dv = op.run_lse(t["q"], t["k"], t["v"], o.to(dev), t["do"], lse.to(dev), t["cu_q"], t["cu_kv"],
+                                inp["scale"], inp["mask"])
+        torch.cuda.synchronize()
+    ref = oracle.backward_from_lse(inp["q"], inp["k"], inp["v"], o, inp["do"], lse, inp["cu_q"], inp["cu_kv"],
+                                   inp["scale"], inp["mask"], inp["max_seqlen_q"], inp["max_seqlen_kv"])
+    res = P.check_full(inp, (dq.float().cpu(), dk.float().cpu(), dv.float().cpu()), ref)
+    print(f"[lse] {case.name}: " + " ".join(f"{k}: rel_l2={v[0]:.2e}" for k, v in res.items()), flush=True)

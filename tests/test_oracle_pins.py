@@ -362,6 +362,18 @@ def test_forward_rows_matches_forward(mask):
         np.testing.assert_allclose(rl, l[[qs + r for r in rows], 1], rtol=1e-12, atol=1e-14)
 
 
+@pytest.mark.parametrize("mask", [MASK_NONE, MASK_CAUSAL, MASK_PADDING_CAUSAL])
+def test_backward_from_lse_equals_backward_from_m_l(mask):
+    """exp(s - m) / l = exp(s - (m + ln l)): the two statistic forms give the same gradients."""
+    padded = 12 if A.is_padded(mask) else 0
+    p = make_problem(mask, [12, 7], [12, 7], heads=2, d=8, seed=8, padded_len=padded, mult=2.0)
+    o, m, l, dq, dk, dv = exact_backward(p)
+    lq, lk, lv = A.backward_from_lse(p["q"], p["k"], p["v"], o, p["do"], m + np.log(l), p["cu_q"], p["cu_kv"],
+                                     p["scale"], mask, p["max_seqlen_q"], p["max_seqlen_kv"])
+    for a, b in ((lq, dq), (lk, dk), (lv, dv)):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------------- sampled rows == full backward
 
 @pytest.mark.parametrize("mask", [MASK_NONE, MASK_CAUSAL, MASK_PADDING_CAUSAL])
