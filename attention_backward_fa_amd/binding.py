@@ -39,7 +39,8 @@ EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_run_lse", "fa_fwd_run", "fa_b
 class FaBwdDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_kv", ctypes.c_int32),
-                ("total_q", ctypes.c_int64), ("total_kv", ctypes.c_int64), ("algorithm", ctypes.c_int32)]
+                ("total_q", ctypes.c_int64), ("total_kv", ctypes.c_int64), ("algorithm", ctypes.c_int32),
+                ("num_heads_kv", ctypes.c_int32)]
 
 
 _lib = None
@@ -92,9 +93,11 @@ def _check(status: int, what: str) -> None:
 
 
 def fa_bwd_create(batch: int, num_heads: int, head_dim: int, max_seqlen_q: int, max_seqlen_kv: int,
-                  total_q: int, total_kv: int, algorithm: int = FA_BWD_ALGO_DEFAULT) -> ctypes.c_void_p:
-    """Create a handle (and its device workspace on the current device)."""
-    desc = FaBwdDesc(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv, algorithm)
+                  total_q: int, total_kv: int, algorithm: int = FA_BWD_ALGO_DEFAULT,
+                  num_heads_kv: int = 0) -> ctypes.c_void_p:
+    """Create a handle (and its device workspace on the current device); num_heads_kv 0 = num_heads."""
+    desc = FaBwdDesc(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv, algorithm,
+                     num_heads_kv)
     handle = ctypes.c_void_p()
     _check(load_library().fa_bwd_create(ctypes.byref(desc), ctypes.byref(handle)), "fa_bwd_create")
     return handle
@@ -140,7 +143,7 @@ def fa_bwd_run(handle, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scal
         raise ValueError(f"q: expected a GPU tensor, got device {dev}")
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
     qs = (d.total_q, d.num_heads, d.head_dim)
-    ks = (d.total_kv, d.num_heads, d.head_dim)
+    ks = (d.total_kv, d.num_heads_kv, d.head_dim)
     ptrs = [
         _expect(q, "q", qs, bf, dev), _expect(k, "k", ks, bf, dev), _expect(v, "v", ks, bf, dev),
         _expect(o, "o", qs, bf, dev), _expect(dout, "dout", qs, bf, dev),
@@ -165,7 +168,7 @@ def fa_bwd_run_lse(handle, q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_kv, s
         raise ValueError(f"q: expected a GPU tensor, got device {dev}")
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
     qs = (d.total_q, d.num_heads, d.head_dim)
-    ks = (d.total_kv, d.num_heads, d.head_dim)
+    ks = (d.total_kv, d.num_heads_kv, d.head_dim)
     ptrs = [
         _expect(q, "q", qs, bf, dev), _expect(k, "k", ks, bf, dev), _expect(v, "v", ks, bf, dev),
         _expect(o, "o", qs, bf, dev), _expect(dout, "dout", qs, bf, dev), _expect(lse, "lse", qs[:2], f32, dev),
@@ -194,7 +197,7 @@ def fa_fwd_run(handle, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, mask:
         raise ValueError(f"q: expected a GPU tensor, got device {dev}")
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
     qs = (d.total_q, d.num_heads, d.head_dim)
-    ks = (d.total_kv, d.num_heads, d.head_dim)
+    ks = (d.total_kv, d.num_heads_kv, d.head_dim)
     ptrs = [
         _expect(q, "q", qs, bf, dev), _expect(k, "k", ks, bf, dev), _expect(v, "v", ks, bf, dev),
         _expect(cu_seqlens_q, "cu_seqlens_q", (d.batch + 1,), i32, dev),
@@ -223,9 +226,9 @@ class FaBwd:
     """Owns one handle; ``run`` allocates nothing when the outputs are passed in."""
 
     def __init__(self, batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv,
-                 algorithm=FA_BWD_ALGO_DEFAULT):
+                 algorithm=FA_BWD_ALGO_DEFAULT, num_heads_kv=0):
         self.handle = fa_bwd_create(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv,
-                                    algorithm)
+                                    algorithm, num_heads_kv)
 
     def run(self, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq=None, dk=None, dv=None,
             stream=None):
@@ -270,7 +273,7 @@ def attention_backward(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scal
                        max_seqlen_q: int, max_seqlen_kv: int, algorithm: int = FA_BWD_ALGO_DEFAULT):
     """One-shot call: create a handle, run on the current stream, destroy (which waits)."""
     with FaBwd(cu_seqlens_q.numel() - 1, q.shape[1], q.shape[2], max_seqlen_q, max_seqlen_kv,
-               q.shape[0], k.shape[0], algorithm) as op:
+               q.shape[0], k.shape[0], algorithm, k.shape[1]) as op:
         return op.run(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask)
 
 
@@ -278,5 +281,5 @@ def attention_forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, mask: 
                       max_seqlen_kv: int):
     """One-shot forward: returns O (bf16), m, l (fp32) on q's device."""
     with FaBwd(cu_seqlens_q.numel() - 1, q.shape[1], q.shape[2], max_seqlen_q, max_seqlen_kv,
-               q.shape[0], k.shape[0]) as op:
+               q.shape[0], k.shape[0], num_heads_kv=k.shape[1]) as op:
         return op.forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask)

@@ -42,6 +42,10 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
       d->total_kv < 1)
     return FA_BWD_ERR_INVALID_ARGUMENT;
   if (d->head_dim != 64 && d->head_dim != 128) return FA_BWD_ERR_UNSUPPORTED;
+  const int32_t hkv = d->num_heads_kv == 0 ? d->num_heads : d->num_heads_kv;
+  if (hkv < 1 || d->num_heads % hkv != 0) return FA_BWD_ERR_INVALID_ARGUMENT;
+  // the single-pass form owns one (kv tile, head) per workgroup; grouped K/V heads need the recompute form
+  if (d->algorithm == FA_BWD_ALGO_SINGLE_PASS && hkv != d->num_heads) return FA_BWD_ERR_UNSUPPORTED;
   if (d->algorithm < FA_BWD_ALGO_DEFAULT || d->algorithm > FA_BWD_ALGO_RECOMPUTE_DQ) return FA_BWD_ERR_INVALID_ARGUMENT;
   // index arithmetic stays in int64; grids must fit the launch limits
   const int64_t rows = (d->total_q > d->total_kv ? d->total_q : d->total_kv);
@@ -80,6 +84,7 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   pa.total_q = d.total_q;
   pa.total_kv = d.total_kv;
   pa.H = d.num_heads;
+  pa.Hk = d.num_heads_kv;
   pa.batch = d.batch;
   pa.max_seqlen_q = d.max_seqlen_q;
   pa.max_seqlen_kv = d.max_seqlen_kv;
@@ -120,6 +125,7 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.total_q = d.total_q;
   ma.total_kv = d.total_kv;
   ma.H = d.num_heads;
+  ma.Hk = d.num_heads_kv;
   ma.batch = d.batch;
   ma.max_seqlen_q = d.max_seqlen_q;
   ma.max_seqlen_kv = d.max_seqlen_kv;
@@ -135,10 +141,11 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
     else
       fa::fa_bwd_main<D, false, true><<<grid, dim3(256), 0, stream>>>(ma);
   } else {
+    const dim3 dgrid((unsigned)(kv_tiles * d.num_heads_kv * d.batch));  // (kv tile, K/V head, sequence)
     if (causal)
-      fa::fa_bwd_dkdv<D, true><<<grid, dim3(512), 0, stream>>>(ma);
+      fa::fa_bwd_dkdv<D, true><<<dgrid, dim3(512), 0, stream>>>(ma);
     else
-      fa::fa_bwd_dkdv<D, false><<<grid, dim3(512), 0, stream>>>(ma);
+      fa::fa_bwd_dkdv<D, false><<<dgrid, dim3(512), 0, stream>>>(ma);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return FA_BWD_ERR_HIP;
@@ -180,6 +187,7 @@ fa_bwd_status launch_fwd(fa_bwd_handle* h, const void* q, const void* k, const v
   fa.total_q = d.total_q;
   fa.total_kv = d.total_kv;
   fa.H = d.num_heads;
+  fa.Hk = d.num_heads_kv;
   fa.batch = d.batch;
   fa.max_seqlen_q = d.max_seqlen_q;
   fa.max_seqlen_kv = d.max_seqlen_kv;
@@ -262,6 +270,7 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
   fa_bwd_handle* h = new (std::nothrow) fa_bwd_handle();
   if (!h) return FA_BWD_ERR_OUT_OF_MEMORY;
   h->desc = *desc;
+  if (h->desc.num_heads_kv == 0) h->desc.num_heads_kv = desc->num_heads;
   h->single_pass = desc->algorithm == FA_BWD_ALGO_SINGLE_PASS;
   if (hipGetDevice(&h->device) != hipSuccess) {
     delete h;

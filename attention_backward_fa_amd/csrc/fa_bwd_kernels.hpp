@@ -59,7 +59,7 @@ struct PreArgs {
   bf16* dk;
   bf16* dv;
   int64_t total_q, total_kv;
-  int H, batch, max_seqlen_q, max_seqlen_kv, padded;
+  int H, Hk, batch, max_seqlen_q, max_seqlen_kv, padded;  // query heads, K/V heads
 };
 
 template <int D>
@@ -96,10 +96,11 @@ __global__ __launch_bounds__(256) void fa_bwd_pre(PreArgs a) {
       a.lse2[sidx] = a.l ? a.m[pair] * kLog2e + __log2f(a.l[pair]) : a.m[pair] * kLog2e;
     }
   }
-  if (t < a.total_kv && !row_in_sequence(t, a.cu_kv, a.batch, a.padded, a.max_seqlen_kv)) {
+  if (h < a.Hk && t < a.total_kv && !row_in_sequence(t, a.cu_kv, a.batch, a.padded, a.max_seqlen_kv)) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    *(u32x4*)(a.dk + off) = z;
-    *(u32x4*)(a.dv + off) = z;
+    const int64_t koff = (t * a.Hk + h) * D + sub * 8;
+    *(u32x4*)(a.dk + koff) = z;
+    *(u32x4*)(a.dv + koff) = z;
   }
 }
 
@@ -119,7 +120,7 @@ struct MainArgs {
   bf16* dk;
   bf16* dv;
   int64_t total_q, total_kv;
-  int H, batch, max_seqlen_q, max_seqlen_kv, padded, causal;
+  int H, Hk, batch, max_seqlen_q, max_seqlen_kv, padded, causal;  // query heads, K/V heads (H % Hk == 0)
   float scale_log2;  // scale * log2(e)
   float scale;
 };
@@ -523,10 +524,10 @@ void fa_bwd_dkdv(MainArgs a) {
   bf16* s_do = (bf16*)(smem + C::OFF_DO);
   float* s_st = (float*)(smem + C::OFF_ST);
 
-  const int HB = a.H * a.batch;
+  const int HB = a.Hk * a.batch;
   const int tile = blockIdx.x / HB;  // heavy (low) kv tiles of every head dispatch first
   const int hb = blockIdx.x - tile * HB;
-  const int b = hb / a.H, h = hb - (hb / a.H) * a.H;
+  const int b = hb / a.Hk, hk = hb - (hb / a.Hk) * a.Hk;  // sequence, K/V head
   int64_t q_start, kv_start;
   int Lq, Lk;
   seq_of(a.cu_q, b, a.padded, a.max_seqlen_q, q_start, Lq);
@@ -540,23 +541,22 @@ void fa_bwd_dkdv(MainArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int grp = w & 3, mt = w >> 2;  // kv row group; M-tile of steps 1-5; 0: dV wave, 1: dK wave
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
-  const int64_t rs = (int64_t)a.H * D;
+  const int64_t rs = (int64_t)a.H * D;    // row stride of Q, dO
   const int rsb = (int)(rs * 2);
-  const bf16* kb = a.k + (kv_start + kv0) * rs + (int64_t)h * D;
-  const bf16* vb = a.v + (kv_start + kv0) * rs + (int64_t)h * D;
-  const bf16* qb = a.q + q_start * rs + (int64_t)h * D;
-  const bf16* db = a.dout + q_start * rs + (int64_t)h * D;
-  const float* lse_b = a.lse2 + (int64_t)h * a.total_q + q_start;
-  const float* dd_b = a.dvec + (int64_t)h * a.total_q + q_start;
+  const int64_t rsk = (int64_t)a.Hk * D;  // row stride of K, V, dK, dV
+  const int rskb = (int)(rsk * 2);
+  const int G = a.H / a.Hk;               // query heads sharing this K/V head: hk * G .. hk * G + G - 1
+  const bf16* kb = a.k + (kv_start + kv0) * rsk + (int64_t)hk * D;
+  const bf16* vb = a.v + (kv_start + kv0) * rsk + (int64_t)hk * D;
 
   // K and V rows 32 grp + c as B operands of S = Q K^T and dP = dO V^T
   const int kv_rows = imin(Lk - kv0, BN);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (int64_t)kv_rows * rsb);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (int64_t)kv_rows * rsb);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (int64_t)kv_rows * rskb);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (int64_t)kv_rows * rskb);
   bf16x8 kf[C::KSD], vf[C::KSD];
 #pragma unroll
   for (int ks = 0; ks < C::KSD; ++ks) {
-    const int off = (32 * grp + c) * rsb + (16 * ks + 8 * hh) * 2;
+    const int off = (32 * grp + c) * rskb + (16 * ks + 8 * hh) * 2;
     kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
     vf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
   }
@@ -570,8 +570,14 @@ void fa_bwd_dkdv(MainArgs a) {
 #pragma unroll
   for (int nt = 0; nt < C::NTD; ++nt) acc[nt] = f32x16{};
 
+  // the q steps: for each query head of the group, the q tiles that can see these keys (causal: from
+  // the tile of the first key on); step st is q tile qt0 + st % nq of query head hk * G + st / nq
   const int n_qt = (Lq + BM - 1) / BM;
-  int qt = CAUSAL ? kv0 / BM : 0;
+  const int qt0 = CAUSAL ? kv0 / BM : 0;
+  const int nq = n_qt > qt0 ? n_qt - qt0 : 0;
+  const int n_steps = G * nq;
+  auto step_head = [&](int st) { return hk * G + st / nq; };
+  auto step_tile = [&](int st) { return qt0 + st % nq; };
   const int jcol = kv0 + 32 * grp + c;  // this lane's key row (sequence-local)
 
   constexpr int NJ = (C::NDMA + C::NW - 1) / C::NW;
@@ -582,11 +588,12 @@ void fa_bwd_dkdv(MainArgs a) {
     const int r = p16 / C::CPR, ch = p16 % C::CPR;
     dma_off[jj] = r * rsb + (ch < D / 8 ? ch : 0) * 16;
   }
-  auto issue_tile = [&](int t, int bi) {
-    const int i0 = t * BM;
+  auto issue_tile = [&](int st, int bi) {
+    const int i0 = step_tile(st) * BM;
+    const int64_t hoff = (q_start + i0) * rs + (int64_t)step_head(st) * D;
     const int64_t bytes = (int64_t)imin(Lq - i0, BM) * rsb;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb + (int64_t)i0 * rs, bytes);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(db + (int64_t)i0 * rs, bytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + hoff, bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + hoff, bytes);
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       const int j = w + C::NW * jj;
@@ -602,12 +609,13 @@ void fa_bwd_dkdv(MainArgs a) {
   };
   // row statistics of q tile t in MFMA row order: threads 0..63 lse2, 64..127 D; rows past the
   // sequence get lse2 = +inf, so their P (and dS) is exactly 0 without a mask
-  auto load_stats = [&](int t) -> float {
+  auto load_stats = [&](int st) -> float {
     const int mi = tid & (BM - 1);
-    const int r = t * BM + 32 * (mi >> 5) + tile_row(mi & 31);
+    const int r = step_tile(st) * BM + 32 * (mi >> 5) + tile_row(mi & 31);
     if (tid >= 2 * BM) return 0.f;
     if (r >= Lq) return tid < BM ? __builtin_inff() : 0.f;
-    return (tid < BM ? lse_b : dd_b)[r];
+    const int64_t sidx = (int64_t)step_head(st) * a.total_q + q_start + r;
+    return (tid < BM ? a.lse2 : a.dvec)[sidx];
   };
   auto store_stats = [&](int bi, float v) {
     if (tid < 2 * BM) s_st[bi * 2 * BM + tid] = v;
@@ -616,23 +624,23 @@ void fa_bwd_dkdv(MainArgs a) {
   auto xslot = [&](int m, int k) { return (bf16x8*)(smem + C::OFF_X) + ((grp * 2 + m) * 2 + k) * 64 + lane; };
 
   int buf = 0;
-  if (qt < n_qt) {
-    issue_tile(qt, 0);
-    store_stats(0, load_stats(qt));
+  if (n_steps > 0) {
+    issue_tile(0, 0);
+    store_stats(0, load_stats(0));
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
 
   const int arow = (32 * mt + tile_row(c)) * QS + 8 * hh;
   const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
-  for (; qt < n_qt; ++qt, buf ^= 1) {
-    const bool has_next = qt + 1 < n_qt;
+  for (int sp = 0; sp < n_steps; ++sp, buf ^= 1) {
+    const bool has_next = sp + 1 < n_steps;
     float st_next = 0.f;
     if (has_next) {
-      issue_tile(qt + 1, buf ^ 1);
-      st_next = load_stats(qt + 1);
+      issue_tile(sp + 1, buf ^ 1);
+      st_next = load_stats(sp + 1);
     }
-    const int i0 = qt * BM;
+    const int i0 = step_tile(sp) * BM;
     const bf16* sq = s_q + buf * C::TILE;
     const bf16* sd = s_do + buf * C::TILE;
     const float* st = s_st + buf * 2 * BM + 32 * mt;
@@ -726,7 +734,7 @@ void fa_bwd_dkdv(MainArgs a) {
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         const int r = kv0 + 32 * grp + 8 * a4 + 4 * hh + bb;
-        if (r < Lk) out[(kv_start + r) * rs + (int64_t)h * D + 32 * nt + c] = to_bf16(acc[nt][4 * a4 + bb] * osc);
+        if (r < Lk) out[(kv_start + r) * rsk + (int64_t)hk * D + 32 * nt + c] = to_bf16(acc[nt][4 * a4 + bb] * osc);
       }
     }
   }
@@ -783,10 +791,13 @@ void fa_bwd_dq(MainArgs a) {
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
-  const int64_t rs = (int64_t)a.H * D;
+  const int64_t rs = (int64_t)a.H * D;    // row stride of the query-side tensors
   const int rsb = (int)(rs * 2);
-  const bf16* kb = a.k + kv_start * rs + (int64_t)h * D;
-  const bf16* vb = a.v + kv_start * rs + (int64_t)h * D;
+  const int64_t rsk = (int64_t)a.Hk * D;  // row stride of K, V
+  const int rskb = (int)(rsk * 2);
+  const int hk = h / (a.H / a.Hk);        // the K/V head this query head reads
+  const bf16* kb = a.k + kv_start * rsk + (int64_t)hk * D;
+  const bf16* vb = a.v + kv_start * rsk + (int64_t)hk * D;
   const bf16* qb = a.q + (q_start + i0) * rs + (int64_t)h * D;
   const bf16* db = a.dout + (q_start + i0) * rs + (int64_t)h * D;
   const int qi = i0 + 32 * w + c;  // this lane's query row (sequence-local) in S^T, dP^T and dQ^T
@@ -821,13 +832,13 @@ void fa_bwd_dq(MainArgs a) {
   for (int jj = 0; jj < NJ; ++jj) {
     const int p16 = 64 * (w + C::NW * jj) + lane;
     const int r = p16 / C::CPR, ch = p16 % C::CPR;
-    dma_off[jj] = r * rsb + (ch < D / 8 ? ch : 0) * 16;
+    dma_off[jj] = r * rskb + (ch < D / 8 ? ch : 0) * 16;
   }
   auto issue_kv = [&](int t, int bi) {
     const int j0 = t * BK;
-    const int64_t bytes = (int64_t)imin(Lk - j0, BK) * rsb;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (int64_t)j0 * rs, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (int64_t)j0 * rs, bytes);
+    const int64_t bytes = (int64_t)imin(Lk - j0, BK) * rskb;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (int64_t)j0 * rsk, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (int64_t)j0 * rsk, bytes);
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       const int j = w + C::NW * jj;
@@ -961,7 +972,7 @@ struct FwdArgs {
   float* m;  // [total_q][H]: row max of the scaled visible logits
   float* l;  // [total_q][H]: row sum of exp(scaled logit - m) over visible keys
   int64_t total_q, total_kv;
-  int H, batch, max_seqlen_q, max_seqlen_kv, padded;
+  int H, Hk, batch, max_seqlen_q, max_seqlen_kv, padded;  // query heads, K/V heads (H % Hk == 0)
   float scale_log2;  // scale * log2(e)
 };
 
@@ -1013,10 +1024,13 @@ void fa_fwd(FwdArgs a) {
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
-  const int64_t rs = (int64_t)a.H * D;
+  const int64_t rs = (int64_t)a.H * D;    // row stride of the query-side tensors
   const int rsb = (int)(rs * 2);
-  const bf16* kb = a.k + kv_start * rs + (int64_t)h * D;
-  const bf16* vb = a.v + kv_start * rs + (int64_t)h * D;
+  const int64_t rsk = (int64_t)a.Hk * D;  // row stride of K, V
+  const int rskb = (int)(rsk * 2);
+  const int hk = h / (a.H / a.Hk);        // the K/V head this query head reads
+  const bf16* kb = a.k + kv_start * rsk + (int64_t)hk * D;
+  const bf16* vb = a.v + kv_start * rsk + (int64_t)hk * D;
   const bf16* qb = a.q + (q_start + i0) * rs + (int64_t)h * D;
   const int qi = i0 + 32 * w + c;  // this lane's query row (sequence-local)
 
@@ -1042,13 +1056,13 @@ void fa_fwd(FwdArgs a) {
   for (int jj = 0; jj < NJ; ++jj) {
     const int p16 = 64 * (w + C::NW * jj) + lane;
     const int r = p16 / C::CPR, ch = p16 % C::CPR;
-    dma_off[jj] = r * rsb + (ch < D / 8 ? ch : 0) * 16;
+    dma_off[jj] = r * rskb + (ch < D / 8 ? ch : 0) * 16;
   }
   auto issue_kv = [&](int t, int bi) {
     const int j0 = t * BK;
-    const int64_t bytes = (int64_t)imin(Lk - j0, BK) * rsb;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (int64_t)j0 * rs, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (int64_t)j0 * rs, bytes);
+    const int64_t bytes = (int64_t)imin(Lk - j0, BK) * rskb;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (int64_t)j0 * rsk, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (int64_t)j0 * rsk, bytes);
 #pragma unroll
     for (int jj = 0; jj < NJ; ++jj) {
       const int j = w + C::NW * jj;

@@ -48,6 +48,7 @@ class Case:
     padded_len: int = 0        # slot length per sequence in padded modes (0 = packed)
     qk_mult: float = 1.0
     draw_lengths: tuple | None = None   # (count, lo, hi_inclusive): draw lengths from the generator
+    heads_kv: int = 0          # K/V heads (0 = heads); query head h reads K/V head h // (heads / heads_kv)
 
     @property
     def scale(self) -> float:
@@ -75,10 +76,10 @@ WORKLOADS = ["tiny", "dense", "varlen", "causal", "longpad"]
 
 
 def custom_case(name: str, heads: int, head_dim: int, mask: int, seed: int, seqlens_q, seqlens_kv=None,
-                padded_len: int = 0, qk_mult: float = 1.0) -> Case:
+                padded_len: int = 0, qk_mult: float = 1.0, heads_kv: int = 0) -> Case:
     return Case(name, heads=heads, head_dim=head_dim, mask=mask, seed=seed, seqlens_q=list(seqlens_q),
                 seqlens_kv=list(seqlens_q if seqlens_kv is None else seqlens_kv), padded_len=padded_len,
-                qk_mult=qk_mult)
+                qk_mult=qk_mult, heads_kv=heads_kv)
 
 
 def _cumsum(lengths) -> torch.Tensor:
@@ -91,7 +92,7 @@ def _cumsum(lengths) -> torch.Tensor:
 def make(case: Case | str) -> dict:
     """Draw one case. Returns CPU tensors and sizes:
 
-    q, k, v, do: bf16 [T, H, d]; cu_q, cu_kv: int32 [B+1]; and the ints/floats
+    q, do: bf16 [T_q, H, d]; k, v: bf16 [T_kv, H_kv, d]; cu_q, cu_kv: int32 [B+1]; and the ints/floats
     scale, mask, max_seqlen_q, max_seqlen_kv, batch.
     """
     if isinstance(case, str):
@@ -110,9 +111,10 @@ def make(case: Case | str) -> dict:
         tq, tkv = sum(lq), sum(lkv)
         msq, mskv = max(lq, default=0), max(lkv, default=0)
     h, d = case.heads, case.head_dim
+    hkv = case.heads_kv or h
     q = torch.randn((tq, h, d), generator=g, dtype=torch.float32)
-    k = torch.randn((tkv, h, d), generator=g, dtype=torch.float32)
-    v = torch.randn((tkv, h, d), generator=g, dtype=torch.float32)
+    k = torch.randn((tkv, hkv, d), generator=g, dtype=torch.float32)
+    v = torch.randn((tkv, hkv, d), generator=g, dtype=torch.float32)
     do = torch.randn((tq, h, d), generator=g, dtype=torch.float32)
     if case.qk_mult != 1.0:
         q.mul_(case.qk_mult)

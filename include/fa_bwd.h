@@ -72,24 +72,28 @@ typedef enum {
 typedef enum {
   FA_BWD_OK = 0,
   FA_BWD_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad mask code, bad scale, misalignment */
-  FA_BWD_ERR_UNSUPPORTED = 2,      /* head_dim other than 64 or 128 */
+  FA_BWD_ERR_UNSUPPORTED = 2,      /* head_dim other than 64 or 128; grouped heads in the single-pass form */
   FA_BWD_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed in fa_bwd_create */
   FA_BWD_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
 } fa_bwd_status;
 
 typedef struct {
   int32_t batch;         /* number of sequences (entries of cu_seqlens minus one), >= 1 */
-  int32_t num_heads;     /* heads of Q, K and V (no grouped heads), >= 1 */
+  int32_t num_heads;     /* heads of Q, O, dO, dQ, m, l, >= 1 */
   int32_t head_dim;      /* 64 or 128 */
   int32_t max_seqlen_q;  /* >= every L_b of the queries; the slot length in padded modes; >= 1 */
   int32_t max_seqlen_kv; /* same for keys/values */
   int64_t total_q;       /* rows of q, o, do, dq, m, l; >= 1 */
   int64_t total_kv;      /* rows of k, v, dk, dv; >= 1 */
   int32_t algorithm;     /* an fa_bwd_algo code */
+  int32_t num_heads_kv;  /* heads of K and V (and dK, dV): 0 = num_heads, else a divisor of num_heads;
+                            query head h reads K/V head h / (num_heads / num_heads_kv), and the
+                            gradient of a shared head sums over its query heads (grouped heads, as
+                            the jax cuDNN wrapper's API allows; recompute form only) */
 } fa_bwd_desc;
 
-/* Validates desc and allocates the device workspace of the handle on the
- * current HIP device: two fp32 [H][total_q] row-statistic arrays and, for
+/* Validates desc (a num_heads_kv of 0 is stored as num_heads) and allocates
+ * the device workspace of the handle on the current HIP device: two fp32 [H][total_q] row-statistic arrays and, for
  * FA_BWD_ALGO_SINGLE_PASS only, an fp32 dQ accumulator of total_q*H*head_dim
  * floats. On success *out holds a new handle; on failure *out is set to NULL.
  * Host-side checks run before any HIP call. */
@@ -99,15 +103,15 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out);
  * stream) and returns without waiting. The caller synchronises its stream
  * before reading dq/dk/dv.
  *   q, o, dout: bf16 [total_q][H][head_dim]        (read only)
- *   k, v:       bf16 [total_kv][H][head_dim]       (read only)
+ *   k, v:       bf16 [total_kv][H_kv][head_dim]    (read only; H_kv = num_heads_kv)
  *   m, l:       fp32 [total_q][H], row max of the scaled visible logits and
  *               the row sum of exp(scaled logit - m) over visible keys, as the
  *               forward produced them (not recomputed here; l > 0 on valid rows)
  *   cu_seqlens_q, cu_seqlens_kv: int32 [batch+1] device arrays (see above)
  *   scale:      the softmax scale applied to Q K^T (finite, > 0), e.g. 1/sqrt(head_dim)
  *   mask:       an fa_bwd_mask code
- *   dq:         bf16 [total_q][H][head_dim]  (written)
- *   dk, dv:     bf16 [total_kv][H][head_dim] (written)
+ *   dq:         bf16 [total_q][H][head_dim]     (written)
+ *   dk, dv:     bf16 [total_kv][H_kv][head_dim] (written)
  * Every argument is checked on the host first; an invalid one returns
  * FA_BWD_ERR_INVALID_ARGUMENT with nothing enqueued. FA_BWD_ERR_HIP reports a
  * failed launch. The handle's workspace is reused by every call, so one
@@ -131,7 +135,7 @@ fa_bwd_status fa_bwd_run_lse(fa_bwd_handle* h, const void* q, const void* k, con
  * consumes, for the sizes of the handle (its workspace is not used; FA_BWD_ALGO_* is ignored).
  * The softmax is the one step 2 of the SK-16 article inverts, P = exp(S*scale - m) / l.
  *   q:          bf16 [total_q][H][head_dim]   (read only)
- *   k, v:       bf16 [total_kv][H][head_dim]  (read only)
+ *   k, v:       bf16 [total_kv][H_kv][head_dim]  (read only)
  *   cu_seqlens_q, cu_seqlens_kv, scale, mask: as for fa_bwd_run
  *   o:          bf16 [total_q][H][head_dim]   (written)
  *   m:          fp32 [total_q][H]  (written) row max of the scaled visible logits

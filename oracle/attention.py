@@ -35,6 +35,11 @@ What it computes, and where the pages define it:
   l = sum over visible keys of exp(scaled logit - m), O = P V; this is the
   reading under which step 2 above is the softmax.
 
+* Grouped heads: K and V may have fewer heads than Q (a divisor of it). Query head h
+  reads key/value head h // (H_q / H_kv), consecutive query heads sharing one K/V head
+  (the grouping of the jax cuDNN wrapper's attention API); dK and dV of a shared head are
+  the sums over its query heads.
+
 Rows outside every sequence: forward gives O = 0, m = 0, l = 1 (finite filler
 that the backward never reads); backward gives dQ = dK = dV = 0. A valid query
 row with no visible key (only when its sequence has no keys) gets P = 0.
@@ -66,6 +71,13 @@ def segments(cu, mask: int, max_seqlen: int):
         start = b * max_seqlen if is_padded(mask) else cu[b]
         out.append((start, length))
     return out
+
+
+def kv_head(h: int, heads_q: int, heads_kv: int) -> int:
+    """The K/V head that query head h reads (consecutive query heads share one)."""
+    if heads_q % heads_kv:
+        raise ValueError(f"{heads_q} query heads are not a multiple of {heads_kv} key/value heads")
+    return h // (heads_q // heads_kv)
 
 
 def visible_block(rows, cols, causal: bool) -> np.ndarray:
@@ -147,7 +159,8 @@ def forward(q, k, v, cu_q, cu_kv, scale: float, mask: int, max_seqlen_q: int = 0
         if lq <= 0:
             continue
         for h in range(h_count):
-            ob, mb, lb = forward_head(q[qs:qs + lq, h], k[ks:ks + lk, h], v[ks:ks + lk, h], scale, causal)
+            hk = kv_head(h, h_count, k.shape[1])
+            ob, mb, lb = forward_head(q[qs:qs + lq, h], k[ks:ks + lk, hk], v[ks:ks + lk, hk], scale, causal)
             o[qs:qs + lq, h], m[qs:qs + lq, h], l[qs:qs + lq, h] = ob, mb, lb
     return o, m, l
 
@@ -166,9 +179,12 @@ def backward(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int,
             continue
         qsl, ksl = slice(qs, qs + max(lq, 0)), slice(ks, ks + max(lk, 0))
         for h in range(q.shape[1]):
-            r = backward_head(q[qsl, h], k[ksl, h], v[ksl, h], o[qsl, h], do[qsl, h],
+            hk = kv_head(h, q.shape[1], k.shape[1])
+            r = backward_head(q[qsl, h], k[ksl, hk], v[ksl, hk], o[qsl, h], do[qsl, h],
                               m[qsl, h], l[qsl, h], scale, causal)
-            dq[qsl, h], dk[ksl, h], dv[ksl, h] = r["dq"], r["dk"], r["dv"]
+            dq[qsl, h] = r["dq"]
+            dk[ksl, hk] += r["dk"]   # a shared K/V head collects the gradients of its query heads
+            dv[ksl, hk] += r["dv"]
     return dq, dk, dv
 
 
@@ -188,7 +204,8 @@ def forward_rows(q, k, v, cu_q, cu_kv, scale: float, mask: int, b: int, h: int, 
     qs, lq = segments(cu_q, mask, max_seqlen_q)[b]
     ks, lk = segments(cu_kv, mask, max_seqlen_kv)[b]
     causal = is_causal(mask)
-    Q, K, V = _f64(q[qs:qs + lq, h]), _f64(k[ks:ks + lk, h]), _f64(v[ks:ks + lk, h])
+    hk = kv_head(h, q.shape[1], k.shape[1])
+    Q, K, V = _f64(q[qs:qs + lq, h]), _f64(k[ks:ks + lk, hk]), _f64(v[ks:ks + lk, hk])
     o_out, m_out, l_out = [], [], []
     for i in q_rows:
         vis = visible_block([i], np.arange(lk), causal)[0]
@@ -209,7 +226,8 @@ def forward_rows(q, k, v, cu_q, cu_kv, scale: float, mask: int, b: int, h: int, 
 
 def backward_rows(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int, b: int, h: int,
                   q_rows, kv_rows, max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
-    """Selected outputs of one (b, h), each computed on its own.
+    """Selected outputs of sequence b, each computed on its own: rows of dQ of query head h and
+    rows of dK/dV of the K/V head that h reads (summed over the query heads sharing it).
 
     dQ row i needs row i of P and dS (all keys); dK/dV row j needs column j of
     P and dS (all queries). Indices are sequence-local. Returns
@@ -220,10 +238,18 @@ def backward_rows(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int, b:
     qs, lq = segments(cu_q, mask, max_seqlen_q)[b]
     ks, lk = segments(cu_kv, mask, max_seqlen_kv)[b]
     causal = is_causal(mask)
-    Q, K, V = _f64(q[qs:qs + lq, h]), _f64(k[ks:ks + lk, h]), _f64(v[ks:ks + lk, h])
-    O, dO = _f64(o[qs:qs + lq, h]), _f64(do[qs:qs + lq, h])
-    M, L = _f64(m[qs:qs + lq, h]), _f64(l[qs:qs + lq, h])
-    dq_out, dk_out, dv_out = [], [], []
+    hq_count, hk_count = q.shape[1], k.shape[1]
+    hk = kv_head(h, hq_count, hk_count)
+    K, V = _f64(k[ks:ks + lk, hk]), _f64(v[ks:ks + lk, hk])
+    d = q.shape[2]
+    dv_d = v.shape[2]
+
+    def head_slices(hq):
+        return (_f64(q[qs:qs + lq, hq]), _f64(o[qs:qs + lq, hq]), _f64(do[qs:qs + lq, hq]),
+                _f64(m[qs:qs + lq, hq]), _f64(l[qs:qs + lq, hq]))
+
+    Q, O, dO, M, L = head_slices(h)
+    dq_out = []
     for i in q_rows:
         vis = visible_block([i], np.arange(lk), causal)
         s = (Q[i:i + 1] @ K.T)
@@ -232,20 +258,21 @@ def backward_rows(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int, b:
         dvec = np.sum(O[i] * dO[i])
         ds = p * (dp - dvec)
         dq_out.append(scale * (ds @ K)[0])
-    if len(kv_rows):
+    dk_out = np.zeros((len(kv_rows), d))
+    dv_out = np.zeros((len(kv_rows), dv_d))
+    group = [hq for hq in range(hq_count) if kv_head(hq, hq_count, hk_count) == hk]
+    for hq in group if len(kv_rows) else []:
+        Q, O, dO, M, L = head_slices(hq)
         dvec_all = np.sum(O * dO, axis=1)
-    for j in kv_rows:
-        vis = visible_block(np.arange(lq), [j], causal)
-        s = Q @ K[j:j + 1].T
-        p = softmax_probs(scale * s, M, L, vis)
-        dp = dO @ V[j:j + 1].T
-        ds = p * (dp - dvec_all[:, None])
-        dk_out.append(scale * (ds.T @ Q)[0])
-        dv_out.append((p.T @ dO)[0])
-    d = q.shape[2]
-    dv_d = v.shape[2]
-    return (np.array(dq_out).reshape(-1, d), np.array(dk_out).reshape(-1, d),
-            np.array(dv_out).reshape(-1, dv_d))
+        for n, j in enumerate(kv_rows):
+            vis = visible_block(np.arange(lq), [j], causal)
+            s = Q @ K[j:j + 1].T
+            p = softmax_probs(scale * s, M, L, vis)
+            dp = dO @ V[j:j + 1].T
+            ds = p * (dp - dvec_all[:, None])
+            dk_out[n] += scale * (ds.T @ Q)[0]
+            dv_out[n] += (p.T @ dO)[0]
+    return np.array(dq_out).reshape(-1, d), dk_out, dv_out
 
 
 def loss(q, k, v, do, cu_q, cu_kv, scale: float, mask: int, max_seqlen_q: int = 0, max_seqlen_kv: int = 0) -> float:

@@ -65,6 +65,10 @@ def _create(**kw):
     (dict(algorithm=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(total_q=1 << 40, num_heads=8), B.FA_BWD_ERR_INVALID_ARGUMENT),          # index range
     (dict(max_seqlen_kv=1 << 30, num_heads=1 << 10, batch=1 << 10), B.FA_BWD_ERR_INVALID_ARGUMENT),  # grid size
+    (dict(num_heads=6, num_heads_kv=4), B.FA_BWD_ERR_INVALID_ARGUMENT),   # K/V heads must divide query heads
+    (dict(num_heads=4, num_heads_kv=-2), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(num_heads=4, num_heads_kv=8), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(num_heads=4, num_heads_kv=2, algorithm=1), B.FA_BWD_ERR_UNSUPPORTED),  # grouped heads: recompute form
 ])
 def test_create_rejects_bad_descriptors_before_any_hip_call(kw, status):
     st, h = _create(**kw)

@@ -15,7 +15,7 @@ import oracle
 from attention_backward_fa_amd import binding as B
 from attention_backward_fa_amd import inputs as I
 from tests import parity as P
-from tests.test_gpu_parity import CASES
+from tests.test_gpu_parity import CASES, GQA_CASES
 
 pytestmark = pytest.mark.gpu
 
@@ -42,7 +42,7 @@ def check_forward(inp, gpu, ref, rows=None):
     return dm, dlse
 
 
-@pytest.mark.parametrize("case", CASES, ids=[c.name for c in CASES])
+@pytest.mark.parametrize("case", CASES + GQA_CASES, ids=[c.name for c in CASES + GQA_CASES])
 def test_forward_parity(case):
     inp = I.make(case)
     print(f"[forward] {case.name}: T_q={inp['q'].shape[0]} H={case.heads} d={case.head_dim} mask={case.mask}",
@@ -56,8 +56,9 @@ def test_forward_parity(case):
     print(f"[forward] {case.name}: m err {dm:.2e} lse err {dlse:.2e}", flush=True)
 
 
-CHAIN = [c for c in CASES if c.name in ("sk16_t01", "ragged_causal_d128", "ragged_causal_d64", "kv_longer_causal",
-                                         "empty_sequence", "padded_causal_d128")]
+CHAIN = [c for c in CASES + GQA_CASES if c.name in ("sk16_t01", "ragged_causal_d128", "ragged_causal_d64",
+                                                     "kv_longer_causal", "empty_sequence", "padded_causal_d128",
+                                                     "gqa_causal_d128", "gqa_padded_causal_d128")]
 
 
 @pytest.mark.parametrize("case", CHAIN, ids=[c.name for c in CHAIN])
@@ -67,7 +68,7 @@ def test_forward_then_backward(case):
     dev = torch.device("cuda")
     t = {k: inp[k].to(dev) for k in ("q", "k", "v", "do", "cu_q", "cu_kv")}
     with B.FaBwd(inp["batch"], case.heads, case.head_dim, inp["max_seqlen_q"], inp["max_seqlen_kv"],
-                 inp["q"].shape[0], inp["k"].shape[0]) as op:
+                 inp["q"].shape[0], inp["k"].shape[0], num_heads_kv=inp["k"].shape[1]) as op:
         o, m, l = op.forward(t["q"], t["k"], t["v"], t["cu_q"], t["cu_kv"], inp["scale"], inp["mask"])
         dq, dk, dv = op.run(t["q"], t["k"], t["v"], o, t["do"], m, l, t["cu_q"], t["cu_kv"], inp["scale"],
                             inp["mask"])

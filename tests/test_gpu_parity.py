@@ -93,3 +93,31 @@ def test_algorithms_agree():
     # k-steps), so they agree to rounding, not bitwise
     for name, x, y in zip(("dq", "dk", "dv"), a, b):
         P.assert_close(name, x.numpy(), y.numpy().astype(np.float64))
+
+
+# grouped K/V heads (query head h reads K/V head h // (H / H_kv)); recompute form only
+GQA_CASES = [
+    I.custom_case("gqa_none_d128", 4, 128, NONE, 221, [200, 129], heads_kv=2),
+    I.custom_case("gqa_causal_d128", 8, 128, CAUSAL, 222, [300, 77], heads_kv=2),
+    I.custom_case("mqa_causal_d64", 4, 64, CAUSAL, 223, [255], heads_kv=1),
+    I.custom_case("gqa_padded_causal_d128", 6, 128, PADC, 224, [150, 97], padded_len=160, heads_kv=3),
+]
+
+
+@pytest.mark.parametrize("case", GQA_CASES, ids=[c.name for c in GQA_CASES])
+def test_parity_grouped_heads(case):
+    inp = I.make(case)
+    print(f"[parity-gqa] {case.name}: H={case.heads} H_kv={case.heads_kv} d={case.head_dim} mask={case.mask}",
+          flush=True)
+    o, m, l = P.oracle_stats(inp)
+    gpu = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_DEFAULT)
+    ref = P.oracle_backward(inp, o, m, l)
+    res = P.check_full(inp, gpu, ref)
+    print(f"[parity-gqa] {case.name}: " + " ".join(f"{k}: rel_l2={v[0]:.2e}" for k, v in res.items()), flush=True)
+
+
+def test_grouped_heads_single_pass_unsupported():
+    inp = I.make(GQA_CASES[0])
+    o, m, l = P.oracle_stats(inp)
+    with pytest.raises(NotImplementedError):
+        P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_SINGLE_PASS)

@@ -10,7 +10,8 @@ cuDNN ``MaskType``. The pins:
 * invariants: dS rows sum to 0 (so dK columns sum to 0), dV columns sum to dO
   columns, rowsum(O*dO) = rowsum(P*dP), causal zero patterns;
 * closed forms: one key, all-equal V rows, Q = 0;
-* torch fp64 autograd of softmax(scale*QK^T + mask) V, an independent library;
+* torch fp64 autograd of softmax(scale*QK^T + mask) V, an independent library (with grouped
+  K/V heads expanded by torch's repeat_interleave, so autograd sums the shared heads' gradients);
 * the forward on its own: O, the row max of the scaled logits and m + ln(l) against torch's
   softmax attention, max and logsumexp; the sampled-row forward against the full one;
 * planted mistakes in the oracle's own source, each caught by one of the above.
@@ -33,7 +34,7 @@ def _rand(shape, rng, mult=1.0):
     return rng.standard_normal(shape) * mult
 
 
-def make_problem(mask, lens_q, lens_kv, heads=2, d=4, seed=0, padded_len=0, mult=1.0):
+def make_problem(mask, lens_q, lens_kv, heads=2, d=4, seed=0, padded_len=0, mult=1.0, heads_kv=None):
     rng = np.random.default_rng(seed)
     if A.is_padded(mask):
         tq = tkv = len(lens_q) * padded_len
@@ -43,8 +44,9 @@ def make_problem(mask, lens_q, lens_kv, heads=2, d=4, seed=0, padded_len=0, mult
         msq, mskv = max(lens_q), max(lens_kv)
     cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
     cu_kv = np.concatenate([[0], np.cumsum(lens_kv)]).astype(np.int64)
-    return dict(q=_rand((tq, heads, d), rng, mult), k=_rand((tkv, heads, d), rng, mult),
-                v=_rand((tkv, heads, d), rng), do=_rand((tq, heads, d), rng),
+    hkv = heads if heads_kv is None else heads_kv
+    return dict(q=_rand((tq, heads, d), rng, mult), k=_rand((tkv, hkv, d), rng, mult),
+                v=_rand((tkv, hkv, d), rng), do=_rand((tq, heads, d), rng),
                 cu_q=cu_q, cu_kv=cu_kv, scale=1.0 / math.sqrt(d), mask=mask,
                 max_seqlen_q=msq, max_seqlen_kv=mskv)
 
@@ -97,6 +99,8 @@ def torch_reference(p):
     nb = len(p["cu_q"]) - 1
     padded = p["mask"] in (MASK_PADDING, MASK_PADDING_CAUSAL)
     causal = p["mask"] in (MASK_CAUSAL, MASK_PADDING_CAUSAL)
+    group = q.shape[1] // k.shape[1]
+    ke, ve = k.repeat_interleave(group, dim=1), v.repeat_interleave(group, dim=1)  # shared K/V heads
     total = torch.zeros((), dtype=torch.float64)
     for b in range(nb):
         lq = int(p["cu_q"][b + 1] - p["cu_q"][b])
@@ -106,7 +110,7 @@ def torch_reference(p):
         if lq == 0 or lk == 0:
             continue
         for h in range(q.shape[1]):
-            qh, kh, vh = q[qs:qs + lq, h], k[ks:ks + lk, h], v[ks:ks + lk, h]
+            qh, kh, vh = q[qs:qs + lq, h], ke[ks:ks + lk, h], ve[ks:ks + lk, h]
             logits = p["scale"] * qh @ kh.T
             if causal:
                 bias = torch.triu(torch.full((lq, lk), float("-inf"), dtype=torch.float64), diagonal=1)
@@ -374,6 +378,51 @@ def test_backward_from_lse_equals_backward_from_m_l(mask):
         np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
 
 
+# ---------------------------------------------------------------- grouped K/V heads
+
+GQA_CASES = [
+    # (mask, lens_q, lens_kv, d, padded_len, heads, heads_kv)
+    (MASK_NONE, [4], [5], 4, 0, 4, 2),
+    (MASK_CAUSAL, [5, 3], [5, 3], 4, 0, 4, 1),
+    (MASK_PADDING_CAUSAL, [4, 2], [4, 3], 4, 4, 6, 3),
+]
+
+
+@pytest.mark.parametrize("mask,lq,lk,d,padded,heads,heads_kv", GQA_CASES)
+def test_grouped_heads_finite_differences(mask, lq, lk, d, padded, heads, heads_kv):
+    p = make_problem(mask, lq, lk, heads=heads, d=d, seed=31 + heads_kv, padded_len=padded, heads_kv=heads_kv)
+    assert fd_error(p) < 2e-6
+
+
+@pytest.mark.parametrize("mask,lq,lk,d,padded,heads,heads_kv", GQA_CASES + [
+    (MASK_CAUSAL, [64, 37], [64, 37], 16, 0, 8, 2),
+])
+def test_grouped_heads_torch_fp64_autograd(mask, lq, lk, d, padded, heads, heads_kv):
+    p = make_problem(mask, lq, lk, heads=heads, d=d, seed=41 + heads_kv, padded_len=padded, mult=2.0,
+                     heads_kv=heads_kv)
+    assert torch_error(p) < 1e-12
+
+
+def test_grouped_heads_backward_rows_matches_full():
+    p = make_problem(MASK_CAUSAL, [30, 17], [30, 17], heads=4, d=8, seed=12, heads_kv=2)
+    o, m, l, dq, dk, dv = exact_backward(p)
+    for b, ((qs, lq), (ks, lk)) in enumerate(zip(A.segments(p["cu_q"], MASK_CAUSAL, 0),
+                                                 A.segments(p["cu_kv"], MASK_CAUSAL, 0))):
+        rows = [0, lq // 2, lq - 1]
+        for h in range(4):
+            sq, sk, sv = A.backward_rows(p["q"], p["k"], p["v"], o, p["do"], m, l, p["cu_q"], p["cu_kv"],
+                                         p["scale"], MASK_CAUSAL, b, h, rows, rows)
+            np.testing.assert_allclose(sq, dq[[qs + r for r in rows], h], rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(sk, dk[[ks + r for r in rows], h // 2], rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(sv, dv[[ks + r for r in rows], h // 2], rtol=1e-12, atol=1e-14)
+
+
+def test_grouped_heads_reject_non_divisor():
+    p = make_problem(MASK_NONE, [3], [3], heads=3, d=4, heads_kv=2)
+    with pytest.raises(ValueError):
+        A.forward(p["q"], p["k"], p["v"], p["cu_q"], p["cu_kv"], p["scale"], MASK_NONE)
+
+
 # ---------------------------------------------------------------- sampled rows == full backward
 
 @pytest.mark.parametrize("mask", [MASK_NONE, MASK_CAUSAL, MASK_PADDING_CAUSAL])
@@ -446,3 +495,11 @@ def test_planted_layout_mistake_fails_torch_check(monkeypatch):
     assert torch_error(p) < 1e-12
     _mutant(monkeypatch, "segments", "start = b * max_seqlen if is_padded(mask) else cu[b]", "start = cu[b]")
     assert torch_error(p) > 1e-3
+
+
+def test_planted_group_overwrite_fails_finite_differences(monkeypatch):
+    # a shared K/V head must collect the gradients of all its query heads, not keep the last one
+    p = make_problem(MASK_CAUSAL, [4], [4], heads=4, d=4, seed=51, heads_kv=2)
+    assert fd_error(p) < 2e-6
+    _mutant(monkeypatch, "backward", 'dk[ksl, hk] += r["dk"]', 'dk[ksl, hk] = r["dk"]')
+    assert fd_error(p) > 1e-3
