@@ -40,7 +40,7 @@ class FaBwdDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_kv", ctypes.c_int32),
                 ("total_q", ctypes.c_int64), ("total_kv", ctypes.c_int64), ("algorithm", ctypes.c_int32),
-                ("num_heads_kv", ctypes.c_int32)]
+                ("num_heads_kv", ctypes.c_int32), ("window", ctypes.c_int32)]
 
 
 _lib = None
@@ -94,10 +94,11 @@ def _check(status: int, what: str) -> None:
 
 def fa_bwd_create(batch: int, num_heads: int, head_dim: int, max_seqlen_q: int, max_seqlen_kv: int,
                   total_q: int, total_kv: int, algorithm: int = FA_BWD_ALGO_DEFAULT,
-                  num_heads_kv: int = 0) -> ctypes.c_void_p:
-    """Create a handle (and its device workspace on the current device); num_heads_kv 0 = num_heads."""
+                  num_heads_kv: int = 0, window: int = 0) -> ctypes.c_void_p:
+    """Create a handle (and its device workspace on the current device); num_heads_kv 0 = num_heads;
+    window 0 = none, w > 0 = each query i sees keys (i - w, i]."""
     desc = FaBwdDesc(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv, algorithm,
-                     num_heads_kv)
+                     num_heads_kv, window)
     handle = ctypes.c_void_p()
     _check(load_library().fa_bwd_create(ctypes.byref(desc), ctypes.byref(handle)), "fa_bwd_create")
     return handle
@@ -226,9 +227,9 @@ class FaBwd:
     """Owns one handle; ``run`` allocates nothing when the outputs are passed in."""
 
     def __init__(self, batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv,
-                 algorithm=FA_BWD_ALGO_DEFAULT, num_heads_kv=0):
+                 algorithm=FA_BWD_ALGO_DEFAULT, num_heads_kv=0, window=0):
         self.handle = fa_bwd_create(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv,
-                                    algorithm, num_heads_kv)
+                                    algorithm, num_heads_kv, window)
 
     def run(self, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq=None, dk=None, dv=None,
             stream=None):
@@ -270,16 +271,17 @@ class FaBwd:
 
 
 def attention_backward(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale: float, mask: int,
-                       max_seqlen_q: int, max_seqlen_kv: int, algorithm: int = FA_BWD_ALGO_DEFAULT):
+                       max_seqlen_q: int, max_seqlen_kv: int, algorithm: int = FA_BWD_ALGO_DEFAULT,
+                       window: int = 0):
     """One-shot call: create a handle, run on the current stream, destroy (which waits)."""
     with FaBwd(cu_seqlens_q.numel() - 1, q.shape[1], q.shape[2], max_seqlen_q, max_seqlen_kv,
-               q.shape[0], k.shape[0], algorithm, k.shape[1]) as op:
+               q.shape[0], k.shape[0], algorithm, k.shape[1], window) as op:
         return op.run(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask)
 
 
 def attention_forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, mask: int, max_seqlen_q: int,
-                      max_seqlen_kv: int):
+                      max_seqlen_kv: int, window: int = 0):
     """One-shot forward: returns O (bf16), m, l (fp32) on q's device."""
     with FaBwd(cu_seqlens_q.numel() - 1, q.shape[1], q.shape[2], max_seqlen_q, max_seqlen_kv,
-               q.shape[0], k.shape[0], num_heads_kv=k.shape[1]) as op:
+               q.shape[0], k.shape[0], num_heads_kv=k.shape[1], window=window) as op:
         return op.forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask)

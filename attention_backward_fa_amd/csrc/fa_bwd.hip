@@ -46,6 +46,8 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   if (hkv < 1 || d->num_heads % hkv != 0) return FA_BWD_ERR_INVALID_ARGUMENT;
   // the single-pass form owns one (kv tile, head) per workgroup; grouped K/V heads need the recompute form
   if (d->algorithm == FA_BWD_ALGO_SINGLE_PASS && hkv != d->num_heads) return FA_BWD_ERR_UNSUPPORTED;
+  if (d->window < 0) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (d->algorithm == FA_BWD_ALGO_SINGLE_PASS && d->window > 0) return FA_BWD_ERR_UNSUPPORTED;
   if (d->algorithm < FA_BWD_ALGO_DEFAULT || d->algorithm > FA_BWD_ALGO_RECOMPUTE_DQ) return FA_BWD_ERR_INVALID_ARGUMENT;
   // index arithmetic stays in int64; grids must fit the launch limits
   const int64_t rows = (d->total_q > d->total_kv ? d->total_q : d->total_kv);
@@ -131,6 +133,7 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.max_seqlen_kv = d.max_seqlen_kv;
   ma.padded = padded;
   ma.causal = causal;
+  ma.window = d.window;
   ma.scale_log2 = scale * fa::kLog2e;
   ma.scale = scale;
   const int64_t kv_tiles = (d.max_seqlen_kv + fa::MainCfg<D>::BN - 1) / fa::MainCfg<D>::BN;
@@ -142,10 +145,12 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
       fa::fa_bwd_main<D, false, true><<<grid, dim3(256), 0, stream>>>(ma);
   } else {
     const dim3 dgrid((unsigned)(kv_tiles * d.num_heads_kv * d.batch));  // (kv tile, K/V head, sequence)
-    if (causal)
-      fa::fa_bwd_dkdv<D, true><<<dgrid, dim3(512), 0, stream>>>(ma);
+    if (d.window > 0)  // the window implies the causal bound
+      fa::fa_bwd_dkdv<D, true, true><<<dgrid, dim3(512), 0, stream>>>(ma);
+    else if (causal)
+      fa::fa_bwd_dkdv<D, true, false><<<dgrid, dim3(512), 0, stream>>>(ma);
     else
-      fa::fa_bwd_dkdv<D, false><<<dgrid, dim3(512), 0, stream>>>(ma);
+      fa::fa_bwd_dkdv<D, false, false><<<dgrid, dim3(512), 0, stream>>>(ma);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return FA_BWD_ERR_HIP;
@@ -157,10 +162,12 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   } else {
     const int64_t q_tiles = (d.max_seqlen_q + fa::DqCfg<D>::BQ - 1) / fa::DqCfg<D>::BQ;
     const dim3 qgrid((unsigned)(q_tiles * d.num_heads * d.batch));
-    if (causal)
-      fa::fa_bwd_dq<D, true><<<qgrid, dim3(256), 0, stream>>>(ma);
+    if (d.window > 0)
+      fa::fa_bwd_dq<D, true, true><<<qgrid, dim3(256), 0, stream>>>(ma);
+    else if (causal)
+      fa::fa_bwd_dq<D, true, false><<<qgrid, dim3(256), 0, stream>>>(ma);
     else
-      fa::fa_bwd_dq<D, false><<<qgrid, dim3(256), 0, stream>>>(ma);
+      fa::fa_bwd_dq<D, false, false><<<qgrid, dim3(256), 0, stream>>>(ma);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return FA_BWD_ERR_HIP;
@@ -193,6 +200,7 @@ fa_bwd_status launch_fwd(fa_bwd_handle* h, const void* q, const void* k, const v
   fa.max_seqlen_kv = d.max_seqlen_kv;
   fa.padded = padded;
   fa.scale_log2 = scale * fa::kLog2e;
+  fa.window = d.window;
   hipEvent_t* ev = nullptr;
   if (h->profiling && h->recorded < kMaxProfiledRuns) {
     const size_t base = (size_t)h->recorded * 4;
@@ -215,10 +223,12 @@ fa_bwd_status launch_fwd(fa_bwd_handle* h, const void* q, const void* k, const v
   using QC = fa::DqCfg<D>;
   const int64_t q_tiles = (d.max_seqlen_q + QC::BQ - 1) / QC::BQ;
   const dim3 grid((unsigned)(q_tiles * d.num_heads * d.batch));
-  if (causal)
-    fa::fa_fwd<D, true><<<grid, dim3(256), 0, stream>>>(fa);
+  if (d.window > 0)
+    fa::fa_fwd<D, true, true><<<grid, dim3(256), 0, stream>>>(fa);
+  else if (causal)
+    fa::fa_fwd<D, true, false><<<grid, dim3(256), 0, stream>>>(fa);
   else
-    fa::fa_fwd<D, false><<<grid, dim3(256), 0, stream>>>(fa);
+    fa::fa_fwd<D, false, false><<<grid, dim3(256), 0, stream>>>(fa);
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && (hipEventRecord(ev[2], stream) != hipSuccess || hipEventRecord(ev[3], stream) != hipSuccess))
     return FA_BWD_ERR_HIP;

@@ -121,6 +121,7 @@ struct MainArgs {
   bf16* dv;
   int64_t total_q, total_kv;
   int H, Hk, batch, max_seqlen_q, max_seqlen_kv, padded, causal;  // query heads, K/V heads (H % Hk == 0)
+  int window;        // > 0: each query sees only its left local window of keys (i - window, i]
   float scale_log2;  // scale * log2(e)
   float scale;
 };
@@ -179,6 +180,7 @@ __device__ __forceinline__ int clamp_len(int64_t start, int len, int64_t total) 
 }
 
 __device__ __forceinline__ int imin(int x, int y) { return x < y ? x : y; }
+__device__ __forceinline__ int imax(int x, int y) { return x > y ? x : y; }
 
 // WITH_DQ: the single-pass form that also forms the dQ partial of every (q tile, kv tile)
 // pair and adds it to the fp32 accumulator with atomics; without it the kernel produces dK
@@ -513,7 +515,7 @@ struct DkdvCfg {
 // each passes the bf16 half its partner needs (dS of M-tile 0, P of M-tile 1) through LDS.
 // Each wave so holds one fp32 accumulator tile, two waves fit on a SIMD, and one's softmax runs
 // beside the other's MFMAs.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -574,7 +576,9 @@ void fa_bwd_dkdv(MainArgs a) {
   // the tile of the first key on); step st is q tile qt0 + st % nq of query head hk * G + st / nq
   const int n_qt = (Lq + BM - 1) / BM;
   const int qt0 = CAUSAL ? kv0 / BM : 0;
-  const int nq = n_qt > qt0 ? n_qt - qt0 : 0;
+  // window: the last query that sees a key of this tile is kv0 + BN - 2 + window
+  const int qt_end = WINDOW ? imin(n_qt, (kv0 + BN - 2 + a.window) / BM + 1) : n_qt;
+  const int nq = qt_end > qt0 ? qt_end - qt0 : 0;
   const int n_steps = G * nq;
   auto step_head = [&](int st) { return hk * G + st / nq; };
   auto step_tile = [&](int st) { return qt0 + st % nq; };
@@ -676,7 +680,12 @@ void fa_bwd_dkdv(MainArgs a) {
       for (int bb = 0; bb < 4; ++bb) {
         const int j = 4 * a4 + bb;
         float p = fast_exp2(s[j] * a.scale_log2 - lse[bb]);
-        if constexpr (CAUSAL) p = (jrel <= tile_row(8 * a4 + 4 * hh + bb)) ? p : 0.f;
+        if constexpr (WINDOW) {  // key j visible from query i iff i - window < j <= i
+          const int r = tile_row(8 * a4 + 4 * hh + bb);
+          p = (jrel <= r && r - jrel < a.window) ? p : 0.f;
+        } else if constexpr (CAUSAL) {
+          p = (jrel <= tile_row(8 * a4 + 4 * hh + bb)) ? p : 0.f;
+        }
         pk[j >> 3][j & 7] = to_bf16(p);
         dsk[j >> 3][j & 7] = to_bf16(p * (dp[j] - dd[bb]));
       }
@@ -765,7 +774,7 @@ struct DqCfg {
 // dQ of one (q tile, head, sequence): loops over the kv tiles, recomputes S^T = K Q^T and
 // dP^T = V dO^T with the forward's statistics (steps 1-5 of the per-tile math), and
 // accumulates dQ^T = K^T dS^T (step 8) in registers; dQ is written once, in bf16.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -819,6 +828,8 @@ void fa_bwd_dq(MainArgs a) {
 
   int n_kt = (Lk + BK - 1) / BK;
   if (CAUSAL) n_kt = imin(n_kt, (i0 + BQ - 1) / BK + 1);
+  // window: the first query of the tile sees no key before i0 - window + 1
+  const int t0 = WINDOW ? imax(0, i0 - a.window + 1) / BK : 0;
 
   {  // zero the K and V buffers once (rows past the sequence are masked, but must be finite)
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -858,13 +869,13 @@ void fa_bwd_dq(MainArgs a) {
   for (int nt = 0; nt < C::NTD; ++nt) acc[nt] = f32x16{};
 
   int buf = 0;
-  if (n_kt > 0) issue_kv(0, 0);
+  if (n_kt > t0) issue_kv(t0, 0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
 
   const int arow = tile_row(c) * QS + 8 * hh;
   const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
-  for (int t = 0; t < n_kt; ++t, buf ^= 1) {
+  for (int t = t0; t < n_kt; ++t, buf ^= 1) {
     if (t + 1 < n_kt) issue_kv(t + 1, buf ^ 1);
     const bf16* sk = (const bf16*)(smem + C::OFF_K + buf * C::TILE_BYTES);
     const bf16* sv = (const bf16*)(smem + C::OFF_V + buf * C::TILE_BYTES);
@@ -901,6 +912,7 @@ void fa_bwd_dq(MainArgs a) {
     // steps 2 and 5: P = exp2(S*scale*log2e - lse2), dS = P (dP - D); key row j = t*BK + kv row.
     // Visible iff j < Lk and (causal) j <= qi: one bound per lane on the tile-local kv row.
     const int lim = CAUSAL ? imin(Lk - 1, qi) - t * BK : Lk - 1 - t * BK;
+    const int lo = qi - a.window + 1 - t * BK;  // window: first visible tile-local key
     bf16x8 dsk[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -910,7 +922,8 @@ void fa_bwd_dq(MainArgs a) {
         for (int bb = 0; bb < 4; ++bb) {
           const int j = 4 * a4 + bb;
           float p = fast_exp2(s[mt][j] * a.scale_log2 - lse);
-          p = (32 * mt + tile_row(8 * a4 + 4 * hh + bb) <= lim) ? p : 0.f;
+          const int kr = 32 * mt + tile_row(8 * a4 + 4 * hh + bb);
+          p = (kr <= lim && (!WINDOW || kr >= lo)) ? p : 0.f;
           dsk[mt][j >> 3][j & 7] = to_bf16(p * (dp[mt][j] - dd));
         }
       }
@@ -973,6 +986,7 @@ struct FwdArgs {
   float* l;  // [total_q][H]: row sum of exp(scaled logit - m) over visible keys
   int64_t total_q, total_kv;
   int H, Hk, batch, max_seqlen_q, max_seqlen_kv, padded;  // query heads, K/V heads (H % Hk == 0)
+  int window;        // > 0: each query sees only its left local window of keys (i - window, i]
   float scale_log2;  // scale * log2(e)
 };
 
@@ -999,7 +1013,7 @@ __global__ __launch_bounds__(256) void fa_fwd_fill(FwdArgs a) {
 // once per row. Same tiling as the dQ kernel: Q in registers, K and V tiles of 64 keys streamed
 // through LDS, each lane owns one query row (its MFMA column), so the running maximum, the row sum
 // and the rescaling of its O row are per-lane values combined with the partner lane (lane ^ 32).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fa_fwd(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -1043,6 +1057,8 @@ void fa_fwd(FwdArgs a) {
 
   int n_kt = (Lk + BK - 1) / BK;
   if (CAUSAL) n_kt = imin(n_kt, (i0 + BQ - 1) / BK + 1);
+  // window: the first query of the tile sees no key before i0 - window + 1
+  const int t0 = WINDOW ? imax(0, i0 - a.window + 1) / BK : 0;
 
   {  // zero the K and V buffers once (keys past the sequence are masked, but must be finite)
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -1084,13 +1100,13 @@ void fa_fwd(FwdArgs a) {
   float lrun = 0.f;                // this lane's part of sum exp2(S*scale*log2(e) - mrun)
 
   int buf = 0;
-  if (n_kt > 0) issue_kv(0, 0);
+  if (n_kt > t0) issue_kv(t0, 0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
 
   const int arow = tile_row(c) * QS + 8 * hh;
   const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
-  for (int t = 0; t < n_kt; ++t, buf ^= 1) {
+  for (int t = t0; t < n_kt; ++t, buf ^= 1) {
     if (t + 1 < n_kt) issue_kv(t + 1, buf ^ 1);
     const bf16* sk = (const bf16*)(smem + C::OFF_K + buf * C::TILE_BYTES);
     const bf16* sv = (const bf16*)(smem + C::OFF_V + buf * C::TILE_BYTES);
@@ -1115,13 +1131,15 @@ void fa_fwd(FwdArgs a) {
     }
     // visible iff key j < Lk and (causal) j <= qi: one bound per lane on the tile-local key
     const int lim = CAUSAL ? imin(Lk - 1, qi) - t * BK : Lk - 1 - t * BK;
+    const int lo = qi - a.window + 1 - t * BK;  // window: first visible tile-local key
     float x[2][16];
     float tmax = -__builtin_inff();
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const bool vis = 32 * mt + tile_row(8 * (j >> 2) + 4 * hh + (j & 3)) <= lim;
+        const int kr = 32 * mt + tile_row(8 * (j >> 2) + 4 * hh + (j & 3));
+        const bool vis = kr <= lim && (!WINDOW || kr >= lo);
         x[mt][j] = vis ? s[mt][j] * a.scale_log2 : -__builtin_inff();
         tmax = fmaxf(tmax, x[mt][j]);
       }

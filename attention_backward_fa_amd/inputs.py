@@ -49,6 +49,7 @@ class Case:
     qk_mult: float = 1.0
     draw_lengths: tuple | None = None   # (count, lo, hi_inclusive): draw lengths from the generator
     heads_kv: int = 0          # K/V heads (0 = heads); query head h reads K/V head h // (heads / heads_kv)
+    window: int = 0            # > 0: each query i sees only keys (i - window, i]
 
     @property
     def scale(self) -> float:
@@ -76,10 +77,10 @@ WORKLOADS = ["tiny", "dense", "varlen", "causal", "longpad"]
 
 
 def custom_case(name: str, heads: int, head_dim: int, mask: int, seed: int, seqlens_q, seqlens_kv=None,
-                padded_len: int = 0, qk_mult: float = 1.0, heads_kv: int = 0) -> Case:
+                padded_len: int = 0, qk_mult: float = 1.0, heads_kv: int = 0, window: int = 0) -> Case:
     return Case(name, heads=heads, head_dim=head_dim, mask=mask, seed=seed, seqlens_q=list(seqlens_q),
                 seqlens_kv=list(seqlens_q if seqlens_kv is None else seqlens_kv), padded_len=padded_len,
-                qk_mult=qk_mult, heads_kv=heads_kv)
+                qk_mult=qk_mult, heads_kv=heads_kv, window=window)
 
 
 def _cumsum(lengths) -> torch.Tensor:
@@ -126,5 +127,5 @@ def make(case: Case | str) -> dict:
         "cu_q": _cumsum(lq), "cu_kv": _cumsum(lkv),
         "scale": case.scale, "mask": case.mask, "batch": batch,
         "max_seqlen_q": msq, "max_seqlen_kv": mskv, "seed": case.seed,
-        "seqlens_q": lq, "seqlens_kv": lkv,
+        "seqlens_q": lq, "seqlens_kv": lkv, "window": case.window,
     }

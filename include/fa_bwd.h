@@ -72,7 +72,8 @@ typedef enum {
 typedef enum {
   FA_BWD_OK = 0,
   FA_BWD_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad mask code, bad scale, misalignment */
-  FA_BWD_ERR_UNSUPPORTED = 2,      /* head_dim other than 64 or 128; grouped heads in the single-pass form */
+  FA_BWD_ERR_UNSUPPORTED = 2,      /* head_dim other than 64 or 128; grouped heads or a window in the
+                                      single-pass form */
   FA_BWD_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed in fa_bwd_create */
   FA_BWD_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
 } fa_bwd_status;
@@ -90,6 +91,9 @@ typedef struct {
                             query head h reads K/V head h / (num_heads / num_heads_kv), and the
                             gradient of a shared head sums over its query heads (grouped heads, as
                             the jax cuDNN wrapper's API allows; recompute form only) */
+  int32_t window;        /* 0: no window; w > 0: every query i sees only its left local window of keys
+                            (i - w, i] (the jax cuDNN wrapper's sliding_window_length), which implies
+                            the causal bound whatever the mask code; recompute form and forward only */
 } fa_bwd_desc;
 
 /* Validates desc (a num_heads_kv of 0 is stored as num_heads) and allocates

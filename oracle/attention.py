@@ -35,6 +35,9 @@ What it computes, and where the pages define it:
   l = sum over visible keys of exp(scaled logit - m), O = P V; this is the
   reading under which step 2 above is the softmax.
 
+* Sliding window (jax cuDNN wrapper, ``sliding_window_length``): with a window w > 0 each query
+  i sees only its left local window of keys (i - w, i]; the window implies the causal bound
+  whatever the mask code. w = 0 means no window.
 * Grouped heads: K and V may have fewer heads than Q (a divisor of it). Query head h
   reads key/value head h // (H_q / H_kv), consecutive query heads sharing one K/V head
   (the grouping of the jax cuDNN wrapper's attention API); dK and dV of a shared head are
@@ -80,19 +83,22 @@ def kv_head(h: int, heads_q: int, heads_kv: int) -> int:
     return h // (heads_q // heads_kv)
 
 
-def visible_block(rows, cols, causal: bool) -> np.ndarray:
+def visible_block(rows, cols, causal: bool, window: int = 0) -> np.ndarray:
     """Boolean [len(rows), len(cols)]: may query rows[a] attend to key cols[b]
-    (sequence-local indices; causal: key j visible from query i iff j <= i)."""
+    (sequence-local indices; causal: key j visible from query i iff j <= i; a window w > 0
+    restricts every query to its left local window (i - w, i])."""
     i = np.asarray(rows)[:, None]
     j = np.asarray(cols)[None, :]
+    if window > 0:
+        return (j <= i) & (j > i - window)
     if causal:
         return j <= i
     return np.ones((i.shape[0], j.shape[1]), dtype=bool)
 
 
-def visible(lq: int, lk: int, causal: bool) -> np.ndarray:
+def visible(lq: int, lk: int, causal: bool, window: int = 0) -> np.ndarray:
     """Boolean [lq, lk]: visibility of every (query, key) pair of one sequence."""
-    return visible_block(np.arange(lq), np.arange(lk), causal)
+    return visible_block(np.arange(lq), np.arange(lk), causal, window)
 
 
 def _f64(x) -> np.ndarray:
@@ -112,11 +118,11 @@ def softmax_probs(s_scaled: np.ndarray, m: np.ndarray, l: np.ndarray, vis: np.nd
     return np.where(vis & ok, np.exp(z) / np.where(ok, l[:, None], 1.0), 0.0)
 
 
-def forward_head(q, k, v, scale: float, causal: bool):
+def forward_head(q, k, v, scale: float, causal: bool, window: int = 0):
     """Forward for one (b, h): returns O [Lq,d], m [Lq], l [Lq] in fp64."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     lq, lk = q.shape[0], k.shape[0]
-    vis = visible(lq, lk, causal)
+    vis = visible(lq, lk, causal, window)
     s = scale * (q @ k.T)
     has_key = vis.any(axis=1)
     m = np.where(has_key, np.max(np.where(vis, s, -np.inf), axis=1, initial=-np.inf), 0.0)
@@ -127,7 +133,7 @@ def forward_head(q, k, v, scale: float, causal: bool):
     return o, m, l
 
 
-def backward_head(q, k, v, o, do, m, l, scale: float, causal: bool):
+def backward_head(q, k, v, o, do, m, l, scale: float, causal: bool, window: int = 0):
     """Backward for one (b, h), steps 1-8 of the module docstring.
 
     Inputs are one sequence's rows of one head; everything is promoted to fp64.
@@ -135,7 +141,7 @@ def backward_head(q, k, v, o, do, m, l, scale: float, causal: bool):
     """
     q, k, v, o, do = _f64(q), _f64(k), _f64(v), _f64(o), _f64(do)
     m, l = _f64(m), _f64(l)
-    vis = visible(q.shape[0], k.shape[0], causal)
+    vis = visible(q.shape[0], k.shape[0], causal, window)
     s = q @ k.T                                   # 1
     p = softmax_probs(scale * s, m, l, vis)       # 2
     dp = do @ v.T                                 # 3
@@ -147,7 +153,8 @@ def backward_head(q, k, v, o, do, m, l, scale: float, causal: bool):
     return {"dq": dq, "dk": dk, "dv": dv, "p": p, "dp": dp, "dvec": dvec, "ds": ds}
 
 
-def forward(q, k, v, cu_q, cu_kv, scale: float, mask: int, max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
+def forward(q, k, v, cu_q, cu_kv, scale: float, mask: int, max_seqlen_q: int = 0, max_seqlen_kv: int = 0,
+            window: int = 0):
     """Forward over [T, H, d] inputs. Returns fp64 O [Tq,H,d], m [Tq,H], l [Tq,H]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     tq, h_count, d = q.shape
@@ -160,13 +167,13 @@ def forward(q, k, v, cu_q, cu_kv, scale: float, mask: int, max_seqlen_q: int = 0
             continue
         for h in range(h_count):
             hk = kv_head(h, h_count, k.shape[1])
-            ob, mb, lb = forward_head(q[qs:qs + lq, h], k[ks:ks + lk, hk], v[ks:ks + lk, hk], scale, causal)
+            ob, mb, lb = forward_head(q[qs:qs + lq, h], k[ks:ks + lk, hk], v[ks:ks + lk, hk], scale, causal, window)
             o[qs:qs + lq, h], m[qs:qs + lq, h], l[qs:qs + lq, h] = ob, mb, lb
     return o, m, l
 
 
 def backward(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int,
-             max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
+             max_seqlen_q: int = 0, max_seqlen_kv: int = 0, window: int = 0):
     """Backward over [T, H, d] inputs. Returns fp64 dQ [Tq,H,d], dK, dV [Tkv,H,d]."""
     q, k, v, o, do = _f64(q), _f64(k), _f64(v), _f64(o), _f64(do)
     m, l = _f64(m), _f64(l)
@@ -181,7 +188,7 @@ def backward(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int,
         for h in range(q.shape[1]):
             hk = kv_head(h, q.shape[1], k.shape[1])
             r = backward_head(q[qsl, h], k[ksl, hk], v[ksl, hk], o[qsl, h], do[qsl, h],
-                              m[qsl, h], l[qsl, h], scale, causal)
+                              m[qsl, h], l[qsl, h], scale, causal, window)
             dq[qsl, h] = r["dq"]
             dk[ksl, hk] += r["dk"]   # a shared K/V head collects the gradients of its query heads
             dv[ksl, hk] += r["dv"]
@@ -189,16 +196,17 @@ def backward(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int,
 
 
 def backward_from_lse(q, k, v, o, do, lse, cu_q, cu_kv, scale: float, mask: int,
-                      max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
+                      max_seqlen_q: int = 0, max_seqlen_kv: int = 0, window: int = 0):
     """Backward from one log-sum-exp statistic per row (lse = m + ln l, the single softmax statistic
     of the jax cuDNN wrapper): step 2 reads P = exp(S*scale - lse), which is the step-2 formula with
     m = lse and l = 1."""
     lse = _f64(lse)
-    return backward(q, k, v, o, do, lse, np.ones_like(lse), cu_q, cu_kv, scale, mask, max_seqlen_q, max_seqlen_kv)
+    return backward(q, k, v, o, do, lse, np.ones_like(lse), cu_q, cu_kv, scale, mask, max_seqlen_q, max_seqlen_kv,
+                    window)
 
 
 def forward_rows(q, k, v, cu_q, cu_kv, scale: float, mask: int, b: int, h: int, q_rows,
-                 max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
+                 max_seqlen_q: int = 0, max_seqlen_kv: int = 0, window: int = 0):
     """O, m, l of selected query rows of one (b, h), each row computed on its own with the steps
     of ``forward_head``; indices are sequence-local. Returns fp64 O [n, d], m [n], l [n]."""
     qs, lq = segments(cu_q, mask, max_seqlen_q)[b]
@@ -208,7 +216,7 @@ def forward_rows(q, k, v, cu_q, cu_kv, scale: float, mask: int, b: int, h: int, 
     Q, K, V = _f64(q[qs:qs + lq, h]), _f64(k[ks:ks + lk, hk]), _f64(v[ks:ks + lk, hk])
     o_out, m_out, l_out = [], [], []
     for i in q_rows:
-        vis = visible_block([i], np.arange(lk), causal)[0]
+        vis = visible_block([i], np.arange(lk), causal, window)[0]
         s = scale * (Q[i] @ K.T)
         if not vis.any():
             o_out.append(np.zeros(V.shape[1]))
@@ -225,7 +233,7 @@ def forward_rows(q, k, v, cu_q, cu_kv, scale: float, mask: int, b: int, h: int, 
 
 
 def backward_rows(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int, b: int, h: int,
-                  q_rows, kv_rows, max_seqlen_q: int = 0, max_seqlen_kv: int = 0):
+                  q_rows, kv_rows, max_seqlen_q: int = 0, max_seqlen_kv: int = 0, window: int = 0):
     """Selected outputs of sequence b, each computed on its own: rows of dQ of query head h and
     rows of dK/dV of the K/V head that h reads (summed over the query heads sharing it).
 
@@ -251,7 +259,7 @@ def backward_rows(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int, b:
     Q, O, dO, M, L = head_slices(h)
     dq_out = []
     for i in q_rows:
-        vis = visible_block([i], np.arange(lk), causal)
+        vis = visible_block([i], np.arange(lk), causal, window)
         s = (Q[i:i + 1] @ K.T)
         p = softmax_probs(scale * s, M[i:i + 1], L[i:i + 1], vis)
         dp = dO[i:i + 1] @ V.T
@@ -265,7 +273,7 @@ def backward_rows(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int, b:
         Q, O, dO, M, L = head_slices(hq)
         dvec_all = np.sum(O * dO, axis=1)
         for n, j in enumerate(kv_rows):
-            vis = visible_block(np.arange(lq), [j], causal)
+            vis = visible_block(np.arange(lq), [j], causal, window)
             s = Q @ K[j:j + 1].T
             p = softmax_probs(scale * s, M, L, vis)
             dp = dO @ V[j:j + 1].T
@@ -275,9 +283,10 @@ def backward_rows(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int, b:
     return np.array(dq_out).reshape(-1, d), dk_out, dv_out
 
 
-def loss(q, k, v, do, cu_q, cu_kv, scale: float, mask: int, max_seqlen_q: int = 0, max_seqlen_kv: int = 0) -> float:
+def loss(q, k, v, do, cu_q, cu_kv, scale: float, mask: int, max_seqlen_q: int = 0, max_seqlen_kv: int = 0,
+         window: int = 0) -> float:
     """Scalar sum(O * dO) with dO a fixed cotangent; its gradient is (dQ, dK, dV)."""
-    o, _, _ = forward(q, k, v, cu_q, cu_kv, scale, mask, max_seqlen_q, max_seqlen_kv)
+    o, _, _ = forward(q, k, v, cu_q, cu_kv, scale, mask, max_seqlen_q, max_seqlen_kv, window)
     return float(np.sum(o * _f64(do)))
 
 

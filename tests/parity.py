@@ -20,7 +20,7 @@ MAX_ABS_TOL = 3e-2
 def oracle_stats(inp):
     """O (bf16), m, l (fp32) from the oracle's fp64 forward on the bf16 inputs."""
     o, m, l = oracle.forward(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_kv"], inp["scale"], inp["mask"],
-                             inp["max_seqlen_q"], inp["max_seqlen_kv"])
+                             inp["max_seqlen_q"], inp["max_seqlen_kv"], inp.get("window", 0))
     return (torch.from_numpy(o).to(torch.bfloat16), torch.from_numpy(m).to(torch.float32),
             torch.from_numpy(l).to(torch.float32))
 
@@ -31,14 +31,14 @@ def run_gpu(inp, o, m, l, device="cuda", algorithm=binding.FA_BWD_ALGO_DEFAULT):
     t = {k: inp[k].to(dev) for k in ("q", "k", "v", "do", "cu_q", "cu_kv")}
     dq, dk, dv = binding.attention_backward(t["q"], t["k"], t["v"], o.to(dev), t["do"], m.to(dev), l.to(dev),
                                             t["cu_q"], t["cu_kv"], inp["scale"], inp["mask"],
-                                            inp["max_seqlen_q"], inp["max_seqlen_kv"], algorithm)
+                                            inp["max_seqlen_q"], inp["max_seqlen_kv"], algorithm, inp.get("window", 0))
     torch.cuda.synchronize()
     return dq.float().cpu(), dk.float().cpu(), dv.float().cpu()
 
 
 def oracle_backward(inp, o, m, l):
     return oracle.backward(inp["q"], inp["k"], inp["v"], o, inp["do"], m, l, inp["cu_q"], inp["cu_kv"],
-                           inp["scale"], inp["mask"], inp["max_seqlen_q"], inp["max_seqlen_kv"])
+                           inp["scale"], inp["mask"], inp["max_seqlen_q"], inp["max_seqlen_kv"], inp.get("window", 0))
 
 
 def metrics(gpu, ref):

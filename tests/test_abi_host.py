@@ -69,6 +69,8 @@ def _create(**kw):
     (dict(num_heads=4, num_heads_kv=-2), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(num_heads=4, num_heads_kv=8), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(num_heads=4, num_heads_kv=2, algorithm=1), B.FA_BWD_ERR_UNSUPPORTED),  # grouped heads: recompute form
+    (dict(window=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(window=64, algorithm=1), B.FA_BWD_ERR_UNSUPPORTED),                    # window: recompute form
 ])
 def test_create_rejects_bad_descriptors_before_any_hip_call(kw, status):
     st, h = _create(**kw)

@@ -121,3 +121,32 @@ def test_grouped_heads_single_pass_unsupported():
     o, m, l = P.oracle_stats(inp)
     with pytest.raises(NotImplementedError):
         P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_SINGLE_PASS)
+
+
+# sliding window: each query i sees keys (i - w, i] only (recompute form)
+WINDOW_CASES = [
+    I.custom_case("window_causal_d128", 2, 128, CAUSAL, 231, [300, 129], window=64),
+    I.custom_case("window_none_d64", 2, 64, NONE, 232, [257], window=40),
+    I.custom_case("window_one_d128", 2, 128, CAUSAL, 233, [130], window=1),
+    I.custom_case("window_wide_padded_d128", 2, 128, PADC, 234, [200, 90], padded_len=224, window=300),
+    I.custom_case("window_gqa_causal_d128", 4, 128, CAUSAL, 235, [333], heads_kv=2, window=128),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=[c.name for c in WINDOW_CASES])
+def test_parity_window(case):
+    inp = I.make(case)
+    print(f"[parity-window] {case.name}: window={case.window} mask={case.mask}", flush=True)
+    o, m, l = P.oracle_stats(inp)
+    gpu = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_DEFAULT)
+    ref = P.oracle_backward(inp, o, m, l)
+    res = P.check_full(inp, gpu, ref)
+    print(f"[parity-window] {case.name}: " + " ".join(f"{k}: rel_l2={v[0]:.2e}" for k, v in res.items()),
+          flush=True)
+
+
+def test_window_single_pass_unsupported():
+    inp = I.make(WINDOW_CASES[0])
+    o, m, l = P.oracle_stats(inp)
+    with pytest.raises(NotImplementedError):
+        P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_SINGLE_PASS)

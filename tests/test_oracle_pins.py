@@ -34,7 +34,7 @@ def _rand(shape, rng, mult=1.0):
     return rng.standard_normal(shape) * mult
 
 
-def make_problem(mask, lens_q, lens_kv, heads=2, d=4, seed=0, padded_len=0, mult=1.0, heads_kv=None):
+def make_problem(mask, lens_q, lens_kv, heads=2, d=4, seed=0, padded_len=0, mult=1.0, heads_kv=None, window=0):
     rng = np.random.default_rng(seed)
     if A.is_padded(mask):
         tq = tkv = len(lens_q) * padded_len
@@ -48,15 +48,15 @@ def make_problem(mask, lens_q, lens_kv, heads=2, d=4, seed=0, padded_len=0, mult
     return dict(q=_rand((tq, heads, d), rng, mult), k=_rand((tkv, hkv, d), rng, mult),
                 v=_rand((tkv, hkv, d), rng), do=_rand((tq, heads, d), rng),
                 cu_q=cu_q, cu_kv=cu_kv, scale=1.0 / math.sqrt(d), mask=mask,
-                max_seqlen_q=msq, max_seqlen_kv=mskv)
+                max_seqlen_q=msq, max_seqlen_kv=mskv, window=window)
 
 
 def exact_backward(p):
     """Backward fed with the unrounded fp64 forward (exact mode)."""
     o, m, l = A.forward(p["q"], p["k"], p["v"], p["cu_q"], p["cu_kv"], p["scale"], p["mask"],
-                        p["max_seqlen_q"], p["max_seqlen_kv"])
+                        p["max_seqlen_q"], p["max_seqlen_kv"], p.get("window", 0))
     dq, dk, dv = A.backward(p["q"], p["k"], p["v"], o, p["do"], m, l, p["cu_q"], p["cu_kv"],
-                            p["scale"], p["mask"], p["max_seqlen_q"], p["max_seqlen_kv"])
+                            p["scale"], p["mask"], p["max_seqlen_q"], p["max_seqlen_kv"], p.get("window", 0))
     return o, m, l, dq, dk, dv
 
 
@@ -70,10 +70,10 @@ def fd_grads(p, eps=1e-6):
             keep = x[idx]
             x[idx] = keep + eps
             lp = A.loss(p["q"], p["k"], p["v"], p["do"], p["cu_q"], p["cu_kv"], p["scale"], p["mask"],
-                        p["max_seqlen_q"], p["max_seqlen_kv"])
+                        p["max_seqlen_q"], p["max_seqlen_kv"], p.get("window", 0))
             x[idx] = keep - eps
             lm = A.loss(p["q"], p["k"], p["v"], p["do"], p["cu_q"], p["cu_kv"], p["scale"], p["mask"],
-                        p["max_seqlen_q"], p["max_seqlen_kv"])
+                        p["max_seqlen_q"], p["max_seqlen_kv"], p.get("window", 0))
             x[idx] = keep
             g[idx] = (lp - lm) / (2 * eps)
         out[name] = g
@@ -112,9 +112,12 @@ def torch_reference(p):
         for h in range(q.shape[1]):
             qh, kh, vh = q[qs:qs + lq, h], ke[ks:ks + lk, h], ve[ks:ks + lk, h]
             logits = p["scale"] * qh @ kh.T
-            if causal:
+            if causal or p.get("window", 0):
                 bias = torch.triu(torch.full((lq, lk), float("-inf"), dtype=torch.float64), diagonal=1)
                 logits = logits + bias
+            if p.get("window", 0):   # keys at or before i - window are outside the left local window
+                logits = logits + torch.tril(torch.full((lq, lk), float("-inf"), dtype=torch.float64),
+                                             diagonal=-p.get("window", 0))
             out = torch.softmax(logits, dim=-1) @ vh
             total = total + (out * do[qs:qs + lq, h]).sum()
     total.backward()
@@ -421,6 +424,45 @@ def test_grouped_heads_reject_non_divisor():
     p = make_problem(MASK_NONE, [3], [3], heads=3, d=4, heads_kv=2)
     with pytest.raises(ValueError):
         A.forward(p["q"], p["k"], p["v"], p["cu_q"], p["cu_kv"], p["scale"], MASK_NONE)
+
+
+# ---------------------------------------------------------------- sliding window
+
+WINDOW_CASES = [
+    # (mask, lens_q, lens_kv, d, padded_len, window)
+    (MASK_CAUSAL, [8], [8], 4, 0, 3),
+    (MASK_CAUSAL, [6, 5], [6, 5], 4, 0, 2),            # two packed sequences
+    (MASK_NONE, [7], [7], 4, 0, 2),                    # the window implies the causal bound
+    (MASK_PADDING_CAUSAL, [6, 4], [6, 4], 4, 6, 4),
+]
+
+
+@pytest.mark.parametrize("mask,lq,lk,d,padded,window", WINDOW_CASES)
+def test_window_finite_differences(mask, lq, lk, d, padded, window):
+    p = make_problem(mask, lq, lk, heads=2, d=d, seed=61 + window, padded_len=padded, window=window)
+    assert fd_error(p) < 2e-6
+
+
+@pytest.mark.parametrize("mask,lq,lk,d,padded,window", WINDOW_CASES + [(MASK_CAUSAL, [96, 40], [96, 40], 16, 0, 33)])
+def test_window_torch_fp64_autograd(mask, lq, lk, d, padded, window):
+    p = make_problem(mask, lq, lk, heads=2, d=d, seed=71 + window, padded_len=padded, mult=2.0, window=window)
+    assert torch_error(p) < 1e-12
+
+
+def test_window_one_gives_identity_attention():
+    # window 1: every query sees only its own key, P = 1, O = V, dQ = dK = 0, dV = dO
+    p = make_problem(MASK_CAUSAL, [6], [6], heads=1, d=4, seed=3, window=1)
+    o, m, l, dq, dk, dv = exact_backward(p)
+    np.testing.assert_allclose(o, p["v"], rtol=1e-14)
+    np.testing.assert_allclose(dv, p["do"], rtol=1e-14)
+    assert np.all(np.abs(dq) < 1e-14) and np.all(np.abs(dk) < 1e-14)
+
+
+def test_planted_window_off_by_one_fails_torch_check(monkeypatch):
+    p = make_problem(MASK_CAUSAL, [7], [7], heads=1, d=4, seed=81, window=3)
+    assert torch_error(p) < 1e-12
+    _mutant(monkeypatch, "visible_block", "(j > i - window)", "(j >= i - window)")
+    assert torch_error(p) > 1e-3
 
 
 # ---------------------------------------------------------------- sampled rows == full backward
