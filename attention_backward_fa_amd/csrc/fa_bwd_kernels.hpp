@@ -491,30 +491,35 @@ struct DkdvCfg {
   static constexpr int BN = 128;                 // kv rows per workgroup: 4 row groups of 32
   static constexpr int BM = 64;                  // q rows per step: 2 M-tiles of 32
   static constexpr int NW = 8;                   // waves: 4 row groups x 2 M-tiles
+  static constexpr int NT = 64 * NW;
   static constexpr int KSD = D / 16;
   static constexpr int NTD = D / 32;
-  static constexpr int QS = D + 8;
+  static constexpr int QS = D + 8;               // padded row stride of every LDS tile
   static constexpr int CPR = QS / 8;
   static constexpr int TILE = BM * QS;
   static constexpr int TILE_BYTES = TILE * 2;
   static constexpr int NDMA = TILE_BYTES / 1024;
-  static constexpr int X_BYTES = 4 * 2 * 2 * 64 * 16;    // bf16 P / dS halves: [group][M-tile][chunk][lane]
-  static constexpr int OFF_Q = 0;                        // Q [2][BM][QS]
-  static constexpr int OFF_DO = OFF_Q + 2 * TILE_BYTES;  // dO [2][BM][QS]
-  static constexpr int OFF_X = OFF_DO + 2 * TILE_BYTES;  // exchange of P (M-tile 1) and dS (M-tile 0)
-  static constexpr int OFF_ST = OFF_X + X_BYTES;         // [2 buffers][lse2, D][BM] fp32
+  static constexpr int KV_BYTES = BN * QS * 2;   // the K (or V) tile of the workgroup
+  static constexpr int NDMA_KV = KV_BYTES / 1024;
+  static constexpr int OFF_K = 0;                             // K [BN][QS]
+  static constexpr int OFF_V = OFF_K + KV_BYTES;              // V [BN][QS]
+  static constexpr int OFF_Q = OFF_V + KV_BYTES;              // Q [2][BM][QS]
+  static constexpr int OFF_DO = OFF_Q + 2 * TILE_BYTES;       // dO [2][BM][QS]
+  static constexpr int OFF_ST = OFF_DO + 2 * TILE_BYTES;      // [2 buffers][lse2, D][BM] fp32
   static constexpr int LDS_BYTES = OFF_ST + 4 * BM * 4;
-  static_assert(TILE_BYTES % 1024 == 0, "a tile is a whole number of 1 KB transfers");
+  static constexpr int PART_BYTES = NTD * 16 * 4 * 64;        // one wave's partial dK or dV tile
+  static_assert(TILE_BYTES % 1024 == 0 && KV_BYTES % 1024 == 0, "tiles are whole 1 KB transfers");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget (one 8-wave workgroup per CU)");
+  static_assert(NW * PART_BYTES <= OFF_ST, "the end-of-kernel exchange of partial sums fits in the tiles");
 };
 
-// dK and dV of one (kv tile, head, sequence). Eight waves: row group r = w % 4 owns kv rows
-// 32 r .. 32 r + 31, and the two waves of a group each take one 32-row M-tile mt = w / 4 of the
-// 64-row q step: both form S = Q K^T, dP = dO V^T, P and dS for their M-tile (steps 1-5). The
-// wave of M-tile 0 then accumulates dV += P^T dO over the whole q step, the other dK += dS^T Q;
-// each passes the bf16 half its partner needs (dS of M-tile 0, P of M-tile 1) through LDS.
-// Each wave so holds one fp32 accumulator tile, two waves fit on a SIMD, and one's softmax runs
-// beside the other's MFMAs.
+// dK and dV of one (kv tile, K/V head, sequence). Eight waves: row group r = w % 4 owns kv rows
+// 32 r .. 32 r + 31, and the two waves of a group each take one 32-row M-tile mt = w / 4 of every
+// 64-row q step. Each wave forms S = Q K^T, dP = dO V^T, P and dS for its M-tile (steps 1-5) and
+// accumulates its partial dV += P^T dO and dK += dS^T Q over its M-tile's rows (steps 7, 6), so
+// the waves of a step never wait for each other; K and V are read from an LDS tile loaded once,
+// which leaves registers for both accumulators. After the last step the two waves of a group
+// combine their partial sums through LDS (the M-tile 0 wave finishes dV, the other dK).
 template <int D, bool CAUSAL, bool WINDOW>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv(MainArgs a) {
@@ -522,6 +527,8 @@ void fa_bwd_dkdv(MainArgs a) {
   using C = DkdvCfg<D>;
   constexpr int BN = C::BN, BM = C::BM, QS = C::QS;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  const bf16* s_k = (const bf16*)(smem + C::OFF_K);
+  const bf16* s_v = (const bf16*)(smem + C::OFF_V);
   bf16* s_q = (bf16*)(smem + C::OFF_Q);
   bf16* s_do = (bf16*)(smem + C::OFF_DO);
   float* s_st = (float*)(smem + C::OFF_ST);
@@ -541,36 +548,19 @@ void fa_bwd_dkdv(MainArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int grp = w & 3, mt = w >> 2;  // kv row group; M-tile of steps 1-5; 0: dV wave, 1: dK wave
+  const int grp = w & 3, mt = w >> 2;  // kv row group; M-tile
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
   const int64_t rs = (int64_t)a.H * D;    // row stride of Q, dO
   const int rsb = (int)(rs * 2);
   const int64_t rsk = (int64_t)a.Hk * D;  // row stride of K, V, dK, dV
   const int rskb = (int)(rsk * 2);
   const int G = a.H / a.Hk;               // query heads sharing this K/V head: hk * G .. hk * G + G - 1
-  const bf16* kb = a.k + (kv_start + kv0) * rsk + (int64_t)hk * D;
-  const bf16* vb = a.v + (kv_start + kv0) * rsk + (int64_t)hk * D;
 
-  // K and V rows 32 grp + c as B operands of S = Q K^T and dP = dO V^T
-  const int kv_rows = imin(Lk - kv0, BN);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (int64_t)kv_rows * rskb);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (int64_t)kv_rows * rskb);
-  bf16x8 kf[C::KSD], vf[C::KSD];
-#pragma unroll
-  for (int ks = 0; ks < C::KSD; ++ks) {
-    const int off = (32 * grp + c) * rskb + (16 * ks + 8 * hh) * 2;
-    kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
-    vf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
-  }
-  {  // zero the Q and dO buffers once: rows past the sequence then hold zeros or earlier valid rows
+  {  // zero the tiles once: rows past the sequences then hold zeros or earlier valid rows
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int o = tid * 16; o < 4 * C::TILE_BYTES; o += 512 * 16) *(u32x4*)(smem + C::OFF_Q + o) = z;
+    for (int o = tid * 16; o < C::OFF_ST; o += C::NT * 16) *(u32x4*)(smem + o) = z;
   }
   __syncthreads();
-
-  f32x16 acc[C::NTD];  // dV (M-tile 0 wave) or dK / scale (M-tile 1 wave) of rows 32 grp .. +31
-#pragma unroll
-  for (int nt = 0; nt < C::NTD; ++nt) acc[nt] = f32x16{};
 
   // the q steps: for each query head of the group, the q tiles that can see these keys (causal: from
   // the tile of the first key on); step st is q tile qt0 + st % nq of query head hk * G + st / nq
@@ -584,14 +574,28 @@ void fa_bwd_dkdv(MainArgs a) {
   auto step_tile = [&](int st) { return qt0 + st % nq; };
   const int jcol = kv0 + 32 * grp + c;  // this lane's key row (sequence-local)
 
+  // 1 KB LDS-DMA transfers of padded rows: transfer j, lane -> row p16 / CPR, 16-byte chunk p16 % CPR
+  auto dma_row_off = [&](int j, int row_bytes) {
+    const int p16 = 64 * j + lane;
+    const int r = p16 / C::CPR, ch = p16 % C::CPR;
+    return r * row_bytes + (ch < D / 8 ? ch : 0) * 16;
+  };
+  {  // the K and V tiles, once
+    const int kv_rows = imin(Lk - kv0, BN);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + (kv_start + kv0) * rsk + (int64_t)hk * D, (int64_t)kv_rows * rskb);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (kv_start + kv0) * rsk + (int64_t)hk * D, (int64_t)kv_rows * rskb);
+    for (int j = w; j < C::NDMA_KV; j += C::NW) {
+      const int off = dma_row_off(j, rskb);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(smem + C::OFF_K + 1024 * j),
+                                               16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(smem + C::OFF_V + 1024 * j),
+                                               16, off, 0, 0, 0);
+    }
+  }
   constexpr int NJ = (C::NDMA + C::NW - 1) / C::NW;
   int dma_off[NJ];
 #pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) {
-    const int p16 = 64 * (w + C::NW * jj) + lane;
-    const int r = p16 / C::CPR, ch = p16 % C::CPR;
-    dma_off[jj] = r * rsb + (ch < D / 8 ? ch : 0) * 16;
-  }
+  for (int jj = 0; jj < NJ; ++jj) dma_off[jj] = dma_row_off(w + C::NW * jj, rsb);
   auto issue_tile = [&](int st, int bi) {
     const int i0 = step_tile(st) * BM;
     const int64_t hoff = (q_start + i0) * rs + (int64_t)step_head(st) * D;
@@ -611,7 +615,7 @@ void fa_bwd_dkdv(MainArgs a) {
       }
     }
   };
-  // row statistics of q tile t in MFMA row order: threads 0..63 lse2, 64..127 D; rows past the
+  // row statistics of a q step in MFMA row order: threads 0..63 lse2, 64..127 D; rows past the
   // sequence get lse2 = +inf, so their P (and dS) is exactly 0 without a mask
   auto load_stats = [&](int st) -> float {
     const int mi = tid & (BM - 1);
@@ -624,8 +628,13 @@ void fa_bwd_dkdv(MainArgs a) {
   auto store_stats = [&](int bi, float v) {
     if (tid < 2 * BM) s_st[bi * 2 * BM + tid] = v;
   };
-  // exchange slot of 16-byte chunk k for M-tile m of this group, this lane
-  auto xslot = [&](int m, int k) { return (bf16x8*)(smem + C::OFF_X) + ((grp * 2 + m) * 2 + k) * 64 + lane; };
+
+  f32x16 acc_v[C::NTD], acc_k[C::NTD];  // partial dV and dK / scale of rows 32 grp .. +31 over this M-tile
+#pragma unroll
+  for (int nt = 0; nt < C::NTD; ++nt) {
+    acc_v[nt] = f32x16{};
+    acc_k[nt] = f32x16{};
+  }
 
   int buf = 0;
   if (n_steps > 0) {
@@ -635,8 +644,9 @@ void fa_bwd_dkdv(MainArgs a) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
 
-  const int arow = (32 * mt + tile_row(c)) * QS + 8 * hh;
-  const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
+  const int arow = (32 * mt + tile_row(c)) * QS + 8 * hh;  // A rows: this M-tile's q rows
+  const int krow = (32 * grp + c) * QS + 8 * hh;            // B columns: this group's keys
+  const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3) + 32 * mt * QS;
   for (int sp = 0; sp < n_steps; ++sp, buf ^= 1) {
     const bool has_next = sp + 1 < n_steps;
     float st_next = 0.f;
@@ -648,24 +658,25 @@ void fa_bwd_dkdv(MainArgs a) {
     const bf16* sq = s_q + buf * C::TILE;
     const bf16* sd = s_do + buf * C::TILE;
     const float* st = s_st + buf * 2 * BM + 32 * mt;
-    // steps 1 and 3 for this wave's M-tile: S = Q K^T, dP = dO V^T  ([q 32] x [kv 32])
+    // steps 1 and 3 for this wave's M-tile: S = Q K^T, dP = dO V^T  ([q 32] x [kv 32]); operands
+    // are read PF k-steps ahead into distinct registers, one scheduling fence per k-step
     f32x16 s = f32x16{}, dp = f32x16{};
     {
       constexpr int PF = 2;
-      bf16x8 qa[C::KSD], da[C::KSD];
-#pragma unroll
-      for (int ks = 0; ks < PF; ++ks) {
+      bf16x8 qa[C::KSD], da[C::KSD], kb[C::KSD], vb[C::KSD];
+      auto ld = [&](int ks) {
         qa[ks] = *(const bf16x8*)(sq + arow + 16 * ks);
         da[ks] = *(const bf16x8*)(sd + arow + 16 * ks);
-      }
+        kb[ks] = *(const bf16x8*)(s_k + krow + 16 * ks);
+        vb[ks] = *(const bf16x8*)(s_v + krow + 16 * ks);
+      };
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) ld(ks);
 #pragma unroll
       for (int ks = 0; ks < C::KSD; ++ks) {
-        if (ks + PF < C::KSD) {
-          qa[ks + PF] = *(const bf16x8*)(sq + arow + 16 * (ks + PF));
-          da[ks + PF] = *(const bf16x8*)(sd + arow + 16 * (ks + PF));
-        }
-        s = mfma32x32x16(qa[ks], kf[ks], s);
-        dp = mfma32x32x16(da[ks], vf[ks], dp);
+        if (ks + PF < C::KSD) ld(ks + PF);
+        s = mfma32x32x16(qa[ks], kb[ks], s);
+        dp = mfma32x32x16(da[ks], vb[ks], dp);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -690,39 +701,27 @@ void fa_bwd_dkdv(MainArgs a) {
         dsk[j >> 3][j & 7] = to_bf16(p * (dp[j] - dd[bb]));
       }
     }
-    // pass the half the partner needs: dS of M-tile 0 to the dK wave, P of M-tile 1 to the dV wave
-    // (selects on the wave-uniform mt; no runtime indexing, so everything stays in registers)
-    const bool v_wave = mt == 0;
-    *xslot(mt, 0) = v_wave ? dsk[0] : pk[0];
-    *xslot(mt, 1) = v_wave ? dsk[1] : pk[1];
-    __syncthreads();  // exchange visible
-    const bf16x8 own0 = v_wave ? pk[0] : dsk[0], own1 = v_wave ? pk[1] : dsk[1];
-    const bf16x8 oth0 = *xslot(1 - mt, 0), oth1 = *xslot(1 - mt, 1);
-    bf16x8 opk[2][2];  // A operands of the second GEMM, per M-tile and k-step
-    opk[0][0] = v_wave ? own0 : oth0;
-    opk[0][1] = v_wave ? own1 : oth1;
-    opk[1][0] = v_wave ? oth0 : own0;
-    opk[1][1] = v_wave ? oth1 : own1;
-    // steps 7 (M-tile 0 wave) and 6 (M-tile 1 wave): dV += P^T dO, dK += dS^T Q over both M-tiles.
-    // The k-index e of the A operand is MFMA row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4;
-    // the transpose reads fetch the matching tile rows.
-    const bf16* tb = mt == 0 ? sd : sq;
+    // steps 7 and 6 over this M-tile: dV += P^T dO, dK += dS^T Q. k-step s2: its k-index e is MFMA
+    // row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4; the transpose reads fetch those rows.
+    // B operands are read PF MFMAs ahead; the dV and dK MFMAs alternate (independent chains).
     {
-      constexpr int NB = 4 * C::NTD, PF = 3;
-      bf16x8 bt[NB];
-      auto bt_load = [&](int i) {
-        const int ksi = i / C::NTD, nt = i % C::NTD;  // ksi = 2 m2 + s2
-        const int o = brow + 16 * ksi * QS + 32 * nt;
-        return concat(lds_read_tr4(tb + o), lds_read_tr4(tb + o + 2 * QS));
+      constexpr int NB = 2 * C::NTD, PF = 2;
+      bf16x8 bd[NB], bq[NB];
+      auto ld = [&](int i) {
+        const int s2 = i / C::NTD, nt = i % C::NTD;
+        const int o = brow + 16 * s2 * QS + 32 * nt;
+        bd[i] = concat(lds_read_tr4(sd + o), lds_read_tr4(sd + o + 2 * QS));
+        bq[i] = concat(lds_read_tr4(sq + o), lds_read_tr4(sq + o + 2 * QS));
       };
 #pragma unroll
-      for (int i = 0; i < PF; ++i) bt[i] = bt_load(i);
+      for (int i = 0; i < PF; ++i) ld(i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        if (i + PF < NB) bt[i + PF] = bt_load(i + PF);
-        const int ksi = i / C::NTD, nt = i % C::NTD;
-        acc[nt] = mfma32x32x16(opk[ksi >> 1][ksi & 1], bt[i], acc[nt]);
+        if (i + PF < NB) ld(i + PF);
+        const int s2 = i / C::NTD, nt = i % C::NTD;
+        acc_v[nt] = mfma32x32x16(pk[s2], bd[i], acc_v[nt]);
+        acc_k[nt] = mfma32x32x16(dsk[s2], bq[i], acc_k[nt]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -733,17 +732,34 @@ void fa_bwd_dkdv(MainArgs a) {
     __syncthreads();
   }
 
+  // combine the two M-tiles' partial sums: the M-tile 0 wave keeps dV and takes the partner's dV,
+  // the M-tile 1 wave keeps dK and takes the partner's dK; each writes the half its partner needs
+  {
+    f32x16* part = (f32x16*)(smem) + (size_t)w * C::NTD * 64 + lane;  // [wave][nt][lane]
+#pragma unroll
+    for (int nt = 0; nt < C::NTD; ++nt) part[nt * 64] = mt == 0 ? acc_k[nt] : acc_v[nt];
+  }
+  __syncthreads();
+  {
+    const f32x16* other = (const f32x16*)(smem) + (size_t)(w ^ 4) * C::NTD * 64 + lane;
+#pragma unroll
+    for (int nt = 0; nt < C::NTD; ++nt) {
+      if (mt == 0) acc_v[nt] += other[nt * 64];
+      else acc_k[nt] += other[nt * 64];
+    }
+  }
   // write-back: M-tile 0 wave dV, M-tile 1 wave dK = scale * acc, bf16, rows 32 grp .. 32 grp + 31
   bf16* out = mt == 0 ? a.dv : a.dk;
   const float osc = mt == 0 ? 1.f : a.scale;
 #pragma unroll
   for (int nt = 0; nt < C::NTD; ++nt) {
+    const f32x16 res = mt == 0 ? acc_v[nt] : acc_k[nt];
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         const int r = kv0 + 32 * grp + 8 * a4 + 4 * hh + bb;
-        if (r < Lk) out[(kv_start + r) * rsk + (int64_t)hk * D + 32 * nt + c] = to_bf16(acc[nt][4 * a4 + bb] * osc);
+        if (r < Lk) out[(kv_start + r) * rsk + (int64_t)hk * D + 32 * nt + c] = to_bf16(res[4 * a4 + bb] * osc);
       }
     }
   }
