@@ -683,24 +683,34 @@ void fa_bwd_dkdv(MainArgs a) {
     // steps 2 and 5: P = exp2(S*scale*log2e - lse2) (causal: 0 where key > query), dS = P (dP - D)
     const int jrel = jcol - i0 - 32 * mt;  // key j visible from M-tile row r iff jrel <= r
     bf16x8 pk[2], dsk[2];
+    auto softmax = [&](auto masked) {
 #pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      const f32x4 lse = *(const f32x4*)(st + 8 * a4 + 4 * hh);
-      const f32x4 dd = *(const f32x4*)(st + BM + 8 * a4 + 4 * hh);
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 lse = *(const f32x4*)(st + 8 * a4 + 4 * hh);
+        const f32x4 dd = *(const f32x4*)(st + BM + 8 * a4 + 4 * hh);
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int j = 4 * a4 + bb;
-        float p = fast_exp2(s[j] * a.scale_log2 - lse[bb]);
-        if constexpr (WINDOW) {  // key j visible from query i iff i - window < j <= i
-          const int r = tile_row(8 * a4 + 4 * hh + bb);
-          p = (jrel <= r && r - jrel < a.window) ? p : 0.f;
-        } else if constexpr (CAUSAL) {
-          p = (jrel <= tile_row(8 * a4 + 4 * hh + bb)) ? p : 0.f;
+        for (int bb = 0; bb < 4; ++bb) {
+          const int j = 4 * a4 + bb;
+          float p = fast_exp2(s[j] * a.scale_log2 - lse[bb]);
+          if constexpr (decltype(masked)::value) {
+            const int r = tile_row(8 * a4 + 4 * hh + bb);
+            if constexpr (WINDOW)  // key j visible from query i iff i - window < j <= i
+              p = (jrel <= r && r - jrel < a.window) ? p : 0.f;
+            else
+              p = (jrel <= r) ? p : 0.f;
+          }
+          pk[j >> 3][j & 7] = to_bf16(p);
+          dsk[j >> 3][j & 7] = to_bf16(p * (dp[j] - dd[bb]));
         }
-        pk[j >> 3][j & 7] = to_bf16(p);
-        dsk[j >> 3][j & 7] = to_bf16(p * (dp[j] - dd[bb]));
       }
-    }
+    };
+    // every key of the group visible from every query of the M-tile: no element mask (wave-uniform)
+    const int kmin = kv0 + 32 * grp, qmin = i0 + 32 * mt;
+    const bool full = !CAUSAL || (kmin + 31 <= qmin && (!WINDOW || qmin + 31 - a.window < kmin));
+    if (full)
+      softmax(std::false_type{});
+    else
+      softmax(std::true_type{});
     // steps 7 and 6 over this M-tile: dV += P^T dO, dK += dS^T Q. k-step s2: its k-index e is MFMA
     // row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4; the transpose reads fetch those rows.
     // B operands are read PF MFMAs ahead; the dV and dK MFMAs alternate (independent chains).
@@ -814,7 +824,8 @@ void fa_bwd_dq(MainArgs a) {
   const int i0 = qtile * BQ;
   if (i0 >= Lq) return;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
   const int64_t rs = (int64_t)a.H * D;    // row stride of the query-side tensors
   const int rsb = (int)(rs * 2);
@@ -930,20 +941,31 @@ void fa_bwd_dq(MainArgs a) {
     const int lim = CAUSAL ? imin(Lk - 1, qi) - t * BK : Lk - 1 - t * BK;
     const int lo = qi - a.window + 1 - t * BK;  // window: first visible tile-local key
     bf16x8 dsk[2][2];
+    auto softmax = [&](auto masked) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
+        for (int a4 = 0; a4 < 4; ++a4) {
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const int j = 4 * a4 + bb;
-          float p = fast_exp2(s[mt][j] * a.scale_log2 - lse);
-          const int kr = 32 * mt + tile_row(8 * a4 + 4 * hh + bb);
-          p = (kr <= lim && (!WINDOW || kr >= lo)) ? p : 0.f;
-          dsk[mt][j >> 3][j & 7] = to_bf16(p * (dp[mt][j] - dd));
+          for (int bb = 0; bb < 4; ++bb) {
+            const int j = 4 * a4 + bb;
+            float p = fast_exp2(s[mt][j] * a.scale_log2 - lse);
+            if constexpr (decltype(masked)::value) {
+              const int kr = 32 * mt + tile_row(8 * a4 + 4 * hh + bb);
+              p = (kr <= lim && (!WINDOW || kr >= lo)) ? p : 0.f;
+            }
+            dsk[mt][j >> 3][j & 7] = to_bf16(p * (dp[mt][j] - dd));
+          }
         }
       }
-    }
+    };
+    // every key of the tile visible from every row of this wave: no element mask (wave-uniform)
+    const int qmin = i0 + 32 * w, kmax = t * BK + BK - 1;
+    const bool full = kmax <= Lk - 1 && (!CAUSAL || kmax <= qmin) && (!WINDOW || qmin + 31 - a.window < t * BK);
+    if (full)
+      softmax(std::false_type{});
+    else
+      softmax(std::true_type{});
     // step 8, transposed: dQ^T += K^T dS^T. k-step ksi = 2 mt + s2: its k-index e is kv MFMA row
     // 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4 of M-tile mt; the transpose reads fetch
     // those K rows. k-steps run outside the NTD independent accumulators; A operands are read PF
