@@ -1074,7 +1074,8 @@ void fa_fwd(FwdArgs a) {
   const int i0 = qtile * BQ;
   if (i0 >= Lq) return;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
   const int64_t rs = (int64_t)a.H * D;    // row stride of the query-side tensors
   const int rsb = (int)(rs * 2);
@@ -1172,16 +1173,27 @@ void fa_fwd(FwdArgs a) {
     const int lo = qi - a.window + 1 - t * BK;  // window: first visible tile-local key
     float x[2][16];
     float tmax = -__builtin_inff();
+    auto scale_mask = [&](auto masked) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int kr = 32 * mt + tile_row(8 * (j >> 2) + 4 * hh + (j & 3));
-        const bool vis = kr <= lim && (!WINDOW || kr >= lo);
-        x[mt][j] = vis ? s[mt][j] * a.scale_log2 : -__builtin_inff();
-        tmax = fmaxf(tmax, x[mt][j]);
+        for (int j = 0; j < 16; ++j) {
+          x[mt][j] = s[mt][j] * a.scale_log2;
+          if constexpr (decltype(masked)::value) {
+            const int kr = 32 * mt + tile_row(8 * (j >> 2) + 4 * hh + (j & 3));
+            x[mt][j] = (kr <= lim && (!WINDOW || kr >= lo)) ? x[mt][j] : -__builtin_inff();
+          }
+          tmax = fmaxf(tmax, x[mt][j]);
+        }
       }
-    }
+    };
+    // every key of the tile visible from every row of this wave: no element mask (wave-uniform)
+    const int qmin = i0 + 32 * w, kmax = t * BK + BK - 1;
+    const bool full = kmax <= Lk - 1 && (!CAUSAL || kmax <= qmin) && (!WINDOW || qmin + 31 - a.window < t * BK);
+    if (full)
+      scale_mask(std::false_type{});
+    else
+      scale_mask(std::true_type{});
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
     const float mnew = fmaxf(mrun, tmax);
     // no visible key yet: keep everything at zero (mnew = -inf would make exp2 produce NaN)
