@@ -216,7 +216,9 @@ def fa_bwd_profile_enable(handle, enable: bool) -> None:
 
 
 def fa_bwd_profile_collect(handle, max_runs: int = 4096):
-    """Per-run kernel times [(pre_ms, main_ms, cast_ms), ...] of the runs recorded since the last call."""
+    """Per-run kernel times [(first_ms, second_ms, third_ms), ...] of the runs recorded since the last call:
+    backward (row statistics, dK/dV or single-pass main kernel, dQ kernel or dQ cast); forward (fill,
+    forward kernel, 0)."""
     buf = (ctypes.c_float * (3 * max_runs))()
     n = ctypes.c_int32()
     _check(load_library().fa_bwd_profile_collect(handle, buf, max_runs, ctypes.byref(n)), "fa_bwd_profile_collect")

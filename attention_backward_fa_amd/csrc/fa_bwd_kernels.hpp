@@ -16,6 +16,10 @@
 //                  waves per SIMD; dK, dV written once per kv tile.
 //   fa_bwd_dq      recompute form, q-outer: recomputes S^T and dP^T and
 //                  accumulates dQ (step 8) in registers; no atomics.
+//   fa_fwd_fill,   the forward that produces O, m, l (the statistics step 2
+//   fa_fwd         reads), for callers without one of their own.
+// The recompute kernels and the forward also take grouped K/V heads and a
+// sliding window (each query sees keys (i - w, i]).
 #pragma once
 #include <type_traits>
 
@@ -43,7 +47,7 @@ __device__ __forceinline__ bool row_in_sequence(int64_t t, const int* cu, int ba
   return t >= cu[0] && t < cu[batch];
 }
 
-// ------------------------------------------------------------------ stage 1
+// ------------------------------------------------------------------ stage 1: row statistics
 
 struct PreArgs {
   const bf16* o;
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre(PreArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ stage 2
+// ------------------------------------------------------------------ stage 2: single-pass main kernel
 
 struct MainArgs {
   const bf16* q;
@@ -484,7 +488,7 @@ void fa_bwd_main(MainArgs a) {
 }
 
 
-// ------------------------------------------------------------------ stage 2a': dK and dV, two waves per SIMD
+// ------------------------------------------------------------------ stage 2a: dK and dV by recompute
 
 template <int D>
 struct DkdvCfg {
@@ -1264,7 +1268,7 @@ void fa_fwd(FwdArgs a) {
 #endif
 }
 
-// ------------------------------------------------------------------ stage 3
+// ------------------------------------------------------------------ stage 3: single-pass dQ cast
 
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_dq_cast(const float* dq_acc, bf16* dq, int64_t total_q, int H,

@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark of the single-pass attention backward on one MI355X.
+"""Benchmark of the attention backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal]
 
@@ -18,9 +18,16 @@ outside the timed region).
 Prints ONE JSON line with the metric, a ``roofline`` object for the longest
 kernel (its duration taken from HIP events the library records around each
 kernel on the launch stream during the timed steps; its work counted as the
-GEMMs that kernel itself runs) and a ``cpu_baseline`` object
-(the fp64 oracle's backward timed on this host's cores over a bounded sample
-of the same workload).
+GEMMs that kernel itself runs; ``traffic`` is the HBM bytes per launch measured
+with rocprofv3 FETCH_SIZE/WRITE_SIZE counters and recorded in
+profiles/fa_bwd_traffic_causal_s8192_h32_d128.md, reported only while the
+kernel sources still hash to the recorded value, else null) and a
+``cpu_baseline`` object (the fp64 oracle's backward timed on this host's cores
+over a bounded sample of the same workload).
+
+``--path forward`` times the forward that produces O, m, l instead, under its
+own metric; ``--calibrate-copy MIB`` first runs a kernel of known traffic, for
+scaling the counters in a ``rocprofv3 --pmc`` run.
 """
 from __future__ import annotations
 

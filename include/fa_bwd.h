@@ -162,16 +162,18 @@ const char* fa_bwd_status_string(fa_bwd_status s);
 /* Descriptor the handle was created with (for bindings); NULL on NULL. */
 const fa_bwd_desc* fa_bwd_get_desc(const fa_bwd_handle* h);
 
-/* Per-kernel timing for benchmarks. While enabled, every fa_bwd_run also
- * records four HIP events on its stream, around its three kernels (row
- * preprocessing, main kernel, then the dQ cast in single-pass form or the dQ
- * kernel in recompute form); recording does not wait.
+/* Per-kernel timing for benchmarks. While enabled, every fa_bwd_run (and
+ * fa_bwd_run_lse) also records four HIP events on its stream, around its three
+ * kernels (row preprocessing; the main kernel in single-pass form or the dK/dV
+ * kernel in recompute form; then the dQ cast or the dQ kernel); an fa_fwd_run
+ * records the fill of rows outside sequences, the forward kernel and an empty
+ * third interval. Recording does not wait.
  * Enabling or disabling forgets the runs recorded so far. At most 4096 runs
  * are kept; later runs are not recorded. */
 fa_bwd_status fa_bwd_profile_enable(fa_bwd_handle* h, int32_t enable);
 
 /* Waits for the recorded runs, writes min(max_runs, recorded) rows of three
- * floats (milliseconds of the preprocessing, main and third kernels) to the
+ * floats (milliseconds of the first, second and third kernels above) to the
  * HOST array ms, stores the row count in *n_runs, and forgets the runs. */
 fa_bwd_status fa_bwd_profile_collect(fa_bwd_handle* h, float* ms, int32_t max_runs, int32_t* n_runs);
 
