@@ -40,7 +40,7 @@ class FaBwdDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_kv", ctypes.c_int32),
                 ("total_q", ctypes.c_int64), ("total_kv", ctypes.c_int64), ("algorithm", ctypes.c_int32),
-                ("num_heads_kv", ctypes.c_int32), ("window", ctypes.c_int32)]
+                ("num_heads_kv", ctypes.c_int32), ("window", ctypes.c_int32), ("head_dim_v", ctypes.c_int32)]
 
 
 _lib = None
@@ -94,11 +94,11 @@ def _check(status: int, what: str) -> None:
 
 def fa_bwd_create(batch: int, num_heads: int, head_dim: int, max_seqlen_q: int, max_seqlen_kv: int,
                   total_q: int, total_kv: int, algorithm: int = FA_BWD_ALGO_DEFAULT,
-                  num_heads_kv: int = 0, window: int = 0) -> ctypes.c_void_p:
+                  num_heads_kv: int = 0, window: int = 0, head_dim_v: int = 0) -> ctypes.c_void_p:
     """Create a handle (and its device workspace on the current device); num_heads_kv 0 = num_heads;
-    window 0 = none, w > 0 = each query i sees keys (i - w, i]."""
+    window 0 = none, w > 0 = each query i sees keys (i - w, i]; head_dim_v (V, O, dO, dV) 0 = head_dim."""
     desc = FaBwdDesc(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv, algorithm,
-                     num_heads_kv, window)
+                     num_heads_kv, window, head_dim_v)
     handle = ctypes.c_void_p()
     _check(load_library().fa_bwd_create(ctypes.byref(desc), ctypes.byref(handle)), "fa_bwd_create")
     return handle
@@ -134,8 +134,9 @@ def fa_bwd_run(handle, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scal
                dq, dk, dv, stream=None) -> None:
     """Enqueue the backward on ``stream`` (default: torch's current stream of q's device).
 
-    Tensors: q, o, dout, dq bf16 [total_q, H, d]; k, v, dk, dv bf16 [total_kv, H, d];
-    m, l fp32 [total_q, H]; cu_seqlens_* int32 [batch + 1]; all on one GPU.
+    Tensors: q, dq bf16 [total_q, H, d]; o, dout bf16 [total_q, H, d_v]; k, dk bf16 [total_kv, H_kv, d];
+    v, dv bf16 [total_kv, H_kv, d_v]; m, l fp32 [total_q, H]; cu_seqlens_* int32 [batch + 1]; all on one GPU
+    (d = head_dim, d_v = head_dim_v of the handle).
     """
     import torch
     d = fa_bwd_get_desc(handle)
@@ -143,16 +144,16 @@ def fa_bwd_run(handle, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scal
     if dev.type != "cuda":
         raise ValueError(f"q: expected a GPU tensor, got device {dev}")
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
-    qs = (d.total_q, d.num_heads, d.head_dim)
-    ks = (d.total_kv, d.num_heads_kv, d.head_dim)
+    qs, os_ = (d.total_q, d.num_heads, d.head_dim), (d.total_q, d.num_heads, d.head_dim_v)
+    ks, vs = (d.total_kv, d.num_heads_kv, d.head_dim), (d.total_kv, d.num_heads_kv, d.head_dim_v)
     ptrs = [
-        _expect(q, "q", qs, bf, dev), _expect(k, "k", ks, bf, dev), _expect(v, "v", ks, bf, dev),
-        _expect(o, "o", qs, bf, dev), _expect(dout, "dout", qs, bf, dev),
+        _expect(q, "q", qs, bf, dev), _expect(k, "k", ks, bf, dev), _expect(v, "v", vs, bf, dev),
+        _expect(o, "o", os_, bf, dev), _expect(dout, "dout", os_, bf, dev),
         _expect(m, "m", qs[:2], f32, dev), _expect(l, "l", qs[:2], f32, dev),
         _expect(cu_seqlens_q, "cu_seqlens_q", (d.batch + 1,), i32, dev),
         _expect(cu_seqlens_kv, "cu_seqlens_kv", (d.batch + 1,), i32, dev),
     ]
-    outs = [_expect(dq, "dq", qs, bf, dev), _expect(dk, "dk", ks, bf, dev), _expect(dv, "dv", ks, bf, dev)]
+    outs = [_expect(dq, "dq", qs, bf, dev), _expect(dk, "dk", ks, bf, dev), _expect(dv, "dv", vs, bf, dev)]
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     st = load_library().fa_bwd_run(handle, *ptrs, ctypes.c_float(scale), int(mask), *outs, ctypes.c_void_p(stream))
@@ -168,15 +169,15 @@ def fa_bwd_run_lse(handle, q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_kv, s
     if dev.type != "cuda":
         raise ValueError(f"q: expected a GPU tensor, got device {dev}")
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
-    qs = (d.total_q, d.num_heads, d.head_dim)
-    ks = (d.total_kv, d.num_heads_kv, d.head_dim)
+    qs, os_ = (d.total_q, d.num_heads, d.head_dim), (d.total_q, d.num_heads, d.head_dim_v)
+    ks, vs = (d.total_kv, d.num_heads_kv, d.head_dim), (d.total_kv, d.num_heads_kv, d.head_dim_v)
     ptrs = [
-        _expect(q, "q", qs, bf, dev), _expect(k, "k", ks, bf, dev), _expect(v, "v", ks, bf, dev),
-        _expect(o, "o", qs, bf, dev), _expect(dout, "dout", qs, bf, dev), _expect(lse, "lse", qs[:2], f32, dev),
+        _expect(q, "q", qs, bf, dev), _expect(k, "k", ks, bf, dev), _expect(v, "v", vs, bf, dev),
+        _expect(o, "o", os_, bf, dev), _expect(dout, "dout", os_, bf, dev), _expect(lse, "lse", qs[:2], f32, dev),
         _expect(cu_seqlens_q, "cu_seqlens_q", (d.batch + 1,), i32, dev),
         _expect(cu_seqlens_kv, "cu_seqlens_kv", (d.batch + 1,), i32, dev),
     ]
-    outs = [_expect(dq, "dq", qs, bf, dev), _expect(dk, "dk", ks, bf, dev), _expect(dv, "dv", ks, bf, dev)]
+    outs = [_expect(dq, "dq", qs, bf, dev), _expect(dk, "dk", ks, bf, dev), _expect(dv, "dv", vs, bf, dev)]
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     st = load_library().fa_bwd_run_lse(handle, *ptrs, ctypes.c_float(scale), int(mask), *outs,
@@ -188,8 +189,9 @@ def fa_fwd_run(handle, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, mask:
                stream=None) -> None:
     """Enqueue the forward (O, m, l for the backward) on ``stream`` (default: torch's current stream).
 
-    Tensors: q, o bf16 [total_q, H, d]; k, v bf16 [total_kv, H, d]; m, l fp32 [total_q, H] (written);
-    cu_seqlens_* int32 [batch + 1]; all on one GPU.
+    Tensors: q bf16 [total_q, H, d]; o bf16 [total_q, H, d_v] (written); k bf16 [total_kv, H_kv, d];
+    v bf16 [total_kv, H_kv, d_v]; m, l fp32 [total_q, H] (written); cu_seqlens_* int32 [batch + 1]; all on
+    one GPU.
     """
     import torch
     d = fa_bwd_get_desc(handle)
@@ -197,14 +199,14 @@ def fa_fwd_run(handle, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, mask:
     if dev.type != "cuda":
         raise ValueError(f"q: expected a GPU tensor, got device {dev}")
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
-    qs = (d.total_q, d.num_heads, d.head_dim)
-    ks = (d.total_kv, d.num_heads_kv, d.head_dim)
+    qs, os_ = (d.total_q, d.num_heads, d.head_dim), (d.total_q, d.num_heads, d.head_dim_v)
+    ks, vs = (d.total_kv, d.num_heads_kv, d.head_dim), (d.total_kv, d.num_heads_kv, d.head_dim_v)
     ptrs = [
-        _expect(q, "q", qs, bf, dev), _expect(k, "k", ks, bf, dev), _expect(v, "v", ks, bf, dev),
+        _expect(q, "q", qs, bf, dev), _expect(k, "k", ks, bf, dev), _expect(v, "v", vs, bf, dev),
         _expect(cu_seqlens_q, "cu_seqlens_q", (d.batch + 1,), i32, dev),
         _expect(cu_seqlens_kv, "cu_seqlens_kv", (d.batch + 1,), i32, dev),
     ]
-    outs = [_expect(o, "o", qs, bf, dev), _expect(m, "m", qs[:2], f32, dev), _expect(l, "l", qs[:2], f32, dev)]
+    outs = [_expect(o, "o", os_, bf, dev), _expect(m, "m", qs[:2], f32, dev), _expect(l, "l", qs[:2], f32, dev)]
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     st = load_library().fa_fwd_run(handle, *ptrs, ctypes.c_float(scale), int(mask), *outs, ctypes.c_void_p(stream))
@@ -229,9 +231,9 @@ class FaBwd:
     """Owns one handle; ``run`` allocates nothing when the outputs are passed in."""
 
     def __init__(self, batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv,
-                 algorithm=FA_BWD_ALGO_DEFAULT, num_heads_kv=0, window=0):
+                 algorithm=FA_BWD_ALGO_DEFAULT, num_heads_kv=0, window=0, head_dim_v=0):
         self.handle = fa_bwd_create(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_kv, total_q, total_kv,
-                                    algorithm, num_heads_kv, window)
+                                    algorithm, num_heads_kv, window, head_dim_v)
 
     def run(self, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq=None, dk=None, dv=None,
             stream=None):
@@ -254,7 +256,7 @@ class FaBwd:
 
     def forward(self, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o=None, m=None, l=None, stream=None):
         import torch
-        o = torch.empty_like(q) if o is None else o
+        o = torch.empty(q.shape[:2] + v.shape[2:], dtype=q.dtype, device=q.device) if o is None else o
         m = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if m is None else m
         l = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if l is None else l
         fa_fwd_run(self.handle, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o, m, l, stream)
@@ -277,7 +279,7 @@ def attention_backward(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scal
                        window: int = 0):
     """One-shot call: create a handle, run on the current stream, destroy (which waits)."""
     with FaBwd(cu_seqlens_q.numel() - 1, q.shape[1], q.shape[2], max_seqlen_q, max_seqlen_kv,
-               q.shape[0], k.shape[0], algorithm, k.shape[1], window) as op:
+               q.shape[0], k.shape[0], algorithm, k.shape[1], window, v.shape[2]) as op:
         return op.run(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask)
 
 
@@ -285,5 +287,5 @@ def attention_forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale: float, mask: 
                       max_seqlen_kv: int, window: int = 0):
     """One-shot forward: returns O (bf16), m, l (fp32) on q's device."""
     with FaBwd(cu_seqlens_q.numel() - 1, q.shape[1], q.shape[2], max_seqlen_q, max_seqlen_kv,
-               q.shape[0], k.shape[0], num_heads_kv=k.shape[1], window=window) as op:
+               q.shape[0], k.shape[0], num_heads_kv=k.shape[1], window=window, head_dim_v=v.shape[2]) as op:
         return op.forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask)

@@ -9,7 +9,7 @@
 #include <vector>
 
 #include "fa_bwd.h"
-#include "fa_bwd_kernels.hpp"
+#include "fa_bwd_launch.hpp"
 
 struct fa_bwd_handle {
   fa_bwd_desc desc;
@@ -36,12 +36,27 @@ void release_events(fa_bwd_handle* h) {
   h->recorded = 0;
 }
 
+bool head_dim_ok(int32_t d) { return d >= 8 && d <= 256 && d % 8 == 0; }
+
+// threads per (token, head) row of the row kernels: a power of two covering the wider row in
+// 8-element chunks
+int threads_per_row(int d_qk, int d_v) {
+  const int chunks = (d_qk > d_v ? d_qk : d_v) / 8;
+  int t = 1;
+  while (t < chunks) t *= 2;
+  return t;
+}
+
 fa_bwd_status check_desc(const fa_bwd_desc* d) {
   if (!d) return FA_BWD_ERR_INVALID_ARGUMENT;
   if (d->batch < 1 || d->num_heads < 1 || d->max_seqlen_q < 1 || d->max_seqlen_kv < 1 || d->total_q < 1 ||
       d->total_kv < 1)
     return FA_BWD_ERR_INVALID_ARGUMENT;
-  if (d->head_dim != 64 && d->head_dim != 128) return FA_BWD_ERR_UNSUPPORTED;
+  const int32_t dv = d->head_dim_v == 0 ? d->head_dim : d->head_dim_v;
+  if (!head_dim_ok(d->head_dim) || !head_dim_ok(dv)) return FA_BWD_ERR_UNSUPPORTED;
+  // the single-pass kernels exist for equal head dims of 64 and 128
+  if (d->algorithm == FA_BWD_ALGO_SINGLE_PASS && (dv != d->head_dim || (d->head_dim != 64 && d->head_dim != 128)))
+    return FA_BWD_ERR_UNSUPPORTED;
   const int32_t hkv = d->num_heads_kv == 0 ? d->num_heads : d->num_heads_kv;
   if (hkv < 1 || d->num_heads % hkv != 0) return FA_BWD_ERR_INVALID_ARGUMENT;
   // the single-pass form owns one (kv tile, head) per workgroup; grouped K/V heads need the recompute form
@@ -52,16 +67,96 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   // index arithmetic stays in int64; grids must fit the launch limits
   const int64_t rows = (d->total_q > d->total_kv ? d->total_q : d->total_kv);
   if (rows > (int64_t(1) << 40) / d->num_heads) return FA_BWD_ERR_INVALID_ARGUMENT;
-  const int64_t kv_tiles = (d->max_seqlen_kv + 127) / 128;
+  // 128 rows of any tensor span less than 2^30 bytes: the kernels' 32-bit tile offsets, and the
+  // out-of-range offset that reads zeros, rely on it
+  const int64_t dmax = d->head_dim > dv ? d->head_dim : dv;
+  if ((int64_t)d->num_heads * dmax * 2 * 128 >= (int64_t(1) << 30)) return FA_BWD_ERR_INVALID_ARGUMENT;
+  const int64_t kv_tiles = (d->max_seqlen_kv + 63) / 64;  // the smallest kv tile of any kernel
   if (kv_tiles * d->num_heads * d->batch > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
   const int64_t q_tiles = (d->max_seqlen_q + 127) / 128;
   if (q_tiles * d->num_heads * d->batch > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
-  const int64_t rows_per_block = 256 / (d->head_dim / 8);
+  const int64_t rows_per_block = 256 / threads_per_row(d->head_dim, dv);
   if ((rows * d->num_heads + rows_per_block - 1) / rows_per_block > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
   return FA_BWD_OK;
 }
 
+// The kernels for the padded head dims: each dim rounded up to 64, 128 or 256, and a dim of 64 next
+// to one of 256 taken as 128.
+int padded_dim(int d) { return d <= 64 ? 64 : d <= 128 ? 128 : 256; }
+
+fa::KernelSet pick_kernels(int d_qk, int d_v) {
+  int pq = padded_dim(d_qk), pv = padded_dim(d_v);
+  if (pq == 256 || pv == 256) {
+    if (pq == 64) pq = 128;
+    if (pv == 64) pv = 128;
+  }
+  const bool exact = d_qk == pq && d_v == pv && pq == pv;  // instantiated for equal padded dims
+  if (pq == 256 || pv == 256) return fa::wide_kernel_set(pq, pv, exact);
+  if (pq == 64 && pv == 64) return exact ? fa::kernel_set<64, 64, true>() : fa::kernel_set<64, 64, false>();
+  if (pq == 128 && pv == 128) return exact ? fa::kernel_set<128, 128, true>() : fa::kernel_set<128, 128, false>();
+  return pq == 64 ? fa::kernel_set<64, 128, false>() : fa::kernel_set<128, 64, false>();
+}
+
+// Records the next run's four events when profiling is on; nullptr otherwise (or past the limit).
+fa_bwd_status next_events(fa_bwd_handle* h, hipEvent_t** out) {
+  *out = nullptr;
+  if (!h->profiling || h->recorded >= kMaxProfiledRuns) return FA_BWD_OK;
+  const size_t base = (size_t)h->recorded * 4;
+  if (h->events.size() < base + 4) {
+    for (int i = 0; i < 4; ++i) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return FA_BWD_ERR_HIP;
+      h->events.push_back(e);
+    }
+  }
+  *out = &h->events[base];
+  ++h->recorded;
+  return FA_BWD_OK;
+}
+
+// The row kernels, one instance per power-of-two threads per row.
+template <int TPR>
+struct pre_kernel {
+  static constexpr auto fn = fa::fa_bwd_pre<TPR, false>;
+};
+template <int TPR>
+struct pre_kernel_exact {  // d_qk = d_v = 8 TPR
+  static constexpr auto fn = fa::fa_bwd_pre<TPR, true>;
+};
+template <int TPR>
+struct fill_kernel {
+  static constexpr auto fn = fa::fa_fwd_fill<TPR>;
+};
+
+template <class Args, template <int> class K>
+void launch_rows(int tpr, dim3 grid, hipStream_t stream, const Args& a) {
+  switch (tpr) {
+    case 1: hipLaunchKernelGGL(K<1>::fn, grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(K<2>::fn, grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(K<4>::fn, grid, dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(K<8>::fn, grid, dim3(256), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(K<16>::fn, grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(K<32>::fn, grid, dim3(256), 0, stream, a); break;
+  }
+}
+
 template <int D>
+void launch_single_pass(const fa::MainArgs& ma, bool causal, hipStream_t stream) {
+  const dim3 grid((unsigned)((ma.max_seqlen_kv + fa::MainCfg<D>::BN - 1) / fa::MainCfg<D>::BN * ma.H * ma.batch));
+  if (causal)
+    fa::fa_bwd_main<D, true, true><<<grid, dim3(256), 0, stream>>>(ma);
+  else
+    fa::fa_bwd_main<D, false, true><<<grid, dim3(256), 0, stream>>>(ma);
+}
+
+template <int D>
+void launch_cast(const fa::MainArgs& ma, hipStream_t stream) {
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t rows = ma.total_q * ma.H;
+  hipLaunchKernelGGL(fa::fa_bwd_dq_cast<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream,
+                     (const float*)ma.dq_acc, ma.dq, ma.total_q, ma.H, ma.scale);
+}
+
 fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void* v, const void* o, const void* dout,
                      const float* m, const float* l, const int32_t* cu_q, const int32_t* cu_kv, float scale,
                      int32_t mask, void* dq, void* dk, void* dv, hipStream_t stream) {
@@ -91,23 +186,20 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   pa.max_seqlen_q = d.max_seqlen_q;
   pa.max_seqlen_kv = d.max_seqlen_kv;
   pa.padded = padded;
+  pa.d_qk = d.head_dim;
+  pa.d_v = d.head_dim_v;
+  const int tpr = threads_per_row(d.head_dim, d.head_dim_v);
   const int64_t rows = (d.total_q > d.total_kv ? d.total_q : d.total_kv) * d.num_heads;
-  constexpr int RPB = 256 / (D / 8);
+  const int rpb = 256 / tpr;
   hipEvent_t* ev = nullptr;
-  if (h->profiling && h->recorded < kMaxProfiledRuns) {
-    const size_t base = (size_t)h->recorded * 4;
-    if (h->events.size() < base + 4) {
-      for (int i = 0; i < 4; ++i) {
-        hipEvent_t e;
-        if (hipEventCreate(&e) != hipSuccess) return FA_BWD_ERR_HIP;
-        h->events.push_back(e);
-      }
-    }
-    ev = &h->events[base];
-    ++h->recorded;
-  }
+  const fa_bwd_status es = next_events(h, &ev);
+  if (es != FA_BWD_OK) return es;
   if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return FA_BWD_ERR_HIP;
-  hipLaunchKernelGGL(fa::fa_bwd_pre<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, pa);
+  const dim3 pre_grid((unsigned)((rows + rpb - 1) / rpb));
+  if (d.head_dim == d.head_dim_v && d.head_dim == 8 * tpr)
+    launch_rows<fa::PreArgs, pre_kernel_exact>(tpr, pre_grid, stream, pa);
+  else
+    launch_rows<fa::PreArgs, pre_kernel>(tpr, pre_grid, stream, pa);
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return FA_BWD_ERR_HIP;
 
@@ -134,53 +226,41 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.padded = padded;
   ma.causal = causal;
   ma.window = d.window;
+  ma.d_qk = d.head_dim;
+  ma.d_v = d.head_dim_v;
   ma.scale_log2 = scale * fa::kLog2e;
   ma.scale = scale;
-  const int64_t kv_tiles = (d.max_seqlen_kv + fa::MainCfg<D>::BN - 1) / fa::MainCfg<D>::BN;
-  const dim3 grid((unsigned)(kv_tiles * d.num_heads * d.batch));
-  if (h->single_pass) {
-    if (causal)
-      fa::fa_bwd_main<D, true, true><<<grid, dim3(256), 0, stream>>>(ma);
+  const fa::KernelSet ks = pick_kernels(d.head_dim, d.head_dim_v);
+  if (h->single_pass) {  // head_dim == head_dim_v, 64 or 128 (checked at create)
+    if (d.head_dim == 128)
+      launch_single_pass<128>(ma, causal, stream);
     else
-      fa::fa_bwd_main<D, false, true><<<grid, dim3(256), 0, stream>>>(ma);
+      launch_single_pass<64>(ma, causal, stream);
   } else {
-    const dim3 dgrid((unsigned)(kv_tiles * d.num_heads_kv * d.batch));  // (kv tile, K/V head, sequence)
-    if (d.window > 0)  // the window implies the causal bound
-      fa::fa_bwd_dkdv<D, true, true><<<dgrid, dim3(512), 0, stream>>>(ma);
-    else if (causal)
-      fa::fa_bwd_dkdv<D, true, false><<<dgrid, dim3(512), 0, stream>>>(ma);
-    else
-      fa::fa_bwd_dkdv<D, false, false><<<dgrid, dim3(512), 0, stream>>>(ma);
+    ks.dkdv(ma, stream);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return FA_BWD_ERR_HIP;
 
   if (h->single_pass) {
-    const int64_t qrows = d.total_q * d.num_heads;
-    hipLaunchKernelGGL(fa::fa_bwd_dq_cast<D>, dim3((unsigned)((qrows + RPB - 1) / RPB)), dim3(256), 0, stream,
-                       (const float*)h->dq_acc, static_cast<bf16*>(dq), d.total_q, d.num_heads, scale);
-  } else {
-    const int64_t q_tiles = (d.max_seqlen_q + fa::DqCfg<D>::BQ - 1) / fa::DqCfg<D>::BQ;
-    const dim3 qgrid((unsigned)(q_tiles * d.num_heads * d.batch));
-    if (d.window > 0)
-      fa::fa_bwd_dq<D, true, true><<<qgrid, dim3(256), 0, stream>>>(ma);
-    else if (causal)
-      fa::fa_bwd_dq<D, true, false><<<qgrid, dim3(256), 0, stream>>>(ma);
+    if (d.head_dim == 128)
+      launch_cast<128>(ma, stream);
     else
-      fa::fa_bwd_dq<D, false, false><<<qgrid, dim3(256), 0, stream>>>(ma);
+      launch_cast<64>(ma, stream);
+  } else {
+    ks.dq(ma, stream);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return FA_BWD_ERR_HIP;
   return FA_BWD_OK;
 }
 
-template <int D>
 fa_bwd_status launch_fwd(fa_bwd_handle* h, const void* q, const void* k, const void* v, const int32_t* cu_q,
                          const int32_t* cu_kv, float scale, int32_t mask, void* o, float* m, float* l,
                          hipStream_t stream) {
   const fa_bwd_desc& d = h->desc;
   const int padded = (mask == FA_BWD_MASK_PADDING || mask == FA_BWD_MASK_PADDING_CAUSAL) ? 1 : 0;
-  const int causal = (mask == FA_BWD_MASK_CAUSAL || mask == FA_BWD_MASK_PADDING_CAUSAL) ? 1 : 0;
+  const bool causal = mask == FA_BWD_MASK_CAUSAL || mask == FA_BWD_MASK_PADDING_CAUSAL;
   using fa::bf16;
   fa::FwdArgs fa;
   fa.q = static_cast<const bf16*>(q);
@@ -199,36 +279,21 @@ fa_bwd_status launch_fwd(fa_bwd_handle* h, const void* q, const void* k, const v
   fa.max_seqlen_q = d.max_seqlen_q;
   fa.max_seqlen_kv = d.max_seqlen_kv;
   fa.padded = padded;
-  fa.scale_log2 = scale * fa::kLog2e;
   fa.window = d.window;
+  fa.d_qk = d.head_dim;
+  fa.d_v = d.head_dim_v;
+  fa.scale_log2 = scale * fa::kLog2e;
   hipEvent_t* ev = nullptr;
-  if (h->profiling && h->recorded < kMaxProfiledRuns) {
-    const size_t base = (size_t)h->recorded * 4;
-    if (h->events.size() < base + 4) {
-      for (int i = 0; i < 4; ++i) {
-        hipEvent_t e;
-        if (hipEventCreate(&e) != hipSuccess) return FA_BWD_ERR_HIP;
-        h->events.push_back(e);
-      }
-    }
-    ev = &h->events[base];
-    ++h->recorded;
-  }
-  constexpr int RPB = 256 / (D / 8);
+  const fa_bwd_status es = next_events(h, &ev);
+  if (es != FA_BWD_OK) return es;
+  const int tpr = threads_per_row(d.head_dim_v, d.head_dim_v);
+  const int rpb = 256 / tpr;
   const int64_t rows = d.total_q * d.num_heads;
   if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return FA_BWD_ERR_HIP;
-  hipLaunchKernelGGL(fa::fa_fwd_fill<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, fa);
+  launch_rows<fa::FwdArgs, fill_kernel>(tpr, dim3((unsigned)((rows + rpb - 1) / rpb)), stream, fa);
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return FA_BWD_ERR_HIP;
-  using QC = fa::DqCfg<D>;
-  const int64_t q_tiles = (d.max_seqlen_q + QC::BQ - 1) / QC::BQ;
-  const dim3 grid((unsigned)(q_tiles * d.num_heads * d.batch));
-  if (d.window > 0)
-    fa::fa_fwd<D, true, true><<<grid, dim3(256), 0, stream>>>(fa);
-  else if (causal)
-    fa::fa_fwd<D, true, false><<<grid, dim3(256), 0, stream>>>(fa);
-  else
-    fa::fa_fwd<D, false, false><<<grid, dim3(256), 0, stream>>>(fa);
+  pick_kernels(d.head_dim, d.head_dim_v).fwd(fa, causal, stream);
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && (hipEventRecord(ev[2], stream) != hipSuccess || hipEventRecord(ev[3], stream) != hipSuccess))
     return FA_BWD_ERR_HIP;
@@ -261,11 +326,8 @@ fa_bwd_status run_common(fa_bwd_handle* h, const void* q, const void* k, const v
     return FA_BWD_ERR_INVALID_ARGUMENT;
   const fa_bwd_status cs = check_run(h, scale, mask);
   if (cs != FA_BWD_OK) return cs;
-  const fa_bwd_desc& d = h->desc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d.head_dim == 128)
-    return launch<128>(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, s);
-  return launch<64>(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, s);
+  return launch(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv,
+                static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -281,6 +343,7 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
   if (!h) return FA_BWD_ERR_OUT_OF_MEMORY;
   h->desc = *desc;
   if (h->desc.num_heads_kv == 0) h->desc.num_heads_kv = desc->num_heads;
+  if (h->desc.head_dim_v == 0) h->desc.head_dim_v = desc->head_dim;
   h->single_pass = desc->algorithm == FA_BWD_ALGO_SINGLE_PASS;
   if (hipGetDevice(&h->device) != hipSuccess) {
     delete h;
@@ -329,10 +392,7 @@ fa_bwd_status fa_fwd_run(fa_bwd_handle* h, const void* q, const void* k, const v
     return FA_BWD_ERR_INVALID_ARGUMENT;
   const fa_bwd_status cs = check_run(h, scale, mask);
   if (cs != FA_BWD_OK) return cs;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (h->desc.head_dim == 128)
-    return launch_fwd<128>(h, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o, m, l, s);
-  return launch_fwd<64>(h, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o, m, l, s);
+  return launch_fwd(h, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o, m, l, static_cast<hipStream_t>(stream));
 }
 
 fa_bwd_status fa_bwd_destroy(fa_bwd_handle* h) {

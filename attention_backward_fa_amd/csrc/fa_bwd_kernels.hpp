@@ -18,8 +18,12 @@
 //                  accumulates dQ (step 8) in registers; no atomics.
 //   fa_fwd_fill,   the forward that produces O, m, l (the statistics step 2
 //   fa_fwd         reads), for callers without one of their own.
-// The recompute kernels and the forward also take grouped K/V heads and a
-// sliding window (each query sees keys (i - w, i]).
+// The recompute kernels and the forward also take grouped K/V heads, a
+// sliding window (each query sees keys (i - w, i]) and any head dims that are
+// multiples of 8 up to 256, separately for Q/K and for V/O/dO (latent
+// attention): they are compiled for padded dims DQ, DV in {64, 128, 256}, and
+// the columns from a head dim up to its padded dim are loaded as zeros and
+// never stored.
 #pragma once
 #include <type_traits>
 
@@ -58,41 +62,44 @@ struct PreArgs {
   const int* cu_kv;
   float* lse2;    // [H][total_q]: m*log2(e) + log2(l)
   float* dvec;    // [H][total_q]: rowsum(O*dO)
-  float* dq_acc;  // [H][total_q][D], zeroed when not null
+  float* dq_acc;  // [H][total_q][d_qk], zeroed when not null
   bf16* dq;       // when not null: rows outside every sequence are zeroed
   bf16* dk;
   bf16* dv;
   int64_t total_q, total_kv;
   int H, Hk, batch, max_seqlen_q, max_seqlen_kv, padded;  // query heads, K/V heads
+  int d_qk, d_v;  // head dims of Q, K (dQ, dK) and of V, O, dO (dV); multiples of 8
 };
 
-template <int D>
+// One thread per 8 features of a (token, head) row, 256 / TPR rows per block; TPR is a power of two
+// >= max(d_qk, d_v) / 8. EXACT: d_qk = d_v = 8 TPR, known at compile time.
+template <int TPR, bool EXACT>
 __global__ __launch_bounds__(256) void fa_bwd_pre(PreArgs a) {
-  constexpr int TPR = D / 8;      // threads per (token, head) row, 8 elements each
-  constexpr int RPB = 256 / TPR;  // rows per block
-  const int sub = threadIdx.x % TPR;
-  const int64_t pair = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;  // = t * H + h
+  const int sub = threadIdx.x & (TPR - 1);
+  const int64_t pair = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;  // = t * H + h
   const int64_t t = pair / a.H;
   const int h = (int)(pair - t * a.H);
-  const int64_t off = pair * D + sub * 8;
+  const int cq = EXACT ? TPR : a.d_qk / 8, cv = EXACT ? TPR : a.d_v / 8;  // 16-byte chunks per row
+  const u32x4 z = {0u, 0u, 0u, 0u};
   if (t < a.total_q) {
-    const bf16x8 ov = *(const bf16x8*)(a.o + off);
-    const bf16x8 gv = *(const bf16x8*)(a.dout + off);
     float acc = 0.f;
+    if (sub < cv) {
+      const int64_t off = pair * (8 * cv) + sub * 8;
+      const bf16x8 ov = *(const bf16x8*)(a.o + off);
+      const bf16x8 gv = *(const bf16x8*)(a.dout + off);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += from_bf16(ov[e]) * from_bf16(gv[e]);
+      for (int e = 0; e < 8; ++e) acc += from_bf16(ov[e]) * from_bf16(gv[e]);
+    }
 #pragma unroll
-    for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
-    if (a.dq_acc) {
-      float* accrow = a.dq_acc + ((int64_t)h * a.total_q + t) * D + sub * 8;
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      *(f32x4*)accrow = z;
-      *(f32x4*)(accrow + 4) = z;
+    for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);  // partners share the row
+    if (a.dq_acc && sub < cq) {
+      float* accrow = a.dq_acc + ((int64_t)h * a.total_q + t) * (8 * cq) + sub * 8;
+      const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)accrow = zf;
+      *(f32x4*)(accrow + 4) = zf;
     }
-    if (a.dq && !row_in_sequence(t, a.cu_q, a.batch, a.padded, a.max_seqlen_q)) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *(u32x4*)(a.dq + off) = z;
-    }
+    if (a.dq && sub < cq && !row_in_sequence(t, a.cu_q, a.batch, a.padded, a.max_seqlen_q))
+      *(u32x4*)(a.dq + pair * (8 * cq) + sub * 8) = z;
     if (sub == 0) {
       const int64_t sidx = (int64_t)h * a.total_q + t;
       a.dvec[sidx] = acc;
@@ -101,10 +108,9 @@ __global__ __launch_bounds__(256) void fa_bwd_pre(PreArgs a) {
     }
   }
   if (h < a.Hk && t < a.total_kv && !row_in_sequence(t, a.cu_kv, a.batch, a.padded, a.max_seqlen_kv)) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const int64_t koff = (t * a.Hk + h) * D + sub * 8;
-    *(u32x4*)(a.dk + koff) = z;
-    *(u32x4*)(a.dv + koff) = z;
+    const int64_t kr = t * a.Hk + h;
+    if (sub < cq) *(u32x4*)(a.dk + kr * (8 * cq) + sub * 8) = z;
+    if (sub < cv) *(u32x4*)(a.dv + kr * (8 * cv) + sub * 8) = z;
   }
 }
 
@@ -126,6 +132,7 @@ struct MainArgs {
   int64_t total_q, total_kv;
   int H, Hk, batch, max_seqlen_q, max_seqlen_kv, padded, causal;  // query heads, K/V heads (H % Hk == 0)
   int window;        // > 0: each query sees only its left local window of keys (i - window, i]
+  int d_qk, d_v;     // head dims of Q, K (dQ, dK) and of V, dO (dV): at most the kernel's padded dims
   float scale_log2;  // scale * log2(e)
   float scale;
 };
@@ -169,8 +176,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
 }
 
+// A buffer offset past every resource this file builds (the host keeps 128 rows of any tensor
+// below 2^30 bytes): a load from it returns 0. Tile columns at or past a head dim that is smaller
+// than the kernel's padded dim are read from here, so they hold zeros.
+constexpr int kOutOfRange = 0x40000000;
+
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// 1 KB LDS-DMA transfers of a tile with padded rows of cpr 16-byte chunks: this lane's offset in
+// transfer j. Chunks at or past the head dim d (zero columns up to the padded dim, row padding)
+// read out of range and load zeros.
+__device__ __forceinline__ int tile_dma_off(int j, int lane, int cpr, int row_bytes, int d) {
+  const int p16 = 64 * j + lane;
+  const int r = p16 / cpr, ch = p16 % cpr;
+  return ch < d / 8 ? r * row_bytes + ch * 16 : kOutOfRange;
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
@@ -490,46 +511,60 @@ void fa_bwd_main(MainArgs a) {
 
 // ------------------------------------------------------------------ stage 2a: dK and dV by recompute
 
-template <int D>
+// Tiling of the dK/dV kernel for padded head dims DQ (Q, K) and DV (V, dO), multiples of 32. Up to
+// 128: eight waves (two per SIMD), a 128-row kv tile whose K and V sit in LDS. Wider heads: four
+// waves (one per SIMD, accumulators in the larger register budget of a single wave), a 64-row kv
+// tile whose K and V fragments are held in registers, so that LDS holds only the Q and dO tiles.
+template <int DQ, int DV>
 struct DkdvCfg {
-  static constexpr int BN = 128;                 // kv rows per workgroup: 4 row groups of 32
+  static constexpr bool WIDE = DQ > 128 || DV > 128;
+  static constexpr int WPE = WIDE ? 1 : 2;       // waves per SIMD
+  static constexpr int BN = WIDE ? 64 : 128;     // kv rows per workgroup: row groups of 32
   static constexpr int BM = 64;                  // q rows per step: 2 M-tiles of 32
-  static constexpr int NW = 8;                   // waves: 4 row groups x 2 M-tiles
+  static constexpr int NG = BN / 32;             // row groups
+  static constexpr int NW = 2 * NG;              // waves: row groups x 2 M-tiles
   static constexpr int NT = 64 * NW;
-  static constexpr int KSD = D / 16;
-  static constexpr int NTD = D / 32;
-  static constexpr int QS = D + 8;               // padded row stride of every LDS tile
-  static constexpr int CPR = QS / 8;
-  static constexpr int TILE = BM * QS;
-  static constexpr int TILE_BYTES = TILE * 2;
-  static constexpr int NDMA = TILE_BYTES / 1024;
-  static constexpr int KV_BYTES = BN * QS * 2;   // the K (or V) tile of the workgroup
-  static constexpr int NDMA_KV = KV_BYTES / 1024;
-  static constexpr int OFF_K = 0;                             // K [BN][QS]
-  static constexpr int OFF_V = OFF_K + KV_BYTES;              // V [BN][QS]
-  static constexpr int OFF_Q = OFF_V + KV_BYTES;              // Q [2][BM][QS]
-  static constexpr int OFF_DO = OFF_Q + 2 * TILE_BYTES;       // dO [2][BM][QS]
-  static constexpr int OFF_ST = OFF_DO + 2 * TILE_BYTES;      // [2 buffers][lse2, D][BM] fp32
-  static constexpr int LDS_BYTES = OFF_ST + 4 * BM * 4;
-  static constexpr int PART_BYTES = NTD * 16 * 4 * 64;        // one wave's partial dK or dV tile
-  static_assert(TILE_BYTES % 1024 == 0 && KV_BYTES % 1024 == 0, "tiles are whole 1 KB transfers");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget (one 8-wave workgroup per CU)");
-  static_assert(NW * PART_BYTES <= OFF_ST, "the end-of-kernel exchange of partial sums fits in the tiles");
+  static constexpr int KSQ = DQ / 16, KSV = DV / 16, KSM = KSQ > KSV ? KSQ : KSV;  // MFMA k-steps
+  static constexpr int NTQ = DQ / 32, NTV = DV / 32, NTM = NTQ > NTV ? NTQ : NTV;  // 32-wide tiles
+  static constexpr int QSQ = DQ + 8, QSV = DV + 8;  // padded row strides of the LDS tiles
+  static constexpr int CPRQ = QSQ / 8, CPRV = QSV / 8;
+  static constexpr int TQ_BYTES = BM * QSQ * 2;  // one Q tile
+  static constexpr int TD_BYTES = BM * QSV * 2;  // one dO tile
+  static constexpr int NDMA_Q = TQ_BYTES / 1024, NDMA_D = TD_BYTES / 1024;
+  static constexpr int K_BYTES = WIDE ? 0 : BN * QSQ * 2;  // the K (and V) tile of the workgroup
+  static constexpr int V_BYTES = WIDE ? 0 : BN * QSV * 2;
+  static constexpr int NDMA_K = K_BYTES / 1024, NDMA_V = V_BYTES / 1024;
+  static constexpr int OFF_K = 0;                             // K [BN][QSQ]
+  static constexpr int OFF_V = OFF_K + K_BYTES;               // V [BN][QSV]
+  static constexpr int OFF_Q = OFF_V + V_BYTES;               // Q [2][BM][QSQ]
+  static constexpr int OFF_DO = OFF_Q + 2 * TQ_BYTES;         // dO [2][BM][QSV]
+  static constexpr int OFF_ST = OFF_DO + 2 * TD_BYTES;        // [2 buffers][lse2, D][BM] fp32
+  static constexpr int OFF_X = OFF_ST + 4 * BM * 4;           // wide: [wave][lane] 2 bf16x8 of P or dS
+  static constexpr int LDS_BYTES = OFF_X + (WIDE ? NW * 64 * 32 : 0);
+  static constexpr int PART_BYTES = WIDE ? 0 : NG * (NTQ + NTV) * 64 * 64;  // partial dK, then dV
+  static_assert(DQ % 32 == 0 && DV % 32 == 0 && DQ <= 256 && DV <= 256, "padded head dims");
+  static_assert(TQ_BYTES % 1024 == 0 && TD_BYTES % 1024 == 0 && K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0,
+                "tiles are whole 1 KB transfers");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget (one workgroup per CU)");
+  static_assert(PART_BYTES <= OFF_ST, "the end-of-kernel exchange of partial sums fits in the tiles");
 };
 
-// dK and dV of one (kv tile, K/V head, sequence). Eight waves: row group r = w % 4 owns kv rows
-// 32 r .. 32 r + 31, and the two waves of a group each take one 32-row M-tile mt = w / 4 of every
-// 64-row q step. Each wave forms S = Q K^T, dP = dO V^T, P and dS for its M-tile (steps 1-5) and
-// accumulates its partial dV += P^T dO and dK += dS^T Q over its M-tile's rows (steps 7, 6), so
-// the waves of a step never wait for each other; K and V are read from an LDS tile loaded once,
-// which leaves registers for both accumulators. After the last step the two waves of a group
-// combine their partial sums through LDS (the M-tile 0 wave finishes dV, the other dK).
-template <int D, bool CAUSAL, bool WINDOW>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+// dK and dV of one (kv tile, K/V head, sequence). Row group r = w % NG owns kv rows 32 r .. 32 r + 31,
+// and the two waves of a group each take one 32-row M-tile mt = w / NG of every 64-row q step. Each
+// wave forms S = Q K^T, dP = dO V^T, P and dS for its M-tile (steps 1-5). Heads up to 128: each wave
+// accumulates its partial dV += P^T dO and dK += dS^T Q over its M-tile's rows (steps 7, 6), so the
+// waves of a step never wait for each other, and after the last step the two waves of a group
+// combine their partial sums through LDS (the M-tile 0 wave finishes dV, the other dK). Wider heads,
+// where both accumulators of a wave would not fit its registers next to the K and V fragments: the
+// waves of a group swap P and dS through LDS each step, and the M-tile 0 wave accumulates dV over
+// both M-tiles, the other dK.
+template <int DQ, int DV, bool CAUSAL, bool WINDOW, bool EXACT>
+__global__ __attribute__((amdgpu_flat_work_group_size(DkdvCfg<DQ, DV>::NT, DkdvCfg<DQ, DV>::NT),
+                          amdgpu_waves_per_eu(DkdvCfg<DQ, DV>::WPE, DkdvCfg<DQ, DV>::WPE)))
 void fa_bwd_dkdv(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = DkdvCfg<D>;
-  constexpr int BN = C::BN, BM = C::BM, QS = C::QS;
+  using C = DkdvCfg<DQ, DV>;
+  constexpr int BN = C::BN, BM = C::BM, NG = C::NG, QSQ = C::QSQ, QSV = C::QSV;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   const bf16* s_k = (const bf16*)(smem + C::OFF_K);
   const bf16* s_v = (const bf16*)(smem + C::OFF_V);
@@ -552,13 +587,14 @@ void fa_bwd_dkdv(MainArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int grp = w & 3, mt = w >> 2;  // kv row group; M-tile
+  const int grp = w % NG, mt = w / NG;  // kv row group; M-tile
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
-  const int64_t rs = (int64_t)a.H * D;    // row stride of Q, dO
-  const int rsb = (int)(rs * 2);
-  const int64_t rsk = (int64_t)a.Hk * D;  // row stride of K, V, dK, dV
-  const int rskb = (int)(rsk * 2);
-  const int G = a.H / a.Hk;               // query heads sharing this K/V head: hk * G .. hk * G + G - 1
+  const int dqk = EXACT ? DQ : a.d_qk, dvd = EXACT ? DV : a.d_v;  // EXACT: the padded dims
+  const int64_t rsq = (int64_t)a.H * dqk, rsd = (int64_t)a.H * dvd;     // row strides of Q and dO
+  const int rsqb = (int)(rsq * 2), rsdb = (int)(rsd * 2);
+  const int64_t rskq = (int64_t)a.Hk * dqk, rskv = (int64_t)a.Hk * dvd;  // of K (dK) and V (dV)
+  const int rskqb = (int)(rskq * 2), rskvb = (int)(rskv * 2);
+  const int G = a.H / a.Hk;  // query heads sharing this K/V head: hk * G .. hk * G + G - 1
 
   {  // zero the tiles once: rows past the sequences then hold zeros or earlier valid rows
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -578,44 +614,68 @@ void fa_bwd_dkdv(MainArgs a) {
   auto step_tile = [&](int st) { return qt0 + st % nq; };
   const int jcol = kv0 + 32 * grp + c;  // this lane's key row (sequence-local)
 
-  // 1 KB LDS-DMA transfers of padded rows: transfer j, lane -> row p16 / CPR, 16-byte chunk p16 % CPR
-  auto dma_row_off = [&](int j, int row_bytes) {
-    const int p16 = 64 * j + lane;
-    const int r = p16 / C::CPR, ch = p16 % C::CPR;
-    return r * row_bytes + (ch < D / 8 ? ch : 0) * 16;
-  };
-  {  // the K and V tiles, once
-    const int kv_rows = imin(Lk - kv0, BN);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + (kv_start + kv0) * rsk + (int64_t)hk * D, (int64_t)kv_rows * rskb);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (kv_start + kv0) * rsk + (int64_t)hk * D, (int64_t)kv_rows * rskb);
-    for (int j = w; j < C::NDMA_KV; j += C::NW) {
-      const int off = dma_row_off(j, rskb);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(smem + C::OFF_K + 1024 * j),
-                                               16, off, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(smem + C::OFF_V + 1024 * j),
-                                               16, off, 0, 0, 0);
+  const int kv_rows = imin(Lk - kv0, BN);
+  const bf16* kbase = a.k + (kv_start + kv0) * rskq + (int64_t)hk * dqk;
+  const bf16* vbase = a.v + (kv_start + kv0) * rskv + (int64_t)hk * dvd;
+  // wide heads: this lane's K and V rows as B-operand fragments (key 32 grp + c, features 16 ks + 8 hh)
+  bf16x8 kreg[C::WIDE ? C::KSQ : 1], vreg[C::WIDE ? C::KSV : 1];
+  if constexpr (C::WIDE) {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (int64_t)kv_rows * rskqb);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (int64_t)kv_rows * rskvb);
+    const int row = 32 * grp + c;
+#pragma unroll
+    for (int ks = 0; ks < C::KSQ; ++ks) {
+      const int col = 16 * ks + 8 * hh;
+      kreg[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, col < dqk ? row * rskqb + col * 2 : kOutOfRange));
     }
+#pragma unroll
+    for (int ks = 0; ks < C::KSV; ++ks) {
+      const int col = 16 * ks + 8 * hh;
+      vreg[ks] = __builtin_bit_cast(bf16x8, buf_load16(rv, col < dvd ? row * rskvb + col * 2 : kOutOfRange));
+    }
+  } else {  // the K and V tiles, once
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (int64_t)kv_rows * rskqb);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (int64_t)kv_rows * rskvb);
+    for (int j = w; j < C::NDMA_K; j += C::NW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(smem + C::OFF_K + 1024 * j),
+                                               16, tile_dma_off(j, lane, C::CPRQ, rskqb, dqk), 0, 0, 0);
+    for (int j = w; j < C::NDMA_V; j += C::NW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(smem + C::OFF_V + 1024 * j),
+                                               16, tile_dma_off(j, lane, C::CPRV, rskvb, dvd), 0, 0, 0);
   }
-  constexpr int NJ = (C::NDMA + C::NW - 1) / C::NW;
-  int dma_off[NJ];
+  constexpr int NJQ = (C::NDMA_Q + C::NW - 1) / C::NW, NJD = (C::NDMA_D + C::NW - 1) / C::NW;
+  int offq[NJQ], offd[NJD];
 #pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) dma_off[jj] = dma_row_off(w + C::NW * jj, rsb);
+  for (int jj = 0; jj < NJQ; ++jj) offq[jj] = tile_dma_off(w + C::NW * jj, lane, C::CPRQ, rsqb, dqk);
+#pragma unroll
+  for (int jj = 0; jj < NJD; ++jj) offd[jj] = tile_dma_off(w + C::NW * jj, lane, C::CPRV, rsdb, dvd);
   auto issue_tile = [&](int st, int bi) {
-    const int i0 = step_tile(st) * BM;
-    const int64_t hoff = (q_start + i0) * rs + (int64_t)step_head(st) * D;
-    const int64_t bytes = (int64_t)imin(Lq - i0, BM) * rsb;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + hoff, bytes);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + hoff, bytes);
+    const int i0 = step_tile(st) * BM, hq = step_head(st);
+    const int rows = imin(Lq - i0, BM);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + (q_start + i0) * rsq + (int64_t)hq * dqk, (int64_t)rows * rsqb);
+    const __amdgpu_buffer_rsrc_t rd =
+        make_rsrc(a.dout + (q_start + i0) * rsd + (int64_t)hq * dvd, (int64_t)rows * rsdb);
+    auto dma_q = [&](int jj, int j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rq, (__attribute__((address_space(3))) void*)(smem + C::OFF_Q + bi * C::TQ_BYTES + 1024 * j), 16,
+          offq[jj], 0, 0, 0);
+    };
+    auto dma_d = [&](int jj, int j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rd, (__attribute__((address_space(3))) void*)(smem + C::OFF_DO + bi * C::TD_BYTES + 1024 * j), 16,
+          offd[jj], 0, 0, 0);
+    };
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
+    for (int jj = 0; jj < (NJQ > NJD ? NJQ : NJD); ++jj) {
       const int j = w + C::NW * jj;
-      if (j < C::NDMA) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rq, (__attribute__((address_space(3))) void*)(smem + C::OFF_Q + bi * C::TILE_BYTES + 1024 * j), 16,
-            dma_off[jj], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rd, (__attribute__((address_space(3))) void*)(smem + C::OFF_DO + bi * C::TILE_BYTES + 1024 * j), 16,
-            dma_off[jj], 0, 0, 0);
+      if constexpr (C::NDMA_Q == C::NDMA_D) {  // one test for both tiles
+        if (j < C::NDMA_Q) {
+          dma_q(jj, j);
+          dma_d(jj, j);
+        }
+      } else {
+        if (jj < NJQ && j < C::NDMA_Q) dma_q(jj, j);
+        if (jj < NJD && j < C::NDMA_D) dma_d(jj, j);
       }
     }
   };
@@ -633,12 +693,15 @@ void fa_bwd_dkdv(MainArgs a) {
     if (tid < 2 * BM) s_st[bi * 2 * BM + tid] = v;
   };
 
-  f32x16 acc_v[C::NTD], acc_k[C::NTD];  // partial dV and dK / scale of rows 32 grp .. +31 over this M-tile
+  // heads up to 128: partial dV and dK / scale of rows 32 grp .. +31 over this M-tile; wider heads:
+  // acc_w holds dV (M-tile 0 wave) or dK / scale (M-tile 1 wave) of those rows over whole steps
+  f32x16 acc_v[C::WIDE ? 1 : C::NTV], acc_k[C::WIDE ? 1 : C::NTQ], acc_w[C::WIDE ? C::NTM : 1];
 #pragma unroll
-  for (int nt = 0; nt < C::NTD; ++nt) {
-    acc_v[nt] = f32x16{};
-    acc_k[nt] = f32x16{};
-  }
+  for (int nt = 0; nt < C::NTV; ++nt) acc_v[C::WIDE ? 0 : nt] = f32x16{};
+#pragma unroll
+  for (int nt = 0; nt < C::NTQ; ++nt) acc_k[C::WIDE ? 0 : nt] = f32x16{};
+#pragma unroll
+  for (int nt = 0; nt < C::NTM; ++nt) acc_w[C::WIDE ? nt : 0] = f32x16{};
 
   int buf = 0;
   if (n_steps > 0) {
@@ -648,9 +711,12 @@ void fa_bwd_dkdv(MainArgs a) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
 
-  const int arow = (32 * mt + tile_row(c)) * QS + 8 * hh;  // A rows: this M-tile's q rows
-  const int krow = (32 * grp + c) * QS + 8 * hh;            // B columns: this group's keys
-  const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3) + 32 * mt * QS;
+  const int arowq = (32 * mt + tile_row(c)) * QSQ + 8 * hh;  // A rows: this M-tile's q rows
+  const int arowd = (32 * mt + tile_row(c)) * QSV + 8 * hh;
+  const int krow = (32 * grp + c) * QSQ + 8 * hh;  // B columns: this group's keys
+  const int vrow = (32 * grp + c) * QSV + 8 * hh;
+  const int browq = (hh + 4 * (gi >> 2)) * QSQ + 16 * (g & 1) + 4 * (gi & 3) + 32 * mt * QSQ;
+  const int browd = (hh + 4 * (gi >> 2)) * QSV + 16 * (g & 1) + 4 * (gi & 3) + 32 * mt * QSV;
   for (int sp = 0; sp < n_steps; ++sp, buf ^= 1) {
     const bool has_next = sp + 1 < n_steps;
     float st_next = 0.f;
@@ -659,28 +725,38 @@ void fa_bwd_dkdv(MainArgs a) {
       st_next = load_stats(sp + 1);
     }
     const int i0 = step_tile(sp) * BM;
-    const bf16* sq = s_q + buf * C::TILE;
-    const bf16* sd = s_do + buf * C::TILE;
+    const bf16* sq = s_q + buf * (C::TQ_BYTES / 2);
+    const bf16* sd = s_do + buf * (C::TD_BYTES / 2);
     const float* st = s_st + buf * 2 * BM + 32 * mt;
     // steps 1 and 3 for this wave's M-tile: S = Q K^T, dP = dO V^T  ([q 32] x [kv 32]); operands
     // are read PF k-steps ahead into distinct registers, one scheduling fence per k-step
     f32x16 s = f32x16{}, dp = f32x16{};
     {
       constexpr int PF = 2;
-      bf16x8 qa[C::KSD], da[C::KSD], kb[C::KSD], vb[C::KSD];
+      bf16x8 qa[C::KSQ], da[C::KSV], kb[C::KSQ], vb[C::KSV];
       auto ld = [&](int ks) {
-        qa[ks] = *(const bf16x8*)(sq + arow + 16 * ks);
-        da[ks] = *(const bf16x8*)(sd + arow + 16 * ks);
-        kb[ks] = *(const bf16x8*)(s_k + krow + 16 * ks);
-        vb[ks] = *(const bf16x8*)(s_v + krow + 16 * ks);
+        if (ks < C::KSQ) {
+          qa[ks] = *(const bf16x8*)(sq + arowq + 16 * ks);
+          if constexpr (C::WIDE)
+            kb[ks] = kreg[ks];
+          else
+            kb[ks] = *(const bf16x8*)(s_k + krow + 16 * ks);
+        }
+        if (ks < C::KSV) {
+          da[ks] = *(const bf16x8*)(sd + arowd + 16 * ks);
+          if constexpr (C::WIDE)
+            vb[ks] = vreg[ks];
+          else
+            vb[ks] = *(const bf16x8*)(s_v + vrow + 16 * ks);
+        }
       };
 #pragma unroll
       for (int ks = 0; ks < PF; ++ks) ld(ks);
 #pragma unroll
-      for (int ks = 0; ks < C::KSD; ++ks) {
-        if (ks + PF < C::KSD) ld(ks + PF);
-        s = mfma32x32x16(qa[ks], kb[ks], s);
-        dp = mfma32x32x16(da[ks], vb[ks], dp);
+      for (int ks = 0; ks < C::KSM; ++ks) {
+        if (ks + PF < C::KSM) ld(ks + PF);
+        if (ks < C::KSQ) s = mfma32x32x16(qa[ks], kb[ks], s);
+        if (ks < C::KSV) dp = mfma32x32x16(da[ks], vb[ks], dp);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -718,14 +794,34 @@ void fa_bwd_dkdv(MainArgs a) {
     // steps 7 and 6 over this M-tile: dV += P^T dO, dK += dS^T Q. k-step s2: its k-index e is MFMA
     // row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4; the transpose reads fetch those rows.
     // B operands are read PF MFMAs ahead; the dV and dK MFMAs alternate (independent chains).
-    {
-      constexpr int NB = 2 * C::NTD, PF = 2;
-      bf16x8 bd[NB], bq[NB];
+    if constexpr (C::WIDE) {
+      // swap with the partner wave: the M-tile 0 wave needs the partner's P (for dV), the other the
+      // partner's dS (for dK); then one GEMM over the step's 64 q rows, k-steps in row order
+      bf16x8* xs = (bf16x8*)(smem + C::OFF_X);
+      const int partner = grp + NG * (1 - mt);
+      xs[(w * 64 + lane) * 2] = mt == 0 ? dsk[0] : pk[0];
+      xs[(w * 64 + lane) * 2 + 1] = mt == 0 ? dsk[1] : pk[1];
+      __syncthreads();
+      bf16x8 am[4];  // A operand of k-step 2 u + s2: M-tile u, its k-step s2
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const bf16x8 own = mt == 0 ? pk[s2] : dsk[s2];
+        const bf16x8 other = xs[(partner * 64 + lane) * 2 + s2];
+        am[s2] = mt == 0 ? own : other;
+        am[2 + s2] = mt == 0 ? other : own;
+      }
+      const int qs = mt == 0 ? QSV : QSQ;  // B: dO (for dV) or Q (for dK) rows of the step
+      const bf16* bsrc = mt == 0 ? sd : sq;
+      const int ntw = mt == 0 ? C::NTV : C::NTQ;
+      const int brow0 = (hh + 4 * (gi >> 2)) * qs + 16 * (g & 1) + 4 * (gi & 3);
+      constexpr int NB = 4 * C::NTM, PF = 2;
+      bf16x8 bw[NB];
       auto ld = [&](int i) {
-        const int s2 = i / C::NTD, nt = i % C::NTD;
-        const int o = brow + 16 * s2 * QS + 32 * nt;
-        bd[i] = concat(lds_read_tr4(sd + o), lds_read_tr4(sd + o + 2 * QS));
-        bq[i] = concat(lds_read_tr4(sq + o), lds_read_tr4(sq + o + 2 * QS));
+        const int ksi = i / C::NTM, nt = i % C::NTM;
+        if (nt < ntw) {
+          const int o = brow0 + 16 * ksi * qs + 32 * nt;
+          bw[i] = concat(lds_read_tr4(bsrc + o), lds_read_tr4(bsrc + o + 2 * qs));
+        }
       };
 #pragma unroll
       for (int i = 0; i < PF; ++i) ld(i);
@@ -733,9 +829,33 @@ void fa_bwd_dkdv(MainArgs a) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         if (i + PF < NB) ld(i + PF);
-        const int s2 = i / C::NTD, nt = i % C::NTD;
-        acc_v[nt] = mfma32x32x16(pk[s2], bd[i], acc_v[nt]);
-        acc_k[nt] = mfma32x32x16(dsk[s2], bq[i], acc_k[nt]);
+        const int ksi = i / C::NTM, nt = i % C::NTM;
+        if (nt < ntw) acc_w[nt] = mfma32x32x16(am[ksi], bw[i], acc_w[nt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      constexpr int NB = 2 * C::NTM, PF = 2;
+      bf16x8 bd[NB], bq[NB];
+      auto ld = [&](int i) {
+        const int s2 = i / C::NTM, nt = i % C::NTM;
+        if (nt < C::NTV) {
+          const int o = browd + 16 * s2 * QSV + 32 * nt;
+          bd[i] = concat(lds_read_tr4(sd + o), lds_read_tr4(sd + o + 2 * QSV));
+        }
+        if (nt < C::NTQ) {
+          const int o = browq + 16 * s2 * QSQ + 32 * nt;
+          bq[i] = concat(lds_read_tr4(sq + o), lds_read_tr4(sq + o + 2 * QSQ));
+        }
+      };
+#pragma unroll
+      for (int i = 0; i < PF; ++i) ld(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (i + PF < NB) ld(i + PF);
+        const int s2 = i / C::NTM, nt = i % C::NTM;
+        if (nt < C::NTV) acc_v[nt] = mfma32x32x16(pk[s2], bd[i], acc_v[nt]);
+        if (nt < C::NTQ) acc_k[nt] = mfma32x32x16(dsk[s2], bq[i], acc_k[nt]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -746,35 +866,63 @@ void fa_bwd_dkdv(MainArgs a) {
     __syncthreads();
   }
 
-  // combine the two M-tiles' partial sums: the M-tile 0 wave keeps dV and takes the partner's dV,
-  // the M-tile 1 wave keeps dK and takes the partner's dK; each writes the half its partner needs
-  {
-    f32x16* part = (f32x16*)(smem) + (size_t)w * C::NTD * 64 + lane;  // [wave][nt][lane]
+  // write-back of rows 32 grp .. 32 grp + 31, features below the head dim, in bf16
+  auto store_dv = [&](const f32x16* acc) {
 #pragma unroll
-    for (int nt = 0; nt < C::NTD; ++nt) part[nt * 64] = mt == 0 ? acc_k[nt] : acc_v[nt];
-  }
-  __syncthreads();
-  {
-    const f32x16* other = (const f32x16*)(smem) + (size_t)(w ^ 4) * C::NTD * 64 + lane;
+    for (int nt = 0; nt < C::NTV; ++nt) {
+      if (32 * nt + c >= dvd) continue;
 #pragma unroll
-    for (int nt = 0; nt < C::NTD; ++nt) {
-      if (mt == 0) acc_v[nt] += other[nt * 64];
-      else acc_k[nt] += other[nt * 64];
-    }
-  }
-  // write-back: M-tile 0 wave dV, M-tile 1 wave dK = scale * acc, bf16, rows 32 grp .. 32 grp + 31
-  bf16* out = mt == 0 ? a.dv : a.dk;
-  const float osc = mt == 0 ? 1.f : a.scale;
+      for (int a4 = 0; a4 < 4; ++a4) {
 #pragma unroll
-  for (int nt = 0; nt < C::NTD; ++nt) {
-    const f32x16 res = mt == 0 ? acc_v[nt] : acc_k[nt];
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int r = kv0 + 32 * grp + 8 * a4 + 4 * hh + bb;
-        if (r < Lk) out[(kv_start + r) * rsk + (int64_t)hk * D + 32 * nt + c] = to_bf16(res[4 * a4 + bb] * osc);
+        for (int bb = 0; bb < 4; ++bb) {
+          const int r = kv0 + 32 * grp + 8 * a4 + 4 * hh + bb;
+          if (r < Lk) a.dv[(kv_start + r) * rskv + (int64_t)hk * dvd + 32 * nt + c] = to_bf16(acc[nt][4 * a4 + bb]);
+        }
       }
+    }
+  };
+  auto store_dk = [&](const f32x16* acc) {  // dK = scale * acc
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt) {
+      if (32 * nt + c >= dqk) continue;
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int r = kv0 + 32 * grp + 8 * a4 + 4 * hh + bb;
+          if (r < Lk)
+            a.dk[(kv_start + r) * rskq + (int64_t)hk * dqk + 32 * nt + c] = to_bf16(acc[nt][4 * a4 + bb] * a.scale);
+        }
+      }
+    }
+  };
+  if constexpr (C::WIDE) {
+    if (mt == 0)
+      store_dv(acc_w);
+    else
+      store_dk(acc_w);
+  } else {
+    // combine the two M-tiles' partial sums through LDS, laid out as [NG][NTQ] partial dK tiles, then
+    // [NG][NTV] partial dV tiles, 64 lanes each: the M-tile 0 wave keeps dV and takes the partner's
+    // dV, the M-tile 1 wave keeps dK and takes the partner's dK; each writes the half its partner needs
+    f32x16* part_k = (f32x16*)(smem) + (size_t)grp * C::NTQ * 64 + lane;
+    f32x16* part_v = (f32x16*)(smem) + (size_t)(NG * C::NTQ + grp * C::NTV) * 64 + lane;
+    if (mt == 0) {
+#pragma unroll
+      for (int nt = 0; nt < C::NTQ; ++nt) part_k[nt * 64] = acc_k[nt];
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < C::NTV; ++nt) part_v[nt * 64] = acc_v[nt];
+    }
+    __syncthreads();
+    if (mt == 0) {
+#pragma unroll
+      for (int nt = 0; nt < C::NTV; ++nt) acc_v[nt] += part_v[nt * 64];
+      store_dv(acc_v);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < C::NTQ; ++nt) acc_k[nt] += part_k[nt * 64];
+      store_dk(acc_k);
     }
   }
 #endif
@@ -782,34 +930,80 @@ void fa_bwd_dkdv(MainArgs a) {
 
 // ------------------------------------------------------------------ stage 2b: dQ by recompute
 
-
-template <int D>
+// Tiling of the dQ kernel and of the forward for padded head dims DQ (Q, K) and DV (V, dO):
+// four waves of 32 q rows, kv steps of 64 keys whose K and V tiles stream through LDS. Heads up
+// to 128 run two waves per SIMD; wider heads one (the larger register budget holds Q, dO and the
+// accumulators).
+template <int DQ, int DV>
 struct DqCfg {
+  static constexpr bool WIDE = DQ > 128 || DV > 128;
+  static constexpr int WPE = WIDE ? 1 : 2;       // waves per SIMD
   static constexpr int BQ = 128;                 // q rows per workgroup (32 per wave)
   static constexpr int BK = 64;                  // kv rows per step
   static constexpr int NW = 4;
-  static constexpr int KSD = D / 16;
-  static constexpr int NTD = D / 32;
-  static constexpr int QS = D + 8;               // padded row stride of the K and V tiles
-  static constexpr int CPR = QS / 8;
-  static constexpr int TILE = BK * QS;
-  static constexpr int TILE_BYTES = TILE * 2;
-  static constexpr int NDMA = TILE_BYTES / 1024;
-  static constexpr int OFF_K = 0;                          // K [2][BK][QS]
-  static constexpr int OFF_V = OFF_K + 2 * TILE_BYTES;     // V [2][BK][QS]
-  static constexpr int LDS_BYTES = OFF_V + 2 * TILE_BYTES;
-  static_assert(TILE_BYTES % 1024 == 0, "a tile is a whole number of 1 KB transfers");
+  static constexpr int KSQ = DQ / 16, KSV = DV / 16, KSM = KSQ > KSV ? KSQ : KSV;  // MFMA k-steps
+  static constexpr int NTQ = DQ / 32, NTV = DV / 32;                                // 32-wide tiles
+  static constexpr int QSQ = DQ + 8, QSV = DV + 8;  // padded row strides of the K and V tiles
+  static constexpr int CPRQ = QSQ / 8, CPRV = QSV / 8;
+  static constexpr int TK_BYTES = BK * QSQ * 2, TV_BYTES = BK * QSV * 2;
+  static constexpr int NDMA_K = TK_BYTES / 1024, NDMA_V = TV_BYTES / 1024;
+  static constexpr int OFF_K = 0;                          // K [2][BK][QSQ]
+  static constexpr int OFF_V = OFF_K + 2 * TK_BYTES;       // V [2][BK][QSV]
+  static constexpr int LDS_BYTES = OFF_V + 2 * TV_BYTES;
+  static_assert(DQ % 32 == 0 && DV % 32 == 0 && DQ <= 256 && DV <= 256, "padded head dims");
+  static_assert(TK_BYTES % 1024 == 0 && TV_BYTES % 1024 == 0, "a tile is a whole number of 1 KB transfers");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// The K and V tiles of kv step t into buffer bi (each wave issues transfers w, w + NW, ...).
+template <class C>
+struct KvTileLoader {
+  static constexpr int NJK = (C::NDMA_K + C::NW - 1) / C::NW, NJV = (C::NDMA_V + C::NW - 1) / C::NW;
+  int offk[NJK], offv[NJV];
+  __device__ __forceinline__ KvTileLoader(int w, int lane, int rskqb, int rskvb, int dqk, int dvd) {
+#pragma unroll
+    for (int jj = 0; jj < NJK; ++jj) offk[jj] = tile_dma_off(w + C::NW * jj, lane, C::CPRQ, rskqb, dqk);
+#pragma unroll
+    for (int jj = 0; jj < NJV; ++jj) offv[jj] = tile_dma_off(w + C::NW * jj, lane, C::CPRV, rskvb, dvd);
+  }
+  __device__ __forceinline__ void issue(char* smem, int w, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                        int bi) const {
+    auto dma_k = [&](int jj, int j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)(smem + C::OFF_K + bi * C::TK_BYTES + 1024 * j), 16,
+          offk[jj], 0, 0, 0);
+    };
+    auto dma_v = [&](int jj, int j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)(smem + C::OFF_V + bi * C::TV_BYTES + 1024 * j), 16,
+          offv[jj], 0, 0, 0);
+    };
+#pragma unroll
+    for (int jj = 0; jj < (NJK > NJV ? NJK : NJV); ++jj) {
+      const int j = w + C::NW * jj;
+      if constexpr (C::NDMA_K == C::NDMA_V) {  // one test for both tiles
+        if (j < C::NDMA_K) {
+          dma_k(jj, j);
+          dma_v(jj, j);
+        }
+      } else {
+        if (jj < NJK && j < C::NDMA_K) dma_k(jj, j);
+        if (jj < NJV && j < C::NDMA_V) dma_v(jj, j);
+      }
+    }
+  }
 };
 
 // dQ of one (q tile, head, sequence): loops over the kv tiles, recomputes S^T = K Q^T and
 // dP^T = V dO^T with the forward's statistics (steps 1-5 of the per-tile math), and
 // accumulates dQ^T = K^T dS^T (step 8) in registers; dQ is written once, in bf16.
-template <int D, bool CAUSAL, bool WINDOW>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+template <int DQ, int DV, bool CAUSAL, bool WINDOW, bool EXACT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(DqCfg<DQ, DV>::WPE, DqCfg<DQ, DV>::WPE)))
 void fa_bwd_dq(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = DqCfg<D>;
-  constexpr int BQ = C::BQ, BK = C::BK, QS = C::QS;
+  using C = DqCfg<DQ, DV>;
+  constexpr int BQ = C::BQ, BK = C::BK, QSQ = C::QSQ, QSV = C::QSV;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int HB = a.H * a.batch;
@@ -831,27 +1025,33 @@ void fa_bwd_dq(MainArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
-  const int64_t rs = (int64_t)a.H * D;    // row stride of the query-side tensors
-  const int rsb = (int)(rs * 2);
-  const int64_t rsk = (int64_t)a.Hk * D;  // row stride of K, V
-  const int rskb = (int)(rsk * 2);
-  const int hk = h / (a.H / a.Hk);        // the K/V head this query head reads
-  const bf16* kb = a.k + kv_start * rsk + (int64_t)hk * D;
-  const bf16* vb = a.v + kv_start * rsk + (int64_t)hk * D;
-  const bf16* qb = a.q + (q_start + i0) * rs + (int64_t)h * D;
-  const bf16* db = a.dout + (q_start + i0) * rs + (int64_t)h * D;
+  const int dqk = EXACT ? DQ : a.d_qk, dvd = EXACT ? DV : a.d_v;  // EXACT: the padded dims
+  const int64_t rsq = (int64_t)a.H * dqk, rsd = (int64_t)a.H * dvd;     // row strides of Q (dQ) and dO
+  const int rsqb = (int)(rsq * 2), rsdb = (int)(rsd * 2);
+  const int64_t rskq = (int64_t)a.Hk * dqk, rskv = (int64_t)a.Hk * dvd;  // of K and V
+  const int rskqb = (int)(rskq * 2), rskvb = (int)(rskv * 2);
+  const int hk = h / (a.H / a.Hk);  // the K/V head this query head reads
+  const bf16* kb = a.k + kv_start * rskq + (int64_t)hk * dqk;
+  const bf16* vb = a.v + kv_start * rskv + (int64_t)hk * dvd;
+  const bf16* qb = a.q + (q_start + i0) * rsq + (int64_t)h * dqk;
+  const bf16* db = a.dout + (q_start + i0) * rsd + (int64_t)h * dvd;
   const int qi = i0 + 32 * w + c;  // this lane's query row (sequence-local) in S^T, dP^T and dQ^T
 
   // Q, dO as B operands of S^T = K Q^T and dP^T = V dO^T: row qi, features 16 ks + 8 hh ..+7
+  // (zeros at or past the head dim)
   const int q_rows = imin(Lq - i0, BQ);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (int64_t)q_rows * rsb);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(db, (int64_t)q_rows * rsb);
-  bf16x8 qf[C::KSD], df[C::KSD];
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (int64_t)q_rows * rsqb);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(db, (int64_t)q_rows * rsdb);
+  bf16x8 qf[C::KSQ], df[C::KSV];
 #pragma unroll
-  for (int ks = 0; ks < C::KSD; ++ks) {
-    const int off = (32 * w + c) * rsb + (16 * ks + 8 * hh) * 2;
-    qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
-    df[ks] = __builtin_bit_cast(bf16x8, buf_load16(rd, off));
+  for (int ks = 0; ks < C::KSQ; ++ks) {
+    const int col = 16 * ks + 8 * hh;
+    qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, col < dqk ? (32 * w + c) * rsqb + col * 2 : kOutOfRange));
+  }
+#pragma unroll
+  for (int ks = 0; ks < C::KSV; ++ks) {
+    const int col = 16 * ks + 8 * hh;
+    df[ks] = __builtin_bit_cast(bf16x8, buf_load16(rd, col < dvd ? (32 * w + c) * rsdb + col * 2 : kOutOfRange));
   }
   // rows past the sequence: lse2 = +inf makes P (and dS) exactly 0
   const float lse = qi < Lq ? a.lse2[(int64_t)h * a.total_q + q_start + qi] : __builtin_inff();
@@ -868,48 +1068,29 @@ void fa_bwd_dq(MainArgs a) {
   }
   __syncthreads();
 
-  constexpr int NJ = (C::NDMA + C::NW - 1) / C::NW;
-  int dma_off[NJ];
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) {
-    const int p16 = 64 * (w + C::NW * jj) + lane;
-    const int r = p16 / C::CPR, ch = p16 % C::CPR;
-    dma_off[jj] = r * rskb + (ch < D / 8 ? ch : 0) * 16;
-  }
+  const KvTileLoader<C> loader(w, lane, rskqb, rskvb, dqk, dvd);
   auto issue_kv = [&](int t, int bi) {
-    const int j0 = t * BK;
-    const int64_t bytes = (int64_t)imin(Lk - j0, BK) * rskb;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (int64_t)j0 * rsk, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (int64_t)j0 * rsk, bytes);
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int j = w + C::NW * jj;
-      if (j < C::NDMA) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void*)(smem + C::OFF_K + bi * C::TILE_BYTES + 1024 * j), 16,
-            dma_off[jj], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)(smem + C::OFF_V + bi * C::TILE_BYTES + 1024 * j), 16,
-            dma_off[jj], 0, 0, 0);
-      }
-    }
+    const int j0 = t * BK, rows = imin(Lk - j0, BK);
+    loader.issue(smem, w, make_rsrc(kb + (int64_t)j0 * rskq, (int64_t)rows * rskqb),
+                 make_rsrc(vb + (int64_t)j0 * rskv, (int64_t)rows * rskvb), bi);
   };
 
-  f32x16 acc[C::NTD];
+  f32x16 acc[C::NTQ];
 #pragma unroll
-  for (int nt = 0; nt < C::NTD; ++nt) acc[nt] = f32x16{};
+  for (int nt = 0; nt < C::NTQ; ++nt) acc[nt] = f32x16{};
 
   int buf = 0;
   if (n_kt > t0) issue_kv(t0, 0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
 
-  const int arow = tile_row(c) * QS + 8 * hh;
-  const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
+  const int arowk = tile_row(c) * QSQ + 8 * hh;
+  const int arowv = tile_row(c) * QSV + 8 * hh;
+  const int browk = (hh + 4 * (gi >> 2)) * QSQ + 16 * (g & 1) + 4 * (gi & 3);
   for (int t = t0; t < n_kt; ++t, buf ^= 1) {
     if (t + 1 < n_kt) issue_kv(t + 1, buf ^ 1);
-    const bf16* sk = (const bf16*)(smem + C::OFF_K + buf * C::TILE_BYTES);
-    const bf16* sv = (const bf16*)(smem + C::OFF_V + buf * C::TILE_BYTES);
+    const bf16* sk = (const bf16*)(smem + C::OFF_K + buf * C::TK_BYTES);
+    const bf16* sv = (const bf16*)(smem + C::OFF_V + buf * C::TV_BYTES);
     // steps 1 and 3, transposed: S^T = K Q^T, dP^T = V dO^T  ([kv 64] x [q 32] per wave)
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -919,23 +1100,23 @@ void fa_bwd_dq(MainArgs a) {
     }
     {  // operands read PF k-steps ahead into distinct registers, one scheduling fence per k-step
       constexpr int PF = 2;
-      bf16x8 ka[C::KSD][2], va[C::KSD][2];
+      bf16x8 ka[C::KSQ][2], va[C::KSV][2];
       auto ld = [&](int ks) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          ka[ks][mt] = *(const bf16x8*)(sk + arow + 32 * mt * QS + 16 * ks);
-          va[ks][mt] = *(const bf16x8*)(sv + arow + 32 * mt * QS + 16 * ks);
+          if (ks < C::KSQ) ka[ks][mt] = *(const bf16x8*)(sk + arowk + 32 * mt * QSQ + 16 * ks);
+          if (ks < C::KSV) va[ks][mt] = *(const bf16x8*)(sv + arowv + 32 * mt * QSV + 16 * ks);
         }
       };
 #pragma unroll
       for (int ks = 0; ks < PF; ++ks) ld(ks);
 #pragma unroll
-      for (int ks = 0; ks < C::KSD; ++ks) {
-        if (ks + PF < C::KSD) ld(ks + PF);
+      for (int ks = 0; ks < C::KSM; ++ks) {
+        if (ks + PF < C::KSM) ld(ks + PF);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          s[mt] = mfma32x32x16(ka[ks][mt], qf[ks], s[mt]);
-          dp[mt] = mfma32x32x16(va[ks][mt], df[ks], dp[mt]);
+          if (ks < C::KSQ) s[mt] = mfma32x32x16(ka[ks][mt], qf[ks], s[mt]);
+          if (ks < C::KSV) dp[mt] = mfma32x32x16(va[ks][mt], df[ks], dp[mt]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -972,15 +1153,15 @@ void fa_bwd_dq(MainArgs a) {
       softmax(std::true_type{});
     // step 8, transposed: dQ^T += K^T dS^T. k-step ksi = 2 mt + s2: its k-index e is kv MFMA row
     // 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4 of M-tile mt; the transpose reads fetch
-    // those K rows. k-steps run outside the NTD independent accumulators; A operands are read PF
+    // those K rows. k-steps run outside the NTQ independent accumulators; A operands are read PF
     // MFMAs ahead.
     {
-      constexpr int NB = 4 * C::NTD, PF = 3;
+      constexpr int NB = 4 * C::NTQ, PF = 3;
       bf16x8 kt[NB];
       auto kt_load = [&](int i) {
-        const int ksi = i / C::NTD, nt = i % C::NTD;
-        const int o = brow + 16 * ksi * QS + 32 * nt;
-        return concat(lds_read_tr4(sk + o), lds_read_tr4(sk + o + 2 * QS));
+        const int ksi = i / C::NTQ, nt = i % C::NTQ;
+        const int o = browk + 16 * ksi * QSQ + 32 * nt;
+        return concat(lds_read_tr4(sk + o), lds_read_tr4(sk + o + 2 * QSQ));
       };
 #pragma unroll
       for (int i = 0; i < PF; ++i) kt[i] = kt_load(i);
@@ -988,7 +1169,7 @@ void fa_bwd_dq(MainArgs a) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         if (i + PF < NB) kt[i + PF] = kt_load(i + PF);
-        const int ksi = i / C::NTD, nt = i % C::NTD;
+        const int ksi = i / C::NTQ, nt = i % C::NTQ;
         acc[nt] = mfma32x32x16(kt[i], dsk[ksi >> 1][ksi & 1], acc[nt]);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1001,11 +1182,12 @@ void fa_bwd_dq(MainArgs a) {
 
   // dQ = scale * (dQ^T)^T in bf16: this lane holds features 32 nt + 8 a4 + 4 hh + bb of row qi
   if (qi < Lq) {
-    bf16* dst = a.dq + (q_start + qi) * rs + (int64_t)h * D + 4 * hh;
+    bf16* dst = a.dq + (q_start + qi) * rsq + (int64_t)h * dqk + 4 * hh;
 #pragma unroll
-    for (int nt = 0; nt < C::NTD; ++nt) {
+    for (int nt = 0; nt < C::NTQ; ++nt) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
+        if (32 * nt + 8 * a4 + 4 * hh >= dqk) continue;  // head dims are multiples of 8
         const bf16x4 v4 = {to_bf16(acc[nt][4 * a4] * a.scale), to_bf16(acc[nt][4 * a4 + 1] * a.scale),
                            to_bf16(acc[nt][4 * a4 + 2] * a.scale), to_bf16(acc[nt][4 * a4 + 3] * a.scale)};
         *(bf16x4*)(dst + 32 * nt + 8 * a4) = v4;
@@ -1023,26 +1205,26 @@ struct FwdArgs {
   const bf16* v;
   const int* cu_q;
   const int* cu_kv;
-  bf16* o;   // [total_q][H][D]
+  bf16* o;   // [total_q][H][d_v]
   float* m;  // [total_q][H]: row max of the scaled visible logits
   float* l;  // [total_q][H]: row sum of exp(scaled logit - m) over visible keys
   int64_t total_q, total_kv;
   int H, Hk, batch, max_seqlen_q, max_seqlen_kv, padded;  // query heads, K/V heads (H % Hk == 0)
   int window;        // > 0: each query sees only its left local window of keys (i - window, i]
+  int d_qk, d_v;     // head dims of Q, K and of V, O
   float scale_log2;  // scale * log2(e)
 };
 
 // Rows outside every sequence: O = 0, m = 0, l = 1 (finite values a backward never reads).
-template <int D>
+// One thread per 8 features of an O row, 256 / TPR rows per block; TPR is a power of two >= d_v / 8.
+template <int TPR>
 __global__ __launch_bounds__(256) void fa_fwd_fill(FwdArgs a) {
-  constexpr int TPR = D / 8;
-  constexpr int RPB = 256 / TPR;
-  const int sub = threadIdx.x % TPR;
-  const int64_t pair = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;  // = t * H + h
+  const int sub = threadIdx.x & (TPR - 1);
+  const int64_t pair = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;  // = t * H + h
   const int64_t t = pair / a.H;
   if (t >= a.total_q || row_in_sequence(t, a.cu_q, a.batch, a.padded, a.max_seqlen_q)) return;
   const u32x4 z = {0u, 0u, 0u, 0u};
-  *(u32x4*)(a.o + pair * D + sub * 8) = z;
+  if (sub < a.d_v / 8) *(u32x4*)(a.o + pair * a.d_v + sub * 8) = z;
   if (sub == 0) {
     a.m[pair] = 0.f;
     a.l[pair] = 1.f;
@@ -1055,12 +1237,13 @@ __global__ __launch_bounds__(256) void fa_fwd_fill(FwdArgs a) {
 // once per row. Same tiling as the dQ kernel: Q in registers, K and V tiles of 64 keys streamed
 // through LDS, each lane owns one query row (its MFMA column), so the running maximum, the row sum
 // and the rescaling of its O row are per-lane values combined with the partner lane (lane ^ 32).
-template <int D, bool CAUSAL, bool WINDOW>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+template <int DQ, int DV, bool CAUSAL, bool WINDOW, bool EXACT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(DqCfg<DQ, DV>::WPE, DqCfg<DQ, DV>::WPE)))
 void fa_fwd(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = DqCfg<D>;
-  constexpr int BQ = C::BQ, BK = C::BK, QS = C::QS;
+  using C = DqCfg<DQ, DV>;
+  constexpr int BQ = C::BQ, BK = C::BK, QSQ = C::QSQ, QSV = C::QSV;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int HB = a.H * a.batch;
@@ -1081,22 +1264,25 @@ void fa_fwd(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
-  const int64_t rs = (int64_t)a.H * D;    // row stride of the query-side tensors
-  const int rsb = (int)(rs * 2);
-  const int64_t rsk = (int64_t)a.Hk * D;  // row stride of K, V
-  const int rskb = (int)(rsk * 2);
-  const int hk = h / (a.H / a.Hk);        // the K/V head this query head reads
-  const bf16* kb = a.k + kv_start * rsk + (int64_t)hk * D;
-  const bf16* vb = a.v + kv_start * rsk + (int64_t)hk * D;
-  const bf16* qb = a.q + (q_start + i0) * rs + (int64_t)h * D;
+  const int dqk = EXACT ? DQ : a.d_qk, dvd = EXACT ? DV : a.d_v;  // EXACT: the padded dims
+  const int64_t rsq = (int64_t)a.H * dqk, rso = (int64_t)a.H * dvd;     // row strides of Q and O
+  const int rsqb = (int)(rsq * 2);
+  const int64_t rskq = (int64_t)a.Hk * dqk, rskv = (int64_t)a.Hk * dvd;  // of K and V
+  const int rskqb = (int)(rskq * 2), rskvb = (int)(rskv * 2);
+  const int hk = h / (a.H / a.Hk);  // the K/V head this query head reads
+  const bf16* kb = a.k + kv_start * rskq + (int64_t)hk * dqk;
+  const bf16* vb = a.v + kv_start * rskv + (int64_t)hk * dvd;
+  const bf16* qb = a.q + (q_start + i0) * rsq + (int64_t)h * dqk;
   const int qi = i0 + 32 * w + c;  // this lane's query row (sequence-local)
 
   const int q_rows = imin(Lq - i0, BQ);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (int64_t)q_rows * rsb);
-  bf16x8 qf[C::KSD];
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qb, (int64_t)q_rows * rsqb);
+  bf16x8 qf[C::KSQ];
 #pragma unroll
-  for (int ks = 0; ks < C::KSD; ++ks)
-    qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, (32 * w + c) * rsb + (16 * ks + 8 * hh) * 2));
+  for (int ks = 0; ks < C::KSQ; ++ks) {
+    const int col = 16 * ks + 8 * hh;
+    qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, col < dqk ? (32 * w + c) * rsqb + col * 2 : kOutOfRange));
+  }
 
   int n_kt = (Lk + BK - 1) / BK;
   if (CAUSAL) n_kt = imin(n_kt, (i0 + BQ - 1) / BK + 1);
@@ -1109,36 +1295,16 @@ void fa_fwd(FwdArgs a) {
   }
   __syncthreads();
 
-  constexpr int NJ = (C::NDMA + C::NW - 1) / C::NW;
-  int dma_off[NJ];
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) {
-    const int p16 = 64 * (w + C::NW * jj) + lane;
-    const int r = p16 / C::CPR, ch = p16 % C::CPR;
-    dma_off[jj] = r * rskb + (ch < D / 8 ? ch : 0) * 16;
-  }
+  const KvTileLoader<C> loader(w, lane, rskqb, rskvb, dqk, dvd);
   auto issue_kv = [&](int t, int bi) {
-    const int j0 = t * BK;
-    const int64_t bytes = (int64_t)imin(Lk - j0, BK) * rskb;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (int64_t)j0 * rsk, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb + (int64_t)j0 * rsk, bytes);
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      const int j = w + C::NW * jj;
-      if (j < C::NDMA) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rk, (__attribute__((address_space(3))) void*)(smem + C::OFF_K + bi * C::TILE_BYTES + 1024 * j), 16,
-            dma_off[jj], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)(smem + C::OFF_V + bi * C::TILE_BYTES + 1024 * j), 16,
-            dma_off[jj], 0, 0, 0);
-      }
-    }
+    const int j0 = t * BK, rows = imin(Lk - j0, BK);
+    loader.issue(smem, w, make_rsrc(kb + (int64_t)j0 * rskq, (int64_t)rows * rskqb),
+                 make_rsrc(vb + (int64_t)j0 * rskv, (int64_t)rows * rskvb), bi);
   };
 
-  f32x16 acc[C::NTD];  // O^T of this lane's row: features 32 nt + 8 a4 + 4 hh + bb
+  f32x16 acc[C::NTV];  // O^T of this lane's row: features 32 nt + 8 a4 + 4 hh + bb
 #pragma unroll
-  for (int nt = 0; nt < C::NTD; ++nt) acc[nt] = f32x16{};
+  for (int nt = 0; nt < C::NTV; ++nt) acc[nt] = f32x16{};
   float mrun = -__builtin_inff();  // running max of S*scale*log2(e) over the keys seen
   float lrun = 0.f;                // this lane's part of sum exp2(S*scale*log2(e) - mrun)
 
@@ -1147,26 +1313,26 @@ void fa_fwd(FwdArgs a) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
 
-  const int arow = tile_row(c) * QS + 8 * hh;
-  const int brow = (hh + 4 * (gi >> 2)) * QS + 16 * (g & 1) + 4 * (gi & 3);
+  const int arowk = tile_row(c) * QSQ + 8 * hh;
+  const int browv = (hh + 4 * (gi >> 2)) * QSV + 16 * (g & 1) + 4 * (gi & 3);
   for (int t = t0; t < n_kt; ++t, buf ^= 1) {
     if (t + 1 < n_kt) issue_kv(t + 1, buf ^ 1);
-    const bf16* sk = (const bf16*)(smem + C::OFF_K + buf * C::TILE_BYTES);
-    const bf16* sv = (const bf16*)(smem + C::OFF_V + buf * C::TILE_BYTES);
+    const bf16* sk = (const bf16*)(smem + C::OFF_K + buf * C::TK_BYTES);
+    const bf16* sv = (const bf16*)(smem + C::OFF_V + buf * C::TV_BYTES);
     // S^T = K Q^T ([kv 64] x [q 32] per wave), operands read PF k-steps ahead
     f32x16 s[2] = {f32x16{}, f32x16{}};
     {
       constexpr int PF = 2;
-      bf16x8 ka[C::KSD][2];
+      bf16x8 ka[C::KSQ][2];
       auto ld = [&](int ks) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) ka[ks][mt] = *(const bf16x8*)(sk + arow + 32 * mt * QS + 16 * ks);
+        for (int mt = 0; mt < 2; ++mt) ka[ks][mt] = *(const bf16x8*)(sk + arowk + 32 * mt * QSQ + 16 * ks);
       };
 #pragma unroll
       for (int ks = 0; ks < PF; ++ks) ld(ks);
 #pragma unroll
-      for (int ks = 0; ks < C::KSD; ++ks) {
-        if (ks + PF < C::KSD) ld(ks + PF);
+      for (int ks = 0; ks < C::KSQ; ++ks) {
+        if (ks + PF < C::KSQ) ld(ks + PF);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) s[mt] = mfma32x32x16(ka[ks][mt], qf[ks], s[mt]);
         __builtin_amdgcn_sched_barrier(0);
@@ -1217,16 +1383,16 @@ void fa_fwd(FwdArgs a) {
     }
     lrun = lrun * alpha + psum;
 #pragma unroll
-    for (int nt = 0; nt < C::NTD; ++nt) acc[nt] *= alpha;
+    for (int nt = 0; nt < C::NTV; ++nt) acc[nt] *= alpha;
     // O^T += V^T P^T: k-step ksi = 2 mt + s2, k-index e is key MFMA row 16 s2 + 4 hh + e (e < 4) or
     // 16 s2 + 8 + 4 hh + e - 4 of M-tile mt; the transpose reads fetch those V rows
     {
-      constexpr int NB = 4 * C::NTD, PF = 3;
+      constexpr int NB = 4 * C::NTV, PF = 3;
       bf16x8 vt[NB];
       auto vt_load = [&](int i) {
-        const int ksi = i / C::NTD, nt = i % C::NTD;
-        const int o = brow + 16 * ksi * QS + 32 * nt;
-        return concat(lds_read_tr4(sv + o), lds_read_tr4(sv + o + 2 * QS));
+        const int ksi = i / C::NTV, nt = i % C::NTV;
+        const int o = browv + 16 * ksi * QSV + 32 * nt;
+        return concat(lds_read_tr4(sv + o), lds_read_tr4(sv + o + 2 * QSV));
       };
 #pragma unroll
       for (int i = 0; i < PF; ++i) vt[i] = vt_load(i);
@@ -1234,7 +1400,7 @@ void fa_fwd(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         if (i + PF < NB) vt[i + PF] = vt_load(i + PF);
-        const int ksi = i / C::NTD, nt = i % C::NTD;
+        const int ksi = i / C::NTV, nt = i % C::NTV;
         acc[nt] = mfma32x32x16(vt[i], pk[ksi >> 1][ksi & 1], acc[nt]);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1249,11 +1415,12 @@ void fa_fwd(FwdArgs a) {
   if (qi < Lq) {
     const bool any = mrun != -__builtin_inff();  // a valid row without keys: O = 0, m = 0, l = 1
     const float inv = any ? 1.f / lsum : 0.f;
-    bf16* dst = a.o + (q_start + qi) * rs + (int64_t)h * D + 4 * hh;
+    bf16* dst = a.o + (q_start + qi) * rso + (int64_t)h * dvd + 4 * hh;
 #pragma unroll
-    for (int nt = 0; nt < C::NTD; ++nt) {
+    for (int nt = 0; nt < C::NTV; ++nt) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
+        if (32 * nt + 8 * a4 + 4 * hh >= dvd) continue;  // head dims are multiples of 8
         const bf16x4 v4 = {to_bf16(acc[nt][4 * a4] * inv), to_bf16(acc[nt][4 * a4 + 1] * inv),
                            to_bf16(acc[nt][4 * a4 + 2] * inv), to_bf16(acc[nt][4 * a4 + 3] * inv)};
         *(bf16x4*)(dst + 32 * nt + 8 * a4) = v4;

@@ -1,0 +1,69 @@
+// fa_bwd_launch.hpp -- launches of the recompute-form kernels (dK/dV, dQ) and of the forward for one
+// pair of padded head dims (DQ for Q and K, DV for V, O and dO). The pairs with a dim above 128 are
+// instantiated only in fa_bwd_wide.hip, which is compiled with MFMA accumulators allowed in the
+// AGPRs: their accumulators need more registers than the 256 VGPRs of one wave.
+#pragma once
+#include "fa_bwd_kernels.hpp"
+
+namespace fa {
+
+// EXACT: the head dims equal the padded ones, so the kernels take them as constants.
+template <int DQ, int DV, bool EXACT>
+struct Recompute {
+  // workgroups of the dK/dV kernel: (kv tile, K/V head, sequence), kv tiles outermost
+  static int64_t dkdv_blocks(const MainArgs& a) {
+    return (int64_t)((a.max_seqlen_kv + DkdvCfg<DQ, DV>::BN - 1) / DkdvCfg<DQ, DV>::BN) * a.Hk * a.batch;
+  }
+  // workgroups of the dQ kernel and of the forward: (q tile, head, sequence), q tiles outermost
+  static int64_t q_blocks(int max_seqlen_q, int H, int batch) {
+    return (int64_t)((max_seqlen_q + DqCfg<DQ, DV>::BQ - 1) / DqCfg<DQ, DV>::BQ) * H * batch;
+  }
+
+  static void dkdv(const MainArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)dkdv_blocks(a)), block(DkdvCfg<DQ, DV>::NT);
+    if (a.window > 0)  // the window implies the causal bound
+      fa_bwd_dkdv<DQ, DV, true, true, EXACT><<<grid, block, 0, s>>>(a);
+    else if (a.causal)
+      fa_bwd_dkdv<DQ, DV, true, false, EXACT><<<grid, block, 0, s>>>(a);
+    else
+      fa_bwd_dkdv<DQ, DV, false, false, EXACT><<<grid, block, 0, s>>>(a);
+  }
+
+  static void dq(const MainArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)q_blocks(a.max_seqlen_q, a.H, a.batch)), block(256);
+    if (a.window > 0)
+      fa_bwd_dq<DQ, DV, true, true, EXACT><<<grid, block, 0, s>>>(a);
+    else if (a.causal)
+      fa_bwd_dq<DQ, DV, true, false, EXACT><<<grid, block, 0, s>>>(a);
+    else
+      fa_bwd_dq<DQ, DV, false, false, EXACT><<<grid, block, 0, s>>>(a);
+  }
+
+  static void fwd(const FwdArgs& a, bool causal, hipStream_t s) {
+    const dim3 grid((unsigned)q_blocks(a.max_seqlen_q, a.H, a.batch)), block(256);
+    if (a.window > 0)
+      fa_fwd<DQ, DV, true, true, EXACT><<<grid, block, 0, s>>>(a);
+    else if (causal)
+      fa_fwd<DQ, DV, true, false, EXACT><<<grid, block, 0, s>>>(a);
+    else
+      fa_fwd<DQ, DV, false, false, EXACT><<<grid, block, 0, s>>>(a);
+  }
+};
+
+// The launches of one pair of padded head dims.
+struct KernelSet {
+  void (*dkdv)(const MainArgs&, hipStream_t);
+  void (*dq)(const MainArgs&, hipStream_t);
+  void (*fwd)(const FwdArgs&, bool, hipStream_t);
+};
+
+template <int DQ, int DV, bool EXACT>
+KernelSet kernel_set() {
+  return {Recompute<DQ, DV, EXACT>::dkdv, Recompute<DQ, DV, EXACT>::dq, Recompute<DQ, DV, EXACT>::fwd};
+}
+
+// The pairs (128, 256), (256, 128) and (256, 256), from fa_bwd_wide.hip; pq, pv are padded dims,
+// exact that the head dims equal them (pq = pv = 256).
+KernelSet wide_kernel_set(int pq, int pv, bool exact);
+
+}  // namespace fa

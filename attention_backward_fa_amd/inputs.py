@@ -7,7 +7,8 @@ forward's outputs and come from whatever forward the caller uses.
 
 Recipe (one CPU ``torch.Generator`` per case, seeded with the case's seed):
   1. varlen lengths first, when the case draws them (``torch.randint``);
-  2. then Q, K, V, dO in that order as fp32 standard normals of shape [T, H, d];
+  2. then Q, K, V, dO in that order as fp32 standard normals of shape [T, H, d]
+     (V and dO with the value head dim d_v when it differs);
   3. Q and K are multiplied by ``qk_mult`` (2 sharpens the softmax: logit std
      about 4 at d = 128 with scale 1/sqrt(d));
   4. all four are cast to bf16 (round to nearest even).
@@ -50,6 +51,7 @@ class Case:
     draw_lengths: tuple | None = None   # (count, lo, hi_inclusive): draw lengths from the generator
     heads_kv: int = 0          # K/V heads (0 = heads); query head h reads K/V head h // (heads / heads_kv)
     window: int = 0            # > 0: each query i sees only keys (i - window, i]
+    head_dim_v: int = 0        # head dim of V and dO (0 = head_dim)
 
     @property
     def scale(self) -> float:
@@ -77,10 +79,11 @@ WORKLOADS = ["tiny", "dense", "varlen", "causal", "longpad"]
 
 
 def custom_case(name: str, heads: int, head_dim: int, mask: int, seed: int, seqlens_q, seqlens_kv=None,
-                padded_len: int = 0, qk_mult: float = 1.0, heads_kv: int = 0, window: int = 0) -> Case:
+                padded_len: int = 0, qk_mult: float = 1.0, heads_kv: int = 0, window: int = 0,
+                head_dim_v: int = 0) -> Case:
     return Case(name, heads=heads, head_dim=head_dim, mask=mask, seed=seed, seqlens_q=list(seqlens_q),
                 seqlens_kv=list(seqlens_q if seqlens_kv is None else seqlens_kv), padded_len=padded_len,
-                qk_mult=qk_mult, heads_kv=heads_kv, window=window)
+                qk_mult=qk_mult, heads_kv=heads_kv, window=window, head_dim_v=head_dim_v)
 
 
 def _cumsum(lengths) -> torch.Tensor:
@@ -93,7 +96,8 @@ def _cumsum(lengths) -> torch.Tensor:
 def make(case: Case | str) -> dict:
     """Draw one case. Returns CPU tensors and sizes:
 
-    q, do: bf16 [T_q, H, d]; k, v: bf16 [T_kv, H_kv, d]; cu_q, cu_kv: int32 [B+1]; and the ints/floats
+    q: bf16 [T_q, H, d]; do: bf16 [T_q, H, d_v]; k: bf16 [T_kv, H_kv, d]; v: bf16 [T_kv, H_kv, d_v];
+    cu_q, cu_kv: int32 [B+1]; and the ints/floats
     scale, mask, max_seqlen_q, max_seqlen_kv, batch.
     """
     if isinstance(case, str):
@@ -112,11 +116,12 @@ def make(case: Case | str) -> dict:
         tq, tkv = sum(lq), sum(lkv)
         msq, mskv = max(lq, default=0), max(lkv, default=0)
     h, d = case.heads, case.head_dim
+    dv = case.head_dim_v or d
     hkv = case.heads_kv or h
     q = torch.randn((tq, h, d), generator=g, dtype=torch.float32)
     k = torch.randn((tkv, hkv, d), generator=g, dtype=torch.float32)
-    v = torch.randn((tkv, hkv, d), generator=g, dtype=torch.float32)
-    do = torch.randn((tq, h, d), generator=g, dtype=torch.float32)
+    v = torch.randn((tkv, hkv, dv), generator=g, dtype=torch.float32)
+    do = torch.randn((tq, h, dv), generator=g, dtype=torch.float32)
     if case.qk_mult != 1.0:
         q.mul_(case.qk_mult)
         k.mul_(case.qk_mult)

@@ -126,8 +126,20 @@ def make_workload(name: str, device):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_bwd_traffic_causal_s8192_h32_d128.md")
 
 
+def _code_only(text: str, python: bool) -> str:
+    """Source text without comments and blank lines, so that edits of comments alone keep the hash."""
+    import re
+    if python:
+        text = re.sub(r'(?m)^\s*#.*$', "", text)
+        text = re.sub(r'(?s)""".*?"""', "", text)
+    else:
+        text = re.sub(r"(?s)/\*.*?\*/", "", text)
+        text = re.sub(r"(?m)//.*$", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources and the build script (sorted by name)."""
+    """sha256 over the code (comments dropped) of the HIP sources and the build script, sorted by name."""
     import hashlib
     csrc = os.path.join(ROOT, "attention_backward_fa_amd", "csrc")
     files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".hpp", ".h")))
@@ -135,8 +147,8 @@ def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            h.update(_code_only(fh.read(), f.endswith(".py")).encode())
     return h.hexdigest()
 
 

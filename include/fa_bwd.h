@@ -14,7 +14,8 @@
  * Layout (the article's [total, heads, head_dim] tensors, section 三, and the
  * BTNH layout with the batch and sequence axes flattened, jax cuDNN wrapper,
  * AttentionLayout): every bf16 tensor is a contiguous row-major
- * [T][H][head_dim] array (token-major, then head, then feature); m and l are
+ * [T][H][d] array (token-major, then head, then feature), with d = head_dim
+ * for Q, K, dQ, dK and d = head_dim_v for V, O, dO, dV; m and l are
  * contiguous fp32 [T_q][H]. All tensor pointers are DEVICE pointers, owned by
  * the caller, 16-byte aligned.
  *
@@ -72,8 +73,9 @@ typedef enum {
 typedef enum {
   FA_BWD_OK = 0,
   FA_BWD_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad mask code, bad scale, misalignment */
-  FA_BWD_ERR_UNSUPPORTED = 2,      /* head_dim other than 64 or 128; grouped heads or a window in the
-                                      single-pass form */
+  FA_BWD_ERR_UNSUPPORTED = 2,      /* a head dim that is not a multiple of 8 in [8, 256]; in the
+                                      single-pass form: head dims other than 64 or 128, unequal head
+                                      dims, grouped heads or a window */
   FA_BWD_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed in fa_bwd_create */
   FA_BWD_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
 } fa_bwd_status;
@@ -81,7 +83,9 @@ typedef enum {
 typedef struct {
   int32_t batch;         /* number of sequences (entries of cu_seqlens minus one), >= 1 */
   int32_t num_heads;     /* heads of Q, O, dO, dQ, m, l, >= 1 */
-  int32_t head_dim;      /* 64 or 128 */
+  int32_t head_dim;      /* head dim of Q, K, dQ, dK: a multiple of 8 from 8 to 256 (the head dim
+                            limits of the jax cuDNN wrapper's bf16 path); the single-pass form takes
+                            64 and 128 */
   int32_t max_seqlen_q;  /* >= every L_b of the queries; the slot length in padded modes; >= 1 */
   int32_t max_seqlen_kv; /* same for keys/values */
   int64_t total_q;       /* rows of q, o, do, dq, m, l; >= 1 */
@@ -94,6 +98,9 @@ typedef struct {
   int32_t window;        /* 0: no window; w > 0: every query i sees only its left local window of keys
                             (i - w, i] (the jax cuDNN wrapper's sliding_window_length), which implies
                             the causal bound whatever the mask code; recompute form and forward only */
+  int32_t head_dim_v;    /* head dim of V, O, dO and dV: 0 = head_dim. It may differ from head_dim
+                            (latent attention: the jax cuDNN wrapper's qH != vH); then S = Q K^T runs
+                            over head_dim and O = P V over head_dim_v. Recompute form and forward only */
 } fa_bwd_desc;
 
 /* Validates desc (a num_heads_kv of 0 is stored as num_heads) and allocates
@@ -106,16 +113,19 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out);
 /* Enqueues the backward on `stream` (a hipStream_t; NULL = the default
  * stream) and returns without waiting. The caller synchronises its stream
  * before reading dq/dk/dv.
- *   q, o, dout: bf16 [total_q][H][head_dim]        (read only)
- *   k, v:       bf16 [total_kv][H_kv][head_dim]    (read only; H_kv = num_heads_kv)
+ *   q:          bf16 [total_q][H][head_dim]        (read only)
+ *   o, dout:    bf16 [total_q][H][head_dim_v]      (read only)
+ *   k:          bf16 [total_kv][H_kv][head_dim]    (read only; H_kv = num_heads_kv)
+ *   v:          bf16 [total_kv][H_kv][head_dim_v]  (read only)
  *   m, l:       fp32 [total_q][H], row max of the scaled visible logits and
  *               the row sum of exp(scaled logit - m) over visible keys, as the
  *               forward produced them (not recomputed here; l > 0 on valid rows)
  *   cu_seqlens_q, cu_seqlens_kv: int32 [batch+1] device arrays (see above)
  *   scale:      the softmax scale applied to Q K^T (finite, > 0), e.g. 1/sqrt(head_dim)
  *   mask:       an fa_bwd_mask code
- *   dq:         bf16 [total_q][H][head_dim]     (written)
- *   dk, dv:     bf16 [total_kv][H_kv][head_dim] (written)
+ *   dq:         bf16 [total_q][H][head_dim]       (written)
+ *   dk:         bf16 [total_kv][H_kv][head_dim]   (written)
+ *   dv:         bf16 [total_kv][H_kv][head_dim_v] (written)
  * Every argument is checked on the host first; an invalid one returns
  * FA_BWD_ERR_INVALID_ARGUMENT with nothing enqueued. FA_BWD_ERR_HIP reports a
  * failed launch. The handle's workspace is reused by every call, so one
@@ -139,9 +149,10 @@ fa_bwd_status fa_bwd_run_lse(fa_bwd_handle* h, const void* q, const void* k, con
  * consumes, for the sizes of the handle (its workspace is not used; FA_BWD_ALGO_* is ignored).
  * The softmax is the one step 2 of the SK-16 article inverts, P = exp(S*scale - m) / l.
  *   q:          bf16 [total_q][H][head_dim]   (read only)
- *   k, v:       bf16 [total_kv][H_kv][head_dim]  (read only)
+ *   k:          bf16 [total_kv][H_kv][head_dim]  (read only)
+ *   v:          bf16 [total_kv][H_kv][head_dim_v]  (read only)
  *   cu_seqlens_q, cu_seqlens_kv, scale, mask: as for fa_bwd_run
- *   o:          bf16 [total_q][H][head_dim]   (written)
+ *   o:          bf16 [total_q][H][head_dim_v] (written)
  *   m:          fp32 [total_q][H]  (written) row max of the scaled visible logits
  *   l:          fp32 [total_q][H]  (written) row sum of exp(scaled logit - m) over visible keys
  * Rows outside every sequence get O = 0, m = 0, l = 1; a row whose sequence has no keys gets the

@@ -58,9 +58,16 @@ def _create(**kw):
     (dict(max_seqlen_kv=-5), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(total_q=0), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(total_kv=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
-    (dict(head_dim=96), B.FA_BWD_ERR_UNSUPPORTED),
-    (dict(head_dim=256), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(head_dim=0), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(head_dim=4), B.FA_BWD_ERR_UNSUPPORTED),       # head dims: multiples of 8 in [8, 256]
+    (dict(head_dim=100), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(head_dim=264), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(head_dim_v=12), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(head_dim_v=-8), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(head_dim=96, algorithm=1), B.FA_BWD_ERR_UNSUPPORTED),                 # single pass: 64 or 128,
+    (dict(head_dim=256, algorithm=1), B.FA_BWD_ERR_UNSUPPORTED),                # equal head dims
+    (dict(head_dim=128, head_dim_v=64, algorithm=1), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(num_heads=1 << 14, head_dim=256), B.FA_BWD_ERR_INVALID_ARGUMENT),     # 128 rows >= 2^30 bytes
     (dict(algorithm=3), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(algorithm=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(total_q=1 << 40, num_heads=8), B.FA_BWD_ERR_INVALID_ARGUMENT),          # index range
@@ -105,7 +112,7 @@ def test_binding_maps_status_to_exceptions():
     with pytest.raises(ValueError):
         B.fa_bwd_create(0, 1, 128, 1, 1, 1, 1)
     with pytest.raises(NotImplementedError):
-        B.fa_bwd_create(1, 1, 80, 1, 1, 1, 1)
+        B.fa_bwd_create(1, 1, 84, 1, 1, 1, 1)
 
 
 def test_missing_library_fails_loudly(tmp_path):

@@ -11,7 +11,8 @@ cuDNN ``MaskType``. The pins:
   columns, rowsum(O*dO) = rowsum(P*dP), causal zero patterns;
 * closed forms: one key, all-equal V rows, Q = 0;
 * torch fp64 autograd of softmax(scale*QK^T + mask) V, an independent library (with grouped
-  K/V heads expanded by torch's repeat_interleave, so autograd sums the shared heads' gradients);
+  K/V heads expanded by torch's repeat_interleave, so autograd sums the shared heads' gradients),
+  also with a value head dim that differs from the query/key one;
 * the forward on its own: O, the row max of the scaled logits and m + ln(l) against torch's
   softmax attention, max and logsumexp; the sampled-row forward against the full one;
 * planted mistakes in the oracle's own source, each caught by one of the above.
@@ -34,7 +35,8 @@ def _rand(shape, rng, mult=1.0):
     return rng.standard_normal(shape) * mult
 
 
-def make_problem(mask, lens_q, lens_kv, heads=2, d=4, seed=0, padded_len=0, mult=1.0, heads_kv=None, window=0):
+def make_problem(mask, lens_q, lens_kv, heads=2, d=4, seed=0, padded_len=0, mult=1.0, heads_kv=None, window=0,
+                 d_v=None):
     rng = np.random.default_rng(seed)
     if A.is_padded(mask):
         tq = tkv = len(lens_q) * padded_len
@@ -45,8 +47,9 @@ def make_problem(mask, lens_q, lens_kv, heads=2, d=4, seed=0, padded_len=0, mult
     cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
     cu_kv = np.concatenate([[0], np.cumsum(lens_kv)]).astype(np.int64)
     hkv = heads if heads_kv is None else heads_kv
+    dv = d if d_v is None else d_v
     return dict(q=_rand((tq, heads, d), rng, mult), k=_rand((tkv, hkv, d), rng, mult),
-                v=_rand((tkv, hkv, d), rng), do=_rand((tq, heads, d), rng),
+                v=_rand((tkv, hkv, dv), rng), do=_rand((tq, heads, dv), rng),
                 cu_q=cu_q, cu_kv=cu_kv, scale=1.0 / math.sqrt(d), mask=mask,
                 max_seqlen_q=msq, max_seqlen_kv=mskv, window=window)
 
@@ -483,6 +486,40 @@ def test_backward_rows_matches_full(mask):
 
 
 # ---------------------------------------------------------------- planted mistakes are caught
+
+# ---------------------------------------------------------------- value head dim != query/key head dim
+
+MLA_CASES = [
+    # (mask, lens_q, lens_kv, d, d_v, padded_len)
+    (MASK_NONE, [3], [5], 4, 2, 0),
+    (MASK_CAUSAL, [5], [5], 2, 6, 0),
+    (MASK_PADDING_CAUSAL, [4, 2], [4, 3], 6, 3, 4),
+]
+
+
+@pytest.mark.parametrize("mask,lq,lk,d,d_v,padded", MLA_CASES)
+def test_value_head_dim_finite_differences(mask, lq, lk, d, d_v, padded):
+    p = make_problem(mask, lq, lk, heads=2, d=d, seed=71, padded_len=padded, d_v=d_v)
+    assert fd_error(p) < 1e-6
+
+
+@pytest.mark.parametrize("mask,lq,lk,d,d_v,padded", MLA_CASES + [(MASK_CAUSAL, [70, 33], [70, 50], 24, 8, 0)])
+def test_value_head_dim_torch_fp64_autograd(mask, lq, lk, d, d_v, padded):
+    p = make_problem(mask, lq, lk, heads=3, d=d, seed=72, padded_len=padded, mult=1.5, d_v=d_v)
+    assert torch_error(p) < 1e-10
+
+
+def test_value_head_dim_rows_match_full():
+    p = make_problem(MASK_CAUSAL, [40, 17], [40, 30], heads=2, d=12, seed=73, d_v=20)
+    o, m, l, dq, dk, dv = exact_backward(p)
+    assert o.shape[2] == 20 and dq.shape[2] == 12 and dk.shape[2] == 12 and dv.shape[2] == 20
+    rows = [0, 5, 39]
+    ro, rm, rl = A.forward_rows(p["q"], p["k"], p["v"], p["cu_q"], p["cu_kv"], p["scale"], p["mask"], 0, 1, rows)
+    assert np.allclose(ro, o[rows, 1]) and np.allclose(rm, m[rows, 1]) and np.allclose(rl, l[rows, 1])
+    rq, rk, rv = A.backward_rows(p["q"], p["k"], p["v"], o, p["do"], m, l, p["cu_q"], p["cu_kv"], p["scale"],
+                                 p["mask"], 0, 1, rows, [0, 7, 39])
+    assert np.allclose(rq, dq[rows, 1]) and np.allclose(rk, dk[[0, 7, 39], 1]) and np.allclose(rv, dv[[0, 7, 39], 1])
+
 
 def _mutant(monkeypatch, func_name, old, new):
     """Replace ``func_name`` in the oracle module by a copy of its source with one edit."""
