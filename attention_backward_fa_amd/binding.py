@@ -32,7 +32,7 @@ FA_BWD_MASK_CAUSAL = 2
 FA_BWD_MASK_PADDING_CAUSAL = 3
 
 # every symbol include/fa_bwd.h declares
-EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_run_lse", "fa_fwd_run", "fa_bwd_destroy",
+EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_run_lse", "fa_fwd_run", "fa_bwd_plan", "fa_bwd_destroy",
             "fa_bwd_status_string", "fa_bwd_get_desc", "fa_bwd_profile_enable", "fa_bwd_profile_collect")
 
 
@@ -63,6 +63,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_run_lse.restype = i32
     lib.fa_fwd_run.argtypes = [vp] * 6 + [f32, i32] + [vp] * 4
     lib.fa_fwd_run.restype = i32
+    lib.fa_bwd_plan.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), i32]
+    lib.fa_bwd_plan.restype = i32
     lib.fa_bwd_destroy.argtypes = [vp]
     lib.fa_bwd_destroy.restype = i32
     lib.fa_bwd_status_string.argtypes = [i32]
@@ -113,6 +115,27 @@ def fa_bwd_get_desc(handle) -> FaBwdDesc:
 
 def fa_bwd_destroy(handle) -> None:
     _check(load_library().fa_bwd_destroy(handle), "fa_bwd_destroy")
+
+
+def fa_bwd_plan(handle, cu_seqlens_q, cu_seqlens_kv, mask: int) -> None:
+    """Longest-first schedule from host sequence offsets (any int sequence, numpy array or CPU tensor of
+    batch + 1 entries); later runs with this mask launch one workgroup per non-empty tile. Both None
+    drops the plan."""
+    if cu_seqlens_q is None and cu_seqlens_kv is None:
+        _check(load_library().fa_bwd_plan(handle, None, None, int(mask)), "fa_bwd_plan")
+        return
+    d = fa_bwd_get_desc(handle)
+    arrays = []
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
+        if cu is None:
+            raise ValueError(f"{name}: both offset arrays or neither")
+        if hasattr(cu, "device") and getattr(cu.device, "type", "cpu") != "cpu":
+            raise ValueError(f"{name}: expected host values, got device {cu.device}")
+        vals = [int(x) for x in (cu.tolist() if hasattr(cu, "tolist") else cu)]
+        if len(vals) != d.batch + 1:
+            raise ValueError(f"{name}: expected {d.batch + 1} entries, got {len(vals)}")
+        arrays.append((ctypes.c_int32 * len(vals))(*vals))
+    _check(load_library().fa_bwd_plan(handle, arrays[0], arrays[1], int(mask)), "fa_bwd_plan")
 
 
 def _expect(t, name, shape, dtype, device):
@@ -261,6 +284,9 @@ class FaBwd:
         l = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if l is None else l
         fa_fwd_run(self.handle, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o, m, l, stream)
         return o, m, l
+
+    def plan(self, cu_seqlens_q, cu_seqlens_kv, mask):
+        fa_bwd_plan(self.handle, cu_seqlens_q, cu_seqlens_kv, mask)
 
     def close(self):
         if self.handle is not None and self.handle.value:

@@ -2,6 +2,7 @@
 // host-side validation, the handle's device workspace and the three launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -21,6 +22,11 @@ struct fa_bwd_handle {
   bool profiling;
   std::vector<hipEvent_t> events;  // 4 per recorded run
   int64_t recorded;                // runs whose events are in `events`
+  // host schedule (fa_bwd_plan): (tile, sequence * heads + head) pairs, the dK/dV kernel's items
+  // first, then the dQ kernel's (also the forward's); null when there is no plan
+  int32_t* sched;
+  int64_t n_kv_items, n_q_items;
+  int32_t plan_mask;
 };
 
 namespace {
@@ -231,13 +237,15 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.scale_log2 = scale * fa::kLog2e;
   ma.scale = scale;
   const fa::KernelSet ks = pick_kernels(d.head_dim, d.head_dim_v);
+  const bool planned = h->sched && h->plan_mask == mask;
+  ma.sched = planned ? h->sched : nullptr;
   if (h->single_pass) {  // head_dim == head_dim_v, 64 or 128 (checked at create)
     if (d.head_dim == 128)
       launch_single_pass<128>(ma, causal, stream);
     else
       launch_single_pass<64>(ma, causal, stream);
-  } else {
-    ks.dkdv(ma, stream);
+  } else if (!planned || h->n_kv_items > 0) {
+    ks.dkdv(ma, h->n_kv_items, stream);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return FA_BWD_ERR_HIP;
@@ -247,8 +255,9 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
       launch_cast<128>(ma, stream);
     else
       launch_cast<64>(ma, stream);
-  } else {
-    ks.dq(ma, stream);
+  } else if (!planned || h->n_q_items > 0) {
+    ma.sched = planned ? h->sched + 2 * h->n_kv_items : nullptr;
+    ks.dq(ma, h->n_q_items, stream);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return FA_BWD_ERR_HIP;
@@ -293,10 +302,73 @@ fa_bwd_status launch_fwd(fa_bwd_handle* h, const void* q, const void* k, const v
   launch_rows<fa::FwdArgs, fill_kernel>(tpr, dim3((unsigned)((rows + rpb - 1) / rpb)), stream, fa);
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return FA_BWD_ERR_HIP;
-  pick_kernels(d.head_dim, d.head_dim_v).fwd(fa, causal, stream);
+  const bool planned = h->sched && h->plan_mask == mask;
+  fa.sched = planned ? h->sched + 2 * h->n_kv_items : nullptr;
+  if (!planned || h->n_q_items > 0) pick_kernels(d.head_dim, d.head_dim_v).fwd(fa, causal, h->n_q_items, stream);
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && (hipEventRecord(ev[2], stream) != hipSuccess || hipEventRecord(ev[3], stream) != hipSuccess))
     return FA_BWD_ERR_HIP;
+  return FA_BWD_OK;
+}
+
+void drop_plan(fa_bwd_handle* h) {
+  if (h->sched) (void)hipFree(h->sched);
+  h->sched = nullptr;
+  h->n_kv_items = h->n_q_items = 0;
+}
+
+// The work items of the recompute kernels for host sequence offsets, longest first. Work counts the
+// tile pairs a workgroup visits, as the kernels bound their loops (causal start, window band).
+fa_bwd_status build_plan(const fa_bwd_desc& d, const int32_t* cq, const int32_t* ck, int32_t mask,
+                         std::vector<int32_t>& out, int64_t& n_kv, int64_t& n_q) {
+  const bool padded = mask == FA_BWD_MASK_PADDING || mask == FA_BWD_MASK_PADDING_CAUSAL;
+  const bool causal = mask == FA_BWD_MASK_CAUSAL || mask == FA_BWD_MASK_PADDING_CAUSAL || d.window > 0;
+  if (cq[0] != 0 || ck[0] != 0) return FA_BWD_ERR_INVALID_ARGUMENT;
+  for (int b = 0; b < d.batch; ++b) {
+    const int64_t lq = (int64_t)cq[b + 1] - cq[b], lk = (int64_t)ck[b + 1] - ck[b];
+    if (lq < 0 || lk < 0 || lq > d.max_seqlen_q || lk > d.max_seqlen_kv) return FA_BWD_ERR_INVALID_ARGUMENT;
+  }
+  if (padded ? ((int64_t)d.batch * d.max_seqlen_q > d.total_q || (int64_t)d.batch * d.max_seqlen_kv > d.total_kv)
+             : (cq[d.batch] > d.total_q || ck[d.batch] > d.total_kv))
+    return FA_BWD_ERR_INVALID_ARGUMENT;
+  const fa::KernelSet ks = pick_kernels(d.head_dim, d.head_dim_v);
+  struct Item {
+    int64_t work;
+    int32_t tile, hb;
+  };
+  std::vector<Item> kv, q;
+  const int G = d.num_heads / d.num_heads_kv, w = d.window;
+  for (int b = 0; b < d.batch; ++b) {
+    const int lq = cq[b + 1] - cq[b], lk = ck[b + 1] - ck[b];
+    const int n_qs = (lq + ks.q_step - 1) / ks.q_step;  // q steps of the dK/dV kernel
+    for (int t = 0; t * ks.kv_tile < lk; ++t) {
+      const int kv0 = t * ks.kv_tile;
+      const int qt0 = causal ? kv0 / ks.q_step : 0;
+      const int qt_end = w > 0 ? std::min(n_qs, (kv0 + ks.kv_tile - 2 + w) / ks.q_step + 1) : n_qs;
+      const int64_t work = (int64_t)G * std::max(0, qt_end - qt0);
+      for (int hk = 0; hk < d.num_heads_kv; ++hk) kv.push_back({work, t, b * d.num_heads_kv + hk});
+    }
+    for (int t = 0; t * ks.q_tile < lq; ++t) {
+      const int i0 = t * ks.q_tile;
+      int n_kt = (lk + ks.kv_step - 1) / ks.kv_step;
+      if (causal) n_kt = std::min(n_kt, (i0 + ks.q_tile - 1) / ks.kv_step + 1);
+      const int t0 = w > 0 ? std::max(0, i0 - w + 1) / ks.kv_step : 0;
+      const int64_t work = std::max(0, n_kt - t0);
+      for (int hq = 0; hq < d.num_heads; ++hq) q.push_back({work, t, b * d.num_heads + hq});
+    }
+  }
+  // most work first; ties in the dense grid's order (tile, then sequence and head)
+  auto longest_first = [](const Item& x, const Item& y) {
+    if (x.work != y.work) return x.work > y.work;
+    return x.tile != y.tile ? x.tile < y.tile : x.hb < y.hb;
+  };
+  std::sort(kv.begin(), kv.end(), longest_first);
+  std::sort(q.begin(), q.end(), longest_first);
+  out.clear();
+  for (const Item& it : kv) out.insert(out.end(), {it.tile, it.hb});
+  for (const Item& it : q) out.insert(out.end(), {it.tile, it.hb});
+  n_kv = (int64_t)kv.size();
+  n_q = (int64_t)q.size();
   return FA_BWD_OK;
 }
 
@@ -395,6 +467,43 @@ fa_bwd_status fa_fwd_run(fa_bwd_handle* h, const void* q, const void* k, const v
   return launch_fwd(h, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o, m, l, static_cast<hipStream_t>(stream));
 }
 
+fa_bwd_status fa_bwd_plan(fa_bwd_handle* h, const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_kv_host,
+                          int32_t mask) {
+  if (!h) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (h->single_pass) return FA_BWD_ERR_UNSUPPORTED;
+  if (!cu_seqlens_q_host != !cu_seqlens_kv_host) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens_q_host && (mask < FA_BWD_MASK_NONE || mask > FA_BWD_MASK_PADDING_CAUSAL))
+    return FA_BWD_ERR_INVALID_ARGUMENT;
+  std::vector<int32_t> items;
+  int64_t n_kv = 0, n_q = 0;
+  if (cu_seqlens_q_host) {
+    const fa_bwd_status st = build_plan(h->desc, cu_seqlens_q_host, cu_seqlens_kv_host, mask, items, n_kv, n_q);
+    if (st != FA_BWD_OK) return st;
+  }
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(h->device) != hipSuccess) return FA_BWD_ERR_HIP;
+  fa_bwd_status st = FA_BWD_OK;
+  if (h->sched && hipDeviceSynchronize() != hipSuccess) st = FA_BWD_ERR_HIP;  // runs may still read it
+  drop_plan(h);
+  if (st == FA_BWD_OK && !items.empty()) {
+    if (hipMalloc(&h->sched, items.size() * sizeof(int32_t)) != hipSuccess) {
+      (void)hipGetLastError();
+      h->sched = nullptr;
+      st = FA_BWD_ERR_OUT_OF_MEMORY;
+    } else if (hipMemcpy(h->sched, items.data(), items.size() * sizeof(int32_t), hipMemcpyHostToDevice) !=
+               hipSuccess) {
+      drop_plan(h);
+      st = FA_BWD_ERR_HIP;
+    } else {
+      h->n_kv_items = n_kv;
+      h->n_q_items = n_q;
+      h->plan_mask = mask;
+    }
+  }
+  (void)hipSetDevice(prev);
+  return st;
+}
+
 fa_bwd_status fa_bwd_destroy(fa_bwd_handle* h) {
   if (!h) return FA_BWD_OK;
   int prev = 0;
@@ -404,6 +513,7 @@ fa_bwd_status fa_bwd_destroy(fa_bwd_handle* h) {
   if (h->dq_acc && hipFree(h->dq_acc) != hipSuccess) st = FA_BWD_ERR_HIP;
   if (hipFree(h->lse2) != hipSuccess) st = FA_BWD_ERR_HIP;
   if (hipFree(h->dvec) != hipSuccess) st = FA_BWD_ERR_HIP;
+  drop_plan(h);
   release_events(h);
   (void)hipSetDevice(prev);
   delete h;

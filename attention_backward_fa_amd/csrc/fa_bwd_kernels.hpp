@@ -135,6 +135,7 @@ struct MainArgs {
   int d_qk, d_v;     // head dims of Q, K (dQ, dK) and of V, dO (dV): at most the kernel's padded dims
   float scale_log2;  // scale * log2(e)
   float scale;
+  const int* sched;  // recompute kernels: (tile, sequence * heads + head) per workgroup, or null (dense grid)
 };
 
 template <int D>
@@ -572,9 +573,11 @@ void fa_bwd_dkdv(MainArgs a) {
   bf16* s_do = (bf16*)(smem + C::OFF_DO);
   float* s_st = (float*)(smem + C::OFF_ST);
 
+  // the host schedule names each workgroup's (kv tile, sequence * Hk + K/V head); the dense grid
+  // puts the heavy (low) kv tiles of every head first
   const int HB = a.Hk * a.batch;
-  const int tile = blockIdx.x / HB;  // heavy (low) kv tiles of every head dispatch first
-  const int hb = blockIdx.x - tile * HB;
+  const int tile = a.sched ? a.sched[2 * blockIdx.x] : blockIdx.x / HB;
+  const int hb = a.sched ? a.sched[2 * blockIdx.x + 1] : blockIdx.x - tile * HB;
   const int b = hb / a.Hk, hk = hb - (hb / a.Hk) * a.Hk;  // sequence, K/V head
   int64_t q_start, kv_start;
   int Lq, Lk;
@@ -1006,9 +1009,11 @@ void fa_bwd_dq(MainArgs a) {
   constexpr int BQ = C::BQ, BK = C::BK, QSQ = C::QSQ, QSV = C::QSV;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
+  // the host schedule names each workgroup's (q tile, sequence * H + head); in the dense grid under
+  // a causal mask the q tiles with the most keys (the last ones) dispatch first
   const int HB = a.H * a.batch;
-  const int tr = blockIdx.x / HB;
-  const int hb = blockIdx.x - tr * HB;
+  const int tr = a.sched ? 0 : blockIdx.x / HB;
+  const int hb = a.sched ? a.sched[2 * blockIdx.x + 1] : blockIdx.x - tr * HB;
   const int b = hb / a.H, h = hb - (hb / a.H) * a.H;
   int64_t q_start, kv_start;
   int Lq, Lk;
@@ -1016,9 +1021,8 @@ void fa_bwd_dq(MainArgs a) {
   seq_of(a.cu_kv, b, a.padded, a.max_seqlen_kv, kv_start, Lk);
   Lq = clamp_len(q_start, Lq, a.total_q);
   Lk = clamp_len(kv_start, Lk, a.total_kv);
-  // causal: the q tiles with the most keys (the last ones) dispatch first
   const int n_qt_max = (a.max_seqlen_q + BQ - 1) / BQ;
-  const int qtile = CAUSAL ? n_qt_max - 1 - tr : tr;
+  const int qtile = a.sched ? a.sched[2 * blockIdx.x] : CAUSAL ? n_qt_max - 1 - tr : tr;
   const int i0 = qtile * BQ;
   if (i0 >= Lq) return;
 
@@ -1213,6 +1217,7 @@ struct FwdArgs {
   int window;        // > 0: each query sees only its left local window of keys (i - window, i]
   int d_qk, d_v;     // head dims of Q, K and of V, O
   float scale_log2;  // scale * log2(e)
+  const int* sched;  // (q tile, sequence * H + head) per workgroup, or null (dense grid)
 };
 
 // Rows outside every sequence: O = 0, m = 0, l = 1 (finite values a backward never reads).
@@ -1246,9 +1251,11 @@ void fa_fwd(FwdArgs a) {
   constexpr int BQ = C::BQ, BK = C::BK, QSQ = C::QSQ, QSV = C::QSV;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
+  // the host schedule names each workgroup's (q tile, sequence * H + head); in the dense grid under
+  // a causal mask the q tiles with the most keys (the last ones) dispatch first
   const int HB = a.H * a.batch;
-  const int tr = blockIdx.x / HB;
-  const int hb = blockIdx.x - tr * HB;
+  const int tr = a.sched ? 0 : blockIdx.x / HB;
+  const int hb = a.sched ? a.sched[2 * blockIdx.x + 1] : blockIdx.x - tr * HB;
   const int b = hb / a.H, h = hb - (hb / a.H) * a.H;
   int64_t q_start, kv_start;
   int Lq, Lk;
@@ -1257,7 +1264,7 @@ void fa_fwd(FwdArgs a) {
   Lq = clamp_len(q_start, Lq, a.total_q);
   Lk = clamp_len(kv_start, Lk, a.total_kv);
   const int n_qt_max = (a.max_seqlen_q + BQ - 1) / BQ;
-  const int qtile = CAUSAL ? n_qt_max - 1 - tr : tr;  // causal: q tiles with the most keys first
+  const int qtile = a.sched ? a.sched[2 * blockIdx.x] : CAUSAL ? n_qt_max - 1 - tr : tr;
   const int i0 = qtile * BQ;
   if (i0 >= Lq) return;
 

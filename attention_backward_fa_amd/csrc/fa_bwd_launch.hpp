@@ -19,8 +19,9 @@ struct Recompute {
     return (int64_t)((max_seqlen_q + DqCfg<DQ, DV>::BQ - 1) / DqCfg<DQ, DV>::BQ) * H * batch;
   }
 
-  static void dkdv(const MainArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)dkdv_blocks(a)), block(DkdvCfg<DQ, DV>::NT);
+  // items: the workgroup count of a host schedule (a.sched), else unused
+  static void dkdv(const MainArgs& a, int64_t items, hipStream_t s) {
+    const dim3 grid((unsigned)(a.sched ? items : dkdv_blocks(a))), block(DkdvCfg<DQ, DV>::NT);
     if (a.window > 0)  // the window implies the causal bound
       fa_bwd_dkdv<DQ, DV, true, true, EXACT><<<grid, block, 0, s>>>(a);
     else if (a.causal)
@@ -29,8 +30,8 @@ struct Recompute {
       fa_bwd_dkdv<DQ, DV, false, false, EXACT><<<grid, block, 0, s>>>(a);
   }
 
-  static void dq(const MainArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)q_blocks(a.max_seqlen_q, a.H, a.batch)), block(256);
+  static void dq(const MainArgs& a, int64_t items, hipStream_t s) {
+    const dim3 grid((unsigned)(a.sched ? items : q_blocks(a.max_seqlen_q, a.H, a.batch))), block(256);
     if (a.window > 0)
       fa_bwd_dq<DQ, DV, true, true, EXACT><<<grid, block, 0, s>>>(a);
     else if (a.causal)
@@ -39,8 +40,8 @@ struct Recompute {
       fa_bwd_dq<DQ, DV, false, false, EXACT><<<grid, block, 0, s>>>(a);
   }
 
-  static void fwd(const FwdArgs& a, bool causal, hipStream_t s) {
-    const dim3 grid((unsigned)q_blocks(a.max_seqlen_q, a.H, a.batch)), block(256);
+  static void fwd(const FwdArgs& a, bool causal, int64_t items, hipStream_t s) {
+    const dim3 grid((unsigned)(a.sched ? items : q_blocks(a.max_seqlen_q, a.H, a.batch))), block(256);
     if (a.window > 0)
       fa_fwd<DQ, DV, true, true, EXACT><<<grid, block, 0, s>>>(a);
     else if (causal)
@@ -50,16 +51,19 @@ struct Recompute {
   }
 };
 
-// The launches of one pair of padded head dims.
+// The launches of one pair of padded head dims, and the tile sizes a host schedule counts in.
 struct KernelSet {
-  void (*dkdv)(const MainArgs&, hipStream_t);
-  void (*dq)(const MainArgs&, hipStream_t);
-  void (*fwd)(const FwdArgs&, bool, hipStream_t);
+  void (*dkdv)(const MainArgs&, int64_t, hipStream_t);
+  void (*dq)(const MainArgs&, int64_t, hipStream_t);
+  void (*fwd)(const FwdArgs&, bool, int64_t, hipStream_t);
+  int kv_tile, q_step;  // dK/dV kernel: kv rows per workgroup, q rows per step
+  int q_tile, kv_step;  // dQ kernel and forward: q rows per workgroup, kv rows per step
 };
 
 template <int DQ, int DV, bool EXACT>
 KernelSet kernel_set() {
-  return {Recompute<DQ, DV, EXACT>::dkdv, Recompute<DQ, DV, EXACT>::dq, Recompute<DQ, DV, EXACT>::fwd};
+  using R = Recompute<DQ, DV, EXACT>;
+  return {R::dkdv, R::dq, R::fwd, DkdvCfg<DQ, DV>::BN, DkdvCfg<DQ, DV>::BM, DqCfg<DQ, DV>::BQ, DqCfg<DQ, DV>::BK};
 }
 
 // The pairs (128, 256), (256, 128) and (256, 256), from fa_bwd_wide.hip; pq, pv are padded dims,

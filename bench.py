@@ -26,8 +26,9 @@ kernel sources still hash to the recorded value, else null) and a
 over a bounded sample of the same workload).
 
 ``--path forward`` times the forward that produces O, m, l instead, under its
-own metric; ``--calibrate-copy MIB`` first runs a kernel of known traffic, for
-scaling the counters in a ``rocprofv3 --pmc`` run.
+own metric; ``--plan`` launches from the host-side longest-first schedule
+(``fa_bwd_plan``) instead of the dense grid; ``--calibrate-copy MIB`` first runs
+a kernel of known traffic, for scaling the counters in a ``rocprofv3 --pmc`` run.
 """
 from __future__ import annotations
 
@@ -241,6 +242,8 @@ def bench_forward(args, device):
     flops = algorithmic_flops(inp) * 0.4
     tq, heads, d = inp["q"].shape
     op = binding.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0])
+    if args.plan:
+        op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
     o = torch.empty_like(dev["q"])
     m = torch.empty((tq, heads), dtype=torch.float32, device=device)
     l = torch.empty((tq, heads), dtype=torch.float32, device=device)
@@ -292,6 +295,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="causal")
+    ap.add_argument("--plan", action="store_true",
+                    help="launch from a host-side longest-first schedule (fa_bwd_plan) instead of the dense grid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--algorithm", choices=list(ALGORITHMS), default="default")
@@ -325,6 +330,8 @@ def main():
     op = binding.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0],
                        algo)
     algo_used = 1 if algo == 1 else 2
+    if args.plan:  # host-side longest-first schedule from the (host) sequence offsets
+        op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
     dq, dk, dv = (torch.empty_like(dev[x]) for x in ("q", "k", "v"))
 
     def step():
@@ -363,7 +370,8 @@ def main():
               "batch": inp["batch"], "heads": heads, "head_dim": d, "seq_len": inp["max_seqlen_q"],
               "total_tokens": tq, "mask": MASK_NAMES[inp["mask"]], "seed": inp["seed"],
               "algorithmic_flops": flops,
-              "algorithm": "single-pass (dQ atomics)" if algo_used == 1 else "recompute (dK/dV kernel + dQ kernel)"}
+              "algorithm": "single-pass (dQ atomics)" if algo_used == 1 else "recompute (dK/dV kernel + dQ kernel)",
+              "schedule": "host longest-first plan" if args.plan else "dense grid"}
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",

@@ -163,6 +163,25 @@ fa_bwd_status fa_fwd_run(fa_bwd_handle* h, const void* q, const void* k, const v
                          const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* o, float* m, float* l,
                          void* stream);
 
+/* Longest-first schedule from host copies of the sequence offsets (the SK-16 article lets its
+ * control flow read actual_q / actual_kv on the host, section 三). Builds the list of work items
+ * of the recompute-form kernels and of the forward, one per (tile, head, sequence) that holds rows
+ * of a sequence, ordered by decreasing work (number of tile pairs it visits; ties in the dense
+ * grid's order: tile, then sequence and head), and keeps it in device memory owned by the handle. Later fa_bwd_run,
+ * fa_bwd_run_lse and fa_fwd_run calls whose mask equals `mask` launch one workgroup per item instead
+ * of the dense grid of max_seqlen tiles x heads x sequences; calls with another mask use the dense
+ * grid. The results are bitwise the same either way: only the launch order and the empty
+ * workgroups change.
+ *   cu_seqlens_q_host, cu_seqlens_kv_host: HOST int32 [batch+1], the values the device arrays of
+ *     those later calls hold (the library cannot compare them; a mismatch gives wrong gradients).
+ *     Checked here: cu[0] = 0, non-decreasing, every length <= its max_seqlen, and cu[batch] <=
+ *     total (packed masks); otherwise FA_BWD_ERR_INVALID_ARGUMENT and the previous plan is kept.
+ *   mask: the fa_bwd_mask code of the later calls (it sets the causal bound of the work counts).
+ * Both arrays NULL: drop the plan. FA_BWD_ERR_UNSUPPORTED for a single-pass handle. Blocks until
+ * the schedule is on the device; must not overlap a run that uses the handle. */
+fa_bwd_status fa_bwd_plan(fa_bwd_handle* h, const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_kv_host,
+                          int32_t mask);
+
 /* Frees the workspace and the handle (NULL is accepted). Waits for the
  * device to finish work that may still use the workspace. */
 fa_bwd_status fa_bwd_destroy(fa_bwd_handle* h);

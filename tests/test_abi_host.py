@@ -98,6 +98,8 @@ def test_run_and_profile_reject_null_handle():
     assert lib.fa_bwd_run(None, *([p] * 9), ctypes.c_float(0.1), 0, p, p, p, None) == B.FA_BWD_ERR_INVALID_ARGUMENT
     assert lib.fa_bwd_run_lse(None, *([p] * 8), ctypes.c_float(0.1), 0, p, p, p, None) == B.FA_BWD_ERR_INVALID_ARGUMENT
     assert lib.fa_fwd_run(None, *([p] * 5), ctypes.c_float(0.1), 0, p, p, p, None) == B.FA_BWD_ERR_INVALID_ARGUMENT
+    cu = (ctypes.c_int32 * 2)(0, 1)
+    assert lib.fa_bwd_plan(None, cu, cu, 0) == B.FA_BWD_ERR_INVALID_ARGUMENT
     n = ctypes.c_int32()
     assert lib.fa_bwd_profile_collect(None, None, 0, ctypes.byref(n)) == B.FA_BWD_ERR_INVALID_ARGUMENT
     assert lib.fa_bwd_profile_enable(None, 1) == B.FA_BWD_ERR_INVALID_ARGUMENT

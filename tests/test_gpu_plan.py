@@ -1,0 +1,121 @@
+"""GPU tests of the host-side schedule (``fa_bwd_plan``): with a plan the recompute kernels and the
+forward launch one workgroup per non-empty (tile, head, sequence), longest first, instead of the
+dense grid. Each workgroup computes what it computes in the dense grid, so planned and dense runs
+must agree bitwise; one planned case is also compared with the oracle. Host-side rejections of bad
+offsets keep the previous plan."""
+import pytest
+import torch
+
+from attention_backward_fa_amd import binding as B
+from attention_backward_fa_amd import inputs as I
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+NONE, PAD, CAUSAL, PADC = I.MASK_NONE, I.MASK_PADDING, I.MASK_CAUSAL, I.MASK_PADDING_CAUSAL
+
+CASES = [
+    I.custom_case("plan_varlen_none", 4, 128, NONE, 401, [700, 65, 1, 300, 0, 129]),
+    I.custom_case("plan_varlen_causal", 4, 128, CAUSAL, 402, [513, 64, 200, 1000]),
+    I.custom_case("plan_kv_longer_causal", 2, 64, CAUSAL, 403, [100, 250], [380, 64]),
+    I.custom_case("plan_padded_causal", 2, 128, PADC, 404, [300, 131], padded_len=320),
+    I.custom_case("plan_gqa_window", 4, 128, CAUSAL, 405, [600, 90], heads_kv=2, window=100),
+    I.custom_case("plan_wide_mla", 2, 192, CAUSAL, 406, [333, 70], head_dim_v=128),
+]
+
+
+def _tensors(inp, dev):
+    return {k: inp[k].to(dev) for k in ("q", "k", "v", "do", "cu_q", "cu_kv")}
+
+
+def _op(inp, case):
+    return B.FaBwd(inp["batch"], case.heads, case.head_dim, inp["max_seqlen_q"], inp["max_seqlen_kv"],
+                   inp["q"].shape[0], inp["k"].shape[0], num_heads_kv=inp["k"].shape[1], window=inp["window"],
+                   head_dim_v=inp["v"].shape[2])
+
+
+def _run(op, inp, t, o, m, l):
+    dq, dk, dv = op.run(t["q"], t["k"], t["v"], o, t["do"], m, l, t["cu_q"], t["cu_kv"], inp["scale"], inp["mask"])
+    fo, fm, fl = op.forward(t["q"], t["k"], t["v"], t["cu_q"], t["cu_kv"], inp["scale"], inp["mask"])
+    torch.cuda.synchronize()
+    return [x.clone() for x in (dq, dk, dv, fo, fm, fl)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c.name for c in CASES])
+def test_planned_equals_dense_bitwise(case):
+    inp = I.make(case)
+    print(f"[plan] {case.name}: lengths {inp['seqlens_q']} mask {case.mask}", flush=True)
+    dev = torch.device("cuda")
+    t = _tensors(inp, dev)
+    o, m, l = (x.to(dev) for x in P.oracle_stats(inp))
+    with _op(inp, case) as op:
+        dense = _run(op, inp, t, o, m, l)
+        op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
+        planned = _run(op, inp, t, o, m, l)
+        op.plan(None, None, inp["mask"])  # dropped: the dense grid again
+        again = _run(op, inp, t, o, m, l)
+    for name, x, y, z in zip(("dq", "dk", "dv", "o", "m", "l"), dense, planned, again):
+        assert torch.equal(x, y), f"{name}: planned run differs from the dense grid"
+        assert torch.equal(x, z), f"{name}: run after dropping the plan differs"
+
+
+def test_planned_matches_oracle():
+    case = CASES[1]
+    inp = I.make(case)
+    dev = torch.device("cuda")
+    t = _tensors(inp, dev)
+    o, m, l = P.oracle_stats(inp)
+    with _op(inp, case) as op:
+        op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
+        dq, dk, dv = op.run(t["q"], t["k"], t["v"], o.to(dev), t["do"], m.to(dev), l.to(dev), t["cu_q"], t["cu_kv"],
+                            inp["scale"], inp["mask"])
+        torch.cuda.synchronize()
+    P.check_full(inp, (dq.float().cpu(), dk.float().cpu(), dv.float().cpu()), P.oracle_backward(inp, o, m, l))
+
+
+def test_plan_for_another_mask_is_not_used():
+    case = CASES[1]
+    inp = I.make(case)
+    dev = torch.device("cuda")
+    t = _tensors(inp, dev)
+    o, m, l = (x.to(dev) for x in P.oracle_stats(inp))
+    with _op(inp, case) as op:
+        dense = _run(op, inp, t, o, m, l)
+        op.plan(inp["cu_q"], inp["cu_kv"], NONE)  # the runs use CAUSAL: dense grid
+        other = _run(op, inp, t, o, m, l)
+    for x, y in zip(dense, other):
+        assert torch.equal(x, y)
+
+
+def test_plan_rejects_bad_offsets_and_keeps_the_previous_plan():
+    case = CASES[0]
+    inp = I.make(case)
+    dev = torch.device("cuda")
+    t = _tensors(inp, dev)
+    o, m, l = (x.to(dev) for x in P.oracle_stats(inp))
+    cu = inp["cu_q"].tolist()
+    with _op(inp, case) as op:
+        op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
+        planned = _run(op, inp, t, o, m, l)
+        bad = [
+            [1] + cu[1:],                                   # cu[0] != 0
+            cu[:2] + [cu[1] - 1] + cu[3:],                  # decreasing
+            cu[:-1] + [cu[-1] + 1],                         # past total_q
+            [0] + [inp["max_seqlen_q"] + 1] * (len(cu) - 1),  # a length above max_seqlen_q
+        ]
+        for b in bad:
+            with pytest.raises(ValueError):
+                op.plan(b, inp["cu_kv"], inp["mask"])
+        with pytest.raises(ValueError):
+            op.plan(cu[:-1], inp["cu_kv"], inp["mask"])     # wrong count
+        with pytest.raises(ValueError):
+            op.plan(inp["cu_q"], None, inp["mask"])         # one array only
+        after = _run(op, inp, t, o, m, l)
+    for x, y in zip(planned, after):
+        assert torch.equal(x, y)
+
+
+def test_single_pass_handle_has_no_plan():
+    with B.FaBwd(1, 2, 128, 64, 64, 64, 64, B.FA_BWD_ALGO_SINGLE_PASS) as op:
+        with pytest.raises(NotImplementedError):
+            op.plan([0, 64], [0, 64], NONE)
