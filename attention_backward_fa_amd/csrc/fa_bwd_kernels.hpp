@@ -706,67 +706,57 @@ void fa_bwd_dkdv(MainArgs a) {
 #pragma unroll
   for (int nt = 0; nt < C::NTM; ++nt) acc_w[C::WIDE ? nt : 0] = f32x16{};
 
-  int buf = 0;
-  if (n_steps > 0) {
-    issue_tile(0, 0);
-    store_stats(0, load_stats(0));
-  }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  __syncthreads();
-
   const int arowq = (32 * mt + tile_row(c)) * QSQ + 8 * hh;  // A rows: this M-tile's q rows
   const int arowd = (32 * mt + tile_row(c)) * QSV + 8 * hh;
   const int krow = (32 * grp + c) * QSQ + 8 * hh;  // B columns: this group's keys
   const int vrow = (32 * grp + c) * QSV + 8 * hh;
   const int browq = (hh + 4 * (gi >> 2)) * QSQ + 16 * (g & 1) + 4 * (gi & 3) + 32 * mt * QSQ;
   const int browd = (hh + 4 * (gi >> 2)) * QSV + 16 * (g & 1) + 4 * (gi & 3) + 32 * mt * QSV;
-  for (int sp = 0; sp < n_steps; ++sp, buf ^= 1) {
-    const bool has_next = sp + 1 < n_steps;
-    float st_next = 0.f;
-    if (has_next) {
-      issue_tile(sp + 1, buf ^ 1);
-      st_next = load_stats(sp + 1);
-    }
-    const int i0 = step_tile(sp) * BM;
-    const bf16* sq = s_q + buf * (C::TQ_BYTES / 2);
-    const bf16* sd = s_do + buf * (C::TD_BYTES / 2);
-    const float* st = s_st + buf * 2 * BM + 32 * mt;
-    // steps 1 and 3 for this wave's M-tile: S = Q K^T, dP = dO V^T  ([q 32] x [kv 32]); operands
-    // are read PF k-steps ahead into distinct registers, one scheduling fence per k-step
-    f32x16 s = f32x16{}, dp = f32x16{};
-    {
-      constexpr int PF = 2;
-      bf16x8 qa[C::KSQ], da[C::KSV], kb[C::KSQ], vb[C::KSV];
-      auto ld = [&](int ks) {
-        if (ks < C::KSQ) {
-          qa[ks] = *(const bf16x8*)(sq + arowq + 16 * ks);
-          if constexpr (C::WIDE)
-            kb[ks] = kreg[ks];
-          else
-            kb[ks] = *(const bf16x8*)(s_k + krow + 16 * ks);
-        }
-        if (ks < C::KSV) {
-          da[ks] = *(const bf16x8*)(sd + arowd + 16 * ks);
-          if constexpr (C::WIDE)
-            vb[ks] = vreg[ks];
-          else
-            vb[ks] = *(const bf16x8*)(s_v + vrow + 16 * ks);
-        }
-      };
-#pragma unroll
-      for (int ks = 0; ks < PF; ++ks) ld(ks);
-#pragma unroll
-      for (int ks = 0; ks < C::KSM; ++ks) {
-        if (ks + PF < C::KSM) ld(ks + PF);
-        if (ks < C::KSQ) s = mfma32x32x16(qa[ks], kb[ks], s);
-        if (ks < C::KSV) dp = mfma32x32x16(da[ks], vb[ks], dp);
-        __builtin_amdgcn_sched_barrier(0);
+  auto tile_q = [&](int bi) { return (const bf16*)s_q + bi * (C::TQ_BYTES / 2); };
+  auto tile_do = [&](int bi) { return (const bf16*)s_do + bi * (C::TD_BYTES / 2); };
+
+  // steps 1 and 3 for this wave's M-tile: S = Q K^T, dP = dO V^T  ([q 32] x [kv 32]); operands
+  // are read PF k-steps ahead into distinct registers, one scheduling fence per k-step
+  auto gemm1 = [&](int bi, f32x16& s, f32x16& dp) {
+    const bf16* sq = tile_q(bi);
+    const bf16* sd = tile_do(bi);
+    s = f32x16{};
+    dp = f32x16{};
+    constexpr int PF = 2;
+    bf16x8 qa[C::KSQ], da[C::KSV], kb[C::KSQ], vb[C::KSV];
+    auto ld = [&](int ks) {
+      if (ks < C::KSQ) {
+        qa[ks] = *(const bf16x8*)(sq + arowq + 16 * ks);
+        if constexpr (C::WIDE)
+          kb[ks] = kreg[ks];
+        else
+          kb[ks] = *(const bf16x8*)(s_k + krow + 16 * ks);
       }
+      if (ks < C::KSV) {
+        da[ks] = *(const bf16x8*)(sd + arowd + 16 * ks);
+        if constexpr (C::WIDE)
+          vb[ks] = vreg[ks];
+        else
+          vb[ks] = *(const bf16x8*)(s_v + vrow + 16 * ks);
+      }
+    };
+#pragma unroll
+    for (int ks = 0; ks < PF; ++ks) ld(ks);
+#pragma unroll
+    for (int ks = 0; ks < C::KSM; ++ks) {
+      if (ks + PF < C::KSM) ld(ks + PF);
+      if (ks < C::KSQ) s = mfma32x32x16(qa[ks], kb[ks], s);
+      if (ks < C::KSV) dp = mfma32x32x16(da[ks], vb[ks], dp);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // steps 2 and 5: P = exp2(S*scale*log2e - lse2) (causal: 0 where key > query), dS = P (dP - D)
+  };
+  // steps 2 and 5 of step sp: P = exp2(S*scale*log2e - lse2) (causal: 0 where key > query),
+  // dS = P (dP - D), as bf16 A operands
+  auto softmax = [&](int sp, int bi, const f32x16& s, const f32x16& dp, bf16x8* pk, bf16x8* dsk) {
+    const int i0 = step_tile(sp) * BM;
+    const float* st = s_st + bi * 2 * BM + 32 * mt;
     const int jrel = jcol - i0 - 32 * mt;  // key j visible from M-tile row r iff jrel <= r
-    bf16x8 pk[2], dsk[2];
-    auto softmax = [&](auto masked) {
+    auto body = [&](auto masked) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const f32x4 lse = *(const f32x4*)(st + 8 * a4 + 4 * hh);
@@ -791,81 +781,112 @@ void fa_bwd_dkdv(MainArgs a) {
     const int kmin = kv0 + 32 * grp, qmin = i0 + 32 * mt;
     const bool full = !CAUSAL || (kmin + 31 <= qmin && (!WINDOW || qmin + 31 - a.window < kmin));
     if (full)
-      softmax(std::false_type{});
+      body(std::false_type{});
     else
-      softmax(std::true_type{});
-    // steps 7 and 6 over this M-tile: dV += P^T dO, dK += dS^T Q. k-step s2: its k-index e is MFMA
-    // row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4; the transpose reads fetch those rows.
-    // B operands are read PF MFMAs ahead; the dV and dK MFMAs alternate (independent chains).
-    if constexpr (C::WIDE) {
-      // swap with the partner wave: the M-tile 0 wave needs the partner's P (for dV), the other the
-      // partner's dS (for dK); then one GEMM over the step's 64 q rows, k-steps in row order
-      bf16x8* xs = (bf16x8*)(smem + C::OFF_X);
-      const int partner = grp + NG * (1 - mt);
-      xs[(w * 64 + lane) * 2] = mt == 0 ? dsk[0] : pk[0];
-      xs[(w * 64 + lane) * 2 + 1] = mt == 0 ? dsk[1] : pk[1];
-      __syncthreads();
-      bf16x8 am[4];  // A operand of k-step 2 u + s2: M-tile u, its k-step s2
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const bf16x8 own = mt == 0 ? pk[s2] : dsk[s2];
-        const bf16x8 other = xs[(partner * 64 + lane) * 2 + s2];
-        am[s2] = mt == 0 ? own : other;
-        am[2 + s2] = mt == 0 ? other : own;
+      body(std::true_type{});
+  };
+  // steps 7 and 6 over this M-tile: dV += P^T dO, dK += dS^T Q. k-step s2: its k-index e is MFMA
+  // row 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4; the transpose reads fetch those rows.
+  // B operands are read PF MFMAs ahead; the dV and dK MFMAs alternate (independent chains).
+  auto gemm2 = [&](int bi, const bf16x8* pk, const bf16x8* dsk) {
+    const bf16* sq = tile_q(bi);
+    const bf16* sd = tile_do(bi);
+    constexpr int NB = 2 * C::NTM, PF = 2;
+    bf16x8 bd[NB], bq[NB];
+    auto ld = [&](int i) {
+      const int s2 = i / C::NTM, nt = i % C::NTM;
+      if (nt < C::NTV) {
+        const int o = browd + 16 * s2 * QSV + 32 * nt;
+        bd[i] = concat(lds_read_tr4(sd + o), lds_read_tr4(sd + o + 2 * QSV));
       }
-      const int qs = mt == 0 ? QSV : QSQ;  // B: dO (for dV) or Q (for dK) rows of the step
-      const bf16* bsrc = mt == 0 ? sd : sq;
-      const int ntw = mt == 0 ? C::NTV : C::NTQ;
-      const int brow0 = (hh + 4 * (gi >> 2)) * qs + 16 * (g & 1) + 4 * (gi & 3);
-      constexpr int NB = 4 * C::NTM, PF = 2;
-      bf16x8 bw[NB];
-      auto ld = [&](int i) {
-        const int ksi = i / C::NTM, nt = i % C::NTM;
-        if (nt < ntw) {
-          const int o = brow0 + 16 * ksi * qs + 32 * nt;
-          bw[i] = concat(lds_read_tr4(bsrc + o), lds_read_tr4(bsrc + o + 2 * qs));
-        }
-      };
+      if (nt < C::NTQ) {
+        const int o = browq + 16 * s2 * QSQ + 32 * nt;
+        bq[i] = concat(lds_read_tr4(sq + o), lds_read_tr4(sq + o + 2 * QSQ));
+      }
+    };
 #pragma unroll
-      for (int i = 0; i < PF; ++i) ld(i);
+    for (int i = 0; i < PF; ++i) ld(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (i + PF < NB) ld(i + PF);
+      const int s2 = i / C::NTM, nt = i % C::NTM;
+      if (nt < C::NTV) acc_v[C::WIDE ? 0 : nt] = mfma32x32x16(pk[s2], bd[i], acc_v[C::WIDE ? 0 : nt]);
+      if (nt < C::NTQ) acc_k[C::WIDE ? 0 : nt] = mfma32x32x16(dsk[s2], bq[i], acc_k[C::WIDE ? 0 : nt]);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        if (i + PF < NB) ld(i + PF);
-        const int ksi = i / C::NTM, nt = i % C::NTM;
-        if (nt < ntw) acc_w[nt] = mfma32x32x16(am[ksi], bw[i], acc_w[nt]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      constexpr int NB = 2 * C::NTM, PF = 2;
-      bf16x8 bd[NB], bq[NB];
-      auto ld = [&](int i) {
-        const int s2 = i / C::NTM, nt = i % C::NTM;
-        if (nt < C::NTV) {
-          const int o = browd + 16 * s2 * QSV + 32 * nt;
-          bd[i] = concat(lds_read_tr4(sd + o), lds_read_tr4(sd + o + 2 * QSV));
-        }
-        if (nt < C::NTQ) {
-          const int o = browq + 16 * s2 * QSQ + 32 * nt;
-          bq[i] = concat(lds_read_tr4(sq + o), lds_read_tr4(sq + o + 2 * QSQ));
-        }
-      };
-#pragma unroll
-      for (int i = 0; i < PF; ++i) ld(i);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        if (i + PF < NB) ld(i + PF);
-        const int s2 = i / C::NTM, nt = i % C::NTM;
-        if (nt < C::NTV) acc_v[nt] = mfma32x32x16(pk[s2], bd[i], acc_v[nt]);
-        if (nt < C::NTQ) acc_k[nt] = mfma32x32x16(dsk[s2], bq[i], acc_k[nt]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
     }
+  };
+  // the wide heads' step 7 / step 6 over the whole step: swap with the partner wave (the M-tile 0
+  // wave needs the partner's P for dV, the other the partner's dS for dK), then one GEMM over the
+  // step's 64 q rows, k-steps in row order
+  auto gemm2_swap = [&](int bi, const bf16x8* pk, const bf16x8* dsk) {
+    bf16x8* xs = (bf16x8*)(smem + C::OFF_X);
+    const int partner = grp + NG * (1 - mt);
+    xs[(w * 64 + lane) * 2] = mt == 0 ? dsk[0] : pk[0];
+    xs[(w * 64 + lane) * 2 + 1] = mt == 0 ? dsk[1] : pk[1];
+    __syncthreads();
+    bf16x8 am[4];  // A operand of k-step 2 u + s2: M-tile u, its k-step s2
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16x8 own = mt == 0 ? pk[s2] : dsk[s2];
+      const bf16x8 other = xs[(partner * 64 + lane) * 2 + s2];
+      am[s2] = mt == 0 ? own : other;
+      am[2 + s2] = mt == 0 ? other : own;
+    }
+    const int qs = mt == 0 ? QSV : QSQ;  // B: dO (for dV) or Q (for dK) rows of the step
+    const bf16* bsrc = mt == 0 ? tile_do(bi) : tile_q(bi);
+    const int ntw = mt == 0 ? C::NTV : C::NTQ;
+    const int brow0 = (hh + 4 * (gi >> 2)) * qs + 16 * (g & 1) + 4 * (gi & 3);
+    constexpr int NB = 4 * C::NTM, PF = 2;
+    bf16x8 bw[NB];
+    auto ld = [&](int i) {
+      const int ksi = i / C::NTM, nt = i % C::NTM;
+      if (nt < ntw) {
+        const int o = brow0 + 16 * ksi * qs + 32 * nt;
+        bw[i] = concat(lds_read_tr4(bsrc + o), lds_read_tr4(bsrc + o + 2 * qs));
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < PF; ++i) ld(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (i + PF < NB) ld(i + PF);
+      const int ksi = i / C::NTM, nt = i % C::NTM;
+      if (nt < ntw) acc_w[C::WIDE ? nt : 0] = mfma32x32x16(am[ksi], bw[i], acc_w[C::WIDE ? nt : 0]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto wait_tiles = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's LDS-DMA transfers and loads have landed
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // all waves in step: tile sp + 1 loads while step sp runs; one barrier per step
+  f32x16 s, dp;
+  bf16x8 pk[2], dsk[2];
+  if (n_steps > 0) {
+    issue_tile(0, 0);
+    store_stats(0, load_stats(0));
+  }
+  wait_tiles();
+  __syncthreads();
+  for (int sp = 0, buf = 0; sp < n_steps; ++sp, buf ^= 1) {
+    const bool has_next = sp + 1 < n_steps;
+    float st_next = 0.f;
+    if (has_next) {
+      issue_tile(sp + 1, buf ^ 1);
+      st_next = load_stats(sp + 1);
+    }
+    gemm1(buf, s, dp);
+    softmax(sp, buf, s, dp, pk, dsk);
+    if constexpr (C::WIDE)
+      gemm2_swap(buf, pk, dsk);
+    else
+      gemm2(buf, pk, dsk);
     if (has_next) store_stats(buf ^ 1, st_next);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next tile's LDS-DMA has landed
-    __builtin_amdgcn_sched_barrier(0);
+    wait_tiles();
     __syncthreads();
   }
 
