@@ -2,11 +2,12 @@
 
     python -m attention_backward_fa_amd.build
 
-Two translation units, compiled in parallel and linked into one library that
+Three translation units, compiled in parallel and linked into one library that
 lands next to this file, where the binding looks for it:
   fa_bwd.hip       the C ABI and the kernels for head dims up to 128, with MFMA
                    accumulators in VGPRs (two waves per SIMD, 256 registers each);
-  fa_bwd_wide.hip  the kernels for head dims above 128 (one wave per SIMD), whose
+  fa_bwd_wide.hip, fa_bwd_wide192.hip
+                   the kernels for head dims above 128 (one wave per SIMD), whose
                    accumulators need the AGPRs as well.
 """
 from __future__ import annotations
@@ -25,6 +26,7 @@ CSRC = os.path.join(HERE, "csrc")
 UNITS = [
     ("fa_bwd.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),  # the softmax reads S and dP without AGPR copies
     ("fa_bwd_wide.hip", []),
+    ("fa_bwd_wide192.hip", []),
 ]
 
 

@@ -86,17 +86,18 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   return FA_BWD_OK;
 }
 
-// The kernels for the padded head dims: each dim rounded up to 64, 128 or 256, and a dim of 64 next
-// to one of 256 taken as 128.
-int padded_dim(int d) { return d <= 64 ? 64 : d <= 128 ? 128 : 256; }
+// The kernels for the padded head dims: each dim rounded up to 64, 128, 192 or 256, and a dim of 64
+// next to one above 128 taken as 128.
+int padded_dim(int d) { return d <= 64 ? 64 : d <= 128 ? 128 : d <= 192 ? 192 : 256; }
 
 fa::KernelSet pick_kernels(int d_qk, int d_v) {
   int pq = padded_dim(d_qk), pv = padded_dim(d_v);
-  if (pq == 256 || pv == 256) {
+  if (pq > 128 || pv > 128) {
     if (pq == 64) pq = 128;
     if (pv == 64) pv = 128;
   }
   const bool exact = d_qk == pq && d_v == pv && pq == pv;  // instantiated for equal padded dims
+  if (pq == 192 || pv == 192) return fa::wide192_kernel_set(pq, pv, exact);
   if (pq == 256 || pv == 256) return fa::wide_kernel_set(pq, pv, exact);
   if (pq == 64 && pv == 64) return exact ? fa::kernel_set<64, 64, true>() : fa::kernel_set<64, 64, false>();
   if (pq == 128 && pv == 128) return exact ? fa::kernel_set<128, 128, true>() : fa::kernel_set<128, 128, false>();

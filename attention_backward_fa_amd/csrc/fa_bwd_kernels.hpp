@@ -21,7 +21,7 @@
 // The recompute kernels and the forward also take grouped K/V heads, a
 // sliding window (each query sees keys (i - w, i]) and any head dims that are
 // multiples of 8 up to 256, separately for Q/K and for V/O/dO (latent
-// attention): they are compiled for padded dims DQ, DV in {64, 128, 256}, and
+// attention): they are compiled for padded dims DQ, DV in {64, 128, 192, 256}, and
 // the columns from a head dim up to its padded dim are loaded as zeros and
 // never stored.
 #pragma once

@@ -1,7 +1,8 @@
 // fa_bwd_launch.hpp -- launches of the recompute-form kernels (dK/dV, dQ) and of the forward for one
 // pair of padded head dims (DQ for Q and K, DV for V, O and dO). The pairs with a dim above 128 are
-// instantiated only in fa_bwd_wide.hip, which is compiled with MFMA accumulators allowed in the
-// AGPRs: their accumulators need more registers than the 256 VGPRs of one wave.
+// instantiated only in fa_bwd_wide.hip and fa_bwd_wide192.hip, which are compiled with MFMA
+// accumulators allowed in the AGPRs: their accumulators need more registers than the 256 VGPRs of
+// one wave.
 #pragma once
 #include "fa_bwd_kernels.hpp"
 
@@ -69,5 +70,8 @@ KernelSet kernel_set() {
 // The pairs (128, 256), (256, 128) and (256, 256), from fa_bwd_wide.hip; pq, pv are padded dims,
 // exact that the head dims equal them (pq = pv = 256).
 KernelSet wide_kernel_set(int pq, int pv, bool exact);
+// The pairs with a 192 (the other 128, 192 or 256), from fa_bwd_wide192.hip; exact: pq = pv = 192 and
+// the head dims equal them.
+KernelSet wide192_kernel_set(int pq, int pv, bool exact);
 
 }  // namespace fa

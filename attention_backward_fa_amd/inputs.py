@@ -74,8 +74,22 @@ CASES = {
     "sk16_t06": Case("sk16_t06", heads=4, head_dim=128, mask=MASK_NONE, seed=106, seqlens_q=[64] * 8, seqlens_kv=[64] * 8),
 }
 
+# the variants of the causal workload that the library also times (grouped K/V heads, a sliding
+# window, head dims other than 128); each keeps one 8192-token sequence
+CASES.update({
+    "causal_gqa": Case("causal_gqa", heads=32, head_dim=128, mask=MASK_CAUSAL, seed=6,
+                       seqlens_q=[8192], seqlens_kv=[8192], heads_kv=8),
+    "causal_window": Case("causal_window", heads=32, head_dim=128, mask=MASK_CAUSAL, seed=7,
+                          seqlens_q=[8192], seqlens_kv=[8192], window=1024),
+    "causal_d256": Case("causal_d256", heads=16, head_dim=256, mask=MASK_CAUSAL, seed=8,
+                        seqlens_q=[8192], seqlens_kv=[8192]),
+    "causal_mla": Case("causal_mla", heads=32, head_dim=192, mask=MASK_CAUSAL, seed=9,
+                       seqlens_q=[8192], seqlens_kv=[8192], head_dim_v=128),
+})
+
 # workload number -> case name, in the order the five synthetic workloads are listed
 WORKLOADS = ["tiny", "dense", "varlen", "causal", "longpad"]
+VARIANTS = ["causal_gqa", "causal_window", "causal_d256", "causal_mla"]
 
 
 def custom_case(name: str, heads: int, head_dim: int, mask: int, seed: int, seqlens_q, seqlens_kv=None,

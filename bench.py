@@ -46,23 +46,41 @@ METRIC = "FA-bwd TFLOP/s + % bf16 MFMA peak, S=8192 H=32 D=128 causal, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MASK_NAMES = {0: "none", 1: "padding", 2: "causal", 3: "padding_causal"}
 ALGORITHMS = {"default": 0, "single-pass": 1, "recompute": 2}
-# share of the 5-GEMM algorithmic FLOPs each kernel runs itself (S, dP, dV, dK, dQ are 2*Lq*Lk*d each)
-KERNEL_SHARE = {
-    1: {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_dq_cast": 0.0},
-    2: {"fa_bwd_pre": 0.0, "fa_bwd_dkdv": 0.8, "fa_bwd_dq": 0.6},
-}
+def kernel_share(algorithm: int, d: int, dv: int) -> dict:
+    """Share of the 5-GEMM algorithmic FLOPs each kernel runs itself. S = QK^T, dK, dQ contract or
+    produce the query/key head dim d, dP, dV the value head dim dv (2 * pairs * dim FLOPs each)."""
+    total = 3 * d + 2 * dv
+    if algorithm == 1:
+        return {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_dq_cast": 0.0}
+    # dK/dV kernel: S, dP, dV, dK; dQ kernel: S and dP again, dQ
+    return {"fa_bwd_pre": 0.0, "fa_bwd_dkdv": (2 * d + 2 * dv) / total, "fa_bwd_dq": (2 * d + dv) / total}
+
+
+def visible_pairs(lq: int, lk: int, causal: bool, window: int) -> float:
+    """(query, key) pairs a sequence's FLOPs count: Lq * Lk, halved under a causal mask (the metric's
+    convention), counted exactly under a sliding window (query i sees keys (i - window, i])."""
+    if window > 0:
+        import numpy as np
+        i = np.arange(lq)
+        hi = np.minimum(i, lk - 1)
+        lo = np.maximum(0, i - window + 1)
+        return float(np.maximum(0, hi - lo + 1).sum())
+    return lq * lk / 2 if causal else float(lq * lk)
 
 
 def algorithmic_flops(inp) -> float:
-    """10 * Lq * Lk * d per (sequence, head); half of that under a causal mask."""
+    """The five GEMMs of the backward over the visible pairs: 2 * pairs * (3 d + 2 d_v) per head, which is
+    10 * Lq * Lk * d (halved when causal) when d_v = d."""
     causal = inp["mask"] in (2, 3)
-    d = inp["q"].shape[2]
-    h = inp["q"].shape[1]
-    total = 0.0
-    for lq, lk in zip(inp["seqlens_q"], inp["seqlens_kv"]):
-        f = 10.0 * lq * lk * d * h
-        total += f / 2 if causal else f
-    return total
+    d, dv, h = inp["q"].shape[2], inp["v"].shape[2], inp["q"].shape[1]
+    return sum(2.0 * visible_pairs(lq, lk, causal, inp.get("window", 0)) * (3 * d + 2 * dv) * h
+               for lq, lk in zip(inp["seqlens_q"], inp["seqlens_kv"]))
+
+
+def forward_flops(inp) -> float:
+    """The forward's two GEMMs (S = QK^T over d, O = PV over d_v) over the same pairs."""
+    d, dv = inp["q"].shape[2], inp["v"].shape[2]
+    return algorithmic_flops(inp) * (d + dv) / (3 * d + 2 * dv)
 
 
 def segments(inp):
@@ -78,21 +96,24 @@ def segments(inp):
 
 def torch_forward_stats(inp, device, block=4096):
     """Input preparation: O (bf16), m, l (fp32) from a plain fp32 softmax-attention
-    forward in torch on the GPU, query rows in blocks. Rows outside every
-    sequence get O = 0, m = 0, l = 1."""
+    forward in torch on the GPU, query rows in blocks (grouped K/V heads repeated per
+    query head; the window, when set, masks keys at or before i - window). Rows outside
+    every sequence get O = 0, m = 0, l = 1."""
     import torch
     q, k, v = inp["q"], inp["k"], inp["v"]
     tq, h, d = q.shape
+    group = h // k.shape[1]
     scale = inp["scale"]
-    causal = inp["mask"] in (2, 3)
+    window = inp.get("window", 0)
+    causal = inp["mask"] in (2, 3) or window > 0
     o = torch.zeros((tq, h, v.shape[2]), dtype=torch.bfloat16, device=device)
     m = torch.zeros((tq, h), dtype=torch.float32, device=device)
     l = torch.ones((tq, h), dtype=torch.float32, device=device)
     for qs, lq, ks, lk in segments(inp):
         if lq <= 0 or lk <= 0:
             continue
-        kt = k[ks:ks + lk].to(device).float().permute(1, 2, 0).contiguous()   # [H, d, Lk]
-        vb = v[ks:ks + lk].to(device).float().permute(1, 0, 2).contiguous()   # [H, Lk, d]
+        kt = k[ks:ks + lk].to(device).float().permute(1, 2, 0).repeat_interleave(group, 0).contiguous()  # [H, d, Lk]
+        vb = v[ks:ks + lk].to(device).float().permute(1, 0, 2).repeat_interleave(group, 0).contiguous()  # [H, Lk, dv]
         for i0 in range(0, lq, block):
             i1 = min(lq, i0 + block)
             qb = q[qs + i0:qs + i1].to(device).float().permute(1, 0, 2).contiguous()  # [H, n, d]
@@ -100,7 +121,8 @@ def torch_forward_stats(inp, device, block=4096):
             if causal:
                 rows = torch.arange(i0, i1, device=device)[:, None]
                 cols = torch.arange(lk, device=device)[None, :]
-                s.masked_fill_((cols > rows)[None], float("-inf"))
+                hidden = (cols > rows) | (cols <= rows - window) if window > 0 else cols > rows
+                s.masked_fill_(hidden[None], float("-inf"))
             mb = s.amax(dim=-1)
             e = torch.exp(s - mb[..., None])
             del s
@@ -111,6 +133,22 @@ def torch_forward_stats(inp, device, block=4096):
             m[qs + i0:qs + i1] = mb.T
             l[qs + i0:qs + i1] = lb.T
     return o, m, l
+
+
+def describe(name: str, inp) -> str:
+    """The workload's name and sizes, with the variant settings that differ from the plain case."""
+    seqlens = sorted(set(inp["seqlens_q"]))
+    heads, d = inp["q"].shape[1], inp["q"].shape[2]
+    text = (f"{name}: batch {inp['batch']}, {heads} heads, "
+            f"seqlens {seqlens if len(seqlens) < 5 else str(len(inp['seqlens_q'])) + ' varlen'}, "
+            f"head_dim {d}, mask {MASK_NAMES[inp['mask']]}")
+    if inp["k"].shape[1] != heads:
+        text += f", {inp['k'].shape[1]} K/V heads"
+    if inp["v"].shape[2] != d:
+        text += f", value head_dim {inp['v'].shape[2]}"
+    if inp.get("window", 0):
+        text += f", window {inp['window']}"
+    return text
 
 
 def make_workload(name: str, device):
@@ -207,7 +245,9 @@ def cpu_baseline(inp, dev, target_s: float = 15.0):
     o, m, l = dev["o"].float().cpu().numpy(), dev["m"].cpu().numpy(), dev["l"].cpu().numpy()
     q, k, v, do = (inp[x].float().numpy() for x in ("q", "k", "v", "do"))
     causal = inp["mask"] in (2, 3)
-    d, heads = q.shape[2], q.shape[1]
+    window = inp.get("window", 0)
+    d, dv, heads = q.shape[2], v.shape[2], q.shape[1]
+    group = heads // k.shape[1]
     pairs = [(b, h) for b in range(len(inp["seqlens_q"])) for h in range(heads)]
     segs = segments(inp)
     done, flops, elapsed = [], 0.0, 0.0
@@ -215,12 +255,12 @@ def cpu_baseline(inp, dev, target_s: float = 15.0):
         qs, lq, ks, lk = segs[b]
         if lq <= 0 or lk <= 0:
             continue
+        hk = h // group
         t0 = time.perf_counter()
-        oracle.backward_head(q[qs:qs + lq, h], k[ks:ks + lk, h], v[ks:ks + lk, h], o[qs:qs + lq, h],
-                             do[qs:qs + lq, h], m[qs:qs + lq, h], l[qs:qs + lq, h], inp["scale"], causal)
+        oracle.backward_head(q[qs:qs + lq, h], k[ks:ks + lk, hk], v[ks:ks + lk, hk], o[qs:qs + lq, h],
+                             do[qs:qs + lq, h], m[qs:qs + lq, h], l[qs:qs + lq, h], inp["scale"], causal, window)
         elapsed += time.perf_counter() - t0
-        f = 10.0 * lq * lk * d
-        flops += f / 2 if causal else f
+        flops += 2.0 * visible_pairs(lq, lk, causal, window) * (3 * d + 2 * dv)
         done.append((b, h))
         if elapsed >= target_s:
             break
@@ -239,12 +279,13 @@ def bench_forward(args, device):
     print(f"[bench] forward, preparing workload {args.workload}", file=sys.stderr, flush=True)
     inp = inputs.make(args.workload)
     dev = {key: inp[key].to(device) for key in ("q", "k", "v", "cu_q", "cu_kv")}
-    flops = algorithmic_flops(inp) * 0.4
+    flops = forward_flops(inp)
     tq, heads, d = inp["q"].shape
-    op = binding.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0])
+    op = binding.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0],
+                       num_heads_kv=inp["k"].shape[1], window=inp["window"], head_dim_v=inp["v"].shape[2])
     if args.plan:
         op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
-    o = torch.empty_like(dev["q"])
+    o = torch.empty((tq, heads, inp["v"].shape[2]), dtype=torch.bfloat16, device=device)
     m = torch.empty((tq, heads), dtype=torch.float32, device=device)
     l = torch.empty((tq, heads), dtype=torch.float32, device=device)
 
@@ -275,9 +316,7 @@ def bench_forward(args, device):
         "metric": "FA-fwd TFLOP/s (forward producing O, m, l), % bf16 MFMA peak", "value": round(tflops, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{args.workload}: batch {inp['batch']}, {heads} heads, "
-                               f"seqlens {seqlens if len(seqlens) < 5 else str(len(inp['seqlens_q'])) + ' varlen'}, "
-                               f"head_dim {d}, mask {MASK_NAMES[inp['mask']]}", "path": "forward",
+        "config": {"workload": describe(args.workload, inp), "path": "forward",
                    "algorithmic_flops": flops},
         "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {"fa_fwd_fill": round(fill_ms, 5), "fa_fwd": round(fwd_ms, 5)},
@@ -328,7 +367,7 @@ def main():
     tq, heads, d = inp["q"].shape
     algo = ALGORITHMS[args.algorithm]
     op = binding.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0],
-                       algo)
+                       algo, num_heads_kv=inp["k"].shape[1], window=inp["window"], head_dim_v=inp["v"].shape[2])
     algo_used = 1 if algo == 1 else 2
     if args.plan:  # host-side longest-first schedule from the (host) sequence offsets
         op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
@@ -356,17 +395,15 @@ def main():
     finite = all(bool(torch.isfinite(x).all()) for x in (dq, dk, dv))
     op.close()
     print(f"[bench] {args.steps} steps: {ms:.4f} ms/step", file=sys.stderr, flush=True)
-    names = list(KERNEL_SHARE[algo_used])
+    shares = kernel_share(algo_used, d, inp["v"].shape[2])
+    names = list(shares)
     kern_ms = {n: sum(s[i] for s in stages) / len(stages) for i, n in enumerate(names)}
     dom = max(kern_ms, key=kern_ms.get)
     tflops = flops / (ms * 1e-3) / 1e12
-    dom_flops = flops * KERNEL_SHARE[algo_used][dom]
+    dom_flops = flops * shares[dom]
     achieved = dom_flops / (kern_ms[dom] * 1e-3) / 1e12
 
-    seqlens = sorted(set(inp["seqlens_q"]))
-    config = {"workload": f"{args.workload}: batch {inp['batch']}, {heads} heads, "
-                          f"seqlens {seqlens if len(seqlens) < 5 else str(len(inp['seqlens_q'])) + ' varlen'}, "
-                          f"head_dim {d}, mask {MASK_NAMES[inp['mask']]}",
+    config = {"workload": describe(args.workload, inp),
               "batch": inp["batch"], "heads": heads, "head_dim": d, "seq_len": inp["max_seqlen_q"],
               "total_tokens": tq, "mask": MASK_NAMES[inp["mask"]], "seed": inp["seed"],
               "algorithmic_flops": flops,

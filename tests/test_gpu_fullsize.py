@@ -23,6 +23,9 @@ pytestmark = pytest.mark.gpu
 
 FULL = ["dense", "varlen", "causal", "longpad"]
 ALGOS = {"default": B.FA_BWD_ALGO_DEFAULT, "singlepass": B.FA_BWD_ALGO_SINGLE_PASS}
+# the workloads with grouped K/V heads, a window or other head dims run the recompute form only
+VARIANTS = ["causal_gqa", "causal_window", "causal_d256", "causal_mla"]
+BACKWARD = [(n, a) for n in FULL for a in ALGOS] + [(n, "default") for n in VARIANTS]
 
 _cache = {}
 
@@ -57,14 +60,15 @@ def _pairs(inp, rng):
     return sorted(pairs)
 
 
-@pytest.mark.parametrize("algo", list(ALGOS))
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name,algo", BACKWARD)
 def test_fullsize_sampled(name, algo):
     inp, dev, host = _workload(name)
     tq, heads, d = inp["q"].shape
     tk = inp["k"].shape[0]
-    print(f"[fullsize] {name} ({algo}): T_q={tq} T_kv={tk} H={heads} d={d} mask={inp['mask']}", flush=True)
-    with B.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, tk, ALGOS[algo]) as op:
+    print(f"[fullsize] {name} ({algo}): T_q={tq} T_kv={tk} H={heads} H_kv={inp['k'].shape[1]} d={d} "
+          f"d_v={inp['v'].shape[2]} mask={inp['mask']} window={inp['window']}", flush=True)
+    with B.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, tk, ALGOS[algo],
+                 num_heads_kv=inp["k"].shape[1], window=inp["window"], head_dim_v=inp["v"].shape[2]) as op:
         dq, dk, dv = op.run(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["m"], dev["l"], dev["cu_q"],
                             dev["cu_kv"], inp["scale"], inp["mask"])
         torch.cuda.synchronize()
@@ -86,10 +90,11 @@ def test_fullsize_sampled(name, algo):
         qr, kr = _rows(lq, rng), _rows(lk, rng)
         rq, rk, rv = oracle.backward_rows(inp["q"], inp["k"], inp["v"], host["o"], inp["do"], host["m"], host["l"],
                                           inp["cu_q"], inp["cu_kv"], inp["scale"], inp["mask"], b, h, qr, kr,
-                                          inp["max_seqlen_q"], inp["max_seqlen_kv"])
+                                          inp["max_seqlen_q"], inp["max_seqlen_kv"], inp["window"])
+        hk = h // (heads // inp["k"].shape[1])  # the K/V head whose dK/dV rows these are
         got["dq"].append(dq[[qs + r for r in qr], h].float().cpu().numpy())
-        got["dk"].append(dk[[ks + r for r in kr], h].float().cpu().numpy())
-        got["dv"].append(dv[[ks + r for r in kr], h].float().cpu().numpy())
+        got["dk"].append(dk[[ks + r for r in kr], hk].float().cpu().numpy())
+        got["dv"].append(dv[[ks + r for r in kr], hk].float().cpu().numpy())
         ref["dq"].append(rq)
         ref["dk"].append(rk)
         ref["dv"].append(rv)

@@ -3,7 +3,7 @@ any multiple of 8 up to 256, and a value head dim (V, O, dO, dV) that differs fr
 one (latent attention). Every valid row is compared with the fp64 oracle on the same seeded inputs,
 with the tolerance of the other parity tests; rows outside every sequence must be exactly zero.
 
-The kernels run on head dims padded to 64, 128 or 256 with zero columns, so the cases cover each
+The kernels run on head dims padded to 64, 128, 192 or 256 with zero columns, so the cases cover each
 pair of padded dims the library instantiates, with head dims both equal to and below the padded
 one, ragged lengths, every mask type, grouped K/V heads and a window.
 """
@@ -34,10 +34,16 @@ CASES = [
     # padded (256, 256)
     I.custom_case("d256_causal", 2, 256, CAUSAL, 308, [300, 129]),
     I.custom_case("d256_none_kv_longer", 2, 256, NONE, 309, [100, 64], [170, 200]),
+    I.custom_case("d232_causal", 2, 232, CAUSAL, 319, [150, 75]),
+    # padded (192, 192)
     I.custom_case("d160_padded", 2, 160, PAD, 310, [200, 90], padded_len=224),
     I.custom_case("d192_causal", 2, 192, CAUSAL, 311, [257, 31]),
-    # padded (256, 128) and (128, 256)
+    # padded (192, 128), (128, 192), (256, 192), (192, 256)
     I.custom_case("mla_192_128_causal", 4, 192, CAUSAL, 312, [260, 111], head_dim_v=128),
+    I.custom_case("mla_128_176_none", 2, 128, NONE, 320, [99, 180], head_dim_v=176),
+    I.custom_case("mla_256_160_causal", 2, 256, CAUSAL, 321, [201], head_dim_v=160),
+    I.custom_case("mla_184_256_padded", 2, 184, PAD, 322, [120, 64], padded_len=128, head_dim_v=256),
+    # padded (256, 128) and (128, 256)
     I.custom_case("mla_256_64_none", 2, 256, NONE, 313, [140], head_dim_v=64),
     I.custom_case("mla_128_256_causal", 2, 128, CAUSAL, 314, [222, 70], head_dim_v=256),
     I.custom_case("mla_48_200_padded_causal", 2, 48, PADC, 315, [130, 60], padded_len=144, head_dim_v=200),
@@ -86,7 +92,7 @@ def test_forward_head_dims(case):
 
 def test_wide_head_dims_bitwise_reproducible():
     """The wide kernels swap P and dS through LDS and use no atomics: repeated runs agree bitwise."""
-    inp = I.make(CASES[11])
+    inp = I.make(next(c for c in CASES if c.name == "mla_192_128_causal"))
     o, m, l = P.oracle_stats(inp)
     a = P.run_gpu(inp, o, m, l)
     b = P.run_gpu(inp, o, m, l)
