@@ -962,9 +962,10 @@ template <int DQ, int DV>
 struct DqCfg {
   static constexpr bool WIDE = DQ > 128 || DV > 128;
   static constexpr int WPE = WIDE ? 1 : 2;       // waves per SIMD
-  static constexpr int BQ = 128;                 // q rows per workgroup (32 per wave)
+  static constexpr int NW = 4;                   // waves, 32 q rows each
+  static constexpr int NT = 64 * NW;
+  static constexpr int BQ = 32 * NW;             // q rows per workgroup
   static constexpr int BK = 64;                  // kv rows per step
-  static constexpr int NW = 4;
   static constexpr int KSQ = DQ / 16, KSV = DV / 16, KSM = KSQ > KSV ? KSQ : KSV;  // MFMA k-steps
   static constexpr int NTQ = DQ / 32, NTV = DV / 32;                                // 32-wide tiles
   static constexpr int QSQ = DQ + 8, QSV = DV + 8;  // padded row strides of the K and V tiles
@@ -1022,7 +1023,7 @@ struct KvTileLoader {
 // dP^T = V dO^T with the forward's statistics (steps 1-5 of the per-tile math), and
 // accumulates dQ^T = K^T dS^T (step 8) in registers; dQ is written once, in bf16.
 template <int DQ, int DV, bool CAUSAL, bool WINDOW, bool EXACT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+__global__ __attribute__((amdgpu_flat_work_group_size(DqCfg<DQ, DV>::NT, DqCfg<DQ, DV>::NT),
                           amdgpu_waves_per_eu(DqCfg<DQ, DV>::WPE, DqCfg<DQ, DV>::WPE)))
 void fa_bwd_dq(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -1089,7 +1090,7 @@ void fa_bwd_dq(MainArgs a) {
 
   {  // zero the K and V buffers once (rows past the sequence are masked, but must be finite)
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int o = tid * 16; o < C::LDS_BYTES; o += 256 * 16) *(u32x4*)(smem + o) = z;
+    for (int o = tid * 16; o < C::LDS_BYTES; o += C::NT * 16) *(u32x4*)(smem + o) = z;
   }
   __syncthreads();
 
@@ -1264,7 +1265,7 @@ __global__ __launch_bounds__(256) void fa_fwd_fill(FwdArgs a) {
 // through LDS, each lane owns one query row (its MFMA column), so the running maximum, the row sum
 // and the rescaling of its O row are per-lane values combined with the partner lane (lane ^ 32).
 template <int DQ, int DV, bool CAUSAL, bool WINDOW, bool EXACT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+__global__ __attribute__((amdgpu_flat_work_group_size(DqCfg<DQ, DV>::NT, DqCfg<DQ, DV>::NT),
                           amdgpu_waves_per_eu(DqCfg<DQ, DV>::WPE, DqCfg<DQ, DV>::WPE)))
 void fa_fwd(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -1319,7 +1320,7 @@ void fa_fwd(FwdArgs a) {
 
   {  // zero the K and V buffers once (keys past the sequence are masked, but must be finite)
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int o = tid * 16; o < C::LDS_BYTES; o += 256 * 16) *(u32x4*)(smem + o) = z;
+    for (int o = tid * 16; o < C::LDS_BYTES; o += C::NT * 16) *(u32x4*)(smem + o) = z;
   }
   __syncthreads();
 

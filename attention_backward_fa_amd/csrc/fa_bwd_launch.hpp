@@ -32,7 +32,7 @@ struct Recompute {
   }
 
   static void dq(const MainArgs& a, int64_t items, hipStream_t s) {
-    const dim3 grid((unsigned)(a.sched ? items : q_blocks(a.max_seqlen_q, a.H, a.batch))), block(256);
+    const dim3 grid((unsigned)(a.sched ? items : q_blocks(a.max_seqlen_q, a.H, a.batch))), block(DqCfg<DQ, DV>::NT);
     if (a.window > 0)
       fa_bwd_dq<DQ, DV, true, true, EXACT><<<grid, block, 0, s>>>(a);
     else if (a.causal)
@@ -42,7 +42,7 @@ struct Recompute {
   }
 
   static void fwd(const FwdArgs& a, bool causal, int64_t items, hipStream_t s) {
-    const dim3 grid((unsigned)(a.sched ? items : q_blocks(a.max_seqlen_q, a.H, a.batch))), block(256);
+    const dim3 grid((unsigned)(a.sched ? items : q_blocks(a.max_seqlen_q, a.H, a.batch))), block(DqCfg<DQ, DV>::NT);
     if (a.window > 0)
       fa_fwd<DQ, DV, true, true, EXACT><<<grid, block, 0, s>>>(a);
     else if (causal)
