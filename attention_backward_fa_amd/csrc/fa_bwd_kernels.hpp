@@ -927,25 +927,40 @@ void fa_bwd_dkdv(MainArgs a) {
       store_dk(acc_w);
   } else {
     // combine the two M-tiles' partial sums through LDS, laid out as [NG][NTQ] partial dK tiles, then
-    // [NG][NTV] partial dV tiles, 64 lanes each: the M-tile 0 wave keeps dV and takes the partner's
-    // dV, the M-tile 1 wave keeps dK and takes the partner's dK; each writes the half its partner needs
-    f32x16* part_k = (f32x16*)(smem) + (size_t)grp * C::NTQ * 64 + lane;
-    f32x16* part_v = (f32x16*)(smem) + (size_t)(NG * C::NTQ + grp * C::NTV) * 64 + lane;
+    // [NG][NTV] partial dV tiles, each as 4 quarters of 64 lanes x 16 bytes (lane-contiguous, so the
+    // 16-byte accesses hit distinct banks): the M-tile 0 wave keeps dV and takes the partner's dV, the
+    // M-tile 1 wave keeps dK and takes the partner's dK; each writes the half its partner needs
+    f32x4* part_k = (f32x4*)(smem) + (size_t)grp * C::NTQ * 256 + lane;
+    f32x4* part_v = (f32x4*)(smem) + (size_t)(NG * C::NTQ + grp * C::NTV) * 256 + lane;
+    auto put = [&](f32x4* dst, const f32x16& x) {
+      dst[0] = __builtin_shufflevector(x, x, 0, 1, 2, 3);
+      dst[64] = __builtin_shufflevector(x, x, 4, 5, 6, 7);
+      dst[128] = __builtin_shufflevector(x, x, 8, 9, 10, 11);
+      dst[192] = __builtin_shufflevector(x, x, 12, 13, 14, 15);
+    };
+    auto add = [&](f32x16& x, const f32x4* src) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 y = src[64 * q4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * q4 + e] += y[e];
+      }
+    };
     if (mt == 0) {
 #pragma unroll
-      for (int nt = 0; nt < C::NTQ; ++nt) part_k[nt * 64] = acc_k[nt];
+      for (int nt = 0; nt < C::NTQ; ++nt) put(part_k + nt * 256, acc_k[nt]);
     } else {
 #pragma unroll
-      for (int nt = 0; nt < C::NTV; ++nt) part_v[nt * 64] = acc_v[nt];
+      for (int nt = 0; nt < C::NTV; ++nt) put(part_v + nt * 256, acc_v[nt]);
     }
     __syncthreads();
     if (mt == 0) {
 #pragma unroll
-      for (int nt = 0; nt < C::NTV; ++nt) acc_v[nt] += part_v[nt * 64];
+      for (int nt = 0; nt < C::NTV; ++nt) add(acc_v[nt], part_v + nt * 256);
       store_dv(acc_v);
     } else {
 #pragma unroll
-      for (int nt = 0; nt < C::NTQ; ++nt) acc_k[nt] += part_k[nt * 64];
+      for (int nt = 0; nt < C::NTQ; ++nt) add(acc_k[nt], part_k + nt * 256);
       store_dk(acc_k);
     }
   }
