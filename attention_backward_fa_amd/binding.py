@@ -25,6 +25,7 @@ FA_BWD_ERR_HIP = 4
 FA_BWD_ALGO_DEFAULT = 0
 FA_BWD_ALGO_SINGLE_PASS = 1
 FA_BWD_ALGO_RECOMPUTE_DQ = 2
+FA_BWD_ALGO_SPLIT_REDUCE = 3
 
 FA_BWD_MASK_NONE = 0
 FA_BWD_MASK_PADDING = 1

@@ -14,9 +14,10 @@
 
 struct fa_bwd_handle {
   fa_bwd_desc desc;
-  bool single_pass;  // FA_BWD_ALGO_SINGLE_PASS (else recompute form)
+  bool single_pass;  // the single-pass main kernel: FA_BWD_ALGO_SINGLE_PASS or FA_BWD_ALGO_SPLIT_REDUCE
+  bool split;        // FA_BWD_ALGO_SPLIT_REDUCE: dQ partials per split, then fa_bwd_split_reduce
   int device;
-  float* dq_acc;  // [H][total_q][head_dim]
+  float* dq_acc;  // [H][total_q][head_dim] (atomics) or [kSplits][H][total_q][head_dim] (split)
   float* lse2;    // [H][total_q]
   float* dvec;    // [H][total_q]
   bool profiling;
@@ -60,16 +61,16 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
     return FA_BWD_ERR_INVALID_ARGUMENT;
   const int32_t dv = d->head_dim_v == 0 ? d->head_dim : d->head_dim_v;
   if (!head_dim_ok(d->head_dim) || !head_dim_ok(dv)) return FA_BWD_ERR_UNSUPPORTED;
+  if (d->algorithm < FA_BWD_ALGO_DEFAULT || d->algorithm > FA_BWD_ALGO_SPLIT_REDUCE) return FA_BWD_ERR_INVALID_ARGUMENT;
+  const bool single = d->algorithm == FA_BWD_ALGO_SINGLE_PASS || d->algorithm == FA_BWD_ALGO_SPLIT_REDUCE;
   // the single-pass kernels exist for equal head dims of 64 and 128
-  if (d->algorithm == FA_BWD_ALGO_SINGLE_PASS && (dv != d->head_dim || (d->head_dim != 64 && d->head_dim != 128)))
-    return FA_BWD_ERR_UNSUPPORTED;
+  if (single && (dv != d->head_dim || (d->head_dim != 64 && d->head_dim != 128))) return FA_BWD_ERR_UNSUPPORTED;
   const int32_t hkv = d->num_heads_kv == 0 ? d->num_heads : d->num_heads_kv;
   if (hkv < 1 || d->num_heads % hkv != 0) return FA_BWD_ERR_INVALID_ARGUMENT;
   // the single-pass form owns one (kv tile, head) per workgroup; grouped K/V heads need the recompute form
-  if (d->algorithm == FA_BWD_ALGO_SINGLE_PASS && hkv != d->num_heads) return FA_BWD_ERR_UNSUPPORTED;
+  if (single && hkv != d->num_heads) return FA_BWD_ERR_UNSUPPORTED;
   if (d->window < 0) return FA_BWD_ERR_INVALID_ARGUMENT;
-  if (d->algorithm == FA_BWD_ALGO_SINGLE_PASS && d->window > 0) return FA_BWD_ERR_UNSUPPORTED;
-  if (d->algorithm < FA_BWD_ALGO_DEFAULT || d->algorithm > FA_BWD_ALGO_RECOMPUTE_DQ) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (single && d->window > 0) return FA_BWD_ERR_UNSUPPORTED;
   // index arithmetic stays in int64; grids must fit the launch limits
   const int64_t rows = (d->total_q > d->total_kv ? d->total_q : d->total_kv);
   if (rows > (int64_t(1) << 40) / d->num_heads) return FA_BWD_ERR_INVALID_ARGUMENT;
@@ -79,7 +80,7 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   if ((int64_t)d->num_heads * dmax * 2 * 128 >= (int64_t(1) << 30)) return FA_BWD_ERR_INVALID_ARGUMENT;
   const int64_t kv_tiles = (d->max_seqlen_kv + 63) / 64;  // the smallest kv tile of any kernel
   if (kv_tiles * d->num_heads * d->batch > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
-  const int64_t q_tiles = (d->max_seqlen_q + 127) / 128;
+  const int64_t q_tiles = (d->max_seqlen_q + 63) / 64;  // the split reduce's 64-row blocks
   if (q_tiles * d->num_heads * d->batch > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
   const int64_t rows_per_block = 256 / threads_per_row(d->head_dim, dv);
   if ((rows * d->num_heads + rows_per_block - 1) / rows_per_block > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
@@ -147,13 +148,21 @@ void launch_rows(int tpr, dim3 grid, hipStream_t stream, const Args& a) {
   }
 }
 
-template <int D>
+// single-pass main kernel: one workgroup per (kv tile, head, sequence), or per (split, head, sequence)
+template <int D, bool SPLIT>
 void launch_single_pass(const fa::MainArgs& ma, bool causal, hipStream_t stream) {
-  const dim3 grid((unsigned)((ma.max_seqlen_kv + fa::MainCfg<D>::BN - 1) / fa::MainCfg<D>::BN * ma.H * ma.batch));
+  const int64_t first = SPLIT ? fa::kSplits : (ma.max_seqlen_kv + fa::MainCfg<D>::BN - 1) / fa::MainCfg<D>::BN;
+  const dim3 grid((unsigned)(first * ma.H * ma.batch));
   if (causal)
-    fa::fa_bwd_main<D, true, true><<<grid, dim3(256), 0, stream>>>(ma);
+    fa::fa_bwd_main<D, true, SPLIT><<<grid, dim3(256), 0, stream>>>(ma);
   else
-    fa::fa_bwd_main<D, false, true><<<grid, dim3(256), 0, stream>>>(ma);
+    fa::fa_bwd_main<D, false, SPLIT><<<grid, dim3(256), 0, stream>>>(ma);
+}
+
+template <int D>
+void launch_split_reduce(const fa::MainArgs& ma, hipStream_t stream) {
+  const dim3 grid((unsigned)((ma.max_seqlen_q + 63) / 64 * ma.H * ma.batch));
+  hipLaunchKernelGGL(fa::fa_bwd_split_reduce<D>, grid, dim3(256), 0, stream, ma);
 }
 
 template <int D>
@@ -181,8 +190,9 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   pa.cu_kv = cu_kv;
   pa.lse2 = h->lse2;
   pa.dvec = h->dvec;
-  pa.dq_acc = h->single_pass ? h->dq_acc : nullptr;
-  pa.dq = h->single_pass ? nullptr : static_cast<bf16*>(dq);
+  const bool atomics = h->single_pass && !h->split;
+  pa.dq_acc = atomics ? h->dq_acc : nullptr;           // zeroed for the atomics
+  pa.dq = atomics ? nullptr : static_cast<bf16*>(dq);  // rows outside every sequence zeroed
   pa.dk = static_cast<bf16*>(dk);
   pa.dv = static_cast<bf16*>(dv);
   pa.total_q = d.total_q;
@@ -242,9 +252,9 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.sched = planned ? h->sched : nullptr;
   if (h->single_pass) {  // head_dim == head_dim_v, 64 or 128 (checked at create)
     if (d.head_dim == 128)
-      launch_single_pass<128>(ma, causal, stream);
+      h->split ? launch_single_pass<128, true>(ma, causal, stream) : launch_single_pass<128, false>(ma, causal, stream);
     else
-      launch_single_pass<64>(ma, causal, stream);
+      h->split ? launch_single_pass<64, true>(ma, causal, stream) : launch_single_pass<64, false>(ma, causal, stream);
   } else if (!planned || h->n_kv_items > 0) {
     ks.dkdv(ma, h->n_kv_items, stream);
   }
@@ -252,10 +262,10 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return FA_BWD_ERR_HIP;
 
   if (h->single_pass) {
-    if (d.head_dim == 128)
-      launch_cast<128>(ma, stream);
+    if (h->split)
+      d.head_dim == 128 ? launch_split_reduce<128>(ma, stream) : launch_split_reduce<64>(ma, stream);
     else
-      launch_cast<64>(ma, stream);
+      d.head_dim == 128 ? launch_cast<128>(ma, stream) : launch_cast<64>(ma, stream);
   } else if (!planned || h->n_q_items > 0) {
     ma.sched = planned ? h->sched + 2 * h->n_kv_items : nullptr;
     ks.dq(ma, h->n_q_items, stream);
@@ -417,13 +427,14 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
   h->desc = *desc;
   if (h->desc.num_heads_kv == 0) h->desc.num_heads_kv = desc->num_heads;
   if (h->desc.head_dim_v == 0) h->desc.head_dim_v = desc->head_dim;
-  h->single_pass = desc->algorithm == FA_BWD_ALGO_SINGLE_PASS;
+  h->single_pass = desc->algorithm == FA_BWD_ALGO_SINGLE_PASS || desc->algorithm == FA_BWD_ALGO_SPLIT_REDUCE;
+  h->split = desc->algorithm == FA_BWD_ALGO_SPLIT_REDUCE;
   if (hipGetDevice(&h->device) != hipSuccess) {
     delete h;
     return FA_BWD_ERR_HIP;
   }
   const size_t stats = (size_t)desc->total_q * desc->num_heads;
-  const size_t acc = stats * desc->head_dim;
+  const size_t acc = stats * desc->head_dim * (h->split ? fa::kSplits : 1);
   if ((h->single_pass && hipMalloc(&h->dq_acc, acc * sizeof(float)) != hipSuccess) ||
       hipMalloc(&h->lse2, stats * sizeof(float)) != hipSuccess ||
       hipMalloc(&h->dvec, stats * sizeof(float)) != hipSuccess) {

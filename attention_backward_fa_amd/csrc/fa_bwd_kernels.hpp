@@ -138,6 +138,10 @@ struct MainArgs {
   const int* sched;  // recompute kernels: (tile, sequence * heads + head) per workgroup, or null (dense grid)
 };
 
+// Splits of the split-and-reduce form: workgroups per (head, sequence), each with its own fp32 dQ
+// buffer; split s takes the kv tiles s, s + kSplits, ...
+constexpr int kSplits = 8;
+
 template <int D>
 struct MainCfg {
   static constexpr int BN = 128;                 // kv rows per workgroup (32 per wave)
@@ -208,10 +212,12 @@ __device__ __forceinline__ int clamp_len(int64_t start, int len, int64_t total) 
 __device__ __forceinline__ int imin(int x, int y) { return x < y ? x : y; }
 __device__ __forceinline__ int imax(int x, int y) { return x > y ? x : y; }
 
-// WITH_DQ: the single-pass form that also forms the dQ partial of every (q tile, kv tile)
-// pair and adds it to the fp32 accumulator with atomics; without it the kernel produces dK
-// and dV only and dQ comes from fa_bwd_dq.
-template <int D, bool CAUSAL, bool WITH_DQ>
+// The single-pass form: one workgroup per (kv tile, head, sequence) forms the dK, dV and dQ
+// contributions of every (q tile, kv tile) pair and adds the dQ partials to the fp32 accumulator
+// with atomics. SPLIT: one workgroup per (split, head, sequence) walks the kv tiles split,
+// split + kSplits, ... in order and adds its dQ partials into its own fp32 buffer of the split
+// with plain loads and stores (the split's first tile stores); fa_bwd_split_reduce sums the splits.
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_main(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -225,8 +231,8 @@ void fa_bwd_main(MainArgs a) {
   float* s_st = (float*)(smem + C::OFF_ST);
 
   const int HB = a.H * a.batch;
-  const int tile = blockIdx.x / HB;  // heavy (low) kv tiles of every head dispatch first
-  const int hb = blockIdx.x - tile * HB;
+  const int first = blockIdx.x / HB;  // the kv tile (heavy low tiles of every head first), or the split
+  const int hb = blockIdx.x - first * HB;
   const int b = hb / a.H, h = hb - (hb / a.H) * a.H;
   int64_t q_start, kv_start;
   int Lq, Lk;
@@ -234,30 +240,30 @@ void fa_bwd_main(MainArgs a) {
   seq_of(a.cu_kv, b, a.padded, a.max_seqlen_kv, kv_start, Lk);
   Lq = clamp_len(q_start, Lq, a.total_q);
   Lk = clamp_len(kv_start, Lk, a.total_kv);
-  const int kv0 = tile * BN;
-  if (kv0 >= Lk) return;
-
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
   const int64_t rs = (int64_t)a.H * D;  // elements between consecutive tokens
   const int rsb = (int)(rs * 2);        // bytes between consecutive tokens
-  const bf16* kb = a.k + (kv_start + kv0) * rs + (int64_t)h * D;
-  const bf16* vb = a.v + (kv_start + kv0) * rs + (int64_t)h * D;
   const bf16* qb = a.q + q_start * rs + (int64_t)h * D;
   const bf16* db = a.dout + q_start * rs + (int64_t)h * D;
   const float* lse_b = a.lse2 + (int64_t)h * a.total_q + q_start;
   const float* dd_b = a.dvec + (int64_t)h * a.total_q + q_start;
-  float* dq_b = a.dq_acc + ((int64_t)h * a.total_q + q_start) * D;
+  // the fp32 dQ accumulator [H][total_q][D], or the split's buffer in [kSplits][H][total_q][D]
+  float* dq_b = a.dq_acc + (((SPLIT ? (int64_t)first * a.H : 0) + h) * a.total_q + q_start) * D;
+
+  for (int tile = first; tile * BN < Lk; tile += kSplits) {
+  const bool first_tile = tile == first;  // split: the first tile stores its dQ partials, later ones add
+  const int kv0 = tile * BN;
+  const bf16* kb = a.k + (kv_start + kv0) * rs + (int64_t)h * D;
+  const bf16* vb = a.v + (kv_start + kv0) * rs + (int64_t)h * D;
 
   // ---- K tile -> LDS (kept for the dQ GEMM); K, V B-operand fragments of S and dP -> registers
   const int kv_rows = imin(Lk - kv0, BN);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (int64_t)kv_rows * rsb);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (int64_t)kv_rows * rsb);
-  if constexpr (WITH_DQ) {
-    for (int ch = tid; ch < BN * D / 8; ch += 256) {
-      const int r = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *(u32x4*)(s_k + r * QS + col) = buf_load16(rk, r * rsb + col * 2);
-    }
+  for (int ch = tid; ch < BN * D / 8; ch += 256) {
+    const int r = ch / (D / 8), col = (ch % (D / 8)) * 8;
+    *(u32x4*)(s_k + r * QS + col) = buf_load16(rk, r * rsb + col * 2);
   }
   bf16x8 kf[C::KSD], vf[C::KSD];
 #pragma unroll
@@ -415,16 +421,14 @@ void fa_bwd_main(MainArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     // dS^T to LDS (for the dQ GEMM): row = this lane's key, 4 consecutive MFMA rows per store
-    if constexpr (WITH_DQ) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const bf16x8 src = (mt == 0 ? dsk0 : dsk1)[a4 >> 1];
-          const int o4 = 4 * (a4 & 1);
-          const bf16x4 v4 = {src[o4], src[o4 + 1], src[o4 + 2], src[o4 + 3]};
-          *(bf16x4*)(s_dst + (32 * w + c) * SS + 32 * mt + 8 * a4 + 4 * hh) = v4;
-        }
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const bf16x8 src = (mt == 0 ? dsk0 : dsk1)[a4 >> 1];
+        const int o4 = 4 * (a4 & 1);
+        const bf16x4 v4 = {src[o4], src[o4 + 1], src[o4 + 2], src[o4 + 3]};
+        *(bf16x4*)(s_dst + (32 * w + c) * SS + 32 * mt + 8 * a4 + 4 * hh) = v4;
       }
     }
   };
@@ -446,19 +450,12 @@ void fa_bwd_main(MainArgs a) {
     }
     const int i0 = qt * BM;
     tile_step(buf, i0);
-    if constexpr (!WITH_DQ) {
-      if (has_next) store_stats(buf ^ 1, st_next);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next tile's LDS-DMA has landed
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      continue;
-    }
     __syncthreads();  // dS^T complete
     if (has_next) store_stats(buf ^ 1, st_next);
 
-    // step 8: dQ partial = dS K over this tile's 128 keys, added to the fp32 accumulator.
-    // k-index 16 ks + 8 hh + 4 half + e reads kv row 16 ks + 2 hh + half + 4 e.
+    // step 8: dQ partial = dS K over this tile's 128 keys, added to the fp32 accumulator (atomics)
+    // or to the split's buffer (plain loads and stores: this thread is the only writer of these
+    // elements). k-index 16 ks + 8 hh + 4 half + e reads kv row 16 ks + 2 hh + half + 4 e.
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(dq_b + (int64_t)i0 * D, (int64_t)imin(Lq - i0, BM) * D * 4);
     const int krow = 2 * hh + 4 * (gi >> 2);
     const int tcol = 16 * (g & 1) + 4 * (gi & 3);
@@ -466,6 +463,18 @@ void fa_bwd_main(MainArgs a) {
     for (int tt = 0; tt < C::TPW; ++tt) {
       const int mtq = (w * C::TPW + tt) & 1;
       f32x16 acc = f32x16{};
+      auto elem_off = [&](int a4, int bb) {
+        return (32 * mtq + tile_row(8 * a4 + 4 * hh + bb)) * D * 4 + (32 * ntq + c) * 4;
+      };
+      f32x16 prev = f32x16{};  // split, later tiles: the partial sums so far, loaded ahead of the MFMAs
+      if (SPLIT && !first_tile) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb)
+            prev[4 * a4 + bb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rq, elem_off(a4, bb), 0, 0));
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < BN / 16; ++ks) {
         const int ra = (16 * ks + krow) * SS + 32 * mtq + tcol;
@@ -478,8 +487,11 @@ void fa_bwd_main(MainArgs a) {
       for (int a4 = 0; a4 < 4; ++a4) {
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-          const int row = 32 * mtq + tile_row(8 * a4 + 4 * hh + bb);
-          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[4 * a4 + bb], rq, (row * D + 32 * ntq + c) * 4, 0, 0);
+          if constexpr (SPLIT)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, prev[4 * a4 + bb] + acc[4 * a4 + bb]), rq,
+                                                  elem_off(a4, bb), 0, 0);
+          else
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[4 * a4 + bb], rq, elem_off(a4, bb), 0, 0);
         }
       }
     }
@@ -505,6 +517,9 @@ void fa_bwd_main(MainArgs a) {
         }
       }
     }
+  }
+  if constexpr (!SPLIT) break;  // one kv tile per workgroup
+  __syncthreads();              // LDS reads of this tile done before the next tile's K and zero fill
   }
 #endif
 }
@@ -1477,6 +1492,62 @@ void fa_fwd(FwdArgs a) {
     }
   }
 #endif
+}
+
+// ------------------------------------------------------------------ stage 3: split-and-reduce dQ sum
+
+// dQ = scale * (sum of the split buffers that hold each row, in split order), in bf16. Split s holds
+// the rows its first kv tile (s * BN) reaches: all rows of the sequence, or under a causal mask the
+// rows from s * BN on; a split without kv tiles holds none. One workgroup per (64-row block, head,
+// sequence); rows outside every sequence are zeroed by fa_bwd_pre.
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_split_reduce(MainArgs a) {
+  constexpr int R = 64, CH = D / 8, BN = MainCfg<D>::BN;
+  const int HB = a.H * a.batch;
+  const int blk = blockIdx.x / HB;
+  const int hb = blockIdx.x - blk * HB;
+  const int b = hb / a.H, h = hb - (hb / a.H) * a.H;
+  int64_t q_start, kv_start;
+  int Lq, Lk;
+  seq_of(a.cu_q, b, a.padded, a.max_seqlen_q, q_start, Lq);
+  seq_of(a.cu_kv, b, a.padded, a.max_seqlen_kv, kv_start, Lk);
+  Lq = clamp_len(q_start, Lq, a.total_q);
+  Lk = clamp_len(kv_start, Lk, a.total_kv);
+  const int r0 = blk * R;
+  if (r0 >= Lq) return;
+  const int n_split = imin(kSplits, (Lk + BN - 1) / BN);  // splits with at least one kv tile
+  const int64_t plane = (int64_t)a.H * a.total_q * D;       // one split's buffer
+  const float* src0 = a.dq_acc + ((int64_t)h * a.total_q + q_start) * D;
+  for (int idx = threadIdx.x; idx < R * CH; idx += 256) {
+    const int r = r0 + idx / CH, ch = idx % CH;
+    if (r >= Lq) continue;
+    const int ns = a.causal ? imin(n_split, r / BN + 1) : n_split;
+    // all kSplits loads in flight at once: splits past ns re-read the last one held (or split 0,
+    // allocated but unused when no split holds the row) and are not added
+    const int last = imax(ns - 1, 0);
+    f32x4 vlo[kSplits], vhi[kSplits];
+#pragma unroll
+    for (int sp = 0; sp < kSplits; ++sp) {
+      const float* src = src0 + imin(sp, last) * plane + (int64_t)r * D + ch * 8;
+      vlo[sp] = *(const f32x4*)src;
+      vhi[sp] = *(const f32x4*)(src + 4);
+    }
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < kSplits; ++sp) {  // split order, the same for every run
+      if (sp < ns) {
+        lo += vlo[sp];
+        hi += vhi[sp];
+      }
+    }
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[e] = to_bf16(lo[e] * a.scale);
+      out[e + 4] = to_bf16(hi[e] * a.scale);
+    }
+    *(bf16x8*)(a.dq + (q_start + r) * ((int64_t)a.H * D) + (int64_t)h * D + ch * 8) = out;
+  }
 }
 
 // ------------------------------------------------------------------ stage 3: single-pass dQ cast

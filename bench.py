@@ -6,7 +6,8 @@
 One step = one ``fa_bwd_run`` over the whole workload, inputs already
 resident in HBM: the row preprocess, then (default, recompute form) the dK/dV
 kernel and the dQ kernel, or (``--algorithm single-pass``) the single-pass
-main kernel with dQ atomics and the dQ cast. The default workload is
+main kernel with dQ atomics and the dQ cast, or (``--algorithm split-reduce``)
+the single-pass main kernel over 8 kv-tile splits with a fixed-order dQ sum. The default workload is
 the causal one: batch 1, 32 heads, 8192 tokens, head_dim 128. Throughput is
 algorithmic TFLOP/s, counting 10*Lq*Lk*d FLOPs per (sequence, head) -- the
 five GEMMs of the backward -- halved for causal masks.
@@ -45,13 +46,17 @@ if ROOT not in sys.path:
 METRIC = "FA-bwd TFLOP/s + % bf16 MFMA peak, S=8192 H=32 D=128 causal, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MASK_NAMES = {0: "none", 1: "padding", 2: "causal", 3: "padding_causal"}
-ALGORITHMS = {"default": 0, "single-pass": 1, "recompute": 2}
+ALGORITHMS = {"default": 0, "single-pass": 1, "recompute": 2, "split-reduce": 3}
+ALGORITHM_NAMES = {1: "single-pass (dQ atomics)", 2: "recompute (dK/dV kernel + dQ kernel)",
+                   3: "split-reduce (single-pass main kernel over 8 kv-tile splits + fixed-order dQ sum)"}
 def kernel_share(algorithm: int, d: int, dv: int) -> dict:
     """Share of the 5-GEMM algorithmic FLOPs each kernel runs itself. S = QK^T, dK, dQ contract or
     produce the query/key head dim d, dP, dV the value head dim dv (2 * pairs * dim FLOPs each)."""
     total = 3 * d + 2 * dv
     if algorithm == 1:
         return {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_dq_cast": 0.0}
+    if algorithm == 3:
+        return {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_split_reduce": 0.0}
     # dK/dV kernel: S, dP, dV, dK; dQ kernel: S and dP again, dQ
     return {"fa_bwd_pre": 0.0, "fa_bwd_dkdv": (2 * d + 2 * dv) / total, "fa_bwd_dq": (2 * d + dv) / total}
 
@@ -368,7 +373,7 @@ def main():
     algo = ALGORITHMS[args.algorithm]
     op = binding.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0],
                        algo, num_heads_kv=inp["k"].shape[1], window=inp["window"], head_dim_v=inp["v"].shape[2])
-    algo_used = 1 if algo == 1 else 2
+    algo_used = 2 if algo == 0 else algo
     if args.plan:  # host-side longest-first schedule from the (host) sequence offsets
         op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
     dq, dk, dv = (torch.empty_like(dev[x]) for x in ("q", "k", "v"))
@@ -407,7 +412,7 @@ def main():
               "batch": inp["batch"], "heads": heads, "head_dim": d, "seq_len": inp["max_seqlen_q"],
               "total_tokens": tq, "mask": MASK_NAMES[inp["mask"]], "seed": inp["seed"],
               "algorithmic_flops": flops,
-              "algorithm": "single-pass (dQ atomics)" if algo_used == 1 else "recompute (dK/dV kernel + dQ kernel)",
+              "algorithm": ALGORITHM_NAMES[algo_used],
               "schedule": "host longest-first plan" if args.plan else "dense grid"}
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -65,17 +65,24 @@ typedef enum {
                                    dQ contributions of every (q tile, kv tile) pair; dQ partial sums are
                                    added to an fp32 workspace with global atomics (summation order not
                                    fixed), then cast to bf16 */
-  FA_BWD_ALGO_RECOMPUTE_DQ = 2  /* the article's two-pass fallback: a kv-outer kernel forms dK, dV and a
+  FA_BWD_ALGO_RECOMPUTE_DQ = 2, /* the article's two-pass fallback: a kv-outer kernel forms dK, dV and a
                                    q-outer kernel recomputes S and dP to form dQ in registers; no
                                    atomics, no dQ workspace, bitwise reproducible */
+  FA_BWD_ALGO_SPLIT_REDUCE = 3  /* the single-pass structure with a fixed-order dQ reduction in place of
+                                   the atomics (the article gives a fixed summation order as a reason for
+                                   its two-pass fallback; this keeps one pass): 8 workgroups per (head,
+                                   sequence) each walk every 8th kv tile and keep their dQ partial sums
+                                   in a buffer of their own (8 fp32 copies of dQ in the workspace); a
+                                   last kernel sums the 8 buffers in a fixed order and casts to bf16;
+                                   bitwise reproducible. Same restrictions as FA_BWD_ALGO_SINGLE_PASS */
 } fa_bwd_algo;
 
 typedef enum {
   FA_BWD_OK = 0,
   FA_BWD_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad mask code, bad scale, misalignment */
   FA_BWD_ERR_UNSUPPORTED = 2,      /* a head dim that is not a multiple of 8 in [8, 256]; in the
-                                      single-pass form: head dims other than 64 or 128, unequal head
-                                      dims, grouped heads or a window */
+                                      single-pass and split-reduce forms: head dims other than 64 or
+                                      128, unequal head dims, grouped heads or a window */
   FA_BWD_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed in fa_bwd_create */
   FA_BWD_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
 } fa_bwd_status;
@@ -106,7 +113,7 @@ typedef struct {
 /* Validates desc (a num_heads_kv of 0 is stored as num_heads) and allocates
  * the device workspace of the handle on the current HIP device: two fp32 [H][total_q] row-statistic arrays and, for
  * FA_BWD_ALGO_SINGLE_PASS only, an fp32 dQ accumulator of total_q*H*head_dim
- * floats. On success *out holds a new handle; on failure *out is set to NULL.
+ * floats (8 of them for FA_BWD_ALGO_SPLIT_REDUCE). On success *out holds a new handle; on failure *out is set to NULL.
  * Host-side checks run before any HIP call. */
 fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out);
 
@@ -177,7 +184,7 @@ fa_bwd_status fa_fwd_run(fa_bwd_handle* h, const void* q, const void* k, const v
  *     Checked here: cu[0] = 0, non-decreasing, every length <= its max_seqlen, and cu[batch] <=
  *     total (packed masks); otherwise FA_BWD_ERR_INVALID_ARGUMENT and the previous plan is kept.
  *   mask: the fa_bwd_mask code of the later calls (it sets the causal bound of the work counts).
- * Both arrays NULL: drop the plan. FA_BWD_ERR_UNSUPPORTED for a single-pass handle. Blocks until
+ * Both arrays NULL: drop the plan. FA_BWD_ERR_UNSUPPORTED for a single-pass or split-reduce handle. Blocks until
  * the schedule is on the device; must not overlap a run that uses the handle. */
 fa_bwd_status fa_bwd_plan(fa_bwd_handle* h, const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_kv_host,
                           int32_t mask);
@@ -195,7 +202,7 @@ const fa_bwd_desc* fa_bwd_get_desc(const fa_bwd_handle* h);
 /* Per-kernel timing for benchmarks. While enabled, every fa_bwd_run (and
  * fa_bwd_run_lse) also records four HIP events on its stream, around its three
  * kernels (row preprocessing; the main kernel in single-pass form or the dK/dV
- * kernel in recompute form; then the dQ cast or the dQ kernel); an fa_fwd_run
+ * kernel in recompute form; then the dQ cast, the split sum or the dQ kernel); an fa_fwd_run
  * records the fill of rows outside sequences, the forward kernel and an empty
  * third interval. Recording does not wait.
  * Enabling or disabling forgets the runs recorded so far. At most 4096 runs

@@ -68,7 +68,11 @@ def _create(**kw):
     (dict(head_dim=256, algorithm=1), B.FA_BWD_ERR_UNSUPPORTED),                # equal head dims
     (dict(head_dim=128, head_dim_v=64, algorithm=1), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(num_heads=1 << 14, head_dim=256), B.FA_BWD_ERR_INVALID_ARGUMENT),     # 128 rows >= 2^30 bytes
-    (dict(algorithm=3), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(head_dim=96, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),                 # split-reduce: the same
+    (dict(head_dim=64, head_dim_v=128, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(num_heads=4, num_heads_kv=1, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(window=32, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(algorithm=4), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(algorithm=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(total_q=1 << 40, num_heads=8), B.FA_BWD_ERR_INVALID_ARGUMENT),          # index range
     (dict(max_seqlen_kv=1 << 30, num_heads=1 << 10, batch=1 << 10), B.FA_BWD_ERR_INVALID_ARGUMENT),  # grid size

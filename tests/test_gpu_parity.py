@@ -36,7 +36,8 @@ CASES = [
 ]
 
 
-ALGOS = {"recompute": B.FA_BWD_ALGO_RECOMPUTE_DQ, "singlepass": B.FA_BWD_ALGO_SINGLE_PASS}
+ALGOS = {"recompute": B.FA_BWD_ALGO_RECOMPUTE_DQ, "singlepass": B.FA_BWD_ALGO_SINGLE_PASS,
+         "splitreduce": B.FA_BWD_ALGO_SPLIT_REDUCE}
 
 
 @pytest.mark.parametrize("algo", list(ALGOS))
@@ -82,6 +83,44 @@ def test_recompute_is_bitwise_reproducible():
     b = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_RECOMPUTE_DQ)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+# sequences longer than 8 kv tiles of 128 keys: each split-reduce workgroup walks several tiles and
+# adds into its own dQ buffer (the first tile stores, later ones load and add)
+LONG_CASES = [
+    I.custom_case("long_causal_d128", 2, 128, CAUSAL, 231, [2300, 1100]),
+    I.custom_case("long_none_kv_longer_d64", 2, 64, NONE, 232, [700, 1500], [2200, 1030]),
+    I.custom_case("long_padded_causal_d128", 1, 128, PADC, 233, [1900, 1024], padded_len=2048),
+]
+
+
+@pytest.mark.parametrize("case", LONG_CASES, ids=[c.name for c in LONG_CASES])
+def test_parity_split_reduce_long(case):
+    inp = I.make(case)
+    print(f"[parity-long] {case.name}: lq {inp['seqlens_q']} lk {inp['seqlens_kv']}", flush=True)
+    o, m, l = P.oracle_stats(inp)
+    ref = P.oracle_backward(inp, o, m, l)
+    gpu = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_SPLIT_REDUCE)
+    res = P.check_full(inp, gpu, ref)
+    again = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_SPLIT_REDUCE)
+    for name, x, y in zip(("dq", "dk", "dv"), gpu, again):
+        assert torch.equal(x, y), f"{name}: split-reduce runs differ"
+    print(f"[parity-long] {case.name}: " + " ".join(f"{k}: rel_l2={v[0]:.2e} max={v[1]:.2e}" for k, v in res.items()),
+          flush=True)
+
+
+def test_split_reduce_is_bitwise_reproducible():
+    """Each dQ element is summed in a fixed order (kv tiles of a split, then the splits): repeated runs
+    are bitwise identical, and dK, dV are those of the single-pass form (no atomics touch them)."""
+    inp = I.make(I.custom_case("repro_split", 4, 128, I.MASK_CAUSAL, 212, [1700, 333]))
+    o, m, l = P.oracle_stats(inp)
+    a = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_SPLIT_REDUCE)
+    b = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_SPLIT_REDUCE)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    c = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_SINGLE_PASS)
+    assert torch.equal(a[1], c[1]) and torch.equal(a[2], c[2])
+    P.assert_close("dq", a[0].numpy(), c[0].numpy().astype(np.float64))
 
 
 def test_algorithms_agree():

@@ -115,7 +115,8 @@ def test_plan_rejects_bad_offsets_and_keeps_the_previous_plan():
         assert torch.equal(x, y)
 
 
-def test_single_pass_handle_has_no_plan():
-    with B.FaBwd(1, 2, 128, 64, 64, 64, 64, B.FA_BWD_ALGO_SINGLE_PASS) as op:
+@pytest.mark.parametrize("algo", [B.FA_BWD_ALGO_SINGLE_PASS, B.FA_BWD_ALGO_SPLIT_REDUCE])
+def test_single_pass_handle_has_no_plan(algo):
+    with B.FaBwd(1, 2, 128, 64, 64, 64, 64, algo) as op:
         with pytest.raises(NotImplementedError):
             op.plan([0, 64], [0, 64], NONE)
