@@ -70,6 +70,9 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   // the single-pass form owns one (kv tile, head) per workgroup; grouped K/V heads need the recompute form
   if (single && hkv != d->num_heads) return FA_BWD_ERR_UNSUPPORTED;
   if (d->window < 0) return FA_BWD_ERR_INVALID_ARGUMENT;
+  // sequence positions, and a window clamped to max_seqlen_q, stay below 2^30: the kernels' tile and
+  // window bounds (kv0 + tile + window, i - window - kv0) then fit in 32 bits
+  if (d->max_seqlen_q > (1 << 30) || d->max_seqlen_kv > (1 << 30)) return FA_BWD_ERR_INVALID_ARGUMENT;
   if (single && d->window > 0) return FA_BWD_ERR_UNSUPPORTED;
   // index arithmetic stays in int64; grids must fit the launch limits
   const int64_t rows = (d->total_q > d->total_kv ? d->total_q : d->total_kv);
@@ -90,6 +93,10 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
 // The kernels for the padded head dims: each dim rounded up to 64, 128, 192 or 256, and a dim of 64
 // next to one above 128 taken as 128.
 int padded_dim(int d) { return d <= 64 ? 64 : d <= 128 ? 128 : d <= 192 ? 192 : 256; }
+
+// A window of max_seqlen_q or more hides no key a causal bound would show (query i < max_seqlen_q sees
+// every key j <= i either way); the kernels and the schedule take it clamped to max_seqlen_q.
+int32_t effective_window(const fa_bwd_desc& d) { return d.window > d.max_seqlen_q ? d.max_seqlen_q : d.window; }
 
 fa::KernelSet pick_kernels(int d_qk, int d_v) {
   int pq = padded_dim(d_qk), pv = padded_dim(d_v);
@@ -242,7 +249,7 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.max_seqlen_kv = d.max_seqlen_kv;
   ma.padded = padded;
   ma.causal = causal;
-  ma.window = d.window;
+  ma.window = effective_window(d);
   ma.d_qk = d.head_dim;
   ma.d_v = d.head_dim_v;
   ma.scale_log2 = scale * fa::kLog2e;
@@ -299,7 +306,7 @@ fa_bwd_status launch_fwd(fa_bwd_handle* h, const void* q, const void* k, const v
   fa.max_seqlen_q = d.max_seqlen_q;
   fa.max_seqlen_kv = d.max_seqlen_kv;
   fa.padded = padded;
-  fa.window = d.window;
+  fa.window = effective_window(d);
   fa.d_qk = d.head_dim;
   fa.d_v = d.head_dim_v;
   fa.scale_log2 = scale * fa::kLog2e;
@@ -348,7 +355,7 @@ fa_bwd_status build_plan(const fa_bwd_desc& d, const int32_t* cq, const int32_t*
     int32_t tile, hb;
   };
   std::vector<Item> kv, q;
-  const int G = d.num_heads / d.num_heads_kv, w = d.window;
+  const int G = d.num_heads / d.num_heads_kv, w = effective_window(d);
   for (int b = 0; b < d.batch; ++b) {
     const int lq = cq[b + 1] - cq[b], lk = ck[b + 1] - ck[b];
     const int n_qs = (lq + ks.q_step - 1) / ks.q_step;  // q steps of the dK/dV kernel

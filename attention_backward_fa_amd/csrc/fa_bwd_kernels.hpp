@@ -1180,7 +1180,11 @@ void fa_bwd_dq(MainArgs a) {
     // steps 2 and 5: P = exp2(S*scale*log2e - lse2), dS = P (dP - D); key row j = t*BK + kv row.
     // Visible iff j < Lk and (causal) j <= qi: one bound per lane on the tile-local kv row.
     const int lim = CAUSAL ? imin(Lk - 1, qi) - t * BK : Lk - 1 - t * BK;
-    const int lo = qi - a.window + 1 - t * BK;  // window: first visible tile-local key
+    // window: visible iff lo <= kr <= lim, one unsigned compare of kr - lo against lim - lo (a row
+    // that sees no key of the tile gets a base past every kv row)
+    const int lo = qi - a.window + 1 - t * BK;
+    const int wbase = lim >= lo ? lo : (1 << 30);
+    const unsigned wspan = lim >= lo ? (unsigned)(lim - lo) : 0u;
     bf16x8 dsk[2][2];
     auto softmax = [&](auto masked) {
 #pragma unroll
@@ -1193,7 +1197,10 @@ void fa_bwd_dq(MainArgs a) {
             float p = fast_exp2(s[mt][j] * a.scale_log2 - lse);
             if constexpr (decltype(masked)::value) {
               const int kr = 32 * mt + tile_row(8 * a4 + 4 * hh + bb);
-              p = (kr <= lim && (!WINDOW || kr >= lo)) ? p : 0.f;
+              if constexpr (WINDOW)
+                p = (unsigned)(kr - wbase) <= wspan ? p : 0.f;
+              else
+                p = kr <= lim ? p : 0.f;
             }
             dsk[mt][j >> 3][j & 7] = to_bf16(p * (dp[mt][j] - dd));
           }

@@ -93,7 +93,7 @@ typedef struct {
   int32_t head_dim;      /* head dim of Q, K, dQ, dK: a multiple of 8 from 8 to 256 (the head dim
                             limits of the jax cuDNN wrapper's bf16 path); the single-pass form takes
                             64 and 128 */
-  int32_t max_seqlen_q;  /* >= every L_b of the queries; the slot length in padded modes; >= 1 */
+  int32_t max_seqlen_q;  /* >= every L_b of the queries; the slot length in padded modes; 1 .. 2^30 */
   int32_t max_seqlen_kv; /* same for keys/values */
   int64_t total_q;       /* rows of q, o, do, dq, m, l; >= 1 */
   int64_t total_kv;      /* rows of k, v, dk, dv; >= 1 */
@@ -104,7 +104,8 @@ typedef struct {
                             the jax cuDNN wrapper's API allows; recompute form only) */
   int32_t window;        /* 0: no window; w > 0: every query i sees only its left local window of keys
                             (i - w, i] (the jax cuDNN wrapper's sliding_window_length), which implies
-                            the causal bound whatever the mask code; recompute form and forward only */
+                            the causal bound whatever the mask code; any w >= max_seqlen_q acts as
+                            w = max_seqlen_q (the causal bound alone); recompute form and forward only */
   int32_t head_dim_v;    /* head dim of V, O, dO and dV: 0 = head_dim. It may differ from head_dim
                             (latent attention: the jax cuDNN wrapper's qH != vH); then S = Q K^T runs
                             over head_dim and O = P V over head_dim_v. Recompute form and forward only */

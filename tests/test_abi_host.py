@@ -81,6 +81,8 @@ def _create(**kw):
     (dict(num_heads=4, num_heads_kv=8), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(num_heads=4, num_heads_kv=2, algorithm=1), B.FA_BWD_ERR_UNSUPPORTED),  # grouped heads: recompute form
     (dict(window=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(max_seqlen_q=(1 << 30) + 1, total_q=1 << 31), B.FA_BWD_ERR_INVALID_ARGUMENT),   # positions < 2^30
+    (dict(max_seqlen_kv=(1 << 30) + 1, total_kv=1 << 31), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(window=64, algorithm=1), B.FA_BWD_ERR_UNSUPPORTED),                    # window: recompute form
 ])
 def test_create_rejects_bad_descriptors_before_any_hip_call(kw, status):

@@ -88,9 +88,9 @@ def test_recompute_is_bitwise_reproducible():
 # sequences longer than 8 kv tiles of 128 keys: each split-reduce workgroup walks several tiles and
 # adds into its own dQ buffer (the first tile stores, later ones load and add)
 LONG_CASES = [
-    I.custom_case("long_causal_d128", 2, 128, CAUSAL, 231, [2300, 1100]),
-    I.custom_case("long_none_kv_longer_d64", 2, 64, NONE, 232, [700, 1500], [2200, 1030]),
-    I.custom_case("long_padded_causal_d128", 1, 128, PADC, 233, [1900, 1024], padded_len=2048),
+    I.custom_case("long_causal_d128", 2, 128, CAUSAL, 241, [2300, 1100]),
+    I.custom_case("long_none_kv_longer_d64", 2, 64, NONE, 242, [700, 1500], [2200, 1030]),
+    I.custom_case("long_padded_causal_d128", 1, 128, PADC, 243, [1900, 1024], padded_len=2048),
 ]
 
 
@@ -169,6 +169,9 @@ WINDOW_CASES = [
     I.custom_case("window_one_d128", 2, 128, CAUSAL, 233, [130], window=1),
     I.custom_case("window_wide_padded_d128", 2, 128, PADC, 234, [200, 90], padded_len=224, window=300),
     I.custom_case("window_gqa_causal_d128", 4, 128, CAUSAL, 235, [333], heads_kv=2, window=128),
+    # windows far past every sequence (up to the int32 maximum): the causal bound alone
+    I.custom_case("window_huge_none_d128", 2, 128, NONE, 236, [300, 129], window=2**31 - 1),
+    I.custom_case("window_huge_padded_d64", 2, 64, PAD, 237, [200, 77], padded_len=256, window=2**30 + 5),
 ]
 
 
@@ -182,6 +185,27 @@ def test_parity_window(case):
     res = P.check_full(inp, gpu, ref)
     print(f"[parity-window] {case.name}: " + " ".join(f"{k}: rel_l2={v[0]:.2e}" for k, v in res.items()),
           flush=True)
+
+
+def test_huge_window_is_the_causal_bound():
+    """A window past every sequence gives the causal result, from the dense grid and from a host schedule."""
+    case = next(c for c in WINDOW_CASES if c.name == "window_huge_none_d128")
+    inp = I.make(case)
+    o, m, l = P.oracle_stats(inp)
+    huge = P.run_gpu(inp, o, m, l)
+    causal = dict(inp, mask=CAUSAL, window=0)
+    ref = P.oracle_backward(causal, o, m, l)
+    P.check_full(causal, huge, ref)
+    dev = torch.device("cuda")
+    t = {k: inp[k].to(dev) for k in ("q", "k", "v", "do", "cu_q", "cu_kv")}
+    with B.FaBwd(inp["batch"], case.heads, case.head_dim, inp["max_seqlen_q"], inp["max_seqlen_kv"],
+                 inp["q"].shape[0], inp["k"].shape[0], window=inp["window"]) as op:
+        op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
+        planned = op.run(t["q"], t["k"], t["v"], o.to(dev), t["do"], m.to(dev), l.to(dev), t["cu_q"], t["cu_kv"],
+                         inp["scale"], inp["mask"])
+        torch.cuda.synchronize()
+    for name, x, y in zip(("dq", "dk", "dv"), huge, planned):
+        assert torch.equal(x, y.float().cpu()), f"{name}: planned run differs from the dense grid"
 
 
 def test_window_single_pass_unsupported():
