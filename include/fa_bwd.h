@@ -57,7 +57,7 @@ typedef enum {
   FA_BWD_MASK_PADDING_CAUSAL = 3
 } fa_bwd_mask;
 
-/* How dQ is formed. Both forms compute the same per-tile math (steps 1-8) and
+/* How dQ is formed. All forms compute the same per-tile math (steps 1-8) and
  * agree within the fp32 rounding of the accumulation order. */
 typedef enum {
   FA_BWD_ALGO_DEFAULT = 0,      /* the faster form on this GPU: FA_BWD_ALGO_RECOMPUTE_DQ */
