@@ -85,6 +85,8 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   if (kv_tiles * d->num_heads * d->batch > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
   const int64_t q_tiles = (d->max_seqlen_q + 63) / 64;  // the split reduce's 64-row blocks
   if (q_tiles * d->num_heads * d->batch > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (d->algorithm == FA_BWD_ALGO_SPLIT_REDUCE && (int64_t)fa::kSplits * d->num_heads * d->batch > kMaxGrid)
+    return FA_BWD_ERR_INVALID_ARGUMENT;
   const int64_t rows_per_block = 256 / threads_per_row(d->head_dim, dv);
   if ((rows * d->num_heads + rows_per_block - 1) / rows_per_block > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
   return FA_BWD_OK;

@@ -76,6 +76,8 @@ def _create(**kw):
     (dict(algorithm=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(total_q=1 << 40, num_heads=8), B.FA_BWD_ERR_INVALID_ARGUMENT),          # index range
     (dict(max_seqlen_kv=1 << 30, num_heads=1 << 10, batch=1 << 10), B.FA_BWD_ERR_INVALID_ARGUMENT),  # grid size
+    (dict(batch=1 << 19, num_heads=1 << 10, max_seqlen_q=1, max_seqlen_kv=1, total_q=1 << 19, total_kv=1 << 19,
+          algorithm=3), B.FA_BWD_ERR_INVALID_ARGUMENT),                            # 8 split workgroups each
     (dict(num_heads=6, num_heads_kv=4), B.FA_BWD_ERR_INVALID_ARGUMENT),   # K/V heads must divide query heads
     (dict(num_heads=4, num_heads_kv=-2), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(num_heads=4, num_heads_kv=8), B.FA_BWD_ERR_INVALID_ARGUMENT),
