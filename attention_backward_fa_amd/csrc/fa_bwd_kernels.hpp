@@ -528,7 +528,8 @@ void fa_bwd_main(MainArgs a) {
 // ------------------------------------------------------------------ stage 2a: dK and dV by recompute
 
 // Tiling of the dK/dV kernel for padded head dims DQ (Q, K) and DV (V, dO), multiples of 32. Up to
-// 128: eight waves (two per SIMD), a 128-row kv tile whose K and V sit in LDS. Wider heads: four
+// 128: eight waves (two per SIMD), a 128-row kv tile; each wave holds the K rows of its 32 keys in
+// registers (the first GEMM then reads only Q, dO and V from LDS), the V tile sits in LDS. Wider heads: four
 // waves (one per SIMD, accumulators in the larger register budget of a single wave), a 64-row kv
 // tile whose K and V fragments are held in registers, so that LDS holds only the Q and dO tiles.
 template <int DQ, int DV>
@@ -547,22 +548,23 @@ struct DkdvCfg {
   static constexpr int TQ_BYTES = BM * QSQ * 2;  // one Q tile
   static constexpr int TD_BYTES = BM * QSV * 2;  // one dO tile
   static constexpr int NDMA_Q = TQ_BYTES / 1024, NDMA_D = TD_BYTES / 1024;
-  static constexpr int K_BYTES = WIDE ? 0 : BN * QSQ * 2;  // the K (and V) tile of the workgroup
+  // K is held in registers by every wave (B-operand fragments of its 32 keys); heads up to 128 keep
+  // the V tile of the workgroup in LDS, wider heads hold V in registers as well
   static constexpr int V_BYTES = WIDE ? 0 : BN * QSV * 2;
-  static constexpr int NDMA_K = K_BYTES / 1024, NDMA_V = V_BYTES / 1024;
-  static constexpr int OFF_K = 0;                             // K [BN][QSQ]
-  static constexpr int OFF_V = OFF_K + K_BYTES;               // V [BN][QSV]
+  static constexpr int NDMA_V = V_BYTES / 1024;
+  static constexpr int OFF_V = 0;                             // V [BN][QSV]
   static constexpr int OFF_Q = OFF_V + V_BYTES;               // Q [2][BM][QSQ]
   static constexpr int OFF_DO = OFF_Q + 2 * TQ_BYTES;         // dO [2][BM][QSV]
   static constexpr int OFF_ST = OFF_DO + 2 * TD_BYTES;        // [2 buffers][lse2, D][BM] fp32
   static constexpr int OFF_X = OFF_ST + 4 * BM * 4;           // wide: [wave][lane] 2 bf16x8 of P or dS
-  static constexpr int LDS_BYTES = OFF_X + (WIDE ? NW * 64 * 32 : 0);
   static constexpr int PART_BYTES = WIDE ? 0 : NG * (NTQ + NTV) * 64 * 64;  // partial dK, then dV
+  static constexpr int TILE_END = OFF_X + (WIDE ? NW * 64 * 32 : 0);
+  // the end-of-kernel exchange of partial sums reuses the whole allocation
+  static constexpr int LDS_BYTES = TILE_END > PART_BYTES ? TILE_END : PART_BYTES;
   static_assert(DQ % 32 == 0 && DV % 32 == 0 && DQ <= 256 && DV <= 256, "padded head dims");
-  static_assert(TQ_BYTES % 1024 == 0 && TD_BYTES % 1024 == 0 && K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0,
+  static_assert(TQ_BYTES % 1024 == 0 && TD_BYTES % 1024 == 0 && V_BYTES % 1024 == 0,
                 "tiles are whole 1 KB transfers");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget (one workgroup per CU)");
-  static_assert(PART_BYTES <= OFF_ST, "the end-of-kernel exchange of partial sums fits in the tiles");
 };
 
 // dK and dV of one (kv tile, K/V head, sequence). Row group r = w % NG owns kv rows 32 r .. 32 r + 31,
@@ -582,7 +584,6 @@ void fa_bwd_dkdv(MainArgs a) {
   using C = DkdvCfg<DQ, DV>;
   constexpr int BN = C::BN, BM = C::BM, NG = C::NG, QSQ = C::QSQ, QSV = C::QSV;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
-  const bf16* s_k = (const bf16*)(smem + C::OFF_K);
   const bf16* s_v = (const bf16*)(smem + C::OFF_V);
   bf16* s_q = (bf16*)(smem + C::OFF_Q);
   bf16* s_do = (bf16*)(smem + C::OFF_DO);
@@ -635,28 +636,28 @@ void fa_bwd_dkdv(MainArgs a) {
   const int kv_rows = imin(Lk - kv0, BN);
   const bf16* kbase = a.k + (kv_start + kv0) * rskq + (int64_t)hk * dqk;
   const bf16* vbase = a.v + (kv_start + kv0) * rskv + (int64_t)hk * dvd;
-  // wide heads: this lane's K and V rows as B-operand fragments (key 32 grp + c, features 16 ks + 8 hh)
-  bf16x8 kreg[C::WIDE ? C::KSQ : 1], vreg[C::WIDE ? C::KSV : 1];
-  if constexpr (C::WIDE) {
+  // this lane's K row (and, for wide heads, V row) as B-operand fragments: key 32 grp + c, features
+  // 16 ks + 8 hh .. + 7 (zeros at or past the head dim)
+  bf16x8 kreg[C::KSQ], vreg[C::WIDE ? C::KSV : 1];
+  {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (int64_t)kv_rows * rskqb);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (int64_t)kv_rows * rskvb);
     const int row = 32 * grp + c;
 #pragma unroll
     for (int ks = 0; ks < C::KSQ; ++ks) {
       const int col = 16 * ks + 8 * hh;
       kreg[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, col < dqk ? row * rskqb + col * 2 : kOutOfRange));
     }
+  }
+  if constexpr (C::WIDE) {
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (int64_t)kv_rows * rskvb);
+    const int row = 32 * grp + c;
 #pragma unroll
     for (int ks = 0; ks < C::KSV; ++ks) {
       const int col = 16 * ks + 8 * hh;
       vreg[ks] = __builtin_bit_cast(bf16x8, buf_load16(rv, col < dvd ? row * rskvb + col * 2 : kOutOfRange));
     }
-  } else {  // the K and V tiles, once
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, (int64_t)kv_rows * rskqb);
+  } else {  // the V tile, once
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, (int64_t)kv_rows * rskvb);
-    for (int j = w; j < C::NDMA_K; j += C::NW)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(smem + C::OFF_K + 1024 * j),
-                                               16, tile_dma_off(j, lane, C::CPRQ, rskqb, dqk), 0, 0, 0);
     for (int j = w; j < C::NDMA_V; j += C::NW)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(smem + C::OFF_V + 1024 * j),
                                                16, tile_dma_off(j, lane, C::CPRV, rskvb, dvd), 0, 0, 0);
@@ -723,7 +724,6 @@ void fa_bwd_dkdv(MainArgs a) {
 
   const int arowq = (32 * mt + tile_row(c)) * QSQ + 8 * hh;  // A rows: this M-tile's q rows
   const int arowd = (32 * mt + tile_row(c)) * QSV + 8 * hh;
-  const int krow = (32 * grp + c) * QSQ + 8 * hh;  // B columns: this group's keys
   const int vrow = (32 * grp + c) * QSV + 8 * hh;
   const int browq = (hh + 4 * (gi >> 2)) * QSQ + 16 * (g & 1) + 4 * (gi & 3) + 32 * mt * QSQ;
   const int browd = (hh + 4 * (gi >> 2)) * QSV + 16 * (g & 1) + 4 * (gi & 3) + 32 * mt * QSV;
@@ -742,10 +742,7 @@ void fa_bwd_dkdv(MainArgs a) {
     auto ld = [&](int ks) {
       if (ks < C::KSQ) {
         qa[ks] = *(const bf16x8*)(sq + arowq + 16 * ks);
-        if constexpr (C::WIDE)
-          kb[ks] = kreg[ks];
-        else
-          kb[ks] = *(const bf16x8*)(s_k + krow + 16 * ks);
+        kb[ks] = kreg[ks];
       }
       if (ks < C::KSV) {
         da[ks] = *(const bf16x8*)(sd + arowd + 16 * ks);
@@ -782,8 +779,8 @@ void fa_bwd_dkdv(MainArgs a) {
           float p = fast_exp2(s[j] * a.scale_log2 - lse[bb]);
           if constexpr (decltype(masked)::value) {
             const int r = tile_row(8 * a4 + 4 * hh + bb);
-            if constexpr (WINDOW)  // key j visible from query i iff i - window < j <= i
-              p = (jrel <= r && r - jrel < a.window) ? p : 0.f;
+            if constexpr (WINDOW)  // key j visible from query i iff 0 <= i - j < window: one unsigned compare
+              p = (unsigned)(r - jrel) < (unsigned)a.window ? p : 0.f;
             else
               p = (jrel <= r) ? p : 0.f;
           }
@@ -1147,12 +1144,17 @@ void fa_bwd_dq(MainArgs a) {
     if (t + 1 < n_kt) issue_kv(t + 1, buf ^ 1);
     const bf16* sk = (const bf16*)(smem + C::OFF_K + buf * C::TK_BYTES);
     const bf16* sv = (const bf16*)(smem + C::OFF_V + buf * C::TV_BYTES);
-    // steps 1 and 3, transposed: S^T = K Q^T, dP^T = V dO^T  ([kv 64] x [q 32] per wave)
+    // steps 1 and 3, transposed: S^T = K Q^T and dP^T - D = V dO^T - D ([kv 64] x [q 32] per wave;
+    // the dP accumulators start from -D of the lane's query row, which folds the subtraction of
+    // step 5 into the GEMM)
     f32x16 s[2], dp[2];
+    float ndd = -dd;
+    asm volatile("" : "+v"(ndd));  // formed per step: a splat kept across the loop would spill
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       s[mt] = f32x16{};
-      dp[mt] = f32x16{};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dp[mt][j] = ndd;
     }
     {  // operands read PF k-steps ahead into distinct registers, one scheduling fence per k-step
       constexpr int PF = 2;
@@ -1202,7 +1204,7 @@ void fa_bwd_dq(MainArgs a) {
               else
                 p = kr <= lim ? p : 0.f;
             }
-            dsk[mt][j >> 3][j & 7] = to_bf16(p * (dp[mt][j] - dd));
+            dsk[mt][j >> 3][j & 7] = to_bf16(p * dp[mt][j]);
           }
         }
       }
