@@ -26,6 +26,8 @@ FA_BWD_ALGO_DEFAULT = 0
 FA_BWD_ALGO_SINGLE_PASS = 1
 FA_BWD_ALGO_RECOMPUTE_DQ = 2
 FA_BWD_ALGO_SPLIT_REDUCE = 3
+FA_BWD_ALGO_RECOMPUTE_DQ_8W = 4
+FA_BWD_ALGO_RECOMPUTE_DQ_4W = 5
 
 FA_BWD_MASK_NONE = 0
 FA_BWD_MASK_PADDING = 1

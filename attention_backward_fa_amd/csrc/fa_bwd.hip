@@ -28,6 +28,11 @@ struct fa_bwd_handle {
   int32_t* sched;
   int64_t n_kv_items, n_q_items;
   int32_t plan_mask;
+  // layout of the dK/dV kernel for heads up to 128: forced by the algorithm code, or chosen by load
+  // balance (four_waves_balances) from the descriptor, without and with a causal bound; planned and
+  // dense runs of a handle take the same layout, so that they agree bitwise
+  int32_t dkdv_layout;  // 0: chosen, 1: eight waves, 2: four waves
+  bool four_dense[2];
 };
 
 namespace {
@@ -45,6 +50,25 @@ void release_events(fa_bwd_handle* h) {
 
 bool head_dim_ok(int32_t d) { return d >= 8 && d <= 256 && d % 8 == 0; }
 
+// Work of the dK/dV workgroups of one sequence (lq queries, lk keys): the 64-row q steps each 128-row
+// kv tile visits, bounded as the kernel bounds its loop (causal start, window band); adds the sum
+// over the tiles to total and keeps the largest.
+void dkdv_work(int64_t lq, int64_t lk, bool causal, int64_t w, int64_t& total, int64_t& largest) {
+  const int64_t n_qs = (lq + 63) / 64;
+  for (int64_t kv0 = 0; kv0 < lk; kv0 += 128) {
+    const int64_t qt0 = causal ? kv0 / 64 : 0;
+    const int64_t qt_end = w > 0 ? std::min(n_qs, (kv0 + 126 + w) / 64 + 1) : n_qs;
+    const int64_t work = std::max<int64_t>(0, qt_end - qt0);
+    total += work;
+    largest = std::max(largest, work);
+  }
+}
+
+// The four-wave dK/dV layout runs two workgroups per CU, each at about half the rate of one
+// eight-wave workgroup. Longest-first dispatch then balances only while the largest workgroup,
+// doubled, still fits within the average work per CU; otherwise the eight-wave layout is kept.
+bool four_waves_balances(int64_t total, int64_t largest, int cus) { return 2 * largest * cus <= total; }
+
 // threads per (token, head) row of the row kernels: a power of two covering the wider row in
 // 8-element chunks
 int threads_per_row(int d_qk, int d_v) {
@@ -61,7 +85,7 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
     return FA_BWD_ERR_INVALID_ARGUMENT;
   const int32_t dv = d->head_dim_v == 0 ? d->head_dim : d->head_dim_v;
   if (!head_dim_ok(d->head_dim) || !head_dim_ok(dv)) return FA_BWD_ERR_UNSUPPORTED;
-  if (d->algorithm < FA_BWD_ALGO_DEFAULT || d->algorithm > FA_BWD_ALGO_SPLIT_REDUCE) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (d->algorithm < FA_BWD_ALGO_DEFAULT || d->algorithm > FA_BWD_ALGO_RECOMPUTE_DQ_4W) return FA_BWD_ERR_INVALID_ARGUMENT;
   const bool single = d->algorithm == FA_BWD_ALGO_SINGLE_PASS || d->algorithm == FA_BWD_ALGO_SPLIT_REDUCE;
   // the single-pass kernels exist for equal head dims of 64 and 128
   if (single && (dv != d->head_dim || (d->head_dim != 64 && d->head_dim != 128))) return FA_BWD_ERR_UNSUPPORTED;
@@ -265,7 +289,8 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
     else
       h->split ? launch_single_pass<64, true>(ma, causal, stream) : launch_single_pass<64, false>(ma, causal, stream);
   } else if (!planned || h->n_kv_items > 0) {
-    ks.dkdv(ma, h->n_kv_items, stream);
+    const bool four = h->dkdv_layout == 2 || (h->dkdv_layout == 0 && h->four_dense[causal]);
+    ks.dkdv(ma, h->n_kv_items, four, stream);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return FA_BWD_ERR_HIP;
@@ -438,9 +463,22 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
   if (h->desc.head_dim_v == 0) h->desc.head_dim_v = desc->head_dim;
   h->single_pass = desc->algorithm == FA_BWD_ALGO_SINGLE_PASS || desc->algorithm == FA_BWD_ALGO_SPLIT_REDUCE;
   h->split = desc->algorithm == FA_BWD_ALGO_SPLIT_REDUCE;
-  if (hipGetDevice(&h->device) != hipSuccess) {
+  h->dkdv_layout = desc->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_8W ? 1 : desc->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_4W ? 2 : 0;
+  int cus = 0;
+  if (hipGetDevice(&h->device) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess || cus < 1) {
     delete h;
     return FA_BWD_ERR_HIP;
+  }
+  {  // the dense grid: every sequence taken at the maximum lengths
+    const fa_bwd_desc& hd = h->desc;
+    const int64_t per_tile_heads = (int64_t)hd.batch * hd.num_heads;  // Hk K/V heads x G query heads each
+    const int G = hd.num_heads / hd.num_heads_kv;
+    for (int c = 0; c < 2; ++c) {
+      int64_t total = 0, largest = 0;
+      dkdv_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), total, largest);
+      h->four_dense[c] = four_waves_balances(total * per_tile_heads, largest * G, cus);
+    }
   }
   const size_t stats = (size_t)desc->total_q * desc->num_heads;
   const size_t acc = stats * desc->head_dim * (h->split ? fa::kSplits : 1);

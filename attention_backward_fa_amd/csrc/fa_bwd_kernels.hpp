@@ -527,26 +527,34 @@ void fa_bwd_main(MainArgs a) {
 
 // ------------------------------------------------------------------ stage 2a: dK and dV by recompute
 
-// Tiling of the dK/dV kernel for padded head dims DQ (Q, K) and DV (V, dO), multiples of 32. Up to
-// 128: eight waves (two per SIMD), a 128-row kv tile; each wave holds the K rows of its 32 keys in
-// registers (the first GEMM then reads only Q, dO and V from LDS), the V tile sits in LDS. Wider heads: four
+// Tiling of the dK/dV kernel for padded head dims DQ (Q, K) and DV (V, dO), multiples of 32, and NMT
+// 32-row M-tiles per q step. Up to 128: a 128-row kv tile; each wave holds the K rows of its 32 keys
+// in registers (the first GEMM then reads only Q, dO and V from LDS), the V tile sits in LDS. With
+// NMT = 2, eight waves (two per SIMD, one workgroup per CU): the two waves of a 32-key group split
+// each 64-row q step. With NMT = 1, four waves (72 KB of LDS at d = 128, so two workgroups share a
+// CU and their waves do not wait on each other's barriers): each wave takes whole 32-row q steps for
+// its keys. Wider heads: four
 // waves (one per SIMD, accumulators in the larger register budget of a single wave), a 64-row kv
 // tile whose K and V fragments are held in registers, so that LDS holds only the Q and dO tiles.
-template <int DQ, int DV>
+template <int DQ, int DV, int NMT_ = 2>
 struct DkdvCfg {
   static constexpr bool WIDE = DQ > 128 || DV > 128;
+  static constexpr int NMT = NMT_;               // M-tiles per step
+  static_assert(NMT == 2 || (NMT == 1 && !WIDE), "wide heads take 64-row q steps");
   static constexpr int WPE = WIDE ? 1 : 2;       // waves per SIMD
   static constexpr int BN = WIDE ? 64 : 128;     // kv rows per workgroup: row groups of 32
-  static constexpr int BM = 64;                  // q rows per step: 2 M-tiles of 32
+  static constexpr int BM = 32 * NMT;            // q rows per step: M-tiles of 32
   static constexpr int NG = BN / 32;             // row groups
-  static constexpr int NW = 2 * NG;              // waves: row groups x 2 M-tiles
+  static constexpr int NW = NMT * NG;            // waves: row groups x M-tiles
   static constexpr int NT = 64 * NW;
   static constexpr int KSQ = DQ / 16, KSV = DV / 16, KSM = KSQ > KSV ? KSQ : KSV;  // MFMA k-steps
   static constexpr int NTQ = DQ / 32, NTV = DV / 32, NTM = NTQ > NTV ? NTQ : NTV;  // 32-wide tiles
   static constexpr int QSQ = DQ + 8, QSV = DV + 8;  // padded row strides of the LDS tiles
   static constexpr int CPRQ = QSQ / 8, CPRV = QSV / 8;
-  static constexpr int TQ_BYTES = BM * QSQ * 2;  // one Q tile
-  static constexpr int TD_BYTES = BM * QSV * 2;  // one dO tile
+  // one Q (dO) tile, and its buffer rounded up to whole 1 KB transfers (the rows past the tile that
+  // the last transfer covers read out of range and land as zeros in the padding)
+  static constexpr int TQ_BYTES = (BM * QSQ * 2 + 1023) / 1024 * 1024;
+  static constexpr int TD_BYTES = (BM * QSV * 2 + 1023) / 1024 * 1024;
   static constexpr int NDMA_Q = TQ_BYTES / 1024, NDMA_D = TD_BYTES / 1024;
   // K is held in registers by every wave (B-operand fragments of its 32 keys); heads up to 128 keep
   // the V tile of the workgroup in LDS, wider heads hold V in registers as well
@@ -557,14 +565,14 @@ struct DkdvCfg {
   static constexpr int OFF_DO = OFF_Q + 2 * TQ_BYTES;         // dO [2][BM][QSV]
   static constexpr int OFF_ST = OFF_DO + 2 * TD_BYTES;        // [2 buffers][lse2, D][BM] fp32
   static constexpr int OFF_X = OFF_ST + 4 * BM * 4;           // wide: [wave][lane] 2 bf16x8 of P or dS
-  static constexpr int PART_BYTES = WIDE ? 0 : NG * (NTQ + NTV) * 64 * 64;  // partial dK, then dV
+  static constexpr int PART_BYTES = NMT == 2 && !WIDE ? NG * (NTQ + NTV) * 64 * 64 : 0;  // partial dK, then dV
   static constexpr int TILE_END = OFF_X + (WIDE ? NW * 64 * 32 : 0);
   // the end-of-kernel exchange of partial sums reuses the whole allocation
   static constexpr int LDS_BYTES = TILE_END > PART_BYTES ? TILE_END : PART_BYTES;
   static_assert(DQ % 32 == 0 && DV % 32 == 0 && DQ <= 256 && DV <= 256, "padded head dims");
   static_assert(TQ_BYTES % 1024 == 0 && TD_BYTES % 1024 == 0 && V_BYTES % 1024 == 0,
                 "tiles are whole 1 KB transfers");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget (one workgroup per CU)");
+  static_assert(LDS_BYTES <= (NMT == 1 ? 80 : 160) * 1024, "LDS budget (two workgroups per CU, or one)");
 };
 
 // dK and dV of one (kv tile, K/V head, sequence). Row group r = w % NG owns kv rows 32 r .. 32 r + 31,
@@ -576,12 +584,12 @@ struct DkdvCfg {
 // where both accumulators of a wave would not fit its registers next to the K and V fragments: the
 // waves of a group swap P and dS through LDS each step, and the M-tile 0 wave accumulates dV over
 // both M-tiles, the other dK.
-template <int DQ, int DV, bool CAUSAL, bool WINDOW, bool EXACT>
-__global__ __attribute__((amdgpu_flat_work_group_size(DkdvCfg<DQ, DV>::NT, DkdvCfg<DQ, DV>::NT),
-                          amdgpu_waves_per_eu(DkdvCfg<DQ, DV>::WPE, DkdvCfg<DQ, DV>::WPE)))
+template <int DQ, int DV, bool CAUSAL, bool WINDOW, bool EXACT, int NMT>
+__global__ __attribute__((amdgpu_flat_work_group_size(DkdvCfg<DQ, DV, NMT>::NT, DkdvCfg<DQ, DV, NMT>::NT),
+                          amdgpu_waves_per_eu(DkdvCfg<DQ, DV, NMT>::WPE, DkdvCfg<DQ, DV, NMT>::WPE)))
 void fa_bwd_dkdv(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = DkdvCfg<DQ, DV>;
+  using C = DkdvCfg<DQ, DV, NMT>;
   constexpr int BN = C::BN, BM = C::BM, NG = C::NG, QSQ = C::QSQ, QSV = C::QSV;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   const bf16* s_v = (const bf16*)(smem + C::OFF_V);
@@ -937,6 +945,9 @@ void fa_bwd_dkdv(MainArgs a) {
       store_dv(acc_w);
     else
       store_dk(acc_w);
+  } else if constexpr (C::NMT == 1) {  // each wave holds the whole sums of its keys
+    store_dv(acc_v);
+    store_dk(acc_k);
   } else {
     // combine the two M-tiles' partial sums through LDS, laid out as [NG][NTQ] partial dK tiles, then
     // [NG][NTV] partial dV tiles, each as 4 quarters of 64 lanes x 16 bytes (lane-contiguous, so the

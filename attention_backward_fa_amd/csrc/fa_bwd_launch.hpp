@@ -20,15 +20,25 @@ struct Recompute {
     return (int64_t)((max_seqlen_q + DqCfg<DQ, DV>::BQ - 1) / DqCfg<DQ, DV>::BQ) * H * batch;
   }
 
-  // items: the workgroup count of a host schedule (a.sched), else unused
-  static void dkdv(const MainArgs& a, int64_t items, hipStream_t s) {
-    const dim3 grid((unsigned)(a.sched ? items : dkdv_blocks(a))), block(DkdvCfg<DQ, DV>::NT);
+  template <int NMT>
+  static void dkdv_layout(const MainArgs& a, int64_t items, hipStream_t s) {
+    const dim3 grid((unsigned)(a.sched ? items : dkdv_blocks(a))), block(DkdvCfg<DQ, DV, NMT>::NT);
     if (a.window > 0)  // the window implies the causal bound
-      fa_bwd_dkdv<DQ, DV, true, true, EXACT><<<grid, block, 0, s>>>(a);
+      fa_bwd_dkdv<DQ, DV, true, true, EXACT, NMT><<<grid, block, 0, s>>>(a);
     else if (a.causal)
-      fa_bwd_dkdv<DQ, DV, true, false, EXACT><<<grid, block, 0, s>>>(a);
+      fa_bwd_dkdv<DQ, DV, true, false, EXACT, NMT><<<grid, block, 0, s>>>(a);
     else
-      fa_bwd_dkdv<DQ, DV, false, false, EXACT><<<grid, block, 0, s>>>(a);
+      fa_bwd_dkdv<DQ, DV, false, false, EXACT, NMT><<<grid, block, 0, s>>>(a);
+  }
+  // items: the workgroup count of a host schedule (a.sched), else unused; four_waves: the four-wave
+  // layout (heads up to 128; wider heads have one layout)
+  static void dkdv(const MainArgs& a, int64_t items, bool four_waves, hipStream_t s) {
+    if constexpr (DkdvCfg<DQ, DV>::WIDE)
+      dkdv_layout<2>(a, items, s);
+    else if (four_waves)
+      dkdv_layout<1>(a, items, s);
+    else
+      dkdv_layout<2>(a, items, s);
   }
 
   static void dq(const MainArgs& a, int64_t items, hipStream_t s) {
@@ -54,17 +64,19 @@ struct Recompute {
 
 // The launches of one pair of padded head dims, and the tile sizes a host schedule counts in.
 struct KernelSet {
-  void (*dkdv)(const MainArgs&, int64_t, hipStream_t);
+  void (*dkdv)(const MainArgs&, int64_t, bool, hipStream_t);
   void (*dq)(const MainArgs&, int64_t, hipStream_t);
   void (*fwd)(const FwdArgs&, bool, int64_t, hipStream_t);
-  int kv_tile, q_step;  // dK/dV kernel: kv rows per workgroup, q rows per step
+  int kv_tile, q_step;  // dK/dV kernel: kv rows per workgroup, q rows per step (eight-wave layout)
+  bool two_layouts;     // the dK/dV kernel also has the four-wave layout
   int q_tile, kv_step;  // dQ kernel and forward: q rows per workgroup, kv rows per step
 };
 
 template <int DQ, int DV, bool EXACT>
 KernelSet kernel_set() {
   using R = Recompute<DQ, DV, EXACT>;
-  return {R::dkdv, R::dq, R::fwd, DkdvCfg<DQ, DV>::BN, DkdvCfg<DQ, DV>::BM, DqCfg<DQ, DV>::BQ, DqCfg<DQ, DV>::BK};
+  return {R::dkdv, R::dq, R::fwd, DkdvCfg<DQ, DV>::BN, DkdvCfg<DQ, DV>::BM, !DkdvCfg<DQ, DV>::WIDE,
+          DqCfg<DQ, DV>::BQ, DqCfg<DQ, DV>::BK};
 }
 
 // The pairs (128, 256), (256, 128) and (256, 256), from fa_bwd_wide.hip; pq, pv are padded dims,

@@ -46,9 +46,12 @@ if ROOT not in sys.path:
 METRIC = "FA-bwd TFLOP/s + % bf16 MFMA peak, S=8192 H=32 D=128 causal, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MASK_NAMES = {0: "none", 1: "padding", 2: "causal", 3: "padding_causal"}
-ALGORITHMS = {"default": 0, "single-pass": 1, "recompute": 2, "split-reduce": 3}
-ALGORITHM_NAMES = {1: "single-pass (dQ atomics)", 2: "recompute (dK/dV kernel + dQ kernel)",
-                   3: "split-reduce (single-pass main kernel over 8 kv-tile splits + fixed-order dQ sum)"}
+ALGORITHMS = {"default": 0, "single-pass": 1, "recompute": 2, "split-reduce": 3, "recompute-8w": 4, "recompute-4w": 5}
+ALGORITHM_NAMES = {1: "single-pass (dQ atomics)",
+                   2: "recompute (dK/dV kernel + dQ kernel; dK/dV layout chosen by load balance)",
+                   3: "split-reduce (single-pass main kernel over 8 kv-tile splits + fixed-order dQ sum)",
+                   4: "recompute (dK/dV kernel in eight-wave workgroups + dQ kernel)",
+                   5: "recompute (dK/dV kernel in four-wave workgroups + dQ kernel)"}
 def kernel_share(algorithm: int, d: int, dv: int) -> dict:
     """Share of the 5-GEMM algorithmic FLOPs each kernel runs itself. S = QK^T, dK, dQ contract or
     produce the query/key head dim d, dP, dV the value head dim dv (2 * pairs * dim FLOPs each)."""

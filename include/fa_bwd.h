@@ -67,14 +67,25 @@ typedef enum {
                                    fixed), then cast to bf16 */
   FA_BWD_ALGO_RECOMPUTE_DQ = 2, /* the article's two-pass fallback: a kv-outer kernel forms dK, dV and a
                                    q-outer kernel recomputes S and dP to form dQ in registers; no
-                                   atomics, no dQ workspace, bitwise reproducible */
-  FA_BWD_ALGO_SPLIT_REDUCE = 3  /* the single-pass structure with a fixed-order dQ reduction in place of
+                                   atomics, no dQ workspace, bitwise reproducible. For head dims up to
+                                   128 the kv-outer kernel has two layouts, chosen per run by load
+                                   balance (the four-wave one when the largest workgroup, doubled,
+                                   fits within the average work per compute unit) */
+  FA_BWD_ALGO_SPLIT_REDUCE = 3, /* the single-pass structure with a fixed-order dQ reduction in place of
                                    the atomics (the article gives a fixed summation order as a reason for
                                    its two-pass fallback; this keeps one pass): 8 workgroups per (head,
                                    sequence) each walk every 8th kv tile and keep their dQ partial sums
                                    in a buffer of their own (8 fp32 copies of dQ in the workspace); a
                                    last kernel sums the 8 buffers in a fixed order and casts to bf16;
                                    bitwise reproducible. Same restrictions as FA_BWD_ALGO_SINGLE_PASS */
+  FA_BWD_ALGO_RECOMPUTE_DQ_8W = 4, /* FA_BWD_ALGO_RECOMPUTE_DQ with the eight-wave layout of the kv-outer
+                                   kernel: one workgroup per compute unit, the two waves of each 32-key
+                                   group split every 64-row q step */
+  FA_BWD_ALGO_RECOMPUTE_DQ_4W = 5  /* FA_BWD_ALGO_RECOMPUTE_DQ with the four-wave layout: two workgroups
+                                   per compute unit, each wave takes whole 32-row q steps for its 32
+                                   keys. Both layouts give the same results within fp32 rounding (the
+                                   order of the dK, dV sums differs); for head dims above 128 both
+                                   codes run the one wide-head layout */
 } fa_bwd_algo;
 
 typedef enum {

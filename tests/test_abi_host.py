@@ -72,7 +72,7 @@ def _create(**kw):
     (dict(head_dim=64, head_dim_v=128, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(num_heads=4, num_heads_kv=1, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(window=32, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
-    (dict(algorithm=4), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(algorithm=6), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(algorithm=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(total_q=1 << 40, num_heads=8), B.FA_BWD_ERR_INVALID_ARGUMENT),          # index range
     (dict(max_seqlen_kv=1 << 30, num_heads=1 << 10, batch=1 << 10), B.FA_BWD_ERR_INVALID_ARGUMENT),  # grid size

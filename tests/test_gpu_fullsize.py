@@ -22,7 +22,8 @@ from tests import parity as P
 pytestmark = pytest.mark.gpu
 
 FULL = ["dense", "varlen", "causal", "longpad"]
-ALGOS = {"default": B.FA_BWD_ALGO_DEFAULT, "singlepass": B.FA_BWD_ALGO_SINGLE_PASS,
+ALGOS = {"default": B.FA_BWD_ALGO_DEFAULT, "eightwave": B.FA_BWD_ALGO_RECOMPUTE_DQ_8W,
+         "fourwave": B.FA_BWD_ALGO_RECOMPUTE_DQ_4W, "singlepass": B.FA_BWD_ALGO_SINGLE_PASS,
          "splitreduce": B.FA_BWD_ALGO_SPLIT_REDUCE}
 # the workloads with grouped K/V heads, a window or other head dims run the recompute form only
 VARIANTS = ["causal_gqa", "causal_window", "causal_d256", "causal_mla"]

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+from attention_backward_fa_amd import binding as B
 from attention_backward_fa_amd import inputs as I
 from tests import parity as P
 from tests.test_gpu_forward import check_forward, gpu_forward
@@ -54,8 +55,9 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("algo", [B.FA_BWD_ALGO_RECOMPUTE_DQ_8W, B.FA_BWD_ALGO_RECOMPUTE_DQ_4W], ids=["8w", "4w"])
 @pytest.mark.parametrize("case", CASES, ids=[c.name for c in CASES])
-def test_parity_head_dims(case):
+def test_parity_head_dims(case, algo):
     inp = I.make(case)
     dv = case.head_dim_v or case.head_dim
     print(f"[headdim] {case.name}: d={case.head_dim} d_v={dv} H={case.heads} H_kv={inp['k'].shape[1]} "
@@ -68,7 +70,7 @@ def test_parity_head_dims(case):
         vk = torch.from_numpy(oracle.valid_rows(inp["cu_kv"], case.mask, inp["max_seqlen_kv"], inp["k"].shape[0]))
         inp["k"][~vk] = float("nan")
         inp["v"][~vk] = float("nan")
-    gpu = P.run_gpu(inp, o, m, l)
+    gpu = P.run_gpu(inp, o, m, l, algorithm=algo)
     assert gpu[0].shape[2] == case.head_dim and gpu[2].shape[2] == dv
     ref = P.oracle_backward(inp, o, m, l)
     res = P.check_full(inp, gpu, ref)

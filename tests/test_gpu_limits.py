@@ -55,7 +55,8 @@ def _head(inp, o, m, l, h):
 @pytest.mark.parametrize("d,algos", [
     (256, [B.FA_BWD_ALGO_DEFAULT]),
     (248, [B.FA_BWD_ALGO_DEFAULT]),
-    (128, [B.FA_BWD_ALGO_DEFAULT, B.FA_BWD_ALGO_SINGLE_PASS, B.FA_BWD_ALGO_SPLIT_REDUCE]),
+    (128, [B.FA_BWD_ALGO_RECOMPUTE_DQ_8W, B.FA_BWD_ALGO_RECOMPUTE_DQ_4W, B.FA_BWD_ALGO_SINGLE_PASS,
+           B.FA_BWD_ALGO_SPLIT_REDUCE]),
 ])
 def test_largest_row_stride(d, algos):
     heads = _limit_heads(d)

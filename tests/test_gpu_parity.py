@@ -36,8 +36,10 @@ CASES = [
 ]
 
 
-ALGOS = {"recompute": B.FA_BWD_ALGO_RECOMPUTE_DQ, "singlepass": B.FA_BWD_ALGO_SINGLE_PASS,
+ALGOS = {"recompute": B.FA_BWD_ALGO_RECOMPUTE_DQ, "recompute8w": B.FA_BWD_ALGO_RECOMPUTE_DQ_8W,
+         "recompute4w": B.FA_BWD_ALGO_RECOMPUTE_DQ_4W, "singlepass": B.FA_BWD_ALGO_SINGLE_PASS,
          "splitreduce": B.FA_BWD_ALGO_SPLIT_REDUCE}
+LAYOUTS = {"8w": B.FA_BWD_ALGO_RECOMPUTE_DQ_8W, "4w": B.FA_BWD_ALGO_RECOMPUTE_DQ_4W}
 
 
 @pytest.mark.parametrize("algo", list(ALGOS))
@@ -75,14 +77,30 @@ def test_repeat_runs_agree_single_pass():
         P.assert_close("repeat", x.numpy(), y.numpy().astype(np.float64))
 
 
-def test_recompute_is_bitwise_reproducible():
-    """No atomics in the recompute form: repeated runs are bitwise identical."""
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_recompute_is_bitwise_reproducible(layout):
+    """No atomics in the recompute form: repeated runs are bitwise identical, in either dK/dV layout."""
     inp = I.make(I.custom_case("repro", 4, 128, I.MASK_CAUSAL, 210, [700, 333]))
     o, m, l = P.oracle_stats(inp)
-    a = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_RECOMPUTE_DQ)
-    b = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_RECOMPUTE_DQ)
+    a = P.run_gpu(inp, o, m, l, algorithm=LAYOUTS[layout])
+    b = P.run_gpu(inp, o, m, l, algorithm=LAYOUTS[layout])
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("case", [I.custom_case("layouts_causal", 3, 128, I.MASK_CAUSAL, 211, [700, 333, 64]),
+                                  I.custom_case("layouts_padded", 2, 64, I.MASK_PADDING, 212, [250, 97],
+                                                padded_len=256)], ids=lambda c: c.name)
+def test_dkdv_layouts_agree(case):
+    """The two dK/dV layouts share the dQ kernel (dQ bitwise equal); their dK, dV differ only in the
+    order of the fp32 sums, so they agree within the tolerance."""
+    inp = I.make(case)
+    o, m, l = P.oracle_stats(inp)
+    a = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_RECOMPUTE_DQ_8W)
+    b = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_RECOMPUTE_DQ_4W)
+    assert torch.equal(a[0], b[0]), "dq differs between the layouts"
+    for name, x, y in zip(("dk", "dv"), a[1:], b[1:]):
+        P.assert_close(name, y.numpy(), x.numpy().astype(np.float64))
 
 
 # sequences longer than 8 kv tiles of 128 keys: each split-reduce workgroup walks several tiles and

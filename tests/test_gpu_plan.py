@@ -28,10 +28,10 @@ def _tensors(inp, dev):
     return {k: inp[k].to(dev) for k in ("q", "k", "v", "do", "cu_q", "cu_kv")}
 
 
-def _op(inp, case):
+def _op(inp, case, algorithm=B.FA_BWD_ALGO_DEFAULT):
     return B.FaBwd(inp["batch"], case.heads, case.head_dim, inp["max_seqlen_q"], inp["max_seqlen_kv"],
-                   inp["q"].shape[0], inp["k"].shape[0], num_heads_kv=inp["k"].shape[1], window=inp["window"],
-                   head_dim_v=inp["v"].shape[2])
+                   inp["q"].shape[0], inp["k"].shape[0], algorithm, num_heads_kv=inp["k"].shape[1],
+                   window=inp["window"], head_dim_v=inp["v"].shape[2])
 
 
 def _run(op, inp, t, o, m, l):
@@ -41,14 +41,15 @@ def _run(op, inp, t, o, m, l):
     return [x.clone() for x in (dq, dk, dv, fo, fm, fl)]
 
 
+@pytest.mark.parametrize("algo", [B.FA_BWD_ALGO_DEFAULT, B.FA_BWD_ALGO_RECOMPUTE_DQ_4W], ids=["default", "4w"])
 @pytest.mark.parametrize("case", CASES, ids=[c.name for c in CASES])
-def test_planned_equals_dense_bitwise(case):
+def test_planned_equals_dense_bitwise(case, algo):
     inp = I.make(case)
-    print(f"[plan] {case.name}: lengths {inp['seqlens_q']} mask {case.mask}", flush=True)
+    print(f"[plan] {case.name}: lengths {inp['seqlens_q']} mask {case.mask} algorithm {algo}", flush=True)
     dev = torch.device("cuda")
     t = _tensors(inp, dev)
     o, m, l = (x.to(dev) for x in P.oracle_stats(inp))
-    with _op(inp, case) as op:
+    with _op(inp, case, algo) as op:
         dense = _run(op, inp, t, o, m, l)
         op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
         planned = _run(op, inp, t, o, m, l)

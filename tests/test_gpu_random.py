@@ -54,13 +54,15 @@ def test_random_configuration(case):
     print(f"[random] {case.name}: lq {inp['seqlens_q']} lk {inp['seqlens_kv']} padded {case.padded_len}", flush=True)
     o, m, l = P.oracle_stats(inp)
     ref = P.oracle_backward(inp, o, m, l)
-    gpu = P.run_gpu(inp, o, m, l)
+    # the two dK/dV layouts in turn (heads above 128 have one layout)
+    algo = (B.FA_BWD_ALGO_RECOMPUTE_DQ_8W, B.FA_BWD_ALGO_RECOMPUTE_DQ_4W)[CASES.index(case) % 2]
+    gpu = P.run_gpu(inp, o, m, l, algorithm=algo)
     res = P.check_full(inp, gpu, ref)
     # the same run from a host schedule: bitwise the same
     dev = torch.device("cuda")
     t = {k: inp[k].to(dev) for k in ("q", "k", "v", "do", "cu_q", "cu_kv")}
     with B.FaBwd(inp["batch"], case.heads, case.head_dim, inp["max_seqlen_q"], inp["max_seqlen_kv"],
-                 inp["q"].shape[0], inp["k"].shape[0], num_heads_kv=inp["k"].shape[1], window=inp["window"],
+                 inp["q"].shape[0], inp["k"].shape[0], algo, num_heads_kv=inp["k"].shape[1], window=inp["window"],
                  head_dim_v=inp["v"].shape[2]) as op:
         op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
         planned = op.run(t["q"], t["k"], t["v"], o.to(dev), t["do"], m.to(dev), l.to(dev), t["cu_q"], t["cu_kv"],
