@@ -67,7 +67,8 @@ void dkdv_work(int64_t lq, int64_t lk, bool causal, int64_t w, int64_t& total, i
 // The four-wave dK/dV layout runs two workgroups per CU, each at about half the rate of one
 // eight-wave workgroup. Longest-first dispatch then balances only while the largest workgroup,
 // doubled, still fits within the average work per CU; otherwise the eight-wave layout is kept.
-bool four_waves_balances(int64_t total, int64_t largest, int cus) { return 2 * largest * cus <= total; }
+// (in double: with the largest descriptors the products pass the int64 range)
+bool four_waves_balances(double total, double largest, int cus) { return 2.0 * largest * cus <= total; }
 
 // threads per (token, head) row of the row kernels: a power of two covering the wider row in
 // 8-element chunks
@@ -477,7 +478,7 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
     for (int c = 0; c < 2; ++c) {
       int64_t total = 0, largest = 0;
       dkdv_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), total, largest);
-      h->four_dense[c] = four_waves_balances(total * per_tile_heads, largest * G, cus);
+      h->four_dense[c] = four_waves_balances((double)total * (double)per_tile_heads, (double)largest * G, cus);
     }
   }
   const size_t stats = (size_t)desc->total_q * desc->num_heads;
