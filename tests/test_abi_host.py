@@ -23,6 +23,16 @@ def test_header_declarations_match_binding():
     assert declared_functions() == sorted(B.EXPORTED)
 
 
+def test_header_enum_values_match_binding():
+    """Every FA_BWD_* enumerator of the header has the same value in the binding (mask codes,
+    algorithm codes, status codes)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    values = {name: int(v) for name, v in re.findall(r"\b(FA_BWD_[A-Z0-9_]+)\s*=\s*(-?\d+)", text)}
+    assert {"FA_BWD_ALGO_RECOMPUTE_DQ_8W", "FA_BWD_ALGO_RECOMPUTE_DQ_4W", "FA_BWD_MASK_CAUSAL", "FA_BWD_OK"} <= set(values)
+    for name, v in values.items():
+        assert getattr(B, name) == v, name
+
+
 def test_library_exports_every_declared_symbol():
     lib = B.load_library()
     for name in declared_functions():
