@@ -103,6 +103,26 @@ def test_dkdv_layouts_agree(case):
         P.assert_close(name, y.numpy(), x.numpy().astype(np.float64))
 
 
+@pytest.mark.parametrize("case,expect", [
+    # causal, 256 heads of 1024 tokens: the dK/dV work (64-row q steps) totals 72 per head, 18432 in
+    # all; the largest workgroup has 16, and 2 * 16 * 256 CUs = 8192 <= 18432: the four-wave layout
+    (I.custom_case("layout_rule_4w", 256, 128, I.MASK_CAUSAL, 213, [1024]), B.FA_BWD_ALGO_RECOMPUTE_DQ_4W),
+    # no mask, 8 heads of 2 x 2048 tokens: 256 workgroups of 32 steps each; 2 * 32 * 256 > 8192: eight waves
+    (I.custom_case("layout_rule_8w", 8, 128, I.MASK_NONE, 214, [2048, 2048]), B.FA_BWD_ALGO_RECOMPUTE_DQ_8W),
+], ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_default_picks_the_balanced_dkdv_layout(case, expect):
+    """The default form takes the dK/dV layout the load-balance rule names (figures for the 256
+    compute units of an MI355X): its results equal that layout's bitwise."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the expected layouts are worked out for 256 compute units")
+    inp = I.make(case)
+    o, m, l = P.oracle_stats(inp)
+    got = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_DEFAULT)
+    ref = P.run_gpu(inp, o, m, l, algorithm=expect)
+    for name, x, y in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(x, y), f"{name}: the default form did not take the expected layout"
+
+
 # sequences longer than 8 kv tiles of 128 keys: each split-reduce workgroup walks several tiles and
 # adds into its own dQ buffer (the first tile stores, later ones load and add)
 LONG_CASES = [
