@@ -125,7 +125,11 @@ typedef struct {
 /* Validates desc (a num_heads_kv of 0 is stored as num_heads) and allocates
  * the device workspace of the handle on the current HIP device: two fp32 [H][total_q] row-statistic arrays and, for
  * FA_BWD_ALGO_SINGLE_PASS only, an fp32 dQ accumulator of total_q*H*head_dim
- * floats (8 of them for FA_BWD_ALGO_SPLIT_REDUCE). On success *out holds a new handle; on failure *out is set to NULL.
+ * floats (8 of them for FA_BWD_ALGO_SPLIT_REDUCE). For FA_BWD_ALGO_DEFAULT and
+ * FA_BWD_ALGO_RECOMPUTE_DQ it also fixes the kv-outer kernel's layout for runs
+ * without and with a causal bound, from the descriptor (every sequence taken at
+ * the maximum lengths) and the device's compute-unit count; planned runs use the
+ * same layout. On success *out holds a new handle; on failure *out is set to NULL.
  * Host-side checks run before any HIP call. */
 fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out);
 
