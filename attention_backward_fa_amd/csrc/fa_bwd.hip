@@ -33,6 +33,9 @@ struct fa_bwd_handle {
   // dense runs of a handle take the same layout, so that they agree bitwise
   int32_t dkdv_layout;  // 0: chosen, 1: eight waves, 2: four waves
   bool four_dense[2];
+  // dQ kernel's dense grid in head-major order per XCD (dq_head_major_balances), without and with a
+  // causal bound
+  bool dq_head_major[2];
 };
 
 namespace {
@@ -69,6 +72,27 @@ void dkdv_work(int64_t lq, int64_t lk, bool causal, int64_t w, int64_t& total, i
 // doubled, still fits within the average work per CU; otherwise the eight-wave layout is kept.
 // (in double: with the largest descriptors the products pass the int64 range)
 bool four_waves_balances(double total, double largest, int cus) { return 2.0 * largest * cus <= total; }
+
+// Work of the dQ kernel's workgroups of one sequence: the 64-key steps each 128-row q tile visits,
+// bounded as the kernel bounds its loop (causal end, window start).
+void dq_work(int64_t lq, int64_t lk, bool causal, int64_t w, int64_t& total, int64_t& largest) {
+  for (int64_t i0 = 0; i0 < lq; i0 += 128) {
+    int64_t n_kt = (lk + 63) / 64;
+    if (causal) n_kt = std::min(n_kt, (i0 + 127) / 64 + 1);
+    const int64_t t0 = w > 0 ? std::max<int64_t>(0, i0 - w + 1) / 64 : 0;
+    const int64_t work = std::max<int64_t>(0, n_kt - t0);
+    total += work;
+    largest = std::max(largest, work);
+  }
+}
+
+// Head-major order per XCD (each of the 8 XCDs takes the q tiles of one (sequence, head) at a time, so
+// that its workgroups share K and V tiles in L2) starts the last head's heaviest tiles late; it is
+// taken when the heads x sequences divide over the XCDs and the largest workgroup is at most a
+// quarter of the work per slot (two workgroups per CU), where that lateness costs little.
+bool dq_head_major_balances(double total, double largest, int cus, int64_t heads_x_seqs) {
+  return heads_x_seqs % 8 == 0 && 8.0 * largest * cus <= total;
+}
 
 // threads per (token, head) row of the row kernels: a power of two covering the wider row in
 // 8-element chunks
@@ -281,6 +305,7 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.d_v = d.head_dim_v;
   ma.scale_log2 = scale * fa::kLog2e;
   ma.scale = scale;
+  ma.head_major = 0;
   const fa::KernelSet ks = pick_kernels(d.head_dim, d.head_dim_v);
   const bool planned = h->sched && h->plan_mask == mask;
   ma.sched = planned ? h->sched : nullptr;
@@ -303,6 +328,7 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
       d.head_dim == 128 ? launch_cast<128>(ma, stream) : launch_cast<64>(ma, stream);
   } else if (!planned || h->n_q_items > 0) {
     ma.sched = planned ? h->sched + 2 * h->n_kv_items : nullptr;
+    ma.head_major = h->dq_head_major[causal] ? 1 : 0;
     ks.dq(ma, h->n_q_items, stream);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
@@ -479,6 +505,10 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
       int64_t total = 0, largest = 0;
       dkdv_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), total, largest);
       h->four_dense[c] = four_waves_balances((double)total * (double)per_tile_heads, (double)largest * G, cus);
+      int64_t qtotal = 0, qlargest = 0;
+      dq_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), qtotal, qlargest);
+      h->dq_head_major[c] =
+          dq_head_major_balances((double)qtotal * (double)per_tile_heads, (double)qlargest, cus, per_tile_heads);
     }
   }
   const size_t stats = (size_t)desc->total_q * desc->num_heads;

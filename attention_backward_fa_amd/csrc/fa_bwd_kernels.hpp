@@ -136,6 +136,8 @@ struct MainArgs {
   float scale_log2;  // scale * log2(e)
   float scale;
   const int* sched;  // recompute kernels: (tile, sequence * heads + head) per workgroup, or null (dense grid)
+  int head_major;    // dQ kernel, dense grid, heads x sequences a multiple of 8: each XCD takes the q
+                     // tiles of one (sequence, head) at a time
 };
 
 // Splits of the split-and-reduce form: workgroups per (head, sequence), each with its own fp32 dQ
@@ -1069,11 +1071,25 @@ void fa_bwd_dq(MainArgs a) {
   constexpr int BQ = C::BQ, BK = C::BK, QSQ = C::QSQ, QSV = C::QSV;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
-  // the host schedule names each workgroup's (q tile, sequence * H + head); in the dense grid under
-  // a causal mask the q tiles with the most keys (the last ones) dispatch first
+  // the host schedule names each workgroup's (q tile, sequence * H + head). The dense grid runs the q
+  // tiles with the most keys (under a causal mask the last ones) first, tile-major over the heads and
+  // sequences; or, head-major per XCD (workgroup i runs on XCD i % 8): XCD x takes the tiles of
+  // (sequence, head) x, then x + 8, ..., so that its workgroups stream the same K and V tiles
   const int HB = a.H * a.batch;
-  const int tr = a.sched ? 0 : blockIdx.x / HB;
-  const int hb = a.sched ? a.sched[2 * blockIdx.x + 1] : blockIdx.x - tr * HB;
+  const int n_qt_max = (a.max_seqlen_q + BQ - 1) / BQ;
+  int tr, hb;
+  if (a.sched) {
+    tr = 0;
+    hb = a.sched[2 * blockIdx.x + 1];
+  } else if (a.head_major) {  // HB % 8 == 0 (host): a bijection of the grid
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int k = slot / n_qt_max;
+    tr = slot - k * n_qt_max;
+    hb = x + 8 * k;
+  } else {
+    tr = blockIdx.x / HB;
+    hb = blockIdx.x - tr * HB;
+  }
   const int b = hb / a.H, h = hb - (hb / a.H) * a.H;
   int64_t q_start, kv_start;
   int Lq, Lk;
@@ -1081,7 +1097,6 @@ void fa_bwd_dq(MainArgs a) {
   seq_of(a.cu_kv, b, a.padded, a.max_seqlen_kv, kv_start, Lk);
   Lq = clamp_len(q_start, Lq, a.total_q);
   Lk = clamp_len(kv_start, Lk, a.total_kv);
-  const int n_qt_max = (a.max_seqlen_q + BQ - 1) / BQ;
   const int qtile = a.sched ? a.sched[2 * blockIdx.x] : CAUSAL ? n_qt_max - 1 - tr : tr;
   const int i0 = qtile * BQ;
   if (i0 >= Lq) return;
