@@ -33,9 +33,9 @@ struct fa_bwd_handle {
   // dense runs of a handle take the same layout, so that they agree bitwise
   int32_t dkdv_layout;  // 0: chosen, 1: eight waves, 2: four waves
   bool four_dense[2];
-  // dQ kernel's dense grid in head-major order per XCD (dq_head_major_balances), without and with a
-  // causal bound
-  bool dq_head_major[2];
+  // the dQ and dK/dV kernels' dense grids in head-major order per XCD (head_major_balances), without
+  // and with a causal bound
+  bool dq_head_major[2], dkdv_head_major[2];
 };
 
 namespace {
@@ -86,12 +86,12 @@ void dq_work(int64_t lq, int64_t lk, bool causal, int64_t w, int64_t& total, int
   }
 }
 
-// Head-major order per XCD (each of the 8 XCDs takes the q tiles of one (sequence, head) at a time, so
-// that its workgroups share K and V tiles in L2) starts the last head's heaviest tiles late; it is
-// taken when the heads x sequences divide over the XCDs and the largest workgroup is at most a
-// quarter of the work per slot (two workgroups per CU), where that lateness costs little.
-bool dq_head_major_balances(double total, double largest, int cus, int64_t heads_x_seqs) {
-  return heads_x_seqs % 8 == 0 && 8.0 * largest * cus <= total;
+// Head-major order per XCD (each of the 8 XCDs takes the tiles of one (sequence, head) at a time, so
+// that its workgroups share the other side's tiles in L2) starts the last head's heaviest tiles late;
+// it is taken when the heads x sequences divide over the XCDs and the largest workgroup is at most a
+// quarter of the work per workgroup slot, where that lateness costs little.
+bool head_major_balances(double total, double largest, int64_t slots, int64_t heads_x_seqs) {
+  return heads_x_seqs % 8 == 0 && 4.0 * largest * slots <= total;
 }
 
 // threads per (token, head) row of the row kernels: a power of two covering the wider row in
@@ -316,6 +316,7 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
       h->split ? launch_single_pass<64, true>(ma, causal, stream) : launch_single_pass<64, false>(ma, causal, stream);
   } else if (!planned || h->n_kv_items > 0) {
     const bool four = h->dkdv_layout == 2 || (h->dkdv_layout == 0 && h->four_dense[causal]);
+    ma.head_major = h->dkdv_head_major[causal] ? 1 : 0;
     ks.dkdv(ma, h->n_kv_items, four, stream);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
@@ -505,10 +506,17 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
       int64_t total = 0, largest = 0;
       dkdv_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), total, largest);
       h->four_dense[c] = four_waves_balances((double)total * (double)per_tile_heads, (double)largest * G, cus);
+      // heads up to 128: two workgroups per CU in the dQ kernel and the four-wave dK/dV layout, one in
+      // the eight-wave one; wider heads: one in both kernels
+      const int64_t kv_heads_x_seqs = (int64_t)hd.batch * hd.num_heads_kv;
+      const bool narrow = pick_kernels(hd.head_dim, hd.head_dim_v).two_layouts;
+      const bool four = narrow && (h->dkdv_layout == 2 || (h->dkdv_layout == 0 && h->four_dense[c]));
+      h->dkdv_head_major[c] = head_major_balances((double)total * (double)per_tile_heads, (double)largest * G,
+                                                  (int64_t)cus * (four ? 2 : 1), kv_heads_x_seqs);
       int64_t qtotal = 0, qlargest = 0;
       dq_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), qtotal, qlargest);
-      h->dq_head_major[c] =
-          dq_head_major_balances((double)qtotal * (double)per_tile_heads, (double)qlargest, cus, per_tile_heads);
+      h->dq_head_major[c] = head_major_balances((double)qtotal * (double)per_tile_heads, (double)qlargest,
+                                                (int64_t)cus * (narrow ? 2 : 1), per_tile_heads);
     }
   }
   const size_t stats = (size_t)desc->total_q * desc->num_heads;

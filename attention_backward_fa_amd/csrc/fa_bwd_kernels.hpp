@@ -136,8 +136,8 @@ struct MainArgs {
   float scale_log2;  // scale * log2(e)
   float scale;
   const int* sched;  // recompute kernels: (tile, sequence * heads + head) per workgroup, or null (dense grid)
-  int head_major;    // dQ kernel, dense grid, heads x sequences a multiple of 8: each XCD takes the q
-                     // tiles of one (sequence, head) at a time
+  int head_major;    // recompute kernels, dense grid, (K/V) heads x sequences a multiple of 8: each XCD
+                     // takes the tiles of one (sequence, head) at a time
 };
 
 // Splits of the split-and-reduce form: workgroups per (head, sequence), each with its own fp32 dQ
@@ -600,10 +600,24 @@ void fa_bwd_dkdv(MainArgs a) {
   float* s_st = (float*)(smem + C::OFF_ST);
 
   // the host schedule names each workgroup's (kv tile, sequence * Hk + K/V head); the dense grid
-  // puts the heavy (low) kv tiles of every head first
+  // puts the heavy (low) kv tiles first, tile-major over the heads and sequences, or head-major per
+  // XCD (workgroup i runs on XCD i % 8): XCD x takes the kv tiles of (sequence, K/V head) x, then
+  // x + 8, ..., so that its workgroups stream the same Q and dO tiles
   const int HB = a.Hk * a.batch;
-  const int tile = a.sched ? a.sched[2 * blockIdx.x] : blockIdx.x / HB;
-  const int hb = a.sched ? a.sched[2 * blockIdx.x + 1] : blockIdx.x - tile * HB;
+  int tile, hb;
+  if (a.sched) {
+    tile = a.sched[2 * blockIdx.x];
+    hb = a.sched[2 * blockIdx.x + 1];
+  } else if (a.head_major) {  // HB % 8 == 0 (host): a bijection of the grid
+    const int n_kt_max = (a.max_seqlen_kv + BN - 1) / BN;
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int k = slot / n_kt_max;
+    tile = slot - k * n_kt_max;
+    hb = x + 8 * k;
+  } else {
+    tile = blockIdx.x / HB;
+    hb = blockIdx.x - tile * HB;
+  }
   const int b = hb / a.Hk, hk = hb - (hb / a.Hk) * a.Hk;  // sequence, K/V head
   int64_t q_start, kv_start;
   int Lq, Lk;
