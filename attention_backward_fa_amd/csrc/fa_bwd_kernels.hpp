@@ -10,10 +10,15 @@
 //                  and runs the five GEMMs of steps 1, 3, 6, 7, 8 on bf16 MFMA
 //                  with the softmax recompute and dS (steps 2, 5) on the VALU;
 //                  dQ partial sums go to the fp32 accumulator with global
-//                  atomics.
+//                  atomics, or (split-and-reduce form) into the buffer of
+//                  one of 8 kv-tile splits with plain loads and stores.
 //   fa_bwd_dq_cast single-pass form: dQ = bf16(scale * accumulator). HBM bound.
+//   fa_bwd_split_reduce  split-and-reduce form: sums the 8 split buffers in a
+//                  fixed order and casts dQ to bf16. HBM bound.
 //   fa_bwd_dkdv    recompute form, kv-outer: steps 1-3 and 5-7 with two
-//                  waves per SIMD; dK, dV written once per kv tile.
+//                  waves per SIMD, each holding its keys' K rows in registers,
+//                  in eight-wave or four-wave workgroups; dK, dV written once
+//                  per kv tile.
 //   fa_bwd_dq      recompute form, q-outer: recomputes S^T and dP^T and
 //                  accumulates dQ (step 8) in registers; no atomics.
 //   fa_fwd_fill,   the forward that produces O, m, l (the statistics step 2
