@@ -43,6 +43,11 @@ What it computes, and where the pages define it:
   (the grouping of the jax cuDNN wrapper's attention API); dK and dV of a shared head are
   the sums over its query heads.
 
+* Query row blocks (``forward_blocked``, ``backward_blocked``): the same steps per block of query
+  rows with the block's full key range, for sizes whose whole-slice matrices do not fit in memory;
+  dK and dV add up the blocks' terms. Pinned against the whole-slice form, the invariants and
+  finite differences in the tests.
+
 Rows outside every sequence: forward gives O = 0, m = 0, l = 1 (finite filler
 that the backward never reads); backward gives dQ = dK = dV = 0. A valid query
 row with no visible key (only when its sequence has no keys) gets P = 0.
@@ -288,6 +293,150 @@ def loss(q, k, v, do, cu_q, cu_kv, scale: float, mask: int, max_seqlen_q: int = 
     """Scalar sum(O * dO) with dO a fixed cotangent; its gradient is (dQ, dK, dV)."""
     o, _, _ = forward(q, k, v, cu_q, cu_kv, scale, mask, max_seqlen_q, max_seqlen_kv, window)
     return float(np.sum(o * _f64(do)))
+
+
+# ---------------------------------------------------------------- query row blocks
+#
+# Full-size problems (a 32768-token sequence) do not fit the whole-slice matrices above (8 GiB per
+# fp64 matrix). The functions below take the same steps over blocks of query rows: each block holds
+# its rows' full key range, so every row is computed exactly as in the whole-slice form (no online
+# softmax), and dK, dV are sums over the blocks of the block's terms -- the sums over i in steps 6
+# and 7 split into partial sums, as the SK-16 article itself accumulates dK/dV over q tiles (§3.1).
+# A block looks only at the keys some row of it can see (keys past the block's last row under a
+# causal bound, keys before its first row's window); the others have P = 0 and add nothing.
+
+
+def key_range(i0: int, i1: int, lk: int, causal: bool, window: int = 0):
+    """[j0, j1): the keys that some query row of [i0, i1) may see (sequence-local indices)."""
+    j1 = min(lk, i1) if (causal or window > 0) else lk
+    j0 = max(0, i0 - window + 1) if window > 0 else 0
+    return j0, max(j0, j1)
+
+
+def forward_head_blocked(q, k, v, scale: float, causal: bool, window: int = 0, block: int = 256):
+    """``forward_head`` over blocks of ``block`` query rows. Returns O [Lq,d_v], m [Lq], l [Lq]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    lq, lk = q.shape[0], k.shape[0]
+    o = np.zeros((lq, v.shape[1]))
+    m = np.zeros(lq)
+    l = np.ones(lq)
+    for i0 in range(0, lq, block):
+        i1 = min(lq, i0 + block)
+        j0, j1 = key_range(i0, i1, lk, causal, window)
+        if j1 <= j0:
+            continue  # no row of the block sees a key: O = 0, m = 0, l = 1
+        vis = visible_block(np.arange(i0, i1), np.arange(j0, j1), causal, window)
+        s = scale * (q[i0:i1] @ k[j0:j1].T)
+        has_key = vis.any(axis=1)
+        mb = np.where(has_key, np.max(np.where(vis, s, -np.inf), axis=1, initial=-np.inf), 0.0)
+        e = np.where(vis, np.exp(np.where(vis, s - mb[:, None], 0.0)), 0.0)
+        lb = np.where(has_key, e.sum(axis=1), 1.0)
+        p = np.where(has_key[:, None], e / lb[:, None], 0.0)
+        o[i0:i1] = p @ v[j0:j1]
+        m[i0:i1] = mb
+        l[i0:i1] = lb
+    return o, m, l
+
+
+def backward_head_blocked(q, k, v, o, do, m, l, scale: float, causal: bool, window: int = 0, block: int = 256):
+    """``backward_head`` (steps 1-8) over blocks of ``block`` query rows: dQ rows of a block come from
+    that block alone, dK and dV add up the blocks' terms. Returns dq [Lq,d], dk [Lk,d], dv [Lk,d_v]."""
+    q, k, v, o, do = _f64(q), _f64(k), _f64(v), _f64(o), _f64(do)
+    m, l = _f64(m), _f64(l)
+    lq, lk = q.shape[0], k.shape[0]
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for i0 in range(0, lq, block):
+        i1 = min(lq, i0 + block)
+        j0, j1 = key_range(i0, i1, lk, causal, window)
+        if j1 <= j0:
+            continue  # no visible key: P = 0, so the block adds nothing and its dQ rows stay 0
+        rows, keys = slice(i0, i1), slice(j0, j1)
+        vis = visible_block(np.arange(i0, i1), np.arange(j0, j1), causal, window)
+        s = q[rows] @ k[keys].T                                   # 1
+        p = softmax_probs(scale * s, m[rows], l[rows], vis)      # 2
+        dp = do[rows] @ v[keys].T                                 # 3
+        dvec = np.sum(o[rows] * do[rows], axis=1)                 # 4
+        ds = p * (dp - dvec[:, None])                             # 5
+        dk[keys] += scale * (ds.T @ q[rows])                      # 6 (this block's terms)
+        dv[keys] += p.T @ do[rows]                                # 7 (this block's terms)
+        dq[rows] = scale * (ds @ k[keys])                         # 8
+    return dq, dk, dv
+
+
+def _slices(cu_q, cu_kv, mask, max_seqlen_q, max_seqlen_kv, heads_q, heads_kv):
+    """(query rows, key rows, query head, K/V head) of every (sequence, head) with rows on both sides."""
+    out = []
+    for (qs, lq), (ks, lk) in zip(segments(cu_q, mask, max_seqlen_q), segments(cu_kv, mask, max_seqlen_kv)):
+        if lq <= 0 or lk <= 0:
+            continue
+        for h in range(heads_q):
+            out.append((slice(qs, qs + lq), slice(ks, ks + lk), h, kv_head(h, heads_q, heads_kv)))
+    return out
+
+
+def _run_slices(fn, items, workers: int):
+    """fn over items, in order; with workers > 1 on a thread pool (the BLAS calls and the large
+    elementwise NumPy operations release the interpreter lock), BLAS held to one thread per call."""
+    if workers <= 1 or len(items) <= 1:
+        return [fn(it) for it in items]
+    from concurrent.futures import ThreadPoolExecutor
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1, user_api="blas")
+    except ImportError:  # pragma: no cover - BLAS then keeps its own thread count
+        limit = None
+    try:
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            return list(pool.map(fn, items))
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+
+
+def forward_blocked(q, k, v, cu_q, cu_kv, scale: float, mask: int, max_seqlen_q: int = 0, max_seqlen_kv: int = 0,
+                    window: int = 0, block: int = 256, workers: int = 1):
+    """``forward`` computed per (sequence, head) by ``forward_head_blocked``. fp64 O, m, l."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    tq, h_count, _ = q.shape
+    o = np.zeros((tq, h_count, v.shape[2]))
+    m = np.zeros((tq, h_count))
+    l = np.ones((tq, h_count))
+    causal = is_causal(mask)
+    items = _slices(cu_q, cu_kv, mask, max_seqlen_q, max_seqlen_kv, h_count, k.shape[1])
+
+    def one(it):
+        qsl, ksl, h, hk = it
+        return forward_head_blocked(q[qsl, h], k[ksl, hk], v[ksl, hk], scale, causal, window, block)
+
+    for (qsl, _, h, _), (ob, mb, lb) in zip(items, _run_slices(one, items, workers)):
+        o[qsl, h], m[qsl, h], l[qsl, h] = ob, mb, lb
+    return o, m, l
+
+
+def backward_blocked(q, k, v, o, do, m, l, cu_q, cu_kv, scale: float, mask: int, max_seqlen_q: int = 0,
+                     max_seqlen_kv: int = 0, window: int = 0, block: int = 256, workers: int = 1):
+    """``backward`` computed per (sequence, head) by ``backward_head_blocked``; a shared K/V head
+    collects the gradients of its query heads in query-head order. fp64 dQ, dK, dV."""
+    q, k, v, o, do = _f64(q), _f64(k), _f64(v), _f64(o), _f64(do)
+    m, l = _f64(m), _f64(l)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    causal = is_causal(mask)
+    items = _slices(cu_q, cu_kv, mask, max_seqlen_q, max_seqlen_kv, q.shape[1], k.shape[1])
+
+    def one(it):
+        qsl, ksl, h, hk = it
+        return backward_head_blocked(q[qsl, h], k[ksl, hk], v[ksl, hk], o[qsl, h], do[qsl, h], m[qsl, h], l[qsl, h],
+                                     scale, causal, window, block)
+
+    for (qsl, ksl, h, hk), (rq, rk, rv) in zip(items, _run_slices(one, items, workers)):
+        dq[qsl, h] = rq
+        dk[ksl, hk] += rk
+        dv[ksl, hk] += rv
+    return dq, dk, dv
 
 
 def valid_rows(cu, mask: int, max_seqlen: int, total: int) -> np.ndarray:

@@ -582,3 +582,100 @@ def test_planted_group_overwrite_fails_finite_differences(monkeypatch):
     assert fd_error(p) < 2e-6
     _mutant(monkeypatch, "backward", 'dk[ksl, hk] += r["dk"]', 'dk[ksl, hk] = r["dk"]')
     assert fd_error(p) > 1e-3
+
+
+# ---------------------------------------------------------------- the query-row-block form
+
+BLOCK_CASES = [
+    (MASK_NONE, [13, 1, 40], [9, 30, 17], 0),
+    (MASK_CAUSAL, [37, 5, 64], [37, 9, 64], 0),
+    (MASK_PADDING, [20, 33], [20, 33], 0),
+    (MASK_PADDING_CAUSAL, [29, 7], [25, 7], 0),
+    (MASK_CAUSAL, [45, 19], [45, 19], 6),
+    (MASK_NONE, [31, 0, 12], [31, 4, 12], 0),
+]
+
+
+@pytest.mark.parametrize("mask,lens_q,lens_kv,window", BLOCK_CASES)
+@pytest.mark.parametrize("block", [1, 3, 8, 64])
+def test_blocked_forward_backward_equal_whole_slice_form(mask, lens_q, lens_kv, window, block):
+    """Row blocks split the sums over query rows (steps 6, 7) and leave every row's own computation
+    unchanged, so both forms agree to rounding; blocks of one row, ragged last blocks and blocks that
+    see no key are covered."""
+    padded = max(max(lens_q), max(lens_kv)) + 3 if A.is_padded(mask) else 0
+    p = make_problem(mask, lens_q, lens_kv, heads=3, d=8, seed=61, padded_len=padded, heads_kv=1, window=window)
+    args = (p["cu_q"], p["cu_kv"], p["scale"], p["mask"], p["max_seqlen_q"], p["max_seqlen_kv"], window)
+    o, m, l = A.forward(p["q"], p["k"], p["v"], *args)
+    ob, mb, lb = A.forward_blocked(p["q"], p["k"], p["v"], *args, block=block, workers=2)
+    assert np.allclose(ob, o, rtol=1e-12, atol=1e-13) and np.allclose(mb, m, rtol=1e-13, atol=1e-14)
+    assert np.allclose(lb, l, rtol=1e-12)
+    ref = A.backward(p["q"], p["k"], p["v"], o, p["do"], m, l, *args)
+    got = A.backward_blocked(p["q"], p["k"], p["v"], o, p["do"], m, l, *args, block=block, workers=3)
+    for r, g in zip(ref, got):
+        assert np.allclose(g, r, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("mask", [MASK_NONE, MASK_CAUSAL])
+def test_blocked_form_keeps_the_invariants(mask):
+    """At a size the whole-slice pins do not reach (two 700-row sequences, blocks of 64): dK columns
+    sum to zero and dV columns sum to the dO columns of the rows that see keys (rows of P sum to 1)."""
+    p = make_problem(mask, [700, 333], [700, 333], heads=2, d=16, seed=62)
+    args = (p["cu_q"], p["cu_kv"], p["scale"], p["mask"], p["max_seqlen_q"], p["max_seqlen_kv"])
+    o, m, l = A.forward_blocked(p["q"], p["k"], p["v"], *args, block=64, workers=4)
+    dq, dk, dv = A.backward_blocked(p["q"], p["k"], p["v"], o, p["do"], m, l, *args, block=64, workers=4)
+    for (qs, lq), (ks, lk) in zip(A.segments(p["cu_q"], mask, 0), A.segments(p["cu_kv"], mask, 0)):
+        for h in range(2):
+            assert np.allclose(dk[ks:ks + lk, h].sum(axis=0), 0.0, atol=1e-9)
+            assert np.allclose(dv[ks:ks + lk, h].sum(axis=0), p["do"][qs:qs + lq, h].sum(axis=0), atol=1e-9)
+    if mask == MASK_CAUSAL:   # row 0 of a sequence sees only key 0 (P = 1): its dQ vanishes up to rounding
+        assert np.allclose(dq[0], 0.0, atol=1e-12) and np.allclose(dq[700], 0.0, atol=1e-12)
+
+
+def test_blocked_form_finite_differences():
+    """Central differences through the blocked forward with blocks of two rows (every block boundary
+    inside the sequences), against the blocked backward."""
+    p = make_problem(MASK_CAUSAL, [5, 4], [5, 4], heads=1, d=4, seed=63)
+    args = (p["cu_q"], p["cu_kv"], p["scale"], p["mask"], p["max_seqlen_q"], p["max_seqlen_kv"])
+
+    def loss():
+        o, _, _ = A.forward_blocked(p["q"], p["k"], p["v"], *args, block=2)
+        return float(np.sum(o * p["do"]))
+
+    o, m, l = A.forward_blocked(p["q"], p["k"], p["v"], *args, block=2)
+    grads = dict(zip(("q", "k", "v"), A.backward_blocked(p["q"], p["k"], p["v"], o, p["do"], m, l, *args, block=2)))
+    eps = 1e-6
+    for name in ("q", "k", "v"):
+        x = p[name]
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = loss()
+            x[idx] = keep - eps
+            lm = loss()
+            x[idx] = keep
+            assert abs((lp - lm) / (2 * eps) - grads[name][idx]) < 2e-6, (name, idx)
+
+
+BLOCK_MUTANTS = [
+    ("backward_head_blocked", "dk[keys] += scale * (ds.T @ q[rows])", "dk[keys] = scale * (ds.T @ q[rows])",
+     "dK keeps the last block only"),
+    ("backward_head_blocked", "dq[rows] = scale * (ds @ k[keys])", "dq[rows] = scale * (ds @ k[rows])",
+     "dQ contracted with the block's own rows"),
+    ("key_range", "j1 = min(lk, i1) if (causal or window > 0) else lk", "j1 = min(lk, i1 - 1) if (causal or window > 0) else lk",
+     "key range misses the block's diagonal key"),
+]
+
+
+@pytest.mark.parametrize("func,old,new,what", BLOCK_MUTANTS, ids=[m[3] for m in BLOCK_MUTANTS])
+def test_planted_block_mistake_is_caught(monkeypatch, func, old, new, what):
+    p = make_problem(MASK_CAUSAL, [9, 6], [9, 6], heads=1, d=4, seed=64)
+    args = (p["cu_q"], p["cu_kv"], p["scale"], p["mask"], p["max_seqlen_q"], p["max_seqlen_kv"])
+    o, m, l = A.forward(p["q"], p["k"], p["v"], *args)
+    ref = A.backward(p["q"], p["k"], p["v"], o, p["do"], m, l, *args)
+    _mutant(monkeypatch, func, old, new)
+    try:
+        got = A.backward_blocked(p["q"], p["k"], p["v"], o, p["do"], m, l, *args, block=4)
+        err = max(float(np.max(np.abs(g - r))) for g, r in zip(got, ref))
+    except ValueError:  # a shape error is also a caught mistake
+        err = float("inf")
+    assert err > 1e-3, what
