@@ -137,7 +137,10 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   if (d->algorithm == FA_BWD_ALGO_SPLIT_REDUCE && (int64_t)fa::kSplits * d->num_heads * d->batch > kMaxGrid)
     return FA_BWD_ERR_INVALID_ARGUMENT;
   const int64_t rows_per_block = 256 / threads_per_row(d->head_dim, dv);
-  if ((rows * d->num_heads + rows_per_block - 1) / rows_per_block > kMaxGrid) return FA_BWD_ERR_INVALID_ARGUMENT;
+  // the row kernels: one block per (group of rows_per_block tokens, head), or per rows_per_block rows
+  if ((rows + rows_per_block - 1) / rows_per_block * d->num_heads > kMaxGrid ||
+      (rows * d->num_heads + rows_per_block - 1) / rows_per_block > kMaxGrid)
+    return FA_BWD_ERR_INVALID_ARGUMENT;
   return FA_BWD_OK;
 }
 
@@ -264,13 +267,13 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   pa.d_qk = d.head_dim;
   pa.d_v = d.head_dim_v;
   const int tpr = threads_per_row(d.head_dim, d.head_dim_v);
-  const int64_t rows = (d.total_q > d.total_kv ? d.total_q : d.total_kv) * d.num_heads;
+  const int64_t tokens = d.total_q > d.total_kv ? d.total_q : d.total_kv;
   const int rpb = 256 / tpr;
   hipEvent_t* ev = nullptr;
   const fa_bwd_status es = next_events(h, &ev);
   if (es != FA_BWD_OK) return es;
   if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return FA_BWD_ERR_HIP;
-  const dim3 pre_grid((unsigned)((rows + rpb - 1) / rpb));
+  const dim3 pre_grid((unsigned)((tokens + rpb - 1) / rpb * d.num_heads));  // (token group, head) per block
   if (d.head_dim == d.head_dim_v && d.head_dim == 8 * tpr)
     launch_rows<fa::PreArgs, pre_kernel_exact>(tpr, pre_grid, stream, pa);
   else

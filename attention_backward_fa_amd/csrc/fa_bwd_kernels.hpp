@@ -76,14 +76,18 @@ struct PreArgs {
   int d_qk, d_v;  // head dims of Q, K (dQ, dK) and of V, O, dO (dV); multiples of 8
 };
 
-// One thread per 8 features of a (token, head) row, 256 / TPR rows per block; TPR is a power of two
-// >= max(d_qk, d_v) / 8. EXACT: d_qk = d_v = 8 TPR, known at compile time.
+// One thread per 8 features of a (token, head) row; TPR is a power of two >= max(d_qk, d_v) / 8.
+// Block i takes 256 / TPR consecutive tokens of head i % H (heads fastest across blocks, so the
+// blocks in flight read one contiguous range of tokens), which makes the statistics it writes
+// into the head-major [H][T_q] arrays one contiguous run. EXACT: d_qk = d_v = 8 TPR.
 template <int TPR, bool EXACT>
 __global__ __launch_bounds__(256) void fa_bwd_pre(PreArgs a) {
+  constexpr int RPB = 256 / TPR;  // tokens per block
   const int sub = threadIdx.x & (TPR - 1);
-  const int64_t pair = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;  // = t * H + h
-  const int64_t t = pair / a.H;
-  const int h = (int)(pair - t * a.H);
+  const unsigned grp = blockIdx.x / (unsigned)a.H;
+  const int h = (int)(blockIdx.x - grp * (unsigned)a.H);
+  const int64_t t = (int64_t)grp * RPB + threadIdx.x / TPR;
+  const int64_t pair = t * a.H + h;
   const int cq = EXACT ? TPR : a.d_qk / 8, cv = EXACT ? TPR : a.d_v / 8;  // 16-byte chunks per row
   const u32x4 z = {0u, 0u, 0u, 0u};
   if (t < a.total_q) {

@@ -26,6 +26,15 @@ kernel sources still hash to the recorded value, else null) and a
 ``cpu_baseline`` object (the fp64 oracle's backward timed on this host's cores
 over a bounded sample of the same workload).
 
+Every timed step records HIP events around its kernels on the launch stream:
+``ms_median`` and ``ms_min`` are the median and the fastest step, ``ms_per_step``
+the mean over the timed region. The outputs of the timed run are compared with
+the oracle's whole (sequence, head) slices that the CPU baseline computes on the
+same inputs (``parity``: per-tensor relative L2 and max-abs error). The dense
+bf16 peak is also re-derived from rocminfo (``peak_derived``: compute units x
+maximum shader clock x 4096 FLOPs per clock per CU); ``pct_peak`` and the
+roofline use the published 2.5 PFLOP/s.
+
 ``--path forward`` times the forward that produces O, m, l instead, under its
 own metric; ``--plan`` launches from the host-side longest-first schedule
 (``fa_bwd_plan``) instead of the dense grid; ``--calibrate-copy MIB`` first runs
@@ -45,6 +54,7 @@ if ROOT not in sys.path:
 
 METRIC = "FA-bwd TFLOP/s + % bf16 MFMA peak, S=8192 H=32 D=128 causal, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+BF16_FLOP_PER_CLK_PER_CU = 4096  # 4 SIMDs, each one 32x32x16 bf16 MFMA (32768 FLOPs) per 32 clocks
 MASK_NAMES = {0: "none", 1: "padding", 2: "causal", 3: "padding_causal"}
 ALGORITHMS = {"default": 0, "single-pass": 1, "recompute": 2, "split-reduce": 3, "recompute-8w": 4, "recompute-4w": 5}
 ALGORITHM_NAMES = {1: "single-pass (dQ atomics)",
@@ -234,6 +244,28 @@ def copy_calibration(mib: int, device) -> None:
     del src, dst
 
 
+def derived_peak():
+    """The dense bf16 MFMA peak from this GPU's own figures: compute units x maximum shader clock x
+    4096 FLOPs per clock per CU, read from rocminfo (run as a child process before the GPU is used)."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for agent in out.split("*******"):
+        if "gfx950" not in agent:
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", agent)
+        clk = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+        if cu and clk:
+            cus, mhz = int(cu.group(1)), int(clk.group(1))
+            return {"source": "rocminfo", "compute_units": cus, "max_sclk_mhz": mhz,
+                    "flop_per_clk_per_cu": BF16_FLOP_PER_CLK_PER_CU,
+                    "tflops": round(cus * mhz * 1e6 * BF16_FLOP_PER_CLK_PER_CU / 1e12, 1)}
+    return None
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -258,25 +290,58 @@ def cpu_baseline(inp, dev, target_s: float = 15.0):
     group = heads // k.shape[1]
     pairs = [(b, h) for b in range(len(inp["seqlens_q"])) for h in range(heads)]
     segs = segments(inp)
-    done, flops, elapsed = [], 0.0, 0.0
+    done, flops, elapsed, slices = [], 0.0, 0.0, []
     for b, h in pairs:
         qs, lq, ks, lk = segs[b]
         if lq <= 0 or lk <= 0:
             continue
         hk = h // group
         t0 = time.perf_counter()
-        oracle.backward_head(q[qs:qs + lq, h], k[ks:ks + lk, hk], v[ks:ks + lk, hk], o[qs:qs + lq, h],
-                             do[qs:qs + lq, h], m[qs:qs + lq, h], l[qs:qs + lq, h], inp["scale"], causal, window)
+        r = oracle.backward_head(q[qs:qs + lq, h], k[ks:ks + lk, hk], v[ks:ks + lk, hk], o[qs:qs + lq, h],
+                                 do[qs:qs + lq, h], m[qs:qs + lq, h], l[qs:qs + lq, h], inp["scale"], causal, window)
         elapsed += time.perf_counter() - t0
         flops += 2.0 * visible_pairs(lq, lk, causal, window) * (3 * d + 2 * dv)
         done.append((b, h))
+        slices.append(((qs, lq, ks, lk, h, hk), r["dq"], r["dk"], r["dv"]))
         if elapsed >= target_s:
             break
     del np
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"fp64 oracle backward on {len(done)} of {len(pairs)} (sequence, head) slices of the same "
                       f"workload and inputs ({elapsed:.1f} s); same FLOP count as the metric",
-            "seconds": elapsed}
+            "seconds": elapsed}, slices
+
+
+def timed_output_parity(inp, outs, slices):
+    """The timed run's dQ, dK, dV against the oracle's whole (sequence, head) slices from the CPU
+    baseline: relative L2 error and max |gpu - ref| / max |ref| per tensor over the sampled slices.
+    dK, dV are compared only without grouped K/V heads (a slice of one query head is then the whole
+    gradient of its K/V head)."""
+    import numpy as np
+    gq, gk, gv = (x.float().cpu().numpy() for x in outs)
+    grouped = inp["k"].shape[1] != inp["q"].shape[1]
+    got = {"dq": [], "dk": [], "dv": []}
+    ref = {"dq": [], "dk": [], "dv": []}
+    for (qs, lq, ks, lk, h, hk), rq, rk, rv in slices:
+        got["dq"].append(gq[qs:qs + lq, h].ravel())
+        ref["dq"].append(rq.ravel())
+        if not grouped:
+            got["dk"].append(gk[ks:ks + lk, hk].ravel())
+            ref["dk"].append(rk.ravel())
+            got["dv"].append(gv[ks:ks + lk, hk].ravel())
+            ref["dv"].append(rv.ravel())
+    out = {"slices": len(slices), "rel_l2_tol": 1e-2, "max_abs_tol": 3e-2}
+    ok = bool(slices)
+    for name in ("dq", "dk", "dv"):
+        if not got[name]:
+            continue
+        g, r = np.concatenate(got[name]).astype(np.float64), np.concatenate(ref[name])
+        rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
+        mx = float(np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-300))
+        out[name] = {"rel_l2": float(f"{rel:.3e}"), "max_abs_over_max_ref": float(f"{mx:.3e}")}
+        ok = ok and np.isfinite(g).all() and rel <= 1e-2 and mx <= 3e-2
+    out["ok"] = bool(ok)
+    return out
 
 
 def bench_forward(args, device):
@@ -358,6 +423,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    peak_info = derived_peak()  # child process, before this process touches the GPU
     import torch
     from attention_backward_fa_amd import binding
     if not torch.cuda.is_available():
@@ -406,6 +472,9 @@ def main():
     shares = kernel_share(algo_used, d, inp["v"].shape[2])
     names = list(shares)
     kern_ms = {n: sum(s[i] for s in stages) / len(stages) for i, n in enumerate(names)}
+    step_ms = sorted(sum(s_) for s_ in stages)  # each timed step, first kernel start to last kernel end
+    med_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1] +
+                                                                         step_ms[len(step_ms) // 2])
     dom = max(kern_ms, key=kern_ms.get)
     tflops = flops / (ms * 1e-3) / 1e12
     dom_flops = flops * shares[dom]
@@ -422,15 +491,19 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config,
         "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "ms_median": round(med_ms, 5), "ms_min": round(step_ms[0], 5),
+        "tflops_median": round(flops / (med_ms * 1e-3) / 1e12, 2),
         "kernels_ms": {n: round(v, 5) for n, v in kern_ms.items()},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(dom, args.workload, algo_used), "work_flops": dom_flops},
+        "peak_derived": peak_info,
         "outputs_finite": finite,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, dev, args.cpu_seconds)
+        out["cpu_baseline"], slices = cpu_baseline(inp, dev, args.cpu_seconds)
+        out["parity"] = timed_output_parity(inp, (dq, dk, dv), slices)
     print(json.dumps(out), flush=True)
 
 

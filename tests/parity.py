@@ -7,20 +7,31 @@ rows outside every sequence must be exactly zero.
 """
 from __future__ import annotations
 
+import hashlib
+import os
+import time
+
 import numpy as np
 import torch
 
 import oracle
-from attention_backward_fa_amd import binding
+import oracle.attention
+from attention_backward_fa_amd import binding, inputs
 
 REL_L2_TOL = 1e-2
 MAX_ABS_TOL = 3e-2
 
 
-def oracle_stats(inp):
-    """O (bf16), m, l (fp32) from the oracle's fp64 forward on the bf16 inputs."""
-    o, m, l = oracle.forward(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_kv"], inp["scale"], inp["mask"],
-                             inp["max_seqlen_q"], inp["max_seqlen_kv"], inp.get("window", 0))
+def cpu_workers() -> int:
+    """Threads for the oracle: this process's CPUs, at most 16 (the host share of one GPU)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_stats(inp, workers: int | None = None):
+    """O (bf16), m, l (fp32) from the oracle's fp64 forward on the bf16 inputs (query row blocks)."""
+    o, m, l = oracle.forward_blocked(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_kv"], inp["scale"],
+                                     inp["mask"], inp["max_seqlen_q"], inp["max_seqlen_kv"], inp.get("window", 0),
+                                     workers=workers or cpu_workers())
     return (torch.from_numpy(o).to(torch.bfloat16), torch.from_numpy(m).to(torch.float32),
             torch.from_numpy(l).to(torch.float32))
 
@@ -36,9 +47,48 @@ def run_gpu(inp, o, m, l, device="cuda", algorithm=binding.FA_BWD_ALGO_DEFAULT):
     return dq.float().cpu(), dk.float().cpu(), dv.float().cpu()
 
 
-def oracle_backward(inp, o, m, l):
-    return oracle.backward(inp["q"], inp["k"], inp["v"], o, inp["do"], m, l, inp["cu_q"], inp["cu_kv"],
-                           inp["scale"], inp["mask"], inp["max_seqlen_q"], inp["max_seqlen_kv"], inp.get("window", 0))
+def oracle_backward(inp, o, m, l, workers: int | None = None):
+    """fp64 dQ, dK, dV of the oracle (query row blocks) on the inputs the GPU sees."""
+    return oracle.backward_blocked(inp["q"], inp["k"], inp["v"], o, inp["do"], m, l, inp["cu_q"], inp["cu_kv"],
+                                   inp["scale"], inp["mask"], inp["max_seqlen_q"], inp["max_seqlen_kv"],
+                                   inp.get("window", 0), workers=workers or cpu_workers())
+
+
+def _cache_path(name: str, seed: int):
+    """File of the optional on-disk cache of oracle results (directory in FA_ORACLE_CACHE, unset = off),
+    keyed by workload, seed and the source of the oracle and of the input generator."""
+    root = os.environ.get("FA_ORACLE_CACHE")
+    if not root:
+        return None
+    h = hashlib.sha256()
+    for mod in (oracle.attention, inputs):
+        with open(mod.__file__, "rb") as fh:
+            h.update(fh.read())
+    return os.path.join(root, f"{name}_seed{seed}_{h.hexdigest()[:16]}.npz")
+
+
+def reference(inp, log=None):
+    """Oracle forward statistics (O bf16, m, l fp32) and backward (dQ, dK, dV) of one workload. With
+    FA_ORACLE_CACHE set, results are kept on disk (gradients as fp32, whose rounding is far below the
+    tolerance) and reused for the same workload, seed and oracle source."""
+    path = _cache_path(inp["name"], inp["seed"])
+    if path and os.path.exists(path):
+        z = np.load(path)
+        return ((torch.from_numpy(z["o"]).to(torch.bfloat16), torch.from_numpy(z["m"]), torch.from_numpy(z["l"])),
+                tuple(z[k].astype(np.float64) for k in ("dq", "dk", "dv")))
+    t0 = time.perf_counter()
+    o, m, l = oracle_stats(inp)
+    if log:
+        log(f"oracle forward {time.perf_counter() - t0:.1f} s")
+    t0 = time.perf_counter()
+    ref = oracle_backward(inp, o, m, l)
+    if log:
+        log(f"oracle backward {time.perf_counter() - t0:.1f} s")
+    if path:
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        np.savez(path, o=o.float().numpy(), m=m.numpy(), l=l.numpy(),
+                 **{k: r.astype(np.float32) for k, r in zip(("dq", "dk", "dv"), ref)})
+    return (o, m, l), ref
 
 
 def metrics(gpu, ref):

@@ -2,7 +2,9 @@
 inputs, every valid row compared, at sizes the oracle finishes in seconds.
 
 Cases: the tiny workload (1 head, 128 tokens, d 64), the d in {64, 128} rows
-of the PyPTO-Gym SK-16 test matrix (§七) as packed sequences, and ragged
+of the PyPTO-Gym SK-16 test matrix (§七) as packed sequences (among them
+test_02: 8 sequences of 2432 tokens, 8 heads, d 64, lengths that are not a
+multiple of the 128-row tiles), and ragged
 cases for every mask type (lengths that are not multiples of the 64-row q
 step or the 128-row kv tile, a single-token sequence, an empty sequence,
 Lq != Lk, padded slots with garbage in the padding rows).
@@ -22,6 +24,7 @@ NONE, PAD, CAUSAL, PADC = I.MASK_NONE, I.MASK_PADDING, I.MASK_CAUSAL, I.MASK_PAD
 CASES = [
     I.CASES["tiny"],
     I.CASES["sk16_t01"],
+    I.CASES["sk16_t02"],
     I.CASES["sk16_t05"],
     I.CASES["sk16_t06"],
     I.custom_case("ragged_none_d128", 3, 128, NONE, 201, [1, 77, 200, 333]),
@@ -42,13 +45,29 @@ ALGOS = {"recompute": B.FA_BWD_ALGO_RECOMPUTE_DQ, "recompute8w": B.FA_BWD_ALGO_R
 LAYOUTS = {"8w": B.FA_BWD_ALGO_RECOMPUTE_DQ_8W, "4w": B.FA_BWD_ALGO_RECOMPUTE_DQ_4W}
 
 
+_held = {}
+
+
+def _case_reference(case):
+    """Inputs, oracle statistics and oracle gradients of one case, computed once for all algorithms
+    (the cases run case-major)."""
+    if case.name not in _held:
+        _held.clear()
+        inp = I.make(case)
+        o, m, l = P.oracle_stats(inp)
+        _held[case.name] = (inp, (o, m, l), P.oracle_backward(inp, o, m, l))
+    inp, (o, m, l), ref = _held[case.name]
+    clone = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    return clone, (o.clone(), m.clone(), l.clone()), ref
+
+
 @pytest.mark.parametrize("algo", list(ALGOS))
 @pytest.mark.parametrize("case", CASES, ids=[c.name for c in CASES])
 def test_parity_full(case, algo):
-    inp = I.make(case)
+    print(f"[parity] {case.name} ({algo})", flush=True)
+    inp, (o, m, l), ref = _case_reference(case)
     print(f"[parity] {case.name} ({algo}): T_q={inp['q'].shape[0]} H={case.heads} d={case.head_dim} "
           f"mask={case.mask}", flush=True)
-    o, m, l = P.oracle_stats(inp)
     if I.is_padded_mask(case.mask):
         # the backward must not read padding rows: fill them with NaN
         vq = torch.from_numpy(P.oracle.valid_rows(inp["cu_q"], case.mask, inp["max_seqlen_q"], inp["q"].shape[0]))
@@ -61,7 +80,6 @@ def test_parity_full(case, algo):
         inp["k"][~vk] = float("nan")
         inp["v"][~vk] = float("nan")
     gpu = P.run_gpu(inp, o, m, l, algorithm=ALGOS[algo])
-    ref = P.oracle_backward(inp, o, m, l)
     res = P.check_full(inp, gpu, ref)
     print(f"[parity] {case.name} ({algo}): " + " ".join(f"{k}: rel_l2={v[0]:.2e} max={v[1]:.2e}" for k, v in res.items()),
           flush=True)
