@@ -21,6 +21,8 @@ FA_BWD_ERR_INVALID_ARGUMENT = 1
 FA_BWD_ERR_UNSUPPORTED = 2
 FA_BWD_ERR_OUT_OF_MEMORY = 3
 FA_BWD_ERR_HIP = 4
+FA_BWD_ERR_SCRATCH_LIMIT = 5
+FA_BWD_NOALLOC_MAX_ROWS = 1 << 22
 
 FA_BWD_ALGO_DEFAULT = 0
 FA_BWD_ALGO_SINGLE_PASS = 1
@@ -35,8 +37,9 @@ FA_BWD_MASK_CAUSAL = 2
 FA_BWD_MASK_PADDING_CAUSAL = 3
 
 # every symbol include/fa_bwd.h declares
-EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_run_lse", "fa_fwd_run", "fa_bwd_plan", "fa_bwd_destroy",
-            "fa_bwd_status_string", "fa_bwd_get_desc", "fa_bwd_profile_enable", "fa_bwd_profile_collect")
+EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_run_lse", "fa_bwd_run_noalloc", "fa_fwd_run", "fa_bwd_plan",
+            "fa_bwd_destroy", "fa_bwd_status_string", "fa_bwd_get_desc", "fa_bwd_profile_enable",
+            "fa_bwd_profile_collect")
 
 
 class FaBwdDesc(ctypes.Structure):
@@ -64,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_run.restype = i32
     lib.fa_bwd_run_lse.argtypes = [vp] * 9 + [f32, i32] + [vp] * 4
     lib.fa_bwd_run_lse.restype = i32
+    lib.fa_bwd_run_noalloc.argtypes = [ctypes.POINTER(FaBwdDesc)] + [vp] * 9 + [f32, i32] + [vp] * 4
+    lib.fa_bwd_run_noalloc.restype = i32
     lib.fa_fwd_run.argtypes = [vp] * 6 + [f32, i32] + [vp] * 4
     lib.fa_fwd_run.restype = i32
     lib.fa_bwd_plan.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32), i32]
@@ -90,7 +95,7 @@ def _check(status: int, what: str) -> None:
     if status == FA_BWD_OK:
         return
     msg = f"{what}: {fa_bwd_status_string(status)} (status {status})"
-    if status == FA_BWD_ERR_INVALID_ARGUMENT:
+    if status in (FA_BWD_ERR_INVALID_ARGUMENT, FA_BWD_ERR_SCRATCH_LIMIT):
         raise ValueError(msg)
     if status == FA_BWD_ERR_UNSUPPORTED:
         raise NotImplementedError(msg)
@@ -184,6 +189,35 @@ def fa_bwd_run(handle, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scal
         stream = torch.cuda.current_stream(dev).cuda_stream
     st = load_library().fa_bwd_run(handle, *ptrs, ctypes.c_float(scale), int(mask), *outs, ctypes.c_void_p(stream))
     _check(st, "fa_bwd_run")
+
+
+def fa_bwd_run_noalloc(desc: FaBwdDesc, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale: float,
+                       mask: int, dq, dk, dv, stream=None) -> None:
+    """The allocation-free backward: no handle, the library's fixed scratch array (at most
+    FA_BWD_NOALLOC_MAX_ROWS = total_q * num_heads); tensors as for ``fa_bwd_run`` with the sizes of
+    ``desc`` (num_heads_kv, head_dim_v of 0 meaning num_heads, head_dim)."""
+    import torch
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError(f"q: expected a GPU tensor, got device {dev}")
+    hk = desc.num_heads_kv or desc.num_heads
+    dvd = desc.head_dim_v or desc.head_dim
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    qs, os_ = (desc.total_q, desc.num_heads, desc.head_dim), (desc.total_q, desc.num_heads, dvd)
+    ks, vs = (desc.total_kv, hk, desc.head_dim), (desc.total_kv, hk, dvd)
+    ptrs = [
+        _expect(q, "q", qs, bf, dev), _expect(k, "k", ks, bf, dev), _expect(v, "v", vs, bf, dev),
+        _expect(o, "o", os_, bf, dev), _expect(dout, "dout", os_, bf, dev),
+        _expect(m, "m", qs[:2], f32, dev), _expect(l, "l", qs[:2], f32, dev),
+        _expect(cu_seqlens_q, "cu_seqlens_q", (desc.batch + 1,), i32, dev),
+        _expect(cu_seqlens_kv, "cu_seqlens_kv", (desc.batch + 1,), i32, dev),
+    ]
+    outs = [_expect(dq, "dq", qs, bf, dev), _expect(dk, "dk", ks, bf, dev), _expect(dv, "dv", vs, bf, dev)]
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = load_library().fa_bwd_run_noalloc(ctypes.byref(desc), *ptrs, ctypes.c_float(scale), int(mask), *outs,
+                                           ctypes.c_void_p(stream))
+    _check(st, "fa_bwd_run_noalloc")
 
 
 def fa_bwd_run_lse(handle, q, k, v, o, dout, lse, cu_seqlens_q, cu_seqlens_kv, scale: float, mask: int,

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -448,6 +449,30 @@ fa_bwd_status build_plan(const fa_bwd_desc& d, const int32_t* cq, const int32_t*
   return FA_BWD_OK;
 }
 
+// The kv-outer kernel's layout and the dense grids' orders for runs without and with a causal bound,
+// from the descriptor (every sequence taken at the maximum lengths) and the compute-unit count.
+void configure_layouts(fa_bwd_handle* h, int cus) {
+  const fa_bwd_desc& hd = h->desc;
+  const int64_t per_tile_heads = (int64_t)hd.batch * hd.num_heads;  // Hk K/V heads x G query heads each
+  const int G = hd.num_heads / hd.num_heads_kv;
+  for (int c = 0; c < 2; ++c) {
+    int64_t total = 0, largest = 0;
+    dkdv_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), total, largest);
+    h->four_dense[c] = four_waves_balances((double)total * (double)per_tile_heads, (double)largest * G, cus);
+    // heads up to 128: two workgroups per CU in the dQ kernel and the four-wave dK/dV layout, one in
+    // the eight-wave one; wider heads: one in both kernels
+    const int64_t kv_heads_x_seqs = (int64_t)hd.batch * hd.num_heads_kv;
+    const bool narrow = pick_kernels(hd.head_dim, hd.head_dim_v).two_layouts;
+    const bool four = narrow && (h->dkdv_layout == 2 || (h->dkdv_layout == 0 && h->four_dense[c]));
+    h->dkdv_head_major[c] = head_major_balances((double)total * (double)per_tile_heads, (double)largest * G,
+                                                (int64_t)cus * (four ? 2 : 1), kv_heads_x_seqs);
+    int64_t qtotal = 0, qlargest = 0;
+    dq_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), qtotal, qlargest);
+    h->dq_head_major[c] = head_major_balances((double)qtotal * (double)per_tile_heads, (double)qlargest,
+                                              (int64_t)cus * (narrow ? 2 : 1), per_tile_heads);
+  }
+}
+
 // Host checks shared by fa_bwd_run and fa_fwd_run.
 fa_bwd_status check_run(const fa_bwd_handle* h, float scale, int32_t mask) {
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_BWD_ERR_INVALID_ARGUMENT;
@@ -461,21 +486,72 @@ fa_bwd_status check_run(const fa_bwd_handle* h, float scale, int32_t mask) {
 }
 
 // (m, l) or, with l null, the log-sum-exp in m: shared checks and launch of both backward entries.
-fa_bwd_status run_common(fa_bwd_handle* h, const void* q, const void* k, const void* v, const void* o,
-                         const void* dout, const float* m, const float* l, const int32_t* cu_seqlens_q,
-                         const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* dq, void* dk, void* dv,
-                         void* stream) {
-  if (!h || !q || !k || !v || !o || !dout || !m || !cu_seqlens_q || !cu_seqlens_kv || !dq || !dk || !dv)
+fa_bwd_status check_pointers(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* m, const float* l, const int32_t* cu_seqlens_q,
+                             const int32_t* cu_seqlens_kv, void* dq, void* dk, void* dv) {
+  if (!q || !k || !v || !o || !dout || !m || !cu_seqlens_q || !cu_seqlens_kv || !dq || !dk || !dv)
     return FA_BWD_ERR_INVALID_ARGUMENT;
   const void* vec[] = {q, k, v, o, dout, dq, dk, dv};
   for (const void* p : vec)
     if (!aligned(p, 16)) return FA_BWD_ERR_INVALID_ARGUMENT;
   if (!aligned(m, 4) || (l && !aligned(l, 4)) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_kv, 4))
     return FA_BWD_ERR_INVALID_ARGUMENT;
+  return FA_BWD_OK;
+}
+
+fa_bwd_status run_common(fa_bwd_handle* h, const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* m, const float* l, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* dq, void* dk, void* dv,
+                         void* stream) {
+  if (!h) return FA_BWD_ERR_INVALID_ARGUMENT;
+  const fa_bwd_status ps = check_pointers(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, dq, dk, dv);
+  if (ps != FA_BWD_OK) return ps;
   const fa_bwd_status cs = check_run(h, scale, mask);
   if (cs != FA_BWD_OK) return cs;
   return launch(h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv,
                 static_cast<hipStream_t>(stream));
+}
+
+// ---- the allocation-free entry point's scratch: the two fp32 [H][total_q] row-statistic arrays
+// (lse2, then D) of one run, for total_q x num_heads up to kNoAllocMaxRows, in a file-scope device array
+// that each GPU holds from the time the library's code is loaded on it until the process ends. Host code
+// never uses the array's name as an address: the device address comes from hipGetSymbolAddress, once
+// per device, with that device current.
+constexpr int64_t kNoAllocMaxRows = int64_t(1) << 22;  // 2 x 4 x 2^22 bytes = 32 MiB
+constexpr int kNoAllocMaxDevices = 64;
+
+struct NoAllocDevice {
+  float* scratch;  // device address of `scratch` on this device
+  int cus;         // its compute units (for the layout rule)
+};
+
+std::mutex g_noalloc_mutex;
+NoAllocDevice g_noalloc[kNoAllocMaxDevices];
+bool g_noalloc_ready[kNoAllocMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) float scratch[2 * kNoAllocMaxRows];
+
+namespace {
+
+// The scratch address and compute-unit count of the current device, looked up on its first use.
+fa_bwd_status noalloc_device(NoAllocDevice* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_BWD_ERR_HIP;
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return FA_BWD_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+  if (!g_noalloc_ready[dev]) {
+    void* ptr = nullptr;
+    int cus = 0;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FA_BWD_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return FA_BWD_ERR_HIP;
+    g_noalloc[dev] = {static_cast<float*>(ptr), cus};
+    g_noalloc_ready[dev] = true;
+  }
+  *out = g_noalloc[dev];
+  return FA_BWD_OK;
 }
 
 }  // namespace
@@ -501,27 +577,7 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
     delete h;
     return FA_BWD_ERR_HIP;
   }
-  {  // the dense grid: every sequence taken at the maximum lengths
-    const fa_bwd_desc& hd = h->desc;
-    const int64_t per_tile_heads = (int64_t)hd.batch * hd.num_heads;  // Hk K/V heads x G query heads each
-    const int G = hd.num_heads / hd.num_heads_kv;
-    for (int c = 0; c < 2; ++c) {
-      int64_t total = 0, largest = 0;
-      dkdv_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), total, largest);
-      h->four_dense[c] = four_waves_balances((double)total * (double)per_tile_heads, (double)largest * G, cus);
-      // heads up to 128: two workgroups per CU in the dQ kernel and the four-wave dK/dV layout, one in
-      // the eight-wave one; wider heads: one in both kernels
-      const int64_t kv_heads_x_seqs = (int64_t)hd.batch * hd.num_heads_kv;
-      const bool narrow = pick_kernels(hd.head_dim, hd.head_dim_v).two_layouts;
-      const bool four = narrow && (h->dkdv_layout == 2 || (h->dkdv_layout == 0 && h->four_dense[c]));
-      h->dkdv_head_major[c] = head_major_balances((double)total * (double)per_tile_heads, (double)largest * G,
-                                                  (int64_t)cus * (four ? 2 : 1), kv_heads_x_seqs);
-      int64_t qtotal = 0, qlargest = 0;
-      dq_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), qtotal, qlargest);
-      h->dq_head_major[c] = head_major_balances((double)qtotal * (double)per_tile_heads, (double)qlargest,
-                                                (int64_t)cus * (narrow ? 2 : 1), per_tile_heads);
-    }
-  }
+  configure_layouts(h, cus);
   const size_t stats = (size_t)desc->total_q * desc->num_heads;
   const size_t acc = stats * desc->head_dim * (h->split ? fa::kSplits : 1);
   if ((h->single_pass && hipMalloc(&h->dq_acc, acc * sizeof(float)) != hipSuccess) ||
@@ -552,6 +608,37 @@ fa_bwd_status fa_bwd_run_lse(fa_bwd_handle* h, const void* q, const void* k, con
                              void* stream) {
   if (!lse) return FA_BWD_ERR_INVALID_ARGUMENT;
   return run_common(h, q, k, v, o, dout, lse, nullptr, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv, stream);
+}
+
+fa_bwd_status fa_bwd_run_noalloc(const fa_bwd_desc* desc, const void* q, const void* k, const void* v,
+                                 const void* o, const void* dout, const float* m, const float* l,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, float scale,
+                                 int32_t mask, void* dq, void* dk, void* dv, void* stream) {
+  const fa_bwd_status ds = check_desc(desc);
+  if (ds != FA_BWD_OK) return ds;
+  if (desc->algorithm == FA_BWD_ALGO_SINGLE_PASS || desc->algorithm == FA_BWD_ALGO_SPLIT_REDUCE)
+    return FA_BWD_ERR_UNSUPPORTED;  // their dQ workspace is not part of the fixed scratch
+  if (desc->total_q > kNoAllocMaxRows / desc->num_heads) return FA_BWD_ERR_SCRATCH_LIMIT;
+  if (!l) return FA_BWD_ERR_INVALID_ARGUMENT;
+  const fa_bwd_status ps = check_pointers(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, dq, dk, dv);
+  if (ps != FA_BWD_OK) return ps;
+  // a handle on the stack (its event list stays empty, so nothing is allocated) that points at the scratch
+  fa_bwd_handle h{};
+  h.desc = *desc;
+  if (h.desc.num_heads_kv == 0) h.desc.num_heads_kv = desc->num_heads;
+  if (h.desc.head_dim_v == 0) h.desc.head_dim_v = desc->head_dim;
+  h.dkdv_layout = desc->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_8W ? 1 : desc->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_4W ? 2 : 0;
+  const fa_bwd_status cs = check_run(&h, scale, mask);
+  if (cs != FA_BWD_OK) return cs;
+  NoAllocDevice nd;
+  const fa_bwd_status ns = noalloc_device(&nd);
+  if (ns != FA_BWD_OK) return ns;
+  (void)hipGetDevice(&h.device);
+  configure_layouts(&h, nd.cus);
+  h.lse2 = nd.scratch;
+  h.dvec = nd.scratch + desc->total_q * desc->num_heads;
+  return launch(&h, q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, scale, mask, dq, dk, dv,
+                static_cast<hipStream_t>(stream));
 }
 
 fa_bwd_status fa_fwd_run(fa_bwd_handle* h, const void* q, const void* k, const void* v,
@@ -628,6 +715,7 @@ const char* fa_bwd_status_string(fa_bwd_status s) {
     case FA_BWD_ERR_UNSUPPORTED: return "unsupported configuration";
     case FA_BWD_ERR_OUT_OF_MEMORY: return "out of device memory";
     case FA_BWD_ERR_HIP: return "HIP runtime error";
+    case FA_BWD_ERR_SCRATCH_LIMIT: return "problem exceeds the fixed scratch of fa_bwd_run_noalloc";
   }
   return "unknown status";
 }

@@ -95,7 +95,9 @@ typedef enum {
                                       single-pass and split-reduce forms: head dims other than 64 or
                                       128, unequal head dims, grouped heads or a window */
   FA_BWD_ERR_OUT_OF_MEMORY = 3,    /* workspace allocation failed in fa_bwd_create */
-  FA_BWD_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+  FA_BWD_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed */
+  FA_BWD_ERR_SCRATCH_LIMIT = 5     /* fa_bwd_run_noalloc: total_q * num_heads exceeds
+                                      FA_BWD_NOALLOC_MAX_ROWS */
 } fa_bwd_status;
 
 typedef struct {
@@ -166,6 +168,28 @@ fa_bwd_status fa_bwd_run_lse(fa_bwd_handle* h, const void* q, const void* k, con
                              const void* dout, const float* lse, const int32_t* cu_seqlens_q,
                              const int32_t* cu_seqlens_kv, float scale, int32_t mask, void* dq, void* dk, void* dv,
                              void* stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The backward of fa_bwd_run for the recompute form
+ * (FA_BWD_ALGO_DEFAULT, _RECOMPUTE_DQ, _RECOMPUTE_DQ_8W, _RECOMPUTE_DQ_4W: the same kernels, the
+ * same layout rule and bitwise the same results as a handle created from `desc`), without a handle
+ * and without any allocation: the two fp32 [H][total_q] row-statistic arrays live in a fixed
+ * device array of the library, 32 MiB, which every GPU the library runs on holds until the process
+ * ends. The caller passes the descriptor and every input and output, with the meanings, layouts,
+ * checks and errors of fa_bwd_create and fa_bwd_run (the dense grid: no host schedule, no
+ * profiling). The first call on a device looks up that device's copy of the array (the caller
+ * makes the device of `stream` current, as for any HIP call); no call allocates or frees memory.
+ *   FA_BWD_ERR_SCRATCH_LIMIT: total_q * num_heads > FA_BWD_NOALLOC_MAX_ROWS (nothing enqueued).
+ *   FA_BWD_ERR_UNSUPPORTED: the single-pass and split-reduce forms (their dQ workspace is not part
+ *     of the fixed array).
+ * All calls on one GPU share its array: calls that can overlap in time on one GPU (two streams,
+ * or a graph replayed beside a direct call) race on it and give wrong gradients. Each call rewrites
+ * every row statistic it reads, so the array needs no clearing between calls. */
+#define FA_BWD_NOALLOC_MAX_ROWS (1 << 22)
+fa_bwd_status fa_bwd_run_noalloc(const fa_bwd_desc* desc, const void* q, const void* k, const void* v,
+                                 const void* o, const void* dout, const float* m, const float* l,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, float scale,
+                                 int32_t mask, void* dq, void* dk, void* dv, void* stream);
 
 /* Forward that produces the backward's inputs, for callers without one of their own: enqueues on
  * `stream` O = softmax(scale * Q K^T, masked) V together with the row statistics the backward

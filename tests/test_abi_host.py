@@ -124,6 +124,38 @@ def test_run_and_profile_reject_null_handle():
     assert not lib.fa_bwd_get_desc(None)
 
 
+def _noalloc(desc, ptr=256, l=True):
+    p = ctypes.c_void_p(ptr)
+    lp = p if l else None
+    return B.load_library().fa_bwd_run_noalloc(ctypes.byref(desc) if desc is not None else None, p, p, p, p, p, p,
+                                                lp, p, p, ctypes.c_float(0.1), 0, p, p, p, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    # total_q * num_heads above the fixed scratch (2^22 rows): rejected before any HIP call
+    (dict(total_q=(1 << 22) + 1, max_seqlen_q=(1 << 22) + 1), B.FA_BWD_ERR_SCRATCH_LIMIT),
+    (dict(num_heads=64, total_q=(1 << 16) + 1), B.FA_BWD_ERR_SCRATCH_LIMIT),
+    (dict(algorithm=1), B.FA_BWD_ERR_UNSUPPORTED),       # single-pass and split-reduce need a dQ workspace
+    (dict(algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(batch=0), B.FA_BWD_ERR_INVALID_ARGUMENT),      # the descriptor checks of fa_bwd_create
+    (dict(head_dim=100), B.FA_BWD_ERR_UNSUPPORTED),
+])
+def test_noalloc_rejects_before_any_hip_call(kw, status):
+    d = dict(batch=1, num_heads=1, head_dim=128, max_seqlen_q=128, max_seqlen_kv=128, total_q=128, total_kv=128,
+             algorithm=0)
+    d.update(kw)
+    assert _noalloc(B.FaBwdDesc(**d)) == status
+
+
+def test_noalloc_rejects_null_and_misaligned_pointers():
+    desc = B.FaBwdDesc(1, 1, 128, 128, 128, 128, 128, 0)
+    assert _noalloc(None) == B.FA_BWD_ERR_INVALID_ARGUMENT
+    assert _noalloc(desc, l=False) == B.FA_BWD_ERR_INVALID_ARGUMENT
+    assert _noalloc(desc, ptr=258) == B.FA_BWD_ERR_INVALID_ARGUMENT
+    assert B.fa_bwd_status_string(B.FA_BWD_ERR_SCRATCH_LIMIT).startswith("problem exceeds")
+    assert B.FA_BWD_NOALLOC_MAX_ROWS == 1 << 22
+
+
 def test_destroy_null_is_ok():
     assert B.load_library().fa_bwd_destroy(None) == B.FA_BWD_OK
 
