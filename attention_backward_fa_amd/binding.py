@@ -30,6 +30,7 @@ FA_BWD_ALGO_RECOMPUTE_DQ = 2
 FA_BWD_ALGO_SPLIT_REDUCE = 3
 FA_BWD_ALGO_RECOMPUTE_DQ_8W = 4
 FA_BWD_ALGO_RECOMPUTE_DQ_4W = 5
+FA_BWD_ALGO_RECOMPUTE_DQ_64K = 6
 
 FA_BWD_MASK_NONE = 0
 FA_BWD_MASK_PADDING = 1
@@ -38,8 +39,8 @@ FA_BWD_MASK_PADDING_CAUSAL = 3
 
 # every symbol include/fa_bwd.h declares
 EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_run_lse", "fa_bwd_run_noalloc", "fa_fwd_run", "fa_bwd_plan",
-            "fa_bwd_destroy", "fa_bwd_status_string", "fa_bwd_get_desc", "fa_bwd_profile_enable",
-            "fa_bwd_profile_collect")
+            "fa_bwd_destroy", "fa_bwd_status_string", "fa_bwd_get_desc", "fa_bwd_dkdv_layout",
+            "fa_bwd_profile_enable", "fa_bwd_profile_collect")
 
 
 class FaBwdDesc(ctypes.Structure):
@@ -79,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_status_string.restype = ctypes.c_char_p
     lib.fa_bwd_get_desc.argtypes = [vp]
     lib.fa_bwd_get_desc.restype = ctypes.POINTER(FaBwdDesc)
+    lib.fa_bwd_dkdv_layout.argtypes = [vp, i32]
+    lib.fa_bwd_dkdv_layout.restype = i32
     lib.fa_bwd_profile_enable.argtypes = [vp, i32]
     lib.fa_bwd_profile_enable.restype = i32
     lib.fa_bwd_profile_collect.argtypes = [vp, ctypes.POINTER(f32), i32, ctypes.POINTER(i32)]
@@ -119,6 +122,11 @@ def fa_bwd_get_desc(handle) -> FaBwdDesc:
     if not ptr:
         raise ValueError("fa_bwd_get_desc: null handle")
     return ptr.contents
+
+
+def fa_bwd_dkdv_layout(handle, mask: int) -> int:
+    """The algorithm code of the dK/dV layout runs under `mask` take on this handle (-1: invalid)."""
+    return int(load_library().fa_bwd_dkdv_layout(handle, int(mask)))
 
 
 def fa_bwd_destroy(handle) -> None:
@@ -321,6 +329,9 @@ class FaBwd:
         l = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if l is None else l
         fa_fwd_run(self.handle, q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, mask, o, m, l, stream)
         return o, m, l
+
+    def dkdv_layout(self, mask):
+        return fa_bwd_dkdv_layout(self.handle, mask)
 
     def plan(self, cu_seqlens_q, cu_seqlens_kv, mask):
         fa_bwd_plan(self.handle, cu_seqlens_q, cu_seqlens_kv, mask)

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "fa_bwd.h"
+#include "fa_bwd_dkdv64.hpp"
 #include "fa_bwd_launch.hpp"
 
 struct fa_bwd_handle {
@@ -32,8 +33,9 @@ struct fa_bwd_handle {
   // layout of the dK/dV kernel for heads up to 128: forced by the algorithm code, or chosen by load
   // balance (four_waves_balances) from the descriptor, without and with a causal bound; planned and
   // dense runs of a handle take the same layout, so that they agree bitwise
-  int32_t dkdv_layout;  // 0: chosen, 1: eight waves, 2: four waves
+  int32_t dkdv_layout;  // 0: chosen, 1: eight waves, 2: four waves, 3: 64 keys per wave
   bool four_dense[2];
+  int32_t layout[2];    // the layout (1, 2 or 3) runs without and with a causal bound take
   // the dQ and dK/dV kernels' dense grids in head-major order per XCD (head_major_balances), without
   // and with a causal bound
   bool dq_head_major[2], dkdv_head_major[2];
@@ -57,11 +59,12 @@ bool head_dim_ok(int32_t d) { return d >= 8 && d <= 256 && d % 8 == 0; }
 // Work of the dK/dV workgroups of one sequence (lq queries, lk keys): the 64-row q steps each 128-row
 // kv tile visits, bounded as the kernel bounds its loop (causal start, window band); adds the sum
 // over the tiles to total and keeps the largest.
-void dkdv_work(int64_t lq, int64_t lk, bool causal, int64_t w, int64_t& total, int64_t& largest) {
-  const int64_t n_qs = (lq + 63) / 64;
-  for (int64_t kv0 = 0; kv0 < lk; kv0 += 128) {
-    const int64_t qt0 = causal ? kv0 / 64 : 0;
-    const int64_t qt_end = w > 0 ? std::min(n_qs, (kv0 + 126 + w) / 64 + 1) : n_qs;
+void dkdv_work(int64_t lq, int64_t lk, bool causal, int64_t w, int64_t& total, int64_t& largest, int64_t bn = 128,
+               int64_t bm = 64) {
+  const int64_t n_qs = (lq + bm - 1) / bm;
+  for (int64_t kv0 = 0; kv0 < lk; kv0 += bn) {
+    const int64_t qt0 = causal ? kv0 / bm : 0;
+    const int64_t qt_end = w > 0 ? std::min(n_qs, (kv0 + bn - 2 + w) / bm + 1) : n_qs;
     const int64_t work = std::max<int64_t>(0, qt_end - qt0);
     total += work;
     largest = std::max(largest, work);
@@ -111,7 +114,7 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
     return FA_BWD_ERR_INVALID_ARGUMENT;
   const int32_t dv = d->head_dim_v == 0 ? d->head_dim : d->head_dim_v;
   if (!head_dim_ok(d->head_dim) || !head_dim_ok(dv)) return FA_BWD_ERR_UNSUPPORTED;
-  if (d->algorithm < FA_BWD_ALGO_DEFAULT || d->algorithm > FA_BWD_ALGO_RECOMPUTE_DQ_4W) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (d->algorithm < FA_BWD_ALGO_DEFAULT || d->algorithm > FA_BWD_ALGO_RECOMPUTE_DQ_64K) return FA_BWD_ERR_INVALID_ARGUMENT;
   const bool single = d->algorithm == FA_BWD_ALGO_SINGLE_PASS || d->algorithm == FA_BWD_ALGO_SPLIT_REDUCE;
   // the single-pass kernels exist for equal head dims of 64 and 128
   if (single && (dv != d->head_dim || (d->head_dim != 64 && d->head_dim != 128))) return FA_BWD_ERR_UNSUPPORTED;
@@ -124,6 +127,9 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   // window bounds (kv0 + tile + window, i - window - kv0) then fit in 32 bits
   if (d->max_seqlen_q > (1 << 30) || d->max_seqlen_kv > (1 << 30)) return FA_BWD_ERR_INVALID_ARGUMENT;
   if (single && d->window > 0) return FA_BWD_ERR_UNSUPPORTED;
+  // the 64-key dK/dV layout exists for head dims of 128 without a window
+  if (d->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_64K && (d->head_dim != 128 || dv != 128 || d->window != 0))
+    return FA_BWD_ERR_UNSUPPORTED;
   // index arithmetic stays in int64; grids must fit the launch limits
   const int64_t rows = (d->total_q > d->total_kv ? d->total_q : d->total_kv);
   if (rows > (int64_t(1) << 40) / d->num_heads) return FA_BWD_ERR_INVALID_ARGUMENT;
@@ -143,6 +149,25 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
       (rows * d->num_heads + rows_per_block - 1) / rows_per_block > kMaxGrid)
     return FA_BWD_ERR_INVALID_ARGUMENT;
   return FA_BWD_OK;
+}
+
+// The dK/dV kernel with 64 keys per wave: head dims of exactly 128 and no window.
+bool keys64_applies(const fa_bwd_desc& d) { return d.head_dim == 128 && d.head_dim_v == 128 && d.window == 0; }
+
+// The 64-key dK/dV layout runs one workgroup per CU over 256 keys (and every query head of its K/V
+// head): the default takes it where longest-first dispatch balances, i.e. the largest workgroup,
+// doubled, fits within the average work per CU. Small grids, and grouped K/V heads that multiply each
+// workgroup's work, keep the 128-key layouts.
+bool keys64_balances(double total, double largest, int cus) { return 2.0 * largest * cus <= total; }
+
+void launch_dkdv64(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
+  using C = fa::Dkdv64Cfg;
+  const int64_t blocks = (int64_t)((ma.max_seqlen_kv + C::BN - 1) / C::BN) * ma.Hk * ma.batch;
+  const dim3 grid((unsigned)(ma.sched ? items : blocks)), block(C::NT);
+  if (ma.causal)
+    fa::fa_bwd_dkdv64<true><<<grid, block, 0, stream>>>(ma);
+  else
+    fa::fa_bwd_dkdv64<false><<<grid, block, 0, stream>>>(ma);
 }
 
 // The kernels for the padded head dims: each dim rounded up to 64, 128, 192 or 256, and a dim of 64
@@ -319,9 +344,11 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
     else
       h->split ? launch_single_pass<64, true>(ma, causal, stream) : launch_single_pass<64, false>(ma, causal, stream);
   } else if (!planned || h->n_kv_items > 0) {
-    const bool four = h->dkdv_layout == 2 || (h->dkdv_layout == 0 && h->four_dense[causal]);
     ma.head_major = h->dkdv_head_major[causal] ? 1 : 0;
-    ks.dkdv(ma, h->n_kv_items, four, stream);
+    if (h->layout[causal] == 3)
+      launch_dkdv64(ma, h->n_kv_items, stream);
+    else
+      ks.dkdv(ma, h->n_kv_items, h->layout[causal] == 2, stream);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return FA_BWD_ERR_HIP;
@@ -396,7 +423,7 @@ void drop_plan(fa_bwd_handle* h) {
 
 // The work items of the recompute kernels for host sequence offsets, longest first. Work counts the
 // tile pairs a workgroup visits, as the kernels bound their loops (causal start, window band).
-fa_bwd_status build_plan(const fa_bwd_desc& d, const int32_t* cq, const int32_t* ck, int32_t mask,
+fa_bwd_status build_plan(const fa_bwd_desc& d, int32_t layout, const int32_t* cq, const int32_t* ck, int32_t mask,
                          std::vector<int32_t>& out, int64_t& n_kv, int64_t& n_q) {
   const bool padded = mask == FA_BWD_MASK_PADDING || mask == FA_BWD_MASK_PADDING_CAUSAL;
   const bool causal = mask == FA_BWD_MASK_CAUSAL || mask == FA_BWD_MASK_PADDING_CAUSAL || d.window > 0;
@@ -409,6 +436,9 @@ fa_bwd_status build_plan(const fa_bwd_desc& d, const int32_t* cq, const int32_t*
              : (cq[d.batch] > d.total_q || ck[d.batch] > d.total_kv))
     return FA_BWD_ERR_INVALID_ARGUMENT;
   const fa::KernelSet ks = pick_kernels(d.head_dim, d.head_dim_v);
+  // kv rows per dK/dV workgroup and q rows per step of the layout the runs take
+  const int kv_tile = layout == 3 ? fa::Dkdv64Cfg::BN : ks.kv_tile;
+  const int q_step = layout == 3 ? fa::Dkdv64Cfg::BM : ks.q_step;
   struct Item {
     int64_t work;
     int32_t tile, hb;
@@ -417,11 +447,11 @@ fa_bwd_status build_plan(const fa_bwd_desc& d, const int32_t* cq, const int32_t*
   const int G = d.num_heads / d.num_heads_kv, w = effective_window(d);
   for (int b = 0; b < d.batch; ++b) {
     const int lq = cq[b + 1] - cq[b], lk = ck[b + 1] - ck[b];
-    const int n_qs = (lq + ks.q_step - 1) / ks.q_step;  // q steps of the dK/dV kernel
-    for (int t = 0; t * ks.kv_tile < lk; ++t) {
-      const int kv0 = t * ks.kv_tile;
-      const int qt0 = causal ? kv0 / ks.q_step : 0;
-      const int qt_end = w > 0 ? std::min(n_qs, (kv0 + ks.kv_tile - 2 + w) / ks.q_step + 1) : n_qs;
+    const int n_qs = (lq + q_step - 1) / q_step;  // q steps of the dK/dV kernel
+    for (int t = 0; t * kv_tile < lk; ++t) {
+      const int kv0 = t * kv_tile;
+      const int qt0 = causal ? kv0 / q_step : 0;
+      const int qt_end = w > 0 ? std::min(n_qs, (kv0 + kv_tile - 2 + w) / q_step + 1) : n_qs;
       const int64_t work = (int64_t)G * std::max(0, qt_end - qt0);
       for (int hk = 0; hk < d.num_heads_kv; ++hk) kv.push_back({work, t, b * d.num_heads_kv + hk});
     }
@@ -449,6 +479,16 @@ fa_bwd_status build_plan(const fa_bwd_desc& d, const int32_t* cq, const int32_t*
   return FA_BWD_OK;
 }
 
+// The dK/dV layout an algorithm code forces (0: chosen by the rule).
+int32_t dkdv_layout_code(int32_t algorithm) {
+  switch (algorithm) {
+    case FA_BWD_ALGO_RECOMPUTE_DQ_8W: return 1;
+    case FA_BWD_ALGO_RECOMPUTE_DQ_4W: return 2;
+    case FA_BWD_ALGO_RECOMPUTE_DQ_64K: return 3;
+    default: return 0;
+  }
+}
+
 // The kv-outer kernel's layout and the dense grids' orders for runs without and with a causal bound,
 // from the descriptor (every sequence taken at the maximum lengths) and the compute-unit count.
 void configure_layouts(fa_bwd_handle* h, int cus) {
@@ -460,12 +500,26 @@ void configure_layouts(fa_bwd_handle* h, int cus) {
     dkdv_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), total, largest);
     h->four_dense[c] = four_waves_balances((double)total * (double)per_tile_heads, (double)largest * G, cus);
     // heads up to 128: two workgroups per CU in the dQ kernel and the four-wave dK/dV layout, one in
-    // the eight-wave one; wider heads: one in both kernels
+    // the eight-wave one and the 64-key one; wider heads: one in both kernels
     const int64_t kv_heads_x_seqs = (int64_t)hd.batch * hd.num_heads_kv;
     const bool narrow = pick_kernels(hd.head_dim, hd.head_dim_v).two_layouts;
     const bool four = narrow && (h->dkdv_layout == 2 || (h->dkdv_layout == 0 && h->four_dense[c]));
+    // the 64-key layout's own tile sizes: 256 keys, 32-row q steps
+    int64_t total64 = 0, largest64 = 0;
+    if (keys64_applies(hd))
+      dkdv_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1, 0, total64, largest64, fa::Dkdv64Cfg::BN,
+                fa::Dkdv64Cfg::BM);
+    const bool keys64 = h->dkdv_layout == 3 ||
+                        (h->dkdv_layout == 0 && keys64_applies(hd) &&
+                         keys64_balances((double)total64 * (double)per_tile_heads, (double)largest64 * G, cus));
+    h->layout[c] = keys64 ? 3 : four ? 2 : 1;
+    if (keys64) {
+      total = total64;
+      largest = largest64;
+    }
     h->dkdv_head_major[c] = head_major_balances((double)total * (double)per_tile_heads, (double)largest * G,
-                                                (int64_t)cus * (four ? 2 : 1), kv_heads_x_seqs);
+                                                (int64_t)cus * (four && h->layout[c] == 2 ? 2 : 1),
+                                                kv_heads_x_seqs);
     int64_t qtotal = 0, qlargest = 0;
     dq_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), qtotal, qlargest);
     h->dq_head_major[c] = head_major_balances((double)qtotal * (double)per_tile_heads, (double)qlargest,
@@ -570,7 +624,7 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
   if (h->desc.head_dim_v == 0) h->desc.head_dim_v = desc->head_dim;
   h->single_pass = desc->algorithm == FA_BWD_ALGO_SINGLE_PASS || desc->algorithm == FA_BWD_ALGO_SPLIT_REDUCE;
   h->split = desc->algorithm == FA_BWD_ALGO_SPLIT_REDUCE;
-  h->dkdv_layout = desc->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_8W ? 1 : desc->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_4W ? 2 : 0;
+  h->dkdv_layout = dkdv_layout_code(desc->algorithm);
   int cus = 0;
   if (hipGetDevice(&h->device) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess || cus < 1) {
@@ -627,7 +681,7 @@ fa_bwd_status fa_bwd_run_noalloc(const fa_bwd_desc* desc, const void* q, const v
   h.desc = *desc;
   if (h.desc.num_heads_kv == 0) h.desc.num_heads_kv = desc->num_heads;
   if (h.desc.head_dim_v == 0) h.desc.head_dim_v = desc->head_dim;
-  h.dkdv_layout = desc->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_8W ? 1 : desc->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_4W ? 2 : 0;
+  h.dkdv_layout = dkdv_layout_code(desc->algorithm);
   const fa_bwd_status cs = check_run(&h, scale, mask);
   if (cs != FA_BWD_OK) return cs;
   NoAllocDevice nd;
@@ -665,7 +719,9 @@ fa_bwd_status fa_bwd_plan(fa_bwd_handle* h, const int32_t* cu_seqlens_q_host, co
   std::vector<int32_t> items;
   int64_t n_kv = 0, n_q = 0;
   if (cu_seqlens_q_host) {
-    const fa_bwd_status st = build_plan(h->desc, cu_seqlens_q_host, cu_seqlens_kv_host, mask, items, n_kv, n_q);
+    const bool causal = mask == FA_BWD_MASK_CAUSAL || mask == FA_BWD_MASK_PADDING_CAUSAL;
+    const fa_bwd_status st =
+        build_plan(h->desc, h->layout[causal ? 1 : 0], cu_seqlens_q_host, cu_seqlens_kv_host, mask, items, n_kv, n_q);
     if (st != FA_BWD_OK) return st;
   }
   int prev = 0;
@@ -721,6 +777,18 @@ const char* fa_bwd_status_string(fa_bwd_status s) {
 }
 
 const fa_bwd_desc* fa_bwd_get_desc(const fa_bwd_handle* h) { return h ? &h->desc : nullptr; }
+
+int32_t fa_bwd_dkdv_layout(const fa_bwd_handle* h, int32_t mask) {
+  if (!h || mask < FA_BWD_MASK_NONE || mask > FA_BWD_MASK_PADDING_CAUSAL) return -1;
+  if (h->single_pass) return h->split ? FA_BWD_ALGO_SPLIT_REDUCE : FA_BWD_ALGO_SINGLE_PASS;
+  if (!pick_kernels(h->desc.head_dim, h->desc.head_dim_v).two_layouts) return FA_BWD_ALGO_RECOMPUTE_DQ;
+  const bool causal = mask == FA_BWD_MASK_CAUSAL || mask == FA_BWD_MASK_PADDING_CAUSAL;
+  switch (h->layout[causal]) {
+    case 3: return FA_BWD_ALGO_RECOMPUTE_DQ_64K;
+    case 2: return FA_BWD_ALGO_RECOMPUTE_DQ_4W;
+    default: return FA_BWD_ALGO_RECOMPUTE_DQ_8W;
+  }
+}
 
 fa_bwd_status fa_bwd_profile_enable(fa_bwd_handle* h, int32_t enable) {
   if (!h) return FA_BWD_ERR_INVALID_ARGUMENT;

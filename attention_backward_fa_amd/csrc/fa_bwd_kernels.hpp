@@ -213,6 +213,21 @@ __device__ __forceinline__ int tile_dma_off(int j, int lane, int cpr, int row_by
 // s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
+// LDS-DMA of 16 bytes per lane: LDS[dst + 16 lane] = resource bytes [voff, voff + 16) (zeros past
+// its end), like __builtin_amdgcn_raw_ptr_buffer_load_lds, but issued from an asm statement so that
+// the compiler does not track it. The compiler cannot tell one LDS buffer from another, so after a
+// tracked transfer it waits for every outstanding vector load before the next LDS read of any
+// buffer, which stalls a pipeline that reads one buffer while the next one fills. The caller
+// orders the transfer itself: s_waitcnt vmcnt(0) and a barrier before any read of the destination.
+// The compiler's own waits stay correct beside it, since vector loads complete in issue order
+// (the transfer only makes them wait longer). M0 holds the LDS address; the compiler writes M0
+// before the statement, which starts with the wait state an LDS-DMA needs after that write.
+__device__ __forceinline__ void dma16_untracked(__amdgpu_buffer_rsrc_t r, int voff,
+                                                __attribute__((address_space(3))) void* dst) {
+  const unsigned m0 = (unsigned)(uintptr_t)dst;
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
+}
+
 // Rows [start, start + len) of a sequence, clamped to the rows that exist, so that
 // every later row check is a single comparison against the length.
 __device__ __forceinline__ int clamp_len(int64_t start, int len, int64_t total) {

@@ -56,22 +56,34 @@ METRIC = "FA-bwd TFLOP/s + % bf16 MFMA peak, S=8192 H=32 D=128 causal, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 BF16_FLOP_PER_CLK_PER_CU = 4096  # 4 SIMDs, each one 32x32x16 bf16 MFMA (32768 FLOPs) per 32 clocks
 MASK_NAMES = {0: "none", 1: "padding", 2: "causal", 3: "padding_causal"}
-ALGORITHMS = {"default": 0, "single-pass": 1, "recompute": 2, "split-reduce": 3, "recompute-8w": 4, "recompute-4w": 5}
+ALGORITHMS = {"default": 0, "single-pass": 1, "recompute": 2, "split-reduce": 3, "recompute-8w": 4, "recompute-4w": 5,
+              "recompute-64k": 6}
 ALGORITHM_NAMES = {1: "single-pass (dQ atomics)",
                    2: "recompute (dK/dV kernel + dQ kernel; dK/dV layout chosen by load balance)",
                    3: "split-reduce (single-pass main kernel over 8 kv-tile splits + fixed-order dQ sum)",
                    4: "recompute (dK/dV kernel in eight-wave workgroups + dQ kernel)",
-                   5: "recompute (dK/dV kernel in four-wave workgroups + dQ kernel)"}
-def kernel_share(algorithm: int, d: int, dv: int) -> dict:
+                   5: "recompute (dK/dV kernel in four-wave workgroups + dQ kernel)",
+                   6: "recompute (dK/dV kernel with 64 keys per wave + dQ kernel)"}
+# the dK/dV layout a handle takes (fa_bwd_dkdv_layout's algorithm codes)
+LAYOUT_NAMES = {1: "none (single-pass form)", 3: "none (single-pass form)",
+                2: "one layout (heads wider than 128)",
+                4: "eight-wave workgroups, 32 keys per wave",
+                5: "four-wave workgroups (two per CU), 32 keys per wave",
+                6: "one four-wave workgroup per CU, 64 keys per wave"}
+
+
+def kernel_share(algorithm: int, d: int, dv: int, layout: int = 0) -> dict:
     """Share of the 5-GEMM algorithmic FLOPs each kernel runs itself. S = QK^T, dK, dQ contract or
-    produce the query/key head dim d, dP, dV the value head dim dv (2 * pairs * dim FLOPs each)."""
+    produce the query/key head dim d, dP, dV the value head dim dv (2 * pairs * dim FLOPs each).
+    Keys are the kernels' function names (the 64-key dK/dV layout is its own kernel)."""
     total = 3 * d + 2 * dv
     if algorithm == 1:
         return {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_dq_cast": 0.0}
     if algorithm == 3:
         return {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_split_reduce": 0.0}
     # dK/dV kernel: S, dP, dV, dK; dQ kernel: S and dP again, dQ
-    return {"fa_bwd_pre": 0.0, "fa_bwd_dkdv": (2 * d + 2 * dv) / total, "fa_bwd_dq": (2 * d + dv) / total}
+    dkdv = "fa_bwd_dkdv64" if layout == 6 else "fa_bwd_dkdv"
+    return {"fa_bwd_pre": 0.0, dkdv: (2 * d + 2 * dv) / total, "fa_bwd_dq": (2 * d + dv) / total}
 
 
 def visible_pairs(lq: int, lk: int, causal: bool, window: int) -> float:
@@ -443,6 +455,7 @@ def main():
     op = binding.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0],
                        algo, num_heads_kv=inp["k"].shape[1], window=inp["window"], head_dim_v=inp["v"].shape[2])
     algo_used = 2 if algo == 0 else algo
+    layout = op.dkdv_layout(inp["mask"])  # the dK/dV layout the recompute form takes on this workload
     if args.plan:  # host-side longest-first schedule from the (host) sequence offsets
         op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
     dq, dk, dv = (torch.empty_like(dev[x]) for x in ("q", "k", "v"))
@@ -469,7 +482,7 @@ def main():
     finite = all(bool(torch.isfinite(x).all()) for x in (dq, dk, dv))
     op.close()
     print(f"[bench] {args.steps} steps: {ms:.4f} ms/step", file=sys.stderr, flush=True)
-    shares = kernel_share(algo_used, d, inp["v"].shape[2])
+    shares = kernel_share(algo_used, d, inp["v"].shape[2], layout)
     names = list(shares)
     kern_ms = {n: sum(s[i] for s in stages) / len(stages) for i, n in enumerate(names)}
     step_ms = sorted(sum(s_) for s_ in stages)  # each timed step, first kernel start to last kernel end
@@ -485,6 +498,7 @@ def main():
               "total_tokens": tq, "mask": MASK_NAMES[inp["mask"]], "seed": inp["seed"],
               "algorithmic_flops": flops,
               "algorithm": ALGORITHM_NAMES[algo_used],
+              "dkdv_layout": LAYOUT_NAMES[layout],
               "schedule": "host longest-first plan" if args.plan else "dense grid"}
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -81,11 +81,15 @@ typedef enum {
   FA_BWD_ALGO_RECOMPUTE_DQ_8W = 4, /* FA_BWD_ALGO_RECOMPUTE_DQ with the eight-wave layout of the kv-outer
                                    kernel: one workgroup per compute unit, the two waves of each 32-key
                                    group split every 64-row q step */
-  FA_BWD_ALGO_RECOMPUTE_DQ_4W = 5  /* FA_BWD_ALGO_RECOMPUTE_DQ with the four-wave layout: two workgroups
+  FA_BWD_ALGO_RECOMPUTE_DQ_4W = 5, /* FA_BWD_ALGO_RECOMPUTE_DQ with the four-wave layout: two workgroups
                                    per compute unit, each wave takes whole 32-row q steps for its 32
                                    keys. Both layouts give the same results within fp32 rounding (the
                                    order of the dK, dV sums differs); for head dims above 128 both
                                    codes run the one wide-head layout */
+  FA_BWD_ALGO_RECOMPUTE_DQ_64K = 6 /* FA_BWD_ALGO_RECOMPUTE_DQ with the 64-key layout of the kv-outer
+                                   kernel: one four-wave workgroup per compute unit over 256 keys, each
+                                   wave holding 64 keys and their dK, dV sums, 32-row q steps; head
+                                   dims of exactly 128 and no window (else FA_BWD_ERR_UNSUPPORTED) */
 } fa_bwd_algo;
 
 typedef enum {
@@ -238,6 +242,18 @@ const char* fa_bwd_status_string(fa_bwd_status s);
 
 /* Descriptor the handle was created with (for bindings); NULL on NULL. */
 const fa_bwd_desc* fa_bwd_get_desc(const fa_bwd_handle* h);
+
+/* Layout of the recompute form's dK/dV kernel that fa_bwd_run takes on this
+ * handle under `mask` (a causal mask, with or without padding, can select
+ * another layout than none or padding), chosen when the handle was created
+ * from the descriptor and the device's compute-unit count:
+ * FA_BWD_ALGO_RECOMPUTE_DQ_8W, FA_BWD_ALGO_RECOMPUTE_DQ_4W or
+ * FA_BWD_ALGO_RECOMPUTE_DQ_64K for head dims up to 128, and
+ * FA_BWD_ALGO_RECOMPUTE_DQ for wider heads (whose kernels have one layout).
+ * Returns FA_BWD_ALGO_SINGLE_PASS or FA_BWD_ALGO_SPLIT_REDUCE for handles of
+ * those forms, and -1 for a NULL handle or an invalid mask. Host only; does
+ * not touch the device. */
+int32_t fa_bwd_dkdv_layout(const fa_bwd_handle* h, int32_t mask);
 
 /* Per-kernel timing for benchmarks. While enabled, every fa_bwd_run (and
  * fa_bwd_run_lse) also records four HIP events on its stream, around its three

@@ -82,7 +82,10 @@ def _create(**kw):
     (dict(head_dim=64, head_dim_v=128, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(num_heads=4, num_heads_kv=1, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(window=32, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
-    (dict(algorithm=6), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(algorithm=7), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(algorithm=6, head_dim=64), B.FA_BWD_ERR_UNSUPPORTED),                 # 64-key layout: d = 128,
+    (dict(algorithm=6, head_dim_v=64), B.FA_BWD_ERR_UNSUPPORTED),               # no window
+    (dict(algorithm=6, window=16), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(algorithm=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(total_q=1 << 40, num_heads=8), B.FA_BWD_ERR_INVALID_ARGUMENT),          # index range
     (dict(max_seqlen_kv=1 << 30, num_heads=1 << 10, batch=1 << 10), B.FA_BWD_ERR_INVALID_ARGUMENT),  # grid size
@@ -122,6 +125,7 @@ def test_run_and_profile_reject_null_handle():
     assert lib.fa_bwd_profile_collect(None, None, 0, ctypes.byref(n)) == B.FA_BWD_ERR_INVALID_ARGUMENT
     assert lib.fa_bwd_profile_enable(None, 1) == B.FA_BWD_ERR_INVALID_ARGUMENT
     assert not lib.fa_bwd_get_desc(None)
+    assert lib.fa_bwd_dkdv_layout(None, 0) == -1
 
 
 def _noalloc(desc, ptr=256, l=True):

@@ -41,7 +41,16 @@ CASES = [
 
 ALGOS = {"recompute": B.FA_BWD_ALGO_RECOMPUTE_DQ, "recompute8w": B.FA_BWD_ALGO_RECOMPUTE_DQ_8W,
          "recompute4w": B.FA_BWD_ALGO_RECOMPUTE_DQ_4W, "singlepass": B.FA_BWD_ALGO_SINGLE_PASS,
-         "splitreduce": B.FA_BWD_ALGO_SPLIT_REDUCE}
+         "splitreduce": B.FA_BWD_ALGO_SPLIT_REDUCE, "recompute64k": B.FA_BWD_ALGO_RECOMPUTE_DQ_64K}
+
+
+def _supported(case, algo):
+    # the 64-key dK/dV layout exists for head dims of 128 without a window
+    return algo != "recompute64k" or (case.head_dim == 128 and case.head_dim_v in (0, 128) and case.window == 0)
+
+
+# (case, algorithm) pairs, case-major so that each case's oracle reference is computed once
+PAIRS = [(c, a) for c in CASES for a in ALGOS if _supported(c, a)]
 LAYOUTS = {"8w": B.FA_BWD_ALGO_RECOMPUTE_DQ_8W, "4w": B.FA_BWD_ALGO_RECOMPUTE_DQ_4W}
 
 
@@ -61,8 +70,7 @@ def _case_reference(case):
     return clone, (o.clone(), m.clone(), l.clone()), ref
 
 
-@pytest.mark.parametrize("algo", list(ALGOS))
-@pytest.mark.parametrize("case", CASES, ids=[c.name for c in CASES])
+@pytest.mark.parametrize("case,algo", PAIRS, ids=[f"{c.name}-{a}" for c, a in PAIRS])
 def test_parity_full(case, algo):
     print(f"[parity] {case.name} ({algo})", flush=True)
     inp, (o, m, l), ref = _case_reference(case)
@@ -122,11 +130,21 @@ def test_dkdv_layouts_agree(case):
 
 
 @pytest.mark.parametrize("case,expect", [
-    # causal, 256 heads of 1024 tokens: the dK/dV work (64-row q steps) totals 72 per head, 18432 in
-    # all; the largest workgroup has 16, and 2 * 16 * 256 CUs = 8192 <= 18432: the four-wave layout
-    (I.custom_case("layout_rule_4w", 256, 128, I.MASK_CAUSAL, 213, [1024]), B.FA_BWD_ALGO_RECOMPUTE_DQ_4W),
-    # no mask, 8 heads of 2 x 2048 tokens: 256 workgroups of 32 steps each; 2 * 32 * 256 > 8192: eight waves
+    # causal, d 64 (no 64-key layout), 256 heads of 1024 tokens: the dK/dV work (128-key tiles, 64-row q
+    # steps) totals 72 per head, 18432 in all; the largest workgroup has 16, and 2 * 16 * 256 CUs =
+    # 8192 <= 18432: the four-wave layout
+    (I.custom_case("layout_rule_4w", 256, 64, I.MASK_CAUSAL, 213, [1024]), B.FA_BWD_ALGO_RECOMPUTE_DQ_4W),
+    # no mask, 8 heads of 2 x 2048 tokens: 256-key tiles of 64 steps (32 rows) total 8192, and
+    # 2 * 64 * 256 > 8192; 128-key tiles: 256 workgroups of 32 steps, 2 * 32 * 256 > 8192: eight waves
     (I.custom_case("layout_rule_8w", 8, 128, I.MASK_NONE, 214, [2048, 2048]), B.FA_BWD_ALGO_RECOMPUTE_DQ_8W),
+    # causal, d 128, 256 heads of 1024 tokens: 256-key tiles of 32, 24, 16 and 8 steps total 80 per
+    # head, 20480 in all, and 2 * 32 * 256 = 16384 <= 20480: the 64-key layout
+    (I.custom_case("layout_rule_64k", 256, 128, I.MASK_CAUSAL, 215, [1024]), B.FA_BWD_ALGO_RECOMPUTE_DQ_64K),
+    # causal, d 128, 64 query heads over 16 K/V heads of 2048 tokens: each workgroup runs the steps of 4
+    # query heads; 256-key tiles: 288 steps per head, 18432 in all, largest workgroup 4 * 64, and
+    # 2 * 256 * 256 > 18432; 128-key tiles: 17408 in all, largest 4 * 32, 2 * 128 * 256 > 17408: eight waves
+    (I.custom_case("layout_rule_gqa", 64, 128, I.MASK_CAUSAL, 216, [2048], heads_kv=16),
+     B.FA_BWD_ALGO_RECOMPUTE_DQ_8W),
 ], ids=lambda x: x.name if hasattr(x, "name") else str(x))
 def test_default_picks_the_balanced_dkdv_layout(case, expect):
     """The default form takes the dK/dV layout the load-balance rule names (figures for the 256
@@ -134,6 +152,11 @@ def test_default_picks_the_balanced_dkdv_layout(case, expect):
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the expected layouts are worked out for 256 compute units")
     inp = I.make(case)
+    tq, heads, d = inp["q"].shape
+    with B.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0],
+                 num_heads_kv=inp["k"].shape[1]) as op:
+        assert op.dkdv_layout(case.mask) == expect
+        assert op.dkdv_layout(-1) == -1
     o, m, l = P.oracle_stats(inp)
     got = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_DEFAULT)
     ref = P.run_gpu(inp, o, m, l, algorithm=expect)
@@ -199,16 +222,21 @@ GQA_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", GQA_CASES, ids=[c.name for c in GQA_CASES])
-def test_parity_grouped_heads(case):
+# the default form, and the 64-key dK/dV layout (whose workgroups run every query head of a K/V head)
+GQA_PAIRS = [(c, a) for c in GQA_CASES for a in ("recompute", "recompute64k") if _supported(c, a)]
+
+
+@pytest.mark.parametrize("case,algo", GQA_PAIRS, ids=[f"{c.name}-{a}" for c, a in GQA_PAIRS])
+def test_parity_grouped_heads(case, algo):
     inp = I.make(case)
-    print(f"[parity-gqa] {case.name}: H={case.heads} H_kv={case.heads_kv} d={case.head_dim} mask={case.mask}",
-          flush=True)
+    print(f"[parity-gqa] {case.name} ({algo}): H={case.heads} H_kv={case.heads_kv} d={case.head_dim} "
+          f"mask={case.mask}", flush=True)
     o, m, l = P.oracle_stats(inp)
-    gpu = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_DEFAULT)
+    gpu = P.run_gpu(inp, o, m, l, algorithm=ALGOS[algo])
     ref = P.oracle_backward(inp, o, m, l)
     res = P.check_full(inp, gpu, ref)
-    print(f"[parity-gqa] {case.name}: " + " ".join(f"{k}: rel_l2={v[0]:.2e}" for k, v in res.items()), flush=True)
+    print(f"[parity-gqa] {case.name} ({algo}): " + " ".join(f"{k}: rel_l2={v[0]:.2e}" for k, v in res.items()),
+          flush=True)
 
 
 def test_grouped_heads_single_pass_unsupported():
