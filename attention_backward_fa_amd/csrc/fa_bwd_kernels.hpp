@@ -56,126 +56,7 @@ __device__ __forceinline__ bool row_in_sequence(int64_t t, const int* cu, int ba
   return t >= cu[0] && t < cu[batch];
 }
 
-// ------------------------------------------------------------------ stage 1: row statistics
-
-struct PreArgs {
-  const bf16* o;
-  const bf16* dout;
-  const float* m;  // row max, or the log-sum-exp when l is null
-  const float* l;  // row sum, or null
-  const int* cu_q;
-  const int* cu_kv;
-  float* lse2;    // [H][total_q]: m*log2(e) + log2(l)
-  float* dvec;    // [H][total_q]: rowsum(O*dO)
-  float* dq_acc;  // [H][total_q][d_qk], zeroed when not null
-  bf16* dq;       // when not null: rows outside every sequence are zeroed
-  bf16* dk;
-  bf16* dv;
-  int64_t total_q, total_kv;
-  int H, Hk, batch, max_seqlen_q, max_seqlen_kv, padded;  // query heads, K/V heads
-  int d_qk, d_v;  // head dims of Q, K (dQ, dK) and of V, O, dO (dV); multiples of 8
-};
-
-// One thread per 8 features of a (token, head) row; TPR is a power of two >= max(d_qk, d_v) / 8.
-// Block i takes 256 / TPR consecutive tokens of head i % H (heads fastest across blocks, so the
-// blocks in flight read one contiguous range of tokens), which makes the statistics it writes
-// into the head-major [H][T_q] arrays one contiguous run. EXACT: d_qk = d_v = 8 TPR.
-template <int TPR, bool EXACT>
-__global__ __launch_bounds__(256) void fa_bwd_pre(PreArgs a) {
-  constexpr int RPB = 256 / TPR;  // tokens per block
-  const int sub = threadIdx.x & (TPR - 1);
-  const unsigned grp = blockIdx.x / (unsigned)a.H;
-  const int h = (int)(blockIdx.x - grp * (unsigned)a.H);
-  const int64_t t = (int64_t)grp * RPB + threadIdx.x / TPR;
-  const int64_t pair = t * a.H + h;
-  const int cq = EXACT ? TPR : a.d_qk / 8, cv = EXACT ? TPR : a.d_v / 8;  // 16-byte chunks per row
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  if (t < a.total_q) {
-    float acc = 0.f;
-    if (sub < cv) {
-      const int64_t off = pair * (8 * cv) + sub * 8;
-      const bf16x8 ov = *(const bf16x8*)(a.o + off);
-      const bf16x8 gv = *(const bf16x8*)(a.dout + off);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc += from_bf16(ov[e]) * from_bf16(gv[e]);
-    }
-#pragma unroll
-    for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);  // partners share the row
-    if (a.dq_acc && sub < cq) {
-      float* accrow = a.dq_acc + ((int64_t)h * a.total_q + t) * (8 * cq) + sub * 8;
-      const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
-      *(f32x4*)accrow = zf;
-      *(f32x4*)(accrow + 4) = zf;
-    }
-    if (a.dq && sub < cq && !row_in_sequence(t, a.cu_q, a.batch, a.padded, a.max_seqlen_q))
-      *(u32x4*)(a.dq + pair * (8 * cq) + sub * 8) = z;
-    if (sub == 0) {
-      const int64_t sidx = (int64_t)h * a.total_q + t;
-      a.dvec[sidx] = acc;
-      // (m, l) from the forward, or (when l is null) m holds the log-sum-exp m + ln(l) itself
-      a.lse2[sidx] = a.l ? a.m[pair] * kLog2e + __log2f(a.l[pair]) : a.m[pair] * kLog2e;
-    }
-  }
-  if (h < a.Hk && t < a.total_kv && !row_in_sequence(t, a.cu_kv, a.batch, a.padded, a.max_seqlen_kv)) {
-    const int64_t kr = t * a.Hk + h;
-    if (sub < cq) *(u32x4*)(a.dk + kr * (8 * cq) + sub * 8) = z;
-    if (sub < cv) *(u32x4*)(a.dv + kr * (8 * cv) + sub * 8) = z;
-  }
-}
-
-// ------------------------------------------------------------------ stage 2: single-pass main kernel
-
-struct MainArgs {
-  const bf16* q;
-  const bf16* k;
-  const bf16* v;
-  const bf16* dout;
-  const float* lse2;
-  const float* dvec;
-  const int* cu_q;
-  const int* cu_kv;
-  float* dq_acc;  // fp32 [H][total_q][D] accumulator (single-pass form)
-  bf16* dq;       // bf16 output (recompute form)
-  bf16* dk;
-  bf16* dv;
-  int64_t total_q, total_kv;
-  int H, Hk, batch, max_seqlen_q, max_seqlen_kv, padded, causal;  // query heads, K/V heads (H % Hk == 0)
-  int window;        // > 0: each query sees only its left local window of keys (i - window, i]
-  int d_qk, d_v;     // head dims of Q, K (dQ, dK) and of V, dO (dV): at most the kernel's padded dims
-  float scale_log2;  // scale * log2(e)
-  float scale;
-  const int* sched;  // recompute kernels: (tile, sequence * heads + head) per workgroup, or null (dense grid)
-  int head_major;    // recompute kernels, dense grid, (K/V) heads x sequences a multiple of 8: each XCD
-                     // takes the tiles of one (sequence, head) at a time
-};
-
-// Splits of the split-and-reduce form: workgroups per (head, sequence), each with its own fp32 dQ
-// buffer; split s takes the kv tiles s, s + kSplits, ...
-constexpr int kSplits = 8;
-
-template <int D>
-struct MainCfg {
-  static constexpr int BN = 128;                 // kv rows per workgroup (32 per wave)
-  static constexpr int BM = 64;                  // q rows per step
-  static constexpr int NW = 4;                   // waves
-  static constexpr int KSD = D / 16;             // MFMA k-steps over the head dim
-  static constexpr int NTD = D / 32;             // 32-wide output tiles over the head dim
-  static constexpr int TPW = D / 64;             // dQ output tiles per wave
-  static constexpr int QS = D + 8;               // row stride (elements) of the Q, dO and K tiles
-  static constexpr int SS = BM + 8;              // row stride (elements) of dS^T
-  static constexpr int CPR = QS / 8;             // 16-byte chunks per padded row
-  static constexpr int TILE = BM * QS;           // elements of one Q or dO buffer
-  static constexpr int TILE_BYTES = TILE * 2;
-  static constexpr int NDMA = TILE_BYTES / 1024; // 1 KB LDS-DMA transfers per tile
-  static constexpr int OFF_K = 0;                          // K tile [BN][QS]
-  static constexpr int OFF_Q = OFF_K + BN * QS * 2;        // Q [2][BM][QS]
-  static constexpr int OFF_DO = OFF_Q + 2 * TILE_BYTES;    // dO [2][BM][QS]
-  static constexpr int OFF_DS = OFF_DO + 2 * TILE_BYTES;   // dS^T [BN][SS]
-  static constexpr int OFF_ST = OFF_DS + BN * SS * 2;      // [2 buffers][lse2, D][BM] fp32
-  static constexpr int LDS_BYTES = OFF_ST + 4 * BM * 4;
-  static_assert(TILE_BYTES % 1024 == 0, "a tile is a whole number of 1 KB transfers");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-};
+// ------------------------------------------------------------------ buffer and tile helpers
 
 // Row of a 32-row M-tile (Q, dO) that MFMA row m reads, and kv row of the 128-row tile that
 // k-index k of the dQ GEMM reads. With rows padded by 16 bytes, this interleave makes the
@@ -237,6 +118,153 @@ __device__ __forceinline__ int clamp_len(int64_t start, int len, int64_t total) 
 
 __device__ __forceinline__ int imin(int x, int y) { return x < y ? x : y; }
 __device__ __forceinline__ int imax(int x, int y) { return x > y ? x : y; }
+
+// ------------------------------------------------------------------ stage 1: row statistics
+
+struct PreArgs {
+  const bf16* o;
+  const bf16* dout;
+  const float* m;  // row max, or the log-sum-exp when l is null
+  const float* l;  // row sum, or null
+  const int* cu_q;
+  const int* cu_kv;
+  float* lse2;    // [H][total_q]: m*log2(e) + log2(l)
+  float* dvec;    // [H][total_q]: rowsum(O*dO)
+  float* dq_acc;  // [H][total_q][d_qk], zeroed when not null
+  bf16* dq;       // when not null: rows outside every sequence are zeroed
+  bf16* dk;
+  bf16* dv;
+  int64_t total_q, total_kv;
+  int H, Hk, batch, max_seqlen_q, max_seqlen_kv, padded;  // query heads, K/V heads
+  int d_qk, d_v;  // head dims of Q, K (dQ, dK) and of V, O, dO (dV); multiples of 8
+};
+
+// Sum of v over aligned groups of N lanes (N a power of two up to 32), in every lane of the group:
+// DPP adds within each 16-lane row (quad swaps, then the half-row and row mirrors), one lane
+// exchange across the two rows of a 32-lane group.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), decltype(ctrl)::value,
+                                                              0xF, 0xF, true));
+  };
+  if constexpr (N >= 2) v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if constexpr (N >= 16) v += dpp(v, std::integral_constant<int, 0x140>{}); // row_mirror
+  if constexpr (N >= 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+// One thread per 8 features of a (token, head) row; TPR is a power of two >= max(d_qk, d_v) / 8.
+// Block i takes 256 / TPR consecutive tokens of head i % H (heads fastest across blocks, so the
+// blocks in flight read one contiguous range of tokens), which makes the statistics it writes
+// into the head-major [H][T_q] arrays one contiguous run. EXACT: d_qk = d_v = 8 TPR.
+// Every load a thread needs (O, dO, m, l and the sequence offsets of its row's zero fills) is
+// issued before the first of them is used, so a wave waits for memory once.
+template <int TPR, bool EXACT>
+__global__ __launch_bounds__(256) void fa_bwd_pre(PreArgs a) {
+  constexpr int RPB = 256 / TPR;  // tokens per block
+  const int sub = threadIdx.x & (TPR - 1);
+  const unsigned grp = blockIdx.x / (unsigned)a.H;
+  const int h = (int)(blockIdx.x - grp * (unsigned)a.H);
+  const int64_t t = (int64_t)grp * RPB + threadIdx.x / TPR;
+  const int64_t pair = t * a.H + h;
+  const int cq = EXACT ? TPR : a.d_qk / 8, cv = EXACT ? TPR : a.d_v / 8;  // 16-byte chunks per row
+  const bool qrow = t < a.total_q;
+  bf16x8 ov{}, gv{};
+  if (qrow && sub < cv) {
+    const int64_t off = pair * (8 * cv) + sub * 8;
+    ov = *(const bf16x8*)(a.o + off);
+    gv = *(const bf16x8*)(a.dout + off);
+  }
+  float mv = 0.f, lv = 1.f;
+  if (qrow && sub == 0) {
+    mv = a.m[pair];
+    if (a.l) lv = a.l[pair];
+  }
+  const bool zero_q = qrow && a.dq && sub < cq && !row_in_sequence(t, a.cu_q, a.batch, a.padded, a.max_seqlen_q);
+  const bool zero_kv = h < a.Hk && t < a.total_kv && !row_in_sequence(t, a.cu_kv, a.batch, a.padded, a.max_seqlen_kv);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  if (qrow) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += from_bf16(ov[e]) * from_bf16(gv[e]);
+    acc = group_sum<TPR>(acc);  // partners share the row
+    if (a.dq_acc && sub < cq) {  // single-pass form: its fp32 dQ accumulator starts at 0
+      float* accrow = a.dq_acc + ((int64_t)h * a.total_q + t) * (8 * cq) + sub * 8;
+      const f32x4 zf = {0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)accrow = zf;
+      *(f32x4*)(accrow + 4) = zf;
+    }
+    if (zero_q) *(u32x4*)(a.dq + pair * (8 * cq) + sub * 8) = z;
+    if (sub == 0) {
+      const int64_t sidx = (int64_t)h * a.total_q + t;
+      a.dvec[sidx] = acc;
+      // (m, l) from the forward, or (when l is null) m holds the log-sum-exp m + ln(l) itself
+      a.lse2[sidx] = a.l ? mv * kLog2e + __log2f(lv) : mv * kLog2e;
+    }
+  }
+  if (zero_kv) {
+    const int64_t kr = t * a.Hk + h;
+    if (sub < cq) *(u32x4*)(a.dk + kr * (8 * cq) + sub * 8) = z;
+    if (sub < cv) *(u32x4*)(a.dv + kr * (8 * cv) + sub * 8) = z;
+  }
+}
+
+// ------------------------------------------------------------------ stage 2: single-pass main kernel
+
+struct MainArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* dout;
+  const float* lse2;
+  const float* dvec;
+  const int* cu_q;
+  const int* cu_kv;
+  float* dq_acc;  // fp32 [H][total_q][D] accumulator (single-pass form)
+  bf16* dq;       // bf16 output (recompute form)
+  bf16* dk;
+  bf16* dv;
+  int64_t total_q, total_kv;
+  int H, Hk, batch, max_seqlen_q, max_seqlen_kv, padded, causal;  // query heads, K/V heads (H % Hk == 0)
+  int window;        // > 0: each query sees only its left local window of keys (i - window, i]
+  int d_qk, d_v;     // head dims of Q, K (dQ, dK) and of V, dO (dV): at most the kernel's padded dims
+  float scale_log2;  // scale * log2(e)
+  float scale;
+  const int* sched;  // recompute kernels: (tile, sequence * heads + head) per workgroup, or null (dense grid)
+  int head_major;    // recompute kernels, dense grid, (K/V) heads x sequences a multiple of 8: each XCD
+                     // takes the tiles of one (sequence, head) at a time
+};
+
+// Splits of the split-and-reduce form: workgroups per (head, sequence), each with its own fp32 dQ
+// buffer; split s takes the kv tiles s, s + kSplits, ...
+constexpr int kSplits = 8;
+
+template <int D>
+struct MainCfg {
+  static constexpr int BN = 128;                 // kv rows per workgroup (32 per wave)
+  static constexpr int BM = 64;                  // q rows per step
+  static constexpr int NW = 4;                   // waves
+  static constexpr int KSD = D / 16;             // MFMA k-steps over the head dim
+  static constexpr int NTD = D / 32;             // 32-wide output tiles over the head dim
+  static constexpr int TPW = D / 64;             // dQ output tiles per wave
+  static constexpr int QS = D + 8;               // row stride (elements) of the Q, dO and K tiles
+  static constexpr int SS = BM + 8;              // row stride (elements) of dS^T
+  static constexpr int CPR = QS / 8;             // 16-byte chunks per padded row
+  static constexpr int TILE = BM * QS;           // elements of one Q or dO buffer
+  static constexpr int TILE_BYTES = TILE * 2;
+  static constexpr int NDMA = TILE_BYTES / 1024; // 1 KB LDS-DMA transfers per tile
+  static constexpr int OFF_K = 0;                          // K tile [BN][QS]
+  static constexpr int OFF_Q = OFF_K + BN * QS * 2;        // Q [2][BM][QS]
+  static constexpr int OFF_DO = OFF_Q + 2 * TILE_BYTES;    // dO [2][BM][QS]
+  static constexpr int OFF_DS = OFF_DO + 2 * TILE_BYTES;   // dS^T [BN][SS]
+  static constexpr int OFF_ST = OFF_DS + BN * SS * 2;      // [2 buffers][lse2, D][BM] fp32
+  static constexpr int LDS_BYTES = OFF_ST + 4 * BM * 4;
+  static_assert(TILE_BYTES % 1024 == 0, "a tile is a whole number of 1 KB transfers");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
 
 // The single-pass form: one workgroup per (kv tile, head, sequence) forms the dK, dV and dQ
 // contributions of every (q tile, kv tile) pair and adds the dQ partials to the fp32 accumulator

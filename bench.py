@@ -22,7 +22,9 @@ kernel on the launch stream during the timed steps; its work counted as the
 GEMMs that kernel itself runs; ``traffic`` is the HBM bytes per launch measured
 with rocprofv3 FETCH_SIZE/WRITE_SIZE counters and recorded in
 profiles/fa_bwd_traffic_causal_s8192_h32_d128.md, reported only while the
-kernel sources still hash to the recorded value, else null) and a
+kernel sources still hash to the recorded value, else null; ``clock_sustained_ghz`` is
+that kernel's shader-cycle count per launch, recorded the same way from GRBM_GUI_ACTIVE in
+profiles/fa_bwd_counters_causal_s8192_h32_d128.md, over its live time in this run) and a
 ``cpu_baseline`` object (the fp64 oracle's backward timed on this host's cores
 over a bounded sample of the same workload).
 
@@ -221,14 +223,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(kernel: str, workload: str, algorithm: int):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or None
-    when the summary is absent, covers another kernel/workload/algorithm, or was
-    taken on kernel sources other than the current ones."""
-    if not os.path.exists(TRAFFIC_FILE):
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_bwd_counters_causal_s8192_h32_d128.md")
+
+
+def profile_record(path: str, field: str, kernel: str, workload: str, algorithm: int):
+    """A number from the record of a committed profile summary, or None when the summary is absent,
+    covers another kernel/workload/algorithm, or was taken on kernel sources other than the current
+    ones."""
+    if not os.path.exists(path):
         return None
     rec = {}
-    with open(TRAFFIC_FILE) as fh:
+    with open(path) as fh:
         for line in fh:
             if line.startswith("- ") and ": " in line:
                 k, v = line[2:].strip().split(": ", 1)
@@ -236,9 +241,22 @@ def recorded_traffic(kernel: str, workload: str, algorithm: int):
     try:
         ok = (rec["kernel"] == kernel and rec["workload"] == workload and int(rec["algorithm"]) == algorithm
               and rec["source_sha256"] == kernel_source_hash())
-        return float(rec["traffic_bytes_per_launch"]) if ok else None
+        return float(rec[field]) if ok else None
     except (KeyError, ValueError):
         return None
+
+
+def recorded_traffic(kernel: str, workload: str, algorithm: int):
+    """HBM bytes per launch of `kernel` from the committed counter summary (FETCH_SIZE + WRITE_SIZE,
+    calibrated), or None."""
+    return profile_record(TRAFFIC_FILE, "traffic_bytes_per_launch", kernel, workload, algorithm)
+
+
+def sustained_clock_ghz(kernel: str, workload: str, algorithm: int, kernel_ms: float):
+    """Shader clock while `kernel` ran in this process: its shader-cycle count per launch from the
+    committed counter summary (GRBM_GUI_ACTIVE per XCD) over its live time, or None."""
+    cycles = profile_record(COUNTERS_FILE, "cycles_per_launch", kernel, workload, algorithm)
+    return None if cycles is None else round(cycles / (kernel_ms * 1e-3) / 1e9, 3)
 
 
 def copy_calibration(mib: int, device) -> None:
@@ -510,7 +528,8 @@ def main():
         "kernels_ms": {n: round(v, 5) for n, v in kern_ms.items()},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": recorded_traffic(dom, args.workload, algo_used), "work_flops": dom_flops},
+                     "traffic": recorded_traffic(dom, args.workload, algo_used), "work_flops": dom_flops,
+                     "clock_sustained_ghz": sustained_clock_ghz(dom, args.workload, algo_used, kern_ms[dom])},
         "peak_derived": peak_info,
         "outputs_finite": finite,
     }
