@@ -414,7 +414,8 @@ void fa_bwd_dkdv64(MainArgs a) {
     // step sp: the tile of sp + 1 loads; the first GEMMs of sp, then the second GEMMs of sp - 1 beside
     // the softmax of sp
     int bq = 0, bp = 0, b1 = 1;  // buffers of steps sp - 1, sp, sp + 1 (rotating through NBUF)
-    for (int sp = 1; sp < n_steps; ++sp) {
+    auto step = [&](int sp, const bf16x8 (&pko)[2][2], const bf16x8 (&dsko)[2][2], bf16x8 (&pkw)[2][2],
+                    bf16x8 (&dskw)[2][2]) {
       cur = nxt;
       nxt = advance(cur);
       bq = bp;
@@ -428,7 +429,19 @@ void fa_bwd_dkdv64(MainArgs a) {
           st2 = load_stats(nxt);
         }
       });
-      slots(std::true_type{}, std::true_type{}, bq, s, dp, pk, dsk, pkn, dskn);
+      slots(std::true_type{}, std::true_type{}, bq, s, dp, pko, dsko, pkw, dskw);
+      if (has1) store_stats(b1, st2);
+      wait_tiles();
+      __syncthreads();
+    };
+    // two steps per iteration, the P and dS registers of one step and the next swapping roles
+    int sp = 1;
+    for (; sp + 1 < n_steps; sp += 2) {
+      step(sp, pk, dsk, pkn, dskn);
+      step(sp + 1, pkn, dskn, pk, dsk);
+    }
+    if (sp < n_steps) {
+      step(sp, pk, dsk, pkn, dskn);
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
@@ -436,9 +449,6 @@ void fa_bwd_dkdv64(MainArgs a) {
           pk[n][e] = pkn[n][e];
           dsk[n][e] = dskn[n][e];
         }
-      if (has1) store_stats(b1, st2);
-      wait_tiles();
-      __syncthreads();
     }
     // epilogue: the second GEMMs of the last step
     slots(std::true_type{}, std::false_type{}, bp, s, dp, pk, dsk, pkn, dskn);
