@@ -175,8 +175,9 @@ __global__ __launch_bounds__(256) void fa_bwd_pre(PreArgs a) {
   bf16x8 ov{}, gv{};
   if (qrow && sub < cv) {
     const int64_t off = pair * (8 * cv) + sub * 8;
-    ov = *(const bf16x8*)(a.o + off);
-    gv = *(const bf16x8*)(a.dout + off);
+    // read once: non-temporal, so that the streamed rows do not displace cached tiles
+    ov = __builtin_nontemporal_load((const bf16x8*)(a.o + off));
+    gv = __builtin_nontemporal_load((const bf16x8*)(a.dout + off));
   }
   float mv = 0.f, lv = 1.f;
   if (qrow && sub == 0) {
