@@ -13,10 +13,11 @@
 // Every Q, dO or transposed operand a wave reads from LDS feeds two MFMAs (one per key tile).
 //
 // Pipeline of a step: the first GEMMs (S, dP) of the step, with the next step's tile transfers
-// issued among them; then 32 slots, each issuing one second-GEMM MFMA of the previous step
-// (dV += P^T dO, dK += dS^T Q) beside part of this step's softmax (P, dS on the VALU), so that one
-// wave keeps the matrix core busy while it computes P and dS. One barrier per step guards the tile
-// buffers.
+// issued among them in four stages (one per MFMA, in the MFMAs' shadow); then 32 slots, each issuing
+// one second-GEMM MFMA of the previous step (dV += P^T dO, dK += dS^T Q) beside part of this step's
+// softmax (P, dS on the VALU), so that one wave keeps the matrix core busy while it computes P and dS.
+// One barrier per step guards the tile buffers; the last four second-GEMM MFMAs of a step wait until
+// after it, and run while the next step's first LDS reads are in flight.
 #pragma once
 #include "fa_bwd_kernels.hpp"
 
@@ -36,6 +37,7 @@ struct Dkdv64Cfg {
   static constexpr int PF_A = 4;                // first GEMMs: LDS operands read this many MFMAs ahead
   static constexpr int PF_B = 2;                // second GEMMs: B fragments read this many pairs ahead
   static constexpr int MID_AT = 8;              // first-GEMM MFMA before which the next tile's loads issue
+  static constexpr int DEFER = 4;               // second-GEMM MFMAs of a step issued after its barrier
   static constexpr int T_BYTES = (BM * QS * 2 + 1023) / 1024 * 1024;  // one Q (dO) buffer, whole 1 KB transfers
   static constexpr int NDMA = T_BYTES / 1024;
   static constexpr int NJ = (NDMA + NW - 1) / NW;  // transfers per wave per tile
@@ -113,14 +115,20 @@ void fa_bwd_dkdv64(MainArgs a) {
   const int qt0 = CAUSAL ? kv0 / BM : 0;
   const int nq = n_qt > qt0 ? n_qt - qt0 : 0;
   const int n_steps = G * nq;
-  // a step's position: q tile and query head, advanced one step at a time (no divisions in the loop)
+  // a step's position: q tile and query head, the byte offset of its Q (and dO) rows from the tensors'
+  // bases and the index of its head's first statistic; advanced one step at a time with additions
   struct Pos {
     int tile, head;
+    int64_t off, srow;
   };
+  const int64_t head_off = (int64_t)(q_start + qt0 * BM) * rsqb;  // of the first step of a head, less the head
   auto advance = [&](Pos p) {
+    p.off += BM * rsqb;
     if (++p.tile == qt0 + nq) {
       p.tile = qt0;
       ++p.head;
+      p.off = head_off + (int64_t)p.head * (D * 2);
+      p.srow += a.total_q;
     }
     return p;
   };
@@ -153,39 +161,60 @@ void fa_bwd_dkdv64(MainArgs a) {
                                                16, tile_dma_off(j, lane, C::CPR, rskqb, D), 0, 0, 0);
   }
   // Q and dO tile of a step into buffer bi: 9 transfers of 1 KB each, transfers w and w + 4 of every
-  // wave and transfer 8 of wave 0 (the per-lane global offsets are formed once)
-  static_assert(C::NDMA == 9 && C::NW == 4, "transfer assignment");
+  // wave and transfer 8 of wave 3 (wave 0 loads the statistics; the per-lane global offsets are formed
+  // once). The work is issued in stages, one per first-GEMM MFMA, so that it runs in their shadow:
+  // stage 0 forms the buffer resources, stages 1-3 issue the transfers and the statistics load.
+  static_assert(C::NDMA == 9 && C::NW == 4 && 2 * BM == 64, "transfer and statistics assignment");
   const int dmo0 = tile_dma_off(w, lane, C::CPR, rsqb, D), dmo1 = tile_dma_off(w + 4, lane, C::CPR, rsqb, D);
   const int dmo2 = tile_dma_off(8, lane, C::CPR, rsqb, D);
-  auto issue_tile = [&](Pos ps, int bi) {
-    const int i0 = ps.tile * BM, hq = ps.head;
-    const int64_t bytes = (int64_t)imin(Lq - i0, BM) * rsqb;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + (q_start + i0) * rsq + (int64_t)hq * D, bytes);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + (q_start + i0) * rsq + (int64_t)hq * D, bytes);
-    // untracked by the compiler: the step's first LDS reads of another buffer must not wait for it
-    // (wait_tiles and the step's barrier order it before buffer bi is read)
-    auto dma = [&](int j, int off) {
-      dma16_untracked(rq, off, (__attribute__((address_space(3))) void*)(smem + C::OFF_Q + bi * C::T_BYTES + 1024 * j));
-      dma16_untracked(rd, off, (__attribute__((address_space(3))) void*)(smem + C::OFF_DO + bi * C::T_BYTES + 1024 * j));
-    };
-    dma(w, dmo0);
-    dma(w + 4, dmo1);
-    if (w == 0) dma(8, dmo2);
+  constexpr int kTileStages = 4;
+  struct TileRsrc {
+    __amdgpu_buffer_rsrc_t q, d;
+  };
+  auto tile_rsrc = [&](const Pos& ps) {
+    // bytes of the tile's rows inside the sequence (below 2^31: 128 rows of a tensor span less than 2^30)
+    const int n = imin(Lq - ps.tile * BM, BM) * rsqb;
+    return TileRsrc{__builtin_amdgcn_make_buffer_rsrc((char*)a.q + ps.off, (short)0, n, kRsrcWord3),
+                    __builtin_amdgcn_make_buffer_rsrc((char*)a.dout + ps.off, (short)0, n, kRsrcWord3)};
+  };
+  // untracked by the compiler: the step's first LDS reads of another buffer must not wait for it
+  // (wait_tiles and the step's barrier order it before buffer bi is read)
+  auto dma = [&](const TileRsrc& r, int bi, int j, int off) {
+    dma16_untracked(r.q, off, (__attribute__((address_space(3))) void*)(smem + C::OFF_Q + bi * C::T_BYTES + 1024 * j));
+    dma16_untracked(r.d, off, (__attribute__((address_space(3))) void*)(smem + C::OFF_DO + bi * C::T_BYTES + 1024 * j));
   };
   // row statistics of a step in MFMA row order, as the starting values of the S and dP accumulators:
-  // threads 0..31 store -lse2 / (scale log2 e), so that P = exp2(S_acc * scale * log2 e); threads
+  // lanes 0..31 of wave 0 store -lse2 / (scale log2 e), so that P = exp2(S_acc * scale * log2 e); lanes
   // 32..63 store -D, so that dS = P * dP_acc. Rows past the sequence get lse2 = +inf: their S starts at
-  // -inf and their P (and dS) is exactly 0.
-  auto load_stats = [&](Pos ps) -> float {
-    const int r = ps.tile * BM + tile_row(tid & 31);
-    if (tid >= 2 * BM) return 0.f;
-    if (r >= Lq) return tid < BM ? __builtin_inff() : 0.f;
-    const int64_t sidx = (int64_t)ps.head * a.total_q + q_start + r;
-    return (tid < BM ? a.lse2 : a.dvec)[sidx];
+  // -inf and their P (and dS) is exactly 0. The load reads a row inside the sequence (the last one for
+  // rows past it) and the store replaces what such rows read.
+  const float* const sbase = lane < BM ? a.lse2 : a.dvec;
+  const int srow_lane = tile_row(lane & 31);
+  auto load_stats = [&](const Pos& ps) -> float {
+    const int r = imin(ps.tile * BM + srow_lane, Lq - 1);
+    return sbase[ps.srow + r];
   };
   const float inv_sl2 = 1.f / a.scale_log2;
-  auto store_stats = [&](int bi, float v) {
-    if (tid < 2 * BM) s_st[bi * 2 * BM + tid] = tid < BM ? -(v * inv_sl2) : -v;
+  auto store_stats = [&](int bi, float v, const Pos& ps) {
+    if (w == 0) {
+      const bool in_seq = ps.tile * BM + srow_lane < Lq;
+      s_st[bi * 2 * BM + lane] = lane < BM ? (in_seq ? -(v * inv_sl2) : -__builtin_inff()) : (in_seq ? -v : -0.f);
+    }
+  };
+  // stage k of the transfers of step ps into buffer bi (and of its statistics into st)
+  auto issue_stage = [&](int k, const Pos& ps, int bi, TileRsrc& r, float& st) {
+    if (k == 0) r = tile_rsrc(ps);
+    if (k == 1) dma(r, bi, w, dmo0);
+    if (k == 2) dma(r, bi, w + 4, dmo1);
+    if (k == 3) {
+      if (w == 3) dma(r, bi, 8, dmo2);
+      if (w == 0) st = load_stats(ps);
+    }
+  };
+  auto issue_tile = [&](const Pos& ps, int bi, float& st) {
+    TileRsrc r;
+#pragma unroll
+    for (int k = 0; k < kTileStages; ++k) issue_stage(k, ps, bi, r, st);
   };
 
   // The dK, dV sums stay in the accumulator registers (AGPRs) for the whole kernel, and the S/dP
@@ -242,35 +271,16 @@ void fa_bwd_dkdv64(MainArgs a) {
   // its P is exactly 0. Element (a4, bb) of a lane is MFMA row 8 a4 + 4 hh + bb = tile row
   // hh + 2 (a4 % 2) + 4 bb + 16 (a4 / 2); key kv0 + 64 w + 32 n + c is visible from query row
   // i0 + r iff kv0 + 64 w + c - i0 - hh <= r - hh - 32 n, a constant right side per element.
-  auto gemm1 = [&](int qtile, int bi, f32x16 (&s)[2], f32x16 (&dp)[2], auto&& mid) {
+  auto gemm1 = [&](int qtile, int bi, f32x16 (&s)[2], f32x16 (&dp)[2], auto&& mid, auto&& pre) {
     constexpr int PF = C::PF_A;
     lds_bf16* sq = base(tq(bi) + arow);
     lds_bf16* sd = base(tdo(bi) + arow);
     const float* st = s_st + bi * 2 * BM;
-    f32x16 s_init[2], dp_init;
+    f32x4 l4[4], d4[4];
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
-      const f32x4 l4 = *(const f32x4*)(st + 8 * a4 + 4 * hh);
-      const f32x4 d4 = *(const f32x4*)(st + BM + 8 * a4 + 4 * hh);
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        s_init[0][4 * a4 + bb] = l4[bb];
-        dp_init[4 * a4 + bb] = d4[bb];
-      }
-    }
-    s_init[1] = s_init[0];
-    if (!full_step(qtile)) {
-      // opaque to the optimiser, so that the 32 comparisons stay against immediates inside the loop
-      // instead of becoming per-element values held across it
-      int t = kv0 + 64 * w + c - qtile * BM - hh;
-      asm volatile("" : "+v"(t));
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb)
-            if (t > 2 * (a4 & 1) + 4 * bb + 16 * (a4 >> 1) - 32 * n) s_init[n][4 * a4 + bb] = -__builtin_inff();
+      l4[a4] = *(const f32x4*)(st + 8 * a4 + 4 * hh);
+      d4[a4] = *(const f32x4*)(st + BM + 8 * a4 + 4 * hh);
     }
     bf16x8 qf[KS], df[KS], vf[KS][2], kf[KS][2];
     lds_bf16* s_kh = base(L + C::OFF_KH / 2 + (64 * w + c) * C::KHS + 8 * hh);
@@ -291,12 +301,36 @@ void fa_bwd_dkdv64(MainArgs a) {
 #pragma unroll
     for (int m = 0; m < PF; ++m) load_op(m);
     __builtin_amdgcn_sched_barrier(0);
+    pre();  // MFMAs that need none of these reads run while they are in flight
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s_init[2], dp_init;
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        s_init[0][4 * a4 + bb] = l4[a4][bb];
+        dp_init[4 * a4 + bb] = d4[a4][bb];
+      }
+    s_init[1] = s_init[0];
+    if (!full_step(qtile)) {
+      // opaque to the optimiser, so that the 32 comparisons stay against immediates inside the loop
+      // instead of becoming per-element values held across it
+      int t = kv0 + 64 * w + c - qtile * BM - hh;
+      asm volatile("" : "+v"(t));
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb)
+            if (t > 2 * (a4 & 1) + 4 * bb + 16 * (a4 >> 1) - 32 * n) s_init[n][4 * a4 + bb] = -__builtin_inff();
+    }
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
       load_op(m + PF);
-      if (m == C::MID_AT) {  // the next step's loads, issued in the shadow of the MFMAs
+      if (m >= C::MID_AT && m < C::MID_AT + kTileStages) {  // the next step's loads, in the MFMAs' shadow
         __builtin_amdgcn_sched_barrier(0);
-        mid();
+        mid(m - C::MID_AT);
         __builtin_amdgcn_sched_barrier(0);
       }
       const int ks = m >> 2, n = m & 1;
@@ -318,9 +352,13 @@ void fa_bwd_dkdv64(MainArgs a) {
   //  - softmax: key tile n = m / 16 first (tile 0's S and dP registers are free for the second half),
   //    element j = m % 16: P = exp2(S_acc * scale * log2 e), dS = P * dP_acc (the accumulators
   //    started from the statistics).
+  //  - beside a softmax (inside the loop), the last DEFER MFMAs are left to the next step, which issues
+  //    them after the barrier while its first LDS reads are in flight; their B fragments go to bfd.
+  constexpr int ND = C::DEFER, NDB = ND / 2 > 0 ? ND / 2 : 1;
+  static_assert(ND % 2 == 0 && ND <= 16, "deferred MFMAs come in key-tile pairs of the dK part");
   auto slots = [&](auto with_g2, auto with_sm, int bq, const f32x16 (&s)[2], const f32x16 (&dp)[2],
                    const bf16x8 (&pk0)[2][2], const bf16x8 (&dsk0)[2][2], bf16x8 (&pk1)[2][2],
-                   bf16x8 (&dsk1)[2][2]) {
+                   bf16x8 (&dsk1)[2][2], bf16x8 (&bfd)[NDB]) {
     constexpr bool G2 = decltype(with_g2)::value, SM = decltype(with_sm)::value;
     constexpr int PFB = C::PF_B;
     lds_bf16* sq = base(tq(bq) + brow);
@@ -373,10 +411,13 @@ void fa_bwd_dkdv64(MainArgs a) {
         const int i = m >> 1, n = m & 1, part = i >> 3, s2 = (i >> 2) & 1, nt = i & 3;
         // the last step (no softmax beside it) follows the loop's exit
         constexpr std::bool_constant<!SM> guarded{};
-        if (part == 0)
+        if (SM && m >= 32 - ND) {
+          if (n == 0) bfd[i - (16 - NDB)] = bf[i];
+        } else if (part == 0) {
           mfma_acc(guarded, accV[n][nt], pk0[n][s2], bf[i]);
-        else
+        } else {
           mfma_acc(guarded, accK[n][nt], dsk0[n][s2], bf[i]);
+        }
       }
       if constexpr (SM) {
         sm_scale(m + 2);
@@ -386,6 +427,16 @@ void fa_bwd_dkdv64(MainArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // the MFMAs a step left over (dK += dS^T Q of its last output tiles), from the dS registers dsk0
+  auto deferred = [&](auto guarded, const bf16x8 (&bfd)[NDB], const bf16x8 (&dsk0)[2][2]) {
+    if constexpr (ND > 0) {
+#pragma unroll
+      for (int m = 32 - ND; m < 32; ++m) {
+        const int i = m >> 1, n = m & 1, s2 = (i >> 2) & 1, nt = i & 3;
+        mfma_acc(guarded, accK[n][nt], dsk0[n][s2], bfd[i - (16 - NDB)]);
+      }
+    }
+  };
   auto wait_tiles = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -393,24 +444,27 @@ void fa_bwd_dkdv64(MainArgs a) {
   };
 
   f32x16 s[2], dp[2];
-  bf16x8 pk[2][2], dsk[2][2], pkn[2][2], dskn[2][2];
+  bf16x8 pk[2][2], dsk[2][2], pkn[2][2], dskn[2][2], bfd[NDB];
   if (n_steps > 0) {
     // prologue: tiles of steps 0 and 1 in flight; the first GEMMs and the softmax of step 0
     float st0 = 0.f, st1 = 0.f;
-    Pos cur = {qt0, hk * G};  // step 0
-    Pos nxt = advance(cur);   // step 1
-    issue_tile(cur, 0);
-    st0 = load_stats(cur);
-    if (n_steps > 1) {
-      issue_tile(nxt, 1);
-      st1 = load_stats(nxt);
-    }
+    Pos cur = {qt0, hk * G, head_off + (int64_t)hk * G * (D * 2), (int64_t)hk * G * a.total_q + q_start};  // step 0
+    Pos nxt = advance(cur);  // step 1
+    issue_tile(cur, 0, st0);
+    if (n_steps > 1) issue_tile(nxt, 1, st1);
     wait_tiles();
-    store_stats(0, st0);
-    store_stats(1, st1);
+    store_stats(0, st0, cur);
+    if (n_steps > 1) store_stats(1, st1, nxt);
     __syncthreads();
-    gemm1(cur.tile, 0, s, dp, [] {});
-    slots(std::false_type{}, std::true_type{}, 0, s, dp, pkn, dskn, pk, dsk);
+    gemm1(cur.tile, 0, s, dp, [](int) {}, [] {});
+    slots(std::false_type{}, std::true_type{}, 0, s, dp, pkn, dskn, pk, dsk, bfd);
+    // the first step's deferred MFMAs (it has none) add zero products
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) bfd[i] = bf16x8{};
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) dskn[n][e] = bf16x8{};
     // step sp: the tile of sp + 1 loads; the first GEMMs of sp, then the second GEMMs of sp - 1 beside
     // the softmax of sp
     int bq = 0, bp = 0, b1 = 1;  // buffers of steps sp - 1, sp, sp + 1 (rotating through NBUF)
@@ -423,14 +477,13 @@ void fa_bwd_dkdv64(MainArgs a) {
       b1 = b1 == C::NBUF - 1 ? 0 : b1 + 1;
       float st2 = 0.f;
       const bool has1 = sp + 1 < n_steps;
-      gemm1(cur.tile, bp, s, dp, [&] {
-        if (has1) {
-          issue_tile(nxt, b1);
-          st2 = load_stats(nxt);
-        }
-      });
-      slots(std::true_type{}, std::true_type{}, bq, s, dp, pko, dsko, pkw, dskw);
-      if (has1) store_stats(b1, st2);
+      TileRsrc rn;
+      // the previous step's deferred MFMAs read the dS registers this step's softmax rewrites
+      gemm1(cur.tile, bp, s, dp, [&](int k) {
+        if (has1) issue_stage(k, nxt, b1, rn, st2);
+      }, [&] { deferred(std::false_type{}, bfd, dskw); });
+      slots(std::true_type{}, std::true_type{}, bq, s, dp, pko, dsko, pkw, dskw, bfd);
+      if (has1) store_stats(b1, st2, nxt);
       wait_tiles();
       __syncthreads();
     };
@@ -440,18 +493,23 @@ void fa_bwd_dkdv64(MainArgs a) {
       step(sp, pk, dsk, pkn, dskn);
       step(sp + 1, pkn, dskn, pk, dsk);
     }
-    if (sp < n_steps) {
+    if (sp < n_steps) {  // then P, dS of the last step in pk, dsk and those of the step before in pkn, dskn
       step(sp, pk, dsk, pkn, dskn);
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
+          const bf16x8 tp = pk[n][e], td = dsk[n][e];
           pk[n][e] = pkn[n][e];
           dsk[n][e] = dskn[n][e];
+          pkn[n][e] = tp;
+          dskn[n][e] = td;
         }
     }
+    // the last step's deferred MFMAs (the step before it in dskn), after the loop's exit
+    deferred(std::true_type{}, bfd, dskn);
     // epilogue: the second GEMMs of the last step
-    slots(std::true_type{}, std::false_type{}, bp, s, dp, pk, dsk, pkn, dskn);
+    slots(std::true_type{}, std::false_type{}, bp, s, dp, pk, dsk, pkn, dskn, bfd);
   }
 
   // the last accumulating MFMA has written the sums before they are read (more than the 18 wait
