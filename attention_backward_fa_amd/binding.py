@@ -31,6 +31,7 @@ FA_BWD_ALGO_SPLIT_REDUCE = 3
 FA_BWD_ALGO_RECOMPUTE_DQ_8W = 4
 FA_BWD_ALGO_RECOMPUTE_DQ_4W = 5
 FA_BWD_ALGO_RECOMPUTE_DQ_64K = 6
+FA_BWD_ALGO_STORED_DS = 7
 
 FA_BWD_MASK_NONE = 0
 FA_BWD_MASK_PADDING = 1

@@ -12,6 +12,7 @@
 
 #include "fa_bwd.h"
 #include "fa_bwd_dkdv64.hpp"
+#include "fa_bwd_dqds.hpp"
 #include "fa_bwd_launch.hpp"
 
 struct fa_bwd_handle {
@@ -39,6 +40,10 @@ struct fa_bwd_handle {
   // the dQ and dK/dV kernels' dense grids in head-major order per XCD (head_major_balances), without
   // and with a causal bound
   bool dq_head_major[2], dkdv_head_major[2];
+  // stored-dS form: the 64-key dK/dV kernel writes dS blocks, the dQ pass reads them
+  bool ds_form;
+  fa::bf16* ds;
+  int32_t ds_nqs, ds_nkt;
 };
 
 namespace {
@@ -114,7 +119,7 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
     return FA_BWD_ERR_INVALID_ARGUMENT;
   const int32_t dv = d->head_dim_v == 0 ? d->head_dim : d->head_dim_v;
   if (!head_dim_ok(d->head_dim) || !head_dim_ok(dv)) return FA_BWD_ERR_UNSUPPORTED;
-  if (d->algorithm < FA_BWD_ALGO_DEFAULT || d->algorithm > FA_BWD_ALGO_RECOMPUTE_DQ_64K) return FA_BWD_ERR_INVALID_ARGUMENT;
+  if (d->algorithm < FA_BWD_ALGO_DEFAULT || d->algorithm > FA_BWD_ALGO_STORED_DS) return FA_BWD_ERR_INVALID_ARGUMENT;
   const bool single = d->algorithm == FA_BWD_ALGO_SINGLE_PASS || d->algorithm == FA_BWD_ALGO_SPLIT_REDUCE;
   // the single-pass kernels exist for equal head dims of 64 and 128
   if (single && (dv != d->head_dim || (d->head_dim != 64 && d->head_dim != 128))) return FA_BWD_ERR_UNSUPPORTED;
@@ -127,8 +132,9 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   // window bounds (kv0 + tile + window, i - window - kv0) then fit in 32 bits
   if (d->max_seqlen_q > (1 << 30) || d->max_seqlen_kv > (1 << 30)) return FA_BWD_ERR_INVALID_ARGUMENT;
   if (single && d->window > 0) return FA_BWD_ERR_UNSUPPORTED;
-  // the 64-key dK/dV layout exists for head dims of 128 without a window
-  if (d->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_64K && (d->head_dim != 128 || dv != 128 || d->window != 0))
+  // the 64-key dK/dV layout (and the stored-dS form built on it) exists for head dims of 128 without a window
+  if ((d->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_64K || d->algorithm == FA_BWD_ALGO_STORED_DS) &&
+      (d->head_dim != 128 || dv != 128 || d->window != 0))
     return FA_BWD_ERR_UNSUPPORTED;
   // index arithmetic stays in int64; grids must fit the launch limits
   const int64_t rows = (d->total_q > d->total_kv ? d->total_q : d->total_kv);
@@ -164,10 +170,34 @@ void launch_dkdv64(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
   using C = fa::Dkdv64Cfg;
   const int64_t blocks = (int64_t)((ma.max_seqlen_kv + C::BN - 1) / C::BN) * ma.Hk * ma.batch;
   const dim3 grid((unsigned)(ma.sched ? items : blocks)), block(C::NT);
-  if (ma.causal)
-    fa::fa_bwd_dkdv64<true><<<grid, block, 0, stream>>>(ma);
+  if (ma.ds)
+    ma.causal ? fa::fa_bwd_dkdv64<true, true><<<grid, block, 0, stream>>>(ma)
+              : fa::fa_bwd_dkdv64<false, true><<<grid, block, 0, stream>>>(ma);
   else
-    fa::fa_bwd_dkdv64<false><<<grid, block, 0, stream>>>(ma);
+    ma.causal ? fa::fa_bwd_dkdv64<true, false><<<grid, block, 0, stream>>>(ma)
+              : fa::fa_bwd_dkdv64<false, false><<<grid, block, 0, stream>>>(ma);
+}
+
+// the stored-dS form's dQ pass: one workgroup per (128-row q tile, head, sequence), as the dQ kernel
+void launch_dq_ds(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
+  using C = fa::DqDsCfg;
+  const int64_t blocks = (int64_t)((ma.max_seqlen_q + C::BQ - 1) / C::BQ) * ma.H * ma.batch;
+  const dim3 grid((unsigned)(ma.sched ? items : blocks)), block(C::NT);
+  if (ma.causal)
+    fa::fa_bwd_dq_ds<true><<<grid, block, 0, stream>>>(ma);
+  else
+    fa::fa_bwd_dq_ds<false><<<grid, block, 0, stream>>>(ma);
+}
+
+// The default takes the stored-dS form where its runs take the 64-key layout and the dS workspace stays
+// within this size (on a GPU with 288 GB of memory); above it, it keeps the recompute form.
+constexpr int64_t kDsDefaultMaxBytes = int64_t(8) << 30;
+
+// dS blocks of the stored-dS form: (32-row q steps) x (256-key kv tiles) per (sequence, query head)
+int64_t ds_blocks(const fa_bwd_desc& d, int32_t& nqs, int32_t& nkt) {
+  nqs = (d.max_seqlen_q + 31) / 32;
+  nkt = (d.max_seqlen_kv + 255) / 256;
+  return (int64_t)nqs * nkt * d.num_heads * d.batch;
 }
 
 // The kernels for the padded head dims: each dim rounded up to 64, 128, 192 or 256, and a dim of 64
@@ -317,6 +347,10 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.cu_q = cu_q;
   ma.cu_kv = cu_kv;
   ma.dq_acc = h->dq_acc;
+  const bool ds_run = h->ds_form && h->layout[causal] == 3;  // the stored-dS form on this run's layout
+  ma.ds = ds_run ? h->ds : nullptr;
+  ma.ds_nqs = h->ds_nqs;
+  ma.ds_nkt = h->ds_nkt;
   ma.dq = static_cast<bf16*>(dq);
   ma.dk = static_cast<bf16*>(dk);
   ma.dv = static_cast<bf16*>(dv);
@@ -361,7 +395,10 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   } else if (!planned || h->n_q_items > 0) {
     ma.sched = planned ? h->sched + 2 * h->n_kv_items : nullptr;
     ma.head_major = h->dq_head_major[causal] ? 1 : 0;
-    ks.dq(ma, h->n_q_items, stream);
+    if (ds_run)
+      launch_dq_ds(ma, h->n_q_items, stream);
+    else
+      ks.dq(ma, h->n_q_items, stream);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return FA_BWD_ERR_HIP;
@@ -484,7 +521,8 @@ int32_t dkdv_layout_code(int32_t algorithm) {
   switch (algorithm) {
     case FA_BWD_ALGO_RECOMPUTE_DQ_8W: return 1;
     case FA_BWD_ALGO_RECOMPUTE_DQ_4W: return 2;
-    case FA_BWD_ALGO_RECOMPUTE_DQ_64K: return 3;
+    case FA_BWD_ALGO_RECOMPUTE_DQ_64K:
+    case FA_BWD_ALGO_STORED_DS: return 3;
     default: return 0;
   }
 }
@@ -632,13 +670,20 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
     return FA_BWD_ERR_HIP;
   }
   configure_layouts(h, cus);
+  const int64_t ds_need = ds_blocks(h->desc, h->ds_nqs, h->ds_nkt) * 256 * 32 * 2;
+  h->ds_form = desc->algorithm == FA_BWD_ALGO_STORED_DS ||
+               (desc->algorithm == FA_BWD_ALGO_DEFAULT && (h->layout[0] == 3 || h->layout[1] == 3) &&
+                ds_need <= kDsDefaultMaxBytes);
+  const size_t ds_bytes = h->ds_form ? (size_t)ds_need : 0;
   const size_t stats = (size_t)desc->total_q * desc->num_heads;
   const size_t acc = stats * desc->head_dim * (h->split ? fa::kSplits : 1);
   if ((h->single_pass && hipMalloc(&h->dq_acc, acc * sizeof(float)) != hipSuccess) ||
+      (h->ds_form && hipMalloc(&h->ds, ds_bytes) != hipSuccess) ||
       hipMalloc(&h->lse2, stats * sizeof(float)) != hipSuccess ||
       hipMalloc(&h->dvec, stats * sizeof(float)) != hipSuccess) {
     (void)hipGetLastError();
     if (h->dq_acc) (void)hipFree(h->dq_acc);
+    if (h->ds) (void)hipFree(h->ds);
     if (h->lse2) (void)hipFree(h->lse2);
     if (h->dvec) (void)hipFree(h->dvec);
     delete h;
@@ -670,8 +715,9 @@ fa_bwd_status fa_bwd_run_noalloc(const fa_bwd_desc* desc, const void* q, const v
                                  int32_t mask, void* dq, void* dk, void* dv, void* stream) {
   const fa_bwd_status ds = check_desc(desc);
   if (ds != FA_BWD_OK) return ds;
-  if (desc->algorithm == FA_BWD_ALGO_SINGLE_PASS || desc->algorithm == FA_BWD_ALGO_SPLIT_REDUCE)
-    return FA_BWD_ERR_UNSUPPORTED;  // their dQ workspace is not part of the fixed scratch
+  if (desc->algorithm == FA_BWD_ALGO_SINGLE_PASS || desc->algorithm == FA_BWD_ALGO_SPLIT_REDUCE ||
+      desc->algorithm == FA_BWD_ALGO_STORED_DS)
+    return FA_BWD_ERR_UNSUPPORTED;  // their dQ (or dS) workspace is not part of the fixed scratch
   if (desc->total_q > kNoAllocMaxRows / desc->num_heads) return FA_BWD_ERR_SCRATCH_LIMIT;
   if (!l) return FA_BWD_ERR_INVALID_ARGUMENT;
   const fa_bwd_status ps = check_pointers(q, k, v, o, dout, m, l, cu_seqlens_q, cu_seqlens_kv, dq, dk, dv);
@@ -755,6 +801,7 @@ fa_bwd_status fa_bwd_destroy(fa_bwd_handle* h) {
   if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(h->device) != hipSuccess) st = FA_BWD_ERR_HIP;
   if (hipDeviceSynchronize() != hipSuccess) st = FA_BWD_ERR_HIP;
   if (h->dq_acc && hipFree(h->dq_acc) != hipSuccess) st = FA_BWD_ERR_HIP;
+  if (h->ds && hipFree(h->ds) != hipSuccess) st = FA_BWD_ERR_HIP;
   if (hipFree(h->lse2) != hipSuccess) st = FA_BWD_ERR_HIP;
   if (hipFree(h->dvec) != hipSuccess) st = FA_BWD_ERR_HIP;
   drop_plan(h);
@@ -783,6 +830,7 @@ int32_t fa_bwd_dkdv_layout(const fa_bwd_handle* h, int32_t mask) {
   if (h->single_pass) return h->split ? FA_BWD_ALGO_SPLIT_REDUCE : FA_BWD_ALGO_SINGLE_PASS;
   if (!pick_kernels(h->desc.head_dim, h->desc.head_dim_v).two_layouts) return FA_BWD_ALGO_RECOMPUTE_DQ;
   const bool causal = mask == FA_BWD_MASK_CAUSAL || mask == FA_BWD_MASK_PADDING_CAUSAL;
+  if (h->ds_form && h->layout[causal] == 3) return FA_BWD_ALGO_STORED_DS;
   switch (h->layout[causal]) {
     case 3: return FA_BWD_ALGO_RECOMPUTE_DQ_64K;
     case 2: return FA_BWD_ALGO_RECOMPUTE_DQ_4W;

@@ -61,7 +61,9 @@ struct Dkdv64Cfg {
   static_assert(OFF_V <= 65536, "step buffers within the immediate-offset reach");
 };
 
-template <bool CAUSAL>
+// DS: also store each step's dS (bf16) as one 16 KB block of the stored-dS form (fa_bwd_dqds.hpp), in the
+// order the lanes hold the values: wave w's piece 2 n + s2 (1 KB) holds lane l's 16 bytes at 16 l.
+template <bool CAUSAL, bool DS>
 __global__ __attribute__((amdgpu_flat_work_group_size(Dkdv64Cfg::NT, Dkdv64Cfg::NT), amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_dkdv64(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -116,19 +118,23 @@ void fa_bwd_dkdv64(MainArgs a) {
   const int nq = n_qt > qt0 ? n_qt - qt0 : 0;
   const int n_steps = G * nq;
   // a step's position: q tile and query head, the byte offset of its Q (and dO) rows from the tensors'
-  // bases and the index of its head's first statistic; advanced one step at a time with additions
+  // bases, the index of its head's first statistic and (storing dS) the element offset of its dS block;
+  // advanced one step at a time with additions
   struct Pos {
     int tile, head;
-    int64_t off, srow;
+    int64_t off, srow, ds;
   };
   const int64_t head_off = (int64_t)(q_start + qt0 * BM) * rsqb;  // of the first step of a head, less the head
+  constexpr int64_t DS_BLOCK = 256 * 32;
   auto advance = [&](Pos p) {
     p.off += BM * rsqb;
+    p.ds += DS_BLOCK;
     if (++p.tile == qt0 + nq) {
       p.tile = qt0;
       ++p.head;
       p.off = head_off + (int64_t)p.head * (D * 2);
       p.srow += a.total_q;
+      p.ds += ((int64_t)a.ds_nkt * a.ds_nqs - nq) * DS_BLOCK;  // the next head's block of this kv tile
     }
     return p;
   };
@@ -199,6 +205,15 @@ void fa_bwd_dkdv64(MainArgs a) {
     if (w == 0) {
       const bool in_seq = ps.tile * BM + srow_lane < Lq;
       s_st[bi * 2 * BM + lane] = lane < BM ? (in_seq ? -(v * inv_sl2) : -__builtin_inff()) : (in_seq ? -v : -0.f);
+    }
+  };
+  // piece e = 2 n + s2 of this wave's part of a step's dS block: this lane's 16 bytes (key 64 w + 32 n + c,
+  // positions 16 hh + 8 s2 ..+7), non-temporal: the blocks are read once, by the dQ pass
+  auto store_ds = [&](const Pos& ps, const bf16x8 (&d)[2][2], int e) {
+    if constexpr (DS) {
+      if (ps.tile >= a.ds_nqs || tile >= a.ds_nkt) return;  // outside the workspace (lengths past the maxima)
+      const int n = e >> 1, s2 = e & 1;
+      __builtin_nontemporal_store(d[n][s2], (bf16x8*)(a.ds + ps.ds + (w * 4 + e) * 512 + lane * 8));
     }
   };
   // stage k of the transfers of step ps into buffer bi (and of its statistics into st)
@@ -328,7 +343,9 @@ void fa_bwd_dkdv64(MainArgs a) {
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
       load_op(m + PF);
-      if (m >= C::MID_AT && m < C::MID_AT + kTileStages) {  // the next step's loads, in the MFMAs' shadow
+      // the next step's loads (and, storing dS, the previous step's four dS pieces first), in the MFMAs'
+      // shadow
+      if (m >= C::MID_AT - (DS ? 4 : 0) && m < C::MID_AT + kTileStages) {
         __builtin_amdgcn_sched_barrier(0);
         mid(m - C::MID_AT);
         __builtin_amdgcn_sched_barrier(0);
@@ -448,7 +465,8 @@ void fa_bwd_dkdv64(MainArgs a) {
   if (n_steps > 0) {
     // prologue: tiles of steps 0 and 1 in flight; the first GEMMs and the softmax of step 0
     float st0 = 0.f, st1 = 0.f;
-    Pos cur = {qt0, hk * G, head_off + (int64_t)hk * G * (D * 2), (int64_t)hk * G * a.total_q + q_start};  // step 0
+    Pos cur = {qt0, hk * G, head_off + (int64_t)hk * G * (D * 2), (int64_t)hk * G * a.total_q + q_start,
+               DS ? (((int64_t)(b * a.H + hk * G) * a.ds_nkt + tile) * a.ds_nqs + qt0) * DS_BLOCK : 0};  // step 0
     Pos nxt = advance(cur);  // step 1
     issue_tile(cur, 0, st0);
     if (n_steps > 1) issue_tile(nxt, 1, st1);
@@ -470,6 +488,7 @@ void fa_bwd_dkdv64(MainArgs a) {
     int bq = 0, bp = 0, b1 = 1;  // buffers of steps sp - 1, sp, sp + 1 (rotating through NBUF)
     auto step = [&](int sp, const bf16x8 (&pko)[2][2], const bf16x8 (&dsko)[2][2], bf16x8 (&pkw)[2][2],
                     bf16x8 (&dskw)[2][2]) {
+      const Pos prv = cur;
       cur = nxt;
       nxt = advance(cur);
       bq = bp;
@@ -480,7 +499,10 @@ void fa_bwd_dkdv64(MainArgs a) {
       TileRsrc rn;
       // the previous step's deferred MFMAs read the dS registers this step's softmax rewrites
       gemm1(cur.tile, bp, s, dp, [&](int k) {
-        if (has1) issue_stage(k, nxt, b1, rn, st2);
+        if (k < 0)
+          store_ds(prv, dsko, k + 4);
+        else if (has1)
+          issue_stage(k, nxt, b1, rn, st2);
       }, [&] { deferred(std::false_type{}, bfd, dskw); });
       slots(std::true_type{}, std::true_type{}, bq, s, dp, pko, dsko, pkw, dskw, bfd);
       if (has1) store_stats(b1, st2, nxt);
@@ -508,6 +530,8 @@ void fa_bwd_dkdv64(MainArgs a) {
     }
     // the last step's deferred MFMAs (the step before it in dskn), after the loop's exit
     deferred(std::true_type{}, bfd, dskn);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_ds(cur, dsk, e);  // the last step's dS
     // epilogue: the second GEMMs of the last step
     slots(std::true_type{}, std::false_type{}, bp, s, dp, pk, dsk, pkn, dskn, bfd);
   }

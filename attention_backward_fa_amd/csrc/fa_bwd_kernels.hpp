@@ -237,6 +237,8 @@ struct MainArgs {
   const int* sched;  // recompute kernels: (tile, sequence * heads + head) per workgroup, or null (dense grid)
   int head_major;    // recompute kernels, dense grid, (K/V) heads x sequences a multiple of 8: each XCD
                      // takes the tiles of one (sequence, head) at a time
+  bf16* ds;          // stored-dS form: dS blocks of 32 q rows x 256 keys, [sequence][head][ds_nqs][ds_nkt]
+  int ds_nqs, ds_nkt;  // 32-row q steps and 256-key kv tiles of the longest sequences
 };
 
 // Splits of the split-and-reduce form: workgroups per (head, sequence), each with its own fp32 dQ
@@ -1098,17 +1100,15 @@ struct KvTileLoader {
 #pragma unroll
     for (int jj = 0; jj < NJV; ++jj) offv[jj] = tile_dma_off(w + C::NW * jj, lane, C::CPRV, rskvb, dvd);
   }
+  // untracked transfers (dma16_untracked): the step's LDS reads of the other buffer must not wait for
+  // them; the end-of-step wait and barrier order them before their buffer is read
   __device__ __forceinline__ void issue(char* smem, int w, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
                                         int bi) const {
     auto dma_k = [&](int jj, int j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void*)(smem + C::OFF_K + bi * C::TK_BYTES + 1024 * j), 16,
-          offk[jj], 0, 0, 0);
+      dma16_untracked(rk, offk[jj], (__attribute__((address_space(3))) void*)(smem + C::OFF_K + bi * C::TK_BYTES + 1024 * j));
     };
     auto dma_v = [&](int jj, int j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void*)(smem + C::OFF_V + bi * C::TV_BYTES + 1024 * j), 16,
-          offv[jj], 0, 0, 0);
+      dma16_untracked(rv, offv[jj], (__attribute__((address_space(3))) void*)(smem + C::OFF_V + bi * C::TV_BYTES + 1024 * j));
     };
 #pragma unroll
     for (int jj = 0; jj < (NJK > NJV ? NJK : NJV); ++jj) {

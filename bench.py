@@ -4,8 +4,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal]
 
 One step = one ``fa_bwd_run`` over the whole workload, inputs already
-resident in HBM: the row preprocess, then (default, recompute form) the dK/dV
-kernel and the dQ kernel, or (``--algorithm single-pass``) the single-pass
+resident in HBM: the row preprocess, then (default) the dK/dV kernel with 64
+keys per wave, which also writes dS, and the dQ = dS K pass (the stored-dS form,
+where the workload takes the 64-key layout and its dS workspace fits 8 GiB; else
+the recompute form: the dK/dV kernel and the dQ kernel that recomputes S and
+dP), or (``--algorithm single-pass``) the single-pass
 main kernel with dQ atomics and the dQ cast, or (``--algorithm split-reduce``)
 the single-pass main kernel over 8 kv-tile splits with a fixed-order dQ sum. The default workload is
 the causal one: batch 1, 32 heads, 8192 tokens, head_dim 128. Throughput is
@@ -59,19 +62,21 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 BF16_FLOP_PER_CLK_PER_CU = 4096  # 4 SIMDs, each one 32x32x16 bf16 MFMA (32768 FLOPs) per 32 clocks
 MASK_NAMES = {0: "none", 1: "padding", 2: "causal", 3: "padding_causal"}
 ALGORITHMS = {"default": 0, "single-pass": 1, "recompute": 2, "split-reduce": 3, "recompute-8w": 4, "recompute-4w": 5,
-              "recompute-64k": 6}
+              "recompute-64k": 6, "stored-ds": 7}
 ALGORITHM_NAMES = {1: "single-pass (dQ atomics)",
                    2: "recompute (dK/dV kernel + dQ kernel; dK/dV layout chosen by load balance)",
                    3: "split-reduce (single-pass main kernel over 8 kv-tile splits + fixed-order dQ sum)",
                    4: "recompute (dK/dV kernel in eight-wave workgroups + dQ kernel)",
                    5: "recompute (dK/dV kernel in four-wave workgroups + dQ kernel)",
-                   6: "recompute (dK/dV kernel with 64 keys per wave + dQ kernel)"}
+                   6: "recompute (dK/dV kernel with 64 keys per wave + dQ kernel)",
+                   7: "stored dS (dK/dV kernel with 64 keys per wave writes dS; dQ = dS K pass)"}
 # the dK/dV layout a handle takes (fa_bwd_dkdv_layout's algorithm codes)
 LAYOUT_NAMES = {1: "none (single-pass form)", 3: "none (single-pass form)",
                 2: "one layout (heads wider than 128)",
                 4: "eight-wave workgroups, 32 keys per wave",
                 5: "four-wave workgroups (two per CU), 32 keys per wave",
-                6: "one four-wave workgroup per CU, 64 keys per wave"}
+                6: "one four-wave workgroup per CU, 64 keys per wave",
+                7: "one four-wave workgroup per CU, 64 keys per wave, dS stored"}
 
 
 def kernel_share(algorithm: int, d: int, dv: int, layout: int = 0) -> dict:
@@ -83,6 +88,8 @@ def kernel_share(algorithm: int, d: int, dv: int, layout: int = 0) -> dict:
         return {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_dq_cast": 0.0}
     if algorithm == 3:
         return {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_split_reduce": 0.0}
+    if algorithm == 7:  # dK/dV kernel: S, dP, dV, dK (and dS stored); the dS pass: dQ
+        return {"fa_bwd_pre": 0.0, "fa_bwd_dkdv64": (2 * d + 2 * dv) / total, "fa_bwd_dq_ds": d / total}
     # dK/dV kernel: S, dP, dV, dK; dQ kernel: S and dP again, dQ
     dkdv = "fa_bwd_dkdv64" if layout == 6 else "fa_bwd_dkdv"
     return {"fa_bwd_pre": 0.0, dkdv: (2 * d + 2 * dv) / total, "fa_bwd_dq": (2 * d + dv) / total}
@@ -472,8 +479,8 @@ def main():
     algo = ALGORITHMS[args.algorithm]
     op = binding.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0],
                        algo, num_heads_kv=inp["k"].shape[1], window=inp["window"], head_dim_v=inp["v"].shape[2])
-    algo_used = 2 if algo == 0 else algo
-    layout = op.dkdv_layout(inp["mask"])  # the dK/dV layout the recompute form takes on this workload
+    layout = op.dkdv_layout(inp["mask"])  # the dK/dV layout (or the stored-dS form) this workload takes
+    algo_used = (7 if layout == 7 else 2) if algo == 0 else algo
     if args.plan:  # host-side longest-first schedule from the (host) sequence offsets
         op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
     dq, dk, dv = (torch.empty_like(dev[x]) for x in ("q", "k", "v"))

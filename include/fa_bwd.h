@@ -60,7 +60,9 @@ typedef enum {
 /* How dQ is formed. All forms compute the same per-tile math (steps 1-8) and
  * agree within the fp32 rounding of the accumulation order. */
 typedef enum {
-  FA_BWD_ALGO_DEFAULT = 0,      /* the faster form on this GPU: FA_BWD_ALGO_RECOMPUTE_DQ */
+  FA_BWD_ALGO_DEFAULT = 0,      /* the faster form on this GPU: FA_BWD_ALGO_STORED_DS where runs take the
+                                   64-key layout (head dims of 128, no window, grids that balance) and its
+                                   dS workspace is at most 8 GiB, else FA_BWD_ALGO_RECOMPUTE_DQ */
   FA_BWD_ALGO_SINGLE_PASS = 1,  /* the article's single-pass structure: one main kernel forms the dK, dV and
                                    dQ contributions of every (q tile, kv tile) pair; dQ partial sums are
                                    added to an fp32 workspace with global atomics (summation order not
@@ -86,10 +88,17 @@ typedef enum {
                                    keys. Both layouts give the same results within fp32 rounding (the
                                    order of the dK, dV sums differs); for head dims above 128 both
                                    codes run the one wide-head layout */
-  FA_BWD_ALGO_RECOMPUTE_DQ_64K = 6 /* FA_BWD_ALGO_RECOMPUTE_DQ with the 64-key layout of the kv-outer
+  FA_BWD_ALGO_RECOMPUTE_DQ_64K = 6, /* FA_BWD_ALGO_RECOMPUTE_DQ with the 64-key layout of the kv-outer
                                    kernel: one four-wave workgroup per compute unit over 256 keys, each
                                    wave holding 64 keys and their dK, dV sums, 32-row q steps; head
                                    dims of exactly 128 and no window (else FA_BWD_ERR_UNSUPPORTED) */
+  FA_BWD_ALGO_STORED_DS = 7        /* the 64-key kv-outer kernel also writes dS (bf16) to a workspace, and
+                                   dQ = scale * dS K (SK-16 article, section 3.1, step 8) runs as a
+                                   q-outer pass over it instead of forming S and dP a second time.
+                                   Workspace: batch * num_heads * ceil(max_seqlen_q / 32) *
+                                   ceil(max_seqlen_kv / 256) blocks of 16 KiB. Deterministic (every
+                                   output row has one owner); same restrictions as
+                                   FA_BWD_ALGO_RECOMPUTE_DQ_64K */
 } fa_bwd_algo;
 
 typedef enum {
@@ -131,7 +140,8 @@ typedef struct {
 /* Validates desc (a num_heads_kv of 0 is stored as num_heads) and allocates
  * the device workspace of the handle on the current HIP device: two fp32 [H][total_q] row-statistic arrays and, for
  * FA_BWD_ALGO_SINGLE_PASS only, an fp32 dQ accumulator of total_q*H*head_dim
- * floats (8 of them for FA_BWD_ALGO_SPLIT_REDUCE). For FA_BWD_ALGO_DEFAULT and
+ * floats (8 of them for FA_BWD_ALGO_SPLIT_REDUCE), and for the stored-dS form (FA_BWD_ALGO_STORED_DS,
+ * or FA_BWD_ALGO_DEFAULT where it takes that form) its dS workspace. For FA_BWD_ALGO_DEFAULT and
  * FA_BWD_ALGO_RECOMPUTE_DQ it also fixes the kv-outer kernel's layout for runs
  * without and with a causal bound, from the descriptor (every sequence taken at
  * the maximum lengths) and the device's compute-unit count; planned runs use the
@@ -175,8 +185,10 @@ fa_bwd_status fa_bwd_run_lse(fa_bwd_handle* h, const void* q, const void* k, con
 
 /* For callers that cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc. The backward of fa_bwd_run for the recompute form
- * (FA_BWD_ALGO_DEFAULT, _RECOMPUTE_DQ, _RECOMPUTE_DQ_8W, _RECOMPUTE_DQ_4W: the same kernels, the
- * same layout rule and bitwise the same results as a handle created from `desc`), without a handle
+ * (FA_BWD_ALGO_RECOMPUTE_DQ, _RECOMPUTE_DQ_8W, _RECOMPUTE_DQ_4W, _RECOMPUTE_DQ_64K: the same kernels,
+ * the same layout rule and bitwise the same results as a handle created from `desc`; with
+ * FA_BWD_ALGO_DEFAULT, those of a handle created with FA_BWD_ALGO_RECOMPUTE_DQ, since the stored-dS
+ * form the default may take needs its dS workspace), without a handle
  * and without any allocation: the two fp32 [H][total_q] row-statistic arrays live in a fixed
  * device array of the library, 32 MiB, which every GPU the library runs on holds until the process
  * ends. The caller passes the descriptor and every input and output, with the meanings, layouts,
@@ -184,8 +196,8 @@ fa_bwd_status fa_bwd_run_lse(fa_bwd_handle* h, const void* q, const void* k, con
  * profiling). The first call on a device looks up that device's copy of the array (the caller
  * makes the device of `stream` current, as for any HIP call); no call allocates or frees memory.
  *   FA_BWD_ERR_SCRATCH_LIMIT: total_q * num_heads > FA_BWD_NOALLOC_MAX_ROWS (nothing enqueued).
- *   FA_BWD_ERR_UNSUPPORTED: the single-pass and split-reduce forms (their dQ workspace is not part
- *     of the fixed array).
+ *   FA_BWD_ERR_UNSUPPORTED: the single-pass, split-reduce and stored-dS forms (their dQ or dS
+ *     workspace is not part of the fixed array).
  * All calls on one GPU share its array: calls that can overlap in time on one GPU (two streams,
  * or a graph replayed beside a direct call) race on it and give wrong gradients. Each call rewrites
  * every row statistic it reads, so the array needs no clearing between calls. */
@@ -249,7 +261,9 @@ const fa_bwd_desc* fa_bwd_get_desc(const fa_bwd_handle* h);
  * from the descriptor and the device's compute-unit count:
  * FA_BWD_ALGO_RECOMPUTE_DQ_8W, FA_BWD_ALGO_RECOMPUTE_DQ_4W or
  * FA_BWD_ALGO_RECOMPUTE_DQ_64K for head dims up to 128, and
- * FA_BWD_ALGO_RECOMPUTE_DQ for wider heads (whose kernels have one layout).
+ * FA_BWD_ALGO_RECOMPUTE_DQ for wider heads (whose kernels have one layout);
+ * FA_BWD_ALGO_STORED_DS where the run takes the stored-dS form (the 64-key layout
+ * writing dS, and the dQ pass over it).
  * Returns FA_BWD_ALGO_SINGLE_PASS or FA_BWD_ALGO_SPLIT_REDUCE for handles of
  * those forms, and -1 for a NULL handle or an invalid mask. Host only; does
  * not touch the device. */

@@ -82,10 +82,12 @@ def _create(**kw):
     (dict(head_dim=64, head_dim_v=128, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(num_heads=4, num_heads_kv=1, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(window=32, algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
-    (dict(algorithm=7), B.FA_BWD_ERR_INVALID_ARGUMENT),
+    (dict(algorithm=8), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(algorithm=6, head_dim=64), B.FA_BWD_ERR_UNSUPPORTED),                 # 64-key layout: d = 128,
     (dict(algorithm=6, head_dim_v=64), B.FA_BWD_ERR_UNSUPPORTED),               # no window
     (dict(algorithm=6, window=16), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(algorithm=7, head_dim=64), B.FA_BWD_ERR_UNSUPPORTED),                 # stored dS: the same
+    (dict(algorithm=7, window=16), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(algorithm=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(total_q=1 << 40, num_heads=8), B.FA_BWD_ERR_INVALID_ARGUMENT),          # index range
     (dict(max_seqlen_kv=1 << 30, num_heads=1 << 10, batch=1 << 10), B.FA_BWD_ERR_INVALID_ARGUMENT),  # grid size
@@ -141,6 +143,7 @@ def _noalloc(desc, ptr=256, l=True):
     (dict(num_heads=64, total_q=(1 << 16) + 1), B.FA_BWD_ERR_SCRATCH_LIMIT),
     (dict(algorithm=1), B.FA_BWD_ERR_UNSUPPORTED),       # single-pass and split-reduce need a dQ workspace
     (dict(algorithm=3), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(algorithm=7), B.FA_BWD_ERR_UNSUPPORTED),       # the stored-dS form needs a dS workspace
     (dict(batch=0), B.FA_BWD_ERR_INVALID_ARGUMENT),      # the descriptor checks of fa_bwd_create
     (dict(head_dim=100), B.FA_BWD_ERR_UNSUPPORTED),
 ])

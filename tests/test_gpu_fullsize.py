@@ -31,7 +31,8 @@ pytestmark = pytest.mark.gpu
 FULL = ["dense", "varlen", "causal", "longpad"]
 ALGOS = {"default": B.FA_BWD_ALGO_DEFAULT, "eightwave": B.FA_BWD_ALGO_RECOMPUTE_DQ_8W,
          "fourwave": B.FA_BWD_ALGO_RECOMPUTE_DQ_4W, "keys64": B.FA_BWD_ALGO_RECOMPUTE_DQ_64K,
-         "singlepass": B.FA_BWD_ALGO_SINGLE_PASS, "splitreduce": B.FA_BWD_ALGO_SPLIT_REDUCE}
+         "singlepass": B.FA_BWD_ALGO_SINGLE_PASS, "splitreduce": B.FA_BWD_ALGO_SPLIT_REDUCE,
+         "storedds": B.FA_BWD_ALGO_STORED_DS}
 # the workloads with grouped K/V heads, a window or other head dims run the recompute form only
 VARIANTS = ["causal_gqa", "causal_window", "causal_d256", "causal_mla"]
 # (workload, algorithm): every algorithm of a workload runs while its reference is held, then the

@@ -41,12 +41,14 @@ CASES = [
 
 ALGOS = {"recompute": B.FA_BWD_ALGO_RECOMPUTE_DQ, "recompute8w": B.FA_BWD_ALGO_RECOMPUTE_DQ_8W,
          "recompute4w": B.FA_BWD_ALGO_RECOMPUTE_DQ_4W, "singlepass": B.FA_BWD_ALGO_SINGLE_PASS,
-         "splitreduce": B.FA_BWD_ALGO_SPLIT_REDUCE, "recompute64k": B.FA_BWD_ALGO_RECOMPUTE_DQ_64K}
+         "splitreduce": B.FA_BWD_ALGO_SPLIT_REDUCE, "recompute64k": B.FA_BWD_ALGO_RECOMPUTE_DQ_64K,
+         "storedds": B.FA_BWD_ALGO_STORED_DS}
 
 
 def _supported(case, algo):
-    # the 64-key dK/dV layout exists for head dims of 128 without a window
-    return algo != "recompute64k" or (case.head_dim == 128 and case.head_dim_v in (0, 128) and case.window == 0)
+    # the 64-key dK/dV layout (and the stored-dS form on it) exists for head dims of 128 without a window
+    return algo not in ("recompute64k", "storedds") or (case.head_dim == 128 and case.head_dim_v in (0, 128)
+                                                        and case.window == 0)
 
 
 # (case, algorithm) pairs, case-major so that each case's oracle reference is computed once
@@ -114,6 +116,26 @@ def test_recompute_is_bitwise_reproducible(layout):
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("case", [I.custom_case("storedds_causal", 3, 128, I.MASK_CAUSAL, 216, [700, 333, 64, 1]),
+                                  I.custom_case("storedds_padded", 2, 128, I.MASK_PADDING_CAUSAL, 217, [300, 131],
+                                                padded_len=320),
+                                  I.custom_case("storedds_kv_longer", 2, 128, I.MASK_NONE, 218, [100, 250],
+                                                [600, 64])], ids=lambda c: c.name)
+def test_stored_ds_matches_recompute(case):
+    """The stored-dS form runs the 64-key dK/dV kernel with dS stores added: its dK, dV equal the 64-key
+    recompute form's bitwise; its dQ sums the same bf16 dS values in another kernel, so it agrees within
+    the tolerance. Repeated runs are bitwise identical (every output row has one owner)."""
+    inp = I.make(case)
+    o, m, l = P.oracle_stats(inp)
+    a = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_RECOMPUTE_DQ_64K)
+    b = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_STORED_DS)
+    c = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_STORED_DS)
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]), "dk, dv differ from the 64-key recompute form"
+    P.assert_close("dq", b[0].numpy(), a[0].numpy().astype(np.float64))
+    for x, y in zip(b, c):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("case", [I.custom_case("layouts_causal", 3, 128, I.MASK_CAUSAL, 211, [700, 333, 64]),
                                   I.custom_case("layouts_padded", 2, 64, I.MASK_PADDING, 212, [250, 97],
                                                 padded_len=256)], ids=lambda c: c.name)
@@ -138,8 +160,9 @@ def test_dkdv_layouts_agree(case):
     # 2 * 64 * 256 > 8192; 128-key tiles: 256 workgroups of 32 steps, 2 * 32 * 256 > 8192: eight waves
     (I.custom_case("layout_rule_8w", 8, 128, I.MASK_NONE, 214, [2048, 2048]), B.FA_BWD_ALGO_RECOMPUTE_DQ_8W),
     # causal, d 128, 256 heads of 1024 tokens: 256-key tiles of 32, 24, 16 and 8 steps total 80 per
-    # head, 20480 in all, and 2 * 32 * 256 = 16384 <= 20480: the 64-key layout
-    (I.custom_case("layout_rule_64k", 256, 128, I.MASK_CAUSAL, 215, [1024]), B.FA_BWD_ALGO_RECOMPUTE_DQ_64K),
+    # head, 20480 in all, and 2 * 32 * 256 = 16384 <= 20480: the 64-key layout, and with it the stored-dS
+    # form (its dS workspace: 256 heads x 32 q steps x 4 kv tiles x 16 KiB = 512 MiB, within 8 GiB)
+    (I.custom_case("layout_rule_64k", 256, 128, I.MASK_CAUSAL, 215, [1024]), B.FA_BWD_ALGO_STORED_DS),
     # causal, d 128, 64 query heads over 16 K/V heads of 2048 tokens: each workgroup runs the steps of 4
     # query heads; 256-key tiles: 288 steps per head, 18432 in all, largest workgroup 4 * 64, and
     # 2 * 256 * 256 > 18432; 128-key tiles: 17408 in all, largest 4 * 32, 2 * 128 * 256 > 17408: eight waves
@@ -223,7 +246,7 @@ GQA_CASES = [
 
 
 # the default form, and the 64-key dK/dV layout (whose workgroups run every query head of a K/V head)
-GQA_PAIRS = [(c, a) for c in GQA_CASES for a in ("recompute", "recompute64k") if _supported(c, a)]
+GQA_PAIRS = [(c, a) for c in GQA_CASES for a in ("recompute", "recompute64k", "storedds") if _supported(c, a)]
 
 
 @pytest.mark.parametrize("case,algo", GQA_PAIRS, ids=[f"{c.name}-{a}" for c, a in GQA_PAIRS])

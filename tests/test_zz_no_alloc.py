@@ -3,9 +3,11 @@
 Two calls in a row through the C ABI, the second on a smaller problem (fewer
 rows x heads, another head dim, a padded mask), so that it runs on the fixed
 scratch array the first call left filled. Each call's dQ, dK, dV must equal
-bitwise those of a handle created from the same descriptor (the same kernels
-and layout rule), lie within the per-tensor tolerance of the fp64 oracle, and
-the output buffers (filled with NaN beforehand) must be fully written.
+bitwise those of a handle of the recompute form created from the same sizes
+(the same kernels and layout rule; the default's stored-dS form needs a dS
+workspace, so the allocation-free default is the recompute form), lie within
+the per-tensor tolerance of the fp64 oracle, and the output buffers (filled
+with NaN beforehand) must be fully written.
 """
 import numpy as np
 import pytest
@@ -40,7 +42,7 @@ def test_noalloc_equals_fa_bwd_run_on_two_calls_the_second_smaller():
         od, md, ld = o.to(dev), m.to(dev), l.to(dev)
         desc = _desc(inp, B.FA_BWD_ALGO_DEFAULT)
         with B.FaBwd(inp["batch"], case.heads, case.head_dim, inp["max_seqlen_q"], inp["max_seqlen_kv"],
-                     inp["q"].shape[0], inp["k"].shape[0]) as op:
+                     inp["q"].shape[0], inp["k"].shape[0], B.FA_BWD_ALGO_RECOMPUTE_DQ) as op:
             want = op.run(t["q"], t["k"], t["v"], od, t["do"], md, ld, t["cu_q"], t["cu_kv"], inp["scale"],
                           inp["mask"])
         got = tuple(torch.full_like(x, float("nan")) for x in want)
