@@ -45,9 +45,13 @@ def _run(op, inp, t, o, m, l):
     return [x.clone() for x in (dq, dk, dv, fo, fm, fl)]
 
 
-@pytest.mark.parametrize("algo", [B.FA_BWD_ALGO_DEFAULT, B.FA_BWD_ALGO_RECOMPUTE_DQ_4W], ids=["default", "4w"])
+@pytest.mark.parametrize("algo", [B.FA_BWD_ALGO_DEFAULT, B.FA_BWD_ALGO_RECOMPUTE_DQ_4W, B.FA_BWD_ALGO_RECOMPUTE_DQ_64K,
+                                  B.FA_BWD_ALGO_STORED_DS], ids=["default", "4w", "64k", "storedds"])
 @pytest.mark.parametrize("case", CASES, ids=[c.name for c in CASES])
 def test_planned_equals_dense_bitwise(case, algo):
+    if algo in (B.FA_BWD_ALGO_RECOMPUTE_DQ_64K, B.FA_BWD_ALGO_STORED_DS) and not (
+            case.head_dim == 128 and case.head_dim_v in (0, 128) and case.window == 0):
+        pytest.skip("the 64-key layout (and the stored-dS form) needs head dims of 128 and no window")
     inp = I.make(case)
     print(f"[plan] {case.name}: lengths {inp['seqlens_q']} mask {case.mask} algorithm {algo}", flush=True)
     dev = torch.device("cuda")
