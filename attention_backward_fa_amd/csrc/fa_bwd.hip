@@ -112,6 +112,17 @@ int threads_per_row(int d_qk, int d_v) {
   return t;
 }
 
+// Bytes of the stored-dS form's workspace: 16 KiB blocks of (32-row q step) x (256-key kv tile) per
+// (sequence, query head); -1 when the size passes kDsMaxBytes (computed in double, so that no product
+// overflows).
+constexpr int64_t kDsMaxBytes = int64_t(1) << 47;
+int64_t ds_bytes_of(const fa_bwd_desc& d, int32_t& nqs, int32_t& nkt) {
+  nqs = (d.max_seqlen_q + 31) / 32;
+  nkt = (d.max_seqlen_kv + 255) / 256;
+  const double bytes = (double)nqs * nkt * d.num_heads * d.batch * (256.0 * 32 * 2);
+  return bytes > (double)kDsMaxBytes ? -1 : (int64_t)bytes;
+}
+
 fa_bwd_status check_desc(const fa_bwd_desc* d) {
   if (!d) return FA_BWD_ERR_INVALID_ARGUMENT;
   if (d->batch < 1 || d->num_heads < 1 || d->max_seqlen_q < 1 || d->max_seqlen_kv < 1 || d->total_q < 1 ||
@@ -136,6 +147,10 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   if ((d->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_64K || d->algorithm == FA_BWD_ALGO_STORED_DS) &&
       (d->head_dim != 128 || dv != 128 || d->window != 0))
     return FA_BWD_ERR_UNSUPPORTED;
+  if (d->algorithm == FA_BWD_ALGO_STORED_DS) {  // its dS workspace must have a size (at most 2^47 bytes)
+    int32_t nqs, nkt;
+    if (ds_bytes_of(*d, nqs, nkt) < 0) return FA_BWD_ERR_UNSUPPORTED;
+  }
   // index arithmetic stays in int64; grids must fit the launch limits
   const int64_t rows = (d->total_q > d->total_kv ? d->total_q : d->total_kv);
   if (rows > (int64_t(1) << 40) / d->num_heads) return FA_BWD_ERR_INVALID_ARGUMENT;
@@ -193,12 +208,6 @@ void launch_dq_ds(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
 // within this size (on a GPU with 288 GB of memory); above it, it keeps the recompute form.
 constexpr int64_t kDsDefaultMaxBytes = int64_t(8) << 30;
 
-// dS blocks of the stored-dS form: (32-row q steps) x (256-key kv tiles) per (sequence, query head)
-int64_t ds_blocks(const fa_bwd_desc& d, int32_t& nqs, int32_t& nkt) {
-  nqs = (d.max_seqlen_q + 31) / 32;
-  nkt = (d.max_seqlen_kv + 255) / 256;
-  return (int64_t)nqs * nkt * d.num_heads * d.batch;
-}
 
 // The kernels for the padded head dims: each dim rounded up to 64, 128, 192 or 256, and a dim of 64
 // next to one above 128 taken as 128.
@@ -670,10 +679,10 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
     return FA_BWD_ERR_HIP;
   }
   configure_layouts(h, cus);
-  const int64_t ds_need = ds_blocks(h->desc, h->ds_nqs, h->ds_nkt) * 256 * 32 * 2;
+  const int64_t ds_need = ds_bytes_of(h->desc, h->ds_nqs, h->ds_nkt);
   h->ds_form = desc->algorithm == FA_BWD_ALGO_STORED_DS ||
                (desc->algorithm == FA_BWD_ALGO_DEFAULT && (h->layout[0] == 3 || h->layout[1] == 3) &&
-                ds_need <= kDsDefaultMaxBytes);
+                ds_need >= 0 && ds_need <= kDsDefaultMaxBytes);
   const size_t ds_bytes = h->ds_form ? (size_t)ds_need : 0;
   const size_t stats = (size_t)desc->total_q * desc->num_heads;
   const size_t acc = stats * desc->head_dim * (h->split ? fa::kSplits : 1);

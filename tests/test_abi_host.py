@@ -88,6 +88,9 @@ def _create(**kw):
     (dict(algorithm=6, window=16), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(algorithm=7, head_dim=64), B.FA_BWD_ERR_UNSUPPORTED),                 # stored dS: the same
     (dict(algorithm=7, window=16), B.FA_BWD_ERR_UNSUPPORTED),
+    # stored dS: a dS workspace past 2^47 bytes (here 2^24 x 2^21 blocks of 16 KiB per head)
+    (dict(algorithm=7, max_seqlen_q=1 << 29, max_seqlen_kv=1 << 29, total_q=1 << 29, total_kv=1 << 29),
+     B.FA_BWD_ERR_UNSUPPORTED),
     (dict(algorithm=-1), B.FA_BWD_ERR_INVALID_ARGUMENT),
     (dict(total_q=1 << 40, num_heads=8), B.FA_BWD_ERR_INVALID_ARGUMENT),          # index range
     (dict(max_seqlen_kv=1 << 30, num_heads=1 << 10, batch=1 << 10), B.FA_BWD_ERR_INVALID_ARGUMENT),  # grid size
