@@ -40,6 +40,8 @@ struct fa_bwd_handle {
   // the dQ and dK/dV kernels' dense grids in head-major order per XCD (head_major_balances), without
   // and with a causal bound
   bool dq_head_major[2], dkdv_head_major[2];
+  // the dQ kernel in two key groups per workgroup (dq_key_split)
+  bool dq_split;
   // stored-dS form: the 64-key dK/dV kernel writes dS blocks, the dQ pass reads them
   bool ds_form;
   fa::bf16* ds;
@@ -101,6 +103,15 @@ void dq_work(int64_t lq, int64_t lk, bool causal, int64_t w, int64_t& total, int
 // quarter of the work per workgroup slot, where that lateness costs little.
 bool head_major_balances(double total, double largest, int64_t slots, int64_t heads_x_seqs) {
   return heads_x_seqs % 8 == 0 && 4.0 * largest * slots <= total;
+}
+
+// The dQ kernel for heads up to 128 (narrow) runs two workgroups of four waves per CU, each wave over
+// one 32-row q step. Where its dense grid has no more workgroups than CUs, that leaves at most one wave
+// per SIMD with nothing to hide its waits behind; there it takes two key groups per workgroup (eight
+// waves, one workgroup per CU), each over every other kv step.
+bool dq_key_split(const fa_bwd_desc& d, bool narrow, int cus) {
+  const int64_t q_blocks = (int64_t)((d.max_seqlen_q + 127) / 128) * d.num_heads * d.batch;
+  return narrow && q_blocks <= cus;
 }
 
 // threads per (token, head) row of the row kernels: a power of two covering the wider row in
@@ -407,7 +418,7 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
     if (ds_run)
       launch_dq_ds(ma, h->n_q_items, stream);
     else
-      ks.dq(ma, h->n_q_items, stream);
+      ks.dq(ma, h->n_q_items, h->dq_split, stream);
   }
   if (hipGetLastError() != hipSuccess) return FA_BWD_ERR_HIP;
   if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return FA_BWD_ERR_HIP;
@@ -540,6 +551,7 @@ int32_t dkdv_layout_code(int32_t algorithm) {
 // from the descriptor (every sequence taken at the maximum lengths) and the compute-unit count.
 void configure_layouts(fa_bwd_handle* h, int cus) {
   const fa_bwd_desc& hd = h->desc;
+  h->dq_split = dq_key_split(hd, pick_kernels(hd.head_dim, hd.head_dim_v).two_layouts, cus);
   const int64_t per_tile_heads = (int64_t)hd.batch * hd.num_heads;  // Hk K/V heads x G query heads each
   const int G = hd.num_heads / hd.num_heads_kv;
   for (int c = 0; c < 2; ++c) {
@@ -570,7 +582,7 @@ void configure_layouts(fa_bwd_handle* h, int cus) {
     int64_t qtotal = 0, qlargest = 0;
     dq_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), qtotal, qlargest);
     h->dq_head_major[c] = head_major_balances((double)qtotal * (double)per_tile_heads, (double)qlargest,
-                                              (int64_t)cus * (narrow ? 2 : 1), per_tile_heads);
+                                              (int64_t)cus * (narrow && !h->dq_split ? 2 : 1), per_tile_heads);
   }
 }
 

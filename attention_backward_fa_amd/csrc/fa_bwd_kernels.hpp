@@ -1129,14 +1129,20 @@ struct KvTileLoader {
 // dQ of one (q tile, head, sequence): loops over the kv tiles, recomputes S^T = K Q^T and
 // dP^T = V dO^T with the forward's statistics (steps 1-5 of the per-tile math), and
 // accumulates dQ^T = K^T dS^T (step 8) in registers; dQ is written once, in bf16.
-template <int DQ, int DV, bool CAUSAL, bool WINDOW, bool EXACT>
-__global__ __attribute__((amdgpu_flat_work_group_size(DqCfg<DQ, DV>::NT, DqCfg<DQ, DV>::NT),
+// KS = 2 (heads up to 128): two groups of four waves per workgroup, each with its own K/V tile
+// buffers; group g takes kv steps t0 + g, t0 + g + 2, ..., and at the end group 1's sums are added to
+// group 0's through LDS (always in that order, so the result is deterministic). For grids with no
+// more workgroups than CUs, where one group per workgroup leaves a single wave on each SIMD.
+template <int DQ, int DV, bool CAUSAL, bool WINDOW, bool EXACT, int KS>
+__global__ __attribute__((amdgpu_flat_work_group_size(DqCfg<DQ, DV>::NT * KS, DqCfg<DQ, DV>::NT * KS),
                           amdgpu_waves_per_eu(DqCfg<DQ, DV>::WPE, DqCfg<DQ, DV>::WPE)))
 void fa_bwd_dq(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = DqCfg<DQ, DV>;
   constexpr int BQ = C::BQ, BK = C::BK, QSQ = C::QSQ, QSV = C::QSV;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  static_assert(KS == 1 || (KS == 2 && !C::WIDE), "the key split needs two sets of tile buffers in LDS");
+  static_assert(KS == 1 || C::NW * C::NTQ * 16 * 64 * 4 <= KS * C::LDS_BYTES, "the sums of group 1 fit the buffers");
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES * KS];
 
   // the host schedule names each workgroup's (q tile, sequence * H + head). The dense grid runs the q
   // tiles with the most keys (under a causal mask the last ones) first, tile-major over the heads and
@@ -1169,7 +1175,10 @@ void fa_bwd_dq(MainArgs a) {
   if (i0 >= Lq) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int w = KS == 1 ? wv : wv & (C::NW - 1);            // the q wave: rows 32 w ..+31 of the tile
+  const int gk = KS == 1 ? 0 : wv / C::NW;                  // the key group
+  char* const gsm = smem + gk * C::LDS_BYTES;               // the group's K/V tile buffers
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
   const int dqk = EXACT ? DQ : a.d_qk, dvd = EXACT ? DV : a.d_v;  // EXACT: the padded dims
   const int64_t rsq = (int64_t)a.H * dqk, rsd = (int64_t)a.H * dvd;     // row strides of Q (dQ) and dO
@@ -1210,14 +1219,14 @@ void fa_bwd_dq(MainArgs a) {
 
   {  // zero the K and V buffers once (rows past the sequence are masked, but must be finite)
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int o = tid * 16; o < C::LDS_BYTES; o += C::NT * 16) *(u32x4*)(smem + o) = z;
+    for (int o = tid * 16; o < C::LDS_BYTES * KS; o += C::NT * KS * 16) *(u32x4*)(smem + o) = z;
   }
   __syncthreads();
 
   const KvTileLoader<C> loader(w, lane, rskqb, rskvb, dqk, dvd);
   auto issue_kv = [&](int t, int bi) {
     const int j0 = t * BK, rows = imin(Lk - j0, BK);
-    loader.issue(smem, w, make_rsrc(kb + (int64_t)j0 * rskq, (int64_t)rows * rskqb),
+    loader.issue(gsm, w, make_rsrc(kb + (int64_t)j0 * rskq, (int64_t)rows * rskqb),
                  make_rsrc(vb + (int64_t)j0 * rskv, (int64_t)rows * rskvb), bi);
   };
 
@@ -1226,116 +1235,137 @@ void fa_bwd_dq(MainArgs a) {
   for (int nt = 0; nt < C::NTQ; ++nt) acc[nt] = f32x16{};
 
   int buf = 0;
-  if (n_kt > t0) issue_kv(t0, 0);
+  if (n_kt > t0 + gk) issue_kv(t0 + gk, 0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
 
   const int arowk = tile_row(c) * QSQ + 8 * hh;
   const int arowv = tile_row(c) * QSV + 8 * hh;
   const int browk = (hh + 4 * (gi >> 2)) * QSQ + 16 * (g & 1) + 4 * (gi & 3);
-  for (int t = t0; t < n_kt; ++t, buf ^= 1) {
-    if (t + 1 < n_kt) issue_kv(t + 1, buf ^ 1);
-    const bf16* sk = (const bf16*)(smem + C::OFF_K + buf * C::TK_BYTES);
-    const bf16* sv = (const bf16*)(smem + C::OFF_V + buf * C::TV_BYTES);
-    // steps 1 and 3, transposed: S^T = K Q^T and dP^T - D = V dO^T - D ([kv 64] x [q 32] per wave;
-    // the dP accumulators start from -D of the lane's query row, which folds the subtraction of
-    // step 5 into the GEMM)
-    f32x16 s[2], dp[2];
-    float ndd = -dd;
-    asm volatile("" : "+v"(ndd));  // formed per step: a splat kept across the loop would spill
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = f32x16{};
-#pragma unroll
-      for (int j = 0; j < 16; ++j) dp[mt][j] = ndd;
-    }
-    {  // operands read PF k-steps ahead into distinct registers, one scheduling fence per k-step
-      constexpr int PF = 2;
-      bf16x8 ka[C::KSQ][2], va[C::KSV][2];
-      auto ld = [&](int ks) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          if (ks < C::KSQ) ka[ks][mt] = *(const bf16x8*)(sk + arowk + 32 * mt * QSQ + 16 * ks);
-          if (ks < C::KSV) va[ks][mt] = *(const bf16x8*)(sv + arowv + 32 * mt * QSV + 16 * ks);
-        }
-      };
-#pragma unroll
-      for (int ks = 0; ks < PF; ++ks) ld(ks);
-#pragma unroll
-      for (int ks = 0; ks < C::KSM; ++ks) {
-        if (ks + PF < C::KSM) ld(ks + PF);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          if (ks < C::KSQ) s[mt] = mfma32x32x16(ka[ks][mt], qf[ks], s[mt]);
-          if (ks < C::KSV) dp[mt] = mfma32x32x16(va[ks][mt], df[ks], dp[mt]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // steps 2 and 5: P = exp2(S*scale*log2e - lse2), dS = P (dP - D); key row j = t*BK + kv row.
-    // Visible iff j < Lk and (causal) j <= qi: one bound per lane on the tile-local kv row.
-    const int lim = CAUSAL ? imin(Lk - 1, qi) - t * BK : Lk - 1 - t * BK;
-    // window: visible iff lo <= kr <= lim, one unsigned compare of kr - lo against lim - lo (a row
-    // that sees no key of the tile gets a base past every kv row)
-    const int lo = qi - a.window + 1 - t * BK;
-    const int wbase = lim >= lo ? lo : (1 << 30);
-    const unsigned wspan = lim >= lo ? (unsigned)(lim - lo) : 0u;
-    bf16x8 dsk[2][2];
-    auto softmax = [&](auto masked) {
-#pragma unroll
+  // steps of both groups (the last one of group 1 may have no tile: it only keeps the barriers)
+  const int n_it = (n_kt - t0 + KS - 1) / KS;
+  for (int it = 0; it < n_it; ++it, buf ^= 1) {
+    const int t = t0 + KS * it + gk;
+    if (t + KS < n_kt) issue_kv(t + KS, buf ^ 1);
+    if (KS == 1 || t < n_kt) {
+      const bf16* sk = (const bf16*)(gsm + C::OFF_K + buf * C::TK_BYTES);
+      const bf16* sv = (const bf16*)(gsm + C::OFF_V + buf * C::TV_BYTES);
+      // steps 1 and 3, transposed: S^T = K Q^T and dP^T - D = V dO^T - D ([kv 64] x [q 32] per wave;
+      // the dP accumulators start from -D of the lane's query row, which folds the subtraction of
+      // step 5 into the GEMM)
+      f32x16 s[2], dp[2];
+      float ndd = -dd;
+      asm volatile("" : "+v"(ndd));  // formed per step: a splat kept across the loop would spill
+  #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            const int j = 4 * a4 + bb;
-            float p = fast_exp2(s[mt][j] * a.scale_log2 - lse);
-            if constexpr (decltype(masked)::value) {
-              const int kr = 32 * mt + tile_row(8 * a4 + 4 * hh + bb);
-              if constexpr (WINDOW)
-                p = (unsigned)(kr - wbase) <= wspan ? p : 0.f;
-              else
-                p = kr <= lim ? p : 0.f;
+        s[mt] = f32x16{};
+  #pragma unroll
+        for (int j = 0; j < 16; ++j) dp[mt][j] = ndd;
+      }
+      {  // operands read PF k-steps ahead into distinct registers, one scheduling fence per k-step
+        constexpr int PF = 2;
+        bf16x8 ka[C::KSQ][2], va[C::KSV][2];
+        auto ld = [&](int ks) {
+  #pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            if (ks < C::KSQ) ka[ks][mt] = *(const bf16x8*)(sk + arowk + 32 * mt * QSQ + 16 * ks);
+            if (ks < C::KSV) va[ks][mt] = *(const bf16x8*)(sv + arowv + 32 * mt * QSV + 16 * ks);
+          }
+        };
+  #pragma unroll
+        for (int ks = 0; ks < PF; ++ks) ld(ks);
+  #pragma unroll
+        for (int ks = 0; ks < C::KSM; ++ks) {
+          if (ks + PF < C::KSM) ld(ks + PF);
+  #pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            if (ks < C::KSQ) s[mt] = mfma32x32x16(ka[ks][mt], qf[ks], s[mt]);
+            if (ks < C::KSV) dp[mt] = mfma32x32x16(va[ks][mt], df[ks], dp[mt]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // steps 2 and 5: P = exp2(S*scale*log2e - lse2), dS = P (dP - D); key row j = t*BK + kv row.
+      // Visible iff j < Lk and (causal) j <= qi: one bound per lane on the tile-local kv row.
+      const int lim = CAUSAL ? imin(Lk - 1, qi) - t * BK : Lk - 1 - t * BK;
+      // window: visible iff lo <= kr <= lim, one unsigned compare of kr - lo against lim - lo (a row
+      // that sees no key of the tile gets a base past every kv row)
+      const int lo = qi - a.window + 1 - t * BK;
+      const int wbase = lim >= lo ? lo : (1 << 30);
+      const unsigned wspan = lim >= lo ? (unsigned)(lim - lo) : 0u;
+      bf16x8 dsk[2][2];
+      auto softmax = [&](auto masked) {
+  #pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+  #pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+  #pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+              const int j = 4 * a4 + bb;
+              float p = fast_exp2(s[mt][j] * a.scale_log2 - lse);
+              if constexpr (decltype(masked)::value) {
+                const int kr = 32 * mt + tile_row(8 * a4 + 4 * hh + bb);
+                if constexpr (WINDOW)
+                  p = (unsigned)(kr - wbase) <= wspan ? p : 0.f;
+                else
+                  p = kr <= lim ? p : 0.f;
+              }
+              dsk[mt][j >> 3][j & 7] = to_bf16(p * dp[mt][j]);
             }
-            dsk[mt][j >> 3][j & 7] = to_bf16(p * dp[mt][j]);
           }
         }
-      }
-    };
-    // every key of the tile visible from every row of this wave: no element mask (wave-uniform)
-    const int qmin = i0 + 32 * w, kmax = t * BK + BK - 1;
-    const bool full = kmax <= Lk - 1 && (!CAUSAL || kmax <= qmin) && (!WINDOW || qmin + 31 - a.window < t * BK);
-    if (full)
-      softmax(std::false_type{});
-    else
-      softmax(std::true_type{});
-    // step 8, transposed: dQ^T += K^T dS^T. k-step ksi = 2 mt + s2: its k-index e is kv MFMA row
-    // 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4 of M-tile mt; the transpose reads fetch
-    // those K rows. k-steps run outside the NTQ independent accumulators; A operands are read PF
-    // MFMAs ahead.
-    {
-      constexpr int NB = 4 * C::NTQ, PF = 3;
-      bf16x8 kt[NB];
-      auto kt_load = [&](int i) {
-        const int ksi = i / C::NTQ, nt = i % C::NTQ;
-        const int o = browk + 16 * ksi * QSQ + 32 * nt;
-        return concat(lds_read_tr4(sk + o), lds_read_tr4(sk + o + 2 * QSQ));
       };
-#pragma unroll
-      for (int i = 0; i < PF; ++i) kt[i] = kt_load(i);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        if (i + PF < NB) kt[i + PF] = kt_load(i + PF);
-        const int ksi = i / C::NTQ, nt = i % C::NTQ;
-        acc[nt] = mfma32x32x16(kt[i], dsk[ksi >> 1][ksi & 1], acc[nt]);
+      // every key of the tile visible from every row of this wave: no element mask (wave-uniform)
+      const int qmin = i0 + 32 * w, kmax = t * BK + BK - 1;
+      const bool full = kmax <= Lk - 1 && (!CAUSAL || kmax <= qmin) && (!WINDOW || qmin + 31 - a.window < t * BK);
+      if (full)
+        softmax(std::false_type{});
+      else
+        softmax(std::true_type{});
+      // step 8, transposed: dQ^T += K^T dS^T. k-step ksi = 2 mt + s2: its k-index e is kv MFMA row
+      // 16 s2 + 4 hh + e (e < 4) or 16 s2 + 8 + 4 hh + e - 4 of M-tile mt; the transpose reads fetch
+      // those K rows. k-steps run outside the NTQ independent accumulators; A operands are read PF
+      // MFMAs ahead.
+      {
+        constexpr int NB = 4 * C::NTQ, PF = 3;
+        bf16x8 kt[NB];
+        auto kt_load = [&](int i) {
+          const int ksi = i / C::NTQ, nt = i % C::NTQ;
+          const int o = browk + 16 * ksi * QSQ + 32 * nt;
+          return concat(lds_read_tr4(sk + o), lds_read_tr4(sk + o + 2 * QSQ));
+        };
+  #pragma unroll
+        for (int i = 0; i < PF; ++i) kt[i] = kt_load(i);
         __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          if (i + PF < NB) kt[i + PF] = kt_load(i + PF);
+          const int ksi = i / C::NTQ, nt = i % C::NTQ;
+          acc[nt] = mfma32x32x16(kt[i], dsk[ksi >> 1][ksi & 1], acc[nt]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the next K/V tiles have landed
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+  }
+
+  if constexpr (KS > 1) {  // group 1's sums through LDS (free after the loop's last barrier), added to group 0's
+    float* red = (float*)smem + w * (C::NTQ * 16 * 64) + lane;
+    if (gk == 1) {
+#pragma unroll
+      for (int nt = 0; nt < C::NTQ; ++nt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) red[(nt * 16 + j) * 64] = acc[nt][j];
+    }
+    __syncthreads();
+    if (gk == 1) return;
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[nt][j] += red[(nt * 16 + j) * 64];
   }
 
   // dQ = scale * (dQ^T)^T in bf16: this lane holds features 32 nt + 8 a4 + 4 hh + bb of row qi

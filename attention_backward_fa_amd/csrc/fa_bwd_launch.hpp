@@ -41,14 +41,24 @@ struct Recompute {
       dkdv_layout<2>(a, items, s);
   }
 
-  static void dq(const MainArgs& a, int64_t items, hipStream_t s) {
-    const dim3 grid((unsigned)(a.sched ? items : q_blocks(a.max_seqlen_q, a.H, a.batch))), block(DqCfg<DQ, DV>::NT);
+  template <int KS>
+  static void dq_groups(const MainArgs& a, int64_t items, hipStream_t s) {
+    const dim3 grid((unsigned)(a.sched ? items : q_blocks(a.max_seqlen_q, a.H, a.batch))),
+        block(DqCfg<DQ, DV>::NT * KS);
     if (a.window > 0)
-      fa_bwd_dq<DQ, DV, true, true, EXACT><<<grid, block, 0, s>>>(a);
+      fa_bwd_dq<DQ, DV, true, true, EXACT, KS><<<grid, block, 0, s>>>(a);
     else if (a.causal)
-      fa_bwd_dq<DQ, DV, true, false, EXACT><<<grid, block, 0, s>>>(a);
+      fa_bwd_dq<DQ, DV, true, false, EXACT, KS><<<grid, block, 0, s>>>(a);
     else
-      fa_bwd_dq<DQ, DV, false, false, EXACT><<<grid, block, 0, s>>>(a);
+      fa_bwd_dq<DQ, DV, false, false, EXACT, KS><<<grid, block, 0, s>>>(a);
+  }
+  // key_split: two groups of four waves per workgroup, each over every other kv step (heads up to
+  // 128; wider heads have one form)
+  static void dq(const MainArgs& a, int64_t items, bool key_split, hipStream_t s) {
+    if constexpr (!DqCfg<DQ, DV>::WIDE) {
+      if (key_split) return dq_groups<2>(a, items, s);
+    }
+    dq_groups<1>(a, items, s);
   }
 
   static void fwd(const FwdArgs& a, bool causal, int64_t items, hipStream_t s) {
@@ -65,7 +75,7 @@ struct Recompute {
 // The launches of one pair of padded head dims, and the tile sizes a host schedule counts in.
 struct KernelSet {
   void (*dkdv)(const MainArgs&, int64_t, bool, hipStream_t);
-  void (*dq)(const MainArgs&, int64_t, hipStream_t);
+  void (*dq)(const MainArgs&, int64_t, bool, hipStream_t);
   void (*fwd)(const FwdArgs&, bool, int64_t, hipStream_t);
   int kv_tile, q_step;  // dK/dV kernel: kv rows per workgroup, q rows per step (eight-wave layout)
   bool two_layouts;     // the dK/dV kernel also has the four-wave layout
