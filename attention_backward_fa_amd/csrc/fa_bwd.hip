@@ -154,9 +154,9 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   // window bounds (kv0 + tile + window, i - window - kv0) then fit in 32 bits
   if (d->max_seqlen_q > (1 << 30) || d->max_seqlen_kv > (1 << 30)) return FA_BWD_ERR_INVALID_ARGUMENT;
   if (single && d->window > 0) return FA_BWD_ERR_UNSUPPORTED;
-  // the 64-key dK/dV layout (and the stored-dS form built on it) exists for head dims of 128 without a window
+  // the 64-key dK/dV layout (and the stored-dS form built on it) exists for head dims of 128
   if ((d->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_64K || d->algorithm == FA_BWD_ALGO_STORED_DS) &&
-      (d->head_dim != 128 || dv != 128 || d->window != 0))
+      (d->head_dim != 128 || dv != 128))
     return FA_BWD_ERR_UNSUPPORTED;
   if (d->algorithm == FA_BWD_ALGO_STORED_DS) {  // its dS workspace must have a size (at most 2^47 bytes)
     int32_t nqs, nkt;
@@ -183,25 +183,29 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   return FA_BWD_OK;
 }
 
-// The dK/dV kernel with 64 keys per wave: head dims of exactly 128 and no window.
-bool keys64_applies(const fa_bwd_desc& d) { return d.head_dim == 128 && d.head_dim_v == 128 && d.window == 0; }
+// The dK/dV kernel with 64 keys per wave: head dims of exactly 128 (with or without a window).
+bool keys64_applies(const fa_bwd_desc& d) { return d.head_dim == 128 && d.head_dim_v == 128; }
 
 // The 64-key dK/dV layout runs one workgroup per CU over 256 keys (and every query head of its K/V
 // head): the default takes it where longest-first dispatch balances, i.e. the largest workgroup,
 // doubled, fits within the average work per CU. Small grids, and grouped K/V heads that multiply each
-// workgroup's work, keep the 128-key layouts.
+// workgroup's work, keep the 128-key layouts; so do windows, whose band edges put the element mask on
+// a large share of the 64-key kernel's steps (the four-wave layout measured faster there).
 bool keys64_balances(double total, double largest, int cus) { return 2.0 * largest * cus <= total; }
 
 void launch_dkdv64(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
   using C = fa::Dkdv64Cfg;
   const int64_t blocks = (int64_t)((ma.max_seqlen_kv + C::BN - 1) / C::BN) * ma.Hk * ma.batch;
   const dim3 grid((unsigned)(ma.sched ? items : blocks)), block(C::NT);
-  if (ma.ds)
-    ma.causal ? fa::fa_bwd_dkdv64<true, true><<<grid, block, 0, stream>>>(ma)
-              : fa::fa_bwd_dkdv64<false, true><<<grid, block, 0, stream>>>(ma);
+  if (ma.window > 0)  // the window implies the causal bound
+    ma.ds ? fa::fa_bwd_dkdv64<true, true, true><<<grid, block, 0, stream>>>(ma)
+          : fa::fa_bwd_dkdv64<true, false, true><<<grid, block, 0, stream>>>(ma);
+  else if (ma.ds)
+    ma.causal ? fa::fa_bwd_dkdv64<true, true, false><<<grid, block, 0, stream>>>(ma)
+              : fa::fa_bwd_dkdv64<false, true, false><<<grid, block, 0, stream>>>(ma);
   else
-    ma.causal ? fa::fa_bwd_dkdv64<true, false><<<grid, block, 0, stream>>>(ma)
-              : fa::fa_bwd_dkdv64<false, false><<<grid, block, 0, stream>>>(ma);
+    ma.causal ? fa::fa_bwd_dkdv64<true, false, false><<<grid, block, 0, stream>>>(ma)
+              : fa::fa_bwd_dkdv64<false, false, false><<<grid, block, 0, stream>>>(ma);
 }
 
 // the stored-dS form's dQ pass: one workgroup per (128-row q tile, head, sequence), as the dQ kernel
@@ -209,10 +213,12 @@ void launch_dq_ds(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
   using C = fa::DqDsCfg;
   const int64_t blocks = (int64_t)((ma.max_seqlen_q + C::BQ - 1) / C::BQ) * ma.H * ma.batch;
   const dim3 grid((unsigned)(ma.sched ? items : blocks)), block(C::NT);
-  if (ma.causal)
-    fa::fa_bwd_dq_ds<true><<<grid, block, 0, stream>>>(ma);
+  if (ma.window > 0)
+    fa::fa_bwd_dq_ds<true, true><<<grid, block, 0, stream>>>(ma);
+  else if (ma.causal)
+    fa::fa_bwd_dq_ds<true, false><<<grid, block, 0, stream>>>(ma);
   else
-    fa::fa_bwd_dq_ds<false><<<grid, block, 0, stream>>>(ma);
+    fa::fa_bwd_dq_ds<false, false><<<grid, block, 0, stream>>>(ma);
 }
 
 // The default takes the stored-dS form where its runs take the 64-key layout and the dS workspace stays
@@ -566,10 +572,10 @@ void configure_layouts(fa_bwd_handle* h, int cus) {
     // the 64-key layout's own tile sizes: 256 keys, 32-row q steps
     int64_t total64 = 0, largest64 = 0;
     if (keys64_applies(hd))
-      dkdv_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1, 0, total64, largest64, fa::Dkdv64Cfg::BN,
-                fa::Dkdv64Cfg::BM);
+      dkdv_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), total64,
+                largest64, fa::Dkdv64Cfg::BN, fa::Dkdv64Cfg::BM);
     const bool keys64 = h->dkdv_layout == 3 ||
-                        (h->dkdv_layout == 0 && keys64_applies(hd) &&
+                        (h->dkdv_layout == 0 && keys64_applies(hd) && hd.window == 0 &&
                          keys64_balances((double)total64 * (double)per_tile_heads, (double)largest64 * G, cus));
     h->layout[c] = keys64 ? 3 : four ? 2 : 1;
     if (keys64) {

@@ -3,6 +3,8 @@
 // Steps 1-3 and 5-7 of the per-tile math of the PyPTO-Gym SK-16 article (section 3.1) for one
 // 256-key tile of one (K/V head, sequence): S = Q K^T, P = exp2(S*scale*log2e - lse2),
 // dP = dO V^T, dS = P (dP - D), dV += P^T dO, dK += dS^T Q, with dK scaled once at the end.
+// WINDOW (with the causal bound): query i sees keys (i - window, i] only (the jax cuDNN wrapper's
+// sliding window); the steps end at the last query row that sees a key of the tile.
 //
 // Layout (one workgroup of four waves per CU, one wave per SIMD):
 //   - wave w owns keys kv0 + 64 w .. + 63 as two 32-key MFMA tiles; the first 64 features of its K
@@ -63,12 +65,13 @@ struct Dkdv64Cfg {
 
 // DS: also store each step's dS (bf16) as one 16 KB block of the stored-dS form (fa_bwd_dqds.hpp), in the
 // order the lanes hold the values: wave w's piece 2 n + s2 (1 KB) holds lane l's 16 bytes at 16 l.
-template <bool CAUSAL, bool DS>
+template <bool CAUSAL, bool DS, bool WINDOW>
 __global__ __attribute__((amdgpu_flat_work_group_size(Dkdv64Cfg::NT, Dkdv64Cfg::NT), amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_dkdv64(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = Dkdv64Cfg;
   constexpr int BN = C::BN, BM = C::BM, QS = C::QS, D = C::D, KS = C::KS, NTD = C::NTD;
+  static_assert(CAUSAL || !WINDOW, "a window implies the causal bound");
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   float* s_st = (float*)(smem + C::OFF_ST);
 
@@ -113,7 +116,9 @@ void fa_bwd_dkdv64(MainArgs a) {
   __syncthreads();
 
   // the steps: for each query head of the group, the 32-row q tiles that can see these keys
-  const int n_qt = (Lq + BM - 1) / BM;
+  // (window: query rows up to kv0 + BN - 1 + window - 1 see a key of the tile; the sum stays below 2^31,
+  // as positions and the window, clamped to the longest sequence, stay below 2^30)
+  const int n_qt = WINDOW ? imin((Lq + BM - 1) / BM, (kv0 + BN - 2 + a.window) / BM + 1) : (Lq + BM - 1) / BM;
   const int qt0 = CAUSAL ? kv0 / BM : 0;
   const int nq = n_qt > qt0 ? n_qt - qt0 : 0;
   const int n_steps = G * nq;
@@ -278,7 +283,9 @@ void fa_bwd_dkdv64(MainArgs a) {
   };
 
   // every key of this wave visible from every row of step sp: no element mask (wave-uniform)
-  auto full_step = [&](int qtile) { return !CAUSAL || kv0 + 64 * w + 63 <= qtile * BM; };
+  auto full_step = [&](int qtile) {
+    return (!CAUSAL || kv0 + 64 * w + 63 <= qtile * BM) && (!WINDOW || qtile * BM + BM - 1 - (kv0 + 64 * w) < a.window);
+  };
   // First GEMMs of step sp over buffer bi: S = Q K^T for both key tiles over the 8 k-steps, then
   // dP = dO V^T; each Q or dO fragment feeds both key tiles. Operands are read PF MFMAs ahead. The
   // accumulators start from the row statistics (above); under a causal mask, on steps whose rows do
@@ -329,16 +336,24 @@ void fa_bwd_dkdv64(MainArgs a) {
     s_init[1] = s_init[0];
     if (!full_step(qtile)) {
       // opaque to the optimiser, so that the 32 comparisons stay against immediates inside the loop
-      // instead of becoming per-element values held across it
+      // instead of becoming per-element values held across it. Window: the key is too old for the
+      // row iff kv0 + 64 w + 32 n + c <= row - window, i.e. t + window <= (the same right side).
       int t = kv0 + 64 * w + c - qtile * BM - hh;
       asm volatile("" : "+v"(t));
+      int tw = 0;
+      if constexpr (WINDOW) {
+        tw = t + a.window;
+        asm volatile("" : "+v"(tw));
+      }
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
-          for (int bb = 0; bb < 4; ++bb)
-            if (t > 2 * (a4 & 1) + 4 * bb + 16 * (a4 >> 1) - 32 * n) s_init[n][4 * a4 + bb] = -__builtin_inff();
+          for (int bb = 0; bb < 4; ++bb) {
+            const int rhs = 2 * (a4 & 1) + 4 * bb + 16 * (a4 >> 1) - 32 * n;
+            if (t > rhs || (WINDOW && tw <= rhs)) s_init[n][4 * a4 + bb] = -__builtin_inff();
+          }
     }
 #pragma unroll
     for (int m = 0; m < 32; ++m) {

@@ -37,12 +37,13 @@ struct DqDsCfg {
   static_assert(TK_BYTES % 1024 == 0, "whole 1 KB transfers");
 };
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool WINDOW>
 __global__ __attribute__((amdgpu_flat_work_group_size(DqDsCfg::NT, DqDsCfg::NT), amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_ds(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = DqDsCfg;
   constexpr int BQ = C::BQ, BK = C::BK, QS = C::QS, D = C::D, NTQ = C::NTQ;
+  static_assert(CAUSAL || !WINDOW, "a window implies the causal bound");
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   // work item: as the recompute form's dQ kernel (host schedule, head-major per XCD, or tile-major with
@@ -91,6 +92,10 @@ void fa_bwd_dq_ds(MainArgs a) {
   // written whole, with zeros where a row does not see a key)
   int n_kt = (Lk + BK - 1) / BK;
   if (CAUSAL) n_kt = imin(n_kt, (i0 + BQ - 1) / BK + 1);
+  // window: from the first key the tile's first row sees. The dK/dV kernel's workgroup of kv tile j
+  // wrote the blocks of q steps up to the last row that sees one of its keys, (256 j + 254 + window) / 32
+  // (all others of this wave's blocks would hold zeros only): past it this wave reads an empty range.
+  const int t0 = WINDOW ? imax(0, i0 - a.window + 1) / BK : 0;
 
   {  // zero the K buffers once (rows past the sequence must be finite)
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -121,7 +126,8 @@ void fa_bwd_dq_ds(MainArgs a) {
   auto load_ds = [&](int s, bf16x8 (&x)[2][2]) {
     const int j = s >> 2, wp = s & 3;
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(dsb + j * tile_stride, t_rows && s < n_kt && j < a.ds_nkt ? C::BLOCK * 2 : 0);
+        make_rsrc(dsb + j * tile_stride, t_rows && s < n_kt && j < a.ds_nkt &&
+                                             (!WINDOW || 32 * t <= 256 * j + 254 + a.window) ? C::BLOCK * 2 : 0);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const bool key_in = 256 * j + 64 * wp + 32 * m + tile_row(c) < Lk;
@@ -197,14 +203,14 @@ void fa_bwd_dq_ds(MainArgs a) {
   };
 
   bf16x8 ds0[2][2], ds1[2][2], ds2[2][2];
-  issue_k(0, 0);
-  load_ds(0, ds0);
-  load_ds(1, ds1);
+  issue_k(t0, t0 & 1);
+  load_ds(t0, ds0);
+  load_ds(t0 + 1, ds1);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
   // three register sets for the dS of steps s, s + 1, s + 2 (each step prefetches into the one the
   // step before it has used)
-  for (int s = 0; s < n_kt; s += 3) {
+  for (int s = t0; s < n_kt; s += 3) {
     step(s, ds0, ds2);
     step(s + 1, ds1, ds0);
     step(s + 2, ds2, ds1);

@@ -61,7 +61,7 @@ typedef enum {
  * agree within the fp32 rounding of the accumulation order. */
 typedef enum {
   FA_BWD_ALGO_DEFAULT = 0,      /* the faster form on this GPU: FA_BWD_ALGO_STORED_DS where runs take the
-                                   64-key layout (head dims of 128, no window, grids that balance) and its
+                                   64-key layout (head dims of 128, grids that balance) and its
                                    dS workspace is at most 8 GiB, else FA_BWD_ALGO_RECOMPUTE_DQ */
   FA_BWD_ALGO_SINGLE_PASS = 1,  /* the article's single-pass structure: one main kernel forms the dK, dV and
                                    dQ contributions of every (q tile, kv tile) pair; dQ partial sums are
@@ -91,7 +91,8 @@ typedef enum {
   FA_BWD_ALGO_RECOMPUTE_DQ_64K = 6, /* FA_BWD_ALGO_RECOMPUTE_DQ with the 64-key layout of the kv-outer
                                    kernel: one four-wave workgroup per compute unit over 256 keys, each
                                    wave holding 64 keys and their dK, dV sums, 32-row q steps; head
-                                   dims of exactly 128 and no window (else FA_BWD_ERR_UNSUPPORTED) */
+                                   dims of exactly 128 (else FA_BWD_ERR_UNSUPPORTED), with or without
+                                   a window */
   FA_BWD_ALGO_STORED_DS = 7        /* the 64-key kv-outer kernel also writes dS (bf16) to a workspace, and
                                    dQ = scale * dS K (SK-16 article, section 3.1, step 8) runs as a
                                    q-outer pass over it instead of forming S and dP a second time.

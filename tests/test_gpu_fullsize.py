@@ -33,12 +33,13 @@ ALGOS = {"default": B.FA_BWD_ALGO_DEFAULT, "eightwave": B.FA_BWD_ALGO_RECOMPUTE_
          "fourwave": B.FA_BWD_ALGO_RECOMPUTE_DQ_4W, "keys64": B.FA_BWD_ALGO_RECOMPUTE_DQ_64K,
          "singlepass": B.FA_BWD_ALGO_SINGLE_PASS, "splitreduce": B.FA_BWD_ALGO_SPLIT_REDUCE,
          "storedds": B.FA_BWD_ALGO_STORED_DS}
-# the workloads with grouped K/V heads, a window or other head dims run the recompute form only
+# the variant workloads (grouped K/V heads, a window, other head dims) in the default form, and the
+# window one also in the 64-key and stored-dS forms
 VARIANTS = ["causal_gqa", "causal_window", "causal_d256", "causal_mla"]
 # (workload, algorithm): every algorithm of a workload runs while its reference is held, then the
 # forward of that workload where it is checked
 CASES = ([(n, a) for n in FULL for a in list(ALGOS) + (["forward"] if n in ("causal", "longpad") else [])]
-         + [(n, "default") for n in VARIANTS])
+         + [(n, a) for n in VARIANTS for a in ["default"] + (["keys64", "storedds"] if n == "causal_window" else [])])
 
 _held = {}
 

@@ -46,9 +46,8 @@ ALGOS = {"recompute": B.FA_BWD_ALGO_RECOMPUTE_DQ, "recompute8w": B.FA_BWD_ALGO_R
 
 
 def _supported(case, algo):
-    # the 64-key dK/dV layout (and the stored-dS form on it) exists for head dims of 128 without a window
-    return algo not in ("recompute64k", "storedds") or (case.head_dim == 128 and case.head_dim_v in (0, 128)
-                                                        and case.window == 0)
+    # the 64-key dK/dV layout (and the stored-dS form on it) exists for head dims of 128
+    return algo not in ("recompute64k", "storedds") or (case.head_dim == 128 and case.head_dim_v in (0, 128))
 
 
 # (case, algorithm) pairs, case-major so that each case's oracle reference is computed once
@@ -120,7 +119,11 @@ def test_recompute_is_bitwise_reproducible(layout):
                                   I.custom_case("storedds_padded", 2, 128, I.MASK_PADDING_CAUSAL, 217, [300, 131],
                                                 padded_len=320),
                                   I.custom_case("storedds_kv_longer", 2, 128, I.MASK_NONE, 218, [100, 250],
-                                                [600, 64])], ids=lambda c: c.name)
+                                                [600, 64]),
+                                  # a window whose band starts at the last key of a 256-key block for the
+                                  # q tile at row 384: the blocks of its later 32-row steps are not written
+                                  I.custom_case("storedds_window_edge", 2, 128, I.MASK_CAUSAL, 219, [700, 450],
+                                                window=130)], ids=lambda c: c.name)
 def test_stored_ds_matches_recompute(case):
     """The stored-dS form runs the 64-key dK/dV kernel with dS stores added: its dK, dV equal the 64-key
     recompute form's bitwise; its dQ sums the same bf16 dS values in another kernel, so it agrees within
@@ -292,6 +295,26 @@ def test_parity_window(case):
     res = P.check_full(inp, gpu, ref)
     print(f"[parity-window] {case.name}: " + " ".join(f"{k}: rel_l2={v[0]:.2e}" for k, v in res.items()),
           flush=True)
+
+
+# the 64-key layout and the stored-dS form with a window: band edges inside and at the end of 256-key
+# blocks, windows of 1 and wider than a block, grouped heads, padding
+WINDOW_64K_CASES = [c for c in WINDOW_CASES if c.head_dim == 128] + [
+    I.custom_case("window_edge_d128", 2, 128, CAUSAL, 238, [700, 450], window=130),
+    I.custom_case("window_short_d128", 2, 128, CAUSAL, 239, [1100], window=40),
+    I.custom_case("window_block_d128", 2, 128, PADC, 240, [600, 520], padded_len=640, window=256),
+]
+
+
+@pytest.mark.parametrize("case,algo", [(c, a) for c in WINDOW_64K_CASES for a in ("recompute64k", "storedds")],
+                         ids=lambda x: x if isinstance(x, str) else x.name)
+def test_parity_window_64k(case, algo):
+    inp = I.make(case)
+    print(f"[parity-window-64k] {case.name} {algo}: window={case.window} mask={case.mask}", flush=True)
+    o, m, l = P.oracle_stats(inp)
+    gpu = P.run_gpu(inp, o, m, l, algorithm=ALGOS[algo])
+    ref = P.oracle_backward(inp, o, m, l)
+    P.check_full(inp, gpu, ref)
 
 
 def test_huge_window_is_the_causal_bound():
