@@ -13,6 +13,7 @@
 #include "fa_bwd.h"
 #include "fa_bwd_dkdv64.hpp"
 #include "fa_bwd_dqds.hpp"
+#include "fa_bwd_dqdsp.hpp"
 #include "fa_bwd_launch.hpp"
 
 struct fa_bwd_handle {
@@ -42,8 +43,9 @@ struct fa_bwd_handle {
   bool dq_head_major[2], dkdv_head_major[2];
   // the dQ kernel in two key groups per workgroup (dq_key_split)
   bool dq_split;
-  // stored-dS form: the 64-key dK/dV kernel writes dS blocks, the dQ pass reads them
-  bool ds_form;
+  // stored-dS form: the 64-key dK/dV kernel writes dS blocks, or the wide-head kernel dS pieces (ds_pieces),
+  // and the dQ pass reads them
+  bool ds_form, ds_pieces;
   fa::bf16* ds;
   int32_t ds_nqs, ds_nkt;
 };
@@ -123,14 +125,22 @@ int threads_per_row(int d_qk, int d_v) {
   return t;
 }
 
-// Bytes of the stored-dS form's workspace: 16 KiB blocks of (32-row q step) x (256-key kv tile) per
-// (sequence, query head); -1 when the size passes kDsMaxBytes (computed in double, so that no product
-// overflows).
+// The stored-dS form of the wide-head kernels (a head dim above 128, no window) stores 32 x 32 pieces;
+// at head dims of exactly 128 the form runs on the 64-key layout, which stores 32 x 256 blocks.
+bool ds_pieces_apply(const fa_bwd_desc& d) {
+  const int32_t dv = d.head_dim_v == 0 ? d.head_dim : d.head_dim_v;
+  return (d.head_dim > 128 || dv > 128) && d.window == 0;
+}
+
+// Bytes of the stored-dS form's workspace per (sequence, query head): 16 KiB blocks of (32-row q step) x
+// (256-key kv tile), or 2 KiB pieces of (32-row q step) x (32-key tile); -1 when the size passes
+// kDsMaxBytes (computed in double, so that no product overflows).
 constexpr int64_t kDsMaxBytes = int64_t(1) << 47;
-int64_t ds_bytes_of(const fa_bwd_desc& d, int32_t& nqs, int32_t& nkt) {
+int64_t ds_bytes_of(const fa_bwd_desc& d, bool pieces, int32_t& nqs, int32_t& nkt) {
+  const int kt = pieces ? 32 : 256;
   nqs = (d.max_seqlen_q + 31) / 32;
-  nkt = (d.max_seqlen_kv + 255) / 256;
-  const double bytes = (double)nqs * nkt * d.num_heads * d.batch * (256.0 * 32 * 2);
+  nkt = (d.max_seqlen_kv + kt - 1) / kt;
+  const double bytes = (double)nqs * nkt * d.num_heads * d.batch * (kt * 32.0 * 2);
   return bytes > (double)kDsMaxBytes ? -1 : (int64_t)bytes;
 }
 
@@ -154,13 +164,14 @@ fa_bwd_status check_desc(const fa_bwd_desc* d) {
   // window bounds (kv0 + tile + window, i - window - kv0) then fit in 32 bits
   if (d->max_seqlen_q > (1 << 30) || d->max_seqlen_kv > (1 << 30)) return FA_BWD_ERR_INVALID_ARGUMENT;
   if (single && d->window > 0) return FA_BWD_ERR_UNSUPPORTED;
-  // the 64-key dK/dV layout (and the stored-dS form built on it) exists for head dims of 128
-  if ((d->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_64K || d->algorithm == FA_BWD_ALGO_STORED_DS) &&
-      (d->head_dim != 128 || dv != 128))
-    return FA_BWD_ERR_UNSUPPORTED;
-  if (d->algorithm == FA_BWD_ALGO_STORED_DS) {  // its dS workspace must have a size (at most 2^47 bytes)
-    int32_t nqs, nkt;
-    if (ds_bytes_of(*d, nqs, nkt) < 0) return FA_BWD_ERR_UNSUPPORTED;
+  // the 64-key dK/dV layout exists for head dims of 128; the stored-dS form runs on it, or on the
+  // wide-head kernels (a head dim above 128) without a window
+  const bool d128 = d->head_dim == 128 && dv == 128;
+  if (d->algorithm == FA_BWD_ALGO_RECOMPUTE_DQ_64K && !d128) return FA_BWD_ERR_UNSUPPORTED;
+  if (d->algorithm == FA_BWD_ALGO_STORED_DS) {
+    if (!d128 && !ds_pieces_apply(*d)) return FA_BWD_ERR_UNSUPPORTED;
+    int32_t nqs, nkt;  // its dS workspace must have a size (at most 2^47 bytes)
+    if (ds_bytes_of(*d, !d128, nqs, nkt) < 0) return FA_BWD_ERR_UNSUPPORTED;
   }
   // index arithmetic stays in int64; grids must fit the launch limits
   const int64_t rows = (d->total_q > d->total_kv ? d->total_q : d->total_kv);
@@ -221,8 +232,34 @@ void launch_dq_ds(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
     fa::fa_bwd_dq_ds<false, false><<<grid, block, 0, stream>>>(ma);
 }
 
-// The default takes the stored-dS form where its runs take the 64-key layout and the dS workspace stays
-// within this size (on a GPU with 288 GB of memory); above it, it keeps the recompute form.
+// the stored-dS form's dQ pass over the wide-head kernels' dS pieces, for the Q/K head dim padded as the
+// wide-head kernels pad it (128, 192 or 256); built here, with the MFMA accumulators in VGPRs, so that
+// two workgroups fit each CU
+template <int DQ>
+void launch_dq_dsp_dim(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
+  using C = fa::DqDspCfg<DQ>;
+  const int64_t blocks = (int64_t)((ma.max_seqlen_q + C::BQ - 1) / C::BQ) * ma.H * ma.batch;
+  const dim3 grid((unsigned)(ma.sched ? items : blocks)), block(C::NT);
+  if (ma.d_qk == DQ)
+    ma.causal ? fa::fa_bwd_dq_dsp<DQ, true, true><<<grid, block, 0, stream>>>(ma)
+              : fa::fa_bwd_dq_dsp<DQ, true, false><<<grid, block, 0, stream>>>(ma);
+  else
+    ma.causal ? fa::fa_bwd_dq_dsp<DQ, false, true><<<grid, block, 0, stream>>>(ma)
+              : fa::fa_bwd_dq_dsp<DQ, false, false><<<grid, block, 0, stream>>>(ma);
+}
+void launch_dq_dsp(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
+  const int pq = ma.d_qk <= 128 ? 128 : ma.d_qk <= 192 ? 192 : 256;
+  if (pq == 128)
+    launch_dq_dsp_dim<128>(ma, items, stream);
+  else if (pq == 192)
+    launch_dq_dsp_dim<192>(ma, items, stream);
+  else
+    launch_dq_dsp_dim<256>(ma, items, stream);
+}
+
+// The default takes the stored-dS form where its runs take the 64-key layout, or run the wide-head
+// kernels without a window, and the dS workspace stays within this size (on a GPU with 288 GB of
+// memory); above it, it keeps the recompute form.
 constexpr int64_t kDsDefaultMaxBytes = int64_t(8) << 30;
 
 
@@ -373,7 +410,8 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.cu_q = cu_q;
   ma.cu_kv = cu_kv;
   ma.dq_acc = h->dq_acc;
-  const bool ds_run = h->ds_form && h->layout[causal] == 3;  // the stored-dS form on this run's layout
+  // the stored-dS form on this run's layout (the 64-key one, or the wide-head kernels)
+  const bool ds_run = h->ds_form && (h->ds_pieces || h->layout[causal] == 3);
   ma.ds = ds_run ? h->ds : nullptr;
   ma.ds_nqs = h->ds_nqs;
   ma.ds_nkt = h->ds_nkt;
@@ -405,6 +443,7 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
       h->split ? launch_single_pass<64, true>(ma, causal, stream) : launch_single_pass<64, false>(ma, causal, stream);
   } else if (!planned || h->n_kv_items > 0) {
     ma.head_major = h->dkdv_head_major[causal] ? 1 : 0;
+    if (h->layout[causal] == 3 && !keys64_applies(d)) return FA_BWD_ERR_UNSUPPORTED;  // d = d_v = 128 only
     if (h->layout[causal] == 3)
       launch_dkdv64(ma, h->n_kv_items, stream);
     else
@@ -421,7 +460,9 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   } else if (!planned || h->n_q_items > 0) {
     ma.sched = planned ? h->sched + 2 * h->n_kv_items : nullptr;
     ma.head_major = h->dq_head_major[causal] ? 1 : 0;
-    if (ds_run)
+    if (ds_run && h->ds_pieces)
+      launch_dq_dsp(ma, h->n_q_items, stream);
+    else if (ds_run)
       launch_dq_ds(ma, h->n_q_items, stream);
     else
       ks.dq(ma, h->n_q_items, h->dq_split, stream);
@@ -574,9 +615,11 @@ void configure_layouts(fa_bwd_handle* h, int cus) {
     if (keys64_applies(hd))
       dkdv_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), total64,
                 largest64, fa::Dkdv64Cfg::BN, fa::Dkdv64Cfg::BM);
-    const bool keys64 = h->dkdv_layout == 3 ||
-                        (h->dkdv_layout == 0 && keys64_applies(hd) && hd.window == 0 &&
-                         keys64_balances((double)total64 * (double)per_tile_heads, (double)largest64 * G, cus));
+    // (forced by FA_BWD_ALGO_RECOMPUTE_DQ_64K, or by FA_BWD_ALGO_STORED_DS at head dims of 128: with a head
+    // dim above 128 the stored-dS form runs on the wide-head kernels)
+    const bool keys64 = keys64_applies(hd) && (h->dkdv_layout == 3 ||
+                        (h->dkdv_layout == 0 && hd.window == 0 &&
+                         keys64_balances((double)total64 * (double)per_tile_heads, (double)largest64 * G, cus)));
     h->layout[c] = keys64 ? 3 : four ? 2 : 1;
     if (keys64) {
       total = total64;
@@ -697,9 +740,10 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
     return FA_BWD_ERR_HIP;
   }
   configure_layouts(h, cus);
-  const int64_t ds_need = ds_bytes_of(h->desc, h->ds_nqs, h->ds_nkt);
+  h->ds_pieces = ds_pieces_apply(h->desc);
+  const int64_t ds_need = ds_bytes_of(h->desc, h->ds_pieces, h->ds_nqs, h->ds_nkt);
   h->ds_form = desc->algorithm == FA_BWD_ALGO_STORED_DS ||
-               (desc->algorithm == FA_BWD_ALGO_DEFAULT && (h->layout[0] == 3 || h->layout[1] == 3) &&
+               (desc->algorithm == FA_BWD_ALGO_DEFAULT && (h->ds_pieces || h->layout[0] == 3 || h->layout[1] == 3) &&
                 ds_need >= 0 && ds_need <= kDsDefaultMaxBytes);
   const size_t ds_bytes = h->ds_form ? (size_t)ds_need : 0;
   const size_t stats = (size_t)desc->total_q * desc->num_heads;
@@ -855,7 +899,8 @@ const fa_bwd_desc* fa_bwd_get_desc(const fa_bwd_handle* h) { return h ? &h->desc
 int32_t fa_bwd_dkdv_layout(const fa_bwd_handle* h, int32_t mask) {
   if (!h || mask < FA_BWD_MASK_NONE || mask > FA_BWD_MASK_PADDING_CAUSAL) return -1;
   if (h->single_pass) return h->split ? FA_BWD_ALGO_SPLIT_REDUCE : FA_BWD_ALGO_SINGLE_PASS;
-  if (!pick_kernels(h->desc.head_dim, h->desc.head_dim_v).two_layouts) return FA_BWD_ALGO_RECOMPUTE_DQ;
+  if (!pick_kernels(h->desc.head_dim, h->desc.head_dim_v).two_layouts)  // wide heads: one layout
+    return h->ds_form ? FA_BWD_ALGO_STORED_DS : FA_BWD_ALGO_RECOMPUTE_DQ;
   const bool causal = mask == FA_BWD_MASK_CAUSAL || mask == FA_BWD_MASK_PADDING_CAUSAL;
   if (h->ds_form && h->layout[causal] == 3) return FA_BWD_ALGO_STORED_DS;
   switch (h->layout[causal]) {

@@ -237,9 +237,20 @@ struct MainArgs {
   const int* sched;  // recompute kernels: (tile, sequence * heads + head) per workgroup, or null (dense grid)
   int head_major;    // recompute kernels, dense grid, (K/V) heads x sequences a multiple of 8: each XCD
                      // takes the tiles of one (sequence, head) at a time
-  bf16* ds;          // stored-dS form: dS blocks of 32 q rows x 256 keys, [sequence][head][ds_nqs][ds_nkt]
-  int ds_nqs, ds_nkt;  // 32-row q steps and 256-key kv tiles of the longest sequences
+  bf16* ds;          // stored-dS form: dS blocks of 32 q rows x 256 keys (64-key dK/dV kernel) or pieces of
+                     // 32 q rows x 32 keys (wide-head kernels), [sequence][head][ds_nkt][ds_nqs]
+  int ds_nqs, ds_nkt;  // 32-row q steps, and 256-key (blocks) or 32-key (pieces) kv tiles, of the longest
+                       // sequences
 };
+
+// Stored-dS form of the wide-head kernels: one dS piece holds a 32-row q step against a 32-key tile,
+// 2 KB of bf16 in the order a wave's lanes hold the values after the dK/dV kernel's softmax (half s2 of
+// 1 KB holds, at lane c + 32 hh, the 16 bytes of dsk[s2]). Piece (t, kt) of (sequence b, query head h)
+// starts at element ds_piece(b * H + h, kt, t).
+constexpr int kDsPiece = 32 * 32;
+__device__ __forceinline__ int64_t ds_piece(const MainArgs& a, int hb, int kt, int t) {
+  return (((int64_t)hb * a.ds_nkt + kt) * a.ds_nqs + t) * kDsPiece;
+}
 
 // Splits of the split-and-reduce form: workgroups per (head, sequence), each with its own fp32 dQ
 // buffer; split s takes the kv tiles s, s + kSplits, ...
@@ -640,7 +651,8 @@ struct DkdvCfg {
 // combine their partial sums through LDS (the M-tile 0 wave finishes dV, the other dK). Wider heads,
 // where both accumulators of a wave would not fit its registers next to the K and V fragments: the
 // waves of a group swap P and dS through LDS each step, and the M-tile 0 wave accumulates dV over
-// both M-tiles, the other dK.
+// both M-tiles, the other dK. Wide heads without a window, when a.ds is set: each wave also stores its
+// step's dS as a piece of the stored-dS form (ds_piece), non-temporal (read once, by the dQ pass).
 template <int DQ, int DV, bool CAUSAL, bool WINDOW, bool EXACT, int NMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(DkdvCfg<DQ, DV, NMT>::NT, DkdvCfg<DQ, DV, NMT>::NT),
                           amdgpu_waves_per_eu(DkdvCfg<DQ, DV, NMT>::WPE, DkdvCfg<DQ, DV, NMT>::WPE)))
@@ -972,6 +984,16 @@ void fa_bwd_dkdv(MainArgs a) {
     }
     gemm1(buf, s, dp);
     softmax(sp, buf, s, dp, pk, dsk);
+    if constexpr (C::WIDE && !WINDOW) {
+      if (a.ds) {  // this wave's piece of the step: 32-row q step t, 32-key tile kt
+        const int t = step_tile(sp) * C::NMT + mt, kt = tile * NG + grp;
+        if (t < a.ds_nqs && kt < a.ds_nkt) {  // inside the workspace (lengths within the maxima)
+          bf16* pc = a.ds + ds_piece(a, b * a.H + step_head(sp), kt, t) + lane * 8;
+          __builtin_nontemporal_store(dsk[0], (bf16x8*)pc);
+          __builtin_nontemporal_store(dsk[1], (bf16x8*)(pc + 512));
+        }
+      }
+    }
     if constexpr (C::WIDE)
       gemm2_swap(buf, pk, dsk);
     else

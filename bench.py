@@ -69,7 +69,7 @@ ALGORITHM_NAMES = {1: "single-pass (dQ atomics)",
                    4: "recompute (dK/dV kernel in eight-wave workgroups + dQ kernel)",
                    5: "recompute (dK/dV kernel in four-wave workgroups + dQ kernel)",
                    6: "recompute (dK/dV kernel with 64 keys per wave + dQ kernel)",
-                   7: "stored dS (dK/dV kernel with 64 keys per wave writes dS; dQ = dS K pass)"}
+                   7: "stored dS (the dK/dV kernel writes dS; dQ = dS K pass)"}
 # the dK/dV layout a handle takes (fa_bwd_dkdv_layout's algorithm codes)
 LAYOUT_NAMES = {1: "none (single-pass form)", 3: "none (single-pass form)",
                 2: "one layout (heads wider than 128)",
@@ -89,7 +89,9 @@ def kernel_share(algorithm: int, d: int, dv: int, layout: int = 0) -> dict:
     if algorithm == 3:
         return {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_split_reduce": 0.0}
     if algorithm == 7:  # dK/dV kernel: S, dP, dV, dK (and dS stored); the dS pass: dQ
-        return {"fa_bwd_pre": 0.0, "fa_bwd_dkdv64": (2 * d + 2 * dv) / total, "fa_bwd_dq_ds": d / total}
+        wide = d > 128 or dv > 128  # the wide-head kernels store dS pieces, read by their own pass
+        return {"fa_bwd_pre": 0.0, "fa_bwd_dkdv" if wide else "fa_bwd_dkdv64": (2 * d + 2 * dv) / total,
+                "fa_bwd_dq_dsp" if wide else "fa_bwd_dq_ds": d / total}
     # dK/dV kernel: S, dP, dV, dK; dQ kernel: S and dP again, dQ
     dkdv = "fa_bwd_dkdv64" if layout == 6 else "fa_bwd_dkdv"
     return {"fa_bwd_pre": 0.0, dkdv: (2 * d + 2 * dv) / total, "fa_bwd_dq": (2 * d + dv) / total}
@@ -523,7 +525,8 @@ def main():
               "total_tokens": tq, "mask": MASK_NAMES[inp["mask"]], "seed": inp["seed"],
               "algorithmic_flops": flops,
               "algorithm": ALGORITHM_NAMES[algo_used],
-              "dkdv_layout": LAYOUT_NAMES[layout],
+              "dkdv_layout": ("one layout (heads wider than 128), dS stored"
+                              if layout == 7 and max(d, inp["v"].shape[2]) > 128 else LAYOUT_NAMES[layout]),
               "schedule": "host longest-first plan" if args.plan else "dense grid"}
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -61,8 +61,9 @@ typedef enum {
  * agree within the fp32 rounding of the accumulation order. */
 typedef enum {
   FA_BWD_ALGO_DEFAULT = 0,      /* the faster form on this GPU: FA_BWD_ALGO_STORED_DS where runs take the
-                                   64-key layout (head dims of 128, grids that balance) and its
-                                   dS workspace is at most 8 GiB, else FA_BWD_ALGO_RECOMPUTE_DQ */
+                                   64-key layout (head dims of 128, no window, grids that balance) or
+                                   the wide-head kernels (a head dim above 128, no window) and its dS
+                                   workspace is at most 8 GiB, else FA_BWD_ALGO_RECOMPUTE_DQ */
   FA_BWD_ALGO_SINGLE_PASS = 1,  /* the article's single-pass structure: one main kernel forms the dK, dV and
                                    dQ contributions of every (q tile, kv tile) pair; dQ partial sums are
                                    added to an fp32 workspace with global atomics (summation order not
@@ -93,13 +94,16 @@ typedef enum {
                                    wave holding 64 keys and their dK, dV sums, 32-row q steps; head
                                    dims of exactly 128 (else FA_BWD_ERR_UNSUPPORTED), with or without
                                    a window */
-  FA_BWD_ALGO_STORED_DS = 7        /* the 64-key kv-outer kernel also writes dS (bf16) to a workspace, and
+  FA_BWD_ALGO_STORED_DS = 7        /* the kv-outer kernel also writes dS (bf16) to a workspace, and
                                    dQ = scale * dS K (SK-16 article, section 3.1, step 8) runs as a
                                    q-outer pass over it instead of forming S and dP a second time.
-                                   Workspace: batch * num_heads * ceil(max_seqlen_q / 32) *
-                                   ceil(max_seqlen_kv / 256) blocks of 16 KiB. Deterministic (every
-                                   output row has one owner); same restrictions as
-                                   FA_BWD_ALGO_RECOMPUTE_DQ_64K */
+                                   Head dims of exactly 128: the 64-key kernel, with or without a
+                                   window; workspace batch * num_heads * ceil(max_seqlen_q / 32) *
+                                   ceil(max_seqlen_kv / 256) blocks of 16 KiB. A head dim above 128
+                                   (the wide-head kernels), no window: the same bytes as pieces of
+                                   32 x 32 (2 KiB). Other head dims, or a window with a head dim
+                                   above 128: FA_BWD_ERR_UNSUPPORTED. Deterministic (every output
+                                   row has one owner) */
 } fa_bwd_algo;
 
 typedef enum {

@@ -87,6 +87,9 @@ def _create(**kw):
     (dict(algorithm=6, head_dim_v=64), B.FA_BWD_ERR_UNSUPPORTED),
     (dict(algorithm=7, head_dim=64), B.FA_BWD_ERR_UNSUPPORTED),                 # stored dS: the same
     (dict(algorithm=7, head_dim=128, head_dim_v=64, window=16), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(algorithm=7, head_dim=96), B.FA_BWD_ERR_UNSUPPORTED),                 # or one above 128, no window
+    (dict(algorithm=7, head_dim=256, window=16), B.FA_BWD_ERR_UNSUPPORTED),
+    (dict(algorithm=7, head_dim=64, head_dim_v=192, window=1), B.FA_BWD_ERR_UNSUPPORTED),
     # stored dS: a dS workspace past 2^47 bytes (here 2^24 x 2^21 blocks of 16 KiB per head)
     (dict(algorithm=7, max_seqlen_q=1 << 29, max_seqlen_kv=1 << 29, total_q=1 << 29, total_kv=1 << 29),
      B.FA_BWD_ERR_UNSUPPORTED),

@@ -1,4 +1,5 @@
-"""GPU parity of the recompute backward and of the forward over head dims other than 64 and 128:
+"""GPU parity of the recompute backward, of the stored-dS form where it applies (a head dim above 128,
+no window) and of the forward over head dims other than 64 and 128:
 any multiple of 8 up to 256, and a value head dim (V, O, dO, dV) that differs from the query/key
 one (latent attention). Every valid row is compared with the fp64 oracle on the same seeded inputs,
 with the tolerance of the other parity tests; rows outside every sequence must be exactly zero.
@@ -55,9 +56,17 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("algo", [B.FA_BWD_ALGO_RECOMPUTE_DQ_8W, B.FA_BWD_ALGO_RECOMPUTE_DQ_4W], ids=["8w", "4w"])
+def _wide_stored_ds(case):
+    """The stored-dS form runs on the wide-head kernels: a head dim above 128 and no window."""
+    return max(case.head_dim, case.head_dim_v or case.head_dim) > 128 and case.window == 0
+
+
+@pytest.mark.parametrize("algo", [B.FA_BWD_ALGO_RECOMPUTE_DQ_8W, B.FA_BWD_ALGO_RECOMPUTE_DQ_4W,
+                                  B.FA_BWD_ALGO_STORED_DS], ids=["8w", "4w", "storedds"])
 @pytest.mark.parametrize("case", CASES, ids=[c.name for c in CASES])
 def test_parity_head_dims(case, algo):
+    if algo == B.FA_BWD_ALGO_STORED_DS and not _wide_stored_ds(case):
+        pytest.skip("the stored-dS form at these head dims needs one above 128 and no window")
     inp = I.make(case)
     dv = case.head_dim_v or case.head_dim
     print(f"[headdim] {case.name}: d={case.head_dim} d_v={dv} H={case.heads} H_kv={inp['k'].shape[1]} "
@@ -90,6 +99,23 @@ def test_forward_head_dims(case):
     assert np.all(o[~valid] == 0) and np.all(m[~valid] == 0) and np.all(l[~valid] == 1)
     dm, dlse = check_forward(inp, (o[valid], m[valid], l[valid]), (ro[valid], rm[valid], rl[valid]))
     print(f"[headdim-forward] {case.name}: m err {dm:.2e} lse err {dlse:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["mla_192_128_causal", "d256_gqa_causal", "mla_184_256_padded", "d232_causal",
+                                  "mla_128_176_none"])
+def test_wide_stored_ds_matches_recompute(name):
+    """The wide-head stored-dS form runs the recompute form's dK/dV kernel with the dS pieces stored: its dK,
+    dV equal the recompute form's bitwise; its dQ sums the same bf16 dS values in another kernel, so it
+    agrees within the tolerance. Repeated runs are bitwise identical."""
+    inp = I.make(next(c for c in CASES if c.name == name))
+    o, m, l = P.oracle_stats(inp)
+    a = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_RECOMPUTE_DQ)
+    b = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_STORED_DS)
+    c = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_STORED_DS)
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]), "dk, dv differ from the recompute form"
+    P.assert_close("dq", b[0].numpy(), a[0].numpy().astype(np.float64))
+    for x, y in zip(b, c):
+        assert torch.equal(x, y)
 
 
 def test_wide_head_dims_bitwise_reproducible():

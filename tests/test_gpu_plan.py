@@ -49,9 +49,12 @@ def _run(op, inp, t, o, m, l):
                                   B.FA_BWD_ALGO_STORED_DS], ids=["default", "4w", "64k", "storedds"])
 @pytest.mark.parametrize("case", CASES, ids=[c.name for c in CASES])
 def test_planned_equals_dense_bitwise(case, algo):
-    if algo in (B.FA_BWD_ALGO_RECOMPUTE_DQ_64K, B.FA_BWD_ALGO_STORED_DS) and not (
-            case.head_dim == 128 and case.head_dim_v in (0, 128)):
-        pytest.skip("the 64-key layout (and the stored-dS form) needs head dims of 128")
+    d128 = case.head_dim == 128 and case.head_dim_v in (0, 128)
+    wide = max(case.head_dim, case.head_dim_v or case.head_dim) > 128 and case.window == 0
+    if algo == B.FA_BWD_ALGO_RECOMPUTE_DQ_64K and not d128:
+        pytest.skip("the 64-key layout needs head dims of 128")
+    if algo == B.FA_BWD_ALGO_STORED_DS and not (d128 or wide):
+        pytest.skip("the stored-dS form needs head dims of 128, or one above 128 and no window")
     inp = I.make(case)
     print(f"[plan] {case.name}: lengths {inp['seqlens_q']} mask {case.mask} algorithm {algo}", flush=True)
     dev = torch.device("cuda")
