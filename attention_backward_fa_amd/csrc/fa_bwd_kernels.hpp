@@ -652,7 +652,8 @@ struct DkdvCfg {
 // where both accumulators of a wave would not fit its registers next to the K and V fragments: the
 // waves of a group swap P and dS through LDS each step, and the M-tile 0 wave accumulates dV over
 // both M-tiles, the other dK. Wide heads without a window, when a.ds is set: each wave also stores its
-// step's dS as a piece of the stored-dS form (ds_piece), non-temporal (read once, by the dQ pass).
+// step's dS as a piece of the stored-dS form (ds_piece), non-temporal (read once, by the dQ pass), at the
+// start of the next step, so that the stores complete before the step's closing wait for its transfers.
 template <int DQ, int DV, bool CAUSAL, bool WINDOW, bool EXACT, int NMT>
 __global__ __attribute__((amdgpu_flat_work_group_size(DkdvCfg<DQ, DV, NMT>::NT, DkdvCfg<DQ, DV, NMT>::NT),
                           amdgpu_waves_per_eu(DkdvCfg<DQ, DV, NMT>::WPE, DkdvCfg<DQ, DV, NMT>::WPE)))
@@ -765,15 +766,13 @@ void fa_bwd_dkdv(MainArgs a) {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + (q_start + i0) * rsq + (int64_t)hq * dqk, (int64_t)rows * rsqb);
     const __amdgpu_buffer_rsrc_t rd =
         make_rsrc(a.dout + (q_start + i0) * rsd + (int64_t)hq * dvd, (int64_t)rows * rsdb);
+    // untracked (dma16_untracked): the step's LDS reads of the other buffer must not wait for these
+    // transfers; wait_tiles and the step's barrier order them before buffer bi is read
     auto dma_q = [&](int jj, int j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rq, (__attribute__((address_space(3))) void*)(smem + C::OFF_Q + bi * C::TQ_BYTES + 1024 * j), 16,
-          offq[jj], 0, 0, 0);
+      dma16_untracked(rq, offq[jj], (__attribute__((address_space(3))) void*)(smem + C::OFF_Q + bi * C::TQ_BYTES + 1024 * j));
     };
     auto dma_d = [&](int jj, int j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rd, (__attribute__((address_space(3))) void*)(smem + C::OFF_DO + bi * C::TD_BYTES + 1024 * j), 16,
-          offd[jj], 0, 0, 0);
+      dma16_untracked(rd, offd[jj], (__attribute__((address_space(3))) void*)(smem + C::OFF_DO + bi * C::TD_BYTES + 1024 * j));
     };
 #pragma unroll
     for (int jj = 0; jj < (NJQ > NJD ? NJQ : NJD); ++jj) {
@@ -968,7 +967,20 @@ void fa_bwd_dkdv(MainArgs a) {
 
   // all waves in step: tile sp + 1 loads while step sp runs; one barrier per step
   f32x16 s, dp;
-  bf16x8 pk[2], dsk[2];
+  bf16x8 pk[2], dsk[2], dsk_prev[2];
+  // this wave's stored-dS piece of step st: 32-row q step t, 32-key tile kt (wide heads, no window)
+  auto store_piece = [&](int st, const bf16x8 (&d)[2]) {
+    if constexpr (C::WIDE && !WINDOW) {
+      if (a.ds) {
+        const int t = step_tile(st) * C::NMT + mt, kt = tile * NG + grp;
+        if (t < a.ds_nqs && kt < a.ds_nkt) {  // inside the workspace (lengths within the maxima)
+          bf16* pc = a.ds + ds_piece(a, b * a.H + step_head(st), kt, t) + lane * 8;
+          __builtin_nontemporal_store(d[0], (bf16x8*)pc);
+          __builtin_nontemporal_store(d[1], (bf16x8*)(pc + 512));
+        }
+      }
+    }
+  };
   if (n_steps > 0) {
     issue_tile(0, 0);
     store_stats(0, load_stats(0));
@@ -982,17 +994,12 @@ void fa_bwd_dkdv(MainArgs a) {
       issue_tile(sp + 1, buf ^ 1);
       st_next = load_stats(sp + 1);
     }
+    if (sp > 0) store_piece(sp - 1, dsk_prev);
     gemm1(buf, s, dp);
     softmax(sp, buf, s, dp, pk, dsk);
     if constexpr (C::WIDE && !WINDOW) {
-      if (a.ds) {  // this wave's piece of the step: 32-row q step t, 32-key tile kt
-        const int t = step_tile(sp) * C::NMT + mt, kt = tile * NG + grp;
-        if (t < a.ds_nqs && kt < a.ds_nkt) {  // inside the workspace (lengths within the maxima)
-          bf16* pc = a.ds + ds_piece(a, b * a.H + step_head(sp), kt, t) + lane * 8;
-          __builtin_nontemporal_store(dsk[0], (bf16x8*)pc);
-          __builtin_nontemporal_store(dsk[1], (bf16x8*)(pc + 512));
-        }
-      }
+      dsk_prev[0] = dsk[0];
+      dsk_prev[1] = dsk[1];
     }
     if constexpr (C::WIDE)
       gemm2_swap(buf, pk, dsk);
@@ -1002,6 +1009,7 @@ void fa_bwd_dkdv(MainArgs a) {
     wait_tiles();
     __syncthreads();
   }
+  if (n_steps > 0) store_piece(n_steps - 1, dsk_prev);  // the last step's piece
 
   // write-back of rows 32 grp .. 32 grp + 31, features below the head dim, in bf16
   auto store_dv = [&](const f32x16* acc) {
