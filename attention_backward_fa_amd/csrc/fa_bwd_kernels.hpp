@@ -632,9 +632,15 @@ struct DkdvCfg {
   static constexpr int OFF_Q = OFF_V + V_BYTES;               // Q [2][BM][QSQ]
   static constexpr int OFF_DO = OFF_Q + 2 * TQ_BYTES;         // dO [2][BM][QSV]
   static constexpr int OFF_ST = OFF_DO + 2 * TD_BYTES;        // [2 buffers][lse2, D][BM] fp32
-  static constexpr int OFF_X = OFF_ST + 4 * BM * 4;           // wide: [wave][lane] 2 bf16x8 of P or dS
+  // wide heads: the two waves of a row group split the second GEMMs' output tiles, as many each; the
+  // M-tile 0 wave takes dV tiles [0, NTV - BY) and dK tiles [NTQ - BX, NTQ), the other the rest
+  static constexpr int BX = WIDE && NTQ > NTV ? (NTQ - NTV) / 2 : 0;
+  static constexpr int BY = WIDE && NTV > NTQ ? (NTV - NTQ) / 2 : 0;
+  static constexpr bool BAL = BX > 0 || BY > 0;      // each wave needs both P and dS of both M-tiles
+  static constexpr int NTW = WIDE ? (NTQ + NTV) / 2 : 1;  // output tiles per wave
+  static constexpr int OFF_X = OFF_ST + 4 * BM * 4;  // wide: [wave][lane] 2 bf16x8 of P or dS (4: both)
   static constexpr int PART_BYTES = NMT == 2 && !WIDE ? NG * (NTQ + NTV) * 64 * 64 : 0;  // partial dK, then dV
-  static constexpr int TILE_END = OFF_X + (WIDE ? NW * 64 * 32 : 0);
+  static constexpr int TILE_END = OFF_X + (WIDE ? NW * 64 * (BAL ? 64 : 32) : 0);
   // the end-of-kernel exchange of partial sums reuses the whole allocation
   static constexpr int LDS_BYTES = TILE_END > PART_BYTES ? TILE_END : PART_BYTES;
   static_assert(DQ % 32 == 0 && DV % 32 == 0 && DQ <= 256 && DV <= 256, "padded head dims");
@@ -803,14 +809,24 @@ void fa_bwd_dkdv(MainArgs a) {
   };
 
   // heads up to 128: partial dV and dK / scale of rows 32 grp .. +31 over this M-tile; wider heads:
-  // acc_w holds dV (M-tile 0 wave) or dK / scale (M-tile 1 wave) of those rows over whole steps
-  f32x16 acc_v[C::WIDE ? 1 : C::NTV], acc_k[C::WIDE ? 1 : C::NTQ], acc_w[C::WIDE ? C::NTM : 1];
+  // acc_w holds this wave's NTW output tiles of those rows over whole steps (wide_tile)
+  f32x16 acc_v[C::WIDE ? 1 : C::NTV], acc_k[C::WIDE ? 1 : C::NTQ], acc_w[C::NTW];
 #pragma unroll
   for (int nt = 0; nt < C::NTV; ++nt) acc_v[C::WIDE ? 0 : nt] = f32x16{};
 #pragma unroll
   for (int nt = 0; nt < C::NTQ; ++nt) acc_k[C::WIDE ? 0 : nt] = f32x16{};
 #pragma unroll
-  for (int nt = 0; nt < C::NTM; ++nt) acc_w[C::WIDE ? nt : 0] = f32x16{};
+  for (int i = 0; i < C::NTW; ++i) acc_w[i] = f32x16{};
+  // wide heads: output tile i of this wave is dV tile nt (is_v) or dK tile nt (wave-uniform)
+  auto wide_tile = [&](int i, bool& is_v, int& nt) {
+    if (mt == 0) {
+      is_v = i < C::NTV - C::BY;
+      nt = is_v ? i : C::NTQ - C::BX + (i - (C::NTV - C::BY));
+    } else {
+      is_v = i >= C::NTQ - C::BX;
+      nt = is_v ? C::NTV - C::BY + (i - (C::NTQ - C::BX)) : i;
+    }
+  };
 
   const int arowq = (32 * mt + tile_row(c)) * QSQ + 8 * hh;  // A rows: this M-tile's q rows
   const int arowd = (32 * mt + tile_row(c)) * QSV + 8 * hh;
@@ -922,31 +938,49 @@ void fa_bwd_dkdv(MainArgs a) {
   // wave needs the partner's P for dV, the other the partner's dS for dK), then one GEMM over the
   // step's 64 q rows, k-steps in row order
   auto gemm2_swap = [&](int bi, const bf16x8* pk, const bf16x8* dsk) {
+    constexpr int NX = C::BAL ? 4 : 2;  // bf16x8 each wave publishes per lane
     bf16x8* xs = (bf16x8*)(smem + C::OFF_X);
     const int partner = grp + NG * (1 - mt);
-    xs[(w * 64 + lane) * 2] = mt == 0 ? dsk[0] : pk[0];
-    xs[(w * 64 + lane) * 2 + 1] = mt == 0 ? dsk[1] : pk[1];
+    if constexpr (C::BAL) {  // both waves need P and dS of both M-tiles
+      xs[(w * 64 + lane) * NX] = pk[0];
+      xs[(w * 64 + lane) * NX + 1] = pk[1];
+      xs[(w * 64 + lane) * NX + 2] = dsk[0];
+      xs[(w * 64 + lane) * NX + 3] = dsk[1];
+    } else {  // the M-tile 0 wave forms dV (needs P), the other dK (needs dS)
+      xs[(w * 64 + lane) * NX] = mt == 0 ? dsk[0] : pk[0];
+      xs[(w * 64 + lane) * NX + 1] = mt == 0 ? dsk[1] : pk[1];
+    }
     __syncthreads();
-    bf16x8 am[4];  // A operand of k-step 2 u + s2: M-tile u, its k-step s2
+    // A operands of k-step 2 u + s2 (M-tile u, its k-step s2): P (for dV tiles) and dS (for dK tiles)
+    bf16x8 ap[4], ad[4];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-      const bf16x8 own = mt == 0 ? pk[s2] : dsk[s2];
-      const bf16x8 other = xs[(partner * 64 + lane) * 2 + s2];
-      am[s2] = mt == 0 ? own : other;
-      am[2 + s2] = mt == 0 ? other : own;
+      bf16x8 op_, od_;
+      if constexpr (C::BAL) {
+        op_ = xs[(partner * 64 + lane) * NX + s2];
+        od_ = xs[(partner * 64 + lane) * NX + 2 + s2];
+      } else {
+        op_ = od_ = xs[(partner * 64 + lane) * NX + s2];
+      }
+      ap[s2] = mt == 0 ? pk[s2] : op_;
+      ap[2 + s2] = mt == 0 ? op_ : pk[s2];
+      ad[s2] = mt == 0 ? dsk[s2] : od_;
+      ad[2 + s2] = mt == 0 ? od_ : dsk[s2];
     }
-    const int qs = mt == 0 ? QSV : QSQ;  // B: dO (for dV) or Q (for dK) rows of the step
-    const bf16* bsrc = mt == 0 ? tile_do(bi) : tile_q(bi);
-    const int ntw = mt == 0 ? C::NTV : C::NTQ;
-    const int brow0 = (hh + 4 * (gi >> 2)) * qs + 16 * (g & 1) + 4 * (gi & 3);
-    constexpr int NB = 4 * C::NTM, PF = 2;
+    // B: dO rows (for dV tiles) or Q rows (for dK tiles) of the step, read transposed
+    const int browv = (hh + 4 * (gi >> 2)) * QSV + 16 * (g & 1) + 4 * (gi & 3);
+    const int browk = (hh + 4 * (gi >> 2)) * QSQ + 16 * (g & 1) + 4 * (gi & 3);
+    constexpr int NB = 4 * C::NTW, PF = 2;
     bf16x8 bw[NB];
     auto ld = [&](int i) {
-      const int ksi = i / C::NTM, nt = i % C::NTM;
-      if (nt < ntw) {
-        const int o = brow0 + 16 * ksi * qs + 32 * nt;
-        bw[i] = concat(lds_read_tr4(bsrc + o), lds_read_tr4(bsrc + o + 2 * qs));
-      }
+      const int ksi = i / C::NTW;
+      bool is_v;
+      int nt;
+      wide_tile(i % C::NTW, is_v, nt);
+      const int qs = is_v ? QSV : QSQ;
+      const bf16* bsrc = is_v ? tile_do(bi) : tile_q(bi);
+      const int o = (is_v ? browv : browk) + 16 * ksi * qs + 32 * nt;
+      bw[i] = concat(lds_read_tr4(bsrc + o), lds_read_tr4(bsrc + o + 2 * qs));
     };
 #pragma unroll
     for (int i = 0; i < PF; ++i) ld(i);
@@ -954,8 +988,11 @@ void fa_bwd_dkdv(MainArgs a) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (i + PF < NB) ld(i + PF);
-      const int ksi = i / C::NTM, nt = i % C::NTM;
-      if (nt < ntw) acc_w[C::WIDE ? nt : 0] = mfma32x32x16(am[ksi], bw[i], acc_w[C::WIDE ? nt : 0]);
+      const int ksi = i / C::NTW, t = i % C::NTW;
+      bool is_v;
+      int nt;
+      wide_tile(t, is_v, nt);
+      acc_w[t] = mfma32x32x16(is_v ? ap[ksi] : ad[ksi], bw[i], acc_w[t]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -1041,11 +1078,27 @@ void fa_bwd_dkdv(MainArgs a) {
       }
     }
   };
-  if constexpr (C::WIDE) {
-    if (mt == 0)
-      store_dv(acc_w);
-    else
-      store_dk(acc_w);
+  if constexpr (C::WIDE) {  // this wave's output tiles (wide_tile): dV, and dK = scale * acc
+#pragma unroll
+    for (int i = 0; i < C::NTW; ++i) {
+      bool is_v;
+      int nt;
+      wide_tile(i, is_v, nt);
+      const int dcol = 32 * nt + c;
+      if (dcol >= (is_v ? dvd : dqk)) continue;
+      bf16* dst = is_v ? a.dv : a.dk;
+      const int64_t rs = is_v ? rskv : rskq;
+      const int64_t col = (int64_t)hk * (is_v ? dvd : dqk) + dcol;
+      const float sc = is_v ? 1.f : a.scale;
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int r = kv0 + 32 * grp + 8 * a4 + 4 * hh + bb;
+          if (r < Lk) dst[(kv_start + r) * rs + col] = to_bf16(acc_w[i][4 * a4 + bb] * sc);
+        }
+      }
+    }
   } else if constexpr (C::NMT == 1) {  // each wave holds the whole sums of its keys
     store_dv(acc_v);
     store_dk(acc_k);
