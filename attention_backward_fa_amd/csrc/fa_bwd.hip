@@ -13,7 +13,6 @@
 #include "fa_bwd.h"
 #include "fa_bwd_dkdv64.hpp"
 #include "fa_bwd_dqds.hpp"
-#include "fa_bwd_dqdsp.hpp"
 #include "fa_bwd_launch.hpp"
 
 struct fa_bwd_handle {
@@ -221,15 +220,15 @@ void launch_dkdv64(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
 
 // the stored-dS form's dQ pass: one workgroup per (128-row q tile, head, sequence), as the dQ kernel
 void launch_dq_ds(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
-  using C = fa::DqDsCfg;
+  using C = fa::DqDsCfg<128>;
   const int64_t blocks = (int64_t)((ma.max_seqlen_q + C::BQ - 1) / C::BQ) * ma.H * ma.batch;
   const dim3 grid((unsigned)(ma.sched ? items : blocks)), block(C::NT);
   if (ma.window > 0)
-    fa::fa_bwd_dq_ds<true, true><<<grid, block, 0, stream>>>(ma);
+    fa::fa_bwd_dq_ds<128, true, false, true, true><<<grid, block, 0, stream>>>(ma);
   else if (ma.causal)
-    fa::fa_bwd_dq_ds<true, false><<<grid, block, 0, stream>>>(ma);
+    fa::fa_bwd_dq_ds<128, true, false, true, false><<<grid, block, 0, stream>>>(ma);
   else
-    fa::fa_bwd_dq_ds<false, false><<<grid, block, 0, stream>>>(ma);
+    fa::fa_bwd_dq_ds<128, true, false, false, false><<<grid, block, 0, stream>>>(ma);
 }
 
 // the stored-dS form's dQ pass over the wide-head kernels' dS pieces, for the Q/K head dim padded as the
@@ -237,15 +236,15 @@ void launch_dq_ds(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
 // two workgroups fit each CU
 template <int DQ>
 void launch_dq_dsp_dim(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
-  using C = fa::DqDspCfg<DQ>;
+  using C = fa::DqDsCfg<DQ>;
   const int64_t blocks = (int64_t)((ma.max_seqlen_q + C::BQ - 1) / C::BQ) * ma.H * ma.batch;
   const dim3 grid((unsigned)(ma.sched ? items : blocks)), block(C::NT);
   if (ma.d_qk == DQ)
-    ma.causal ? fa::fa_bwd_dq_dsp<DQ, true, true><<<grid, block, 0, stream>>>(ma)
-              : fa::fa_bwd_dq_dsp<DQ, true, false><<<grid, block, 0, stream>>>(ma);
+    ma.causal ? fa::fa_bwd_dq_ds<DQ, true, true, true, false><<<grid, block, 0, stream>>>(ma)
+              : fa::fa_bwd_dq_ds<DQ, true, true, false, false><<<grid, block, 0, stream>>>(ma);
   else
-    ma.causal ? fa::fa_bwd_dq_dsp<DQ, false, true><<<grid, block, 0, stream>>>(ma)
-              : fa::fa_bwd_dq_dsp<DQ, false, false><<<grid, block, 0, stream>>>(ma);
+    ma.causal ? fa::fa_bwd_dq_ds<DQ, false, true, true, false><<<grid, block, 0, stream>>>(ma)
+              : fa::fa_bwd_dq_ds<DQ, false, true, false, false><<<grid, block, 0, stream>>>(ma);
 }
 void launch_dq_dsp(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
   const int pq = ma.d_qk <= 128 ? 128 : ma.d_qk <= 192 ? 192 : 256;

@@ -1,6 +1,7 @@
-// fa_bwd_dqds.hpp -- dQ of the stored-dS form for head dims of 128: dQ = scale * dS K (step 8 of the
-// per-tile math of the PyPTO-Gym SK-16 article, section 3.1) from the dS blocks the 64-key dK/dV kernel
-// wrote, so that S and dP are not formed a second time.
+// fa_bwd_dqds.hpp -- dQ of the stored-dS form: dQ = scale * dS K (step 8 of the per-tile math of the
+// PyPTO-Gym SK-16 article, section 3.1) from the dS the dK/dV kernel wrote, so that S and dP are not
+// formed a second time: the 64-key kernel's blocks (head dims of 128) or the wide-head kernel's pieces
+// (PIECES, a head dim above 128).
 //
 // A dS block holds one 32-row q step against one 256-key kv tile (16 KB of bf16) in the order the dK/dV
 // kernel's lanes hold the values: piece ((w * 2 + n) * 2 + s2) of 1 KB holds, at lane l = c + 32 hh,
@@ -9,21 +10,28 @@
 // and every load of the reader then covers whole 1 KB runs. Block (t, j) of (sequence b, query head h)
 // sits at ds + (((b H + h) nkt + j) nqs + t) * 8192 elements (a writer workgroup, one kv tile, writes
 // its steps' blocks one after another), for the nqs steps and nkt tiles of the longest sequences;
-// steps and tiles outside those are neither written nor read.
+// steps and tiles outside those are neither written nor read. A dS piece (ds_piece) holds a 32-row q step
+// against a 32-key tile, 2 KB in the order of the wide-head kernel's lanes: half s2 (1 KB) holds, at lane
+// c + 32 hh, the 16 bytes of key c at positions 16 hh + 8 s2 ..+7, the positions standing for query rows
+// as in a block; piece (t, kt) of (sequence b, query head h) starts at element ds_piece(b * H + h, kt, t).
 //
 // One workgroup of four waves per (128-row q tile, head, sequence), two per CU; wave w takes q step
 // 4 * tile + w. Per 64-key step a wave loads its 64 x 32 dS values straight into registers (16 bytes
 // per lane per 32 x 16 piece, in the A-operand layout of an MFMA whose rows are keys), two steps ahead,
 // transposes them with two MFMAs against identity B operands per 32-key tile (exact: one product per
 // output, by 1), and accumulates dQ^T += K^T dS^T with K from an LDS tile, as the recompute form's dQ
-// kernel does.
+// kernel does. Under a causal mask, a wave reading pieces stops at its own diagonal (key tiles kt <= t):
+// the wide-head kernel's steps start at the q step of its 64-key tile's first key, so a piece past a
+// wave's diagonal may not have been written (it holds no visible pair); a block is written whole for
+// every step a kv tile's workgroup runs.
 #pragma once
 #include "fa_bwd_kernels.hpp"
 
 namespace fa {
 
+template <int DQ>
 struct DqDsCfg {
-  static constexpr int D = 128;
+  static constexpr int D = DQ;               // the Q/K head dim, padded to a multiple of 32
   static constexpr int NW = 4, NT = 64 * NW;
   static constexpr int BQ = 32 * NW;         // q rows per workgroup
   static constexpr int BK = 64;              // keys per step
@@ -34,16 +42,20 @@ struct DqDsCfg {
   static constexpr int NTQ = D / 32;         // 32-wide feature tiles of dQ^T
   static constexpr int BLOCK = 256 * 32;     // elements of one dS block
   static constexpr int LDS_BYTES = 2 * TK_BYTES;
+  static_assert(DQ % 32 == 0 && DQ <= 256, "padded head dims");
   static_assert(TK_BYTES % 1024 == 0, "whole 1 KB transfers");
 };
 
-template <bool CAUSAL, bool WINDOW>
-__global__ __attribute__((amdgpu_flat_work_group_size(DqDsCfg::NT, DqDsCfg::NT), amdgpu_waves_per_eu(2, 2)))
+// EXACT: the Q/K head dim equals DQ (else a.d_qk, padded to DQ); PIECES: the wide-head kernel's pieces
+// (no window), else the 64-key kernel's blocks
+template <int DQ, bool EXACT, bool PIECES, bool CAUSAL, bool WINDOW>
+__global__ __attribute__((amdgpu_flat_work_group_size(DqDsCfg<DQ>::NT, DqDsCfg<DQ>::NT), amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_ds(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = DqDsCfg;
+  using C = DqDsCfg<DQ>;
   constexpr int BQ = C::BQ, BK = C::BK, QS = C::QS, D = C::D, NTQ = C::NTQ;
   static_assert(CAUSAL || !WINDOW, "a window implies the causal bound");
+  static_assert(!PIECES || !WINDOW, "pieces are stored without a window");
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   // work item: as the recompute form's dQ kernel (host schedule, head-major per XCD, or tile-major with
@@ -77,16 +89,20 @@ void fa_bwd_dq_ds(MainArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, c = lane & 31, g = lane >> 4, gi = lane & 15;
-  const int64_t rsq = (int64_t)a.H * D, rskq = (int64_t)a.Hk * D;
+  const int dqk = EXACT ? D : a.d_qk;
+  const int64_t rsq = (int64_t)a.H * dqk, rskq = (int64_t)a.Hk * dqk;  // row strides of dQ and of K
   const int rskqb = (int)(rskq * 2);
   const int hk = h / (a.H / a.Hk);
-  const bf16* kb = a.k + kv_start * rskq + (int64_t)hk * D;
+  const bf16* kb = a.k + kv_start * rskq + (int64_t)hk * dqk;
   const int t = qtile * 4 + w;  // this wave's 32-row q step
-  // the wave's dS blocks (one per 256-key kv tile). A step whose rows all lie past the sequence has no
-  // blocks (past the longest sequence, none inside the workspace): its loads read an empty range.
+  // the wave's dS blocks (one per 256-key kv tile) or pieces (one per 32-key tile). A step whose rows
+  // all lie past the sequence has none (past the longest sequence, none inside the workspace): its loads
+  // read an empty range.
   const bool t_rows = 32 * t < Lq && t < a.ds_nqs;
-  const bf16* dsb = a.ds + ((int64_t)hb * a.ds_nkt * a.ds_nqs + (t_rows ? t : 0)) * C::BLOCK;
-  const int64_t tile_stride = (int64_t)a.ds_nqs * C::BLOCK;  // from a kv tile's block to the next's
+  const bf16* dsb = a.ds + (PIECES ? ds_piece(a, hb, 0, t_rows ? t : 0)
+                                   : ((int64_t)hb * a.ds_nkt * a.ds_nqs + (t_rows ? t : 0)) * C::BLOCK);
+  // from a kv tile's block (a key tile's piece) to the next's
+  const int64_t tile_stride = (int64_t)a.ds_nqs * (PIECES ? kDsPiece : C::BLOCK);
 
   // 64-key steps: under a causal mask up to the last row's diagonal (the blocks of those keys were
   // written whole, with zeros where a row does not see a key)
@@ -108,7 +124,7 @@ void fa_bwd_dq_ds(MainArgs a) {
   constexpr int NJ = (C::NDMA_K + C::NW - 1) / C::NW;
   int offk[NJ];
 #pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) offk[jj] = tile_dma_off(w + C::NW * jj, lane, C::CPR, rskqb, D);
+  for (int jj = 0; jj < NJ; ++jj) offk[jj] = tile_dma_off(w + C::NW * jj, lane, C::CPR, rskqb, dqk);
   auto issue_k = [&](int s, int bi) {
     const int j0 = s * BK, rows = s < n_kt ? imin(Lk - j0, BK) : 0;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb + (int64_t)j0 * rskq, (int64_t)rows * rskqb);
@@ -120,21 +136,36 @@ void fa_bwd_dq_ds(MainArgs a) {
     }
   };
   // dS of step s: for key tile m (32 keys) and k-step e (16 positions), this lane's 16 bytes: key
-  // 64 (s % 4) + 32 m + tile_row(c) of block s / 4, positions 16 e + 8 hh ..+7, i.e. lane tile_row(c)
-  // + 32 e of piece ((s % 4) * 2 + m) * 2 + hh. Keys past the sequence, and steps past the last, read
-  // as zeros.
+  // 64 s + 32 m + tile_row(c), positions 16 e + 8 hh ..+7, i.e. lane tile_row(c) + 32 e of piece
+  // ((s % 4) * 2 + m) * 2 + hh of block s / 4, or of half hh of piece (t, 2 s + m). Keys past the
+  // sequence, steps past the last and (pieces) key tiles past the wave's diagonal read as zeros.
   auto load_ds = [&](int s, bf16x8 (&x)[2][2]) {
-    const int j = s >> 2, wp = s & 3;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(dsb + j * tile_stride, t_rows && s < n_kt && j < a.ds_nkt &&
-                                             (!WINDOW || 32 * t <= 256 * j + 254 + a.window) ? C::BLOCK * 2 : 0);
+    if constexpr (PIECES) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const bool key_in = 256 * j + 64 * wp + 32 * m + tile_row(c) < Lk;
+      for (int m = 0; m < 2; ++m) {
+        const int kt = 2 * s + m;
+        const bool live = t_rows && s < n_kt && kt < a.ds_nkt && (!CAUSAL || kt <= t);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(dsb + kt * tile_stride, live ? kDsPiece * 2 : 0);
+        const bool key_in = 32 * kt + tile_row(c) < Lk;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int off = ((((wp * 2 + m) * 2 + hh) * 512) + (tile_row(c) + 32 * e) * 8) * 2;
-        x[m][e] = __builtin_bit_cast(bf16x8, buf_load16(rs, key_in ? off : kOutOfRange));
+        for (int e = 0; e < 2; ++e) {
+          const int off = (hh * 512 + (tile_row(c) + 32 * e) * 8) * 2;
+          x[m][e] = __builtin_bit_cast(bf16x8, buf_load16(rs, key_in ? off : kOutOfRange));
+        }
+      }
+    } else {
+      const int j = s >> 2, wp = s & 3;
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(dsb + j * tile_stride, t_rows && s < n_kt && j < a.ds_nkt &&
+                                               (!WINDOW || 32 * t <= 256 * j + 254 + a.window) ? C::BLOCK * 2 : 0);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const bool key_in = 256 * j + 64 * wp + 32 * m + tile_row(c) < Lk;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int off = ((((wp * 2 + m) * 2 + hh) * 512) + (tile_row(c) + 32 * e) * 8) * 2;
+          x[m][e] = __builtin_bit_cast(bf16x8, buf_load16(rs, key_in ? off : kOutOfRange));
+        }
       }
     }
   };
@@ -220,11 +251,12 @@ void fa_bwd_dq_ds(MainArgs a) {
   const int p = c;
   const int qi = 32 * t + tile_row(8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3));
   if (qi < Lq) {
-    bf16* dst = a.dq + (q_start + qi) * rsq + (int64_t)h * D + 4 * hh;
+    bf16* dst = a.dq + (q_start + qi) * rsq + (int64_t)h * dqk + 4 * hh;
 #pragma unroll
     for (int nt = 0; nt < NTQ; ++nt) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
+        if (32 * nt + 8 * a4 + 4 * hh >= dqk) continue;  // head dims are multiples of 8
         const bf16x4 v4 = {to_bf16(acc[nt][4 * a4] * a.scale), to_bf16(acc[nt][4 * a4 + 1] * a.scale),
                            to_bf16(acc[nt][4 * a4 + 2] * a.scale), to_bf16(acc[nt][4 * a4 + 3] * a.scale)};
         *(bf16x4*)(dst + 32 * nt + 8 * a4) = v4;

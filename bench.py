@@ -89,9 +89,9 @@ def kernel_share(algorithm: int, d: int, dv: int, layout: int = 0) -> dict:
     if algorithm == 3:
         return {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_split_reduce": 0.0}
     if algorithm == 7:  # dK/dV kernel: S, dP, dV, dK (and dS stored); the dS pass: dQ
-        wide = d > 128 or dv > 128  # the wide-head kernels store dS pieces, read by their own pass
+        wide = d > 128 or dv > 128  # the wide-head kernels store dS pieces (the dS pass reads either form)
         return {"fa_bwd_pre": 0.0, "fa_bwd_dkdv" if wide else "fa_bwd_dkdv64": (2 * d + 2 * dv) / total,
-                "fa_bwd_dq_dsp" if wide else "fa_bwd_dq_ds": d / total}
+                "fa_bwd_dq_ds": d / total}
     # dK/dV kernel: S, dP, dV, dK; dQ kernel: S and dP again, dQ
     dkdv = "fa_bwd_dkdv64" if layout == 6 else "fa_bwd_dkdv"
     return {"fa_bwd_pre": 0.0, dkdv: (2 * d + 2 * dv) / total, "fa_bwd_dq": (2 * d + dv) / total}
