@@ -40,7 +40,7 @@ FA_BWD_MASK_PADDING_CAUSAL = 3
 
 # every symbol include/fa_bwd.h declares
 EXPORTED = ("fa_bwd_create", "fa_bwd_run", "fa_bwd_run_lse", "fa_bwd_run_noalloc", "fa_fwd_run", "fa_bwd_plan",
-            "fa_bwd_destroy", "fa_bwd_status_string", "fa_bwd_get_desc", "fa_bwd_dkdv_layout",
+            "fa_bwd_destroy", "fa_bwd_status_string", "fa_bwd_get_desc", "fa_bwd_dkdv_layout", "fa_bwd_dq_form",
             "fa_bwd_profile_enable", "fa_bwd_profile_collect")
 
 
@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_get_desc.restype = ctypes.POINTER(FaBwdDesc)
     lib.fa_bwd_dkdv_layout.argtypes = [vp, i32]
     lib.fa_bwd_dkdv_layout.restype = i32
+    lib.fa_bwd_dq_form.argtypes = [vp, i32]
+    lib.fa_bwd_dq_form.restype = i32
     lib.fa_bwd_profile_enable.argtypes = [vp, i32]
     lib.fa_bwd_profile_enable.restype = i32
     lib.fa_bwd_profile_collect.argtypes = [vp, ctypes.POINTER(f32), i32, ctypes.POINTER(i32)]
@@ -128,6 +130,12 @@ def fa_bwd_get_desc(handle) -> FaBwdDesc:
 def fa_bwd_dkdv_layout(handle, mask: int) -> int:
     """The algorithm code of the dK/dV layout runs under `mask` take on this handle (-1: invalid)."""
     return int(load_library().fa_bwd_dkdv_layout(handle, int(mask)))
+
+
+def fa_bwd_dq_form(handle, mask: int) -> int:
+    """The algorithm code of the way runs under `mask` form dQ on this handle (stored dS or recompute;
+    -1: invalid)."""
+    return int(load_library().fa_bwd_dq_form(handle, int(mask)))
 
 
 def fa_bwd_destroy(handle) -> None:
@@ -333,6 +341,9 @@ class FaBwd:
 
     def dkdv_layout(self, mask):
         return fa_bwd_dkdv_layout(self.handle, mask)
+
+    def dq_form(self, mask):
+        return fa_bwd_dq_form(self.handle, mask)
 
     def plan(self, cu_seqlens_q, cu_seqlens_kv, mask):
         fa_bwd_plan(self.handle, cu_seqlens_q, cu_seqlens_kv, mask)

@@ -42,11 +42,13 @@ struct fa_bwd_handle {
   bool dq_head_major[2], dkdv_head_major[2];
   // the dQ kernel in two key groups per workgroup (dq_key_split)
   bool dq_split;
-  // stored-dS form: the 64-key dK/dV kernel writes dS blocks, or the wide-head kernel dS pieces (ds_pieces),
-  // and the dQ pass reads them
-  bool ds_form, ds_pieces;
+  // stored-dS form: the dK/dV kernel writes dS, and the dQ pass reads it, in the format ds_fmt gives for
+  // runs without and with a causal bound (kDsNone, kDsBlocks: the 64-key kernel's 32 x 256 blocks,
+  // kDsPieces: the wide-head kernel's 32 x 32 pieces); ds_form: some run takes it
+  bool ds_form;
+  int32_t ds_fmt[2];
   fa::bf16* ds;
-  int32_t ds_nqs, ds_nkt;
+  int32_t ds_nqs, ds_nkt_blocks, ds_nkt_pieces;
 };
 
 namespace {
@@ -126,6 +128,7 @@ int threads_per_row(int d_qk, int d_v) {
 
 // The stored-dS form of the wide-head kernels (a head dim above 128, no window) stores 32 x 32 pieces;
 // at head dims of exactly 128 the form runs on the 64-key layout, which stores 32 x 256 blocks.
+constexpr int32_t kDsNone = 0, kDsBlocks = 1, kDsPieces = 2;
 bool ds_pieces_apply(const fa_bwd_desc& d) {
   const int32_t dv = d.head_dim_v == 0 ? d.head_dim : d.head_dim_v;
   return (d.head_dim > 128 || dv > 128) && d.window == 0;
@@ -409,11 +412,14 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   ma.cu_q = cu_q;
   ma.cu_kv = cu_kv;
   ma.dq_acc = h->dq_acc;
-  // the stored-dS form on this run's layout (the 64-key one, or the wide-head kernels)
-  const bool ds_run = h->ds_form && (h->ds_pieces || h->layout[causal] == 3);
+  // the stored-dS form on this run (the 64-key layout's blocks, or the wide-head kernel's pieces)
+  const int32_t ds_fmt = h->ds_form ? h->ds_fmt[causal] : kDsNone;
+  const bool ds_run = ds_fmt != kDsNone;
+  // pieces come from the wide-head kernels only, without a window
+  if (ds_fmt == kDsPieces && !ds_pieces_apply(d)) return FA_BWD_ERR_UNSUPPORTED;
   ma.ds = ds_run ? h->ds : nullptr;
   ma.ds_nqs = h->ds_nqs;
-  ma.ds_nkt = h->ds_nkt;
+  ma.ds_nkt = ds_fmt == kDsPieces ? h->ds_nkt_pieces : h->ds_nkt_blocks;
   ma.dq = static_cast<bf16*>(dq);
   ma.dk = static_cast<bf16*>(dk);
   ma.dv = static_cast<bf16*>(dv);
@@ -459,7 +465,7 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
   } else if (!planned || h->n_q_items > 0) {
     ma.sched = planned ? h->sched + 2 * h->n_kv_items : nullptr;
     ma.head_major = h->dq_head_major[causal] ? 1 : 0;
-    if (ds_run && h->ds_pieces)
+    if (ds_fmt == kDsPieces)
       launch_dq_dsp(ma, h->n_q_items, stream);
     else if (ds_run)
       launch_dq_ds(ma, h->n_q_items, stream);
@@ -739,11 +745,31 @@ fa_bwd_status fa_bwd_create(const fa_bwd_desc* desc, fa_bwd_handle** out) {
     return FA_BWD_ERR_HIP;
   }
   configure_layouts(h, cus);
-  h->ds_pieces = ds_pieces_apply(h->desc);
-  const int64_t ds_need = ds_bytes_of(h->desc, h->ds_pieces, h->ds_nqs, h->ds_nkt);
-  h->ds_form = desc->algorithm == FA_BWD_ALGO_STORED_DS ||
-               (desc->algorithm == FA_BWD_ALGO_DEFAULT && (h->ds_pieces || h->layout[0] == 3 || h->layout[1] == 3) &&
-                ds_need >= 0 && ds_need <= kDsDefaultMaxBytes);
+  // the dS format of runs without and with a causal bound: the explicit form everywhere its kernels run,
+  // the default where it is faster (the 64-key layout, wide heads without a window) and its workspace
+  // stays within kDsDefaultMaxBytes. (The 128-key layouts could store pieces too, but their stores cost
+  // more than the dQ pass saves.)
+  const int64_t need_blocks = ds_bytes_of(h->desc, false, h->ds_nqs, h->ds_nkt_blocks);
+  const int64_t need_pieces = ds_bytes_of(h->desc, true, h->ds_nqs, h->ds_nkt_pieces);
+  const bool d128 = h->desc.head_dim == 128 && h->desc.head_dim_v == 128;
+  const bool explicit_ds = desc->algorithm == FA_BWD_ALGO_STORED_DS;
+  int64_t ds_need = 0;
+  h->ds_form = false;
+  for (int c = 0; c < 2; ++c) {
+    int32_t fmt = kDsNone;
+    if (ds_pieces_apply(h->desc))
+      fmt = kDsPieces;
+    else if (d128 && h->layout[c] == 3)
+      fmt = kDsBlocks;
+    const int64_t need = fmt == kDsBlocks ? need_blocks : fmt == kDsPieces ? need_pieces : 0;
+    if (!explicit_ds && (desc->algorithm != FA_BWD_ALGO_DEFAULT || need < 0 || need > kDsDefaultMaxBytes))
+      fmt = kDsNone;
+    h->ds_fmt[c] = fmt;
+    if (fmt != kDsNone) {
+      h->ds_form = true;
+      ds_need = std::max(ds_need, need);
+    }
+  }
   const size_t ds_bytes = h->ds_form ? (size_t)ds_need : 0;
   const size_t stats = (size_t)desc->total_q * desc->num_heads;
   const size_t acc = stats * desc->head_dim * (h->split ? fa::kSplits : 1);
@@ -899,14 +925,20 @@ int32_t fa_bwd_dkdv_layout(const fa_bwd_handle* h, int32_t mask) {
   if (!h || mask < FA_BWD_MASK_NONE || mask > FA_BWD_MASK_PADDING_CAUSAL) return -1;
   if (h->single_pass) return h->split ? FA_BWD_ALGO_SPLIT_REDUCE : FA_BWD_ALGO_SINGLE_PASS;
   if (!pick_kernels(h->desc.head_dim, h->desc.head_dim_v).two_layouts)  // wide heads: one layout
-    return h->ds_form ? FA_BWD_ALGO_STORED_DS : FA_BWD_ALGO_RECOMPUTE_DQ;
+    return FA_BWD_ALGO_RECOMPUTE_DQ;
   const bool causal = mask == FA_BWD_MASK_CAUSAL || mask == FA_BWD_MASK_PADDING_CAUSAL;
-  if (h->ds_form && h->layout[causal] == 3) return FA_BWD_ALGO_STORED_DS;
   switch (h->layout[causal]) {
     case 3: return FA_BWD_ALGO_RECOMPUTE_DQ_64K;
     case 2: return FA_BWD_ALGO_RECOMPUTE_DQ_4W;
     default: return FA_BWD_ALGO_RECOMPUTE_DQ_8W;
   }
+}
+
+int32_t fa_bwd_dq_form(const fa_bwd_handle* h, int32_t mask) {
+  if (!h || mask < FA_BWD_MASK_NONE || mask > FA_BWD_MASK_PADDING_CAUSAL) return -1;
+  if (h->single_pass) return h->split ? FA_BWD_ALGO_SPLIT_REDUCE : FA_BWD_ALGO_SINGLE_PASS;
+  const bool causal = mask == FA_BWD_MASK_CAUSAL || mask == FA_BWD_MASK_PADDING_CAUSAL;
+  return h->ds_form && h->ds_fmt[causal] != kDsNone ? FA_BWD_ALGO_STORED_DS : FA_BWD_ALGO_RECOMPUTE_DQ;
 }
 
 fa_bwd_status fa_bwd_profile_enable(fa_bwd_handle* h, int32_t enable) {

@@ -1006,8 +1006,9 @@ void fa_bwd_dkdv(MainArgs a) {
   f32x16 s, dp;
   bf16x8 pk[2], dsk[2], dsk_prev[2];
   // this wave's stored-dS piece of step st: 32-row q step t, 32-key tile kt (wide heads, no window)
+  constexpr bool kPieces = C::WIDE && !WINDOW;
   auto store_piece = [&](int st, const bf16x8 (&d)[2]) {
-    if constexpr (C::WIDE && !WINDOW) {
+    if constexpr (kPieces) {
       if (a.ds) {
         const int t = step_tile(st) * C::NMT + mt, kt = tile * NG + grp;
         if (t < a.ds_nqs && kt < a.ds_nkt) {  // inside the workspace (lengths within the maxima)
@@ -1034,7 +1035,7 @@ void fa_bwd_dkdv(MainArgs a) {
     if (sp > 0) store_piece(sp - 1, dsk_prev);
     gemm1(buf, s, dp);
     softmax(sp, buf, s, dp, pk, dsk);
-    if constexpr (C::WIDE && !WINDOW) {
+    if constexpr (kPieces) {
       dsk_prev[0] = dsk[0];
       dsk_prev[1] = dsk[1];
     }

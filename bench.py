@@ -75,8 +75,7 @@ LAYOUT_NAMES = {1: "none (single-pass form)", 3: "none (single-pass form)",
                 2: "one layout (heads wider than 128)",
                 4: "eight-wave workgroups, 32 keys per wave",
                 5: "four-wave workgroups (two per CU), 32 keys per wave",
-                6: "one four-wave workgroup per CU, 64 keys per wave",
-                7: "one four-wave workgroup per CU, 64 keys per wave, dS stored"}
+                6: "one four-wave workgroup per CU, 64 keys per wave"}
 
 
 def kernel_share(algorithm: int, d: int, dv: int, layout: int = 0) -> dict:
@@ -88,12 +87,10 @@ def kernel_share(algorithm: int, d: int, dv: int, layout: int = 0) -> dict:
         return {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_dq_cast": 0.0}
     if algorithm == 3:
         return {"fa_bwd_pre": 0.0, "fa_bwd_main": 1.0, "fa_bwd_split_reduce": 0.0}
-    if algorithm == 7:  # dK/dV kernel: S, dP, dV, dK (and dS stored); the dS pass: dQ
-        wide = d > 128 or dv > 128  # the wide-head kernels store dS pieces (the dS pass reads either form)
-        return {"fa_bwd_pre": 0.0, "fa_bwd_dkdv" if wide else "fa_bwd_dkdv64": (2 * d + 2 * dv) / total,
-                "fa_bwd_dq_ds": d / total}
-    # dK/dV kernel: S, dP, dV, dK; dQ kernel: S and dP again, dQ
     dkdv = "fa_bwd_dkdv64" if layout == 6 else "fa_bwd_dkdv"
+    if algorithm == 7:  # dK/dV kernel: S, dP, dV, dK (and dS stored); the dS pass: dQ
+        return {"fa_bwd_pre": 0.0, dkdv: (2 * d + 2 * dv) / total, "fa_bwd_dq_ds": d / total}
+    # dK/dV kernel: S, dP, dV, dK; dQ kernel: S and dP again, dQ
     return {"fa_bwd_pre": 0.0, dkdv: (2 * d + 2 * dv) / total, "fa_bwd_dq": (2 * d + dv) / total}
 
 
@@ -481,8 +478,8 @@ def main():
     algo = ALGORITHMS[args.algorithm]
     op = binding.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0],
                        algo, num_heads_kv=inp["k"].shape[1], window=inp["window"], head_dim_v=inp["v"].shape[2])
-    layout = op.dkdv_layout(inp["mask"])  # the dK/dV layout (or the stored-dS form) this workload takes
-    algo_used = (7 if layout == 7 else 2) if algo == 0 else algo
+    layout = op.dkdv_layout(inp["mask"])  # the dK/dV layout this workload takes
+    algo_used = op.dq_form(inp["mask"]) if algo == 0 else algo  # the default: stored dS or recompute
     if args.plan:  # host-side longest-first schedule from the (host) sequence offsets
         op.plan(inp["cu_q"], inp["cu_kv"], inp["mask"])
     dq, dk, dv = (torch.empty_like(dev[x]) for x in ("q", "k", "v"))
@@ -525,8 +522,7 @@ def main():
               "total_tokens": tq, "mask": MASK_NAMES[inp["mask"]], "seed": inp["seed"],
               "algorithmic_flops": flops,
               "algorithm": ALGORITHM_NAMES[algo_used],
-              "dkdv_layout": ("one layout (heads wider than 128), dS stored"
-                              if layout == 7 and max(d, inp["v"].shape[2]) > 128 else LAYOUT_NAMES[layout]),
+              "dkdv_layout": LAYOUT_NAMES[layout] + (", dS stored" if algo_used == 7 else ""),
               "schedule": "host longest-first plan" if args.plan else "dense grid"}
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

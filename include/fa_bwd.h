@@ -260,19 +260,26 @@ const char* fa_bwd_status_string(fa_bwd_status s);
 /* Descriptor the handle was created with (for bindings); NULL on NULL. */
 const fa_bwd_desc* fa_bwd_get_desc(const fa_bwd_handle* h);
 
-/* Layout of the recompute form's dK/dV kernel that fa_bwd_run takes on this
- * handle under `mask` (a causal mask, with or without padding, can select
- * another layout than none or padding), chosen when the handle was created
- * from the descriptor and the device's compute-unit count:
- * FA_BWD_ALGO_RECOMPUTE_DQ_8W, FA_BWD_ALGO_RECOMPUTE_DQ_4W or
- * FA_BWD_ALGO_RECOMPUTE_DQ_64K for head dims up to 128, and
- * FA_BWD_ALGO_RECOMPUTE_DQ for wider heads (whose kernels have one layout);
- * FA_BWD_ALGO_STORED_DS where the run takes the stored-dS form (the 64-key layout
- * writing dS, and the dQ pass over it).
+/* Layout of the dK/dV kernel that fa_bwd_run takes on this handle under `mask`
+ * (a causal mask, with or without padding, can select another layout than none
+ * or padding), chosen when the handle was created from the descriptor and the
+ * device's compute-unit count: FA_BWD_ALGO_RECOMPUTE_DQ_8W,
+ * FA_BWD_ALGO_RECOMPUTE_DQ_4W or FA_BWD_ALGO_RECOMPUTE_DQ_64K for head dims up
+ * to 128, and FA_BWD_ALGO_RECOMPUTE_DQ for wider heads (whose kernels have one
+ * layout), whether or not the run stores dS (fa_bwd_dq_form).
  * Returns FA_BWD_ALGO_SINGLE_PASS or FA_BWD_ALGO_SPLIT_REDUCE for handles of
  * those forms, and -1 for a NULL handle or an invalid mask. Host only; does
  * not touch the device. */
 int32_t fa_bwd_dkdv_layout(const fa_bwd_handle* h, int32_t mask);
+
+/* How fa_bwd_run forms dQ on this handle under `mask`, fixed when the handle was
+ * created: FA_BWD_ALGO_STORED_DS (the dK/dV kernel writes dS and a q-outer pass
+ * forms dQ = scale * dS K) or FA_BWD_ALGO_RECOMPUTE_DQ (a q-outer kernel forms S
+ * and dP again), as FA_BWD_ALGO_DEFAULT chooses by the rule stated with it or
+ * the algorithm code forces; FA_BWD_ALGO_SINGLE_PASS or
+ * FA_BWD_ALGO_SPLIT_REDUCE for handles of those forms; -1 for a NULL handle or
+ * an invalid mask. Host only; does not touch the device. */
+int32_t fa_bwd_dq_form(const fa_bwd_handle* h, int32_t mask);
 
 /* Per-kernel timing for benchmarks. While enabled, every fa_bwd_run (and
  * fa_bwd_run_lse) also records four HIP events on its stream, around its three

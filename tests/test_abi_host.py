@@ -133,6 +133,7 @@ def test_run_and_profile_reject_null_handle():
     assert lib.fa_bwd_profile_enable(None, 1) == B.FA_BWD_ERR_INVALID_ARGUMENT
     assert not lib.fa_bwd_get_desc(None)
     assert lib.fa_bwd_dkdv_layout(None, 0) == -1
+    assert lib.fa_bwd_dq_form(None, 0) == -1
 
 
 def _noalloc(desc, ptr=256, l=True):

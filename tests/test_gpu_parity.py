@@ -154,27 +154,32 @@ def test_dkdv_layouts_agree(case):
         P.assert_close(name, y.numpy(), x.numpy().astype(np.float64))
 
 
-@pytest.mark.parametrize("case,expect", [
+@pytest.mark.parametrize("case,expect,form", [
     # causal, d 64 (no 64-key layout), 256 heads of 1024 tokens: the dK/dV work (128-key tiles, 64-row q
     # steps) totals 72 per head, 18432 in all; the largest workgroup has 16, and 2 * 16 * 256 CUs =
     # 8192 <= 18432: the four-wave layout
-    (I.custom_case("layout_rule_4w", 256, 64, I.MASK_CAUSAL, 213, [1024]), B.FA_BWD_ALGO_RECOMPUTE_DQ_4W),
+    (I.custom_case("layout_rule_4w", 256, 64, I.MASK_CAUSAL, 213, [1024]), B.FA_BWD_ALGO_RECOMPUTE_DQ_4W,
+     B.FA_BWD_ALGO_RECOMPUTE_DQ),
     # no mask, 8 heads of 2 x 2048 tokens: 256-key tiles of 64 steps (32 rows) total 8192, and
     # 2 * 64 * 256 > 8192; 128-key tiles: 256 workgroups of 32 steps, 2 * 32 * 256 > 8192: eight waves
-    (I.custom_case("layout_rule_8w", 8, 128, I.MASK_NONE, 214, [2048, 2048]), B.FA_BWD_ALGO_RECOMPUTE_DQ_8W),
+    (I.custom_case("layout_rule_8w", 8, 128, I.MASK_NONE, 214, [2048, 2048]), B.FA_BWD_ALGO_RECOMPUTE_DQ_8W,
+     B.FA_BWD_ALGO_RECOMPUTE_DQ),
     # causal, d 128, 256 heads of 1024 tokens: 256-key tiles of 32, 24, 16 and 8 steps total 80 per
     # head, 20480 in all, and 2 * 32 * 256 = 16384 <= 20480: the 64-key layout, and with it the stored-dS
     # form (its dS workspace: 256 heads x 32 q steps x 4 kv tiles x 16 KiB = 512 MiB, within 8 GiB)
-    (I.custom_case("layout_rule_64k", 256, 128, I.MASK_CAUSAL, 215, [1024]), B.FA_BWD_ALGO_STORED_DS),
+    (I.custom_case("layout_rule_64k", 256, 128, I.MASK_CAUSAL, 215, [1024]), B.FA_BWD_ALGO_RECOMPUTE_DQ_64K,
+     B.FA_BWD_ALGO_STORED_DS),
     # causal, d 128, 64 query heads over 16 K/V heads of 2048 tokens: each workgroup runs the steps of 4
     # query heads; 256-key tiles: 288 steps per head, 18432 in all, largest workgroup 4 * 64, and
     # 2 * 256 * 256 > 18432; 128-key tiles: 17408 in all, largest 4 * 32, 2 * 128 * 256 > 17408: eight waves
     (I.custom_case("layout_rule_gqa", 64, 128, I.MASK_CAUSAL, 216, [2048], heads_kv=16),
-     B.FA_BWD_ALGO_RECOMPUTE_DQ_8W),
+     B.FA_BWD_ALGO_RECOMPUTE_DQ_8W, B.FA_BWD_ALGO_RECOMPUTE_DQ),
 ], ids=lambda x: x.name if hasattr(x, "name") else str(x))
-def test_default_picks_the_balanced_dkdv_layout(case, expect):
+def test_default_picks_the_balanced_dkdv_layout(case, expect, form):
     """The default form takes the dK/dV layout the load-balance rule names (figures for the 256
-    compute units of an MI355X): its results equal that layout's bitwise."""
+    compute units of an MI355X) and the dQ form its rule names: its dK, dV equal that layout's recompute
+    form bitwise (the same kernel, with dS stores where it stores dS), and its dQ equals the recompute
+    form's bitwise or, from stored dS, within the tolerance."""
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the expected layouts are worked out for 256 compute units")
     inp = I.make(case)
@@ -182,12 +187,16 @@ def test_default_picks_the_balanced_dkdv_layout(case, expect):
     with B.FaBwd(inp["batch"], heads, d, inp["max_seqlen_q"], inp["max_seqlen_kv"], tq, inp["k"].shape[0],
                  num_heads_kv=inp["k"].shape[1]) as op:
         assert op.dkdv_layout(case.mask) == expect
-        assert op.dkdv_layout(-1) == -1
+        assert op.dq_form(case.mask) == form
+        assert op.dkdv_layout(-1) == -1 and op.dq_form(-1) == -1
     o, m, l = P.oracle_stats(inp)
     got = P.run_gpu(inp, o, m, l, algorithm=B.FA_BWD_ALGO_DEFAULT)
     ref = P.run_gpu(inp, o, m, l, algorithm=expect)
-    for name, x, y in zip(("dq", "dk", "dv"), got, ref):
-        assert torch.equal(x, y), f"{name}: the default form did not take the expected layout"
+    assert torch.equal(got[1], ref[1]) and torch.equal(got[2], ref[2]), "dk, dv: not the expected layout"
+    if form == B.FA_BWD_ALGO_STORED_DS:
+        P.assert_close("dq", got[0].numpy(), ref[0].numpy().astype(np.float64))
+    else:
+        assert torch.equal(got[0], ref[0]), "dq: not the recompute form"
 
 
 # sequences longer than 8 kv tiles of 128 keys: each split-reduce workgroup walks several tiles and
