@@ -40,6 +40,8 @@ struct fa_bwd_handle {
   // the dQ and dK/dV kernels' dense grids in head-major order per XCD (head_major_balances), without
   // and with a causal bound
   bool dq_head_major[2], dkdv_head_major[2];
+  // the stored-dS pass's dense grid in head-major order (two workgroups per CU at every head dim)
+  bool ds_head_major[2];
   // the dQ kernel in two key groups per workgroup (dq_key_split)
   bool dq_split;
   // stored-dS form: the dK/dV kernel writes dS, and the dQ pass reads it, in the format ds_fmt gives for
@@ -464,7 +466,7 @@ fa_bwd_status launch(fa_bwd_handle* h, const void* q, const void* k, const void*
       d.head_dim == 128 ? launch_cast<128>(ma, stream) : launch_cast<64>(ma, stream);
   } else if (!planned || h->n_q_items > 0) {
     ma.sched = planned ? h->sched + 2 * h->n_kv_items : nullptr;
-    ma.head_major = h->dq_head_major[causal] ? 1 : 0;
+    ma.head_major = (ds_run ? h->ds_head_major[causal] : h->dq_head_major[causal]) ? 1 : 0;
     if (ds_fmt == kDsPieces)
       launch_dq_dsp(ma, h->n_q_items, stream);
     else if (ds_run)
@@ -637,6 +639,8 @@ void configure_layouts(fa_bwd_handle* h, int cus) {
     dq_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), qtotal, qlargest);
     h->dq_head_major[c] = head_major_balances((double)qtotal * (double)per_tile_heads, (double)qlargest,
                                               (int64_t)cus * (narrow && !h->dq_split ? 2 : 1), per_tile_heads);
+    h->ds_head_major[c] = head_major_balances((double)qtotal * (double)per_tile_heads, (double)qlargest,
+                                              (int64_t)cus * 2, per_tile_heads);
   }
 }
 
