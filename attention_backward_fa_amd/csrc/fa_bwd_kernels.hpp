@@ -817,9 +817,9 @@ void fa_bwd_dkdv(MainArgs a) {
   for (int nt = 0; nt < C::NTQ; ++nt) acc_k[C::WIDE ? 0 : nt] = f32x16{};
 #pragma unroll
   for (int i = 0; i < C::NTW; ++i) acc_w[i] = f32x16{};
-  // wide heads: output tile i of this wave is dV tile nt (is_v) or dK tile nt (wave-uniform)
-  auto wide_tile = [&](int i, bool& is_v, int& nt) {
-    if (mt == 0) {
+  // wide heads: output tile i of the M-tile m wave is dV tile nt (is_v) or dK tile nt (wave-uniform)
+  auto wide_tile = [&](int m, int i, bool& is_v, int& nt) {
+    if (m == 0) {
       is_v = i < C::NTV - C::BY;
       nt = is_v ? i : C::NTQ - C::BX + (i - (C::NTV - C::BY));
     } else {
@@ -936,8 +936,11 @@ void fa_bwd_dkdv(MainArgs a) {
   };
   // the wide heads' step 7 / step 6 over the whole step: swap with the partner wave (the M-tile 0
   // wave needs the partner's P for dV, the other the partner's dS for dK), then one GEMM over the
-  // step's 64 q rows, k-steps in row order
-  auto gemm2_swap = [&](int bi, const bf16x8* pk, const bf16x8* dsk) {
+  // step's 64 q rows, k-steps in row order. Built once per M-tile (mt_c, called under a wave-uniform
+  // branch), so that the roles' choices of A operands, output tiles and B rows are made at compile
+  // time rather than by per-element selects
+  auto gemm2_swap = [&](auto mt_c, int bi, const bf16x8* pk, const bf16x8* dsk) {
+    constexpr int mt = decltype(mt_c)::value;
     // the balanced layout publishes four values per lane, stored [wave][value][lane] so that each 16-byte
     // access of a wave is one contiguous 1 KB run (a 64-byte lane stride costs bank conflicts: -6 % on
     // the balanced pass); two values keep [wave][lane][value], measured as fast or slightly faster
@@ -980,7 +983,7 @@ void fa_bwd_dkdv(MainArgs a) {
       const int ksi = i / C::NTW;
       bool is_v;
       int nt;
-      wide_tile(i % C::NTW, is_v, nt);
+      wide_tile(mt, i % C::NTW, is_v, nt);
       const int qs = is_v ? QSV : QSQ;
       const bf16* bsrc = is_v ? tile_do(bi) : tile_q(bi);
       const int o = (is_v ? browv : browk) + 16 * ksi * qs + 32 * nt;
@@ -995,7 +998,7 @@ void fa_bwd_dkdv(MainArgs a) {
       const int ksi = i / C::NTW, t = i % C::NTW;
       bool is_v;
       int nt;
-      wide_tile(t, is_v, nt);
+      wide_tile(mt, t, is_v, nt);
       acc_w[t] = mfma32x32x16(is_v ? ap[ksi] : ad[ksi], bw[i], acc_w[t]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1029,27 +1032,54 @@ void fa_bwd_dkdv(MainArgs a) {
   }
   wait_tiles();
   __syncthreads();
-  for (int sp = 0, buf = 0; sp < n_steps; ++sp, buf ^= 1) {
-    const bool has_next = sp + 1 < n_steps;
-    float st_next = 0.f;
-    if (has_next) {
-      issue_tile(sp + 1, buf ^ 1);
-      st_next = load_stats(sp + 1);
-    }
-    if (sp > 0) store_piece(sp - 1, dsk_prev);
-    gemm1(buf, s, dp);
-    softmax(sp, buf, s, dp, pk, dsk);
-    if constexpr (kPieces) {
-      dsk_prev[0] = dsk[0];
-      dsk_prev[1] = dsk[1];
-    }
-    if constexpr (C::WIDE)
-      gemm2_swap(buf, pk, dsk);
+  if constexpr (C::WIDE) {
+    // one copy of the loop per M-tile (a branch inside it would make the two gemm2_swap copies
+    // keep the accumulators in different registers, and copy them back every step)
+    auto step_loop = [&](auto mt_c) {
+      for (int sp = 0, buf = 0; sp < n_steps; ++sp, buf ^= 1) {
+        const bool has_next = sp + 1 < n_steps;
+        float st_next = 0.f;
+        if (has_next) {
+          issue_tile(sp + 1, buf ^ 1);
+          st_next = load_stats(sp + 1);
+        }
+        if (sp > 0) store_piece(sp - 1, dsk_prev);
+        gemm1(buf, s, dp);
+        softmax(sp, buf, s, dp, pk, dsk);
+        if constexpr (kPieces) {
+          dsk_prev[0] = dsk[0];
+          dsk_prev[1] = dsk[1];
+        }
+        gemm2_swap(mt_c, buf, pk, dsk);
+        if (has_next) store_stats(buf ^ 1, st_next);
+        wait_tiles();
+        __syncthreads();
+      }
+    };
+    if (mt == 0)
+      step_loop(std::integral_constant<int, 0>{});
     else
+      step_loop(std::integral_constant<int, 1>{});
+  } else {
+    for (int sp = 0, buf = 0; sp < n_steps; ++sp, buf ^= 1) {
+      const bool has_next = sp + 1 < n_steps;
+      float st_next = 0.f;
+      if (has_next) {
+        issue_tile(sp + 1, buf ^ 1);
+        st_next = load_stats(sp + 1);
+      }
+      if (sp > 0) store_piece(sp - 1, dsk_prev);
+      gemm1(buf, s, dp);
+      softmax(sp, buf, s, dp, pk, dsk);
+      if constexpr (kPieces) {
+        dsk_prev[0] = dsk[0];
+        dsk_prev[1] = dsk[1];
+      }
       gemm2(buf, pk, dsk);
-    if (has_next) store_stats(buf ^ 1, st_next);
-    wait_tiles();
-    __syncthreads();
+      if (has_next) store_stats(buf ^ 1, st_next);
+      wait_tiles();
+      __syncthreads();
+    }
   }
   if (n_steps > 0) store_piece(n_steps - 1, dsk_prev);  // the last step's piece
 
@@ -1088,7 +1118,7 @@ void fa_bwd_dkdv(MainArgs a) {
     for (int i = 0; i < C::NTW; ++i) {
       bool is_v;
       int nt;
-      wide_tile(i, is_v, nt);
+      wide_tile(mt, i, is_v, nt);
       const int dcol = 32 * nt + c;
       if (dcol >= (is_v ? dvd : dqk)) continue;
       bf16* dst = is_v ? a.dv : a.dk;
