@@ -601,14 +601,18 @@ void fa_bwd_main(MainArgs a) {
 // NMT = 2, eight waves (two per SIMD, one workgroup per CU): the two waves of a 32-key group split
 // each 64-row q step. With NMT = 1, four waves (72 KB of LDS at d = 128, so two workgroups share a
 // CU and their waves do not wait on each other's barriers): each wave takes whole 32-row q steps for
-// its keys. Wider heads: four
-// waves (one per SIMD, accumulators in the larger register budget of a single wave), a 64-row kv
-// tile whose K and V fragments are held in registers, so that LDS holds only the Q and dO tiles.
+// its keys. Wider heads: one wave per
+// SIMD (accumulators in the larger register budget of a single wave), a 64-row kv tile whose K and V
+// fragments are held in registers, so that LDS holds only the Q and dO tiles; with NMT = 2 four waves
+// whose row groups' two waves swap P and dS each step and split the output tiles, with NMT = 1 (where
+// one wave holds both outputs' accumulators, head dims summing to at most 320) two waves, each with
+// whole 32-row q steps and whole sums for its keys, two workgroups per CU.
 template <int DQ, int DV, int NMT_ = 2>
 struct DkdvCfg {
   static constexpr bool WIDE = DQ > 128 || DV > 128;
   static constexpr int NMT = NMT_;               // M-tiles per step
-  static_assert(NMT == 2 || (NMT == 1 && !WIDE), "wide heads take 64-row q steps");
+  static_assert(NMT == 1 || NMT == 2, "one or two M-tiles per step");
+  static constexpr bool SWAP = WIDE && NMT == 2;  // the two waves of a row group swap P and dS
   static constexpr int WPE = WIDE ? 1 : 2;       // waves per SIMD
   static constexpr int BN = WIDE ? 64 : 128;     // kv rows per workgroup: row groups of 32
   static constexpr int BM = 32 * NMT;            // q rows per step: M-tiles of 32
@@ -634,13 +638,13 @@ struct DkdvCfg {
   static constexpr int OFF_ST = OFF_DO + 2 * TD_BYTES;        // [2 buffers][lse2, D][BM] fp32
   // wide heads: the two waves of a row group split the second GEMMs' output tiles, as many each; the
   // M-tile 0 wave takes dV tiles [0, NTV - BY) and dK tiles [NTQ - BX, NTQ), the other the rest
-  static constexpr int BX = WIDE && NTQ > NTV ? (NTQ - NTV) / 2 : 0;
-  static constexpr int BY = WIDE && NTV > NTQ ? (NTV - NTQ) / 2 : 0;
+  static constexpr int BX = SWAP && NTQ > NTV ? (NTQ - NTV) / 2 : 0;
+  static constexpr int BY = SWAP && NTV > NTQ ? (NTV - NTQ) / 2 : 0;
   static constexpr bool BAL = BX > 0 || BY > 0;      // each wave needs both P and dS of both M-tiles
-  static constexpr int NTW = WIDE ? (NTQ + NTV) / 2 : 1;  // output tiles per wave
+  static constexpr int NTW = SWAP ? (NTQ + NTV) / 2 : 1;  // output tiles per wave
   static constexpr int OFF_X = OFF_ST + 4 * BM * 4;  // wide: [wave][lane] 2 bf16x8 of P or dS (4: both)
   static constexpr int PART_BYTES = NMT == 2 && !WIDE ? NG * (NTQ + NTV) * 64 * 64 : 0;  // partial dK, then dV
-  static constexpr int TILE_END = OFF_X + (WIDE ? NW * 64 * (BAL ? 64 : 32) : 0);
+  static constexpr int TILE_END = OFF_X + (SWAP ? NW * 64 * (BAL ? 64 : 32) : 0);
   // the end-of-kernel exchange of partial sums reuses the whole allocation
   static constexpr int LDS_BYTES = TILE_END > PART_BYTES ? TILE_END : PART_BYTES;
   static_assert(DQ % 32 == 0 && DV % 32 == 0 && DQ <= 256 && DV <= 256, "padded head dims");
@@ -650,14 +654,15 @@ struct DkdvCfg {
 };
 
 // dK and dV of one (kv tile, K/V head, sequence). Row group r = w % NG owns kv rows 32 r .. 32 r + 31,
-// and the two waves of a group each take one 32-row M-tile mt = w / NG of every 64-row q step. Each
-// wave forms S = Q K^T, dP = dO V^T, P and dS for its M-tile (steps 1-5). Heads up to 128: each wave
-// accumulates its partial dV += P^T dO and dK += dS^T Q over its M-tile's rows (steps 7, 6), so the
-// waves of a step never wait for each other, and after the last step the two waves of a group
-// combine their partial sums through LDS (the M-tile 0 wave finishes dV, the other dK). Wider heads,
-// where both accumulators of a wave would not fit its registers next to the K and V fragments: the
-// waves of a group swap P and dS through LDS each step, and the M-tile 0 wave accumulates dV over
-// both M-tiles, the other dK. Wide heads without a window, when a.ds is set: each wave also stores its
+// and with NMT = 2 the two waves of a group each take one 32-row M-tile mt = w / NG of every 64-row q
+// step (NMT = 1: one wave per group, 32-row q steps). Each wave forms S = Q K^T, dP = dO V^T, P and dS
+// for its M-tile (steps 1-5). Heads up to 128, and wider heads with NMT = 1: each wave accumulates its
+// partial dV += P^T dO and dK += dS^T Q over its M-tile's rows (steps 7, 6), so the waves of a step
+// never wait for each other, and with NMT = 2 after the last step the two waves of a group combine
+// their partial sums through LDS (the M-tile 0 wave finishes dV, the other dK). Wider heads with
+// NMT = 2, where both accumulators of a wave would not fit its registers next to the K and V fragments:
+// the waves of a group swap P and dS through LDS each step, and split the output tiles, each over
+// both M-tiles (wide_tile). Wide heads without a window, when a.ds is set: each wave also stores its
 // step's dS as a piece of the stored-dS form (ds_piece), non-temporal (read once, by the dQ pass), at the
 // start of the next step, so that the stores complete before the step's closing wait for its transfers.
 template <int DQ, int DV, bool CAUSAL, bool WINDOW, bool EXACT, int NMT>
@@ -808,13 +813,13 @@ void fa_bwd_dkdv(MainArgs a) {
     if (tid < 2 * BM) s_st[bi * 2 * BM + tid] = v;
   };
 
-  // heads up to 128: partial dV and dK / scale of rows 32 grp .. +31 over this M-tile; wider heads:
-  // acc_w holds this wave's NTW output tiles of those rows over whole steps (wide_tile)
-  f32x16 acc_v[C::WIDE ? 1 : C::NTV], acc_k[C::WIDE ? 1 : C::NTQ], acc_w[C::NTW];
+  // partial dV and dK / scale of rows 32 grp .. +31 over this M-tile; with the P/dS swap (wider heads,
+  // NMT = 2), acc_w holds this wave's NTW output tiles of those rows over whole steps (wide_tile)
+  f32x16 acc_v[C::SWAP ? 1 : C::NTV], acc_k[C::SWAP ? 1 : C::NTQ], acc_w[C::NTW];
 #pragma unroll
-  for (int nt = 0; nt < C::NTV; ++nt) acc_v[C::WIDE ? 0 : nt] = f32x16{};
+  for (int nt = 0; nt < C::NTV; ++nt) acc_v[C::SWAP ? 0 : nt] = f32x16{};
 #pragma unroll
-  for (int nt = 0; nt < C::NTQ; ++nt) acc_k[C::WIDE ? 0 : nt] = f32x16{};
+  for (int nt = 0; nt < C::NTQ; ++nt) acc_k[C::SWAP ? 0 : nt] = f32x16{};
 #pragma unroll
   for (int i = 0; i < C::NTW; ++i) acc_w[i] = f32x16{};
   // wide heads: output tile i of the M-tile m wave is dV tile nt (is_v) or dK tile nt (wave-uniform)
@@ -929,8 +934,8 @@ void fa_bwd_dkdv(MainArgs a) {
     for (int i = 0; i < NB; ++i) {
       if (i + PF < NB) ld(i + PF);
       const int s2 = i / C::NTM, nt = i % C::NTM;
-      if (nt < C::NTV) acc_v[C::WIDE ? 0 : nt] = mfma32x32x16(pk[s2], bd[i], acc_v[C::WIDE ? 0 : nt]);
-      if (nt < C::NTQ) acc_k[C::WIDE ? 0 : nt] = mfma32x32x16(dsk[s2], bq[i], acc_k[C::WIDE ? 0 : nt]);
+      if (nt < C::NTV) acc_v[C::SWAP ? 0 : nt] = mfma32x32x16(pk[s2], bd[i], acc_v[C::SWAP ? 0 : nt]);
+      if (nt < C::NTQ) acc_k[C::SWAP ? 0 : nt] = mfma32x32x16(dsk[s2], bq[i], acc_k[C::SWAP ? 0 : nt]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -1032,7 +1037,7 @@ void fa_bwd_dkdv(MainArgs a) {
   }
   wait_tiles();
   __syncthreads();
-  if constexpr (C::WIDE) {
+  if constexpr (C::SWAP) {
     // one copy of the loop per M-tile (a branch inside it would make the two gemm2_swap copies
     // keep the accumulators in different registers, and copy them back every step)
     auto step_loop = [&](auto mt_c) {
@@ -1113,7 +1118,7 @@ void fa_bwd_dkdv(MainArgs a) {
       }
     }
   };
-  if constexpr (C::WIDE) {  // this wave's output tiles (wide_tile): dV, and dK = scale * acc
+  if constexpr (C::SWAP) {  // this wave's output tiles (wide_tile): dV, and dK = scale * acc
 #pragma unroll
     for (int i = 0; i < C::NTW; ++i) {
       bool is_v;

@@ -31,9 +31,13 @@ struct Recompute {
       fa_bwd_dkdv<DQ, DV, false, false, EXACT, NMT><<<grid, block, 0, s>>>(a);
   }
   // items: the workgroup count of a host schedule (a.sched), else unused; four_waves: the four-wave
-  // layout (heads up to 128; wider heads have one layout)
+  // layout (heads up to 128; wider heads have one layout per pair of head dims: one M-tile per step
+  // where both outputs' accumulators fit one wave, same tiles and order of every sum as two M-tiles,
+  // without the P/dS swap; else two)
   static void dkdv(const MainArgs& a, int64_t items, bool four_waves, hipStream_t s) {
-    if constexpr (DkdvCfg<DQ, DV>::WIDE)
+    if constexpr (DkdvCfg<DQ, DV>::WIDE && DQ + DV <= 320)  // accumulators of both outputs fit one wave
+      dkdv_layout<1>(a, items, s);
+    else if constexpr (DkdvCfg<DQ, DV>::WIDE)
       dkdv_layout<2>(a, items, s);
     else if (four_waves)
       dkdv_layout<1>(a, items, s);
