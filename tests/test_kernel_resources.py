@@ -86,14 +86,16 @@ def test_dq_kernel_budgets(notes):
 
 def test_128key_and_wide_dkdv_budgets(notes):
     # <DQ, DV, causal, window, exact, M-tiles>: heads up to 128 two waves per SIMD (eight-wave workgroups,
-    # or two four-wave workgroups per CU), wider heads one; no VGPR spills
+    # or two four-wave workgroups per CU), wider heads one (four-wave workgroups with two M-tiles, or
+    # two two-wave workgroups per CU with one); no VGPR spills
     for name, (args, vgpr, spill, lds) in _kernels(notes, "_ZN2fa11fa_bwd_dkdvI").items():
         dq, dv, nmt = args[0], args[1], args[5]
         assert spill == 0, name
         if max(dq, dv) <= 128:
             assert vgpr <= 256 and (2 if nmt == 1 else 1) * lds <= LDS_PER_CU, name
         else:
-            assert vgpr <= 512 and lds <= LDS_PER_CU, name
+            assert vgpr <= 512 and (2 if nmt == 1 else 1) * lds <= LDS_PER_CU, name
+            assert nmt == 2 or dq + dv <= 320, name  # one M-tile only where both outputs' sums fit
 
 
 def test_row_kernels_do_not_spill(notes):
