@@ -223,17 +223,26 @@ void launch_dkdv64(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
               : fa::fa_bwd_dkdv64<false, false, false><<<grid, block, 0, stream>>>(ma);
 }
 
-// the stored-dS form's dQ pass: one workgroup per (128-row q tile, head, sequence), as the dQ kernel
-void launch_dq_ds(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
-  using C = fa::DqDsCfg<128>;
+// the stored-dS form's dQ pass over the 64-key kernel's dS blocks: on the dense grid one eight-wave
+// workgroup per (256-row q tile, head, sequence); under a host schedule, whose work items are the dQ
+// kernel's 128-row q tiles, four-wave workgroups (each wave computes the same sums in either)
+template <int NW>
+void launch_dq_ds_waves(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
+  using C = fa::DqDsCfg<128, NW>;
   const int64_t blocks = (int64_t)((ma.max_seqlen_q + C::BQ - 1) / C::BQ) * ma.H * ma.batch;
   const dim3 grid((unsigned)(ma.sched ? items : blocks)), block(C::NT);
   if (ma.window > 0)
-    fa::fa_bwd_dq_ds<128, true, false, true, true><<<grid, block, 0, stream>>>(ma);
+    fa::fa_bwd_dq_ds<128, true, false, true, true, NW><<<grid, block, 0, stream>>>(ma);
   else if (ma.causal)
-    fa::fa_bwd_dq_ds<128, true, false, true, false><<<grid, block, 0, stream>>>(ma);
+    fa::fa_bwd_dq_ds<128, true, false, true, false, NW><<<grid, block, 0, stream>>>(ma);
   else
-    fa::fa_bwd_dq_ds<128, true, false, false, false><<<grid, block, 0, stream>>>(ma);
+    fa::fa_bwd_dq_ds<128, true, false, false, false, NW><<<grid, block, 0, stream>>>(ma);
+}
+void launch_dq_ds(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
+  if (ma.sched)
+    launch_dq_ds_waves<4>(ma, items, stream);
+  else
+    launch_dq_ds_waves<8>(ma, items, stream);
 }
 
 // the stored-dS form's dQ pass over the wide-head kernels' dS pieces, for the Q/K head dim padded as the

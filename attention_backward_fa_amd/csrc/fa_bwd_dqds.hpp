@@ -29,10 +29,12 @@
 
 namespace fa {
 
-template <int DQ>
+// NW_ waves, one 32-row q step each: four (two workgroups per CU), or eight (one per CU; each K tile
+// brought to LDS serves twice the rows, so the pass fetches fewer K bytes)
+template <int DQ, int NW_ = 4>
 struct DqDsCfg {
   static constexpr int D = DQ;               // the Q/K head dim, padded to a multiple of 32
-  static constexpr int NW = 4, NT = 64 * NW;
+  static constexpr int NW = NW_, NT = 64 * NW;
   static constexpr int BQ = 32 * NW;         // q rows per workgroup
   static constexpr int BK = 64;              // keys per step
   static constexpr int QS = D + 8;           // padded row stride of the K tile
@@ -48,11 +50,12 @@ struct DqDsCfg {
 
 // EXACT: the Q/K head dim equals DQ (else a.d_qk, padded to DQ); PIECES: the wide-head kernel's pieces
 // (no window), else the 64-key kernel's blocks
-template <int DQ, bool EXACT, bool PIECES, bool CAUSAL, bool WINDOW>
-__global__ __attribute__((amdgpu_flat_work_group_size(DqDsCfg<DQ>::NT, DqDsCfg<DQ>::NT), amdgpu_waves_per_eu(2, 2)))
+template <int DQ, bool EXACT, bool PIECES, bool CAUSAL, bool WINDOW, int NW = 4>
+__global__ __attribute__((amdgpu_flat_work_group_size(DqDsCfg<DQ, NW>::NT, DqDsCfg<DQ, NW>::NT),
+                          amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_ds(MainArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using C = DqDsCfg<DQ>;
+  using C = DqDsCfg<DQ, NW>;
   constexpr int BQ = C::BQ, BK = C::BK, QS = C::QS, D = C::D, NTQ = C::NTQ;
   static_assert(CAUSAL || !WINDOW, "a window implies the causal bound");
   static_assert(!PIECES || !WINDOW, "pieces are stored without a window");
@@ -94,7 +97,7 @@ void fa_bwd_dq_ds(MainArgs a) {
   const int rskqb = (int)(rskq * 2);
   const int hk = h / (a.H / a.Hk);
   const bf16* kb = a.k + kv_start * rskq + (int64_t)hk * dqk;
-  const int t = qtile * 4 + w;  // this wave's 32-row q step
+  const int t = qtile * NW + w;  // this wave's 32-row q step
   // the wave's dS blocks (one per 256-key kv tile) or pieces (one per 32-key tile). A step whose rows
   // all lie past the sequence has none (past the longest sequence, none inside the workspace): its loads
   // read an empty range.
