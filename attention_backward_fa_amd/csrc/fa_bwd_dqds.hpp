@@ -30,7 +30,7 @@
 namespace fa {
 
 // NW_ waves, one 32-row q step each: four (two workgroups per CU), or eight (one per CU; each K tile
-// brought to LDS serves twice the rows, so the pass fetches fewer K bytes)
+// brought to LDS serves twice the rows, half the transfers from L2)
 template <int DQ, int NW_ = 4>
 struct DqDsCfg {
   static constexpr int D = DQ;               // the Q/K head dim, padded to a multiple of 32
