@@ -247,18 +247,26 @@ void launch_dq_ds(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
 
 // the stored-dS form's dQ pass over the wide-head kernels' dS pieces, for the Q/K head dim padded as the
 // wide-head kernels pad it (128, 192 or 256); built here, with the MFMA accumulators in VGPRs, so that
-// two workgroups fit each CU
-template <int DQ>
-void launch_dq_dsp_dim(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
-  using C = fa::DqDsCfg<DQ>;
+// two four-wave workgroups fit each CU. At 256, on the dense grid, one eight-wave workgroup per CU
+// (measured faster there; at 192 the whole step measured slower)
+template <int DQ, int NW>
+void launch_dq_dsp_waves(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
+  using C = fa::DqDsCfg<DQ, NW>;
   const int64_t blocks = (int64_t)((ma.max_seqlen_q + C::BQ - 1) / C::BQ) * ma.H * ma.batch;
   const dim3 grid((unsigned)(ma.sched ? items : blocks)), block(C::NT);
   if (ma.d_qk == DQ)
-    ma.causal ? fa::fa_bwd_dq_ds<DQ, true, true, true, false><<<grid, block, 0, stream>>>(ma)
-              : fa::fa_bwd_dq_ds<DQ, true, true, false, false><<<grid, block, 0, stream>>>(ma);
+    ma.causal ? fa::fa_bwd_dq_ds<DQ, true, true, true, false, NW><<<grid, block, 0, stream>>>(ma)
+              : fa::fa_bwd_dq_ds<DQ, true, true, false, false, NW><<<grid, block, 0, stream>>>(ma);
   else
-    ma.causal ? fa::fa_bwd_dq_ds<DQ, false, true, true, false><<<grid, block, 0, stream>>>(ma)
-              : fa::fa_bwd_dq_ds<DQ, false, true, false, false><<<grid, block, 0, stream>>>(ma);
+    ma.causal ? fa::fa_bwd_dq_ds<DQ, false, true, true, false, NW><<<grid, block, 0, stream>>>(ma)
+              : fa::fa_bwd_dq_ds<DQ, false, true, false, false, NW><<<grid, block, 0, stream>>>(ma);
+}
+template <int DQ>
+void launch_dq_dsp_dim(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
+  if (DQ == 256 && !ma.sched)
+    launch_dq_dsp_waves<DQ, 8>(ma, items, stream);
+  else
+    launch_dq_dsp_waves<DQ, 4>(ma, items, stream);
 }
 void launch_dq_dsp(const fa::MainArgs& ma, int64_t items, hipStream_t stream) {
   const int pq = ma.d_qk <= 128 ? 128 : ma.d_qk <= 192 ? 192 : 256;
