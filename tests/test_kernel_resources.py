@@ -67,9 +67,11 @@ def test_64key_dkdv_kernel_one_wave_per_simd(notes):
 
 
 def test_stored_ds_pass_two_waves_per_simd(notes):
-    # <DQ, exact, pieces, causal, window>: two workgroups of four waves per CU
+    # <DQ, exact, pieces, causal, window, waves>: two workgroups of four waves per CU, or one of eight
     for name, (args, vgpr, spill, lds) in _kernels(notes, "_ZN2fa12fa_bwd_dq_dsI").items():
-        assert vgpr <= 256 and spill == 0 and 2 * lds <= LDS_PER_CU, name
+        waves = args[5]
+        assert waves in (4, 8), name
+        assert vgpr <= 256 and spill == 0 and (8 // waves) * lds <= LDS_PER_CU, name
 
 
 def test_dq_kernel_budgets(notes):
