@@ -21,6 +21,8 @@ CASES = [
     I.custom_case("plan_padded_causal", 2, 128, PADC, 404, [300, 131], padded_len=320),
     I.custom_case("plan_gqa_window", 4, 128, CAUSAL, 405, [600, 90], heads_kv=2, window=100),
     I.custom_case("plan_wide_mla", 2, 192, CAUSAL, 406, [333, 70], head_dim_v=128),
+    # d = 256: the stored-dS pass runs eight-wave workgroups on the dense grid, four-wave ones planned
+    I.custom_case("plan_wide_d256", 2, 256, CAUSAL, 408, [300, 77, 260]),
     # 96 heads x 4 sequences of up to 1024 tokens, no mask: the dQ kernel's dense grid runs head-major
     # per XCD (384 (sequence, head) pairs divide over 8 XCDs; the largest workgroup, 16 key steps, is
     # under a quarter of the work per slot on 256 CUs)
