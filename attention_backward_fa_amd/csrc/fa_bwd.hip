@@ -656,6 +656,8 @@ void configure_layouts(fa_bwd_handle* h, int cus) {
     dq_work(hd.max_seqlen_q, hd.max_seqlen_kv, c == 1 || hd.window > 0, effective_window(hd), qtotal, qlargest);
     h->dq_head_major[c] = head_major_balances((double)qtotal * (double)per_tile_heads, (double)qlargest,
                                               (int64_t)cus * (narrow && !h->dq_split ? 2 : 1), per_tile_heads);
+    // the stored-dS pass: counted as 128-row tiles, two per CU; its eight-wave workgroups (256 rows, one
+    // per CU) double the largest item and halve the slots, the same product
     h->ds_head_major[c] = head_major_balances((double)qtotal * (double)per_tile_heads, (double)qlargest,
                                               (int64_t)cus * 2, per_tile_heads);
   }
